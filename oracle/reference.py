@@ -1,0 +1,171 @@
+"""Plain reference of the quantized GEMM: decode -> dequantize -> float64 GEMM.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+What is computed (readings of the Humming pages, listed with reasons in the
+design notes):
+
+* The announcement's section "Shared CUDA components" says dequantization and
+  scaling are part of the kernel's computation, and the English benchmark page,
+  section "H100 group-32 W4A8", says the fused kernel and the QDQ baseline
+  (dequantize, then a plain GEMM) were all numerically correct.  So the
+  reference is the QDQ form written out: decode every code exactly,
+  dequantize, and multiply in float64.
+* Dequantized weight (A16 formats): the exact real ``(q - z) * s``, with q the
+  decoded code, z the group's zero point (0 for symmetric formats) and s the
+  group's bf16 scale, groups running along K.  No rounding is applied: the
+  product of a <=5-bit integer and a bf16 is exact in binary32 and in float64.
+* MXFP4 weights and MXFP8 activations: ``e2m1(c) * 2^(e-127)`` and
+  ``e4m3(a) * 2^(ea-127)``, one e8m0 scale per 32 consecutive K elements.
+* Y = Xdq @ Wdq^T summed in float64.
+* MoE (announcement, "WnA16" section: tokens spread over experts with
+  per-expert load): pair p = t*topk + j goes to expert topk_ids[t, j]; its output
+  row is the dense product of its input row with that expert's weights.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+from . import formats as F
+
+W_INT4, W_UINT4, W_INT3, W_UINT3, W_MXFP4 = 0, 1, 2, 3, 4
+A_BF16, A_MXFP8 = 0, 1
+_BITS = {W_INT4: 4, W_UINT4: 4, W_INT3: 3, W_UINT3: 3, W_MXFP4: 4}
+
+
+# ----------------------------------------------------------------------------
+# dequantization
+# ----------------------------------------------------------------------------
+
+def weight_values(wtype: int, codes_packed: np.ndarray, k: int) -> np.ndarray:
+    """Decoded weight codes (before scaling) as float64 [..., N, K]."""
+    bits = _BITS[wtype]
+    c = F.unpack_bitstream(codes_packed, bits, k)
+    if wtype in (W_INT4, W_INT3):
+        return F.decode_int(c, bits)
+    if wtype in (W_UINT4, W_UINT3):
+        return F.decode_uint(c)
+    return F.decode_e2m1(c)
+
+
+def dequant_weights(wtype: int, codes_packed: np.ndarray, scales: np.ndarray,
+                    zeros: np.ndarray | None, k: int, group: int) -> np.ndarray:
+    """Wdq [..., N, K] float64.
+
+    A16 formats: (q - z) * s[n, k // group], s a bf16 pattern.  MXFP4: e2m1 *
+    2^(e - 127) with group 32.
+    """
+    v = weight_values(wtype, codes_packed, k)
+    if wtype == W_MXFP4:
+        assert group == 32
+        s = F.decode_e8m0(scales)
+    else:
+        s = F.decode_bf16(scales)
+        if zeros is not None:
+            v = v - np.repeat(np.asarray(zeros, dtype=np.float64), group, axis=-1)
+    return v * np.repeat(s, group, axis=-1)
+
+
+def dequant_activations(atype: int, x: np.ndarray, x_scales: np.ndarray | None,
+                        k: int) -> np.ndarray:
+    """Xdq [rows, K] float64: bf16 patterns, or e4m3 codes times e8m0 per-32 scales."""
+    if atype == A_BF16:
+        return F.decode_bf16(x)[..., :k]
+    v = F.decode_e4m3(np.asarray(x)[..., :k])
+    return v * np.repeat(F.decode_e8m0(x_scales), 32, axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# GEMM
+# ----------------------------------------------------------------------------
+
+def gemm(xdq: np.ndarray, wdq: np.ndarray) -> np.ndarray:
+    """Y = X @ W^T in float64 (numpy's float64 matmul)."""
+    return np.matmul(np.asarray(xdq, np.float64), np.asarray(wdq, np.float64).T)
+
+
+def gemm_exact(xdq: np.ndarray, wdq: np.ndarray) -> list:
+    """Exact rational Y = X @ W^T by brute force (tiny shapes only)."""
+    m, k = xdq.shape
+    n = wdq.shape[0]
+    xf = [[Fraction(float(xdq[i, j])) for j in range(k)] for i in range(m)]
+    wf = [[Fraction(float(wdq[i, j])) for j in range(k)] for i in range(n)]
+    return [[sum((xf[i][j] * wf[o][j] for j in range(k)), Fraction(0)) for o in range(n)]
+            for i in range(m)]
+
+
+def qg_gemm(wtype: int, codes_packed, scales, zeros, n: int, k: int, group: int,
+            atype: int, x, x_scales=None) -> np.ndarray:
+    """Dense reference: Y[M, N] float64 from standard-format inputs."""
+    wdq = dequant_weights(wtype, codes_packed, scales, zeros, k, group)
+    assert wdq.shape == (n, k)
+    xdq = dequant_activations(atype, x, x_scales, k)
+    return gemm(xdq, wdq)
+
+
+# ----------------------------------------------------------------------------
+# MoE
+# ----------------------------------------------------------------------------
+
+def moe_counts(topk_ids: np.ndarray, experts: int) -> np.ndarray:
+    """Rows routed to each expert."""
+    return np.bincount(np.asarray(topk_ids).reshape(-1), minlength=experts).astype(np.int64)
+
+
+def moe_offsets(topk_ids: np.ndarray, experts: int) -> np.ndarray:
+    """Exclusive prefix sum of the per-expert counts, length E + 1."""
+    c = moe_counts(topk_ids, experts)
+    return np.concatenate([[0], np.cumsum(c)]).astype(np.int64)
+
+
+def moe_sorted_pairs(topk_ids: np.ndarray, experts: int) -> np.ndarray:
+    """One valid expert-sorted order of the pair ids p = t*topk + j (stable)."""
+    e = np.asarray(topk_ids).reshape(-1)
+    return np.argsort(e, kind="stable").astype(np.int64)
+
+
+def moe_gemm(expert_weights, x_rows: np.ndarray, topk_ids: np.ndarray,
+             rows_by_token: bool) -> np.ndarray:
+    """Grouped reference, output rows indexed by pair id.
+
+    ``expert_weights(e)`` returns Wdq[e] (float64 [N, K]); ``x_rows`` is the
+    dequantized input: [T, K] when ``rows_by_token`` (row of pair p is token
+    p // topk) or [P, K] indexed by pair.
+    """
+    t, topk = topk_ids.shape
+    flat = np.asarray(topk_ids).reshape(-1)
+    p_total = t * topk
+    y = None
+    for e in np.unique(flat):
+        pairs = np.nonzero(flat == e)[0]
+        rows = pairs // topk if rows_by_token else pairs
+        ye = gemm(x_rows[rows], expert_weights(int(e)))
+        if y is None:
+            y = np.zeros((p_total, ye.shape[1]), dtype=np.float64)
+        y[pairs] = ye
+    return y
+
+
+# ----------------------------------------------------------------------------
+# comparison
+# ----------------------------------------------------------------------------
+
+def round_bf16(y: np.ndarray) -> np.ndarray:
+    """Round float64 to the nearest-even bf16 value (normal range), as float64."""
+    y = np.asarray(y, dtype=np.float64)
+    m, e = np.frexp(y)          # y = m * 2^e, 0.5 <= |m| < 1
+    quantum = np.ldexp(1.0, e - 8)  # 8 significant bits
+    return np.where(y == 0, 0.0, np.rint(y / quantum) * quantum)
+
+
+def normwise_error(y: np.ndarray, yref: np.ndarray) -> float:
+    """max |Y - Yref| / max |Yref| (0 when both are zero)."""
+    y = np.asarray(y, dtype=np.float64)
+    yref = np.asarray(yref, dtype=np.float64)
+    den = np.max(np.abs(yref)) if yref.size else 0.0
+    num = np.max(np.abs(y - yref)) if yref.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)
