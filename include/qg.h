@@ -1,0 +1,214 @@
+/*
+ * qg.h -- C ABI of the MI355X (gfx950) quantized GEMM library (libqg.so).
+ *
+ * The library computes Y = X * dequant(W)^T for low-bit weights with the
+ * dequantization done inside the GEMM kernels, for dense layers and for
+ * token-sorted MoE grouped layers.  The operations follow the problem
+ * statement of the Humming announcement (vLLM / Ant Group, "Announcing
+ * Humming", spke.com Japanese translation):
+ *   - section "Unified quantization representation": a weight format is
+ *     described by its bit width / number format, scale granularity, scale
+ *     type and an optional zero point; activations have their own format.
+ *   - section "Per-workload tuning and JIT compilation": preprocessing
+ *     validates parameters, pads dimensions and repacks the tensors into the
+ *     layout of the target kernel; at inference the chosen kernel runs on the
+ *     preprocessed weights and the runtime activations; configurations are
+ *     prepared per input-size (M) range and dispatched at run time.
+ *   - section "Shared CUDA components": dequantization and scaling happen
+ *     inside the kernel; dense and MoE GEMMs have their own task mapping.
+ * and the AIREITER benchmark page ("vLLM Humming performance benchmark"),
+ * sections "H100 group-32 W4A8" (MXFP4 weights x MXFP8 activations, one scale
+ * per 32) and "SM80 single-request decode" (INT3 weights, M = 1).
+ *
+ * Conventions for every entry point:
+ *   - Plain C, no exceptions cross the boundary, no abort/assert on caller
+ *     input.  Every call validates all arguments before it launches anything;
+ *     a failed validation has no side effects and returns a status.
+ *   - "device" pointers are HIP device memory on the current device, "host"
+ *     pointers are ordinary process memory.  The caller owns every buffer,
+ *     including packed weights and workspaces; the library allocates nothing
+ *     that outlives a call and has no destroy call.
+ *   - Device work is enqueued on the caller's stream and is asynchronous;
+ *     only qg_preprocess synchronizes (its stream) before returning.
+ *   - Calls are thread-safe; two calls that share a workspace must be ordered
+ *     on one stream.
+ *
+ * Standard (input) format handed to qg_preprocess, per expert:
+ *   codes  : [N][K] row-major, each row an LSB-first bitstream of b-bit codes
+ *            (code k sits in bits [b*k, b*k+b) of the row; rows are K*b/8
+ *            bytes).  INT-b codes are two's complement, UINT-b codes are plain,
+ *            e2m1 uses bit 3 as its sign.
+ *   scales : [N][K/g]: bf16 bit patterns (A16 formats) or e8m0 bytes (MXFP4).
+ *   zeros  : [N][K/g] uint8 in 0..2^b-1 for UINT-b formats, NULL otherwise.
+ * Activations: x is [rows][ldx] row-major: bf16, or e4m3 bytes (MXFP8) with
+ * x_scales [rows][K/32] e8m0 bytes (row stride K/32).  y is [rows][ldy]
+ * row-major, bf16 or fp32.
+ *
+ * Numerics (the contract the CPU oracle checks):
+ *   - A16 formats: the dequantized weight is the exact real (q - z) * s, with
+ *     q the decoded code, z the group's zero point (0 for signed formats) and
+ *     s the group's bf16 scale.  Kernels form sum_k x*(q - z) per K-group with
+ *     bf16 MFMA (codes are exact in bf16) and apply s per group in fp32.
+ *   - MXFP4 x MXFP8: e2m1 * 2^(e-127) times e4m3 * 2^(ea-127), exact operands
+ *     into gfx950 scaled MFMA.
+ *   - fp32 accumulation; QG_O_BF16 output is the fp32 result rounded to
+ *     nearest-even; QG_O_F32 exposes the fp32 accumulators.
+ */
+#ifndef QG_H_
+#define QG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+#define QG_LAYOUT_VERSION 1
+
+typedef enum {
+  QG_OK = 0,
+  QG_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad enum, negative size */
+  QG_ERR_SHAPE = 2,            /* K % group != 0, K % 32 != 0, ld too small, ... */
+  QG_ERR_ALIGNMENT = 3,        /* a device pointer or leading dimension misaligned */
+  QG_ERR_UNSUPPORTED = 4,      /* valid request with no kernel: caller may fall back */
+  QG_ERR_BUFFER_TOO_SMALL = 5, /* packed buffer or workspace below the required size */
+  QG_ERR_HIP = 6               /* a HIP call failed; see qg_last_hip_error() */
+} qg_status;
+
+typedef enum {
+  QG_W_INT4 = 0,  /* signed two's complement [-8, 7], no zero point */
+  QG_W_UINT4 = 1, /* unsigned [0, 15] with a uint4 zero point per group */
+  QG_W_INT3 = 2,  /* signed two's complement [-4, 3], no zero point */
+  QG_W_UINT3 = 3, /* unsigned [0, 7] with a zero point per group */
+  QG_W_MXFP4 = 4  /* OCP e2m1 with one e8m0 scale per 32 along K */
+} qg_wtype;
+
+typedef enum { QG_S_BF16 = 0, QG_S_E8M0 = 1 } qg_stype;
+typedef enum { QG_A_BF16 = 0, QG_A_MXFP8 = 1 } qg_atype;
+typedef enum { QG_O_BF16 = 0, QG_O_F32 = 1 } qg_otype;
+
+/* How MoE rows are addressed.  A pair p = t*topk + j is token t's j-th expert
+ * choice.  BY_TOKEN: row t of the operand (gate/up input).  BY_PAIR: row p
+ * (down input, and the usual output).  SORTED: row i of the expert-sorted
+ * order, i.e. the row of pair sorted_pair_ids[i]. */
+typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } qg_rowmode;
+
+/* Layer + compute description ("Layer Config" / "Compute Config" of the
+ * announcement's tuning section).  Supported (wtype, stype, atype, group):
+ *   INT4/UINT4/INT3/UINT3, BF16 scales, BF16 activations, group 32 or 128;
+ *   MXFP4, E8M0 scales, MXFP8 activations, group 32.
+ * Other valid combinations return QG_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t abi_version; /* must be QG_ABI_VERSION */
+  int32_t wtype;       /* qg_wtype */
+  int32_t stype;       /* qg_stype */
+  int32_t group_size;  /* K elements per scale */
+  int32_t atype;       /* qg_atype the weights will be multiplied with */
+  int32_t num_experts; /* 1 for a dense layer */
+  int64_t n;           /* output features (rows of W) */
+  int64_t k;           /* input features; must be a multiple of 32 and of group_size */
+} qg_layer_desc;
+
+/* A preprocessed weight: plain data, owned by the caller, safe to copy.
+ * Filled by qg_preprocess (or qg_weight_bind for a blob packed earlier). */
+typedef struct {
+  qg_layer_desc desc;
+  void *data;              /* device buffer holding the packed layout */
+  uint64_t bytes;          /* size of data in bytes */
+  int32_t layout_version;  /* QG_LAYOUT_VERSION */
+  int32_t n_tiles;         /* ceil(N / 16) */
+  int32_t k_blocks;        /* K / 128 rounded up */
+  int32_t groups_padded;   /* K / group rounded up to a multiple of 32 */
+  uint64_t expert_stride;  /* bytes from one expert's section to the next */
+  uint64_t scales_offset;  /* byte offset of the scales inside an expert section */
+  uint64_t zeros_offset;   /* byte offset of the zero points (0 if none) */
+} qg_weight;
+
+/* Bytes of device memory the packed layout of `desc` needs (all experts). */
+qg_status qg_packed_size(const qg_layer_desc *desc, uint64_t *bytes);
+
+/* Host-only repack of experts [expert_begin, expert_begin + expert_count) from
+ * the standard format into the packed layout.  codes/scales/zeros point at the
+ * first of those experts (host memory, standard format).  dst is a host buffer
+ * of qg_packed_size bytes laid out for all experts; only the given experts'
+ * sections are written.  Runs on the CPU; needs no GPU. */
+qg_status qg_repack_host(const qg_layer_desc *desc, const void *codes, const void *scales,
+                         const void *zeros, int32_t expert_begin, int32_t expert_count,
+                         void *dst, uint64_t dst_bytes);
+
+/* Validate, pad and repack host standard-format tensors for experts
+ * [expert_begin, expert_begin + expert_count) and copy them into the device
+ * buffer dst_dev (qg_packed_size bytes, 256-byte aligned).  Fills *out (which
+ * is valid once every expert has been preprocessed).  Synchronizes `stream`
+ * before returning. */
+qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes, const void *scales,
+                        const void *zeros, int32_t expert_begin, int32_t expert_count,
+                        void *dst_dev, uint64_t dst_bytes, hipStream_t stream, qg_weight *out);
+
+/* Describe an already packed device blob (e.g. one restored from storage that
+ * qg_repack_host produced) without touching it. */
+qg_status qg_weight_bind(const qg_layer_desc *desc, void *dst_dev, uint64_t dst_bytes,
+                         qg_weight *out);
+
+/* Workspace bytes qg_gemm needs for `m` rows (0 when none is needed). */
+qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes);
+
+/* Dense GEMM: y[m][n] = x[m][:K] * dequant(W)^T.
+ *   x        device, [m][ldx] bf16 or e4m3 bytes (per desc.atype), 16-B aligned,
+ *            ldx >= K and ldx*elem_size a multiple of 16 bytes.
+ *   x_scales device, [m][K/32] e8m0 (MXFP8 only, else ignored / may be NULL).
+ *   y        device, [m][ldy] of otype, 16-B aligned, ldy >= N.
+ *   ws       device workspace of at least qg_gemm_workspace_size bytes
+ *            (may be NULL when that size is 0).
+ * m == 0 is a no-op returning QG_OK.  Asynchronous on `stream`. */
+qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                  int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
+                  hipStream_t stream);
+
+/* Workspace bytes for qg_moe_sort + qg_moe_gemm with this many tokens. */
+qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
+                                uint64_t *bytes);
+
+/* Route-sort the pairs of a top-k router by expert (counting sort on the GPU).
+ *   topk_ids        device int32 [num_tokens][topk], values in 0..num_experts-1
+ *                   (out-of-range ids are skipped and counted nowhere).
+ *   sorted_pair_ids device int32 [num_tokens*topk]: pair ids grouped by expert;
+ *                   the order inside an expert's segment is unspecified.
+ *   expert_offsets  device int32 [num_experts+1]: segment e is
+ *                   [offsets[e], offsets[e+1]).
+ *   ws              device workspace of qg_moe_workspace_size bytes.
+ * Asynchronous on `stream`.  num_tokens == 0 writes zero offsets. */
+qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, int32_t topk,
+                      int32_t num_experts, int32_t *sorted_pair_ids, int32_t *expert_offsets,
+                      void *ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* Grouped GEMM over the sorted pairs: for every pair p routed to expert e,
+ *   y[row_y(p)] = x[row_x(p)] * dequant(W[e])^T
+ * with row_x given by x_rows (BY_TOKEN: p / topk; BY_PAIR: p; SORTED: the
+ * pair's position in sorted_pair_ids) and row_y by y_rows (BY_PAIR or SORTED).
+ * x, x_scales, y as in qg_gemm with ldx = K and ldy = N (dense rows).
+ * Asynchronous on `stream`. */
+qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, int32_t x_rows,
+                      const int32_t *sorted_pair_ids, const int32_t *expert_offsets,
+                      int64_t num_tokens, int32_t topk, void *y, int32_t otype, int32_t y_rows,
+                      void *ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* Name of the kernel variant the tuning table selects for `m` rows (dense) and
+ * the tile parameters, written as a NUL-terminated string into buf. */
+qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf, uint64_t buf_bytes);
+
+/* Static description of a status code (never NULL). */
+const char *qg_status_string(qg_status status);
+
+/* The hipError_t behind the calling thread's last QG_ERR_HIP (0 if none). */
+int32_t qg_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QG_H_ */

@@ -29,6 +29,12 @@ def unpack_bitstream(packed: np.ndarray, bits: int, count: int) -> np.ndarray:
     """
     packed = np.asarray(packed, dtype=np.uint8)
     lead = packed.shape[:-1]
+    if bits == 4:
+        # two codes per byte: even k in the low nibble, odd k in the high nibble
+        out = np.empty(lead + (2 * packed.shape[-1],), dtype=np.int64)
+        out[..., 0::2] = packed & 15
+        out[..., 1::2] = packed >> 4
+        return out[..., :count]
     flat = packed.reshape(-1, packed.shape[-1])
     out = np.zeros((flat.shape[0], count), dtype=np.int64)
     for j in range(bits):

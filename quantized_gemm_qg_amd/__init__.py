@@ -1,0 +1,211 @@
+"""Python binding of libqg (the MI355X quantized GEMM C ABI in ``include/qg.h``).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels of
+``libqg.so``.  PyTorch supplies device memory and streams; the functions take
+raw device pointers (ints) or torch tensors (their ``data_ptr()`` is passed).
+The library must be built first (``python quantized_gemm_qg_amd/build.py``);
+importing this package without it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqg.so")
+
+QG_OK, QG_ERR_INVALID_ARGUMENT, QG_ERR_SHAPE, QG_ERR_ALIGNMENT = 0, 1, 2, 3
+QG_ERR_UNSUPPORTED, QG_ERR_BUFFER_TOO_SMALL, QG_ERR_HIP = 4, 5, 6
+W_INT4, W_UINT4, W_INT3, W_UINT3, W_MXFP4 = 0, 1, 2, 3, 4
+S_BF16, S_E8M0 = 0, 1
+A_BF16, A_MXFP8 = 0, 1
+O_BF16, O_F32 = 0, 1
+ROWS_BY_TOKEN, ROWS_BY_PAIR, ROWS_SORTED = 0, 1, 2
+ABI_VERSION, LAYOUT_VERSION = 1, 1
+
+# every symbol include/qg.h declares
+EXPORTS = (
+    "qg_packed_size", "qg_repack_host", "qg_preprocess", "qg_weight_bind",
+    "qg_gemm_workspace_size", "qg_gemm", "qg_moe_workspace_size", "qg_moe_sort",
+    "qg_moe_gemm", "qg_describe_dispatch", "qg_status_string", "qg_last_hip_error",
+)
+
+
+class QGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32), ("wtype", ctypes.c_int32), ("stype", ctypes.c_int32),
+        ("group_size", ctypes.c_int32), ("atype", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+    ]
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [
+        ("desc", LayerDesc), ("data", ctypes.c_void_p), ("bytes", ctypes.c_uint64),
+        ("layout_version", ctypes.c_int32), ("n_tiles", ctypes.c_int32),
+        ("k_blocks", ctypes.c_int32), ("groups_padded", ctypes.c_int32),
+        ("expert_stride", ctypes.c_uint64), ("scales_offset", ctypes.c_uint64),
+        ("zeros_offset", ctypes.c_uint64),
+    ]
+
+
+def _load():
+    # libqg must use the same HIP runtime as the caller's device memory and
+    # streams.  torch ships its own libamdhip64 (soname libamdhip64.so.7) and
+    # asks for it by another name; loading torch first lets the dynamic linker
+    # satisfy libqg's dependency with that already-loaded runtime instead of
+    # mapping a second copy from /opt/rocm.
+    import torch  # noqa: F401
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libqg.so not found at {_LIB_PATH}; build it with `python quantized_gemm_qg_amd/build.py`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+    D, W = ctypes.POINTER(LayerDesc), ctypes.POINTER(Weight)
+    sig = {
+        "qg_packed_size": (I32, [D, ctypes.POINTER(U64)]),
+        "qg_repack_host": (I32, [D, P, P, P, I32, I32, P, U64]),
+        "qg_preprocess": (I32, [D, P, P, P, I32, I32, P, U64, P, W]),
+        "qg_weight_bind": (I32, [D, P, U64, W]),
+        "qg_gemm_workspace_size": (I32, [W, I64, ctypes.POINTER(U64)]),
+        "qg_gemm": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, P]),
+        "qg_moe_workspace_size": (I32, [W, I64, I32, ctypes.POINTER(U64)]),
+        "qg_moe_sort": (I32, [P, I64, I32, I32, P, P, P, U64, P]),
+        "qg_moe_gemm": (I32, [W, P, P, I32, P, P, I64, I32, P, I32, I32, P, U64, P]),
+        "qg_describe_dispatch": (I32, [W, I64, ctypes.c_char_p, U64]),
+        "qg_status_string": (ctypes.c_char_p, [I32]),
+        "qg_last_hip_error": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+LIB_PATH = _LIB_PATH
+
+
+def _ptr(x) -> int | None:
+    """Device/host address of a torch tensor, a numpy array, an int, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(st: int, where: str):
+    if st != QG_OK:
+        raise QGError(st, where)
+
+
+def status_string(status: int) -> str:
+    return _lib.qg_status_string(status).decode()
+
+
+def last_hip_error() -> int:
+    return _lib.qg_last_hip_error()
+
+
+def layer_desc(wtype: int, n: int, k: int, group_size: int, atype: int | None = None,
+               num_experts: int = 1, stype: int | None = None) -> LayerDesc:
+    mx = wtype == W_MXFP4
+    return LayerDesc(ABI_VERSION, wtype, S_E8M0 if stype is None and mx else (stype or S_BF16),
+                     group_size, (A_MXFP8 if mx else A_BF16) if atype is None else atype,
+                     num_experts, n, k)
+
+
+def packed_size(desc: LayerDesc) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.qg_packed_size(ctypes.byref(desc), ctypes.byref(out)), "qg_packed_size")
+    return out.value
+
+
+def repack_host(desc: LayerDesc, codes, scales, zeros, dst, expert_begin: int = 0,
+                expert_count: int | None = None) -> None:
+    if expert_count is None:
+        expert_count = desc.num_experts
+    nbytes = dst.nbytes if hasattr(dst, "nbytes") else dst.numel() * dst.element_size()
+    _check(_lib.qg_repack_host(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
+                               expert_begin, expert_count, _ptr(dst), nbytes), "qg_repack_host")
+
+
+def preprocess(desc: LayerDesc, codes, scales, zeros, dst_dev, dst_bytes: int | None = None,
+               expert_begin: int = 0, expert_count: int | None = None, stream=None) -> Weight:
+    """codes/scales/zeros: host numpy arrays in the standard format; dst_dev: a
+    device buffer (torch uint8 tensor) of packed_size(desc) bytes."""
+    if expert_count is None:
+        expert_count = desc.num_experts
+    if dst_bytes is None:
+        dst_bytes = dst_dev.numel() * dst_dev.element_size()
+    w = Weight()
+    _check(_lib.qg_preprocess(ctypes.byref(desc), _ptr(codes), _ptr(scales), _ptr(zeros),
+                              expert_begin, expert_count, _ptr(dst_dev), dst_bytes,
+                              _stream(stream), ctypes.byref(w)), "qg_preprocess")
+    return w
+
+
+def weight_bind(desc: LayerDesc, dst_dev, dst_bytes: int) -> Weight:
+    w = Weight()
+    _check(_lib.qg_weight_bind(ctypes.byref(desc), _ptr(dst_dev), dst_bytes, ctypes.byref(w)),
+           "qg_weight_bind")
+    return w
+
+
+def gemm_workspace_size(w: Weight, m: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.qg_gemm_workspace_size(ctypes.byref(w), m, ctypes.byref(out)), "qg_gemm_workspace_size")
+    return out.value
+
+
+def gemm(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, ws=None,
+         ws_bytes: int = 0, stream=None) -> None:
+    _check(_lib.qg_gemm(ctypes.byref(w), _ptr(x), _ptr(x_scales), m, ldx, _ptr(y), otype, ldy,
+                        _ptr(ws), ws_bytes, _stream(stream)), "qg_gemm")
+
+
+def moe_workspace_size(w: Weight, num_tokens: int, topk: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.qg_moe_workspace_size(ctypes.byref(w), num_tokens, topk, ctypes.byref(out)),
+           "qg_moe_workspace_size")
+    return out.value
+
+
+def moe_sort(topk_ids, num_tokens: int, topk: int, num_experts: int, sorted_pair_ids,
+             expert_offsets, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.qg_moe_sort(_ptr(topk_ids), num_tokens, topk, num_experts, _ptr(sorted_pair_ids),
+                            _ptr(expert_offsets), _ptr(ws), ws_bytes, _stream(stream)), "qg_moe_sort")
+
+
+def moe_gemm(w: Weight, x, x_scales, x_rows: int, sorted_pair_ids, expert_offsets,
+             num_tokens: int, topk: int, y, otype: int, y_rows: int, ws=None, ws_bytes: int = 0,
+             stream=None) -> None:
+    _check(_lib.qg_moe_gemm(ctypes.byref(w), _ptr(x), _ptr(x_scales), x_rows,
+                            _ptr(sorted_pair_ids), _ptr(expert_offsets), num_tokens, topk, _ptr(y),
+                            otype, y_rows, _ptr(ws), ws_bytes, _stream(stream)), "qg_moe_gemm")
+
+
+def describe_dispatch(w: Weight, m: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(_lib.qg_describe_dispatch(ctypes.byref(w), m, buf, 256), "qg_describe_dispatch")
+    return buf.value.decode()

@@ -1,0 +1,390 @@
+// The C ABI of libqg: argument validation, the tuning table keyed on the M
+// range, and dispatch to the HIP kernels on the caller's stream.
+//
+// Configuration selection follows the announcement's tuning section: a
+// configuration is prepared per input-size (M) range and picked at run time by
+// a device heuristic; here the heuristic is compiled in for one device
+// (MI355X / gfx950) and indexed by (format, M bucket, N, K).
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "qg_internal.h"
+
+namespace qg {
+
+static thread_local int32_t g_last_hip_error = 0;
+void set_last_hip_error(int32_t e) { g_last_hip_error = e; }
+
+static qg_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return QG_OK;
+  set_last_hip_error((int32_t)e);
+  return QG_ERR_HIP;
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Optional override for experiments: QG_TUNE="T,KR,W,splits".
+static bool env_variant(Variant *v) {
+  const char *s = getenv("QG_TUNE");
+  if (!s || !*s) return false;
+  int T, KR, W, S;
+  if (sscanf(s, "%d,%d,%d,%d", &T, &KR, &W, &S) != 4) return false;
+  if (T < 1 || KR < 1 || W < 1 || W > 16 || S < 1) return false;
+  v->kind = 0;
+  v->T = T;
+  v->KR = KR;
+  v->W = W;
+  v->splits = S;
+  return true;
+}
+
+// Kernel instances compiled ahead of time (see the launchers): T in {1, 2},
+// KR in {1, 2, 4, 8}, W in 1..16.  The per-lane register budget (1024-thread
+// workgroups -> 128 VGPRs) bounds KR: at most 8 K-groups per wave for the
+// integer formats (KR * 128 / group <= 8), KR <= 4 for MX, KR <= 4 when T = 2.
+static int max_kr(const qg_layer_desc &d, int T) {
+  int kr = d.wtype == QG_W_MXFP4 ? 4 : 8 * d.group_size / 128;
+  if (T == 2 && kr > 4) kr = 4;
+  return kr < 1 ? 1 : kr;
+}
+
+static int clamp_kr(int kr, int hi) {
+  kr = kr > hi ? hi : kr;
+  return kr >= 8 ? 8 : kr >= 4 ? 4 : kr >= 2 ? 2 : 1;
+}
+
+// Skinny path: each wave streams KR k-blocks of T n-tiles; a workgroup of W
+// waves covers W*KR k-blocks; `splits` workgroups cover K.  Chosen so one
+// launch has enough waves in flight to cover HBM latency (every wave issues
+// all of its 128-bit weight loads up front) while keeping the X fragments and
+// the weight slices in VGPRs.
+static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles) {
+  Variant v{0, 1, 8, 1, 1};
+  int kr = k_blocks >= 64 ? 8 : k_blocks >= 16 ? 4 : k_blocks >= 4 ? 2 : 1;
+  // small-N / long-K shapes: fewer k-blocks per wave to create more waves
+  const int64_t wgs = (int64_t)n_tiles * m_tiles;
+  if (wgs < 512 && kr > 2) kr /= 2;
+  kr = clamp_kr(kr, max_kr(d, 1));
+  int w = (k_blocks + kr - 1) / kr;
+  int splits = 1;
+  while (w > 16) {
+    ++splits;
+    w = (k_blocks + kr * splits - 1) / (kr * splits);
+  }
+  v.KR = kr;
+  v.W = w;
+  v.splits = splits;
+  return v;
+}
+
+// A variant must cover every k-block: W * KR * splits >= k_blocks.
+static bool covers(const Variant &v, int k_blocks) {
+  return (int64_t)v.W * v.KR * v.splits >= k_blocks;
+}
+
+Variant select_dense(const qg_weight &w, int64_t m) {
+  Variant v;
+  if (env_variant(&v)) {
+    v.KR = clamp_kr(v.KR, max_kr(w.desc, v.T));
+    while (!covers(v, w.k_blocks)) ++v.splits;
+    return v;
+  }
+  const int64_t m_tiles = (m + 15) / 16;
+  return skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles);
+}
+
+Variant select_moe(const qg_weight &w, int64_t pairs) {
+  Variant v;
+  if (env_variant(&v)) {
+    v.KR = clamp_kr(v.KR, max_kr(w.desc, v.T));
+    v.splits = 1;
+    return v;
+  }
+  (void)pairs;
+  Variant s = skinny_for(w.desc, w.n_tiles, w.k_blocks, 1 << 20);
+  // the grouped kernel keeps K inside one workgroup (no cross-workgroup split)
+  if (s.splits > 1) {
+    s.KR = clamp_kr(8, max_kr(w.desc, 1));
+    s.W = (w.k_blocks + s.KR - 1) / s.KR;
+    if (s.W > 16) s.W = 16;
+    s.splits = 1;
+  }
+  return s;
+}
+
+static qg_status check_weight(const qg_weight *w, Layout *L) {
+  if (!w || !w->data) return QG_ERR_INVALID_ARGUMENT;
+  qg_status st = make_layout(&w->desc, L);
+  if (st != QG_OK) return st;
+  if (w->layout_version != QG_LAYOUT_VERSION) return QG_ERR_INVALID_ARGUMENT;
+  if (w->bytes < L->total_bytes) return QG_ERR_BUFFER_TOO_SMALL;
+  if (w->n_tiles != L->n_tiles || w->k_blocks != L->k_blocks ||
+      w->groups_padded != L->groups_padded || w->expert_stride != L->expert_stride)
+    return QG_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)w->data & 255u) != 0) return QG_ERR_ALIGNMENT;
+  return QG_OK;
+}
+
+static void fill_weight(const qg_layer_desc *d, const Layout &L, void *dev, uint64_t bytes,
+                        qg_weight *out) {
+  memset(out, 0, sizeof(*out));
+  out->desc = *d;
+  out->data = dev;
+  out->bytes = bytes;
+  out->layout_version = QG_LAYOUT_VERSION;
+  out->n_tiles = L.n_tiles;
+  out->k_blocks = L.k_blocks;
+  out->groups_padded = L.groups_padded;
+  out->expert_stride = L.expert_stride;
+  out->scales_offset = L.scales_offset;
+  out->zeros_offset = L.has_zp ? L.zeros_offset : 0;
+}
+
+static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) {
+  if (v.splits <= 1 || m <= 0) return 0;
+  const int64_t m_tiles = (m + 15) / 16;
+  const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
+  const uint64_t counters = align_up((uint64_t)m_tiles * n_blocks * 4, 256);
+  const uint64_t partials = (uint64_t)v.splits * m_tiles * n_blocks * (uint64_t)v.T * 256 * 4;
+  return counters + partials;
+}
+
+static void base_args(const qg_weight &w, GemmArgs *a) {
+  memset(a, 0, sizeof(*a));
+  a->wbase = (const uint8_t *)w.data;
+  a->expert_stride = w.expert_stride;
+  a->scales_offset = w.scales_offset;
+  a->zeros_offset = w.zeros_offset;
+  a->n_tiles = w.n_tiles;
+  a->k_blocks = w.k_blocks;
+  a->groups_padded = w.groups_padded;
+  a->kb_pad = (int32_t)align_up((uint64_t)w.k_blocks, 4);
+  a->n = (int32_t)w.desc.n;
+  a->k = (int32_t)w.desc.k;
+  a->splits = 1;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" const char *qg_status_string(qg_status s) {
+  switch (s) {
+    case QG_OK: return "ok";
+    case QG_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case QG_ERR_SHAPE: return "invalid shape";
+    case QG_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case QG_ERR_UNSUPPORTED: return "unsupported combination";
+    case QG_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case QG_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+extern "C" int32_t qg_last_hip_error(void) { return g_last_hip_error; }
+
+extern "C" qg_status qg_weight_bind(const qg_layer_desc *desc, void *dst_dev, uint64_t dst_bytes,
+                                    qg_weight *out) {
+  Layout L;
+  qg_status st = make_layout(desc, &L);
+  if (st != QG_OK) return st;
+  if (!dst_dev || !out) return QG_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)dst_dev & 255u) != 0) return QG_ERR_ALIGNMENT;
+  if (dst_bytes < L.total_bytes) return QG_ERR_BUFFER_TOO_SMALL;
+  fill_weight(desc, L, dst_dev, dst_bytes, out);
+  return QG_OK;
+}
+
+extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
+                                   const void *scales, const void *zeros, int32_t expert_begin,
+                                   int32_t expert_count, void *dst_dev, uint64_t dst_bytes,
+                                   hipStream_t stream, qg_weight *out) {
+  Layout L;
+  qg_status st = make_layout(desc, &L);
+  if (st != QG_OK) return st;
+  if (!codes || !scales || !dst_dev || !out) return QG_ERR_INVALID_ARGUMENT;
+  if (L.has_zp && !zeros) return QG_ERR_INVALID_ARGUMENT;
+  if (expert_begin < 0 || expert_count <= 0 ||
+      (int64_t)expert_begin + expert_count > desc->num_experts)
+    return QG_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)dst_dev & 255u) != 0) return QG_ERR_ALIGNMENT;
+  if (dst_bytes < L.total_bytes) return QG_ERR_BUFFER_TOO_SMALL;
+  // Stage through a pinned host buffer in chunks of experts (bounded host memory).
+  const uint64_t chunk_experts =
+      std::max<uint64_t>(1, std::min<uint64_t>(expert_count, (1ull << 30) / L.expert_stride));
+  const uint64_t stage_bytes = chunk_experts * L.expert_stride;
+  void *stage = nullptr;
+  hipError_t he = hipHostMalloc(&stage, stage_bytes, hipHostMallocDefault);
+  if (he != hipSuccess) return hip_status(he);
+  uint64_t cb = (uint64_t)desc->n * desc->k * L.bits / 8;
+  uint64_t sb = (uint64_t)desc->n * (desc->k / desc->group_size) * (L.is_mx ? 1 : 2);
+  uint64_t zb = L.has_zp ? (uint64_t)desc->n * (desc->k / desc->group_size) : 0;
+  qg_status result = QG_OK;
+  for (int64_t e0 = 0; e0 < expert_count; e0 += (int64_t)chunk_experts) {
+    const int cnt = (int)std::min<int64_t>((int64_t)chunk_experts, expert_count - e0);
+    // repack into the stage as if it held experts [0, cnt)
+    qg_layer_desc d1 = *desc;
+    d1.num_experts = cnt;
+    st = qg_repack_host(&d1, (const uint8_t *)codes + e0 * cb, (const uint8_t *)scales + e0 * sb,
+                        L.has_zp ? (const uint8_t *)zeros + e0 * zb : nullptr, 0, cnt, stage,
+                        stage_bytes);
+    if (st != QG_OK) {
+      result = st;
+      break;
+    }
+    uint8_t *dst = (uint8_t *)dst_dev + (uint64_t)(expert_begin + e0) * L.expert_stride;
+    he = hipMemcpyAsync(dst, stage, (uint64_t)cnt * L.expert_stride, hipMemcpyHostToDevice, stream);
+    if (he == hipSuccess) he = hipStreamSynchronize(stream);
+    if (he != hipSuccess) {
+      result = hip_status(he);
+      break;
+    }
+  }
+  hipHostFree(stage);
+  if (result == QG_OK) fill_weight(desc, L, dst_dev, dst_bytes, out);
+  return result;
+}
+
+extern "C" qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (!bytes || m < 0) return QG_ERR_INVALID_ARGUMENT;
+  *bytes = dense_ws_bytes(*w, select_dense(*w, m), m);
+  return QG_OK;
+}
+
+extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                             int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws,
+                             uint64_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  const qg_layer_desc &d = w->desc;
+  if (d.num_experts != 1) return QG_ERR_INVALID_ARGUMENT;
+  if (m < 0 || (otype != QG_O_BF16 && otype != QG_O_F32)) return QG_ERR_INVALID_ARGUMENT;
+  if (m > (1ll << 30)) return QG_ERR_UNSUPPORTED;
+  if (m == 0) return QG_OK;
+  if (!x || !y) return QG_ERR_INVALID_ARGUMENT;
+  if (L.is_mx && !x_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (ldx < d.k || ldy < d.n) return QG_ERR_SHAPE;
+  const int xel = L.is_mx ? 1 : 2;
+  const int yel = otype == QG_O_F32 ? 4 : 2;
+  if (!aligned16(x) || !aligned16(y) || (ldx * xel) % 16 != 0 || (ldy * yel) % 4 != 0)
+    return QG_ERR_ALIGNMENT;
+  const Variant v = select_dense(*w, m);
+  const uint64_t need = dense_ws_bytes(*w, v, m);
+  if (need > 0) {
+    if (!ws) return QG_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
+    if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
+  }
+  GemmArgs a;
+  base_args(*w, &a);
+  a.x = x;
+  a.x_scales = (const uint8_t *)x_scales;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.otype = otype;
+  a.m = (int32_t)m;
+  a.splits = v.splits;
+  hipError_t he = hipSuccess;
+  if (v.splits > 1) {
+    const int64_t m_tiles = (m + 15) / 16;
+    const int64_t n_blocks = (w->n_tiles + v.T - 1) / v.T;
+    const uint64_t cnt = (uint64_t)m_tiles * n_blocks;
+    a.counters = (uint32_t *)ws;
+    a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
+    he = launch_fill_u32(a.counters, cnt, 0u, stream);
+    if (he != hipSuccess) return hip_status(he);
+  }
+  he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
+  return hip_status(he);
+}
+
+extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
+                                           uint64_t *bytes) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (!bytes || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
+  *bytes = align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256);
+  return QG_OK;
+}
+
+extern "C" qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, int32_t topk,
+                                 int32_t num_experts, int32_t *sorted_pair_ids,
+                                 int32_t *expert_offsets, void *ws, uint64_t ws_bytes,
+                                 hipStream_t stream) {
+  if (num_tokens < 0 || topk <= 0 || num_experts <= 0 || num_experts > 4096)
+    return QG_ERR_INVALID_ARGUMENT;
+  if (num_tokens * (int64_t)topk > (1ll << 30)) return QG_ERR_UNSUPPORTED;
+  if (!expert_offsets || !ws) return QG_ERR_INVALID_ARGUMENT;
+  if (num_tokens > 0 && (!topk_ids || !sorted_pair_ids)) return QG_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < align_up((uint64_t)(num_experts + 1) * 4, 256)) return QG_ERR_BUFFER_TOO_SMALL;
+  if (((uintptr_t)ws & 3u) != 0 || ((uintptr_t)expert_offsets & 3u) != 0) return QG_ERR_ALIGNMENT;
+  return hip_status(launch_moe_sort(topk_ids, num_tokens * topk, num_experts, sorted_pair_ids,
+                                    expert_offsets, (int32_t *)ws, stream));
+}
+
+extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales,
+                                 int32_t x_rows, const int32_t *sorted_pair_ids,
+                                 const int32_t *expert_offsets, int64_t num_tokens, int32_t topk,
+                                 void *y, int32_t otype, int32_t y_rows, void *ws,
+                                 uint64_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  const qg_layer_desc &d = w->desc;
+  if (num_tokens < 0 || topk <= 0 || (otype != QG_O_BF16 && otype != QG_O_F32))
+    return QG_ERR_INVALID_ARGUMENT;
+  if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  const int64_t pairs = num_tokens * topk;
+  if (pairs > (1ll << 30)) return QG_ERR_UNSUPPORTED;
+  if (pairs == 0) return QG_OK;
+  if (!x || !y || !sorted_pair_ids || !expert_offsets) return QG_ERR_INVALID_ARGUMENT;
+  if (L.is_mx && !x_scales) return QG_ERR_INVALID_ARGUMENT;
+  const int xel = L.is_mx ? 1 : 2;
+  const int yel = otype == QG_O_F32 ? 4 : 2;
+  if (!aligned16(x) || !aligned16(y) || (d.k * xel) % 16 != 0 || (d.n * yel) % 4 != 0)
+    return QG_ERR_ALIGNMENT;
+  const Variant v = select_moe(*w, pairs);
+  if (!covers(v, w->k_blocks)) return QG_ERR_UNSUPPORTED;  // K too long for one workgroup
+  GemmArgs a;
+  base_args(*w, &a);
+  a.x = x;
+  a.x_scales = (const uint8_t *)x_scales;
+  a.ldx = d.k;
+  a.y = y;
+  a.ldy = d.n;
+  a.otype = otype;
+  a.sorted_ids = sorted_pair_ids;
+  a.offsets = expert_offsets;
+  a.num_experts = d.num_experts;
+  a.topk = topk;
+  a.x_rows = x_rows;
+  a.y_rows = y_rows;
+  const int64_t max_tiles = (pairs + 15) / 16 + d.num_experts;
+  hipError_t he = L.is_mx ? launch_moe_mx(a, d, v, max_tiles, stream)
+                          : launch_moe_a16(a, d, v, max_tiles, stream);
+  return hip_status(he);
+}
+
+extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf,
+                                          uint64_t buf_bytes) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
+  const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
+  snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
+           v.KR, v.W, v.splits);
+  return QG_OK;
+}

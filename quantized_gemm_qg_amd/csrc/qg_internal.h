@@ -1,0 +1,136 @@
+// Internal declarations shared by the host side of libqg (validation, repack,
+// dispatch) and the HIP kernel launchers.  Not part of the public ABI.
+//
+// Packed layout, version 1 (one section per expert, each part 256-B aligned):
+//
+//   codes   k-blocks of 128 along K, n-tiles of 16 along N, block (t, kb) at
+//           byte ((t * k_blocks) + kb) * block_bytes.  Inside a block, lane
+//           l = 0..63 of a wave owns a contiguous slice: output column
+//           n = 16 t + (l % 16) and the K range the bf16 / f8f6f4 MFMA B
+//           operand of that lane covers (q = l / 16):
+//     * 4-bit integer (block 1024 B, 16 B per lane = 4 dwords): dword j
+//       (one 16x16x32 MFMA) holds k = 128 kb + 32 j + 8 q + e, e = 0..7, with
+//       code e in nibble slot (e / 2) + 4 (e % 2), so one shift + and/or turns
+//       slots (i, i + 4) into the bf16 pair (e = 2i, 2i + 1).
+//     * 3-bit integer (block 768 B, 12 B per lane = 3 dwords): dword j < 3
+//       holds MFMA j's eight codes in bits 0..2 of the same nibble slots; the
+//       eight codes of MFMA 3 are spread over the slots' bit 3, bit b of a code
+//       living in dword b.
+//     * Integer codes are stored offset-binary (u = c + 2^(b-1) for signed
+//       formats), so every integer format computes (u - z) with z = 2^(b-1)
+//       implied for signed formats.
+//     * e2m1 (block 1024 B, 16 B per lane): the lane's 32 codes k = 128 kb +
+//       32 q + e in standard order (two per byte, low nibble first), i.e. the
+//       16-B chunk of the standard row that one 16x16x128 scaled MFMA lane reads.
+//   scales  A16: bf16 [n_pad][groups_padded] (groups rounded up to 32);  MXFP4: e8m0 [n_pad][4][kb_pad]
+//           (byte (n, q, kb) scales k = 128 kb + 32 q .. +31), kb_pad = k_blocks
+//           rounded up to 4 so a lane reads four k-blocks' scales as one dword.
+//   zeros   UINT formats: [n_pad][groups_padded / 8] uint32, group g in nibble
+//           g % 8 of word g / 8.
+//
+// Padding (n >= N, k >= K) holds code 0 with scale 0 (A16) or scale code 0
+// (MX), so padded weights are exactly zero; kernels also zero activations
+// beyond K.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/qg.h"
+
+namespace qg {
+
+constexpr int kTileN = 16;    // N per tile
+constexpr int kBlockK = 128;  // K per block
+
+struct Layout {
+  int n_tiles = 0;
+  int k_blocks = 0;
+  int groups = 0;         // K / group
+  int groups_padded = 0;  // rounded up to 32
+  int kb_pad = 0;         // k_blocks rounded up to 4
+  int bits = 0;
+  bool has_zp = false;
+  bool is_mx = false;
+  uint64_t block_bytes = 0;
+  uint64_t codes_bytes = 0;
+  uint64_t scales_offset = 0;
+  uint64_t scales_bytes = 0;
+  uint64_t zeros_offset = 0;
+  uint64_t zeros_bytes = 0;
+  uint64_t expert_stride = 0;
+  uint64_t total_bytes = 0;
+};
+
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// Validates a descriptor; fills the layout on success.
+qg_status make_layout(const qg_layer_desc *d, Layout *out);
+
+// Host repack of one expert's standard-format tensors into its packed section.
+void repack_expert(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
+                   const uint8_t *scales, const uint8_t *zeros, uint8_t *dst);
+
+// Thread-local record of the last HIP error.
+void set_last_hip_error(int32_t e);
+
+// ---------------------------------------------------------------------------
+// kernel launch parameters
+// ---------------------------------------------------------------------------
+
+struct GemmArgs {
+  // packed weight
+  const uint8_t *wbase;
+  uint64_t expert_stride;
+  uint64_t scales_offset;
+  uint64_t zeros_offset;
+  int32_t n_tiles, k_blocks, groups_padded, kb_pad;
+  int32_t n, k;
+  // activations / output
+  const void *x;
+  const uint8_t *x_scales;
+  int64_t ldx;
+  void *y;
+  int64_t ldy;
+  int32_t otype;
+  int32_t m;  // dense rows
+  // split-K workspace (dense)
+  float *partials;
+  uint32_t *counters;
+  int32_t splits;
+  // MoE
+  const int32_t *sorted_ids;
+  const int32_t *offsets;
+  int32_t num_experts;
+  int32_t topk;
+  int32_t x_rows;
+  int32_t y_rows;
+};
+
+// One entry of the tuning table: a kernel variant and its tile parameters.
+struct Variant {
+  int kind;    // 0 = skinny (16-row tiles, weights streamed to VGPRs)
+  int T;       // n-tiles per wave
+  int KR;      // k-blocks per wave
+  int W;       // waves per workgroup (split of K inside the workgroup)
+  int splits;  // split of K across workgroups
+};
+
+Variant select_dense(const qg_weight &w, int64_t m);
+Variant select_moe(const qg_weight &w, int64_t pairs);
+
+hipError_t launch_dense_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                            hipStream_t s);
+hipError_t launch_dense_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                           hipStream_t s);
+hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                          int64_t max_tiles, hipStream_t s);
+hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                         int64_t max_tiles, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, uint64_t count, uint32_t value, hipStream_t s);
+hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,
+                           int32_t *sorted, int32_t *offsets, int32_t *ws_counts,
+                           hipStream_t s);
+
+}  // namespace qg

@@ -1,0 +1,644 @@
+// HIP kernels for gfx950 (MI355X): quantized GEMM with in-kernel
+// dequantization, dense and MoE-grouped, plus the MoE routing sort.
+//
+// The announcement's "Shared CUDA components" section splits a quantized GEMM
+// kernel into task scheduling, data movement, dequantization + scaling,
+// matrix-core compute and an output stage; the same split is used here, built
+// for CDNA4:
+//
+//   scheduling   one work item = (16-row tile, 16*T output columns, K split);
+//                dense launches one workgroup per item, the MoE launch loops a
+//                persistent grid over items derived from the expert offsets.
+//   data path    weights stream HBM -> VGPR with one 128-bit load per lane per
+//                16x128 block (the packed layout puts each lane's MFMA B
+//                operand in one contiguous 16-byte slice); activations go
+//                straight from global memory (L2) into MFMA A-operand registers
+//                and are reused for every output tile of the wave.
+//   dequant      integer codes u become bf16 (1 + u/16) (INT4) or (1 + u/8)
+//                (INT3) with one shift + and/or per pair of codes (the code
+//                lands in the top mantissa bits); the offset and zero point
+//                are removed per K-group on the MFMA partial sums:
+//                  sum x*(u - z) = MAG * sum x*(1 + u/MAG) - (MAG + z) * sum x
+//                so the group scale s applies as two fp32 FMAs per accumulator,
+//                and (u - z) * s is exact.  MXFP4 x MXFP8 needs no conversion:
+//                e2m1 codes and e8m0 scales feed the scaled MFMA directly.
+//   compute      v_mfma_f32_16x16x32_bf16, v_mfma_scale_f32_16x16x128_f8f6f4.
+//   output       workgroup waves (split along K) reduce through LDS in a fixed
+//                order; a cross-workgroup K split writes fp32 partials and the
+//                last workgroup of a tile (device-scope counter) sums them in
+//                split order, so results do not depend on arrival order.
+#include <hip/hip_runtime.h>
+
+#include "qg_internal.h"
+
+namespace qg {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+
+constexpr int kMaxWaves = 16;
+constexpr int kMaxExperts = 1024;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// register-level unpacking (layout in qg_internal.h)
+// ---------------------------------------------------------------------------
+
+// 4-bit: slots (i, i+4) -> bf16 pair 1 + u/16, code at mantissa bits 3..6.
+__device__ __forceinline__ u32x4 unpack4(uint32_t w) {
+  u32x4 r;
+  r.x = ((w << 3) & 0x00780078u) | 0x3F803F80u;
+  r.y = ((w >> 1) & 0x00780078u) | 0x3F803F80u;
+  r.z = ((w >> 5) & 0x00780078u) | 0x3F803F80u;
+  r.w = ((w >> 9) & 0x00780078u) | 0x3F803F80u;
+  return r;
+}
+
+// 3-bit codes in bits 0..2 of each nibble slot -> bf16 pair 1 + u/8.
+__device__ __forceinline__ u32x4 unpack3(uint32_t w) {
+  u32x4 r;
+  r.x = ((w << 4) & 0x00700070u) | 0x3F803F80u;
+  r.y = (w & 0x00700070u) | 0x3F803F80u;
+  r.z = ((w >> 4) & 0x00700070u) | 0x3F803F80u;
+  r.w = ((w >> 8) & 0x00700070u) | 0x3F803F80u;
+  return r;
+}
+
+// The fourth MFMA of a 3-bit lane slice: bit b of each code sits in bit 3 of
+// the nibble slot of dword b; gather them into bits 0..2.
+__device__ __forceinline__ uint32_t gather3(uint32_t d0, uint32_t d1, uint32_t d2) {
+  return ((d0 >> 3) & 0x11111111u) | ((d1 >> 2) & 0x22222222u) | ((d2 >> 1) & 0x44444444u);
+}
+
+template <int BITS>
+__device__ __forceinline__ u32x4 unpack_b(const u32x4 &w, int j) {
+  if constexpr (BITS == 4) {
+    return unpack4(w[j]);
+  } else {
+    return j < 3 ? unpack3(w[j]) : unpack3(gather3(w.x, w.y, w.z));
+  }
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ void store_out(void *y, int64_t ldy, int otype, int64_t row, int col,
+                                          float v) {
+  if (otype == QG_O_F32) {
+    ((float *)y)[row * ldy + col] = v;
+  } else {
+    __bf16 b = (__bf16)v;  // round to nearest even
+    ((__bf16 *)y)[row * ldy + col] = b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// work-item decoding shared by the dense and MoE launches
+// ---------------------------------------------------------------------------
+
+struct Item {
+  int expert;
+  int row0;    // first row of the 16-row tile (dense: row; MoE: sorted position)
+  int rows;    // valid rows in the tile (1..16)
+  int nb;      // n-block
+  int split;   // K split
+};
+
+// Exclusive prefix of per-expert 16-row tile counts, in LDS.  Returns total tiles.
+__device__ int moe_tile_prefix(const int32_t *offsets, int experts, int *prefix) {
+  const int tid = threadIdx.x, nth = blockDim.x;
+  __shared__ int part[kMaxWaves * 64 + 1];
+  const int per = (experts + nth - 1) / nth;
+  const int e0 = tid * per;
+  int local = 0;
+  for (int e = e0; e < e0 + per && e < experts; ++e) {
+    const int c = offsets[e + 1] - offsets[e];
+    local += (c + 15) >> 4;
+  }
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < nth; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    part[nth] = run;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int e = e0; e < e0 + per && e < experts; ++e) {
+    prefix[e] = run;
+    const int c = offsets[e + 1] - offsets[e];
+    run += (c + 15) >> 4;
+  }
+  if (tid == 0) prefix[experts] = part[nth];
+  __syncthreads();
+  return prefix[experts];
+}
+
+__device__ __forceinline__ Item decode_item(const GemmArgs &a, bool moe, int64_t item,
+                                            int n_blocks, int total_tiles, const int *prefix) {
+  Item it;
+  if (!moe) {
+    // dense: x = n-block fastest so neighbouring workgroups share the X tile
+    it.expert = 0;
+    it.nb = (int)(item % n_blocks);
+    const int64_t rest = item / n_blocks;
+    const int64_t m_tiles = (a.m + 15) / 16;
+    const int mt = (int)(rest % m_tiles);
+    it.split = (int)(rest / m_tiles);
+    it.row0 = mt * 16;
+    it.rows = min(16, a.m - it.row0);
+    return it;
+  }
+  // MoE: m-tile fastest so the tiles of one expert run together and share
+  // that expert's weight slice in L2.
+  const int mt = (int)(item % total_tiles);
+  it.nb = (int)(item / total_tiles);
+  it.split = 0;
+  int lo = 0, hi = a.num_experts;  // largest e with prefix[e] <= mt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= mt) lo = mid; else hi = mid;
+  }
+  it.expert = lo;
+  const int seg0 = a.offsets[lo], seg1 = a.offsets[lo + 1];
+  it.row0 = seg0 + (mt - prefix[lo]) * 16;
+  it.rows = min(16, seg1 - it.row0);
+  return it;
+}
+
+// Row of the activation operand for tile row r (or -1).
+__device__ __forceinline__ int64_t x_row_of(const GemmArgs &a, bool moe, const Item &it, int r) {
+  if (r >= it.rows) return -1;
+  const int pos = it.row0 + r;
+  if (!moe) return pos;
+  if (a.x_rows == QG_ROWS_SORTED) return pos;
+  const int p = a.sorted_ids[pos];
+  return a.x_rows == QG_ROWS_BY_TOKEN ? (int64_t)(p / a.topk) : (int64_t)p;
+}
+
+__device__ __forceinline__ int64_t y_row_of(const GemmArgs &a, bool moe, const Item &it, int r) {
+  const int pos = it.row0 + r;
+  if (!moe || a.y_rows == QG_ROWS_SORTED) return pos;
+  return a.sorted_ids[pos];
+}
+
+// ---------------------------------------------------------------------------
+// wave bodies: one wave computes acc[t] (16 rows x 16 columns of n-tile nt0+t)
+// over k-blocks [kb0, kb0 + KR) of its expert.
+// ---------------------------------------------------------------------------
+
+template <int BITS, bool ZP, int GROUP, int T, int KR>
+__device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
+                                         const uint16_t *xrow, int nt0, int kb0, f32x4 (&acc)[T]) {
+  constexpr int LB = BITS == 4 ? 16 : 12;    // packed bytes per lane per block
+  constexpr int BB = 64 * LB;                // packed bytes per block
+  constexpr int JPG = GROUP / 32;            // MFMAs per K-group
+  constexpr int GPB = 128 / GROUP;           // K-groups per block
+  constexpr float MAG = BITS == 4 ? 16.f : 8.f;
+  constexpr int ZSYM = BITS == 4 ? 8 : 4;
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int kbs = a.k_blocks, gp = a.groups_padded;
+
+  // 1. weight stream: every 128-bit load of the wave is issued up front
+  u32x4 wq[T][KR];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int kb = 0; kb < KR; ++kb) {
+      const int nt = nt0 + t, b = kb0 + kb;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (nt < a.n_tiles && b < kbs) {
+        const uint8_t *p = wexp + ((uint64_t)nt * kbs + b) * BB + lane * LB;
+        if constexpr (BITS == 4) {
+          v = __builtin_nontemporal_load((const u32x4 *)p);
+        } else {
+          const uint32_t *p32 = (const uint32_t *)p;
+          v.x = __builtin_nontemporal_load(p32);
+          v.y = __builtin_nontemporal_load(p32 + 1);
+          v.z = __builtin_nontemporal_load(p32 + 2);
+        }
+      }
+      wq[t][kb] = v;
+    }
+
+  // 2. per-group scales (bf16 pairs) and zero points (nibbles) of this lane's
+  //    column for groups g0 .. g0 + NG - 1, with vector loads; g0 is a multiple
+  //    of NG and the padded group count a multiple of 32, so no load crosses a row
+  constexpr int NG = KR * GPB;
+  constexpr int SW = (NG + 1) / 2;        // dwords of scales
+  constexpr int ZW = ZP ? (NG + 7) / 8 : 1;  // dwords of zero points
+  const int g0 = kb0 * GPB;
+  uint32_t sw[T][SW], zw[T][ZW];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int n = (nt0 + t) * 16 + r16;
+    const bool ok = nt0 + t < a.n_tiles;
+    const uint8_t *sp = wexp + a.scales_offset + ((uint64_t)n * gp + g0) * 2;
+    if constexpr (NG == 1) {
+      sw[t][0] = ok ? (uint32_t)*(const uint16_t *)sp : 0u;
+    } else if constexpr (NG == 2) {
+      sw[t][0] = ok ? *(const uint32_t *)sp : 0u;
+    } else if constexpr (NG == 4) {
+      const uint2 v = ok ? *(const uint2 *)sp : make_uint2(0u, 0u);
+      sw[t][0] = v.x; sw[t][1] = v.y;
+    } else {
+#pragma unroll
+      for (int c = 0; c < SW / 4; ++c) {
+        const u32x4 v = ok ? *(const u32x4 *)(sp + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+        sw[t][4 * c] = v.x; sw[t][4 * c + 1] = v.y; sw[t][4 * c + 2] = v.z; sw[t][4 * c + 3] = v.w;
+      }
+    }
+    if constexpr (ZP) {
+      const uint32_t *zp = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)n * (gp >> 3) + (g0 >> 3);
+#pragma unroll
+      for (int c = 0; c < ZW; ++c) zw[t][c] = ok ? zp[c] : 0u;
+    } else {
+      zw[t][0] = 0u;
+    }
+  }
+  // scale s and zero point z of group g0 + i -> (MAG * s, -(MAG + z) * s)
+  auto group_consts = [&](int t, int i, float &c1, float &c2) {
+    const float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    int z = ZSYM;
+    if constexpr (ZP) z = (int)((zw[t][i >> 3] >> (4 * ((g0 + i) & 7))) & 15u);
+    c1 = MAG * s;
+    c2 = -(MAG + (float)z) * s;
+  };
+
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  f32x4 c[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) c[t] = acc[t];
+#pragma unroll
+  for (int kb = 0; kb < KR; ++kb) {
+    // 3. activation fragments (A operand: row r16, k = 32 j + 8 q .. +7), reused
+    //    for every n-tile of the wave
+    u32x4 xf[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = (kb0 + kb) * 128 + 32 * j + 8 * q;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (xrow && k < a.k) v = *(const u32x4 *)(xrow + k);
+      xf[j] = v;
+    }
+#pragma unroll
+    for (int gi = 0; gi < GPB; ++gi) {
+      // 4. group row sums of X on the matrix core (B = all ones)
+      f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xf[j], ones, xs);
+      const int i = kb * GPB + gi;
+      // 5. dequantize + MFMA + per-group scaling
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        f32x4 g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = gi * JPG; j < (gi + 1) * JPG; ++j)
+          g = mfma_bf16(xf[j], unpack_b<BITS>(wq[t][kb], j), g);
+        float c1, c2;
+        group_consts(t, i, c1, c2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          c[t][e] = __builtin_fmaf(xs[e], c2, c[t][e]);
+          c[t][e] = __builtin_fmaf(g[e], c1, c[t][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = c[t];
+}
+
+// MXFP4 weights x MXFP8 activations: one scaled MFMA per 16x128 block.
+template <int T, int KR>
+__device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
+                                        const uint8_t *xrow, const uint8_t *xsrow, int nt0, int kb0,
+                                        f32x4 (&acc)[T]) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int kbs = a.k_blocks;
+  u32x4 wq[T][KR];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int kb = 0; kb < KR; ++kb) {
+      const int nt = nt0 + t, b = kb0 + kb;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (nt < a.n_tiles && b < kbs)
+        v = __builtin_nontemporal_load(
+            (const u32x4 *)(wexp + ((uint64_t)nt * kbs + b) * 1024 + lane * 16));
+      wq[t][kb] = v;
+    }
+  // A operand (8-bit) of v_mfma_scale_f32_16x16x128_f8f6f4: lane group q holds
+  // K 16q..16q+15 in VGPRs 0-3 and K 64+16q..64+16q+15 in VGPRs 4-7 of the
+  // 128-K step, while its scale byte names K-block q (32q..32q+31).  The 4-bit
+  // B operand holds K 32q..32q+31 contiguously, as packed.
+  i32x8 xf[KR];
+  int xsc[KR];
+#pragma unroll
+  for (int kb = 0; kb < KR; ++kb) {
+    const int k0 = (kb0 + kb) * 128;
+    i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    int sc = 127;
+    if (xrow) {
+      if (k0 + 16 * q < a.k) {
+        const u32x4 lo = *(const u32x4 *)(xrow + k0 + 16 * q);
+        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      }
+      if (k0 + 64 + 16 * q < a.k) {
+        const u32x4 hi = *(const u32x4 *)(xrow + k0 + 64 + 16 * q);
+        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+      }
+      if (k0 + 32 * q < a.k) sc = xsrow[(k0 >> 5) + q];
+    }
+    xf[kb] = v;
+    xsc[kb] = sc;
+  }
+  const uint8_t *sbase = wexp + a.scales_offset;
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int n = (nt0 + t) * 16 + r16;
+    const bool n_ok = nt0 + t < a.n_tiles;
+    f32x4 c = acc[t];
+#pragma unroll
+    for (int kb = 0; kb < KR; ++kb) {
+      const int b = kb0 + kb;
+      int wsc = 0;
+      if (n_ok && b < kbs) wsc = sbase[((uint64_t)n * 4 + q) * a.kb_pad + b];
+      const u32x4 w = wq[t][kb];
+      const i32x8 bw = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      // cbsz = 0: A is fp8 e4m3; blgp = 4: B is fp4 e2m1
+      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf[kb], bw, c, 0, 4, 0, xsc[kb], 0, wsc);
+    }
+    acc[t] = c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel: a loop over work items (one item per workgroup for dense
+// launches; a persistent grid for MoE)
+// ---------------------------------------------------------------------------
+
+template <int FMT, int GROUP, int T, int KR>
+__global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int moe,
+                                                                int64_t total_items_dense) {
+  // FMT: 0 INT4 sym, 1 INT4 + zp, 2 INT3 sym, 3 INT3 + zp, 4 MXFP4 x MXFP8
+  __shared__ float red[kMaxWaves * T * 256];
+  __shared__ int prefix[kMaxExperts + 1];
+  __shared__ int last_flag;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int n_blocks = (a.n_tiles + T - 1) / T;
+
+  int total_tiles = 0;
+  int64_t total_items = total_items_dense;
+  if (moe) {
+    total_tiles = moe_tile_prefix(a.offsets, a.num_experts, prefix);
+    total_items = (int64_t)total_tiles * n_blocks;
+  }
+
+  for (int64_t item = blockIdx.x; item < total_items; item += gridDim.x) {
+    const Item it = decode_item(a, moe != 0, item, n_blocks, total_tiles, prefix);
+    const uint8_t *wexp = a.wbase + (uint64_t)it.expert * a.expert_stride;
+    const int nt0 = it.nb * T;
+    const int kb0 = (it.split * nwaves + wave) * KR;
+    const int64_t xr = x_row_of(a, moe != 0, it, r16);
+
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = {0.f, 0.f, 0.f, 0.f};
+    if (kb0 < a.k_blocks) {
+      if constexpr (FMT == 4) {
+        const uint8_t *xrow = xr >= 0 ? (const uint8_t *)a.x + xr * a.ldx : nullptr;
+        const uint8_t *xsrow = xr >= 0 ? a.x_scales + xr * (int64_t)(a.k >> 5) : nullptr;
+        mx_wave<T, KR>(a, wexp, xrow, xsrow, nt0, kb0, acc);
+      } else {
+        const uint16_t *xrow = xr >= 0 ? (const uint16_t *)a.x + xr * a.ldx : nullptr;
+        constexpr int BITS = (FMT <= 1) ? 4 : 3;
+        constexpr bool ZP = (FMT == 1 || FMT == 3);
+        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc);
+      }
+    }
+
+    // reduce the K-split waves of the workgroup in a fixed order
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(wave * T + t) * 256 + e * 64 + lane] = acc[t][e];
+    __syncthreads();
+
+    const bool split_k = a.splits > 1;
+    for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
+      float s = 0.f;
+      for (int w = 0; w < nwaves; ++w) s += red[w * T * 256 + idx];
+      red[idx] = s;  // wave 0's slot now holds the workgroup sum (same thread reads it)
+    }
+    if (split_k) {
+      // write this split's partial tile, then the last workgroup sums the splits
+      const int64_t m_tiles = (a.m + 15) / 16;
+      const int64_t tile = (int64_t)(it.row0 / 16) * n_blocks + it.nb;
+      float *part = a.partials + ((int64_t)it.split * m_tiles * n_blocks + tile) * (T * 256);
+      for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x)
+        __hip_atomic_store(part + idx, red[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __threadfence();
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        last_flag = (prev == (uint32_t)(a.splits - 1));
+      }
+      __syncthreads();
+      if (!last_flag) continue;  // uniform across the workgroup
+      __threadfence();
+      for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
+        float s = 0.f;
+        for (int sp = 0; sp < a.splits; ++sp)
+          s += __hip_atomic_load(a.partials + ((int64_t)sp * m_tiles * n_blocks + tile) * (T * 256) + idx,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        red[idx] = s;
+      }
+    }
+    // output stage: element idx = (t, e, lane) -> row 4 (lane / 16) + e, column lane % 16
+    for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
+      const int t = idx >> 8, e = (idx >> 6) & 3, l = idx & 63;
+      const int r = 4 * (l >> 4) + e;
+      const int col = (nt0 + t) * 16 + (l & 15);
+      if (r < it.rows && col < a.n && nt0 + t < a.n_tiles)
+        store_out(a.y, a.ldy, a.otype, y_row_of(a, moe != 0, it, r), col, red[idx]);
+    }
+    __syncthreads();  // red[] and last_flag are reused by the next item
+  }
+  (void)q;
+}
+
+__global__ void fill_u32_kernel(uint32_t *p, uint64_t count, uint32_t v) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = v;
+}
+
+// Counting sort of router pairs by expert in one workgroup (LDS histogram).
+__global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t *ids, int64_t pairs,
+                                                        int32_t experts, int32_t *sorted,
+                                                        int32_t *offsets) {
+  __shared__ int cnt[kMaxExperts + 1];
+  __shared__ int cur[kMaxExperts];
+  const int tid = threadIdx.x, nth = blockDim.x;
+  for (int e = tid; e < experts; e += nth) cnt[e] = 0;
+  __syncthreads();
+  for (int64_t p = tid; p < pairs; p += nth) {
+    const int e = ids[p];
+    if (e >= 0 && e < experts) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < experts; ++e) {
+      const int c = cnt[e];
+      cnt[e] = run;
+      cur[e] = run;
+      run += c;
+    }
+    cnt[experts] = run;
+  }
+  __syncthreads();
+  for (int e = tid; e <= experts; e += nth) offsets[e] = cnt[e];
+  for (int64_t p = tid; p < pairs; p += nth) {
+    const int e = ids[p];
+    if (e >= 0 && e < experts) sorted[atomicAdd(&cur[e], 1)] = (int32_t)p;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+template <int FMT, int GROUP>
+static hipError_t launch_skinny(const GemmArgs &a, const Variant &v, bool moe, int64_t grid,
+                                int64_t items, hipStream_t s) {
+  dim3 block(64 * v.W);
+  dim3 g((unsigned)grid);
+#define QG_KR_CASE(KRV)                                                                   \
+  case KRV:                                                                               \
+    if (v.T == 2)                                                                         \
+      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 2, KRV>), g, block, 0, s, a, (int)moe, items); \
+    else                                                                                  \
+      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 1, KRV>), g, block, 0, s, a, (int)moe, items); \
+    break;
+  switch (v.KR) {
+    QG_KR_CASE(1)
+    QG_KR_CASE(2)
+    QG_KR_CASE(4)
+    QG_KR_CASE(8)
+    default: return hipErrorInvalidValue;
+  }
+#undef QG_KR_CASE
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const GemmArgs &a, int group, const Variant &v, bool moe,
+                             int64_t grid, int64_t items, hipStream_t s) {
+  if constexpr (FMT == 4) {
+    return launch_skinny<4, 32>(a, v, moe, grid, items, s);
+  } else {
+    switch (group) {
+      case 32: return launch_skinny<FMT, 32>(a, v, moe, grid, items, s);
+      case 64: return launch_skinny<FMT, 64>(a, v, moe, grid, items, s);
+      case 128: return launch_skinny<FMT, 128>(a, v, moe, grid, items, s);
+    }
+    return hipErrorInvalidValue;
+  }
+}
+
+static int fmt_of(const qg_layer_desc &d) {
+  switch (d.wtype) {
+    case QG_W_INT4: return 0;
+    case QG_W_UINT4: return 1;
+    case QG_W_INT3: return 2;
+    case QG_W_UINT3: return 3;
+    default: return 4;
+  }
+}
+
+static hipError_t launch_any(const GemmArgs &a, const qg_layer_desc &d, const Variant &v, bool moe,
+                             int64_t grid, int64_t items, hipStream_t s) {
+  if (v.W < 1 || v.W > kMaxWaves || (v.T != 1 && v.T != 2)) return hipErrorInvalidValue;
+  if (grid <= 0) return hipSuccess;
+  switch (fmt_of(d)) {
+    case 0: return launch_fmt<0>(a, d.group_size, v, moe, grid, items, s);
+    case 1: return launch_fmt<1>(a, d.group_size, v, moe, grid, items, s);
+    case 2: return launch_fmt<2>(a, d.group_size, v, moe, grid, items, s);
+    case 3: return launch_fmt<3>(a, d.group_size, v, moe, grid, items, s);
+    default: return launch_fmt<4>(a, d.group_size, v, moe, grid, items, s);
+  }
+}
+
+static hipError_t launch_dense(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                               hipStream_t s) {
+  const int64_t n_blocks = (a.n_tiles + v.T - 1) / v.T;
+  const int64_t m_tiles = (a.m + 15) / 16;
+  const int64_t items = n_blocks * m_tiles * v.splits;
+  if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+  return launch_any(a, d, v, false, items, items, s);
+}
+
+hipError_t launch_dense_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                            hipStream_t s) {
+  return launch_dense(a, d, v, s);
+}
+
+hipError_t launch_dense_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                           hipStream_t s) {
+  return launch_dense(a, d, v, s);
+}
+
+static hipError_t launch_moe(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                             int64_t max_tiles, hipStream_t s) {
+  if (a.num_experts > kMaxExperts) return hipErrorInvalidValue;
+  const int64_t n_blocks = (a.n_tiles + v.T - 1) / v.T;
+  // persistent grid: enough workgroups to fill the chip, never more than the
+  // largest possible item count
+  const int64_t cap = 256 * std::max(1, 16 / v.W) * 2;
+  const int64_t grid = std::min<int64_t>(max_tiles * n_blocks, cap);
+  return launch_any(a, d, v, true, grid, 0, s);
+}
+
+hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                          int64_t max_tiles, hipStream_t s) {
+  return launch_moe(a, d, v, max_tiles, s);
+}
+
+hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                         int64_t max_tiles, hipStream_t s) {
+  return launch_moe(a, d, v, max_tiles, s);
+}
+
+hipError_t launch_fill_u32(uint32_t *p, uint64_t count, uint32_t value, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((count + 255) / 256);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, p, count, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts, int32_t *sorted,
+                           int32_t *offsets, int32_t *ws_counts, hipStream_t s) {
+  (void)ws_counts;
+  if (experts > kMaxExperts) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(1024), 0, s, ids, pairs, experts, sorted,
+                     offsets);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -1,0 +1,226 @@
+// Validation of layer descriptors and the host repack from the standard format
+// into the packed kernel layout (the announcement's "Per-workload tuning and JIT
+// compilation" section: preprocessing validates parameters, pads dimensions and
+// repacks tensors for the target kernel).  Pure CPU code.
+#include <string.h>
+
+#include <algorithm>
+#include <thread>
+#include <vector>
+
+#include "qg_internal.h"
+
+namespace qg {
+
+static bool is_a16(int w) { return w == QG_W_INT4 || w == QG_W_UINT4 || w == QG_W_INT3 || w == QG_W_UINT3; }
+
+qg_status make_layout(const qg_layer_desc *d, Layout *out) {
+  if (!d || !out) return QG_ERR_INVALID_ARGUMENT;
+  if (d->abi_version != QG_ABI_VERSION) return QG_ERR_INVALID_ARGUMENT;
+  if (d->wtype < QG_W_INT4 || d->wtype > QG_W_MXFP4) return QG_ERR_INVALID_ARGUMENT;
+  if (d->stype < QG_S_BF16 || d->stype > QG_S_E8M0) return QG_ERR_INVALID_ARGUMENT;
+  if (d->atype < QG_A_BF16 || d->atype > QG_A_MXFP8) return QG_ERR_INVALID_ARGUMENT;
+  if (d->n <= 0 || d->k <= 0 || d->num_experts <= 0 || d->group_size <= 0) return QG_ERR_SHAPE;
+  if (d->n > (1 << 24) || d->k > (1 << 24) || d->num_experts > 4096) return QG_ERR_UNSUPPORTED;
+  if (d->k % 32 != 0 || d->k % d->group_size != 0) return QG_ERR_SHAPE;
+  Layout L;
+  if (is_a16(d->wtype)) {
+    if (d->stype != QG_S_BF16 || d->atype != QG_A_BF16) return QG_ERR_UNSUPPORTED;
+    if (d->group_size != 32 && d->group_size != 64 && d->group_size != 128) return QG_ERR_UNSUPPORTED;
+    L.bits = (d->wtype == QG_W_INT4 || d->wtype == QG_W_UINT4) ? 4 : 3;
+    L.has_zp = (d->wtype == QG_W_UINT4 || d->wtype == QG_W_UINT3);
+  } else {
+    if (d->stype != QG_S_E8M0 || d->atype != QG_A_MXFP8 || d->group_size != 32)
+      return QG_ERR_UNSUPPORTED;
+    L.bits = 4;
+    L.is_mx = true;
+  }
+  L.n_tiles = (int)((d->n + kTileN - 1) / kTileN);
+  L.k_blocks = (int)((d->k + kBlockK - 1) / kBlockK);
+  L.groups = (int)(d->k / d->group_size);
+  const int groups_in_padded_k = L.k_blocks * kBlockK / d->group_size;
+  L.groups_padded = (int)align_up((uint64_t)groups_in_padded_k, 32);
+  L.kb_pad = (int)align_up((uint64_t)L.k_blocks, 4);
+  L.block_bytes = (L.bits == 4) ? 1024 : 768;
+  const uint64_t n_pad = (uint64_t)L.n_tiles * kTileN;
+  L.codes_bytes = (uint64_t)L.n_tiles * L.k_blocks * L.block_bytes;
+  L.scales_offset = align_up(L.codes_bytes, 256);
+  L.scales_bytes = L.is_mx ? n_pad * 4 * (uint64_t)L.kb_pad : n_pad * (uint64_t)L.groups_padded * 2;
+  uint64_t end = L.scales_offset + L.scales_bytes;
+  if (L.has_zp) {
+    L.zeros_offset = align_up(end, 256);
+    L.zeros_bytes = n_pad * (uint64_t)(L.groups_padded / 8) * 4;
+    end = L.zeros_offset + L.zeros_bytes;
+  }
+  L.expert_stride = align_up(end, 256);
+  L.total_bytes = L.expert_stride * (uint64_t)d->num_experts;
+  *out = L;
+  return QG_OK;
+}
+
+// nibble slot of code e (0..7) inside a 4-bit dword: pairs (e = 2i, 2i + 1)
+// sit in slots (i, i + 4)
+static inline int slot_of(int e) { return (e >> 1) + 4 * (e & 1); }
+
+static inline uint32_t read_bits(const uint8_t *row, uint64_t bitpos, int bits) {
+  uint32_t v = 0;
+  for (int b = 0; b < bits; ++b) {
+    const uint64_t p = bitpos + b;
+    v |= (uint32_t)((row[p >> 3] >> (p & 7)) & 1u) << b;
+  }
+  return v;
+}
+
+static void repack_codes_int4(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
+                              uint8_t *dst) {
+  const uint64_t row_bytes = (uint64_t)d.k / 2;
+  const uint32_t flip = (d.wtype == QG_W_INT4) ? 0x88888888u : 0u;
+  for (int64_t n = 0; n < d.n; ++n) {
+    const uint8_t *row = codes + n * row_bytes;
+    const int t = (int)(n / kTileN), ln = (int)(n % kTileN);
+    for (int64_t k0 = 0; k0 < d.k; k0 += 8) {
+      // eight codes k0..k0+7 = four bytes of the standard row, code e in bits 4e
+      uint32_t w;
+      memcpy(&w, row + k0 / 2, 4);
+      uint32_t out = 0;
+      for (int e = 0; e < 8; ++e) out |= ((w >> (4 * e)) & 15u) << (4 * slot_of(e));
+      out ^= flip;
+      const int kb = (int)(k0 / kBlockK), kk = (int)(k0 % kBlockK);
+      const int j = kk / 32, q = (kk % 32) / 8;
+      const int lane = ln + 16 * q;
+      uint8_t *blk = dst + ((uint64_t)t * L.k_blocks + kb) * L.block_bytes;
+      memcpy(blk + lane * 16 + j * 4, &out, 4);
+    }
+  }
+}
+
+static void repack_codes_int3(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
+                              uint8_t *dst) {
+  const uint64_t row_bytes = (uint64_t)d.k * 3 / 8;
+  const uint32_t off = (d.wtype == QG_W_INT3) ? 4u : 0u;
+  for (int64_t n = 0; n < d.n; ++n) {
+    const uint8_t *row = codes + n * row_bytes;
+    const int t = (int)(n / kTileN), ln = (int)(n % kTileN);
+    for (int64_t k = 0; k < d.k; ++k) {
+      const uint32_t u = (read_bits(row, (uint64_t)k * 3, 3) ^ off) & 7u;
+      const int kb = (int)(k / kBlockK), kk = (int)(k % kBlockK);
+      const int j = kk / 32, q = (kk % 32) / 8, e = kk % 8;
+      const int lane = ln + 16 * q;
+      uint8_t *blk = dst + ((uint64_t)t * L.k_blocks + kb) * L.block_bytes + lane * 12;
+      const int s = slot_of(e);
+      if (j < 3) {
+        uint32_t w;
+        memcpy(&w, blk + 4 * j, 4);
+        w |= u << (4 * s);
+        memcpy(blk + 4 * j, &w, 4);
+      } else {
+        for (int b = 0; b < 3; ++b) {
+          uint32_t w;
+          memcpy(&w, blk + 4 * b, 4);
+          w |= ((u >> b) & 1u) << (4 * s + 3);
+          memcpy(blk + 4 * b, &w, 4);
+        }
+      }
+    }
+  }
+}
+
+static void repack_codes_mx(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
+                            uint8_t *dst) {
+  const uint64_t row_bytes = (uint64_t)d.k / 2;
+  for (int64_t n = 0; n < d.n; ++n) {
+    const uint8_t *row = codes + n * row_bytes;
+    const int t = (int)(n / kTileN), ln = (int)(n % kTileN);
+    for (int64_t k0 = 0; k0 < d.k; k0 += 32) {
+      const int kb = (int)(k0 / kBlockK), q = (int)((k0 % kBlockK) / 32);
+      const int lane = ln + 16 * q;
+      uint8_t *blk = dst + ((uint64_t)t * L.k_blocks + kb) * L.block_bytes;
+      memcpy(blk + lane * 16, row + k0 / 2, 16);
+    }
+  }
+}
+
+void repack_expert(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
+                   const uint8_t *scales, const uint8_t *zeros, uint8_t *dst) {
+  memset(dst, 0, L.expert_stride);
+  if (L.is_mx) {
+    repack_codes_mx(d, L, codes, dst);
+    const int nb32 = (int)(d.k / 32);
+    for (int64_t n = 0; n < d.n; ++n)
+      for (int i = 0; i < nb32; ++i) {
+        const int kb = i / 4, q = i % 4;
+        dst[L.scales_offset + ((uint64_t)n * 4 + q) * L.kb_pad + kb] = scales[n * nb32 + i];
+      }
+    return;
+  }
+  if (L.bits == 4)
+    repack_codes_int4(d, L, codes, dst);
+  else
+    repack_codes_int3(d, L, codes, dst);
+  const uint16_t *s16 = (const uint16_t *)scales;
+  uint16_t *ds = (uint16_t *)(dst + L.scales_offset);
+  for (int64_t n = 0; n < d.n; ++n)
+    for (int g = 0; g < L.groups; ++g) ds[n * L.groups_padded + g] = s16[n * L.groups + g];
+  if (L.has_zp) {
+    uint32_t *dz = (uint32_t *)(dst + L.zeros_offset);
+    const int words = L.groups_padded / 8;
+    for (int64_t n = 0; n < d.n; ++n)
+      for (int g = 0; g < L.groups; ++g)
+        dz[n * words + g / 8] |= (uint32_t)(zeros[n * L.groups + g] & 15u) << (4 * (g % 8));
+  }
+}
+
+// Bytes of one expert's standard-format tensors.
+static void std_sizes(const qg_layer_desc &d, const Layout &L, uint64_t *codes, uint64_t *scales,
+                      uint64_t *zeros) {
+  *codes = (uint64_t)d.n * d.k * L.bits / 8;
+  *scales = (uint64_t)d.n * (d.k / d.group_size) * (L.is_mx ? 1 : 2);
+  *zeros = L.has_zp ? (uint64_t)d.n * (d.k / d.group_size) : 0;
+}
+
+}  // namespace qg
+
+using namespace qg;
+
+extern "C" qg_status qg_packed_size(const qg_layer_desc *desc, uint64_t *bytes) {
+  if (!bytes) return QG_ERR_INVALID_ARGUMENT;
+  Layout L;
+  qg_status st = make_layout(desc, &L);
+  if (st != QG_OK) return st;
+  *bytes = L.total_bytes;
+  return QG_OK;
+}
+
+extern "C" qg_status qg_repack_host(const qg_layer_desc *desc, const void *codes,
+                                    const void *scales, const void *zeros, int32_t expert_begin,
+                                    int32_t expert_count, void *dst, uint64_t dst_bytes) {
+  Layout L;
+  qg_status st = make_layout(desc, &L);
+  if (st != QG_OK) return st;
+  if (!codes || !scales || !dst) return QG_ERR_INVALID_ARGUMENT;
+  if (L.has_zp && !zeros) return QG_ERR_INVALID_ARGUMENT;
+  if (expert_begin < 0 || expert_count < 0 ||
+      (int64_t)expert_begin + expert_count > desc->num_experts)
+    return QG_ERR_INVALID_ARGUMENT;
+  if (dst_bytes < L.total_bytes) return QG_ERR_BUFFER_TOO_SMALL;
+  uint64_t cb, sb, zb;
+  std_sizes(*desc, L, &cb, &sb, &zb);
+  const int nthreads =
+      std::max(1, std::min<int>(expert_count, (int)std::min(16u, std::thread::hardware_concurrency())));
+  auto work = [&](int tid) {
+    for (int e = tid; e < expert_count; e += nthreads) {
+      const uint8_t *c = (const uint8_t *)codes + (uint64_t)e * cb;
+      const uint8_t *s = (const uint8_t *)scales + (uint64_t)e * sb;
+      const uint8_t *z = L.has_zp ? (const uint8_t *)zeros + (uint64_t)e * zb : nullptr;
+      repack_expert(*desc, L, c, s, z, (uint8_t *)dst + (uint64_t)(expert_begin + e) * L.expert_stride);
+    }
+  };
+  if (nthreads == 1) {
+    work(0);
+  } else {
+    std::vector<std::thread> pool;
+    for (int t = 0; t < nthreads; ++t) pool.emplace_back(work, t);
+    for (auto &th : pool) th.join();
+  }
+  return QG_OK;
+}

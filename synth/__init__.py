@@ -93,6 +93,20 @@ def int_weights(r: np.random.Generator, n: int, k: int, wtype: int, group: int,
     return pack_codes(raw, bits), sc, zp, raw
 
 
+def int4_weights_packed(r: np.random.Generator, n: int, k: int, wtype: int, group: int):
+    """Large 4-bit weights drawn directly in packed form.
+
+    Uniform random bytes are exactly a stream of i.i.d. uniform 4-bit codes, so
+    this has the distribution of :func:`int_weights` without the per-code
+    packing cost.  Returns ``(codes_packed, scales_bits, zeros_or_None)``.
+    """
+    assert WTYPE_BITS[wtype] == 4 and wtype != W_MXFP4 and k % group == 0
+    codes = r.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    sc = scales_bf16(r, (n, k // group))
+    zp = r.integers(0, 16, size=(n, k // group), dtype=np.uint8) if WTYPE_HAS_ZP[wtype] else None
+    return codes, sc, zp
+
+
 def x_bf16(r: np.random.Generator, m: int, k: int, sigma: float = 1.0) -> np.ndarray:
     """bf16 bit patterns of N(0, sigma) activations, shape [m, k]."""
     return f32_to_bf16_bits(r.normal(0.0, sigma, size=(m, k)).astype(np.float32))

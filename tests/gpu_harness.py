@@ -1,0 +1,100 @@
+"""Helpers for the GPU parity tests: build seeded inputs, run libqg through its
+C ABI on cuda:0, and compute the oracle on the same inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import quantized_gemm_qg_amd as qg
+import synth
+
+TOL_BF16 = 2e-2   # normwise, bf16 outputs
+TOL_F32 = 1e-5    # normwise, fp32 accumulators
+
+
+def require_gpu():
+    import pytest
+    if not torch.cuda.is_available():
+        pytest.skip("needs an MI355X GPU")
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+class Layer:
+    """A (possibly multi-expert) quantized weight in standard format plus its
+    packed device copy."""
+
+    def __init__(self, wtype, n, k, group, seed=0, experts=1, active=None):
+        self.wtype, self.n, self.k, self.group, self.experts = wtype, n, k, group, experts
+        self.mx = wtype == qg.W_MXFP4
+        self.desc = qg.layer_desc(wtype, n, k, group, num_experts=experts)
+        self.buf = torch.empty(qg.packed_size(self.desc), dtype=torch.uint8, device="cuda")
+        self.std = {}
+        ids = range(experts) if active is None else sorted(set(int(e) for e in active))
+        self.w = None
+        for i, e in enumerate(ids):
+            if experts > 8 and i % 8 == 0:
+                print(f"    weights expert {e} ({i + 1}/{len(ids)})", flush=True)
+            r = synth.rng(seed, 1000 + e)
+            if self.mx:
+                codes, sc, _ = synth.mx_weights(r, n, k)
+                zp = None
+            elif wtype in (qg.W_INT4, qg.W_UINT4) and n * k >= (1 << 22):
+                codes, sc, zp = synth.int4_weights_packed(r, n, k, wtype, group)
+            else:
+                codes, sc, zp, _ = synth.int_weights(r, n, k, wtype, group)
+            self.std[e] = (codes, sc, zp)
+            self.w = qg.preprocess(self.desc, codes, sc, zp, self.buf, expert_begin=e, expert_count=1)
+        if self.w is None:  # no active expert: bind the (zero) buffer
+            self.w = qg.weight_bind(self.desc, self.buf, self.buf.numel())
+        self._wdq = {}
+
+    def wdq(self, e=0) -> np.ndarray:
+        if e not in self._wdq:
+            codes, sc, zp = self.std[e]
+            self._wdq[e] = oracle.dequant_weights(self.wtype, codes, sc, zp, self.k, self.group)
+        return self._wdq[e]
+
+    def drop_wdq(self):
+        self._wdq.clear()
+
+
+class Acts:
+    """Activations in the library's input format and their exact values."""
+
+    def __init__(self, mx: bool, m: int, k: int, seed=0, values=None):
+        r = synth.rng(seed, 7)
+        self.mx = mx
+        if mx:
+            if values is None:
+                self.codes, self.scales = synth.mx_activations(r, m, k)
+            else:
+                self.codes, self.scales = values
+            self.xdq = oracle.dequant_activations(oracle.A_MXFP8, self.codes, self.scales, k)
+            self.x = to_dev(self.codes)
+            self.xs = to_dev(self.scales)
+        else:
+            self.bits = synth.x_bf16(r, m, k) if values is None else values
+            self.xdq = oracle.dequant_activations(oracle.A_BF16, self.bits, None, k)
+            self.x = to_dev(self.bits)
+            self.xs = None
+
+
+def run_gemm(layer: Layer, acts: Acts, m: int, otype=qg.O_BF16) -> torch.Tensor:
+    y = torch.empty((m, layer.n), dtype=torch.float32 if otype == qg.O_F32 else torch.bfloat16,
+                    device="cuda")
+    ws_bytes = qg.gemm_workspace_size(layer.w, m)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    qg.gemm(layer.w, acts.x, acts.xs, m, layer.k, y, otype, layer.n, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return y
+
+
+def err(y: torch.Tensor, yref: np.ndarray) -> float:
+    return oracle.normwise_error(y.float().cpu().numpy().astype(np.float64), yref)

@@ -1,0 +1,272 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+* libqg.so loads and exports every entry point ``include/qg.h`` declares;
+* descriptor validation returns the documented status codes;
+* the host repack writes the packed layout its header comment describes
+  (read back here by an independent decoder of that layout);
+* argument errors in qg_gemm / qg_moe_gemm / qg_moe_sort come back as status
+  codes before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_gemm_qg_amd as qg
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "qg.h")).read()
+    declared = set(re.findall(r"^(?:qg_status|const char \*|int32_t)\s*(qg_\w+)\(", hdr, re.M))
+    assert declared == set(qg.EXPORTS)
+    lib = ctypes.CDLL(qg.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _desc(**kw):
+    base = dict(wtype=qg.W_INT4, n=256, k=512, group_size=128)
+    base.update(kw)
+    return qg.layer_desc(base.pop("wtype"), base.pop("n"), base.pop("k"), base.pop("group_size"),
+                         **base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=500), qg.QG_ERR_SHAPE),                      # K % 32
+    (dict(k=480, group_size=128), qg.QG_ERR_SHAPE),      # K % group
+    (dict(n=0), qg.QG_ERR_SHAPE),
+    (dict(group_size=256, k=512), qg.QG_ERR_UNSUPPORTED),
+    (dict(atype=qg.A_MXFP8), qg.QG_ERR_UNSUPPORTED),     # INT4 x MXFP8: no kernel
+    (dict(wtype=qg.W_MXFP4, group_size=32, atype=qg.A_BF16), qg.QG_ERR_UNSUPPORTED),
+    (dict(wtype=qg.W_MXFP4, group_size=128), qg.QG_ERR_UNSUPPORTED),
+    (dict(stype=qg.S_E8M0), qg.QG_ERR_UNSUPPORTED),
+    (dict(wtype=9), qg.QG_ERR_INVALID_ARGUMENT),
+])
+def test_descriptor_validation(kw, status):
+    with pytest.raises(qg.QGError) as e:
+        qg.packed_size(_desc(**kw))
+    assert e.value.status == status
+
+
+def test_bad_abi_version():
+    d = _desc()
+    d.abi_version = 99
+    with pytest.raises(qg.QGError) as e:
+        qg.packed_size(d)
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+
+
+def _layout(d):
+    n_tiles = -(-d.n // 16)
+    k_blocks = -(-d.k // 128)
+    gpad = -(-(k_blocks * 128 // d.group_size) // 32) * 32
+    kb_pad = -(-k_blocks // 4) * 4
+    bits = 3 if d.wtype in (qg.W_INT3, qg.W_UINT3) else 4
+    mx = d.wtype == qg.W_MXFP4
+    zp = d.wtype in (qg.W_UINT4, qg.W_UINT3)
+    bb = 1024 if bits == 4 else 768
+    codes = n_tiles * k_blocks * bb
+    al = lambda v: -(-v // 256) * 256  # noqa: E731
+    s_off = al(codes)
+    s_bytes = n_tiles * 16 * 4 * kb_pad if mx else n_tiles * 16 * gpad * 2
+    end = s_off + s_bytes
+    z_off = 0
+    if zp:
+        z_off = al(end)
+        end = z_off + n_tiles * 16 * (gpad // 8) * 4
+    return dict(n_tiles=n_tiles, k_blocks=k_blocks, gpad=gpad, kb_pad=kb_pad, bits=bits, mx=mx,
+                zp=zp, bb=bb, s_off=s_off, z_off=z_off, stride=al(end))
+
+
+def test_packed_size_formula():
+    for d in (_desc(), _desc(wtype=qg.W_UINT4, n=14336, k=4096),
+              _desc(wtype=qg.W_INT3, n=40, k=640, group_size=32),
+              _desc(wtype=qg.W_MXFP4, n=1280, k=640, group_size=32, num_experts=3)):
+        assert qg.packed_size(d) == _layout(d)["stride"] * d.num_experts
+
+
+def _slot(e):
+    return e // 2 + 4 * (e % 2)
+
+
+def _unpack_packed(d, buf):
+    """Independent reader of the packed layout -> (codes[n,k] standard values,
+    scales[n,g], zeros[n,g] or None) for expert 0."""
+    L = _layout(d)
+    n, k = d.n, d.k
+    codes = np.zeros((n, k), np.int64)
+    for nn in range(n):
+        t, ln = divmod(nn, 16)
+        for kk in range(k):
+            kb, r = divmod(kk, 128)
+            blk = (t * L["k_blocks"] + kb) * L["bb"]
+            if L["mx"]:
+                q, e = divmod(r, 32)
+                byte = buf[blk + (ln + 16 * q) * 16 + e // 2]
+                codes[nn, kk] = (byte >> (4 * (e % 2))) & 15
+                continue
+            j, rr = divmod(r, 32)
+            q, e = divmod(rr, 8)
+            lane = ln + 16 * q
+            if L["bits"] == 4:
+                w = int.from_bytes(bytes(buf[blk + lane * 16 + 4 * j: blk + lane * 16 + 4 * j + 4]), "little")
+                u = (w >> (4 * _slot(e))) & 15
+                codes[nn, kk] = u ^ 8 if d.wtype == qg.W_INT4 else u
+            else:
+                ws = [int.from_bytes(bytes(buf[blk + lane * 12 + 4 * b: blk + lane * 12 + 4 * b + 4]), "little")
+                      for b in range(3)]
+                if j < 3:
+                    u = (ws[j] >> (4 * _slot(e))) & 7
+                else:
+                    u = sum(((ws[b] >> (4 * _slot(e) + 3)) & 1) << b for b in range(3))
+                codes[nn, kk] = u ^ 4 if d.wtype == qg.W_INT3 else u
+    G = k // d.group_size
+    if L["mx"]:
+        sc = np.zeros((n, k // 32), np.int64)
+        for nn in range(n):
+            for i in range(k // 32):
+                kb, q = divmod(i, 4)
+                sc[nn, i] = buf[L["s_off"] + (nn * 4 + q) * L["kb_pad"] + kb]
+        return codes, sc, None
+    s16 = np.frombuffer(bytes(buf[L["s_off"]:L["s_off"] + d.n * L["gpad"] * 2]), np.uint16)
+    sc = s16.reshape(d.n, L["gpad"])[:, :G].astype(np.int64)
+    zp = None
+    if L["zp"]:
+        words = np.frombuffer(bytes(buf[L["z_off"]:L["z_off"] + d.n * L["gpad"] // 2]), np.uint32)
+        words = words.reshape(d.n, L["gpad"] // 8).astype(np.int64)
+        zp = np.array([[(words[nn, g // 8] >> (4 * (g % 8))) & 15 for g in range(G)]
+                       for nn in range(d.n)])
+    return codes, sc, zp
+
+
+@pytest.mark.parametrize("wtype,n,k,g", [
+    (qg.W_INT4, 40, 256, 128), (qg.W_UINT4, 33, 640, 64), (qg.W_INT3, 20, 384, 128),
+    (qg.W_UINT3, 16, 256, 32), (qg.W_MXFP4, 24, 640, 32)])
+def test_repack_roundtrip(wtype, n, k, g):
+    r = synth.rng(42, wtype)
+    d = qg.layer_desc(wtype, n, k, g)
+    if wtype == qg.W_MXFP4:
+        codes, sc, raw = synth.mx_weights(r, n, k)
+        zp = None
+    else:
+        codes, sc, zp, raw = synth.int_weights(r, n, k, wtype, g)
+    buf = np.zeros(qg.packed_size(d), np.uint8)
+    qg.repack_host(d, codes, sc, zp, buf)
+    got_c, got_s, got_z = _unpack_packed(d, buf)
+    assert np.array_equal(got_c, raw.astype(np.int64))
+    assert np.array_equal(got_s, sc.astype(np.int64))
+    if zp is not None:
+        assert np.array_equal(got_z, zp.astype(np.int64))
+    # padding beyond N is zero
+    L = _layout(d)
+    assert not buf[L["stride"]:].any()
+
+
+def test_repack_selected_experts_only():
+    r = synth.rng(1, 1)
+    d = qg.layer_desc(qg.W_INT4, 32, 256, 128, num_experts=3)
+    codes, sc, zp, raw = synth.int_weights(r, 32, 256, qg.W_INT4, 128, experts=1)
+    buf = np.zeros(qg.packed_size(d), np.uint8)
+    qg.repack_host(d, codes, sc, None, buf, expert_begin=2, expert_count=1)
+    stride = _layout(d)["stride"]
+    assert not buf[:2 * stride].any() and buf[2 * stride:].any()
+    with pytest.raises(qg.QGError) as e:
+        qg.repack_host(d, codes, sc, None, buf, expert_begin=2, expert_count=2)
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+    with pytest.raises(qg.QGError) as e:
+        qg.repack_host(d, codes, sc, None, buf[:100])
+    assert e.value.status == qg.QG_ERR_BUFFER_TOO_SMALL
+
+
+FAKE_DEV = 1 << 40  # 256-aligned address that is never dereferenced
+
+
+def _bound(desc):
+    return qg.weight_bind(desc, FAKE_DEV, qg.packed_size(desc))
+
+
+def test_gemm_argument_errors_before_launch():
+    w = _bound(qg.layer_desc(qg.W_UINT4, 256, 512, 128))
+    S = 0  # null stream: never used because validation fails first
+    # m == 0 is a no-op
+    qg.gemm(w, None, None, 0, 512, None, qg.O_BF16, 256, stream=S)
+    cases = [
+        (dict(x=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(otype=7), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(ldx=100), qg.QG_ERR_SHAPE),
+        (dict(ldy=10), qg.QG_ERR_SHAPE),
+        (dict(x=FAKE_DEV + 2), qg.QG_ERR_ALIGNMENT),
+        (dict(ldx=516), qg.QG_ERR_ALIGNMENT),
+        (dict(m=-1), qg.QG_ERR_INVALID_ARGUMENT),
+    ]
+    for kw, status in cases:
+        a = dict(x=FAKE_DEV, m=4, ldx=512, y=FAKE_DEV, otype=qg.O_BF16, ldy=256)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.gemm(w, a["x"], None, a["m"], a["ldx"], a["y"], a["otype"], a["ldy"], stream=S)
+        assert e.value.status == status, kw
+    bad = qg.Weight.from_buffer_copy(w)
+    bad.layout_version = 7
+    with pytest.raises(qg.QGError) as e:
+        qg.gemm(bad, FAKE_DEV, None, 4, 512, FAKE_DEV, qg.O_BF16, 256, stream=S)
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+    mx = _bound(qg.layer_desc(qg.W_MXFP4, 256, 512, 32))
+    with pytest.raises(qg.QGError) as e:  # MXFP8 activations need their scales
+        qg.gemm(mx, FAKE_DEV, None, 4, 512, FAKE_DEV, qg.O_BF16, 256, stream=S)
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+
+
+def test_moe_argument_errors_before_launch():
+    w = _bound(qg.layer_desc(qg.W_INT4, 256, 512, 128, num_experts=8))
+    S = 0
+    qg.moe_gemm(w, FAKE_DEV, None, qg.ROWS_BY_TOKEN, FAKE_DEV, FAKE_DEV, 0, 2, FAKE_DEV,
+                qg.O_BF16, qg.ROWS_BY_PAIR, stream=S)  # no tokens: no-op
+    with pytest.raises(qg.QGError) as e:
+        qg.moe_gemm(w, FAKE_DEV, None, qg.ROWS_BY_TOKEN, FAKE_DEV, FAKE_DEV, 4, 2, FAKE_DEV,
+                    qg.O_BF16, qg.ROWS_BY_TOKEN, stream=S)  # y by token is not a mode
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+    with pytest.raises(qg.QGError) as e:
+        qg.moe_gemm(w, FAKE_DEV, None, qg.ROWS_BY_TOKEN, None, FAKE_DEV, 4, 2, FAKE_DEV,
+                    qg.O_BF16, qg.ROWS_BY_PAIR, stream=S)
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+    assert qg.moe_workspace_size(w, 64, 8) >= 9 * 4
+    with pytest.raises(qg.QGError) as e:
+        qg.moe_sort(FAKE_DEV, 4, 2, 8, FAKE_DEV, FAKE_DEV, FAKE_DEV, 8, stream=S)
+    assert e.value.status == qg.QG_ERR_BUFFER_TOO_SMALL
+    with pytest.raises(qg.QGError) as e:
+        qg.moe_sort(FAKE_DEV, 4, 0, 8, FAKE_DEV, FAKE_DEV, FAKE_DEV, 256, stream=S)
+    assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+
+
+def test_dispatch_table_covers_k():
+    for wt, n, k, g in [(qg.W_UINT4, 14336, 4096, 128), (qg.W_UINT4, 4096, 14336, 128),
+                        (qg.W_INT3, 4096, 14336, 128), (qg.W_INT4, 256, 512, 128),
+                        (qg.W_INT4, 4096, 14336, 32), (qg.W_MXFP4, 3072, 4096, 32),
+                        (qg.W_MXFP4, 4096, 640, 32)]:
+        w = _bound(qg.layer_desc(wt, n, k, g))
+        for m in (1, 4, 16, 64, 4096):
+            s = qg.describe_dispatch(w, m)
+            T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
+            assert W * KR * S >= -(-k // 128), s
+            assert 1 <= W <= 16
+    # a split-K layout asks for a workspace
+    w = _bound(qg.layer_desc(qg.W_INT4, 4096, 14336, 32))
+    assert qg.gemm_workspace_size(w, 1) > 0
+    assert qg.gemm_workspace_size(_bound(qg.layer_desc(qg.W_UINT4, 14336, 4096, 128)), 1) == 0
+
+
+def test_binding_maps_a_single_hip_runtime():
+    """libqg must share the caller's (torch's) HIP runtime: one libamdhip64 mapped."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import quantized_gemm_qg_amd, torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "1"

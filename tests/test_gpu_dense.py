@@ -1,0 +1,155 @@
+"""GPU parity of the dense path (qg_gemm through the C ABI) against the CPU oracle.
+
+Tolerances (normwise max |Y - Yref| / max |Yref|): 2e-2 for bf16 outputs and
+1e-5 for the fp32 accumulators (QG_O_F32).  Dequantized weights are checked
+bit-exactly through one-hot activation rows.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_qg_amd as qg
+import synth
+from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, err, require_gpu, run_gemm
+
+pytestmark = pytest.mark.gpu
+
+A16 = [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_UINT3]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _check(layer, acts, m, rows=None):
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
+        y = run_gemm(layer, acts, m, otype)
+        if rows is None:
+            yref = oracle.gemm(acts.xdq, layer.wdq())
+            e = err(y, yref)
+        else:
+            yref = oracle.gemm(acts.xdq[rows], layer.wdq())
+            e = oracle.normwise_error(y[rows].float().cpu().numpy().astype(np.float64), yref)
+        print(f"  otype={otype} err={e:.3e}", flush=True)
+        assert e <= tol, (otype, e)
+        assert torch.isfinite(y.float()).all()
+
+
+def test_tiny_w4a16_config():
+    """M=16, N=256, K=512, symmetric INT4 group 128, bf16 activations."""
+    layer = Layer(qg.W_INT4, 256, 512, 128, seed=0)
+    _check(layer, Acts(False, 16, 512, seed=0), 16)
+
+
+@pytest.mark.parametrize("wtype", A16)
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_a16_formats_and_groups(wtype, group):
+    layer = Layer(wtype, 96, 768, group, seed=wtype * 10 + group)
+    for m in (1, 5, 16):
+        _check(layer, Acts(False, m, 768, seed=m), m)
+
+
+@pytest.mark.parametrize("wtype", A16 + [qg.W_MXFP4])
+def test_identity_rows_give_exact_dequantized_weights(wtype):
+    """One-hot X rows return Wdq[:, k] exactly in the fp32 output."""
+    n, k = 40, 640
+    g = 32 if wtype == qg.W_MXFP4 else 128
+    layer = Layer(wtype, n, k, g, seed=5)
+    wdq = layer.wdq()
+    ks = [0, 1, 7, 8, 31, 32, 95, 96, 127, 128, 255, 256, 383, 511, 512, 639]
+    m = len(ks)
+    if wtype == qg.W_MXFP4:
+        codes = np.zeros((m, k), np.uint8)
+        for i, kk in enumerate(ks):
+            codes[i, kk] = 0x38  # e4m3 1.0
+        acts = Acts(True, m, k, values=(codes, np.full((m, k // 32), 127, np.uint8)))
+    else:
+        bits = np.zeros((m, k), np.uint16)
+        for i, kk in enumerate(ks):
+            bits[i, kk] = 0x3F80
+        acts = Acts(False, m, k, values=bits)
+    y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
+    for i, kk in enumerate(ks):
+        assert np.array_equal(y[i].astype(np.float64), wdq[:, kk]), kk
+
+
+@pytest.mark.parametrize("m", [1, 2, 15, 17, 33, 64])
+def test_ragged_shapes(m):
+    """N not a multiple of 16, K = 640 (five 128-blocks), several row tiles."""
+    layer = Layer(qg.W_UINT4, 72, 640, 64, seed=m)
+    _check(layer, Acts(False, m, 640, seed=m), m)
+    mxl = Layer(qg.W_MXFP4, 40, 640, 32, seed=m)
+    _check(mxl, Acts(True, m, 640, seed=m), m)
+
+
+def test_split_k_path_matches(monkeypatch):
+    layer = Layer(qg.W_UINT4, 64, 4096, 128, seed=3)
+    acts = Acts(False, 16, 4096, seed=3)
+    ref = oracle.gemm(acts.xdq, layer.wdq())
+    for tune in ("1,2,4,4", "1,1,2,16", "2,2,4,4", "1,8,1,4"):
+        monkeypatch.setenv("QG_TUNE", tune)
+        assert "splits" in qg.describe_dispatch(layer.w, 16)
+        assert qg.gemm_workspace_size(layer.w, 16) > 0
+        for _ in range(2):  # counters reset between calls
+            y = run_gemm(layer, acts, 16, qg.O_F32)
+            assert err(y, ref) <= TOL_F32, tune
+
+
+def test_tuning_variants_agree(monkeypatch):
+    layer = Layer(qg.W_INT3, 64, 2048, 128, seed=4)
+    acts = Acts(False, 7, 2048, seed=4)
+    ref = oracle.gemm(acts.xdq, layer.wdq())
+    for tune in ("1,1,16,1", "1,2,8,1", "1,4,4,1", "2,4,4,1", "2,1,16,1", "1,8,2,1"):
+        monkeypatch.setenv("QG_TUNE", tune)
+        y = run_gemm(layer, acts, 7, qg.O_F32)
+        assert err(y, ref) <= TOL_F32, tune
+
+
+def test_mx_small_and_medium_m():
+    layer = Layer(qg.W_MXFP4, 1280, 4096, 32, seed=9)
+    for m in (1, 16, 100):
+        _check(layer, Acts(True, m, 4096, seed=m), m)
+
+
+def test_zero_rows_is_noop():
+    layer = Layer(qg.W_INT4, 64, 256, 128)
+    y = torch.full((1, 64), 7.0, device="cuda")
+    qg.gemm(layer.w, torch.empty(256, dtype=torch.int16, device="cuda"), None, 0, 256, y,
+            qg.O_F32, 64)
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# full-size decode shapes (dense W4A16, memory bound): every element compared
+# ---------------------------------------------------------------------------
+
+DECODE_SHAPES = [(14336, 4096), (4096, 14336)]
+
+
+@pytest.mark.parametrize("wtype", [qg.W_UINT4, qg.W_INT3])
+@pytest.mark.parametrize("nk", DECODE_SHAPES)
+def test_decode_full_size(wtype, nk):
+    n, k = nk
+    print(f"decode wtype={wtype} N={n} K={k}", flush=True)
+    layer = Layer(wtype, n, k, 128, seed=11)
+    for m in (1, 4, 16):
+        _check(layer, Acts(False, m, k, seed=20 + m), m)
+
+
+@pytest.mark.parametrize("nk", [(3072, 4096), (14336, 4096)])
+def test_w4a8_mx_full_size_sampled_rows(nk):
+    """(4096, N, 4096) MXFP4 x MXFP8: all outputs computed, 96 sampled rows
+    compared against the oracle (the oracle computes those rows only)."""
+    n, k = nk
+    m = 4096
+    print(f"mx M={m} N={n} K={k}", flush=True)
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=13)
+    acts = Acts(True, m, k, seed=13)
+    rows = np.sort(synth.rng(0, 99).choice(m, 96, replace=False))
+    rows[0], rows[-1] = 0, m - 1
+    _check(layer, acts, m, rows=rows)

@@ -1,0 +1,147 @@
+"""GPU parity of the MoE path: qg_moe_sort (routing sort) and qg_moe_gemm
+(grouped GEMM) through the C ABI, against the oracle's sort invariants and its
+per-expert dense products."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_qg_amd as qg
+import synth
+from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def sort_on_gpu(ids: np.ndarray, experts: int, layer: Layer):
+    t, topk = ids.shape
+    d_ids = to_dev(ids.astype(np.int32))
+    sorted_ids = torch.full((max(t * topk, 1),), -1, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
+    ws_bytes = qg.moe_workspace_size(layer.w, t, topk)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    qg.moe_sort(d_ids, t, topk, experts, sorted_ids, offsets, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return sorted_ids, offsets
+
+
+def check_sort(ids, experts, sorted_ids, offsets):
+    offs = offsets.cpu().numpy().astype(np.int64)
+    assert np.array_equal(offs, oracle.moe_offsets(ids, experts))
+    s = sorted_ids.cpu().numpy()[: ids.size]
+    flat = ids.reshape(-1)
+    for e in range(experts):
+        seg = s[offs[e]:offs[e + 1]]
+        assert set(seg.tolist()) == set(np.nonzero(flat == e)[0].tolist())
+
+
+def run_moe(layer, acts, sorted_ids, offsets, t, topk, x_rows, y_rows, otype):
+    p = t * topk
+    y = torch.zeros((p, layer.n), dtype=torch.float32 if otype == qg.O_F32 else torch.bfloat16,
+                    device="cuda")
+    qg.moe_gemm(layer.w, acts.x, acts.xs, x_rows, sorted_ids, offsets, t, topk, y, otype, y_rows)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+def moe_reference(layer, xdq, ids, by_token, verbose=False):
+    def wdq(e):
+        if verbose:
+            print(f"    oracle expert {e}", flush=True)
+        return layer.wdq(e)
+    return oracle.moe_gemm(wdq, xdq, ids, rows_by_token=by_token)
+
+
+@pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_MXFP4])
+def test_moe_small_all_row_modes(wtype):
+    t, e, topk, n, k = 37, 16, 4, 80, 640
+    g = 32 if wtype == qg.W_MXFP4 else 128
+    ids = synth.route(synth.rng(1, wtype), t, e, topk)
+    layer = Layer(wtype, n, k, g, seed=2, experts=e)
+    sorted_ids, offsets = sort_on_gpu(ids, e, layer)
+    check_sort(ids, e, sorted_ids, offsets)
+    mx = wtype == qg.W_MXFP4
+    # gate/up style: rows by token
+    acts = Acts(mx, t, k, seed=3)
+    ref = moe_reference(layer, acts.xdq, ids, True)
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
+        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+        assert oracle.normwise_error(y, ref) <= tol
+    # down style: rows by pair, output in sorted order
+    h = Acts(mx, t * topk, k, seed=4)
+    ref_pair = moe_reference(layer, h.xdq, ids, False)
+    y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
+    s = sorted_ids.cpu().numpy()
+    assert oracle.normwise_error(y, ref_pair[s]) <= TOL_F32
+    # sorted input rows
+    hs = Acts(mx, t * topk, k, seed=4)
+    y = run_moe(layer, hs, sorted_ids, offsets, t, topk, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, qg.O_F32)
+    # pair s[i] reads H row i
+    inv = np.empty_like(s)
+    inv[s] = np.arange(s.size)
+    ref2 = np.stack([hs.xdq[inv[p]] @ layer.wdq(int(ids.reshape(-1)[p])).T for p in range(t * topk)])
+    assert oracle.normwise_error(y, ref2) <= TOL_F32
+
+
+def test_moe_empty_and_single_row_experts():
+    e, topk, n, k = 8, 2, 48, 256
+    ids = np.array([[0, 7], [0, 7], [0, 3], [0, 7]], np.int32)  # experts 1,2,4,5,6 empty; 3 has one row
+    t = ids.shape[0]
+    layer = Layer(qg.W_UINT4, n, k, 128, seed=6, experts=e)
+    sorted_ids, offsets = sort_on_gpu(ids, e, layer)
+    check_sort(ids, e, sorted_ids, offsets)
+    acts = Acts(False, t, k, seed=7)
+    y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, qg.O_F32)
+    assert oracle.normwise_error(y, moe_reference(layer, acts.xdq, ids, True)) <= TOL_F32
+
+
+def test_moe_sort_zero_tokens_and_out_of_range_ids():
+    layer = Layer(qg.W_INT4, 32, 256, 128, experts=4)
+    ids = np.zeros((0, 2), np.int32)
+    _, offsets = sort_on_gpu(ids, 4, layer)
+    assert (offsets.cpu().numpy() == 0).all()
+    ids = np.array([[0, 9], [-1, 2]], np.int32)
+    sorted_ids, offsets = sort_on_gpu(ids, 4, layer)
+    offs = offsets.cpu().numpy()
+    assert offs.tolist() == [0, 1, 1, 2, 2]
+    assert sorted(sorted_ids.cpu().numpy()[:2].tolist()) == [0, 3]
+
+
+def _moe_full(wtype, experts, topk, n1, k1, n2, k2, tokens, seed):
+    """gate_up (rows by token) and down (rows by pair) at full expert shapes;
+    only the experts the router picks get weights (others are never read)."""
+    g = 32 if wtype == qg.W_MXFP4 else 128
+    mx = wtype == qg.W_MXFP4
+    ids = synth.route(synth.rng(seed, 1), tokens, experts, topk)
+    active = np.unique(ids)
+    print(f"moe wtype={wtype} E={experts} T={tokens} active={active.size}", flush=True)
+    up = Layer(wtype, n1, k1, g, seed=seed, experts=experts, active=active)
+    print("  gate_up weights ready", flush=True)
+    sorted_ids, offsets = sort_on_gpu(ids, experts, up)
+    check_sort(ids, experts, sorted_ids, offsets)
+    x = Acts(mx, tokens, k1, seed=seed + 1)
+    y = run_moe(up, x, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, qg.O_BF16)
+    e1 = oracle.normwise_error(y, moe_reference(up, x.xdq, ids, True, verbose=True))
+    up.drop_wdq()
+    del up
+    down = Layer(wtype, n2, k2, g, seed=seed + 7, experts=experts, active=active)
+    print("  down weights ready", flush=True)
+    h = Acts(mx, tokens * topk, k2, seed=seed + 2)
+    y = run_moe(down, h, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR, qg.O_BF16)
+    e2 = oracle.normwise_error(y, moe_reference(down, h.xdq, ids, False, verbose=True))
+    print(f"  gate_up err={e1:.3e} down err={e2:.3e}", flush=True)
+    assert e1 <= TOL_BF16 and e2 <= TOL_BF16
+
+
+def test_moe_w4a16_256_experts_t64():
+    _moe_full(qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, 64, seed=40)
+
+
+@pytest.mark.parametrize("tokens", [1, 64])
+def test_moe_w4a8_128_experts_padding_shape(tokens):
+    _moe_full(qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens, seed=50)
