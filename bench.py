@@ -83,7 +83,7 @@ def time_dense(qg, torch, wts, x, xs, m, steps, warmup, otype=None):
     otype = qg.O_BF16 if otype is None else otype
     y = torch.empty((m, wts.n), dtype=torch.bfloat16, device="cuda")
     ws_bytes = qg.gemm_workspace_size(wts.ws[0], m)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         qg.gemm(wts.ws[i % len(wts.ws)], x, xs, m, wts.k, y, otype, wts.n, ws, ws_bytes, stream)
@@ -148,7 +148,7 @@ def main():
     stream = torch.cuda.current_stream()
     ys = [torch.empty((m, L.n), dtype=torch.bfloat16, device="cuda") for L in layers]
     wsb = [qg.gemm_workspace_size(L.ws[0], m) for L in layers]
-    wsp = [torch.empty(max(b, 1), dtype=torch.uint8, device="cuda") for b in wsb]
+    wsp = [torch.zeros(max(b, 1), dtype=torch.uint8, device="cuda") for b in wsb]
     for i in range(args.warmup):
         for j, (L, (x, _, _), y) in enumerate(zip(layers, xs, ys)):
             qg.gemm(L.ws[i % ROTATE], x, None, m, L.k, y, qg.O_BF16, L.n, wsp[j], wsb[j], stream)

@@ -154,7 +154,10 @@ qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes, const void
 qg_status qg_weight_bind(const qg_layer_desc *desc, void *dst_dev, uint64_t dst_bytes,
                          qg_weight *out);
 
-/* Workspace bytes qg_gemm needs for `m` rows (0 when none is needed). */
+/* Workspace bytes qg_gemm needs for `m` rows (0 when none is needed).  A
+ * workspace must be zero-filled once before its first use (e.g. with
+ * hipMemsetAsync); every completed qg_gemm call leaves it zero-filled again, so
+ * one workspace serves any sequence of calls ordered on one stream. */
 qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes);
 
 /* Dense GEMM: y[m][n] = x[m][:K] * dequant(W)^T.
@@ -168,6 +171,7 @@ qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes)
 qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
                   int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
                   hipStream_t stream);
+/* (ws, when needed, must hold zeros on entry; see qg_gemm_workspace_size.) */
 
 /* Workspace bytes for qg_moe_sort + qg_moe_gemm with this many tokens. */
 qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
@@ -196,6 +200,16 @@ qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, i
                       const int32_t *sorted_pair_ids, const int32_t *expert_offsets,
                       int64_t num_tokens, int32_t topk, void *y, int32_t otype, int32_t y_rows,
                       void *ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* Measurement utilities, used for roofline calibration and cold-cache timing.
+ * qg_stream_read reads `bytes` (a multiple of 16; src 16-B aligned, device)
+ * with 128-bit loads and folds them into `sink` (device, at least 16 KiB, any
+ * contents); nothing else is written.  Reading a buffer larger than the 256 MB
+ * MALL evicts earlier data from the caches.  qg_stream_copy copies `bytes`
+ * (a multiple of 16, both pointers 16-B aligned, device, non-overlapping).
+ * Both are asynchronous on `stream`. */
+qg_status qg_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t stream);
+qg_status qg_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t stream);
 
 /* Name of the kernel variant the tuning table selects for `m` rows (dense) and
  * the tile parameters, written as a NUL-terminated string into buf. */

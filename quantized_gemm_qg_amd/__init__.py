@@ -26,7 +26,8 @@ ABI_VERSION, LAYOUT_VERSION = 1, 1
 EXPORTS = (
     "qg_packed_size", "qg_repack_host", "qg_preprocess", "qg_weight_bind",
     "qg_gemm_workspace_size", "qg_gemm", "qg_moe_workspace_size", "qg_moe_sort",
-    "qg_moe_gemm", "qg_describe_dispatch", "qg_status_string", "qg_last_hip_error",
+    "qg_moe_gemm", "qg_stream_read", "qg_stream_copy", "qg_describe_dispatch",
+    "qg_status_string", "qg_last_hip_error",
 )
 
 
@@ -77,6 +78,8 @@ def _load():
         "qg_moe_workspace_size": (I32, [W, I64, I32, ctypes.POINTER(U64)]),
         "qg_moe_sort": (I32, [P, I64, I32, I32, P, P, P, U64, P]),
         "qg_moe_gemm": (I32, [W, P, P, I32, P, P, I64, I32, P, I32, I32, P, U64, P]),
+        "qg_stream_read": (I32, [P, U64, P, P]),
+        "qg_stream_copy": (I32, [P, P, U64, P]),
         "qg_describe_dispatch": (I32, [W, I64, ctypes.c_char_p, U64]),
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_last_hip_error": (I32, []),
@@ -209,3 +212,11 @@ def describe_dispatch(w: Weight, m: int) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(_lib.qg_describe_dispatch(ctypes.byref(w), m, buf, 256), "qg_describe_dispatch")
     return buf.value.decode()
+
+
+def stream_read(src, nbytes: int, sink, stream=None) -> None:
+    _check(_lib.qg_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "qg_stream_read")
+
+
+def stream_copy(dst, src, nbytes: int, stream=None) -> None:
+    _check(_lib.qg_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "qg_stream_copy")

@@ -41,42 +41,54 @@ static bool env_variant(Variant *v) {
   return true;
 }
 
-// Kernel instances compiled ahead of time (see the launchers): T in {1, 2},
-// KR in {1, 2, 4, 8}, W in 1..16.  The per-lane register budget (1024-thread
-// workgroups -> 128 VGPRs) bounds KR: at most 8 K-groups per wave for the
-// integer formats (KR * 128 / group <= 8), KR <= 4 for MX, KR <= 4 when T = 2.
-static int max_kr(const qg_layer_desc &d, int T) {
-  int kr = d.wtype == QG_W_MXFP4 ? 4 : 8 * d.group_size / 128;
-  if (T == 2 && kr > 4) kr = 4;
-  return kr < 1 ? 1 : kr;
+// Kernel instances compiled ahead of time (see the launchers): T (n-tiles per
+// wave) in {1, 2, 4}, KR (k-blocks per wave) in {1, 2, 4}, W in 1..16.  Each
+// wave keeps all its activation fragments (16 VGPRs per k-block) and weight
+// slices (4 per block) in registers, and 1024-thread workgroups cap a lane at
+// 128 VGPRs, so only the spill-free (T, KR) pairs are used: T * KR <= 4 or
+// (T, KR) = (4, 2) for the integer formats, T * KR <= 8 but not (4, 4) for MX.
+static bool variant_ok(const qg_layer_desc &d, int T, int KR) {
+  if ((T != 1 && T != 2 && T != 4) || (KR != 1 && KR != 2 && KR != 4)) return false;
+  if (d.wtype == QG_W_MXFP4) return T * KR <= 8 && !(T == 4 && KR == 4);
+  return T * KR <= 4 || (T == 4 && KR == 2);
 }
 
-static int clamp_kr(int kr, int hi) {
-  kr = kr > hi ? hi : kr;
-  return kr >= 8 ? 8 : kr >= 4 ? 4 : kr >= 2 ? 2 : 1;
+static int clamp_kr(const qg_layer_desc &d, int T, int kr) {
+  for (int c = 4; c >= 1; c /= 2)
+    if (c <= kr && variant_ok(d, T, c)) return c;
+  return 1;
 }
 
-// Skinny path: each wave streams KR k-blocks of T n-tiles; a workgroup of W
-// waves covers W*KR k-blocks; `splits` workgroups cover K.  Chosen so one
-// launch has enough waves in flight to cover HBM latency (every wave issues
-// all of its 128-bit weight loads up front) while keeping the X fragments and
-// the weight slices in VGPRs.
+// Skinny path: each wave streams T n-tiles x KR k-blocks (8 KB of INT4 codes
+// at T * KR = 8), a workgroup of W waves covers W * KR k-blocks and `splits`
+// workgroups cover K.  Every load of a wave is issued before its first wait, so
+// the launch is one memory round trip per wave; the table aims for ~8 blocks
+// per wave and enough workgroups to cover all 256 CUs, and avoids a K split
+// (which costs a partials round trip and a counter-clearing launch) unless N
+// alone gives too few workgroups.
 static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles) {
-  Variant v{0, 1, 8, 1, 1};
-  int kr = k_blocks >= 64 ? 8 : k_blocks >= 16 ? 4 : k_blocks >= 4 ? 2 : 1;
-  // small-N / long-K shapes: fewer k-blocks per wave to create more waves
-  const int64_t wgs = (int64_t)n_tiles * m_tiles;
-  if (wgs < 512 && kr > 2) kr /= 2;
-  kr = clamp_kr(kr, max_kr(d, 1));
-  int w = (k_blocks + kr - 1) / kr;
+  const bool mx = d.wtype == QG_W_MXFP4;
+  // T x KR per wave: 4 x 2 (integer formats), 2 x 4 (MX); fewer for short K.
+  // Measured on the decode shapes: fewer, fuller workgroups beat more, emptier
+  // ones (224 workgroups of 8 KB waves beat 448 of 4 KB), so T shrinks only
+  // when N alone would leave more than half of the CUs idle.
+  int T = mx ? 2 : 4, KR = mx ? 4 : 2;
+  while (KR > 1 && KR > k_blocks) KR /= 2;
+  const bool long_k = (k_blocks + KR - 1) / KR > 16;  // K gets split anyway
+  while (!long_k && T > 1 && (int64_t)((n_tiles + T - 1) / T) * m_tiles < 128) T /= 2;
+  KR = clamp_kr(d, T, KR);
+  Variant v{0, T, KR, 1, 1};
+  const int64_t n_blocks = (n_tiles + T - 1) / T;
+  const int waves_k = (k_blocks + KR - 1) / KR;
   int splits = 1;
-  while (w > 16) {
+  // split K when the workgroup would exceed 16 waves, or when N alone gives
+  // fewer than 128 workgroups and each split keeps >= 4 waves
+  while (splits < waves_k &&
+         ((waves_k + splits - 1) / splits > 16 ||
+          (n_blocks * m_tiles * splits < 128 && waves_k / (splits + 1) >= 4)))
     ++splits;
-    w = (k_blocks + kr * splits - 1) / (kr * splits);
-  }
-  v.KR = kr;
-  v.W = w;
-  v.splits = splits;
+  v.W = (waves_k + splits - 1) / splits;
+  v.splits = (waves_k + v.W - 1) / v.W;
   return v;
 }
 
@@ -85,10 +97,15 @@ static bool covers(const Variant &v, int k_blocks) {
   return (int64_t)v.W * v.KR * v.splits >= k_blocks;
 }
 
+static void sanitize(const qg_layer_desc &d, Variant *v) {
+  if (!variant_ok(d, v->T, v->KR)) v->KR = clamp_kr(d, v->T, v->KR);
+  if (!variant_ok(d, v->T, v->KR)) v->T = 1;
+}
+
 Variant select_dense(const qg_weight &w, int64_t m) {
   Variant v;
   if (env_variant(&v)) {
-    v.KR = clamp_kr(v.KR, max_kr(w.desc, v.T));
+    sanitize(w.desc, &v);
     while (!covers(v, w.k_blocks)) ++v.splits;
     return v;
   }
@@ -99,17 +116,18 @@ Variant select_dense(const qg_weight &w, int64_t m) {
 Variant select_moe(const qg_weight &w, int64_t pairs) {
   Variant v;
   if (env_variant(&v)) {
-    v.KR = clamp_kr(v.KR, max_kr(w.desc, v.T));
+    sanitize(w.desc, &v);
     v.splits = 1;
     return v;
   }
-  (void)pairs;
-  Variant s = skinny_for(w.desc, w.n_tiles, w.k_blocks, 1 << 20);
   // the grouped kernel keeps K inside one workgroup (no cross-workgroup split)
+  const int64_t m_tiles = std::max<int64_t>(1, (pairs + 15) / 16);
+  Variant s = skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles);
   if (s.splits > 1) {
-    s.KR = clamp_kr(8, max_kr(w.desc, 1));
-    s.W = (w.k_blocks + s.KR - 1) / s.KR;
-    if (s.W > 16) s.W = 16;
+    // long K: the deepest spill-free wave (KR = 4), T reduced to fit
+    s.KR = 4;
+    s.T = w.desc.wtype == QG_W_MXFP4 ? 2 : 1;
+    s.W = std::min(16, (w.k_blocks + s.KR - 1) / s.KR);
     s.splits = 1;
   }
   return s;
@@ -294,13 +312,13 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   a.splits = v.splits;
   hipError_t he = hipSuccess;
   if (v.splits > 1) {
+    // counters start at zero (the caller zero-fills the workspace once) and
+    // every call leaves them at zero again
     const int64_t m_tiles = (m + 15) / 16;
     const int64_t n_blocks = (w->n_tiles + v.T - 1) / v.T;
     const uint64_t cnt = (uint64_t)m_tiles * n_blocks;
     a.counters = (uint32_t *)ws;
     a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
-    he = launch_fill_u32(a.counters, cnt, 0u, stream);
-    if (he != hipSuccess) return hip_status(he);
   }
   he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -375,6 +393,24 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   hipError_t he = L.is_mx ? launch_moe_mx(a, d, v, max_tiles, stream)
                           : launch_moe_a16(a, d, v, max_tiles, stream);
   return hip_status(he);
+}
+
+extern "C" qg_status qg_stream_read(const void *src, uint64_t bytes, void *sink,
+                                    hipStream_t stream) {
+  if (bytes == 0) return QG_OK;
+  if (!src || !sink) return QG_ERR_INVALID_ARGUMENT;
+  if (bytes % 16 != 0 || !aligned16(src) || ((uintptr_t)sink & 3u) != 0) return QG_ERR_ALIGNMENT;
+  return hip_status(launch_stream_read(src, bytes, sink, stream));
+}
+
+extern "C" qg_status qg_stream_copy(void *dst, const void *src, uint64_t bytes,
+                                    hipStream_t stream) {
+  if (bytes == 0) return QG_OK;
+  if (!src || !dst) return QG_ERR_INVALID_ARGUMENT;
+  if (bytes % 16 != 0 || !aligned16(src) || !aligned16(dst)) return QG_ERR_ALIGNMENT;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return QG_ERR_INVALID_ARGUMENT;  // overlap
+  return hip_status(launch_stream_copy(dst, src, bytes, stream));
 }
 
 extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf,

@@ -128,7 +128,8 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
                           int64_t max_tiles, hipStream_t s);
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s);
-hipError_t launch_fill_u32(uint32_t *p, uint64_t count, uint32_t value, hipStream_t s);
+hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
+hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,
                            int32_t *sorted, int32_t *offsets, int32_t *ws_counts,
                            hipStream_t s);

@@ -29,7 +29,23 @@
 //                split order, so results do not depend on arrival order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "qg_internal.h"
+
+// Weight slices are read once per launch: stream them with non-temporal loads.
+#ifndef QG_WEIGHT_NT
+#define QG_WEIGHT_NT 1
+#endif
+
+template <typename V>
+__device__ __forceinline__ V load_stream(const V *p) {
+#if QG_WEIGHT_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
 
 namespace qg {
 
@@ -209,66 +225,78 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   const int q = lane >> 4, r16 = lane & 15;
   const int kbs = a.k_blocks, gp = a.groups_padded;
 
-  // 1. weight stream: every 128-bit load of the wave is issued up front
+  // Every load of the wave is issued before the first wait, so one memory
+  // round trip covers the whole item.  Loads are unconditional: rows past the
+  // tile read a valid row (their outputs are never stored), K past the end
+  // reads k = 0 (those K-groups carry scale 0), and out-of-range n-tiles or
+  // k-blocks read a clamped block (n-tiles past N are never stored; k-blocks
+  // past K have scale 0).
+  // 1. activation fragments, A operand: row r16, k = 128 kb + 32 j + 8 q .. +7
+  u32x4 xf[KR][4];
+#pragma unroll
+  for (int kb = 0; kb < KR; ++kb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = (kb0 + kb) * 128 + 32 * j + 8 * q;
+      xf[kb][j] = *(const u32x4 *)(xrow + (k < a.k ? k : 0));
+    }
+  // 2. weight slices
   u32x4 wq[T][KR];
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
     for (int kb = 0; kb < KR; ++kb) {
-      const int nt = nt0 + t, b = kb0 + kb;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (nt < a.n_tiles && b < kbs) {
-        const uint8_t *p = wexp + ((uint64_t)nt * kbs + b) * BB + lane * LB;
-        if constexpr (BITS == 4) {
-          v = __builtin_nontemporal_load((const u32x4 *)p);
-        } else {
-          const uint32_t *p32 = (const uint32_t *)p;
-          v.x = __builtin_nontemporal_load(p32);
-          v.y = __builtin_nontemporal_load(p32 + 1);
-          v.z = __builtin_nontemporal_load(p32 + 2);
-        }
+      const int nt = min(nt0 + t, a.n_tiles - 1), b = min(kb0 + kb, kbs - 1);
+      const uint8_t *p = wexp + ((uint64_t)nt * kbs + b) * BB + lane * LB;
+      if constexpr (BITS == 4) {
+        wq[t][kb] = load_stream((const u32x4 *)p);
+      } else {
+        const uint32_t *p32 = (const uint32_t *)p;
+        wq[t][kb] = u32x4{load_stream(p32), load_stream(p32 + 1), load_stream(p32 + 2), 0u};
       }
-      wq[t][kb] = v;
     }
-
-  // 2. per-group scales (bf16 pairs) and zero points (nibbles) of this lane's
-  //    column for groups g0 .. g0 + NG - 1, with vector loads; g0 is a multiple
-  //    of NG and the padded group count a multiple of 32, so no load crosses a row
+  // 3. per-group scales (bf16 pairs) and zero points (nibbles) of this lane's
+  //    column for groups g0 .. g0 + NG - 1; g0 is a multiple of NG and the
+  //    padded group count a multiple of 32, so no vector load crosses a row
   constexpr int NG = KR * GPB;
-  constexpr int SW = (NG + 1) / 2;        // dwords of scales
+  constexpr int SW = (NG + 1) / 2;           // dwords of scales
   constexpr int ZW = ZP ? (NG + 7) / 8 : 1;  // dwords of zero points
   const int g0 = kb0 * GPB;
+  const int gl = min(g0, gp - NG);           // clamped (a wave past K reads padding)
   uint32_t sw[T][SW], zw[T][ZW];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int n = (nt0 + t) * 16 + r16;
-    const bool ok = nt0 + t < a.n_tiles;
-    const uint8_t *sp = wexp + a.scales_offset + ((uint64_t)n * gp + g0) * 2;
+    const int n = min(nt0 + t, a.n_tiles - 1) * 16 + r16;
+    const uint8_t *sp = wexp + a.scales_offset + ((uint64_t)n * gp + gl) * 2;
     if constexpr (NG == 1) {
-      sw[t][0] = ok ? (uint32_t)*(const uint16_t *)sp : 0u;
+      sw[t][0] = (uint32_t)*(const uint16_t *)sp;
     } else if constexpr (NG == 2) {
-      sw[t][0] = ok ? *(const uint32_t *)sp : 0u;
+      sw[t][0] = *(const uint32_t *)sp;
     } else if constexpr (NG == 4) {
-      const uint2 v = ok ? *(const uint2 *)sp : make_uint2(0u, 0u);
+      const uint2 v = *(const uint2 *)sp;
       sw[t][0] = v.x; sw[t][1] = v.y;
     } else {
 #pragma unroll
       for (int c = 0; c < SW / 4; ++c) {
-        const u32x4 v = ok ? *(const u32x4 *)(sp + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 v = *(const u32x4 *)(sp + 16 * c);
         sw[t][4 * c] = v.x; sw[t][4 * c + 1] = v.y; sw[t][4 * c + 2] = v.z; sw[t][4 * c + 3] = v.w;
       }
     }
     if constexpr (ZP) {
-      const uint32_t *zp = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)n * (gp >> 3) + (g0 >> 3);
+      const uint32_t *zp = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)n * (gp >> 3) + (gl >> 3);
 #pragma unroll
-      for (int c = 0; c < ZW; ++c) zw[t][c] = ok ? zp[c] : 0u;
+      for (int c = 0; c < ZW; ++c) zw[t][c] = zp[c];
     } else {
       zw[t][0] = 0u;
     }
   }
+  // keep every load above this point: the wave waits once for all of them
+  __builtin_amdgcn_sched_barrier(0);
+  const bool kvalid = kb0 < kbs;  // wave-uniform; a wave entirely past K adds nothing
   // scale s and zero point z of group g0 + i -> (MAG * s, -(MAG + z) * s)
   auto group_consts = [&](int t, int i, float &c1, float &c2) {
-    const float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    s = kvalid ? s : 0.f;
     int z = ZSYM;
     if constexpr (ZP) z = (int)((zw[t][i >> 3] >> (4 * ((g0 + i) & 7))) & 15u);
     c1 = MAG * s;
@@ -281,22 +309,12 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   for (int t = 0; t < T; ++t) c[t] = acc[t];
 #pragma unroll
   for (int kb = 0; kb < KR; ++kb) {
-    // 3. activation fragments (A operand: row r16, k = 32 j + 8 q .. +7), reused
-    //    for every n-tile of the wave
-    u32x4 xf[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = (kb0 + kb) * 128 + 32 * j + 8 * q;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (xrow && k < a.k) v = *(const u32x4 *)(xrow + k);
-      xf[j] = v;
-    }
 #pragma unroll
     for (int gi = 0; gi < GPB; ++gi) {
       // 4. group row sums of X on the matrix core (B = all ones)
       f32x4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xf[j], ones, xs);
+      for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xf[kb][j], ones, xs);
       const int i = kb * GPB + gi;
       // 5. dequantize + MFMA + per-group scaling
 #pragma unroll
@@ -304,7 +322,7 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
         f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = gi * JPG; j < (gi + 1) * JPG; ++j)
-          g = mfma_bf16(xf[j], unpack_b<BITS>(wq[t][kb], j), g);
+          g = mfma_bf16(xf[kb][j], unpack_b<BITS>(wq[t][kb], j), g);
         float c1, c2;
         group_consts(t, i, c1, c2);
 #pragma unroll
@@ -327,58 +345,59 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, r16 = lane & 15;
   const int kbs = a.k_blocks;
-  u32x4 wq[T][KR];
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-#pragma unroll
-    for (int kb = 0; kb < KR; ++kb) {
-      const int nt = nt0 + t, b = kb0 + kb;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (nt < a.n_tiles && b < kbs)
-        v = __builtin_nontemporal_load(
-            (const u32x4 *)(wexp + ((uint64_t)nt * kbs + b) * 1024 + lane * 16));
-      wq[t][kb] = v;
-    }
   // A operand (8-bit) of v_mfma_scale_f32_16x16x128_f8f6f4: lane group q holds
   // K 16q..16q+15 in VGPRs 0-3 and K 64+16q..64+16q+15 in VGPRs 4-7 of the
   // 128-K step, while its scale byte names K-block q (32q..32q+31).  The 4-bit
-  // B operand holds K 32q..32q+31 contiguously, as packed.
+  // B operand holds K 32q..32q+31 contiguously, as packed.  Loads are
+  // unconditional with clamped addresses (see a16_wave); a chunk past K reads
+  // k = 0 and is zeroed, since e8m0 has no zero scale.
   i32x8 xf[KR];
   int xsc[KR];
 #pragma unroll
   for (int kb = 0; kb < KR; ++kb) {
     const int k0 = (kb0 + kb) * 128;
-    i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    int sc = 127;
-    if (xrow) {
-      if (k0 + 16 * q < a.k) {
-        const u32x4 lo = *(const u32x4 *)(xrow + k0 + 16 * q);
-        v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-      }
-      if (k0 + 64 + 16 * q < a.k) {
-        const u32x4 hi = *(const u32x4 *)(xrow + k0 + 64 + 16 * q);
-        v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-      }
-      if (k0 + 32 * q < a.k) sc = xsrow[(k0 >> 5) + q];
-    }
-    xf[kb] = v;
+    const int klo = k0 + 16 * q, khi = k0 + 64 + 16 * q;
+    const u32x4 lo = *(const u32x4 *)(xrow + (klo < a.k ? klo : 0));
+    const u32x4 hi = *(const u32x4 *)(xrow + (khi < a.k ? khi : 0));
+    const int kb32 = (k0 >> 5) + q;
+    const int sc = xsrow[kb32 < (a.k >> 5) ? kb32 : 0];
+    const bool lo_ok = klo < a.k, hi_ok = khi < a.k;
+    xf[kb] = i32x8{(int)(lo_ok ? lo.x : 0u), (int)(lo_ok ? lo.y : 0u), (int)(lo_ok ? lo.z : 0u),
+                   (int)(lo_ok ? lo.w : 0u), (int)(hi_ok ? hi.x : 0u), (int)(hi_ok ? hi.y : 0u),
+                   (int)(hi_ok ? hi.z : 0u), (int)(hi_ok ? hi.w : 0u)};
     xsc[kb] = sc;
   }
+  u32x4 wq[T][KR];
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int kb = 0; kb < KR; ++kb) {
+      const int nt = min(nt0 + t, a.n_tiles - 1), b = min(kb0 + kb, kbs - 1);
+      wq[t][kb] = load_stream((const u32x4 *)(wexp + ((uint64_t)nt * kbs + b) * 1024 + lane * 16));
+    }
   const uint8_t *sbase = wexp + a.scales_offset;
+  int wsc[T][KR];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
-    const int n = (nt0 + t) * 16 + r16;
-    const bool n_ok = nt0 + t < a.n_tiles;
+    const int n = min(nt0 + t, a.n_tiles - 1) * 16 + r16;
+#pragma unroll
+    for (int kb = 0; kb < KR; ++kb)
+      wsc[t][kb] = sbase[((uint64_t)n * 4 + q) * a.kb_pad + min(kb0 + kb, kbs - 1)];
+  }
+  // keep every load above this point: the wave waits once for all of them
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
     f32x4 c = acc[t];
 #pragma unroll
     for (int kb = 0; kb < KR; ++kb) {
-      const int b = kb0 + kb;
-      int wsc = 0;
-      if (n_ok && b < kbs) wsc = sbase[((uint64_t)n * 4 + q) * a.kb_pad + b];
+      const bool ok = kb0 + kb < kbs;  // wave-uniform
       const u32x4 w = wq[t][kb];
-      const i32x8 bw = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+      const i32x8 bw = {(int)(ok ? w.x : 0u), (int)(ok ? w.y : 0u), (int)(ok ? w.z : 0u),
+                        (int)(ok ? w.w : 0u), 0, 0, 0, 0};
       // cbsz = 0: A is fp8 e4m3; blgp = 4: B is fp4 e2m1
-      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf[kb], bw, c, 0, 4, 0, xsc[kb], 0, wsc);
+      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(xf[kb], bw, c, 0, 4, 0, xsc[kb], 0,
+                                                            wsc[t][kb]);
     }
     acc[t] = c;
   }
@@ -393,13 +412,13 @@ template <int FMT, int GROUP, int T, int KR>
 __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int moe,
                                                                 int64_t total_items_dense) {
   // FMT: 0 INT4 sym, 1 INT4 + zp, 2 INT3 sym, 3 INT3 + zp, 4 MXFP4 x MXFP8
-  __shared__ float red[kMaxWaves * T * 256];
+  extern __shared__ float red[];  // [waves][T][256]: sized by the launcher
   __shared__ int prefix[kMaxExperts + 1];
   __shared__ int last_flag;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
-  const int q = lane >> 4, r16 = lane & 15;
+  const int r16 = lane & 15;
   const int n_blocks = (a.n_tiles + T - 1) / T;
 
   int total_tiles = 0;
@@ -414,18 +433,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
     const uint8_t *wexp = a.wbase + (uint64_t)it.expert * a.expert_stride;
     const int nt0 = it.nb * T;
     const int kb0 = (it.split * nwaves + wave) * KR;
-    const int64_t xr = x_row_of(a, moe != 0, it, r16);
+    // rows past the tile read the tile's first row: their outputs are never stored
+    const int64_t xr = x_row_of(a, moe != 0, it, r16 < it.rows ? r16 : 0);
 
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = {0.f, 0.f, 0.f, 0.f};
     if (kb0 < a.k_blocks) {
       if constexpr (FMT == 4) {
-        const uint8_t *xrow = xr >= 0 ? (const uint8_t *)a.x + xr * a.ldx : nullptr;
-        const uint8_t *xsrow = xr >= 0 ? a.x_scales + xr * (int64_t)(a.k >> 5) : nullptr;
+        const uint8_t *xrow = (const uint8_t *)a.x + xr * a.ldx;
+        const uint8_t *xsrow = a.x_scales + xr * (int64_t)(a.k >> 5);
         mx_wave<T, KR>(a, wexp, xrow, xsrow, nt0, kb0, acc);
       } else {
-        const uint16_t *xrow = xr >= 0 ? (const uint16_t *)a.x + xr * a.ldx : nullptr;
+        const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
         constexpr int BITS = (FMT <= 1) ? 4 : 3;
         constexpr bool ZP = (FMT == 1 || FMT == 3);
         a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc);
@@ -446,29 +466,38 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
       red[idx] = s;  // wave 0's slot now holds the workgroup sum (same thread reads it)
     }
     if (split_k) {
-      // write this split's partial tile, then the last workgroup sums the splits
+      // Write this split's partial tile (valid rows only), then the last
+      // workgroup of the tile sums the splits in split order and resets the
+      // tile's counter to zero for the next call.  Partials move with
+      // agent-scope atomic stores/loads (write-through, coherent across the
+      // XCD L2s), so no L2 write-back or invalidate fence is needed: the stores
+      // are complete (vmcnt = 0) before the counter add that publishes them,
+      // and the last workgroup's loads are issued after that add returns.
       const int64_t m_tiles = (a.m + 15) / 16;
       const int64_t tile = (int64_t)(it.row0 / 16) * n_blocks + it.nb;
       float *part = a.partials + ((int64_t)it.split * m_tiles * n_blocks + tile) * (T * 256);
       for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x)
-        __hip_atomic_store(part + idx, red[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
+        if (4 * ((idx & 63) >> 4) + ((idx >> 6) & 3) < it.rows)
+          __hip_atomic_store(part + idx, red[idx], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_ACQ_REL,
+        const uint32_t prev = __hip_atomic_fetch_add(a.counters + tile, 1u, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
         last_flag = (prev == (uint32_t)(a.splits - 1));
       }
       __syncthreads();
       if (!last_flag) continue;  // uniform across the workgroup
-      __threadfence();
       for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
         float s = 0.f;
-        for (int sp = 0; sp < a.splits; ++sp)
-          s += __hip_atomic_load(a.partials + ((int64_t)sp * m_tiles * n_blocks + tile) * (T * 256) + idx,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (4 * ((idx & 63) >> 4) + ((idx >> 6) & 3) < it.rows)
+          for (int sp = 0; sp < a.splits; ++sp)
+            s += __hip_atomic_load(a.partials + ((int64_t)sp * m_tiles * n_blocks + tile) * (T * 256) + idx,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         red[idx] = s;
       }
+      if (threadIdx.x == 0)
+        __hip_atomic_store(a.counters + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // output stage: element idx = (t, e, lane) -> row 4 (lane / 16) + e, column lane % 16
     for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
@@ -480,12 +509,53 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
     }
     __syncthreads();  // red[] and last_flag are reused by the next item
   }
-  (void)q;
 }
 
-__global__ void fill_u32_kernel(uint32_t *p, uint64_t count, uint32_t v) {
-  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = v;
+// Plain streaming kernels (measurement utilities): grid-stride 128-bit loads,
+// four in flight per lane.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *src, uint64_t n16,
+                                                          uint32_t *sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[(blockIdx.x * blockDim.x + threadIdx.x) & 4095] = acc;  // keeps the loads live
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(u32x4 *dst, const u32x4 *src,
+                                                          uint64_t n16) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const uint64_t want = (n16 + 1023) / 1024;
+  const unsigned blocks = (unsigned)std::min<uint64_t>(std::max<uint64_t>(want, 1), 256 * 16);
+  hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, s, (const u32x4 *)src, n16,
+                     (uint32_t *)sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)std::min<uint64_t>((n16 + 255) / 256, 256 * 16);
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(blocks), dim3(256), 0, s, (u32x4 *)dst,
+                     (const u32x4 *)src, n16);
+  return hipGetLastError();
 }
 
 // Counting sort of router pairs by expert in one workgroup (LDS histogram).
@@ -529,18 +599,20 @@ static hipError_t launch_skinny(const GemmArgs &a, const Variant &v, bool moe, i
                                 int64_t items, hipStream_t s) {
   dim3 block(64 * v.W);
   dim3 g((unsigned)grid);
+  const size_t lds = (size_t)v.W * v.T * 256 * sizeof(float);
 #define QG_KR_CASE(KRV)                                                                   \
   case KRV:                                                                               \
-    if (v.T == 2)                                                                         \
-      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 2, KRV>), g, block, 0, s, a, (int)moe, items); \
+    if (v.T == 4)                                                                         \
+      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 4, KRV>), g, block, lds, s, a, (int)moe, items); \
+    else if (v.T == 2)                                                                    \
+      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 2, KRV>), g, block, lds, s, a, (int)moe, items); \
     else                                                                                  \
-      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 1, KRV>), g, block, 0, s, a, (int)moe, items); \
+      hipLaunchKernelGGL((skinny_kernel<FMT, GROUP, 1, KRV>), g, block, lds, s, a, (int)moe, items); \
     break;
   switch (v.KR) {
     QG_KR_CASE(1)
     QG_KR_CASE(2)
     QG_KR_CASE(4)
-    QG_KR_CASE(8)
     default: return hipErrorInvalidValue;
   }
 #undef QG_KR_CASE
@@ -574,7 +646,7 @@ static int fmt_of(const qg_layer_desc &d) {
 
 static hipError_t launch_any(const GemmArgs &a, const qg_layer_desc &d, const Variant &v, bool moe,
                              int64_t grid, int64_t items, hipStream_t s) {
-  if (v.W < 1 || v.W > kMaxWaves || (v.T != 1 && v.T != 2)) return hipErrorInvalidValue;
+  if (v.W < 1 || v.W > kMaxWaves || (v.T != 1 && v.T != 2 && v.T != 4)) return hipErrorInvalidValue;
   if (grid <= 0) return hipSuccess;
   switch (fmt_of(d)) {
     case 0: return launch_fmt<0>(a, d.group_size, v, moe, grid, items, s);
@@ -623,13 +695,6 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s) {
   return launch_moe(a, d, v, max_tiles, s);
-}
-
-hipError_t launch_fill_u32(uint32_t *p, uint64_t count, uint32_t value, hipStream_t s) {
-  if (count == 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((count + 255) / 256);
-  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, p, count, value);
-  return hipGetLastError();
 }
 
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts, int32_t *sorted,

@@ -90,7 +90,7 @@ def run_gemm(layer: Layer, acts: Acts, m: int, otype=qg.O_BF16) -> torch.Tensor:
     y = torch.empty((m, layer.n), dtype=torch.float32 if otype == qg.O_F32 else torch.bfloat16,
                     device="cuda")
     ws_bytes = qg.gemm_workspace_size(layer.w, m)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     qg.gemm(layer.w, acts.x, acts.xs, m, layer.k, y, otype, layer.n, ws, ws_bytes)
     torch.cuda.synchronize()
     return y

@@ -270,3 +270,15 @@ def test_binding_maps_a_single_hip_runtime():
             "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n") % ROOT
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert out.stdout.strip() == "1"
+
+
+def test_moe_dispatch_covers_configured_shapes():
+    """The grouped kernel keeps K in one workgroup: every configured expert
+    shape (gate_up and down of both MoE configurations) must be covered."""
+    for wt, n, k, g, e in [(qg.W_INT4, 4096, 7168, 128, 256), (qg.W_INT4, 7168, 2048, 128, 256),
+                           (qg.W_MXFP4, 1280, 4096, 32, 128), (qg.W_MXFP4, 4096, 640, 32, 128)]:
+        w = _bound(qg.layer_desc(wt, n, k, g, num_experts=e))
+        for pairs in (8, 512, 4096, 32768):
+            s = qg.describe_dispatch(w, pairs)
+            T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
+            assert S == 1 and W * KR >= -(-k // 128) and W <= 16, s

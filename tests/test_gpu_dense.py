@@ -87,16 +87,24 @@ def test_ragged_shapes(m):
 
 
 def test_split_k_path_matches(monkeypatch):
+    """K split across workgroups: one zero-filled workspace serves consecutive
+    calls with different split counts (the counters reset themselves)."""
     layer = Layer(qg.W_UINT4, 64, 4096, 128, seed=3)
-    acts = Acts(False, 16, 4096, seed=3)
-    ref = oracle.gemm(acts.xdq, layer.wdq())
-    for tune in ("1,2,4,4", "1,1,2,16", "2,2,4,4", "1,8,1,4"):
-        monkeypatch.setenv("QG_TUNE", tune)
-        assert "splits" in qg.describe_dispatch(layer.w, 16)
-        assert qg.gemm_workspace_size(layer.w, 16) > 0
-        for _ in range(2):  # counters reset between calls
-            y = run_gemm(layer, acts, 16, qg.O_F32)
-            assert err(y, ref) <= TOL_F32, tune
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    for m in (16, 3):
+        acts = Acts(False, m, 4096, seed=3)
+        ref = oracle.gemm(acts.xdq, layer.wdq())
+        for tune in ("1,2,4,4", "1,1,2,16", "2,2,4,4", "4,2,8,2", "1,4,1,8"):
+            monkeypatch.setenv("QG_TUNE", tune)
+            assert int(qg.describe_dispatch(layer.w, m).split("splits=")[1]) > 1
+            need = qg.gemm_workspace_size(layer.w, m)
+            assert 0 < need <= ws.numel()
+            for _ in range(2):
+                y = torch.empty((m, 64), dtype=torch.float32, device="cuda")
+                qg.gemm(layer.w, acts.x, None, m, 4096, y, qg.O_F32, 64, ws, ws.numel())
+                torch.cuda.synchronize()
+                assert err(y, ref) <= TOL_F32, tune
+            assert int(ws[:4 * 64].view(torch.int32).abs().sum()) == 0  # counters back at zero
 
 
 def test_tuning_variants_agree(monkeypatch):
