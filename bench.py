@@ -1,22 +1,29 @@
 """Benchmark of the quantized GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick] [--no-cpu]
 
 Primary workload (the metric's "weight GB/s at M=1 decode"): dense W4A16
-decode, asymmetric INT4 with uint4 zero points, group 128, bf16 scales, bf16
+decode -- asymmetric INT4 with uint4 zero points, group 128, bf16 scales, bf16
 N(0,1) activations, M = 1.  One step = the two decode GEMMs of an MLP block,
-(N, K) = (14336, 4096) and (4096, 14336), each one qg_gemm launch.  Weights are
-resident in HBM before timing; every step reads a different copy of the
-weights (8 rotating copies, 488 MB > 256 MB MALL + L2), so each launch streams
-its weights from HBM as a decode step over distinct layers would.
+(N, K) = (14336, 4096) then (4096, 14336), one qg_gemm launch each.  Weights
+are resident in HBM before timing; consecutive steps read different copies
+of the weights (8 rotating copies, 488 MB > the 256 MB MALL), as a decode
+pass over distinct layers would.
 
-value = algorithmic weight bytes (packed codes at 0.5 B/weight + bf16 scales +
-4-bit zero points, unpadded) per step / step time.
+value = algorithmic weight bytes per step (codes at 0.5 B/weight + bf16 scales
++ 4-bit zero points, unpadded) / step time.
 
-The JSON line also carries the roofline of the dominant kernel (per-launch HIP
-events on the launch stream, averaged over the timed steps), the CPU oracle
-timed on a bounded sample (rank 0 only), and with --extra the other decode
-shapes/formats, the W4A8 MXFP4 x MXFP8 GEMM at M = 4096 and MoE grouped runs.
+roofline: the dominant kernel's algorithmic bytes per launch / its average
+launch duration, from HIP events around a run of back-to-back launches of that
+kernel alone on the launch stream.
+
+Unless --quick, the line also carries the other configurations ("extra"):
+INT3 and M = 4 / 16 decode, the W4A8 MXFP4 x MXFP8 GEMM at M = 4096, and the
+MoE grouped configurations (gate_up + down latency, the routing sort apart).
+MoE weights are random bytes written straight into the packed layout on the
+device (uniform codes, |N(0, 0.02)| bf16 or e8m0 scales near 2^-7): the kernels
+read the same bytes a preprocessed checkpoint would give, and multi-GB expert
+sets are ready in seconds; parity tests go through qg_preprocess instead.
 """
 from __future__ import annotations
 
@@ -32,10 +39,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-FP8_PEAK_TFLOPS = 5000.0
-BF16_PEAK_TFLOPS = 2500.0
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 METRIC = "TFLOPS at M=4096 (W4A16, W4A8-MXFP4) + weight GB/s at M=1 decode, 1 GPU"
 ROTATE = 8
+MALL_BYTES = 256 << 20
 
 
 def weight_bytes(n: int, k: int, bits: int, group: int, zp: bool, scale_bytes: int = 2) -> int:
@@ -45,7 +52,7 @@ def weight_bytes(n: int, k: int, bits: int, group: int, zp: bool, scale_bytes: i
 
 
 class DenseWeights:
-    """ROTATE packed copies of one seeded weight matrix on the device."""
+    """`copies` packed copies of one seeded weight matrix on the device."""
 
     def __init__(self, qg, synth, torch, wtype, n, k, group, seed, copies=ROTATE):
         self.n, self.k, self.group, self.wtype = n, k, group, wtype
@@ -78,24 +85,143 @@ def make_x(qg, synth, torch, mx, m, k, seed):
     return torch.from_numpy(b.view(np.int16)).cuda(), None, b
 
 
-def time_dense(qg, torch, wts, x, xs, m, steps, warmup, otype=None):
-    """Times `steps` launches rotating over the weight copies; returns mean ms per launch."""
-    otype = qg.O_BF16 if otype is None else otype
+def timed(torch, launch, iters, warmup):
+    """Mean ms per call of `launch(i)` over `iters` back-to-back calls, HIP
+    events at both ends on the current stream."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(iters):
+        launch(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
+def dense_launcher(qg, torch, wts, x, xs, m):
     y = torch.empty((m, wts.n), dtype=torch.bfloat16, device="cuda")
     ws_bytes = qg.gemm_workspace_size(wts.ws[0], m)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        qg.gemm(wts.ws[i % len(wts.ws)], x, xs, m, wts.k, y, otype, wts.n, ws, ws_bytes, stream)
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
-    for i in range(steps):
-        ev[i][0].record(stream)
-        qg.gemm(wts.ws[i % len(wts.ws)], x, xs, m, wts.k, y, otype, wts.n, ws, ws_bytes, stream)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    stream = torch.cuda.current_stream().cuda_stream
+    n = len(wts.ws)
+    return lambda i: qg.gemm(wts.ws[i % n], x, xs, m, wts.k, y, qg.O_BF16, wts.n, ws, ws_bytes, stream)
+
+
+# ---------------------------------------------------------------------------
+# MoE configurations
+# ---------------------------------------------------------------------------
+
+def fill_packed_random(qg, torch, w, buf, gen):
+    """Random valid content written straight into a packed weight buffer."""
+    d = w.desc
+    E, n, k = d.num_experts, d.n, d.k
+    v = buf.view(E, w.expert_stride)
+    bits = 3 if d.wtype in (qg.W_INT3, qg.W_UINT3) else 4
+    codes_bytes = w.n_tiles * w.k_blocks * (1024 if bits == 4 else 768)
+    for e0 in range(0, E, 16):  # bounded temporaries
+        e1 = min(E, e0 + 16)
+        v[e0:e1, :codes_bytes] = torch.randint(0, 256, (e1 - e0, codes_bytes), dtype=torch.uint8,
+                                               device="cuda", generator=gen)
+    n_pad = w.n_tiles * 16
+    so = w.scales_offset
+    if d.wtype == qg.W_MXFP4:
+        kb_pad = -(-w.k_blocks // 4) * 4
+        sc = v[:, so:so + n_pad * 4 * kb_pad].view(E, n_pad, 4, kb_pad)
+        sc[:, :n, :, :k // 128] = torch.randint(118, 123, (E, n, 4, k // 128), dtype=torch.uint8,
+                                                device="cuda", generator=gen)
+        if k % 128:
+            sc[:, :n, :(k % 128) // 32, k // 128] = 120
+    else:
+        gp, G = w.groups_padded, k // d.group_size
+        s16 = v[:, so:so + n_pad * gp * 2].contiguous().view(torch.int16).view(E, n_pad, gp)
+        vals = (torch.randn((E, n, G), device="cuda", generator=gen) * 0.02).abs()
+        s16[:, :n, :G] = vals.to(torch.bfloat16).view(torch.int16)
+        v[:, so:so + n_pad * gp * 2] = s16.view(E, -1).view(torch.uint8)
+        if d.wtype in (qg.W_UINT4, qg.W_UINT3):
+            zo = w.zeros_offset
+            zw = v[:, zo:zo + n_pad * gp // 2].view(E, n_pad, gp // 2)
+            zw[:, :n, :G // 2] = torch.randint(0, 256, (E, n, G // 2), dtype=torch.uint8, device="cuda",
+                                               generator=gen)
+
+
+class MoELayer:
+    def __init__(self, qg, torch, wtype, experts, n, k, copies, gen):
+        g = 32 if wtype == qg.W_MXFP4 else 128
+        desc = qg.layer_desc(wtype, n, k, g, num_experts=experts)
+        size = qg.packed_size(desc)
+        self.n, self.k, self.ws = n, k, []
+        self.bufs = []
+        for _ in range(copies):
+            b = torch.zeros(size, dtype=torch.uint8, device="cuda")
+            w = qg.weight_bind(desc, b, size)
+            fill_packed_random(qg, torch, w, b, gen)
+            self.ws.append(w)
+            self.bufs.append(b)
+
+
+def mx_acts_device(torch, rows, k, gen):
+    """MXFP8 activations quantized on the device from N(0,1): per-32 e8m0
+    exponent floor(log2 amax) - 8, elements rounded to e4m3 (saturating)."""
+    x = torch.randn((rows, k // 32, 32), device="cuda", generator=gen)
+    amax = x.abs().amax(dim=2).clamp_min(2.0 ** -100)
+    e = torch.floor(torch.log2(amax)) - 8
+    q = (x / torch.exp2(e)[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).view(rows, k).contiguous(), (e + 127).to(torch.uint8).contiguous()
+
+
+def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters):
+    mx = wtype == qg.W_MXFP4
+    g = 32 if mx else 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    ids = synth.route(synth.rng(7, tokens), tokens, experts, topk)
+    active = int(np.unique(ids).size)
+    p = tokens * topk
+    touched = active * (weight_bytes(n1, k1, 4, g, False, 1 if mx else 2) +
+                        weight_bytes(n2, k2, 4, g, False, 1 if mx else 2))
+    copies = int(min(16, max(1, -(-2 * MALL_BYTES // touched))))
+    up = MoELayer(qg, torch, wtype, experts, n1, k1, copies, gen)
+    down = MoELayer(qg, torch, wtype, experts, n2, k2, copies, gen)
+    d_ids = torch.from_numpy(ids).cuda()
+    sorted_ids = torch.empty(p, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
+    wsb = qg.moe_workspace_size(up.ws[0], tokens, topk)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    t_sort = timed(torch, lambda i: qg.moe_sort(d_ids, tokens, topk, experts, sorted_ids, offsets,
+                                                ws, wsb, stream), iters, 3)
+    if mx:
+        x, xs = mx_acts_device(torch, tokens, k1, gen)
+        h, hs = mx_acts_device(torch, p, k2, gen)
+    else:
+        x = torch.randn((tokens, k1), device="cuda", generator=gen).to(torch.bfloat16)
+        h = torch.randn((p, k2), device="cuda", generator=gen).to(torch.bfloat16)
+        xs = hs = None
+    y1 = torch.empty((p, n1), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((p, n2), dtype=torch.bfloat16, device="cuda")
+    t_up = timed(torch, lambda i: qg.moe_gemm(up.ws[i % copies], x, xs, qg.ROWS_BY_TOKEN, sorted_ids,
+                                              offsets, tokens, topk, y1, qg.O_BF16, qg.ROWS_BY_PAIR,
+                                              None, 0, stream), iters, 2)
+    t_dn = timed(torch, lambda i: qg.moe_gemm(down.ws[i % copies], h, hs, qg.ROWS_BY_PAIR, sorted_ids,
+                                              offsets, tokens, topk, y2, qg.O_BF16, qg.ROWS_BY_PAIR,
+                                              None, 0, stream), iters, 2)
+    t = t_up + t_dn
+    flops = 2.0 * p * (n1 * k1 + n2 * k2)
+    tflops = flops / (t * 1e-3) / 1e12
+    gbs = touched / (t * 1e-3) / 1e9
+    peak = PEAK_TFLOPS["fp8" if mx else "bf16"]
+    out = {"tokens": tokens, "active_experts": active, "weight_copies": copies,
+           "gate_up_us": round(t_up * 1e3, 2), "down_us": round(t_dn * 1e3, 2),
+           "sort_us": round(t_sort * 1e3, 2), "TFLOPS": round(tflops, 2),
+           "weight_GBs": round(gbs, 1), "mfma_frac": round(tflops / peak, 4),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+           "dispatch": qg.describe_dispatch(up.ws[0], p)}
+    del up, down
+    torch.cuda.empty_cache()
+    print(f"[bench] {name} T={tokens}: {out}", file=sys.stderr, flush=True)
+    return out
 
 
 def cpu_baseline(oracle, shapes, budget_s=15.0):
@@ -113,8 +239,8 @@ def cpu_baseline(oracle, shapes, budget_s=15.0):
             break
     return {"value": round(done_bytes / el / 1e9, 3), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{reps} repetitions of the M=1 decode step (both (N,K) shapes), "
-                      f"{el:.1f} s of CPU time"}
+            "sample": f"{reps} repetitions of the M=1 decode step (both (N,K) shapes, "
+                      f"{2 * reps} GEMMs), {el:.1f} s wall on the host"}
 
 
 def main():
@@ -122,12 +248,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="primary decode workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--extra", action="store_true", help="also time the other configurations")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU component)", file=sys.stderr)
+              "(the quantized GEMM path has no multi-GPU component)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -144,35 +270,21 @@ def main():
     print(f"[bench] preparing decode weights {shapes} x{ROTATE} copies", file=sys.stderr, flush=True)
     layers = [DenseWeights(qg, synth, torch, qg.W_UINT4, n, k, 128, seed=i) for i, (n, k) in enumerate(shapes)]
     xs = [make_x(qg, synth, torch, False, 1, k, seed=10 + i) for i, (_, k) in enumerate(shapes)]
-    m = 1
-    stream = torch.cuda.current_stream()
-    ys = [torch.empty((m, L.n), dtype=torch.bfloat16, device="cuda") for L in layers]
-    wsb = [qg.gemm_workspace_size(L.ws[0], m) for L in layers]
-    wsp = [torch.zeros(max(b, 1), dtype=torch.uint8, device="cuda") for b in wsb]
-    for i in range(args.warmup):
-        for j, (L, (x, _, _), y) in enumerate(zip(layers, xs, ys)):
-            qg.gemm(L.ws[i % ROTATE], x, None, m, L.k, y, qg.O_BF16, L.n, wsp[j], wsb[j], stream)
-    torch.cuda.synchronize()
-    # timed region: K steps; per-launch events on the launch stream
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in layers] for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        for j, (L, (x, _, _), y) in enumerate(zip(layers, xs, ys)):
-            ev[s][j][0].record(stream)
-            qg.gemm(L.ws[s % ROTATE], x, None, m, L.k, y, qg.O_BF16, L.n, wsp[j], wsb[j], stream)
-            ev[s][j][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    per_kernel_ms = [float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
-                     for j in range(len(layers))]
+    launchers = [dense_launcher(qg, torch, L, x, None, 1) for L, (x, _, _) in zip(layers, xs)]
+
+    def step(i):
+        for f in launchers:
+            f(i)
+
+    # timed region: K steps bracketed by a synchronize and events on both sides
+    ms_step = timed(torch, step, args.steps, args.warmup)
     step_bytes = sum(L.bytes for L in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    # per-kernel average launch durations (each kernel alone, back to back)
+    per_kernel_ms = [timed(torch, f, args.steps, 5) for f in launchers]
     dom = int(np.argmax(per_kernel_ms))
     achieved = layers[dom].bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
+    print(f"[bench] decode step {ms_step * 1e3:.2f} us, {value:.0f} GB/s", file=sys.stderr, flush=True)
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -184,11 +296,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "u4 codes, bf16 MFMA, f32 accumulate",
-        "data": "synthetic (seeded), weights resident in HBM, 8 rotating copies",
+        "dtype": "u4 weights, bf16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded); weights resident in HBM, 8 rotating copies",
         "config": {
             "workload": "dense W4A16 decode: UINT4 + uint4 zero point, group 128, bf16 scales, "
-                        "M=1, (N,K)=(14336,4096) then (4096,14336)",
+                        "bf16 activations, M=1, (N,K)=(14336,4096) then (4096,14336)",
             "m": 1, "shapes": shapes, "group": 128, "weight_bytes_per_step": step_bytes,
             "dispatch": [qg.describe_dispatch(L.ws[0], 1) for L in layers],
         },
@@ -196,31 +308,45 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": f"skinny_kernel (dense W4A16, N={layers[dom].n}, K={layers[dom].k}, M=1)",
+            "kernel": f"skinny_kernel dense W4A16 N={layers[dom].n} K={layers[dom].k} M=1",
+            "bytes_per_launch": layers[dom].bytes,
         },
     }
 
-    if args.extra:
+    if not args.quick:
         extra = {}
         for wtype, name in ((qg.W_UINT4, "uint4_zp"), (qg.W_INT3, "int3")):
             for i, (n, k) in enumerate(shapes):
                 L = layers[i] if wtype == qg.W_UINT4 else DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=30 + i)
                 for mm in (1, 4, 16):
                     x, _, _ = make_x(qg, synth, torch, False, mm, k, seed=40 + mm)
-                    t = time_dense(qg, torch, L, x, None, mm, 100, 10)
+                    t = timed(torch, dense_launcher(qg, torch, L, x, None, mm), 100, 10)
                     extra[f"decode_{name}_M{mm}_N{n}_K{k}"] = {
                         "us": round(t * 1e3, 2), "weight_GBs": round(L.bytes / (t * 1e-3) / 1e9, 1),
-                        "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)}
-                print(f"[bench] extra {name} {n}x{k} done", file=sys.stderr, flush=True)
+                        "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "dispatch": qg.describe_dispatch(L.ws[0], mm)}
+            print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
         for n in (3072, 14336):
             L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
             x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)
-            t = time_dense(qg, torch, L, x, xsc, 4096, 10, 2)
+            t = timed(torch, dense_launcher(qg, torch, L, x, xsc, 4096), 5, 1)
             fl = 2.0 * 4096 * n * 4096
             extra[f"w4a8_mx_M4096_N{n}_K4096"] = {
-                "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 1),
-                "fp8_frac": round(fl / (t * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
-            print(f"[bench] extra mx N={n} done", file=sys.stderr, flush=True)
+                "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+                "fp8_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
+            print(f"[bench] extra mx N={n}: {extra[f'w4a8_mx_M4096_N{n}_K4096']}", file=sys.stderr, flush=True)
+            del L
+        moe = {}
+        for tokens in (64, 4096):
+            moe[f"w4a16_E256_top8_T{tokens}"] = bench_moe(
+                qg, synth, torch, "moe_w4a16", qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, tokens,
+                iters=5 if tokens > 64 else 30)
+        for tokens in (1, 64, 512, 4096):
+            moe[f"w4a8_E128_top8_T{tokens}"] = bench_moe(
+                qg, synth, torch, "moe_w4a8", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
+                iters=5 if tokens > 512 else 30)
+        extra["moe"] = moe
         out["extra"] = extra
 
     if not args.no_cpu:
