@@ -34,6 +34,7 @@ static bool env_variant(Variant *v) {
   if (sscanf(s, "%d,%d,%d,%d", &T, &KR, &W, &S) != 4) return false;
   if (T < 1 || KR < 1 || W < 1 || W > 16 || S < 1) return false;
   v->kind = 0;
+  v->bn = 0;
   v->T = T;
   v->KR = KR;
   v->W = W;
@@ -77,7 +78,7 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
   const bool long_k = (k_blocks + KR - 1) / KR > 16;  // K gets split anyway
   while (!long_k && T > 1 && (int64_t)((n_tiles + T - 1) / T) * m_tiles < 128) T /= 2;
   KR = clamp_kr(d, T, KR);
-  Variant v{0, T, KR, 1, 1};
+  Variant v{0, T, KR, 1, 1, 0};
   const int64_t n_blocks = (n_tiles + T - 1) / T;
   const int waves_k = (k_blocks + KR - 1) / KR;
   int splits = 1;
@@ -102,8 +103,27 @@ static void sanitize(const qg_layer_desc &d, Variant *v) {
   if (!variant_ok(d, v->T, v->KR)) v->T = 1;
 }
 
+// Large M on MX formats: the LDS-tiled scaled-MFMA kernel (256 x BN tiles).
+// BN = 256 halves the L2 traffic per flop but needs twice the columns to fill
+// the chip; it is used once the 256-column tiling still gives >= 512 tiles.
+static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
+  if (w.desc.wtype != QG_W_MXFP4 || m < 256 || w.desc.k % 128 != 0) return false;
+  const char *s = getenv("QG_TILED");
+  if (s && *s == '0') return false;
+  const int64_t m_tiles = (m + 255) / 256;
+  const int64_t n_pad = (int64_t)w.n_tiles * 16;
+  int bn = 128;  // the 256-column instance still spills at 2 waves per SIMD
+  (void)m_tiles;
+  (void)n_pad;
+  const char *b = getenv("QG_TILED_BN");
+  if (b && (atoi(b) == 128 || atoi(b) == 256)) bn = atoi(b);
+  *v = Variant{1, 1, 1, 1, 1, bn};
+  return true;
+}
+
 Variant select_dense(const qg_weight &w, int64_t m) {
   Variant v;
+  if (tiled_for(w, m, &v)) return v;
   if (env_variant(&v)) {
     sanitize(w.desc, &v);
     while (!covers(v, w.k_blocks)) ++v.splits;
@@ -320,7 +340,10 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
     a.counters = (uint32_t *)ws;
     a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
   }
-  he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
+  if (v.kind == 1)
+    he = launch_mx_tiled(a, v.bn, stream);
+  else
+    he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
 }
 
@@ -420,7 +443,10 @@ extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *b
   if (st != QG_OK) return st;
   if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
   const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
-  snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
-           v.KR, v.W, v.splits);
+  if (v.kind == 1)
+    snprintf(buf, buf_bytes, "%s_tiled BM=256 BN=%d", L.is_mx ? "mx" : "a16", v.bn);
+  else
+    snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
+             v.KR, v.W, v.splits);
   return QG_OK;
 }

@@ -251,6 +251,9 @@ def test_dispatch_table_covers_k():
         w = _bound(qg.layer_desc(wt, n, k, g))
         for m in (1, 4, 16, 64, 4096):
             s = qg.describe_dispatch(w, m)
+            if "tiled" in s:  # LDS-tiled large-M path: loops over all of K
+                assert wt == qg.W_MXFP4 and m >= 256 and k % 128 == 0, s
+                continue
             T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
             assert W * KR * S >= -(-k // 128), s
             assert 1 <= W <= 16

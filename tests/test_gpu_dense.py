@@ -161,3 +161,23 @@ def test_w4a8_mx_full_size_sampled_rows(nk):
     rows = np.sort(synth.rng(0, 99).choice(m, 96, replace=False))
     rows[0], rows[-1] = 0, m - 1
     _check(layer, acts, m, rows=rows)
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (300, 200, 640), (777, 1040, 4096)])
+def test_mx_tiled_large_m_ragged(m, n, k):
+    """The LDS-tiled MX kernel (M >= 256) with partial row and column tiles."""
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=m)
+    assert "tiled" in qg.describe_dispatch(layer.w, m)
+    _check(layer, Acts(True, m, k, seed=m), m)
+
+
+def test_mx_tiled_identity_rows_exact():
+    n, k, m = 64, 640, 256
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=21)
+    wdq = layer.wdq()
+    codes = np.zeros((m, k), np.uint8)
+    codes[np.arange(m), np.arange(m) * 2 % k] = 0x38
+    acts = Acts(True, m, k, values=(codes, np.full((m, k // 32), 127, np.uint8)))
+    y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
+    for i in range(m):
+        assert np.array_equal(y[i].astype(np.float64), wdq[:, (2 * i) % k]), i
