@@ -103,21 +103,19 @@ static void sanitize(const qg_layer_desc &d, Variant *v) {
   if (!variant_ok(d, v->T, v->KR)) v->T = 1;
 }
 
-// Large M on MX formats: the LDS-tiled scaled-MFMA kernel (256 x BN tiles).
-// BN = 256 halves the L2 traffic per flop but needs twice the columns to fill
-// the chip; it is used once the 256-column tiling still gives >= 512 tiles.
+// Large M on MX formats: the LDS-tiled scaled-MFMA kernel (BM x 256 tiles).
+// BM = 256 halves the L2 traffic per flop but needs twice the rows to fill the
+// chip; it is used when it still gives at least three tiles per CU.
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
-  if (w.desc.wtype != QG_W_MXFP4 || m < 256 || w.desc.k % 128 != 0) return false;
+  if (w.desc.wtype != QG_W_MXFP4 || m < 128 || w.desc.k % 128 != 0) return false;
   const char *s = getenv("QG_TILED");
   if (s && *s == '0') return false;
-  const int64_t m_tiles = (m + 255) / 256;
-  const int64_t n_pad = (int64_t)w.n_tiles * 16;
-  int bn = 128;  // the 256-column instance still spills at 2 waves per SIMD
-  (void)m_tiles;
-  (void)n_pad;
-  const char *b = getenv("QG_TILED_BN");
-  if (b && (atoi(b) == 128 || atoi(b) == 256)) bn = atoi(b);
-  *v = Variant{1, 1, 1, 1, 1, bn};
+  // 256-row tiles halve the weight re-reads and win at every measured shape
+  // once M fills them; 128-row tiles for M in [128, 256)
+  int bm = m >= 256 ? 256 : 128;
+  const char *b = getenv("QG_TILED_BM");
+  if (b && (atoi(b) == 128 || atoi(b) == 256)) bm = atoi(b);
+  *v = Variant{1, 1, 1, 1, 1, bm};
   return true;
 }
 
@@ -444,7 +442,7 @@ extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *b
   if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
   const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
   if (v.kind == 1)
-    snprintf(buf, buf_bytes, "%s_tiled BM=256 BN=%d", L.is_mx ? "mx" : "a16", v.bn);
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=256", L.is_mx ? "mx" : "a16", v.bn);
   else
     snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
              v.KR, v.W, v.splits);

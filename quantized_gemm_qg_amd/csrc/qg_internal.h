@@ -115,7 +115,7 @@ struct Variant {
   int KR;      // k-blocks per wave
   int W;       // waves per workgroup (split of K inside the workgroup)
   int splits;  // split of K across workgroups
-  int bn;      // tiled: workgroup tile columns (128 or 256)
+  int bn;      // tiled: workgroup tile rows (128 or 256); tiles are bn x 256
 };
 
 Variant select_dense(const qg_weight &w, int64_t m);
@@ -129,7 +129,7 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
                           int64_t max_tiles, hipStream_t s);
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s);
-hipError_t launch_mx_tiled(const GemmArgs &a, int bn, hipStream_t s);
+hipError_t launch_mx_tiled(const GemmArgs &a, int bm, hipStream_t s);
 hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,

@@ -6,17 +6,26 @@
 // e8m0 block scales directly (v_mfma_scale_f32_16x16x128_f8f6f4), so nothing is
 // dequantized: the kernel only moves bytes.
 //
-// Tiling: a workgroup computes a 256 x BN tile of Y with 2 x (BN / 64) waves,
-// each wave 128 x 64 (8 x 4 MFMA blocks of 16 x 16, 128 fp32 accumulators per
-// lane).  K advances 128 per step through double-buffered LDS:
-//   A  256 rows x 128 e4m3 bytes, row pitch 144 B (the 16 B pad spreads the
-//      rows of one MFMA fragment read over all LDS banks);
-//   B  BN / 16 packed weight blocks of 1 KB copied verbatim (the packed layout
-//      already stores each lane's 16-byte B operand contiguously, so lane l
-//      reads bytes [16 l, 16 l + 16) of a block: conflict-free);
-//   SA the activations' four e8m0 scales of each row for this K step.
-// Weight scales (one byte per lane per 16-column block and K step) are read
-// from global memory a dword (four K steps) at a time.
+// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x 256 tile of Y, each
+// wave (BM / 2) x 128: (BM / 32) x 8 MFMA blocks of 16 x 16, up to 256 fp32
+// accumulators per lane held in AGPRs, one wave per SIMD.  Large wave tiles
+// keep LDS traffic at 384 B per MFMA (BM = 256), well under the LDS bandwidth
+// the matrix core needs, and large workgroup tiles halve the L2 -> LDS bytes
+// per flop.  K advances 128 per step through a 3-stage LDS ring filled directly
+// from global memory by global_load_lds_dwordx4 (no register staging), so two
+// K steps are in flight while a third is multiplied.  One stage holds
+//   A   BM rows x 128 e4m3 bytes; each row's eight 16-byte chunks are stored
+//       in XOR-swizzled order (chunk c at slot c ^ (row & 7)) so the 16 rows
+//       of an MFMA fragment read hit all LDS banks without padding;
+//   B   16 packed weight blocks of 1 KB copied verbatim (the packed layout
+//       already stores each lane's 16-byte B operand contiguously);
+//   SA  the four e8m0 scales of each activation row for this K step;
+//   SW  for each of the 256 weight columns and quarters q, the dword holding
+//       its e8m0 scales of K steps kb & ~3 .. +3.
+// Every wave issues the same number of loads per stage, so "stage kb has
+// landed" is a wait until at most one stage of the wave's loads is
+// outstanding, followed by a workgroup barrier.  Inside a K step the next row
+// block's LDS reads are scheduled ahead of the current block's 8 MFMAs.
 //
 // Work order: workgroups are dealt round-robin to the 8 XCDs; the tile index
 // is remapped so each XCD owns a contiguous range of a grouped (GM m-tiles at
@@ -32,24 +41,22 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
 
-constexpr int kTBM = 256;        // tile rows
-constexpr int kAPitch = 144;     // LDS bytes per A row
+constexpr int kTBN = 256;   // tile columns
 constexpr int kXcds = 8;
 constexpr int kGroupM = 4;
+constexpr int kStages = 3;
+constexpr int kThreads = 256;
 
-template <int BN>
-struct MxTile {
-  static constexpr int WAVES_N = BN / 64;
-  static constexpr int WAVES = 2 * WAVES_N;
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int NBLK = BN / 16;                  // packed weight blocks per K step
-  static constexpr int A_BYTES = kTBM * kAPitch;         // 36864
-  static constexpr int B_BYTES = NBLK * 1024;
-  static constexpr int SA_BYTES = kTBM * 4;
-  static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES;
-  static constexpr int A_CHUNKS = kTBM * 8;              // 16-byte chunks of the A tile
-  static constexpr int A_PER_T = A_CHUNKS / THREADS;
-  static constexpr int B_PER_T = NBLK * 64 / THREADS;
+template <int BM>
+struct MxCfg {
+  static constexpr int A = BM * 128;
+  static constexpr int B = (kTBN / 16) * 1024;   // 16 KB
+  static constexpr int SA = BM * 4;
+  static constexpr int SW = kTBN * 4 * 4;        // 4 KB
+  static constexpr int STAGE = A + B + SA + SW;
+  static constexpr int A_LOADS = BM * 128 / 1024 / 4;  // 1 KB loads of A per wave
+  static constexpr int LOADS = A_LOADS + 4 + 1 + 4;    // A + B + SA + SW per wave
+  static constexpr int MB = BM / 32;                   // 16-row blocks per wave
 };
 
 __device__ __forceinline__ void tile_of(int pid, int m_tiles, int n_tiles, int *tm, int *tn) {
@@ -64,130 +71,145 @@ __device__ __forceinline__ void tile_of(int pid, int m_tiles, int n_tiles, int *
   *tn = r / gm;
 }
 
-template <int BN>
-__global__ __launch_bounds__(MxTile<BN>::THREADS) void mx_tiled_kernel(GemmArgs a) {
-  using C = MxTile<BN>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+// Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds + lane *
+// size).  Non-template device functions, so the host pass never analyzes the
+// device-only builtin.
+__device__ __forceinline__ void lds_dma16(const void *g, void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void *g, void *l) {
+  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+}
+
+// s_waitcnt with vmcnt <= n (n <= 63), expcnt and lgkmcnt unconstrained
+#define QG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+template <int BM>
+__global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
+  using C = MxCfg<BM>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
 
-  const int m_tiles = (a.m + kTBM - 1) / kTBM;
-  const int bn_tiles = (a.n_tiles * 16 + BN - 1) / BN;
-  const int total = m_tiles * bn_tiles;
+  const int m_tiles = (a.m + BM - 1) / BM;
+  const int n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
+  const int total = m_tiles * n_tiles_wg;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   if ((int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds) >= total) return;
   int tm, tn;
-  tile_of(blockIdx.x, m_tiles, bn_tiles, &tm, &tn);
-  const int m0 = tm * kTBM;
-  const int nt0 = tn * C::NBLK;  // first 16-column n-tile
+  tile_of(blockIdx.x, m_tiles, n_tiles_wg, &tm, &tn);
+  const int m0 = tm * BM;
+  const int nt0 = tn * (kTBN / 16);  // first 16-column n-tile
   const int kbs = a.k_blocks;
-  const int kq = a.k >> 5;       // activation scale bytes per row
-
+  const int kq = a.k >> 5;           // activation scale bytes per row
   const uint8_t *x = (const uint8_t *)a.x;
-  // --- global -> register staging of one K step ---
-  u32x4 sa_[C::A_PER_T];
-  u32x4 sb_[C::B_PER_T];
-  uint32_t ss_ = 0;
-  auto load_stage = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int row = min(m0 + (c >> 3), a.m - 1);
-      sa_[i] = *(const u32x4 *)(x + (int64_t)row * a.ldx + kb * 128 + 16 * (c & 7));
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      const int c = tid + i * C::THREADS;
-      const int nt = min(nt0 + (c >> 6), a.n_tiles - 1);
-      sb_[i] = *(const u32x4 *)(a.wbase + ((uint64_t)nt * kbs + kb) * 1024 + 16 * (c & 63));
-    }
-    if (tid < kTBM) {
-      const int row = min(m0 + tid, a.m - 1);
-      ss_ = *(const uint32_t *)(a.x_scales + (int64_t)row * kq + 4 * kb);
-    }
-  };
-  auto store_stage = [&](int buf) {
-    uint8_t *s = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_T; ++i) {
-      const int c = tid + i * C::THREADS;
-      *(u32x4 *)(s + (c >> 3) * kAPitch + 16 * (c & 7)) = sa_[i];
-    }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_T; ++i) {
-      const int c = tid + i * C::THREADS;
-      *(u32x4 *)(s + C::A_BYTES + 16 * c) = sb_[i];
-    }
-    if (tid < kTBM) *(uint32_t *)(s + C::A_BYTES + C::B_BYTES + 4 * tid) = ss_;
-  };
-
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // weight scales: lane (column n, quarter q) reads the dword holding K steps
-  // kb & ~3 .. +3 of its column
   const uint8_t *wsc = a.wbase + a.scales_offset;
-  int ncol[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    ncol[j] = min(nt0 + wn * 4 + j, a.n_tiles - 1) * 16 + r16;
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  uint32_t wsw[4] = {0u, 0u, 0u, 0u};
+  // per-lane source offsets (32-bit, added to wave-uniform bases at issue)
+  uint32_t a_off[C::A_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int row = 8 * (wave * C::A_LOADS + i) + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7);
+    a_off[i] = (uint32_t)((int64_t)min(m0 + row, a.m - 1) * a.ldx + 16 * c);
+  }
+  const uint8_t *b_base = a.wbase + 16 * lane;
+  uint32_t b_blk[4];  // first packed block of each of the wave's four n-tiles
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b_blk[i] = (uint32_t)min(nt0 + wave * 4 + i, a.n_tiles - 1) * kbs;
+  // SA: BM rows of 4 bytes = BM / 64 loads of 256 B; with BM = 128 waves 2 and
+  // 3 repeat waves 0 and 1 (same bytes to the same place)
+  const int sa_row = (wave % (BM / 64)) * 64 + lane;
+  const uint8_t *sa_src = a.x_scales + (int64_t)min(m0 + sa_row, a.m - 1) * kq;
+  uint32_t sw_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = (wave * 4 + i) * 64 + lane;  // (column, quarter) pair
+    const int n = min(nt0 * 16 + (e >> 2), a.n_tiles * 16 - 1);
+    sw_off[i] = (uint32_t)(((uint64_t)n * 4 + (e & 3)) * a.kb_pad);
+  }
+
+  auto issue = [&](int kb, int buf) {
+    uint8_t *st = smem + buf * C::STAGE;
+    const uint8_t *xk = x + kb * 128;
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i)
+      lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + (wave * 4 + i) * 1024);
+    lds_dma4(sa_src + 4 * kb, st + C::A + C::B + (wave % (BM / 64)) * 256);
+    const uint8_t *wk = wsc + (kb & ~3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_dma4(wk + sw_off[i], st + C::A + C::B + C::SA + (wave * 4 + i) * 256);
+  };
+
+  f32x4 acc[C::MB][8];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (kbs > 1) issue(1, 1);
   for (int kb = 0; kb < kbs; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < kbs) load_stage(kb + 1);
-    if ((kb & 3) == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wsw[j] = *(const uint32_t *)(wsc + ((uint64_t)ncol[j] * 4 + q) * a.kb_pad + kb);
+    if (kb + 1 < kbs) {
+      QG_WAIT_VMCNT(C::LOADS);
+    } else {
+      QG_WAIT_VMCNT(0);
     }
-    const uint8_t *s = smem + buf * C::STAGE;
-    // B fragments and scales of the wave's four 16-column blocks
-    i32x8 bf[4];
-    int bsc[4];
+    __builtin_amdgcn_s_barrier();  // stage kb is in LDS; stage kb - 1 is free
+    if (kb + 2 < kbs) issue(kb + 2, (kb + 2) % kStages);
+    const uint8_t *st = smem + (kb % kStages) * C::STAGE;
+    i32x8 bf[8];
+    int bsc[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 v = *(const u32x4 *)(s + C::A_BYTES + (wn * 4 + j) * 1024 + 16 * lane);
+    for (int j = 0; j < 8; ++j) {
+      const int blk = wn * 8 + j;
+      const u32x4 v = *(const u32x4 *)(st + C::A + blk * 1024 + 16 * lane);
       bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      bsc[j] = (int)((wsw[j] >> (8 * (kb & 3))) & 0xFFu);
+      const uint32_t sw = *(const uint32_t *)(st + C::A + C::B + C::SA + ((blk * 16 + r16) * 4 + q) * 4);
+      bsc[j] = (int)((sw >> (8 * (kb & 3))) & 0xFFu);
     }
+    auto read_a = [&](int i, i32x8 &af, int &asc) {
+      const int row = wm * (BM / 2) + i * 16 + r16;
+      const uint8_t *ap = st + row * 128;
+      const u32x4 lo = *(const u32x4 *)(ap + 16 * (q ^ (row & 7)));
+      const u32x4 hi = *(const u32x4 *)(ap + 16 * ((4 + q) ^ (row & 7)));
+      af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      asc = st[C::A + C::B + 4 * row + q];
+    };
+    i32x8 af[2];
+    int asc[2];
+    read_a(0, af[0], asc[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 19, 0);  // B (16) + A block 0 (3) reads first
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int row = wm * 128 + i * 16 + r16;
-      const uint8_t *ap = s + row * kAPitch;
-      const u32x4 lo = *(const u32x4 *)(ap + 16 * q);
-      const u32x4 hi = *(const u32x4 *)(ap + 64 + 16 * q);
-      const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      const int asc = s[C::A_BYTES + C::B_BYTES + 4 * row + q];
+    for (int i = 0; i < C::MB; ++i) {
+      if (i + 1 < C::MB) read_a(i + 1, af[(i + 1) & 1], asc[(i + 1) & 1]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 4, 0,
-                                                                      asc, 0, bsc[j]);
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], 0, 4,
+                                                                      0, asc[i & 1], 0, bsc[j]);
+      if (i + 1 < C::MB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next block's reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                    // this block's MFMAs
     }
-    if (kb + 1 < kbs) store_stage(buf ^ 1);
-    __syncthreads();
   }
 
   // output: block (i, j) lane holds rows 4q..4q+3 of column r16
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < C::MB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = (nt0 + wn * 4 + j) * 16 + r16;
+    for (int j = 0; j < 8; ++j) {
+      const int col = (nt0 + wn * 8 + j) * 16 + r16;
       if (col >= a.n) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * 128 + i * 16 + 4 * q + e;
+        const int row = m0 + wm * (BM / 2) + i * 16 + 4 * q + e;
         if (row >= a.m) continue;
         if (a.otype == QG_O_F32)
           ((float *)a.y)[(int64_t)row * a.ldy + col] = acc[i][j][e];
@@ -197,28 +219,25 @@ __global__ __launch_bounds__(MxTile<BN>::THREADS) void mx_tiled_kernel(GemmArgs 
     }
 }
 
-template <int BN>
-static hipError_t launch_mx_tiled_bn(const GemmArgs &a, hipStream_t s) {
-  using C = MxTile<BN>;
-  const int m_tiles = (a.m + kTBM - 1) / kTBM;
-  const int bn_tiles = (a.n_tiles * 16 + BN - 1) / BN;
-  const int total = m_tiles * bn_tiles;
+template <int BM>
+static hipError_t launch_mx_tiled_bm(const GemmArgs &a, hipStream_t s) {
+  using C = MxCfg<BM>;
+  const int m_tiles = (a.m + BM - 1) / BM;
+  const int n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
+  const int total = m_tiles * n_tiles_wg;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int grid = per_xcd * kXcds;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BN>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * C::STAGE);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(mx_tiled_kernel<BN>, dim3(grid), dim3(C::THREADS), 2 * C::STAGE, s, a);
+  const size_t lds = (size_t)kStages * C::STAGE;
+  hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BM>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mx_tiled_kernel<BM>, dim3(per_xcd * kXcds), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_mx_tiled(const GemmArgs &a, int bn, hipStream_t s) {
+// bm: workgroup tile rows (128 or 256); the tile is bm x 256
+hipError_t launch_mx_tiled(const GemmArgs &a, int bm, hipStream_t s) {
   if (a.k % 128 != 0) return hipErrorInvalidValue;
-  return bn == 256 ? launch_mx_tiled_bn<256>(a, s) : launch_mx_tiled_bn<128>(a, s);
+  return bm == 256 ? launch_mx_tiled_bm<256>(a, s) : launch_mx_tiled_bm<128>(a, s);
 }
 
 }  // namespace qg

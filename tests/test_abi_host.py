@@ -285,3 +285,16 @@ def test_moe_dispatch_covers_configured_shapes():
             s = qg.describe_dispatch(w, pairs)
             T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
             assert S == 1 and W * KR >= -(-k // 128) and W <= 16, s
+
+
+def test_library_has_no_undefined_internal_symbols():
+    """Every kernel and launcher of the library is defined in libqg.so itself
+    (an uninstantiated kernel template would leave an undefined qg:: symbol)."""
+    import shutil
+    import subprocess
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--undefined-only", qg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    assert not [l for l in out.splitlines() if "_ZN2qg" in l], out
