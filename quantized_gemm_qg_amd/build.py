@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqg.so")
-SOURCES = ["qg_api.cpp", "qg_repack.cpp", "qg_kernels.hip", "qg_tiled.hip"]
+SOURCES = ["qg_api.cpp", "qg_repack.cpp", "qg_kernels.hip", "qg_tiled.hip", "qg_tiled_a16.hip"]
 ARCH = os.environ.get("QG_OFFLOAD_ARCH", "gfx950")
 
 
@@ -39,9 +39,15 @@ def _flags():
     ]
 
 
+# Per-source extra flags.  The integer-format tiled kernel keeps its MFMA
+# results in VGPRs (they feed fp32 FMAs right away); left to its heuristics the
+# compiler puts them in AGPRs and copies every one back.
+EXTRA = {"qg_tiled_a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", *_flags(), "-x", "hip", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), "-c", *_flags(), *EXTRA.get(src, []), "-x", "hip", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -103,19 +103,25 @@ static void sanitize(const qg_layer_desc &d, Variant *v) {
   if (!variant_ok(d, v->T, v->KR)) v->T = 1;
 }
 
-// Large M on MX formats: the LDS-tiled scaled-MFMA kernel (BM x 256 tiles).
-// BM = 256 halves the L2 traffic per flop but needs twice the rows to fill the
-// chip; it is used when it still gives at least three tiles per CU.
+// Large M: the LDS-tiled kernels, scaled MFMA for MX (BM x 256 tiles, from
+// M = 128) and bf16 MFMA for the integer formats (BM x 128 tiles, from M = 256,
+// where the 16-row skinny kernel stops being weight-bound).
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
-  if (w.desc.wtype != QG_W_MXFP4 || m < 128 || w.desc.k % 128 != 0) return false;
+  if (w.desc.k % 128 != 0) return false;
   const char *s = getenv("QG_TILED");
   if (s && *s == '0') return false;
+  const bool mx = w.desc.wtype == QG_W_MXFP4;
+  // the integer-format kernel addresses X and the codes with 32-bit offsets
+  if (!mx && ((uint64_t)m * w.desc.k * 2 >= (1ull << 31) ||
+              (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31)))
+    return false;
+  if (m < (mx ? 128 : 256)) return false;
   // 256-row tiles halve the weight re-reads and win at every measured shape
   // once M fills them; 128-row tiles for M in [128, 256)
   int bm = m >= 256 ? 256 : 128;
   const char *b = getenv("QG_TILED_BM");
   if (b && (atoi(b) == 128 || atoi(b) == 256)) bm = atoi(b);
-  *v = Variant{1, 1, 1, 1, 1, bm};
+  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm};
   return true;
 }
 
@@ -180,7 +186,9 @@ static void fill_weight(const qg_layer_desc *d, const Layout &L, void *dev, uint
 }
 
 static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) {
-  if (v.splits <= 1 || m <= 0) return 0;
+  if (m <= 0) return 0;
+  if (v.kind == 2) return a16_tiled_ws_bytes(w.desc, m);
+  if (v.splits <= 1) return 0;
   const int64_t m_tiles = (m + 15) / 16;
   const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
   const uint64_t counters = align_up((uint64_t)m_tiles * n_blocks * 4, 256);
@@ -340,6 +348,8 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   }
   if (v.kind == 1)
     he = launch_mx_tiled(a, v.bn, stream);
+  else if (v.kind == 2)
+    he = launch_a16_tiled(a, d, v.bn, ws, stream);
   else
     he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -441,8 +451,9 @@ extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *b
   if (st != QG_OK) return st;
   if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
   const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
-  if (v.kind == 1)
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=256", L.is_mx ? "mx" : "a16", v.bn);
+  if (v.kind == 1 || v.kind == 2)
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", L.is_mx ? "mx" : "a16", v.bn,
+             L.is_mx ? 256 : 128);
   else
     snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
              v.KR, v.W, v.splits);

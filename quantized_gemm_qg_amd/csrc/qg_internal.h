@@ -110,12 +110,13 @@ struct GemmArgs {
 
 // One entry of the tuning table: a kernel variant and its tile parameters.
 struct Variant {
-  int kind;    // 0 = skinny (16-row tiles, weights streamed to VGPRs), 1 = tiled (LDS)
+  int kind;    // 0 = skinny (16-row tiles, weights streamed to VGPRs), 1 = MX tiled (LDS),
+               // 2 = integer-format tiled (LDS, bf16 MFMA)
   int T;       // n-tiles per wave
   int KR;      // k-blocks per wave
   int W;       // waves per workgroup (split of K inside the workgroup)
   int splits;  // split of K across workgroups
-  int bn;      // tiled: workgroup tile rows (128 or 256); tiles are bn x 256
+  int bn;      // tiled: workgroup tile rows (128 or 256); tiles are bn x 256 (MX) or bn x 128
 };
 
 Variant select_dense(const qg_weight &w, int64_t m);
@@ -130,6 +131,11 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s);
 hipError_t launch_mx_tiled(const GemmArgs &a, int bm, hipStream_t s);
+// Integer formats at large M: group row sums of X into ws, then the tiled
+// kernel.  ws holds (K / group) * m floats (a16_tiled_ws_bytes).
+hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, void *ws,
+                            hipStream_t s);
+uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m);
 hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,

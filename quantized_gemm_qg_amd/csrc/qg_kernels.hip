@@ -31,6 +31,7 @@
 
 #include <algorithm>
 
+#include "qg_device.h"
 #include "qg_internal.h"
 
 // Weight slices are read once per launch: stream them with non-temporal loads.
@@ -49,59 +50,8 @@ __device__ __forceinline__ V load_stream(const V *p) {
 
 namespace qg {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-
 constexpr int kMaxWaves = 16;
 constexpr int kMaxExperts = 1024;
-
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// register-level unpacking (layout in qg_internal.h)
-// ---------------------------------------------------------------------------
-
-// 4-bit: slots (i, i+4) -> bf16 pair 1 + u/16, code at mantissa bits 3..6.
-__device__ __forceinline__ u32x4 unpack4(uint32_t w) {
-  u32x4 r;
-  r.x = ((w << 3) & 0x00780078u) | 0x3F803F80u;
-  r.y = ((w >> 1) & 0x00780078u) | 0x3F803F80u;
-  r.z = ((w >> 5) & 0x00780078u) | 0x3F803F80u;
-  r.w = ((w >> 9) & 0x00780078u) | 0x3F803F80u;
-  return r;
-}
-
-// 3-bit codes in bits 0..2 of each nibble slot -> bf16 pair 1 + u/8.
-__device__ __forceinline__ u32x4 unpack3(uint32_t w) {
-  u32x4 r;
-  r.x = ((w << 4) & 0x00700070u) | 0x3F803F80u;
-  r.y = (w & 0x00700070u) | 0x3F803F80u;
-  r.z = ((w >> 4) & 0x00700070u) | 0x3F803F80u;
-  r.w = ((w >> 8) & 0x00700070u) | 0x3F803F80u;
-  return r;
-}
-
-// The fourth MFMA of a 3-bit lane slice: bit b of each code sits in bit 3 of
-// the nibble slot of dword b; gather them into bits 0..2.
-__device__ __forceinline__ uint32_t gather3(uint32_t d0, uint32_t d1, uint32_t d2) {
-  return ((d0 >> 3) & 0x11111111u) | ((d1 >> 2) & 0x22222222u) | ((d2 >> 1) & 0x44444444u);
-}
-
-template <int BITS>
-__device__ __forceinline__ u32x4 unpack_b(const u32x4 &w, int j) {
-  if constexpr (BITS == 4) {
-    return unpack4(w[j]);
-  } else {
-    return j < 3 ? unpack3(w[j]) : unpack3(gather3(w.x, w.y, w.z));
-  }
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 __device__ __forceinline__ void store_out(void *y, int64_t ldy, int otype, int64_t row, int col,
                                           float v) {

@@ -33,17 +33,12 @@
 // rows and weight columns in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include "qg_device.h"
 #include "qg_internal.h"
 
 namespace qg {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
-
 constexpr int kTBN = 256;   // tile columns
-constexpr int kXcds = 8;
-constexpr int kGroupM = 4;
 constexpr int kStages = 3;
 constexpr int kThreads = 256;
 
@@ -59,31 +54,6 @@ struct MxCfg {
   static constexpr int MB = BM / 32;                   // 16-row blocks per wave
 };
 
-__device__ __forceinline__ void tile_of(int pid, int m_tiles, int n_tiles, int *tm, int *tn) {
-  const int total = m_tiles * n_tiles;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int t = (pid % kXcds) * per_xcd + pid / kXcds;  // contiguous range per XCD
-  const int group = kGroupM * n_tiles;
-  const int first_m = (t / group) * kGroupM;
-  const int gm = min(kGroupM, m_tiles - first_m);
-  const int r = t % group;
-  *tm = first_m + r % gm;
-  *tn = r / gm;
-}
-
-// Direct global -> LDS loads (each lane's 16 or 4 bytes land at lds + lane *
-// size).  Non-template device functions, so the host pass never analyzes the
-// device-only builtin.
-__device__ __forceinline__ void lds_dma16(const void *g, void *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void *g, void *l) {
-  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
-}
-
-// s_waitcnt with vmcnt <= n (n <= 63), expcnt and lgkmcnt unconstrained
-#define QG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
 template <int BM>
 __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
   using C = MxCfg<BM>;
@@ -96,11 +66,8 @@ __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
 
   const int m_tiles = (a.m + BM - 1) / BM;
   const int n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
-  const int total = m_tiles * n_tiles_wg;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  if ((int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds) >= total) return;
   int tm, tn;
-  tile_of(blockIdx.x, m_tiles, n_tiles_wg, &tm, &tn);
+  if (!tile_of(blockIdx.x, m_tiles, n_tiles_wg, &tm, &tn)) return;
   const int m0 = tm * BM;
   const int nt0 = tn * (kTBN / 16);  // first 16-column n-tile
   const int kbs = a.k_blocks;

@@ -1,0 +1,328 @@
+// Large-M tiled kernel for the integer weight formats (INT4 / UINT4 / INT3 /
+// UINT3 codes, bf16 group scales along K, optional 4-bit zero points) with
+// bf16 activations, on gfx950's v_mfma_f32_16x16x32_bf16.
+//
+// The announcement's "Shared CUDA components" section puts dequantization and
+// scaling inside the GEMM's data path, between the operand loads and the
+// matrix-core step.  Here the packed codes travel HBM -> LDS untouched (a
+// quarter of the bytes of a bf16 weight); each wave turns its columns' codes
+// into bf16 MFMA operands in registers, once per 128-K step, and reuses them
+// for all BM / 2 rows of its tile.
+//
+// Arithmetic.  An offset-binary code u becomes the bf16 value 1 + u / MAG
+// (MAG = 16 for 4-bit, 8 for 3-bit codes: the code lands in the top mantissa
+// bits).  Per K-group the wave computes on the matrix core
+//     G = sum_k x_k * (1 + u_k / MAG) - (1 + z / MAG) * xs,   xs = sum_k x_k
+// by starting the MFMA accumulation from the second term, so G = sum x (u - z)
+// / MAG exactly up to fp32 rounding, and then adds G * (MAG * s) to the output
+// accumulator: one fp32 FMA per accumulator per group.  For symmetric formats
+// z = 2^(b-1) is a constant and the starting value depends on the row only.
+// xs (the group row sums of X, for symmetric formats already multiplied by
+// -(1 + z / MAG)) comes from a small pre-pass kernel that reads X once; the
+// dequantized weight is the exact real (u - z) * s.
+//
+// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x 128 tile of Y, each
+// wave (BM / 2) x 64 as (BM / 32) x 4 blocks of 16 x 16.  K advances 128 per
+// stage; one stage holds
+//   A   BM rows x 128 bf16 (256 B per row, 16-byte chunks XOR-swizzled by
+//       the row's low 4 bits so the 16 rows of a fragment read hit distinct
+//       banks),
+//   B   the 8 packed 16 x 128 blocks of the tile's columns, copied verbatim,
+//   SS  per column the 16-byte run of bf16 scales holding this step's groups,
+//   SZ  per column the dword of zero-point nibbles (formats with zero points),
+//   SX  the group row sums of the tile's rows for this step's groups.
+// Stages are filled straight from global memory with global_load_lds (no
+// register staging) into a 2-deep (BM = 256) or 3-deep (BM = 128) ring; every
+// wave issues the same number of loads per stage, so "stage kb has landed" is
+// an explicit vmcnt wait plus a workgroup barrier.  The workgroup order is the
+// XCD-aware raster of the MX tiled kernel.
+#include <hip/hip_runtime.h>
+
+#include "qg_device.h"
+#include "qg_internal.h"
+
+namespace qg {
+
+constexpr int kA16BN = 128;       // tile columns (8 packed n-tiles)
+constexpr int kA16Threads = 256;  // 4 waves
+constexpr int kLdsBytes = 160 * 1024;
+
+template <int BM, int BITS, bool ZP, int GROUP>
+struct A16Cfg {
+  static constexpr int LB = BITS == 4 ? 16 : 12;  // packed bytes per lane per block
+  static constexpr int BB = 64 * LB;              // packed bytes per 16 x 128 block
+  static constexpr int GPB = 128 / GROUP;         // groups per 128-K step
+  static constexpr int JPG = GROUP / 32;          // K32 MFMA steps per group
+  static constexpr int A = BM * 256;
+  static constexpr int B = 8 * BB;
+  static constexpr int SS = kA16BN * 16;
+  static constexpr int SZ = ZP ? kA16BN * 4 : 0;
+  static constexpr int SX = GPB * BM * 4;
+  static constexpr int OFF_B = A;
+  static constexpr int OFF_SS = OFF_B + B;
+  static constexpr int OFF_SZ = OFF_SS + SS;
+  static constexpr int OFF_SX = OFF_SZ + SZ;
+  static constexpr int STAGE = OFF_SX + SX;
+  static constexpr int STAGES = 3 * STAGE <= kLdsBytes ? 3 : 2;
+  static constexpr int A_LOADS = BM / 16;             // 1-KB copies of A per wave
+  static constexpr int B_LOADS = BITS == 4 ? 2 : 6;   // 1-KB (4-bit) or 256-B (3-bit) copies
+  static constexpr int LOADS = A_LOADS + B_LOADS + 1 + (ZP ? 1 : 0) + GPB;
+  static constexpr int MI = BM / 32;                  // 16-row blocks per wave
+  static constexpr float MAG = BITS == 4 ? 16.f : 8.f;
+  static constexpr int ZSYM = BITS == 4 ? 8 : 4;
+  static_assert(2 * STAGE <= kLdsBytes, "stage does not fit twice in LDS");
+};
+
+// Workgroup barrier that the compiler may not move LDS accesses across; the
+// memory-counter waits are explicit (QG_WAIT_VMCNT) so that loads of later
+// stages stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BITS, bool ZP, int GROUP>
+__global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, const float *xs,
+                                                                 int xs_rows) {
+  using C = A16Cfg<BM, BITS, ZP, GROUP>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int q = lane >> 4, r16 = lane & 15;
+
+  const int m_tiles = (a.m + BM - 1) / BM;
+  const int n_tiles_wg = (a.n_tiles + 7) / 8;
+  int tm, tn;
+  if (!tile_of(blockIdx.x, m_tiles, n_tiles_wg, &tm, &tn)) return;
+  const int m0 = tm * BM;
+  const int nt0 = tn * 8;
+  const int kbs = a.k_blocks, gp = a.groups_padded;
+  const uint32_t umask = sgpr_const(BITS == 4 ? 0x00780078u : 0x00700070u);
+  const uint32_t umagic = vgpr_const(0x3F803F80u);
+
+  // ---- per-lane source offsets (32-bit, added to uniform bases at issue) ----
+  // A: copy i of this wave fills tile rows 4 (wave * A_LOADS + i) + lane / 16,
+  // LDS slot lane % 16, with the row's chunk (slot ^ (row & 15))
+  const uint8_t *x = (const uint8_t *)a.x;
+  uint32_t a_off[C::A_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::A_LOADS; ++i) {
+    const int row = 4 * (wave * C::A_LOADS + i) + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    a_off[i] = (uint32_t)((int64_t)min(m0 + row, a.m - 1) * a.ldx * 2 + 16 * c);
+  }
+  // B: 4-bit, copy i = block 2 wave + i; 3-bit, copy i = 256-byte piece
+  // 6 wave + i of the 8 blocks (three pieces per 768-byte block)
+  uint32_t b_off[C::B_LOADS];
+#pragma unroll
+  for (int i = 0; i < C::B_LOADS; ++i) {
+    if constexpr (BITS == 4) {
+      const int blk = 2 * wave + i;
+      b_off[i] = (uint32_t)(min(nt0 + blk, a.n_tiles - 1) * kbs) * 1024u + 16u * lane;
+    } else {
+      const int piece = 6 * wave + i, blk = piece / 3;
+      b_off[i] = (uint32_t)(min(nt0 + blk, a.n_tiles - 1) * kbs) * 768u + 256u * (piece % 3) + 4u * lane;
+    }
+  }
+  // SS / SZ: column 64 (wave & 1) + lane of the tile (waves 2, 3 repeat 0, 1)
+  const int ncol = min(nt0 * 16 + 64 * (wave & 1) + lane, a.n_tiles * 16 - 1);
+  const uint8_t *ss_src = a.wbase + a.scales_offset + (uint64_t)ncol * gp * 2;
+  const uint32_t *sz_src = (const uint32_t *)(a.wbase + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
+  const int sx_row = 64 * (wave % (BM / 64)) + lane;
+  const float *sx_src = xs + min(m0 + sx_row, a.m - 1);
+
+  auto issue = [&](int kb, int buf) {
+    uint8_t *st = smem + buf * C::STAGE;
+    const uint8_t *xk = x + kb * 256;
+#pragma unroll
+    for (int i = 0; i < C::A_LOADS; ++i)
+      lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_LOADS; ++i) {
+      if constexpr (BITS == 4)
+        lds_dma16(a.wbase + b_off[i] + kb * 1024u, st + C::OFF_B + (2 * wave + i) * 1024);
+      else
+        lds_dma4(a.wbase + b_off[i] + kb * 768u, st + C::OFF_B + (6 * wave + i) * 256);
+    }
+    const int g0 = kb * C::GPB;
+    lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + (wave & 1) * 1024);
+    if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + (wave & 1) * 256);
+#pragma unroll
+    for (int gi = 0; gi < C::GPB; ++gi)
+      lds_dma4(sx_src + (int64_t)(g0 + gi) * xs_rows,
+               st + C::OFF_SX + (gi * BM + 64 * (wave % (BM / 64))) * 4);
+  };
+
+  f32x4 acc[C::MI][4];
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  if (C::STAGES == 3 && kbs > 1) issue(1, 1);
+  for (int kb = 0; kb < kbs; ++kb) {
+    if (C::STAGES == 3 && kb + 1 < kbs) {
+      QG_WAIT_VMCNT(C::LOADS);
+    } else {
+      QG_WAIT_VMCNT(0);
+    }
+    lds_barrier();  // stage kb is in LDS; the buffer of stage kb - 1 is free
+    if (kb + C::STAGES - 1 < kbs) issue(kb + C::STAGES - 1, (kb + C::STAGES - 1) % C::STAGES);
+    const uint8_t *st = smem + (kb % C::STAGES) * C::STAGE;
+
+    // weight operands of the wave's 4 column blocks for the 4 K32 steps
+    u32x4 bw[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int blk = wn * 4 + j;
+      u32x4 v;
+      if constexpr (BITS == 4) {
+        v = *(const u32x4 *)(st + C::OFF_B + blk * 1024 + 16 * lane);
+      } else {
+        const uint32_t *p = (const uint32_t *)(st + C::OFF_B + blk * 768 + 12 * lane);
+        v = u32x4{p[0], p[1], p[2], 0u};
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) bw[j][s] = unpack_br<BITS>(v, s, umask, umagic);
+    }
+#pragma unroll
+    for (int gi = 0; gi < C::GPB; ++gi) {
+      const int gg = kb * C::GPB + gi;
+      float c1[4], zf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = wn * 64 + 16 * j + r16;
+        const uint32_t sb = *(const uint16_t *)(st + C::OFF_SS + col * 16 + 2 * (gg & 7));
+        c1[j] = C::MAG * bf16_bits_to_f32(sb);
+        int z = C::ZSYM;
+        if constexpr (ZP) z = (int)((*(const uint32_t *)(st + C::OFF_SZ + col * 4) >> (4 * (gg & 7))) & 15u);
+        // symmetric formats: the row sums arrive pre-multiplied by -(1 + z / MAG)
+        zf[j] = ZP ? -(1.f + (float)z / C::MAG) : 1.f;
+      }
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int r0 = wm * (BM / 2) + 16 * i;
+        const uint8_t *arow = st + (r0 + r16) * 256;
+        u32x4 af[C::JPG];
+#pragma unroll
+        for (int ss = 0; ss < C::JPG; ++ss)
+          af[ss] = *(const u32x4 *)(arow + 16 * ((4 * (gi * C::JPG + ss) + q) ^ r16));
+        const f32x4 sx = *(const f32x4 *)(st + C::OFF_SX + (gi * BM + r0 + 4 * q) * 4);
+        f32x4 g[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[j] = ZP ? sx * zf[j] : sx;
+#pragma unroll
+        for (int ss = 0; ss < C::JPG; ++ss)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) g[j] = mfma_bf16(af[ss], bw[j][gi * C::JPG + ss], g[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(g[j][e], c1[j], acc[i][j][e]);
+      }
+    }
+  }
+
+  // output: block (i, j) lane holds rows 4q .. 4q + 3 of column r16
+#pragma unroll
+  for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = (nt0 + wn * 4 + j) * 16 + r16;
+      if (col >= a.n) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = m0 + wm * (BM / 2) + 16 * i + 4 * q + e;
+        if (row >= a.m) continue;
+        if (a.otype == QG_O_F32)
+          ((float *)a.y)[(int64_t)row * a.ldy + col] = acc[i][j][e];
+        else
+          ((__bf16 *)a.y)[(int64_t)row * a.ldy + col] = (__bf16)acc[i][j][e];
+      }
+    }
+}
+
+// Group row sums of bf16 X: xs[g * rows + r] = factor * (sum of x[r, g*GROUP ..
+// + GROUP-1]) in fp32.  One wave per row; lane l sums 16-byte chunks l, l + 64,
+// ..., and the GROUP / 8 lanes holding one group's chunks combine by butterfly.
+template <int GROUP>
+__global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *x, int64_t ldx, int rows,
+                                                         int k, float factor, float *xs) {
+  constexpr int CPG = GROUP / 8;  // chunks per group
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const uint16_t *xr = x + (int64_t)row * ldx;
+  const int chunks = k / 8;  // a multiple of 16 (K % 128 == 0)
+  for (int c = lane; c < chunks; c += 64) {
+    const u32x4 v = *(const u32x4 *)(xr + 8 * c);
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s += __uint_as_float(v[e] << 16);
+      s += __uint_as_float(v[e] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int off = 1; off < CPG; off <<= 1) s += __shfl_xor(s, off);
+    if ((lane & (CPG - 1)) == 0) xs[(int64_t)(c / CPG) * rows + row] = s * factor;
+  }
+}
+
+template <int BM, int BITS, bool ZP, int GROUP>
+static hipError_t launch_a16_tiled_t(const GemmArgs &a, float *xs, hipStream_t s) {
+  using C = A16Cfg<BM, BITS, ZP, GROUP>;
+  const int rows_blocks = (a.m + 3) / 4;
+  const float factor = ZP ? 1.f : -(1.f + (float)C::ZSYM / C::MAG);
+  hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3(rows_blocks), dim3(256), 0, s,
+                     (const uint16_t *)a.x, a.ldx, a.m, a.k, factor, xs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int m_tiles = (a.m + BM - 1) / BM;
+  const int n_tiles_wg = (a.n_tiles + 7) / 8;
+  const int total = m_tiles * n_tiles_wg;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const size_t lds = (size_t)C::STAGES * C::STAGE;
+  e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, BITS, ZP, GROUP>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((a16_tiled_kernel<BM, BITS, ZP, GROUP>), dim3(per_xcd * kXcds),
+                     dim3(kA16Threads), lds, s, a, (const float *)xs, a.m);
+  return hipGetLastError();
+}
+
+template <int BM, int BITS, bool ZP>
+static hipError_t launch_group(const GemmArgs &a, int group, float *xs, hipStream_t s) {
+  switch (group) {
+    case 32: return launch_a16_tiled_t<BM, BITS, ZP, 32>(a, xs, s);
+    case 64: return launch_a16_tiled_t<BM, BITS, ZP, 64>(a, xs, s);
+    case 128: return launch_a16_tiled_t<BM, BITS, ZP, 128>(a, xs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BM>
+static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, float *xs, hipStream_t s) {
+  switch (d.wtype) {
+    case QG_W_INT4: return launch_group<BM, 4, false>(a, d.group_size, xs, s);
+    case QG_W_UINT4: return launch_group<BM, 4, true>(a, d.group_size, xs, s);
+    case QG_W_INT3: return launch_group<BM, 3, false>(a, d.group_size, xs, s);
+    case QG_W_UINT3: return launch_group<BM, 3, true>(a, d.group_size, xs, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m) {
+  return align_up((uint64_t)(d.k / d.group_size) * (uint64_t)m * 4, 256);
+}
+
+hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, void *ws,
+                            hipStream_t s) {
+  if (a.k % 128 != 0) return hipErrorInvalidValue;
+  return bm == 256 ? launch_fmt<256>(a, d, (float *)ws, s) : launch_fmt<128>(a, d, (float *)ws, s);
+}
+
+}  // namespace qg

@@ -181,3 +181,59 @@ def test_mx_tiled_identity_rows_exact():
     y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
     for i in range(m):
         assert np.array_equal(y[i].astype(np.float64), wdq[:, (2 * i) % k]), i
+
+
+# ---------------------------------------------------------------------------
+# LDS-tiled bf16-MFMA kernel for the integer formats (M >= 256)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bm", ["256", "128"])
+@pytest.mark.parametrize("wtype", A16)
+@pytest.mark.parametrize("group", [32, 64, 128])
+def test_a16_tiled_formats_and_groups(monkeypatch, bm, wtype, group):
+    """Every integer format and group size through the tiled kernel, with a
+    partial row tile and a partial column tile (N = 200 is not a multiple of
+    the 128-column tile)."""
+    monkeypatch.setenv("QG_TILED_BM", bm)
+    layer = Layer(wtype, 200, 640, group, seed=wtype * 10 + group)
+    m = 300
+    assert f"a16_tiled BM={bm}" in qg.describe_dispatch(layer.w, m)
+    _check(layer, Acts(False, m, 640, seed=m + group), m)
+
+
+@pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (512, 72, 128), (777, 1040, 4096)])
+def test_a16_tiled_ragged(m, n, k):
+    layer = Layer(qg.W_UINT4, n, k, 128, seed=m)
+    assert "a16_tiled" in qg.describe_dispatch(layer.w, m)
+    _check(layer, Acts(False, m, k, seed=m), m)
+
+
+@pytest.mark.parametrize("wtype", A16)
+def test_a16_tiled_identity_rows_exact(wtype):
+    """One-hot X rows through the tiled kernel return Wdq[:, k] bit-exactly."""
+    n, k, m = 136, 640, 320
+    layer = Layer(wtype, n, k, 64, seed=23)
+    wdq = layer.wdq()
+    bits = np.zeros((m, k), np.uint16)
+    cols = (np.arange(m) * 2 + 1) % k
+    bits[np.arange(m), cols] = 0x3F80
+    acts = Acts(False, m, k, values=bits)
+    assert "a16_tiled" in qg.describe_dispatch(layer.w, m)
+    y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
+    for i in range(m):
+        assert np.array_equal(y[i].astype(np.float64), wdq[:, cols[i]]), i
+
+
+@pytest.mark.parametrize("nk", [(14336, 4096), (4096, 14336)])
+def test_w4a16_large_m_full_size_sampled_rows(nk):
+    """(4096, N, K) symmetric INT4, group 128: all outputs computed, 64 sampled
+    rows compared against the oracle."""
+    n, k = nk
+    m = 4096
+    print(f"w4a16 M={m} N={n} K={k}", flush=True)
+    layer = Layer(qg.W_INT4, n, k, 128, seed=17)
+    acts = Acts(False, m, k, seed=17)
+    rows = np.sort(synth.rng(0, 98).choice(m, 64, replace=False))
+    rows[0], rows[-1] = 0, m - 1
+    assert "a16_tiled" in qg.describe_dispatch(layer.w, m)
+    _check(layer, acts, m, rows=rows)
