@@ -201,12 +201,14 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
         xs = hs = None
     y1 = torch.empty((p, n1), dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty((p, n2), dtype=torch.bfloat16, device="cuda")
+    gws = max(qg.moe_workspace_size(up.ws[0], tokens, topk), qg.moe_workspace_size(down.ws[0], tokens, topk))
+    gw = torch.empty(max(gws, 1), dtype=torch.uint8, device="cuda")
     t_up = timed(torch, lambda i: qg.moe_gemm(up.ws[i % copies], x, xs, qg.ROWS_BY_TOKEN, sorted_ids,
                                               offsets, tokens, topk, y1, qg.O_BF16, qg.ROWS_BY_PAIR,
-                                              None, 0, stream), iters, 2)
+                                              gw, gws, stream), iters, 2)
     t_dn = timed(torch, lambda i: qg.moe_gemm(down.ws[i % copies], h, hs, qg.ROWS_BY_PAIR, sorted_ids,
                                               offsets, tokens, topk, y2, qg.O_BF16, qg.ROWS_BY_PAIR,
-                                              None, 0, stream), iters, 2)
+                                              gw, gws, stream), iters, 2)
     t = t_up + t_dn
     flops = 2.0 * p * (n1 * k1 + n2 * k2)
     tflops = flops / (t * 1e-3) / 1e12

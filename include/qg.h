@@ -173,7 +173,8 @@ qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64
                   hipStream_t stream);
 /* (ws, when needed, must hold zeros on entry; see qg_gemm_workspace_size.) */
 
-/* Workspace bytes for qg_moe_sort + qg_moe_gemm with this many tokens. */
+/* Workspace bytes for qg_moe_sort and qg_moe_gemm with this many tokens (one
+ * buffer of this size serves both; its contents on entry do not matter). */
 qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
                                 uint64_t *bytes);
 
@@ -195,6 +196,11 @@ qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, int32_t topk,
  * with row_x given by x_rows (BY_TOKEN: p / topk; BY_PAIR: p; SORTED: the
  * pair's position in sorted_pair_ids) and row_y by y_rows (BY_PAIR or SORTED).
  * x, x_scales, y as in qg_gemm with ldx = K and ldy = N (dense rows).
+ * ws: device, 256-B aligned, at least qg_moe_workspace_size bytes (holds the
+ * tile list of the large-expert kernel and, for integer formats, the group
+ * row sums of x; overwritten by every call, so calls sharing one ws must be
+ * ordered on one stream).
+ * More than 1024 experts: QG_ERR_UNSUPPORTED (here and in qg_moe_sort).
  * Asynchronous on `stream`. */
 qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, int32_t x_rows,
                       const int32_t *sorted_pair_ids, const int32_t *expert_offsets,

@@ -157,6 +157,39 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
   return s;
 }
 
+// MoE: experts with at least this many rows go to the tiled kernels (128-row
+// tiles), the rest to the skinny kernel; 0 = skinny only.  Below ~64 rows a
+// 128-row tile wastes more matrix-core work than re-reading the expert's
+// weights per 16-row tile costs.  QG_MOE_TILED_MIN overrides (0 disables).
+static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
+  const qg_layer_desc &d = w.desc;
+  if (d.k % 128 != 0 || d.num_experts > kMaxExperts) return 0;
+  const bool mx = d.wtype == QG_W_MXFP4;
+  // 32-bit offsets inside the kernels
+  if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
+      (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31))
+    return 0;
+  int min_rows = 64;
+  const char *e = getenv("QG_MOE_TILED_MIN");
+  if (e && *e) min_rows = std::max(0, atoi(e));
+  if (min_rows <= 0 || pairs < min_rows) return 0;
+  return min_rows;
+}
+
+// Tile-list capacity: one tile per 128 rows plus one partial tile per expert
+// that has tiles (at most pairs / min_rows of them).
+static int64_t moe_tiles_cap(const qg_weight &w, int64_t pairs, int min_rows) {
+  return pairs / kMoeTileRows + std::min<int64_t>(w.desc.num_experts, pairs / min_rows) + 1;
+}
+
+// MoE workspace: [tile list][group row sums of X (integer formats)]
+static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_count, int min_rows) {
+  if (min_rows <= 0) return 0;
+  uint64_t b = align_up((uint64_t)(2 + 2 * moe_tiles_cap(w, pairs, min_rows)) * 4, 256);
+  if (w.desc.wtype != QG_W_MXFP4) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
+  return b;
+}
+
 static qg_status check_weight(const qg_weight *w, Layout *L) {
   if (!w || !w->data) return QG_ERR_INVALID_ARGUMENT;
   qg_status st = make_layout(&w->desc, L);
@@ -347,9 +380,9 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
     a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
   }
   if (v.kind == 1)
-    he = launch_mx_tiled(a, v.bn, stream);
+    he = launch_mx_tiled(a, v.bn, false, 0, stream);
   else if (v.kind == 2)
-    he = launch_a16_tiled(a, d, v.bn, ws, stream);
+    he = launch_a16_tiled(a, d, v.bn, false, m, 0, ws, stream);
   else
     he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -361,7 +394,11 @@ extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_token
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
   if (!bytes || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
-  *bytes = align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256);
+  const int64_t pairs = num_tokens * topk;
+  // the sort's need, or the grouped GEMM's with X indexed by pair (the larger
+  // of the two x row counts)
+  *bytes = std::max<uint64_t>(align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256),
+                              moe_ws_bytes(*w, pairs, pairs, moe_tiled_min_rows(*w, pairs, pairs)));
   return QG_OK;
 }
 
@@ -369,8 +406,8 @@ extern "C" qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, in
                                  int32_t num_experts, int32_t *sorted_pair_ids,
                                  int32_t *expert_offsets, void *ws, uint64_t ws_bytes,
                                  hipStream_t stream) {
-  if (num_tokens < 0 || topk <= 0 || num_experts <= 0 || num_experts > 4096)
-    return QG_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || topk <= 0 || num_experts <= 0) return QG_ERR_INVALID_ARGUMENT;
+  if (num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
   if (num_tokens * (int64_t)topk > (1ll << 30)) return QG_ERR_UNSUPPORTED;
   if (!expert_offsets || !ws) return QG_ERR_INVALID_ARGUMENT;
   if (num_tokens > 0 && (!topk_ids || !sorted_pair_ids)) return QG_ERR_INVALID_ARGUMENT;
@@ -385,8 +422,6 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
                                  const int32_t *expert_offsets, int64_t num_tokens, int32_t topk,
                                  void *y, int32_t otype, int32_t y_rows, void *ws,
                                  uint64_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
@@ -395,6 +430,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     return QG_ERR_INVALID_ARGUMENT;
   if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
   if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  if (d.num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
   const int64_t pairs = num_tokens * topk;
   if (pairs > (1ll << 30)) return QG_ERR_UNSUPPORTED;
   if (pairs == 0) return QG_OK;
@@ -406,6 +442,14 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     return QG_ERR_ALIGNMENT;
   const Variant v = select_moe(*w, pairs);
   if (!covers(v, w->k_blocks)) return QG_ERR_UNSUPPORTED;  // K too long for one workgroup
+  const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
+  const int min_rows = moe_tiled_min_rows(*w, pairs, x_rows_count);
+  const uint64_t need = moe_ws_bytes(*w, pairs, x_rows_count, min_rows);
+  if (need > 0) {
+    if (!ws) return QG_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
+    if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
+  }
   GemmArgs a;
   base_args(*w, &a);
   a.x = x;
@@ -420,9 +464,27 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   a.topk = topk;
   a.x_rows = x_rows;
   a.y_rows = y_rows;
+  hipError_t he = hipSuccess;
+  if (min_rows > 0) {
+    // experts with >= min_rows rows: tile list, then the tiled kernel
+    const int64_t cap = moe_tiles_cap(*w, pairs, min_rows);
+    int32_t *tiles = (int32_t *)ws;
+    he = launch_moe_tiles(expert_offsets, d.num_experts, min_rows, kMoeTileRows, (int32_t)pairs,
+                          (int32_t)cap, tiles, stream);
+    if (he != hipSuccess) return hip_status(he);
+    a.tiles = tiles;
+    if (L.is_mx) {
+      he = launch_mx_tiled(a, kMoeTileRows, true, cap, stream);
+    } else {
+      void *xs = (uint8_t *)ws + align_up((uint64_t)(2 + 2 * cap) * 4, 256);
+      he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, xs, stream);
+    }
+    if (he != hipSuccess) return hip_status(he);
+    a.moe_min_rows = min_rows;
+  }
+  // the remaining (small) experts
   const int64_t max_tiles = (pairs + 15) / 16 + d.num_experts;
-  hipError_t he = L.is_mx ? launch_moe_mx(a, d, v, max_tiles, stream)
-                          : launch_moe_a16(a, d, v, max_tiles, stream);
+  he = L.is_mx ? launch_moe_mx(a, d, v, max_tiles, stream) : launch_moe_a16(a, d, v, max_tiles, stream);
   return hip_status(he);
 }
 

@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "qg_internal.h"
+
 namespace qg {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
@@ -129,6 +131,53 @@ __device__ __forceinline__ bool tile_of(int pid, int m_tiles, int n_tiles, int *
   const int r = t % group;
   *tm = first_m + r % gm;
   *tn = r / gm;
+  return true;
+}
+
+// Rows of one tiled-kernel tile.  Dense: rows m0 .. m0 + BM - 1 of X and Y.
+// MoE: sorted positions pos0 .. pos0 + rows - 1 of one expert's segment; the
+// X row of a position follows the x row mode (the token p / topk of pair
+// p = sorted_ids[pos], the pair itself, or the position), the Y row the y row
+// mode.  Rows past the tile's valid rows map to its last valid row, so their
+// loads stay in bounds; their outputs are never stored.
+struct TileRows {
+  int base;  // m0 (dense) or pos0 (MoE)
+  int rows;  // valid rows in the tile
+  bool moe;
+
+  __device__ __forceinline__ int64_t x(const GemmArgs &a, int r) const {
+    const int pos = base + min(r, rows - 1);
+    if (!moe || a.x_rows == QG_ROWS_SORTED) return pos;
+    const int p = a.sorted_ids[pos];
+    return a.x_rows == QG_ROWS_BY_TOKEN ? (int64_t)(p / a.topk) : (int64_t)p;
+  }
+  __device__ __forceinline__ int64_t y(const GemmArgs &a, int r) const {
+    const int pos = base + r;
+    if (!moe || a.y_rows == QG_ROWS_SORTED) return pos;
+    return a.sorted_ids[pos];
+  }
+};
+
+// Workgroup id -> (tile rows, n-tile, weight base) of a tiled kernel; false if
+// the workgroup has no tile.  MoE tiles come from the tile list (see
+// launch_moe_tiles); the raster runs over the list entries.
+template <int BM>
+__device__ __forceinline__ bool tiled_work(const GemmArgs &a, bool moe, int n_tiles_wg, TileRows *tr,
+                                           int *tn, const uint8_t **wexp) {
+  int tm;
+  if (!moe) {
+    if (!tile_of(blockIdx.x, (a.m + BM - 1) / BM, n_tiles_wg, &tm, tn)) return false;
+    *tr = TileRows{tm * BM, min(BM, a.m - tm * BM), false};
+    *wexp = a.wbase;
+    return true;
+  }
+  const int count = a.tiles[0];
+  if (!tile_of(blockIdx.x, count, n_tiles_wg, &tm, tn)) return false;
+  const int e = a.tiles[2 + 2 * tm], pos0 = a.tiles[3 + 2 * tm];
+  const int rows = min(BM, a.offsets[e + 1] - pos0);
+  if (rows <= 0) return false;
+  *tr = TileRows{pos0, rows, true};
+  *wexp = a.wbase + (uint64_t)e * a.expert_stride;
   return true;
 }
 

@@ -106,7 +106,14 @@ struct GemmArgs {
   int32_t topk;
   int32_t x_rows;
   int32_t y_rows;
+  // MoE split between the two kernels: the tiled kernels walk the tile list
+  // [count, 0, (expert, first sorted row) ...] of experts with at least
+  // moe_min_rows rows; the skinny kernel skips those experts (0 = skips none)
+  const int32_t *tiles;
+  int32_t moe_min_rows;
 };
+
+constexpr int kMaxExperts = 1024;  // LDS-resident per-expert tables
 
 // One entry of the tuning table: a kernel variant and its tile parameters.
 struct Variant {
@@ -130,12 +137,20 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
                           int64_t max_tiles, hipStream_t s);
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s);
-hipError_t launch_mx_tiled(const GemmArgs &a, int bm, hipStream_t s);
+// MoE launches of the tiled kernels walk the tile list a.tiles of capacity
+// tiles_cap, cut at kMoeTileRows rows.
+constexpr int kMoeTileRows = 128;
+hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, hipStream_t s);
 // Integer formats at large M: group row sums of X into ws, then the tiled
 // kernel.  ws holds (K / group) * m floats (a16_tiled_ws_bytes).
-hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, void *ws,
-                            hipStream_t s);
+// xs_rows: rows of X (dense: m; MoE: tokens or pairs, by the x row mode).
+hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
+                            int64_t xs_rows, int64_t tiles_cap, void *ws, hipStream_t s);
 uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m);
+// MoE tile list for the tiled kernels (experts with >= min_rows rows, bm-row
+// tiles): tiles[0] = count, then (expert, first sorted row) pairs.
+hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows, int32_t bm,
+                            int32_t pairs, int32_t capacity, int32_t *tiles, hipStream_t s);
 hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,

@@ -51,7 +51,6 @@ __device__ __forceinline__ V load_stream(const V *p) {
 namespace qg {
 
 constexpr int kMaxWaves = 16;
-constexpr int kMaxExperts = 1024;
 
 __device__ __forceinline__ void store_out(void *y, int64_t ldy, int otype, int64_t row, int col,
                                           float v) {
@@ -75,17 +74,21 @@ struct Item {
   int split;   // K split
 };
 
+// 16-row tiles of an expert with c rows for the skinny kernel; experts with
+// at least min_rows rows (min_rows > 0) belong to the tiled kernels.
+__device__ __forceinline__ int skinny_tiles(int c, int min_rows) {
+  return (min_rows > 0 && c >= min_rows) ? 0 : (c + 15) >> 4;
+}
+
 // Exclusive prefix of per-expert 16-row tile counts, in LDS.  Returns total tiles.
-__device__ int moe_tile_prefix(const int32_t *offsets, int experts, int *prefix) {
+__device__ int moe_tile_prefix(const int32_t *offsets, int experts, int min_rows, int *prefix) {
   const int tid = threadIdx.x, nth = blockDim.x;
   __shared__ int part[kMaxWaves * 64 + 1];
   const int per = (experts + nth - 1) / nth;
   const int e0 = tid * per;
   int local = 0;
-  for (int e = e0; e < e0 + per && e < experts; ++e) {
-    const int c = offsets[e + 1] - offsets[e];
-    local += (c + 15) >> 4;
-  }
+  for (int e = e0; e < e0 + per && e < experts; ++e)
+    local += skinny_tiles(offsets[e + 1] - offsets[e], min_rows);
   part[tid] = local;
   __syncthreads();
   if (tid == 0) {
@@ -101,8 +104,7 @@ __device__ int moe_tile_prefix(const int32_t *offsets, int experts, int *prefix)
   int run = part[tid];
   for (int e = e0; e < e0 + per && e < experts; ++e) {
     prefix[e] = run;
-    const int c = offsets[e + 1] - offsets[e];
-    run += (c + 15) >> 4;
+    run += skinny_tiles(offsets[e + 1] - offsets[e], min_rows);
   }
   if (tid == 0) prefix[experts] = part[nth];
   __syncthreads();
@@ -374,7 +376,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
   int total_tiles = 0;
   int64_t total_items = total_items_dense;
   if (moe) {
-    total_tiles = moe_tile_prefix(a.offsets, a.num_experts, prefix);
+    total_tiles = moe_tile_prefix(a.offsets, a.num_experts, a.moe_min_rows, prefix);
     total_items = (int64_t)total_tiles * n_blocks;
   }
 
@@ -540,6 +542,47 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t *ids, int6
   }
 }
 
+// Tile list of the tiled MoE kernels: experts with at least min_rows rows, cut
+// into bm-row tiles.  tiles[0] = count, tiles[1] = 0, then (expert, first
+// sorted row) per tile in expert order; at most `capacity` tiles are written
+// (counts are clamped to [0, pairs], so malformed offsets cannot overrun it).
+__global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t *offsets, int32_t experts,
+                                                         int32_t min_rows, int32_t bm, int32_t pairs,
+                                                         int32_t capacity, int32_t *tiles) {
+  __shared__ int part[1025];
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int per = (experts + nth - 1) / nth;
+  const int e0 = tid * per;
+  auto ntiles = [&](int e) {
+    const int c = min(max(offsets[e + 1] - offsets[e], 0), pairs);
+    return c >= min_rows ? (c + bm - 1) / bm : 0;
+  };
+  int local = 0;
+  for (int e = e0; e < e0 + per && e < experts; ++e) local += ntiles(e);
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < nth; ++t) {
+      const int v = part[t];
+      part[t] = run;
+      run += v;
+    }
+    tiles[0] = min(run, capacity);
+    tiles[1] = 0;
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int e = e0; e < e0 + per && e < experts; ++e) {
+    const int n = ntiles(e), first = offsets[e];
+    for (int t = 0; t < n; ++t, ++run) {
+      if (run >= capacity) return;
+      tiles[2 + 2 * run] = e;
+      tiles[3 + 2 * run] = first + t * bm;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -645,6 +688,13 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s) {
   return launch_moe(a, d, v, max_tiles, s);
+}
+
+hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows, int32_t bm,
+                            int32_t pairs, int32_t capacity, int32_t *tiles, hipStream_t s) {
+  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, experts, min_rows, bm,
+                     pairs, capacity, tiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts, int32_t *sorted,

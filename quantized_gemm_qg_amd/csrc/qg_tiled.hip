@@ -54,7 +54,7 @@ struct MxCfg {
   static constexpr int MB = BM / 32;                   // 16-row blocks per wave
 };
 
-template <int BM>
+template <int BM, bool MOE>
 __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
   using C = MxCfg<BM>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
@@ -64,16 +64,15 @@ __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
 
-  const int m_tiles = (a.m + BM - 1) / BM;
-  const int n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
-  int tm, tn;
-  if (!tile_of(blockIdx.x, m_tiles, n_tiles_wg, &tm, &tn)) return;
-  const int m0 = tm * BM;
+  TileRows tr;
+  int tn;
+  const uint8_t *wexp;
+  if (!tiled_work<BM>(a, MOE, (a.n_tiles * 16 + kTBN - 1) / kTBN, &tr, &tn, &wexp)) return;
   const int nt0 = tn * (kTBN / 16);  // first 16-column n-tile
   const int kbs = a.k_blocks;
   const int kq = a.k >> 5;           // activation scale bytes per row
   const uint8_t *x = (const uint8_t *)a.x;
-  const uint8_t *wsc = a.wbase + a.scales_offset;
+  const uint8_t *wsc = wexp + a.scales_offset;
 
   // per-lane source offsets (32-bit, added to wave-uniform bases at issue)
   uint32_t a_off[C::A_LOADS];
@@ -81,16 +80,16 @@ __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
   for (int i = 0; i < C::A_LOADS; ++i) {
     const int row = 8 * (wave * C::A_LOADS + i) + (lane >> 3);
     const int c = (lane & 7) ^ (row & 7);
-    a_off[i] = (uint32_t)((int64_t)min(m0 + row, a.m - 1) * a.ldx + 16 * c);
+    a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
   }
-  const uint8_t *b_base = a.wbase + 16 * lane;
+  const uint8_t *b_base = wexp + 16 * lane;
   uint32_t b_blk[4];  // first packed block of each of the wave's four n-tiles
 #pragma unroll
   for (int i = 0; i < 4; ++i) b_blk[i] = (uint32_t)min(nt0 + wave * 4 + i, a.n_tiles - 1) * kbs;
   // SA: BM rows of 4 bytes = BM / 64 loads of 256 B; with BM = 128 waves 2 and
   // 3 repeat waves 0 and 1 (same bytes to the same place)
   const int sa_row = (wave % (BM / 64)) * 64 + lane;
-  const uint8_t *sa_src = a.x_scales + (int64_t)min(m0 + sa_row, a.m - 1) * kq;
+  const uint8_t *sa_src = a.x_scales + tr.x(a, sa_row) * kq;
   uint32_t sw_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -176,35 +175,39 @@ __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
       if (col >= a.n) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * (BM / 2) + i * 16 + 4 * q + e;
-        if (row >= a.m) continue;
+        const int r = wm * (BM / 2) + i * 16 + 4 * q + e;
+        if (r >= tr.rows) continue;
+        const int64_t row = tr.y(a, r);
         if (a.otype == QG_O_F32)
-          ((float *)a.y)[(int64_t)row * a.ldy + col] = acc[i][j][e];
+          ((float *)a.y)[row * a.ldy + col] = acc[i][j][e];
         else
-          ((__bf16 *)a.y)[(int64_t)row * a.ldy + col] = (__bf16)acc[i][j][e];
+          ((__bf16 *)a.y)[row * a.ldy + col] = (__bf16)acc[i][j][e];
       }
     }
 }
 
-template <int BM>
-static hipError_t launch_mx_tiled_bm(const GemmArgs &a, hipStream_t s) {
+template <int BM, bool MOE>
+static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
   using C = MxCfg<BM>;
-  const int m_tiles = (a.m + BM - 1) / BM;
-  const int n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
-  const int total = m_tiles * n_tiles_wg;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
+  const int64_t n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
+  const int64_t total = m_tiles * n_tiles_wg;
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)kStages * C::STAGE;
-  hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BM>,
+  hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BM, MOE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mx_tiled_kernel<BM>, dim3(per_xcd * kXcds), dim3(kThreads), lds, s, a);
+  hipLaunchKernelGGL((mx_tiled_kernel<BM, MOE>), dim3((unsigned)(per_xcd * kXcds)), dim3(kThreads),
+                     lds, s, a);
   return hipGetLastError();
 }
 
-// bm: workgroup tile rows (128 or 256); the tile is bm x 256
-hipError_t launch_mx_tiled(const GemmArgs &a, int bm, hipStream_t s) {
+// Dense: bm-row tiles (128 or 256), tiles bm x 256.  MoE: the tile list a.tiles
+// (capacity tiles_cap) of kMoeTileRows-row tiles.
+hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, hipStream_t s) {
   if (a.k % 128 != 0) return hipErrorInvalidValue;
-  return bm == 256 ? launch_mx_tiled_bm<256>(a, s) : launch_mx_tiled_bm<128>(a, s);
+  if (moe) return launch_mx_tiled_bm<kMoeTileRows, true>(a, tiles_cap, s);
+  return bm == 256 ? launch_mx_tiled_bm<256, false>(a, 0, s) : launch_mx_tiled_bm<128, false>(a, 0, s);
 }
 
 }  // namespace qg

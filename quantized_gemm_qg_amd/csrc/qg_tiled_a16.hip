@@ -82,7 +82,7 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BITS, bool ZP, int GROUP>
+template <int BM, int BITS, bool ZP, int GROUP, bool MOE>
 __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, const float *xs,
                                                                  int xs_rows) {
   using C = A16Cfg<BM, BITS, ZP, GROUP>;
@@ -93,11 +93,10 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane >> 4, r16 = lane & 15;
 
-  const int m_tiles = (a.m + BM - 1) / BM;
-  const int n_tiles_wg = (a.n_tiles + 7) / 8;
-  int tm, tn;
-  if (!tile_of(blockIdx.x, m_tiles, n_tiles_wg, &tm, &tn)) return;
-  const int m0 = tm * BM;
+  TileRows tr;
+  int tn;
+  const uint8_t *wexp;
+  if (!tiled_work<BM>(a, MOE, (a.n_tiles + 7) / 8, &tr, &tn, &wexp)) return;
   const int nt0 = tn * 8;
   const int kbs = a.k_blocks, gp = a.groups_padded;
   const uint32_t umask = sgpr_const(BITS == 4 ? 0x00780078u : 0x00700070u);
@@ -112,7 +111,7 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
   for (int i = 0; i < C::A_LOADS; ++i) {
     const int row = 4 * (wave * C::A_LOADS + i) + (lane >> 4);
     const int c = (lane & 15) ^ (row & 15);
-    a_off[i] = (uint32_t)((int64_t)min(m0 + row, a.m - 1) * a.ldx * 2 + 16 * c);
+    a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx * 2 + 16 * c);
   }
   // B: 4-bit, copy i = block 2 wave + i; 3-bit, copy i = 256-byte piece
   // 6 wave + i of the 8 blocks (three pieces per 768-byte block)
@@ -129,10 +128,10 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
   }
   // SS / SZ: column 64 (wave & 1) + lane of the tile (waves 2, 3 repeat 0, 1)
   const int ncol = min(nt0 * 16 + 64 * (wave & 1) + lane, a.n_tiles * 16 - 1);
-  const uint8_t *ss_src = a.wbase + a.scales_offset + (uint64_t)ncol * gp * 2;
-  const uint32_t *sz_src = (const uint32_t *)(a.wbase + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
+  const uint8_t *ss_src = wexp + a.scales_offset + (uint64_t)ncol * gp * 2;
+  const uint32_t *sz_src = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
   const int sx_row = 64 * (wave % (BM / 64)) + lane;
-  const float *sx_src = xs + min(m0 + sx_row, a.m - 1);
+  const float *sx_src = xs + tr.x(a, sx_row);
 
   auto issue = [&](int kb, int buf) {
     uint8_t *st = smem + buf * C::STAGE;
@@ -143,9 +142,9 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
       if constexpr (BITS == 4)
-        lds_dma16(a.wbase + b_off[i] + kb * 1024u, st + C::OFF_B + (2 * wave + i) * 1024);
+        lds_dma16(wexp + b_off[i] + kb * 1024u, st + C::OFF_B + (2 * wave + i) * 1024);
       else
-        lds_dma4(a.wbase + b_off[i] + kb * 768u, st + C::OFF_B + (6 * wave + i) * 256);
+        lds_dma4(wexp + b_off[i] + kb * 768u, st + C::OFF_B + (6 * wave + i) * 256);
     }
     const int g0 = kb * C::GPB;
     lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + (wave & 1) * 1024);
@@ -236,12 +235,13 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
       if (col >= a.n) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = m0 + wm * (BM / 2) + 16 * i + 4 * q + e;
-        if (row >= a.m) continue;
+        const int r = wm * (BM / 2) + 16 * i + 4 * q + e;
+        if (r >= tr.rows) continue;
+        const int64_t row = tr.y(a, r);
         if (a.otype == QG_O_F32)
-          ((float *)a.y)[(int64_t)row * a.ldy + col] = acc[i][j][e];
+          ((float *)a.y)[row * a.ldy + col] = acc[i][j][e];
         else
-          ((__bf16 *)a.y)[(int64_t)row * a.ldy + col] = (__bf16)acc[i][j][e];
+          ((__bf16 *)a.y)[row * a.ldy + col] = (__bf16)acc[i][j][e];
       }
     }
 }
@@ -272,45 +272,49 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *x, int6
   }
 }
 
-template <int BM, int BITS, bool ZP, int GROUP>
-static hipError_t launch_a16_tiled_t(const GemmArgs &a, float *xs, hipStream_t s) {
+template <int BM, int BITS, bool ZP, int GROUP, bool MOE>
+static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t tiles_cap, float *xs,
+                                     hipStream_t s) {
   using C = A16Cfg<BM, BITS, ZP, GROUP>;
-  const int rows_blocks = (a.m + 3) / 4;
   const float factor = ZP ? 1.f : -(1.f + (float)C::ZSYM / C::MAG);
-  hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3(rows_blocks), dim3(256), 0, s,
-                     (const uint16_t *)a.x, a.ldx, a.m, a.k, factor, xs);
+  const int64_t rows_blocks = (xs_rows + 3) / 4;
+  hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3((unsigned)rows_blocks), dim3(256), 0, s,
+                     (const uint16_t *)a.x, a.ldx, (int)xs_rows, a.k, factor, xs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int m_tiles = (a.m + BM - 1) / BM;
-  const int n_tiles_wg = (a.n_tiles + 7) / 8;
-  const int total = m_tiles * n_tiles_wg;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
+  const int64_t n_tiles_wg = (a.n_tiles + 7) / 8;
+  const int64_t total = m_tiles * n_tiles_wg;
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::STAGES * C::STAGE;
-  e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, BITS, ZP, GROUP>,
+  e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, BITS, ZP, GROUP, MOE>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((a16_tiled_kernel<BM, BITS, ZP, GROUP>), dim3(per_xcd * kXcds),
-                     dim3(kA16Threads), lds, s, a, (const float *)xs, a.m);
+  hipLaunchKernelGGL((a16_tiled_kernel<BM, BITS, ZP, GROUP, MOE>), dim3((unsigned)(per_xcd * kXcds)),
+                     dim3(kA16Threads), lds, s, a, (const float *)xs, (int)xs_rows);
   return hipGetLastError();
 }
 
-template <int BM, int BITS, bool ZP>
-static hipError_t launch_group(const GemmArgs &a, int group, float *xs, hipStream_t s) {
+template <int BM, int BITS, bool ZP, bool MOE>
+static hipError_t launch_group(const GemmArgs &a, int group, int64_t xs_rows, int64_t cap, float *xs,
+                               hipStream_t s) {
   switch (group) {
-    case 32: return launch_a16_tiled_t<BM, BITS, ZP, 32>(a, xs, s);
-    case 64: return launch_a16_tiled_t<BM, BITS, ZP, 64>(a, xs, s);
-    case 128: return launch_a16_tiled_t<BM, BITS, ZP, 128>(a, xs, s);
+    case 32: return launch_a16_tiled_t<BM, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, s);
+    case 64: return launch_a16_tiled_t<BM, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, s);
+    case 128: return launch_a16_tiled_t<BM, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int BM>
-static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, float *xs, hipStream_t s) {
+template <int BM, bool MOE>
+static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t xs_rows, int64_t cap,
+                             float *xs, hipStream_t s) {
+  const int g = d.group_size;
   switch (d.wtype) {
-    case QG_W_INT4: return launch_group<BM, 4, false>(a, d.group_size, xs, s);
-    case QG_W_UINT4: return launch_group<BM, 4, true>(a, d.group_size, xs, s);
-    case QG_W_INT3: return launch_group<BM, 3, false>(a, d.group_size, xs, s);
-    case QG_W_UINT3: return launch_group<BM, 3, true>(a, d.group_size, xs, s);
+    case QG_W_INT4: return launch_group<BM, 4, false, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_UINT4: return launch_group<BM, 4, true, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_INT3: return launch_group<BM, 3, false, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_UINT3: return launch_group<BM, 3, true, MOE>(a, g, xs_rows, cap, xs, s);
   }
   return hipErrorInvalidValue;
 }
@@ -319,10 +323,15 @@ uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m) {
   return align_up((uint64_t)(d.k / d.group_size) * (uint64_t)m * 4, 256);
 }
 
-hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, void *ws,
-                            hipStream_t s) {
+// Dense: a.m rows in bm-row tiles.  MoE: the tile list a.tiles (capacity
+// tiles_cap) of 128-row tiles.
+hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
+                            int64_t xs_rows, int64_t tiles_cap, void *ws, hipStream_t s) {
   if (a.k % 128 != 0) return hipErrorInvalidValue;
-  return bm == 256 ? launch_fmt<256>(a, d, (float *)ws, s) : launch_fmt<128>(a, d, (float *)ws, s);
+  float *xs = (float *)ws;
+  if (moe) return launch_fmt<kMoeTileRows, true>(a, d, xs_rows, tiles_cap, xs, s);
+  return bm == 256 ? launch_fmt<256, false>(a, d, xs_rows, 0, xs, s)
+                   : launch_fmt<128, false>(a, d, xs_rows, 0, xs, s);
 }
 
 }  // namespace qg

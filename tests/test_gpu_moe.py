@@ -8,7 +8,7 @@ import torch
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, require_gpu, to_dev
+from gpu_harness import TOL_BF16, Acts, Layer, require_gpu, to_dev, tol_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,10 @@ def run_moe(layer, acts, sorted_ids, offsets, t, topk, x_rows, y_rows, otype):
     p = t * topk
     y = torch.zeros((p, layer.n), dtype=torch.float32 if otype == qg.O_F32 else torch.bfloat16,
                     device="cuda")
-    qg.moe_gemm(layer.w, acts.x, acts.xs, x_rows, sorted_ids, offsets, t, topk, y, otype, y_rows)
+    ws_bytes = qg.moe_workspace_size(layer.w, t, topk)
+    ws = torch.full((max(ws_bytes, 1),), 0x5A, dtype=torch.uint8, device="cuda")  # contents must not matter
+    qg.moe_gemm(layer.w, acts.x, acts.xs, x_rows, sorted_ids, offsets, t, topk, y, otype, y_rows,
+                ws, ws_bytes)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
 
@@ -57,8 +60,12 @@ def moe_reference(layer, xdq, ids, by_token, verbose=False):
     return oracle.moe_gemm(wdq, xdq, ids, rows_by_token=by_token)
 
 
-@pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_MXFP4])
-def test_moe_small_all_row_modes(wtype):
+@pytest.mark.parametrize("tiled_min", ["0", "1", "12"])
+@pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_UINT3, qg.W_MXFP4])
+def test_moe_small_all_row_modes(monkeypatch, wtype, tiled_min):
+    """All row modes, with experts split between the kernels by row count:
+    skinny only (0), tiled only (1: every expert with a row), and mixed (12)."""
+    monkeypatch.setenv("QG_MOE_TILED_MIN", tiled_min)
     t, e, topk, n, k = 37, 16, 4, 80, 640
     g = 32 if wtype == qg.W_MXFP4 else 128
     ids = synth.route(synth.rng(1, wtype), t, e, topk)
@@ -69,7 +76,7 @@ def test_moe_small_all_row_modes(wtype):
     # gate/up style: rows by token
     acts = Acts(mx, t, k, seed=3)
     ref = moe_reference(layer, acts.xdq, ids, True)
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(mx))):
         y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
         assert oracle.normwise_error(y, ref) <= tol
     # down style: rows by pair, output in sorted order
@@ -77,7 +84,7 @@ def test_moe_small_all_row_modes(wtype):
     ref_pair = moe_reference(layer, h.xdq, ids, False)
     y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
     s = sorted_ids.cpu().numpy()
-    assert oracle.normwise_error(y, ref_pair[s]) <= TOL_F32
+    assert oracle.normwise_error(y, ref_pair[s]) <= tol_f32(mx)
     # sorted input rows
     hs = Acts(mx, t * topk, k, seed=4)
     y = run_moe(layer, hs, sorted_ids, offsets, t, topk, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, qg.O_F32)
@@ -85,7 +92,7 @@ def test_moe_small_all_row_modes(wtype):
     inv = np.empty_like(s)
     inv[s] = np.arange(s.size)
     ref2 = np.stack([hs.xdq[inv[p]] @ layer.wdq(int(ids.reshape(-1)[p])).T for p in range(t * topk)])
-    assert oracle.normwise_error(y, ref2) <= TOL_F32
+    assert oracle.normwise_error(y, ref2) <= tol_f32(mx)
 
 
 def test_moe_empty_and_single_row_experts():
@@ -97,7 +104,7 @@ def test_moe_empty_and_single_row_experts():
     check_sort(ids, e, sorted_ids, offsets)
     acts = Acts(False, t, k, seed=7)
     y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, qg.O_F32)
-    assert oracle.normwise_error(y, moe_reference(layer, acts.xdq, ids, True)) <= TOL_F32
+    assert oracle.normwise_error(y, moe_reference(layer, acts.xdq, ids, True)) <= tol_f32(False)
 
 
 def test_moe_sort_zero_tokens_and_out_of_range_ids():
@@ -145,3 +152,72 @@ def test_moe_w4a16_256_experts_t64():
 @pytest.mark.parametrize("tokens", [1, 64])
 def test_moe_w4a8_128_experts_padding_shape(tokens):
     _moe_full(qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens, seed=50)
+
+
+@pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_MXFP4])
+def test_moe_tiled_multi_tile_experts(wtype):
+    """Skewed routing over 8 experts with hundreds of rows each: experts span
+    several 128-row tiles with a partial last tile; small experts stay on the
+    skinny kernel (default split).  N = 200 leaves a partial column tile."""
+    t, e, topk, n, k = 512, 8, 2, 200, 1024
+    g = 32 if wtype == qg.W_MXFP4 else 64
+    mx = wtype == qg.W_MXFP4
+    ids = synth.route(synth.rng(3, wtype), t, e, topk)
+    counts = np.bincount(ids.ravel(), minlength=e)
+    assert counts.max() > 256 and counts.min() < 64, counts
+    layer = Layer(wtype, n, k, g, seed=9, experts=e)
+    sorted_ids, offsets = sort_on_gpu(ids, e, layer)
+    acts = Acts(mx, t, k, seed=10)
+    ref = moe_reference(layer, acts.xdq, ids, True)
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(mx))):
+        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+        assert oracle.normwise_error(y, ref) <= tol
+    h = Acts(mx, t * topk, k, seed=11)
+    y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
+    s = sorted_ids.cpu().numpy()
+    assert oracle.normwise_error(y, moe_reference(layer, h.xdq, ids, False)[s]) <= tol_f32(mx)
+
+
+def _moe_sampled(wtype, experts, topk, n, k, tokens, seed, by_token, n_experts_checked=12):
+    """Full-size grouped GEMM; the oracle checks every pair of a sample of
+    experts (the largest, the smallest and some in between)."""
+    g = 32 if wtype == qg.W_MXFP4 else 128
+    mx = wtype == qg.W_MXFP4
+    ids = synth.route(synth.rng(seed, 1), tokens, experts, topk)
+    counts = np.bincount(ids.ravel(), minlength=experts)
+    active = np.nonzero(counts)[0]
+    order = active[np.argsort(-counts[active], kind="stable")]
+    pick = np.unique(np.concatenate([order[:4], order[-4:],
+                                     order[np.linspace(0, order.size - 1, n_experts_checked - 8).astype(int)]]))
+    print(f"moe wtype={wtype} E={experts} T={tokens} N={n} K={k} active={active.size} "
+          f"max rows={counts.max()} checked experts={pick.tolist()}", flush=True)
+    layer = Layer(wtype, n, k, g, seed=seed, experts=experts, active=active)
+    sorted_ids, offsets = sort_on_gpu(ids, experts, layer)
+    rows = tokens if by_token else tokens * topk
+    acts = Acts(mx, rows, k, seed=seed + 1)
+    y = run_moe(layer, acts, sorted_ids, offsets, tokens, topk,
+                qg.ROWS_BY_TOKEN if by_token else qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR, qg.O_BF16)
+    flat = ids.reshape(-1)
+    worst = 0.0
+    for e in pick:
+        pairs = np.nonzero(flat == e)[0]
+        xr = acts.xdq[pairs // topk if by_token else pairs]
+        ref = oracle.gemm(xr, layer.wdq(int(e)))
+        layer.drop_wdq()
+        err = oracle.normwise_error(y[pairs], ref)
+        worst = max(worst, err)
+        assert err <= TOL_BF16, (e, err)
+    print(f"  worst err={worst:.3e}", flush=True)
+
+
+def test_moe_w4a16_256_experts_t4096_gate_up_sampled():
+    _moe_sampled(qg.W_INT4, 256, 8, 4096, 7168, 4096, seed=60, by_token=True)
+
+
+def test_moe_w4a16_256_experts_t4096_down_sampled():
+    _moe_sampled(qg.W_INT4, 256, 8, 7168, 2048, 4096, seed=61, by_token=False)
+
+
+@pytest.mark.parametrize("nk,by_token", [((1280, 4096), True), ((4096, 640), False)])
+def test_moe_w4a8_128_experts_t4096_sampled(nk, by_token):
+    _moe_sampled(qg.W_MXFP4, 128, 8, nk[0], nk[1], 4096, seed=62, by_token=by_token)
