@@ -135,7 +135,7 @@ def fill_packed_random(qg, torch, w, buf, gen):
             sc[:, :n, :(k % 128) // 32, k // 128] = 120
     else:
         gp, G = w.groups_padded, k // d.group_size
-        s16 = v[:, so:so + n_pad * gp * 2].contiguous().view(torch.int16).view(E, n_pad, gp)
+        s16 = v[:, so:so + n_pad * gp * 2].clone().view(torch.int16).view(E, n_pad, gp)
         vals = (torch.randn((E, n, G), device="cuda", generator=gen) * 0.02).abs()
         s16[:, :n, :G] = vals.to(torch.bfloat16).view(torch.int16)
         v[:, so:so + n_pad * gp * 2] = s16.view(E, -1).view(torch.uint8)

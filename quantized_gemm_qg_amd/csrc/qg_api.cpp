@@ -176,6 +176,12 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
   return min_rows;
 }
 
+// Raster group of the tiled MoE launches (QG_MOE_GROUP_M overrides).
+static int moe_group_m() {
+  const char *e = getenv("QG_MOE_GROUP_M");
+  return (e && atoi(e) >= 1 && atoi(e) <= 64) ? atoi(e) : 1;
+}
+
 // Tile-list capacity: one tile per 128 rows plus one partial tile per expert
 // that has tiles (at most pairs / min_rows of them).
 static int64_t moe_tiles_cap(const qg_weight &w, int64_t pairs, int min_rows) {
@@ -242,6 +248,9 @@ static void base_args(const qg_weight &w, GemmArgs *a) {
   a->n = (int32_t)w.desc.n;
   a->k = (int32_t)w.desc.k;
   a->splits = 1;
+  // raster group of the dense tiled launches (QG_GROUP_M overrides)
+  const char *g = getenv("QG_GROUP_M");
+  a->group_m = (g && atoi(g) >= 1 && atoi(g) <= 64) ? atoi(g) : 4;
 }
 
 }  // namespace qg
@@ -473,6 +482,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
                           (int32_t)cap, tiles, stream);
     if (he != hipSuccess) return hip_status(he);
     a.tiles = tiles;
+    a.group_m = moe_group_m();
     if (L.is_mx) {
       he = launch_mx_tiled(a, kMoeTileRows, true, cap, stream);
     } else {

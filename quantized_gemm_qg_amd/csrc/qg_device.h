@@ -112,26 +112,52 @@ __device__ __forceinline__ void lds_dma4(const void *g, void *l) {
 // s_waitcnt with vmcnt <= n (n <= 63), expcnt and lgkmcnt unconstrained
 #define QG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-constexpr int kXcds = 8;    // L2 domains; workgroup ids are dealt round-robin over them
-constexpr int kGroupM = 4;  // m-tiles per raster group
+constexpr int kXcds = 8;  // L2 domains; workgroup ids are dealt round-robin over them
 
 // Workgroup id -> (m-tile, n-tile).  Each XCD gets a contiguous range of a
-// raster that walks kGroupM m-tiles across all n-tiles, so the tiles running
+// raster that walks group_m m-tiles across all n-tiles, so the tiles running
 // together on one XCD share activation rows and weight columns in its L2.
 // Returns false for ids past the last tile (the grid is rounded up to a
-// multiple of kXcds).
-__device__ __forceinline__ bool tile_of(int pid, int m_tiles, int n_tiles, int *tm, int *tn) {
+// multiple of kXcds, and MoE grids cover the tile list's capacity).
+__device__ __forceinline__ bool tile_of(int pid, int m_tiles, int n_tiles, int group_m, int *tm,
+                                        int *tn) {
   const int total = m_tiles * n_tiles;
   const int per_xcd = (total + kXcds - 1) / kXcds;
+  // one-to-one only for pid / kXcds < per_xcd; larger grids (MoE launches
+  // sized for the tile list's capacity) must not revisit tiles
+  if (pid / kXcds >= per_xcd) return false;
   const int t = (pid % kXcds) * per_xcd + pid / kXcds;
   if (t >= total) return false;
-  const int group = kGroupM * n_tiles;
-  const int first_m = (t / group) * kGroupM;
-  const int gm = min(kGroupM, m_tiles - first_m);
+  const int group = group_m * n_tiles;
+  const int first_m = (t / group) * group_m;
+  const int gm = min(group_m, m_tiles - first_m);
   const int r = t % group;
   *tm = first_m + r % gm;
   *tn = r / gm;
   return true;
+}
+
+// Exclusive prefix sum of v over the workgroup (blockDim.x a multiple of 64,
+// at most 16 waves); *total gets the sum.  wave_tot: 16 ints of LDS.
+__device__ __forceinline__ int block_scan_excl(int v, int *wave_tot, int *total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = wave_tot[w];
+    base += w < wave ? t : 0;
+    tot += t;
+  }
+  __syncthreads();  // wave_tot may be reused
+  *total = tot;
+  return base + x - v;
 }
 
 // Rows of one tiled-kernel tile.  Dense: rows m0 .. m0 + BM - 1 of X and Y.
@@ -166,19 +192,94 @@ __device__ __forceinline__ bool tiled_work(const GemmArgs &a, bool moe, int n_ti
                                            int *tn, const uint8_t **wexp) {
   int tm;
   if (!moe) {
-    if (!tile_of(blockIdx.x, (a.m + BM - 1) / BM, n_tiles_wg, &tm, tn)) return false;
+    if (!tile_of(blockIdx.x, (a.m + BM - 1) / BM, n_tiles_wg, a.group_m, &tm, tn)) return false;
     *tr = TileRows{tm * BM, min(BM, a.m - tm * BM), false};
     *wexp = a.wbase;
     return true;
   }
   const int count = a.tiles[0];
-  if (!tile_of(blockIdx.x, count, n_tiles_wg, &tm, tn)) return false;
+  if (!tile_of(blockIdx.x, count, n_tiles_wg, a.group_m, &tm, tn)) return false;
   const int e = a.tiles[2 + 2 * tm], pos0 = a.tiles[3 + 2 * tm];
   const int rows = min(BM, a.offsets[e + 1] - pos0);
   if (rows <= 0) return false;
   *tr = TileRows{pos0, rows, true};
   *wexp = a.wbase + (uint64_t)e * a.expert_stride;
   return true;
+}
+
+// Epilogue of the tiled kernels: a wave's (16 MI) x (16 NJ) accumulator tile
+// (C layout: block (i, j), lane (q, r) holds rows 4q..4q+3 of column r) goes
+// out through a wave-private LDS buffer, 16 rows at a time, so that every
+// lane stores 16 contiguous bytes of one output row (the C layout alone
+// would give 2- or 4-byte stores, 32 bytes per row per instruction).  The
+// wave's output row indices are gathered into LDS first, all loads before
+// the first store (MoE rows come from the sorted pair list, and a load after
+// a store to y could not be hoisted above it).  Rows at or past tr.rows and
+// columns at or past N are not stored.  `lds` must hold store_tile_lds_bytes
+// and may overlap nothing another wave still reads.
+template <int MI, int NJ>
+constexpr int store_tile_lds_bytes() {
+  return 16 * (16 * NJ * 4 + 16) + 16 * MI * 4;
+}
+
+template <int MI, int NJ, typename F>
+__device__ __forceinline__ void store_tile(const GemmArgs &a, const TileRows &tr, F &&acc_at,
+                                           int row0, int col0, uint8_t *lds) {
+  constexpr int WN = 16 * NJ;  // columns of the wave tile
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, r16 = lane & 15;
+  const bool f32 = a.otype == QG_O_F32;
+  const int el = f32 ? 4 : 2;
+  const int pitch = WN * el + 16;           // padded row pitch (bytes)
+  const int cpr = WN * el / 16;             // 16-byte chunks per row
+  const int rows_per_pass = 64 / cpr;
+  const bool vec16 = ((a.ldy * el) & 15) == 0;  // y itself is 16-byte aligned
+  int *yrow = (int *)(lds + 16 * (WN * 4 + 16));  // [16 MI] output rows of the wave
+#pragma unroll
+  for (int t = 0; t < (16 * MI + 63) / 64; ++t) {
+    const int r = 64 * t + lane;
+    if (r < 16 * MI) yrow[r] = row0 + r < tr.rows ? (int)tr.y(a, row0 + r) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const f32x4 v = acc_at(i, j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        uint8_t *p = lds + (4 * q + e) * pitch + (16 * j + r16) * el;
+        if (f32)
+          *(float *)p = v[e];
+        else
+          *(__bf16 *)p = (__bf16)v[e];
+      }
+    }
+    // the wave's own LDS accesses complete in order; this keeps the compiler
+    // from moving the reads above the writes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int pass = 0; pass < 16 / rows_per_pass; ++pass) {
+      const int rr = pass * rows_per_pass + lane / cpr, c = lane % cpr;
+      const u32x4 v = *(const u32x4 *)(lds + rr * pitch + 16 * c);
+      const int yr = yrow[16 * i + rr];
+      const int col = col0 + c * (16 / el);
+      if (yr >= 0 && col < a.n) {
+        uint8_t *dst = (uint8_t *)a.y + ((int64_t)yr * a.ldy + col) * el;
+        if (col + 16 / el <= a.n) {
+          if (vec16) {
+            *(u32x4 *)dst = v;
+          } else {  // rows only 4-byte aligned (ldy * elem size not a multiple of 16)
+            uint32_t *d4 = (uint32_t *)dst;
+            d4[0] = v.x; d4[1] = v.y; d4[2] = v.z; d4[3] = v.w;
+          }
+        } else {  // right edge of the matrix: element by element
+          const uint8_t *src = (const uint8_t *)&v;
+          for (int b = 0; b < (a.n - col) * el; ++b) dst[b] = src[b];
+        }
+      }
+    }
+    asm volatile("" ::: "memory");  // next block's writes stay below these reads
+  }
 }
 
 }  // namespace qg

@@ -111,6 +111,8 @@ struct GemmArgs {
   // moe_min_rows rows; the skinny kernel skips those experts (0 = skips none)
   const int32_t *tiles;
   int32_t moe_min_rows;
+  // tiled kernels: m-tiles per raster group (see tile_of)
+  int32_t group_m;
 };
 
 constexpr int kMaxExperts = 1024;  // LDS-resident per-expert tables

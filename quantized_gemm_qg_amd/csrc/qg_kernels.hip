@@ -83,32 +83,21 @@ __device__ __forceinline__ int skinny_tiles(int c, int min_rows) {
 // Exclusive prefix of per-expert 16-row tile counts, in LDS.  Returns total tiles.
 __device__ int moe_tile_prefix(const int32_t *offsets, int experts, int min_rows, int *prefix) {
   const int tid = threadIdx.x, nth = blockDim.x;
-  __shared__ int part[kMaxWaves * 64 + 1];
+  __shared__ int wave_tot[kMaxWaves];
   const int per = (experts + nth - 1) / nth;
   const int e0 = tid * per;
   int local = 0;
   for (int e = e0; e < e0 + per && e < experts; ++e)
     local += skinny_tiles(offsets[e + 1] - offsets[e], min_rows);
-  part[tid] = local;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < nth; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
-    }
-    part[nth] = run;
-  }
-  __syncthreads();
-  int run = part[tid];
+  int total;
+  int run = block_scan_excl(local, wave_tot, &total);
   for (int e = e0; e < e0 + per && e < experts; ++e) {
     prefix[e] = run;
     run += skinny_tiles(offsets[e + 1] - offsets[e], min_rows);
   }
-  if (tid == 0) prefix[experts] = part[nth];
+  if (tid == 0) prefix[experts] = total;
   __syncthreads();
-  return prefix[experts];
+  return total;
 }
 
 __device__ __forceinline__ Item decode_item(const GemmArgs &a, bool moe, int64_t item,
@@ -549,7 +538,7 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t *ids, int6
 __global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t *offsets, int32_t experts,
                                                          int32_t min_rows, int32_t bm, int32_t pairs,
                                                          int32_t capacity, int32_t *tiles) {
-  __shared__ int part[1025];
+  __shared__ int wave_tot[16];
   const int tid = threadIdx.x, nth = blockDim.x;
   const int per = (experts + nth - 1) / nth;
   const int e0 = tid * per;
@@ -559,20 +548,12 @@ __global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t *offsets,
   };
   int local = 0;
   for (int e = e0; e < e0 + per && e < experts; ++e) local += ntiles(e);
-  part[tid] = local;
-  __syncthreads();
+  int total;
+  int run = block_scan_excl(local, wave_tot, &total);
   if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < nth; ++t) {
-      const int v = part[t];
-      part[t] = run;
-      run += v;
-    }
-    tiles[0] = min(run, capacity);
+    tiles[0] = min(total, capacity);
     tiles[1] = 0;
   }
-  __syncthreads();
-  int run = part[tid];
   for (int e = e0; e < e0 + per && e < experts; ++e) {
     const int n = ntiles(e), first = offsets[e];
     for (int t = 0; t < n; ++t, ++run) {

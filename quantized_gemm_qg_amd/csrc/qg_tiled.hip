@@ -166,24 +166,12 @@ __global__ __launch_bounds__(kThreads) void mx_tiled_kernel(GemmArgs a) {
     }
   }
 
-  // output: block (i, j) lane holds rows 4q..4q+3 of column r16
-#pragma unroll
-  for (int i = 0; i < C::MB; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = (nt0 + wn * 8 + j) * 16 + r16;
-      if (col >= a.n) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = wm * (BM / 2) + i * 16 + 4 * q + e;
-        if (r >= tr.rows) continue;
-        const int64_t row = tr.y(a, r);
-        if (a.otype == QG_O_F32)
-          ((float *)a.y)[row * a.ldy + col] = acc[i][j][e];
-        else
-          ((__bf16 *)a.y)[row * a.ldy + col] = (__bf16)acc[i][j][e];
-      }
-    }
+  // output through LDS (the ring is free once every wave is past its last stage)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  store_tile<C::MB, 8>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / 2),
+                       (nt0 + wn * 8) * 16, smem + wave * store_tile_lds_bytes<C::MB, 8>());
 }
 
 template <int BM, bool MOE>

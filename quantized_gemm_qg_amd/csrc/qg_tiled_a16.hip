@@ -23,18 +23,21 @@
 //
 // Tiling: a workgroup of 4 waves (2 x 2) computes a BM x 128 tile of Y, each
 // wave (BM / 2) x 64 as (BM / 32) x 4 blocks of 16 x 16.  K advances 128 per
-// stage; one stage holds
+// stage; one step uses
 //   A   BM rows x 128 bf16 (256 B per row, 16-byte chunks XOR-swizzled by
 //       the row's low 4 bits so the 16 rows of a fragment read hit distinct
 //       banks),
+//   SX  the group row sums of the tile's rows for this step's groups,
 //   B   the 8 packed 16 x 128 blocks of the tile's columns, copied verbatim,
 //   SS  per column the 16-byte run of bf16 scales holding this step's groups,
-//   SZ  per column the dword of zero-point nibbles (formats with zero points),
-//   SX  the group row sums of the tile's rows for this step's groups.
-// Stages are filled straight from global memory with global_load_lds (no
-// register staging) into a 2-deep (BM = 256) or 3-deep (BM = 128) ring; every
-// wave issues the same number of loads per stage, so "stage kb has landed" is
-// an explicit vmcnt wait plus a workgroup barrier.  The workgroup order is the
+//   SZ  per column the dword of zero-point nibbles (formats with zero points).
+// A and SX fill one ring, B, SS and SZ another, both straight from global
+// memory with global_load_lds (no register staging).  The activation ring is
+// 2 (BM = 256) or 3 (BM = 128) stages deep; the weight ring, whose bytes come
+// from HBM with little reuse when every expert has its own weights, runs as
+// deep as LDS allows (up to 5 stages ahead).  Every wave issues the same number
+// of loads per stage, so "stage kb has landed" is an explicit vmcnt wait plus
+// a workgroup barrier.  The workgroup order is the
 // XCD-aware raster of the MX tiled kernel.
 #include <hip/hip_runtime.h>
 
@@ -53,24 +56,41 @@ struct A16Cfg {
   static constexpr int BB = 64 * LB;              // packed bytes per 16 x 128 block
   static constexpr int GPB = 128 / GROUP;         // groups per 128-K step
   static constexpr int JPG = GROUP / 32;          // K32 MFMA steps per group
+  // activation ring stage: A tile, then the group row sums
   static constexpr int A = BM * 256;
+  static constexpr int SX = GPB * BM * 4;
+  static constexpr int A_STAGE = A + SX;
+  // weight ring stage: packed blocks, scales, zero points
   static constexpr int B = 8 * BB;
   static constexpr int SS = kA16BN * 16;
   static constexpr int SZ = ZP ? kA16BN * 4 : 0;
-  static constexpr int SX = GPB * BM * 4;
-  static constexpr int OFF_B = A;
-  static constexpr int OFF_SS = OFF_B + B;
+  static constexpr int OFF_SS = B;
   static constexpr int OFF_SZ = OFF_SS + SS;
-  static constexpr int OFF_SX = OFF_SZ + SZ;
-  static constexpr int STAGE = OFF_SX + SX;
-  static constexpr int STAGES = 3 * STAGE <= kLdsBytes ? 3 : 2;
-  static constexpr int A_LOADS = BM / 16;             // 1-KB copies of A per wave
+  static constexpr int B_STAGE = OFF_SZ + SZ;
+  // ring depths: the weights come from HBM with little reuse across
+  // workgroups (MoE experts), so their ring runs as deep as LDS allows
+  static constexpr int NA = 3 * A_STAGE + 2 * B_STAGE <= kLdsBytes ? 3 : 2;
+  static constexpr int NB_FIT = (kLdsBytes - NA * A_STAGE) / B_STAGE;
+  static constexpr int NB = NB_FIT > 6 ? 6 : NB_FIT;
+  static constexpr int OFF_BRING = NA * A_STAGE;
+  static constexpr int LDS = NA * A_STAGE + NB * B_STAGE;
+  // loads per wave and stage
+  static constexpr int A_LOADS = BM / 16;             // 1-KB copies of A
+  static constexpr int A_ISSUE = A_LOADS + GPB;
   static constexpr int B_LOADS = BITS == 4 ? 2 : 6;   // 1-KB (4-bit) or 256-B (3-bit) copies
-  static constexpr int LOADS = A_LOADS + B_LOADS + 1 + (ZP ? 1 : 0) + GPB;
+  static constexpr int B_ISSUE = B_LOADS + 1 + (ZP ? 1 : 0);
+  // Each step issues its activation loads, then its weight loads.  In steady
+  // state, the loads issued after the later of stage kb's two groups: stage
+  // kb's weights went out in an earlier step than its activations when the
+  // weight ring is deeper (followed by that step's weight loads), in the same
+  // step otherwise.
+  static constexpr int AFTER_A = (NB > NA ? B_ISSUE : 0) + (NA - 2) * (A_ISSUE + B_ISSUE);
   static constexpr int MI = BM / 32;                  // 16-row blocks per wave
   static constexpr float MAG = BITS == 4 ? 16.f : 8.f;
   static constexpr int ZSYM = BITS == 4 ? 8 : 4;
-  static_assert(2 * STAGE <= kLdsBytes, "stage does not fit twice in LDS");
+  static_assert(NB >= 2 && NB >= NA, "weight ring too shallow");
+  static_assert(LDS <= kLdsBytes, "rings exceed LDS");
+  static_assert(AFTER_A <= 63, "vmcnt range");
 };
 
 // Workgroup barrier that the compiler may not move LDS accesses across; the
@@ -133,26 +153,29 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
   const int sx_row = 64 * (wave % (BM / 64)) + lane;
   const float *sx_src = xs + tr.x(a, sx_row);
 
-  auto issue = [&](int kb, int buf) {
-    uint8_t *st = smem + buf * C::STAGE;
+  auto issue_a = [&](int kb) {
+    uint8_t *st = smem + (kb % C::NA) * C::A_STAGE;
     const uint8_t *xk = x + kb * 256;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
 #pragma unroll
+    for (int gi = 0; gi < C::GPB; ++gi)
+      lds_dma4(sx_src + (int64_t)(kb * C::GPB + gi) * xs_rows,
+               st + C::A + (gi * BM + 64 * (wave % (BM / 64))) * 4);
+  };
+  auto issue_b = [&](int kb) {
+    uint8_t *st = smem + C::OFF_BRING + (kb % C::NB) * C::B_STAGE;
+#pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
       if constexpr (BITS == 4)
-        lds_dma16(wexp + b_off[i] + kb * 1024u, st + C::OFF_B + (2 * wave + i) * 1024);
+        lds_dma16(wexp + b_off[i] + kb * 1024u, st + (2 * wave + i) * 1024);
       else
-        lds_dma4(wexp + b_off[i] + kb * 768u, st + C::OFF_B + (6 * wave + i) * 256);
+        lds_dma4(wexp + b_off[i] + kb * 768u, st + (6 * wave + i) * 256);
     }
     const int g0 = kb * C::GPB;
     lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + (wave & 1) * 1024);
     if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + (wave & 1) * 256);
-#pragma unroll
-    for (int gi = 0; gi < C::GPB; ++gi)
-      lds_dma4(sx_src + (int64_t)(g0 + gi) * xs_rows,
-               st + C::OFF_SX + (gi * BM + 64 * (wave % (BM / 64))) * 4);
   };
 
   f32x4 acc[C::MI][4];
@@ -161,17 +184,28 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0, 0);
-  if (C::STAGES == 3 && kbs > 1) issue(1, 1);
+  // prologue: activations NA - 1 stages ahead, weights NB - 1 stages ahead
+  for (int s = 0; s < C::NB - 1; ++s) {
+    if (s < C::NA - 1 && s < kbs) issue_a(s);
+    if (s < kbs) issue_b(s);
+  }
   for (int kb = 0; kb < kbs; ++kb) {
-    if (C::STAGES == 3 && kb + 1 < kbs) {
-      QG_WAIT_VMCNT(C::LOADS);
+    // once at most AFTER_A loads are outstanding, both groups of stage kb have
+    // landed (memory counters retire in issue order).  Near the end fewer
+    // loads follow, so the wait is tightened, never loosened; in the prologue
+    // more loads follow, so it is conservative.
+    if (kb + C::NB - 2 < kbs) {
+      QG_WAIT_VMCNT(C::AFTER_A);
+    } else if (C::NA == 3 && kb + 1 < kbs) {
+      QG_WAIT_VMCNT(C::A_ISSUE);
     } else {
       QG_WAIT_VMCNT(0);
     }
-    lds_barrier();  // stage kb is in LDS; the buffer of stage kb - 1 is free
-    if (kb + C::STAGES - 1 < kbs) issue(kb + C::STAGES - 1, (kb + C::STAGES - 1) % C::STAGES);
-    const uint8_t *st = smem + (kb % C::STAGES) * C::STAGE;
+    lds_barrier();  // stage kb is in LDS; the buffers of stage kb - 1 are free
+    if (kb + C::NA - 1 < kbs) issue_a(kb + C::NA - 1);
+    if (kb + C::NB - 1 < kbs) issue_b(kb + C::NB - 1);
+    const uint8_t *st = smem + (kb % C::NA) * C::A_STAGE;
+    const uint8_t *sb = smem + C::OFF_BRING + (kb % C::NB) * C::B_STAGE;
 
     // weight operands of the wave's 4 column blocks for the 4 K32 steps
     u32x4 bw[4][4];
@@ -180,9 +214,9 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
       const int blk = wn * 4 + j;
       u32x4 v;
       if constexpr (BITS == 4) {
-        v = *(const u32x4 *)(st + C::OFF_B + blk * 1024 + 16 * lane);
+        v = *(const u32x4 *)(sb + blk * 1024 + 16 * lane);
       } else {
-        const uint32_t *p = (const uint32_t *)(st + C::OFF_B + blk * 768 + 12 * lane);
+        const uint32_t *p = (const uint32_t *)(sb + blk * 768 + 12 * lane);
         v = u32x4{p[0], p[1], p[2], 0u};
       }
 #pragma unroll
@@ -195,10 +229,10 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = wn * 64 + 16 * j + r16;
-        const uint32_t sb = *(const uint16_t *)(st + C::OFF_SS + col * 16 + 2 * (gg & 7));
-        c1[j] = C::MAG * bf16_bits_to_f32(sb);
+        const uint32_t sbits = *(const uint16_t *)(sb + C::OFF_SS + col * 16 + 2 * (gg & 7));
+        c1[j] = C::MAG * bf16_bits_to_f32(sbits);
         int z = C::ZSYM;
-        if constexpr (ZP) z = (int)((*(const uint32_t *)(st + C::OFF_SZ + col * 4) >> (4 * (gg & 7))) & 15u);
+        if constexpr (ZP) z = (int)((*(const uint32_t *)(sb + C::OFF_SZ + col * 4) >> (4 * (gg & 7))) & 15u);
         // symmetric formats: the row sums arrive pre-multiplied by -(1 + z / MAG)
         zf[j] = ZP ? -(1.f + (float)z / C::MAG) : 1.f;
       }
@@ -210,7 +244,7 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
 #pragma unroll
         for (int ss = 0; ss < C::JPG; ++ss)
           af[ss] = *(const u32x4 *)(arow + 16 * ((4 * (gi * C::JPG + ss) + q) ^ r16));
-        const f32x4 sx = *(const f32x4 *)(st + C::OFF_SX + (gi * BM + r0 + 4 * q) * 4);
+        const f32x4 sx = *(const f32x4 *)(st + C::A + (gi * BM + r0 + 4 * q) * 4);
         f32x4 g[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) g[j] = ZP ? sx * zf[j] : sx;
@@ -226,24 +260,10 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
     }
   }
 
-  // output: block (i, j) lane holds rows 4q .. 4q + 3 of column r16
-#pragma unroll
-  for (int i = 0; i < C::MI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = (nt0 + wn * 4 + j) * 16 + r16;
-      if (col >= a.n) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = wm * (BM / 2) + 16 * i + 4 * q + e;
-        if (r >= tr.rows) continue;
-        const int64_t row = tr.y(a, r);
-        if (a.otype == QG_O_F32)
-          ((float *)a.y)[row * a.ldy + col] = acc[i][j][e];
-        else
-          ((__bf16 *)a.y)[row * a.ldy + col] = (__bf16)acc[i][j][e];
-      }
-    }
+  // output through LDS (the ring is free once every wave is past its last stage)
+  lds_barrier();
+  store_tile<C::MI, 4>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / 2),
+                       (nt0 + wn * 4) * 16, smem + wave * store_tile_lds_bytes<C::MI, 4>());
 }
 
 // Group row sums of bf16 X: xs[g * rows + r] = factor * (sum of x[r, g*GROUP ..
@@ -286,7 +306,7 @@ static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t
   const int64_t n_tiles_wg = (a.n_tiles + 7) / 8;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)C::STAGES * C::STAGE;
+  const size_t lds = (size_t)C::LDS;
   e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, BITS, ZP, GROUP, MOE>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

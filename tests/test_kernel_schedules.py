@@ -1,0 +1,90 @@
+"""Host-side replays of the tiled kernels' work distribution and pipeline
+waits (CPU).  They restate, in Python, the index arithmetic of tile_of and
+the issue/wait schedule of the integer-format tiled kernel, and check the
+invariants those rely on: every tile is computed exactly once for any grid at
+least as large as the live tile count, and every wait leaves the stage about
+to be used complete.  A change to either piece of device code must keep these
+invariants; update the replay with it."""
+import itertools
+
+XCDS = 8
+LDS = 160 * 1024
+
+
+def tile_of(pid, m_tiles, n_tiles, group_m):
+    total = m_tiles * n_tiles
+    per = (total + XCDS - 1) // XCDS
+    if pid // XCDS >= per:
+        return None
+    t = (pid % XCDS) * per + pid // XCDS
+    if t >= total:
+        return None
+    group = group_m * n_tiles
+    first = (t // group) * group_m
+    gm = min(group_m, m_tiles - first)
+    r = t % group
+    return first + r % gm, r // gm
+
+
+def test_raster_visits_every_tile_once_for_oversized_grids():
+    for m, n, gm, extra in itertools.product([1, 2, 3, 7, 32, 33, 264], [1, 3, 8, 24, 32, 112],
+                                             [1, 4, 8], [0, 1, 300]):
+        grid = (((m + extra) * n + XCDS - 1) // XCDS) * XCDS
+        live = [s for s in (tile_of(p, m, n, gm) for p in range(grid)) if s is not None]
+        assert len(live) == m * n and len(set(live)) == m * n, (m, n, gm, extra)
+        assert all(0 <= a < m and 0 <= b < n for a, b in live)
+
+
+def a16_rings(bm, bits, zp, group):
+    gpb = 128 // group
+    a_stage = bm * 256 + gpb * bm * 4
+    b_stage = 8 * 64 * (16 if bits == 4 else 12) + 128 * 16 + (128 * 4 if zp else 0)
+    na = 3 if 3 * a_stage + 2 * b_stage <= LDS else 2
+    nb = min(6, (LDS - na * a_stage) // b_stage)
+    a_issue = bm // 16 + gpb
+    b_issue = (2 if bits == 4 else 6) + 1 + (1 if zp else 0)
+    after = (b_issue if nb > na else 0) + (na - 2) * (a_issue + b_issue)
+    return na, nb, a_issue, b_issue, after, na * a_stage + nb * b_stage
+
+
+def test_a16_tiled_ring_waits_cover_each_stage():
+    for bm, bits, zp, group in itertools.product([128, 256], [3, 4], [False, True], [32, 64, 128]):
+        na, nb, ai, bi, after, lds = a16_rings(bm, bits, zp, group)
+        assert 2 <= na <= nb and lds <= LDS and after <= 63
+        for kbs in range(1, 13):
+            seq = []
+            for s in range(nb - 1):
+                if s < na - 1 and s < kbs:
+                    seq += [("A", s)] * ai
+                if s < kbs:
+                    seq += [("B", s)] * bi
+            for kb in range(kbs):
+                if kb + nb - 2 < kbs:
+                    w = after
+                elif na == 3 and kb + 1 < kbs:
+                    w = ai
+                else:
+                    w = 0
+                outstanding = seq[len(seq) - w:] if w else []
+                assert ("A", kb) in seq and ("B", kb) in seq
+                assert ("A", kb) not in outstanding and ("B", kb) not in outstanding, (bm, bits, zp, group, kbs, kb)
+                if kb + na - 1 < kbs:
+                    seq += [("A", kb + na - 1)] * ai
+                if kb + nb - 1 < kbs:
+                    seq += [("B", kb + nb - 1)] * bi
+
+
+def test_moe_tile_list_capacity_bounds_the_tiles():
+    """tiles <= pairs / 128 + min(E, pairs / min_rows) + 1 for any split of the
+    pairs over experts (one partial tile per expert that has tiles)."""
+    import numpy as np
+    r = np.random.default_rng(0)
+    for _ in range(200):
+        e = int(r.integers(1, 300))
+        pairs = int(r.integers(1, 40000))
+        min_rows = int(r.choice([1, 12, 64]))
+        cuts = np.sort(r.integers(0, pairs + 1, e - 1))
+        counts = np.diff(np.concatenate([[0], cuts, [pairs]]))
+        tiles = sum(-(-c // 128) for c in counts if c >= min_rows)
+        cap = pairs // 128 + min(e, pairs // min_rows) + 1
+        assert tiles <= cap
