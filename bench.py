@@ -245,6 +245,61 @@ def cpu_baseline(oracle, shapes, budget_s=15.0):
                       f"{2 * reps} GEMMs), {el:.1f} s wall on the host"}
 
 
+# HBM traffic of the dominant decode kernel, from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE passes scaled by the same counters on a copy of known size (see
+# the traffic summary under profiles/).  Used only while the kernel sources
+# still hash to what was measured.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_w4a16_m1_hbm_traffic.md")
+KERNEL_SOURCES = ["qg_kernels.hip", "qg_device.h", "qg_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "quantized_gemm_qg_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """Bytes per launch recorded for the current kernel sources, else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        for key in ("source_hash:", "traffic_bytes_per_launch:"):
+            if line.strip().startswith(key):
+                vals[key] = line.split(":", 1)[1].strip().strip("`")
+    if vals.get("source_hash:") != kernel_source_hash() or "traffic_bytes_per_launch:" not in vals:
+        return None
+    return int(vals["traffic_bytes_per_launch:"])
+
+
+def pmc_workload(qg, synth, torch):
+    """A short run for rocprofv3 counter passes: qg_stream_copy of 256 MiB
+    (three launches, the calibration), then the dominant decode kernel (dense
+    W4A16 UINT4 + zp, M=1, N=4096, K=14336) 20 times on rotating weight copies."""
+    n_copy = 256 << 20
+    src = torch.empty(n_copy, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        qg.stream_copy(dst, src, n_copy, stream)
+    torch.cuda.synchronize()
+    del src, dst
+    L = DenseWeights(qg, synth, torch, qg.W_UINT4, 4096, 14336, 128, seed=1)
+    x, _, _ = make_x(qg, synth, torch, False, 1, 14336, seed=11)
+    f = dense_launcher(qg, torch, L, x, None, 1)
+    for i in range(20):
+        f(i)
+    torch.cuda.synchronize()
+    print(f"pmc workload: copy {n_copy} B x3, decode N=4096 K=14336 M=1 x20 "
+          f"({L.bytes} algorithmic bytes per launch), source hash {kernel_source_hash()}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +307,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="primary decode workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-workload", action="store_true",
+                    help="only run the copy calibration + decode kernel for rocprofv3 counter passes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -267,6 +324,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.pmc_workload:
+        pmc_workload(qg, synth, torch)
+        return
 
     shapes = [(14336, 4096), (4096, 14336)]
     print(f"[bench] preparing decode weights {shapes} x{ROTATE} copies", file=sys.stderr, flush=True)
@@ -309,7 +369,7 @@ def main():
         "per_kernel_us": [round(t * 1e3, 3) for t in per_kernel_ms],
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if dom == 1 else None,
             "kernel": f"skinny_kernel dense W4A16 N={layers[dom].n} K={layers[dom].k} M=1",
             "bytes_per_launch": layers[dom].bytes,
         },
@@ -328,6 +388,17 @@ def main():
                         "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "dispatch": qg.describe_dispatch(L.ws[0], mm)}
             print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
+        for n, k in ((14336, 4096), (4096, 14336)):
+            L = DenseWeights(qg, synth, torch, qg.W_INT4, n, k, 128, seed=60, copies=2)
+            x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=61)
+            t = timed(torch, dense_launcher(qg, torch, L, x, None, 4096), 10, 2)
+            fl = 2.0 * 4096 * n * k
+            extra[f"w4a16_int4_M4096_N{n}_K{k}"] = {
+                "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+                "bf16_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
+            print(f"[bench] extra w4a16 N={n} K={k}: {extra[f'w4a16_int4_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
+            del L
         for n in (3072, 14336):
             L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
             x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)
