@@ -125,9 +125,54 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   return true;
 }
 
+// Dense decode kernel (integer formats, M <= 16, K % 512 == 0): the rows sit
+// in LDS and one workgroup covers all of K, so no K split.  (T, KR) pairs
+// compiled: (4, 2), (2, 4), (1, 8), (2, 8) for group 128, the first two for
+// group 64 (group 32 stays on the skinny kernel); W = ceil(k_blocks / KR) <= 16.
+// QG_DECODE="T,KR" picks one, "0" disables the kernel.
+static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, Variant *v) {
+  const int g = w.desc.group_size;
+  const bool compiled = (g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) ||
+                                      (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
+                        (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)));
+  if (!compiled) return false;
+  const int kbs = w.k_blocks;
+  const int W = (kbs + KR - 1) / KR;
+  if (W > 16 || W < 1) return false;
+  const int gpb = 128 / w.desc.group_size;
+  if ((int64_t)W * KR * gpb > w.groups_padded) return false;  // scale reads stay in the row
+  const uint64_t lds = align_up((uint64_t)m * ((uint64_t)W * KR * 256 + 16), 256) + (uint64_t)W * T * m * 64;
+  if (lds > 160 * 1024) return false;
+  *v = Variant{3, T, KR, W, 1, 0};
+  return true;
+}
+
+static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
+  const qg_layer_desc &d = w.desc;
+  if (d.wtype == QG_W_MXFP4 || m < 1 || m > 16 || d.k % 512 != 0) return false;
+  const char *e = getenv("QG_DECODE");
+  if (e && *e == '0') return false;
+  int T, KR;
+  if (e && sscanf(e, "%d,%d", &T, &KR) == 2) return decode_fits(w, m, T, KR, v);
+  // Measured on the decode shapes: one n-tile and 8 k-blocks per wave wins
+  // (small workgroups start and drain independently, which hides the
+  // dequantization behind the weight stream); at 16 rows the skinny kernel's
+  // register-resident fragments win, so the decode kernel stops at 8 rows.
+  if (m > 8) return false;
+  static const int pairs[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
+  const int kbs = w.k_blocks;
+  for (const auto &p : pairs) {
+    if ((kbs + p[1] - 1) / p[1] > 16) continue;
+    if ((w.n_tiles + p[0] - 1) / p[0] < 200 && p[0] > 1) continue;
+    if (decode_fits(w, m, p[0], p[1], v)) return true;
+  }
+  return false;
+}
+
 Variant select_dense(const qg_weight &w, int64_t m) {
   Variant v;
   if (tiled_for(w, m, &v)) return v;
+  if (!getenv("QG_TUNE") && decode_for(w, m, &v)) return v;
   if (env_variant(&v)) {
     sanitize(w.desc, &v);
     while (!covers(v, w.k_blocks)) ++v.splits;
@@ -390,6 +435,8 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   }
   if (v.kind == 1)
     he = launch_mx_tiled(a, v.bn, false, 0, stream);
+  else if (v.kind == 3)
+    he = launch_decode_a16(a, d, v, stream);
   else if (v.kind == 2)
     he = launch_a16_tiled(a, d, v.bn, false, m, 0, ws, stream);
   else
@@ -523,7 +570,9 @@ extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *b
   if (st != QG_OK) return st;
   if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
   const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
-  if (v.kind == 1 || v.kind == 2)
+  if (v.kind == 3)
+    snprintf(buf, buf_bytes, "a16_decode T=%d KR=%d W=%d", v.T, v.KR, v.W);
+  else if (v.kind == 1 || v.kind == 2)
     snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", L.is_mx ? "mx" : "a16", v.bn,
              L.is_mx ? 256 : 128);
   else

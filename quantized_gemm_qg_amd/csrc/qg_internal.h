@@ -120,7 +120,7 @@ constexpr int kMaxExperts = 1024;  // LDS-resident per-expert tables
 // One entry of the tuning table: a kernel variant and its tile parameters.
 struct Variant {
   int kind;    // 0 = skinny (16-row tiles, weights streamed to VGPRs), 1 = MX tiled (LDS),
-               // 2 = integer-format tiled (LDS, bf16 MFMA)
+               // 2 = integer-format tiled (LDS, bf16 MFMA), 3 = decode (activations in LDS)
   int T;       // n-tiles per wave
   int KR;      // k-blocks per wave
   int W;       // waves per workgroup (split of K inside the workgroup)
@@ -135,6 +135,10 @@ hipError_t launch_dense_a16(const GemmArgs &a, const qg_layer_desc &d, const Var
                             hipStream_t s);
 hipError_t launch_dense_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                            hipStream_t s);
+// Dense decode for the integer formats (m <= 16, K % 512 == 0): activations
+// staged in LDS, one workgroup per v.T n-tiles over all of K (v.W * v.KR * 128 >= K).
+hipError_t launch_decode_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                             hipStream_t s);
 hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                           int64_t max_tiles, hipStream_t s);
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,

@@ -153,9 +153,20 @@ __device__ __forceinline__ int64_t y_row_of(const GemmArgs &a, bool moe, const I
 // over k-blocks [kb0, kb0 + KR) of its expert.
 // ---------------------------------------------------------------------------
 
-template <int BITS, bool ZP, int GROUP, int T, int KR>
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// XL: the activation row comes from LDS (xrow is an LDS address holding the
+// row's K values); its fragments are read at their MFMA instead of being held
+// in registers.  after_issue() runs once every global load of the wave has
+// been issued, before the first use of any.
+// vrows: valid rows of the tile; accumulator rows at or past it (row 4q + e
+// has e >= vrows for every lane) skip their group corrections.
+template <int BITS, bool ZP, int GROUP, int T, int KR, bool XL = false, typename Hook = NoHook>
 __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
-                                         const uint16_t *xrow, int nt0, int kb0, f32x4 (&acc)[T]) {
+                                         const uint16_t *xrow, int nt0, int kb0, f32x4 (&acc)[T],
+                                         int vrows = 16, Hook after_issue = Hook()) {
   constexpr int LB = BITS == 4 ? 16 : 12;    // packed bytes per lane per block
   constexpr int BB = 64 * LB;                // packed bytes per block
   constexpr int JPG = GROUP / 32;            // MFMAs per K-group
@@ -167,36 +178,15 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   const int kbs = a.k_blocks, gp = a.groups_padded;
 
   // Every load of the wave is issued before the first wait, so one memory
-  // round trip covers the whole item.  Loads are unconditional: rows past the
-  // tile read a valid row (their outputs are never stored), K past the end
-  // reads k = 0 (those K-groups carry scale 0), and out-of-range n-tiles or
-  // k-blocks read a clamped block (n-tiles past N are never stored; k-blocks
-  // past K have scale 0).
-  // 1. activation fragments, A operand: row r16, k = 128 kb + 32 j + 8 q .. +7
-  u32x4 xf[KR][4];
-#pragma unroll
-  for (int kb = 0; kb < KR; ++kb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = (kb0 + kb) * 128 + 32 * j + 8 * q;
-      xf[kb][j] = *(const u32x4 *)(xrow + (k < a.k ? k : 0));
-    }
-  // 2. weight slices
-  u32x4 wq[T][KR];
-#pragma unroll
-  for (int t = 0; t < T; ++t)
-#pragma unroll
-    for (int kb = 0; kb < KR; ++kb) {
-      const int nt = min(nt0 + t, a.n_tiles - 1), b = min(kb0 + kb, kbs - 1);
-      const uint8_t *p = wexp + ((uint64_t)nt * kbs + b) * BB + lane * LB;
-      if constexpr (BITS == 4) {
-        wq[t][kb] = load_stream((const u32x4 *)p);
-      } else {
-        const uint32_t *p32 = (const uint32_t *)p;
-        wq[t][kb] = u32x4{load_stream(p32), load_stream(p32 + 1), load_stream(p32 + 2), 0u};
-      }
-    }
-  // 3. per-group scales (bf16 pairs) and zero points (nibbles) of this lane's
+  // round trip covers the whole item: scales and zero points first (every
+  // block's correction needs them), then the activation fragments, then the
+  // weight blocks in consumption order, so the compiler's progressive waits
+  // let block kb's work start while later blocks are still arriving.  Loads
+  // are unconditional: rows past the tile read a valid row (their outputs are
+  // never stored), K past the end reads k = 0 (those K-groups carry scale 0),
+  // and out-of-range n-tiles or k-blocks read a clamped block (n-tiles past N
+  // are never stored; k-blocks past K have scale 0).
+  // 1. per-group scales (bf16 pairs) and zero points (nibbles) of this lane's
   //    column for groups g0 .. g0 + NG - 1; g0 is a multiple of NG and the
   //    padded group count a multiple of 32, so no vector load crosses a row
   constexpr int NG = KR * GPB;
@@ -231,8 +221,37 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
       zw[t][0] = 0u;
     }
   }
+  // 2. activation fragments, A operand: row r16, k = 128 kb + 32 j + 8 q .. +7
+  u32x4 xf[XL ? 1 : KR][4];
+  auto xfrag = [&](int kb, int j) -> u32x4 {
+    const int k = (kb0 + kb) * 128 + 32 * j + 8 * q;
+    if constexpr (XL) return *(const u32x4 *)(xrow + k);  // LDS row zero-padded past K
+    return *(const u32x4 *)(xrow + (k < a.k ? k : 0));
+  };
+  if constexpr (!XL) {
+#pragma unroll
+    for (int kb = 0; kb < KR; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xf[kb][j] = xfrag(kb, j);
+  }
+  // 3. weight slices, in the order the MFMAs consume them
+  u32x4 wq[T][KR];
+#pragma unroll
+  for (int kb = 0; kb < KR; ++kb)
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int nt = min(nt0 + t, a.n_tiles - 1), b = min(kb0 + kb, kbs - 1);
+      const uint8_t *p = wexp + ((uint64_t)nt * kbs + b) * BB + lane * LB;
+      if constexpr (BITS == 4) {
+        wq[t][kb] = load_stream((const u32x4 *)p);
+      } else {
+        const uint32_t *p32 = (const uint32_t *)p;
+        wq[t][kb] = u32x4{load_stream(p32), load_stream(p32 + 1), load_stream(p32 + 2), 0u};
+      }
+    }
   // keep every load above this point: the wave waits once for all of them
   __builtin_amdgcn_sched_barrier(0);
+  after_issue();
   const bool kvalid = kb0 < kbs;  // wave-uniform; a wave entirely past K adds nothing
   // scale s and zero point z of group g0 + i -> (MAG * s, -(MAG + z) * s)
   auto group_consts = [&](int t, int i, float &c1, float &c2) {
@@ -245,17 +264,22 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   };
 
   const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const uint32_t umask = sgpr_const(BITS == 4 ? 0x00780078u : 0x00700070u);
+  const uint32_t umagic = vgpr_const(0x3F803F80u);
   f32x4 c[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) c[t] = acc[t];
 #pragma unroll
   for (int kb = 0; kb < KR; ++kb) {
+    u32x4 xk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xk[j] = XL ? xfrag(kb, j) : xf[XL ? 0 : kb][j];
 #pragma unroll
     for (int gi = 0; gi < GPB; ++gi) {
       // 4. group row sums of X on the matrix core (B = all ones)
       f32x4 xs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xf[kb][j], ones, xs);
+      for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xk[j], ones, xs);
       const int i = kb * GPB + gi;
       // 5. dequantize + MFMA + per-group scaling
 #pragma unroll
@@ -263,11 +287,12 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
         f32x4 g = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = gi * JPG; j < (gi + 1) * JPG; ++j)
-          g = mfma_bf16(xf[kb][j], unpack_b<BITS>(wq[t][kb], j), g);
+          g = mfma_bf16(xk[j], unpack_br<BITS>(wq[t][kb], j, umask, umagic), g);
         float c1, c2;
         group_consts(t, i, c1, c2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          if (e >= vrows) continue;  // wave-uniform
           c[t][e] = __builtin_fmaf(xs[e], c2, c[t][e]);
           c[t][e] = __builtin_fmaf(g[e], c1, c[t][e]);
         }
@@ -310,9 +335,9 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
   }
   u32x4 wq[T][KR];
 #pragma unroll
-  for (int t = 0; t < T; ++t)
+  for (int kb = 0; kb < KR; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < KR; ++kb) {
+    for (int t = 0; t < T; ++t) {
       const int nt = min(nt0 + t, a.n_tiles - 1), b = min(kb0 + kb, kbs - 1);
       wq[t][kb] = load_stream((const u32x4 *)(wexp + ((uint64_t)nt * kbs + b) * 1024 + lane * 16));
     }
@@ -389,7 +414,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
         const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
         constexpr int BITS = (FMT <= 1) ? 4 : 3;
         constexpr bool ZP = (FMT == 1 || FMT == 3);
-        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc);
+        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc, it.rows);
       }
     }
 
@@ -449,6 +474,80 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
         store_out(a.y, a.ldy, a.otype, y_row_of(a, moe != 0, it, r), col, red[idx]);
     }
     __syncthreads();  // red[] and last_flag are reused by the next item
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dense decode (M <= 16 rows, integer formats): the workgroup covers all of K
+// ---------------------------------------------------------------------------
+//
+// The skinny kernel keeps every wave's activation fragments in registers (16
+// VGPRs per 128-K block), which caps a 1024-thread workgroup at 16 waves x 2
+// blocks and forces a cross-workgroup K split for long K.  Here the rows are
+// copied once into LDS with global_load_lds, issued before the weight loads
+// so that a partial wait covers them while the weights are still in flight;
+// waves read fragments from LDS at their MFMA.  KR = 8 blocks per wave then
+// fits, 16 waves cover K = 16384 in one workgroup, and the output needs only
+// the in-workgroup reduction (of the valid rows).  One workgroup per T
+// n-tiles.  Requires K % 512 == 0 (each 64-lane copy stays within a row) and
+// rows * (2K + 16) bytes of LDS.
+template <int FMT, int GROUP, int T, int KR>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
+  constexpr int BITS = (FMT <= 1) ? 4 : 3;
+  constexpr bool ZP = (FMT == 1 || FMT == 3);
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int rows = a.m;                       // 1..16
+  const int kspan = nwaves * KR * 128;        // K covered by the waves (>= K)
+  const int xpitch = kspan * 2 + 16;          // bytes per row in LDS (padded: bank spread)
+  float *red = (float *)(dsm + ((rows * xpitch + 255) & ~255));  // [waves][T][rows][16]
+  const int nt0 = blockIdx.x * T;
+
+  // 1. activations -> LDS, 512 values (64 lanes x 16 B) per copy; columns
+  //    K .. kspan (a partial last wave) are zeros
+  const int per_row = a.k >> 9;
+  for (int i = wave; i < rows * per_row; i += nwaves) {
+    const int r = i / per_row, c0 = (i - r * per_row) << 9;
+    lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + c0 + lane * 8, dsm + r * xpitch + c0 * 2);
+  }
+  const int tail = (kspan - a.k) >> 3;  // 16-byte chunks per row
+  for (int i = threadIdx.x; i < rows * tail; i += blockDim.x) {
+    const int r = i / tail;
+    *(u32x4 *)(dsm + r * xpitch + a.k * 2 + (i - r * tail) * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. weights (all loads in flight), then the wait that covers the copies
+  //    above: at least T * KR weight loads were issued after them
+  f32x4 acc[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) acc[t] = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t *xrow = (const uint16_t *)(dsm + min(r16, rows - 1) * xpitch);
+  auto x_ready = [&]() {
+    QG_WAIT_VMCNT(T * KR);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  a16_wave<BITS, ZP, GROUP, T, KR, true>(a, a.wbase, xrow, nt0, wave * KR, acc, rows, x_ready);
+
+  // 3. reduce the waves (valid rows only) and store
+#pragma unroll
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * q + e;
+      if (r < rows) red[((wave * T + t) * rows + r) * 16 + r16] = acc[t][e];
+    }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < T * rows * 16; idx += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < nwaves; ++w) sum += red[w * T * rows * 16 + idx];
+    const int t = idx / (rows * 16), r = (idx / 16) % rows, col = (nt0 + t) * 16 + (idx & 15);
+    if (col < a.n && nt0 + t < a.n_tiles) store_out(a.y, a.ldy, a.otype, r, col, sum);
   }
 }
 
@@ -638,6 +737,57 @@ static hipError_t launch_dense(const GemmArgs &a, const qg_layer_desc &d, const 
   const int64_t items = n_blocks * m_tiles * v.splits;
   if (items > 0x7fffffffLL) return hipErrorInvalidValue;
   return launch_any(a, d, v, false, items, items, s);
+}
+
+template <int FMT, int GROUP>
+static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream_t s) {
+  const int n_blocks = (a.n_tiles + v.T - 1) / v.T;
+  const size_t lds = (((size_t)a.m * ((size_t)v.W * v.KR * 256 + 16) + 255) & ~(size_t)255) +
+                     (size_t)v.W * v.T * a.m * 16 * sizeof(float);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+#define QG_DECODE_LAUNCH(TV, KRV)                                                            \
+  {                                                                                          \
+    auto kern = decode_kernel<FMT, GROUP, TV, KRV>;                                          \
+    hipError_t e = hipFuncSetAttribute((const void *)kern,                                   \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    if (e != hipSuccess) return e;                                                           \
+    hipLaunchKernelGGL(kern, dim3(n_blocks), dim3(64 * v.W), lds, s, a);                     \
+    return hipGetLastError();                                                                \
+  }
+  // instances without register spills (a wave holds KR * 128 / GROUP group
+  // scales per n-tile): every pair for group 128, T * KR <= 8 for group 64
+  if constexpr (GROUP >= 64) {
+    if (v.T == 4 && v.KR == 2) QG_DECODE_LAUNCH(4, 2)
+    if (v.T == 2 && v.KR == 4) QG_DECODE_LAUNCH(2, 4)
+  }
+  if constexpr (GROUP == 128) {
+    if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
+    if (v.T == 2 && v.KR == 8) QG_DECODE_LAUNCH(2, 8)
+  }
+#undef QG_DECODE_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+static hipError_t launch_decode_f(const GemmArgs &a, int group, const Variant &v, hipStream_t s) {
+  switch (group) {
+    case 32: return launch_decode_g<FMT, 32>(a, v, s);
+    case 64: return launch_decode_g<FMT, 64>(a, v, s);
+    case 128: return launch_decode_g<FMT, 128>(a, v, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
+                             hipStream_t s) {
+  if (a.m < 1 || a.m > 16 || a.k % 512 != 0 || v.W * v.KR * 128 < a.k) return hipErrorInvalidValue;
+  switch (fmt_of(d)) {
+    case 0: return launch_decode_f<0>(a, d.group_size, v, s);
+    case 1: return launch_decode_f<1>(a, d.group_size, v, s);
+    case 2: return launch_decode_f<2>(a, d.group_size, v, s);
+    case 3: return launch_decode_f<3>(a, d.group_size, v, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_dense_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,

@@ -257,6 +257,11 @@ def test_dispatch_table_covers_k():
                 if wt != qg.W_MXFP4:  # the group row sums of X live in the workspace
                     assert qg.gemm_workspace_size(w, m) >= (k // g) * m * 4
                 continue
+            if "decode" in s:  # activations in LDS, one workgroup over all of K
+                assert wt != qg.W_MXFP4 and m <= 16 and k % 512 == 0, s
+                T, KR, W = (int(v) for v in re.findall(r"=(\d+)", s))
+                assert W * KR >= -(-k // 128) and 1 <= W <= 16, s
+                continue
             T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
             assert W * KR * S >= -(-k // 128), s
             assert 1 <= W <= 16

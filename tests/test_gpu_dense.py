@@ -239,3 +239,41 @@ def test_w4a16_large_m_full_size_sampled_rows(nk):
     rows[0], rows[-1] = 0, m - 1
     assert "a16_tiled" in qg.describe_dispatch(layer.w, m)
     _check(layer, acts, m, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# dense decode kernel (integer formats, M <= 16, K % 512 == 0, rows in LDS)
+# ---------------------------------------------------------------------------
+
+DECODE_VARIANTS = {128: ["4,2", "2,4", "1,8", "2,8"], 64: ["4,2", "2,4"]}
+
+
+@pytest.mark.parametrize("wtype", A16)
+@pytest.mark.parametrize("group", [64, 128])
+def test_decode_kernel_variants(monkeypatch, wtype, group):
+    """Every compiled (T, KR) of the decode kernel; N = 200 leaves a partial
+    n-tile block, K = 1536 (12 blocks) a partial last wave for KR = 8."""
+    layer = Layer(wtype, 200, 1536, group, seed=wtype * 10 + group + 1)
+    for tune in DECODE_VARIANTS[group]:
+        monkeypatch.setenv("QG_DECODE", tune)
+        for m in (1, 3, 16):
+            assert "a16_decode" in qg.describe_dispatch(layer.w, m), (tune, m)
+            print(f"  decode {tune} m={m}", flush=True)
+            _check(layer, Acts(False, m, 1536, seed=m + group), m)
+
+
+@pytest.mark.parametrize("wtype", A16)
+def test_decode_kernel_identity_rows_exact(wtype):
+    n, k = 72, 1024
+    layer = Layer(wtype, n, k, 128, seed=31)
+    wdq = layer.wdq()
+    ks = [0, 1, 31, 32, 127, 128, 255, 511, 512, 513, 767, 896, 1000, 1023, 300, 700]
+    m = len(ks)
+    bits = np.zeros((m, k), np.uint16)
+    for i, kk in enumerate(ks):
+        bits[i, kk] = 0x3F80
+    acts = Acts(False, m, k, values=bits)
+    assert "a16_decode" in qg.describe_dispatch(layer.w, m)
+    y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
+    for i, kk in enumerate(ks):
+        assert np.array_equal(y[i].astype(np.float64), wdq[:, kk]), kk
