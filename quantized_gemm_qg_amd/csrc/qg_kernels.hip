@@ -304,10 +304,10 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
 }
 
 // MXFP4 weights x MXFP8 activations: one scaled MFMA per 16x128 block.
-template <int T, int KR>
+template <int T, int KR, typename Hook = NoHook>
 __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
                                         const uint8_t *xrow, const uint8_t *xsrow, int nt0, int kb0,
-                                        f32x4 (&acc)[T]) {
+                                        f32x4 (&acc)[T], Hook after_issue = Hook()) {
   const int lane = threadIdx.x & 63;
   const int q = lane >> 4, r16 = lane & 15;
   const int kbs = a.k_blocks;
@@ -352,6 +352,7 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
   }
   // keep every load above this point: the wave waits once for all of them
   __builtin_amdgcn_sched_barrier(0);
+  after_issue();
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     f32x4 c = acc[t];
@@ -394,13 +395,28 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
     total_items = (int64_t)total_tiles * n_blocks;
   }
 
+  // The item's activation rows (for MoE, pair ids loaded from the sorted list)
+  // are resolved one item ahead, while the previous item's loads are in
+  // flight, so an item's loads never wait on that dependent round trip.
+  // rows past the tile read the tile's first row: their outputs are never stored
+  int nxt_xr = 0;  // rows < 2^30
+  if ((int64_t)blockIdx.x < total_items) {
+    const Item first = decode_item(a, moe != 0, blockIdx.x, n_blocks, total_tiles, prefix);
+    nxt_xr = (int)x_row_of(a, moe != 0, first, r16 < first.rows ? r16 : 0);
+  }
   for (int64_t item = blockIdx.x; item < total_items; item += gridDim.x) {
     const Item it = decode_item(a, moe != 0, item, n_blocks, total_tiles, prefix);
+    const int64_t xr = nxt_xr;
     const uint8_t *wexp = a.wbase + (uint64_t)it.expert * a.expert_stride;
     const int nt0 = it.nb * T;
     const int kb0 = (it.split * nwaves + wave) * KR;
-    // rows past the tile read the tile's first row: their outputs are never stored
-    const int64_t xr = x_row_of(a, moe != 0, it, r16 < it.rows ? r16 : 0);
+    auto prefetch_next = [&]() {
+      const int64_t next = item + gridDim.x;
+      if (next < total_items) {  // workgroup-uniform
+        const Item n_it = decode_item(a, moe != 0, next, n_blocks, total_tiles, prefix);
+        nxt_xr = (int)x_row_of(a, moe != 0, n_it, r16 < n_it.rows ? r16 : 0);
+      }
+    };
 
     f32x4 acc[T];
 #pragma unroll
@@ -409,13 +425,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
       if constexpr (FMT == 4) {
         const uint8_t *xrow = (const uint8_t *)a.x + xr * a.ldx;
         const uint8_t *xsrow = a.x_scales + xr * (int64_t)(a.k >> 5);
-        mx_wave<T, KR>(a, wexp, xrow, xsrow, nt0, kb0, acc);
+        mx_wave<T, KR>(a, wexp, xrow, xsrow, nt0, kb0, acc, prefetch_next);
       } else {
         const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
         constexpr int BITS = (FMT <= 1) ? 4 : 3;
         constexpr bool ZP = (FMT == 1 || FMT == 3);
-        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc, it.rows);
+        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc, it.rows, prefetch_next);
       }
+    } else {
+      prefetch_next();
     }
 
     // reduce the K-split waves of the workgroup in a fixed order
