@@ -370,7 +370,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if dom == 1 else None,
-            "kernel": f"skinny_kernel dense W4A16 N={layers[dom].n} K={layers[dom].k} M=1",
+            "kernel": f"{qg.describe_dispatch(layers[dom].ws[0], 1)}: dense W4A16 N={layers[dom].n} "
+                      f"K={layers[dom].k} M=1",
             "bytes_per_launch": layers[dom].bytes,
         },
     }

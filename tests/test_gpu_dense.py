@@ -263,7 +263,8 @@ def test_decode_kernel_variants(monkeypatch, wtype, group):
 
 
 @pytest.mark.parametrize("wtype", A16)
-def test_decode_kernel_identity_rows_exact(wtype):
+def test_decode_kernel_identity_rows_exact(monkeypatch, wtype):
+    monkeypatch.setenv("QG_DECODE", "1,8")  # 16 rows: past the default row limit
     n, k = 72, 1024
     layer = Layer(wtype, n, k, 128, seed=31)
     wdq = layer.wdq()
