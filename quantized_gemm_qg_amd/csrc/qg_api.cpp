@@ -221,6 +221,15 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
   return min_rows;
 }
 
+// Waves of the MX tiled kernel: 8 (two per SIMD, wave tile 64 x 128) keeps
+// the matrix core fed while the other wave of the SIMD waits on LDS reads or
+// the stage barrier; measured 1.3x faster than 4 at M = 4096.
+int mx_tiled_waves() {
+  const char *e = getenv("QG_MX_WAVES");
+  if (e && (atoi(e) == 4 || atoi(e) == 8)) return atoi(e);
+  return 8;
+}
+
 // Raster group of the tiled MoE launches (QG_MOE_GROUP_M overrides).
 static int moe_group_m() {
   const char *e = getenv("QG_MOE_GROUP_M");
@@ -434,7 +443,7 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
     a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
   }
   if (v.kind == 1)
-    he = launch_mx_tiled(a, v.bn, false, 0, stream);
+    he = launch_mx_tiled(a, v.bn, false, 0, mx_tiled_waves(), stream);
   else if (v.kind == 3)
     he = launch_decode_a16(a, d, v, stream);
   else if (v.kind == 2)
@@ -531,7 +540,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     a.tiles = tiles;
     a.group_m = moe_group_m();
     if (L.is_mx) {
-      he = launch_mx_tiled(a, kMoeTileRows, true, cap, stream);
+      he = launch_mx_tiled(a, kMoeTileRows, true, cap, mx_tiled_waves(), stream);
     } else {
       void *xs = (uint8_t *)ws + align_up((uint64_t)(2 + 2 * cap) * 4, 256);
       he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, xs, stream);

@@ -146,7 +146,9 @@ hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Varian
 // MoE launches of the tiled kernels walk the tile list a.tiles of capacity
 // tiles_cap, cut at kMoeTileRows rows.
 constexpr int kMoeTileRows = 128;
-hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, hipStream_t s);
+hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, int waves,
+                           hipStream_t s);
+int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // Integer formats at large M: group row sums of X into ws, then the tiled
 // kernel.  ws holds (K / group) * m floats (a16_tiled_ws_bytes).
 // xs_rows: rows of X (dense: m; MoE: tokens or pairs, by the x row mode).
