@@ -230,6 +230,15 @@ int mx_tiled_waves() {
   return 8;
 }
 
+// Waves of the integer-format tiled kernel: 8 (4 x 2, two per SIMD, wave
+// tile (BM / 4) x 64) hides one wave's waits behind the other's MFMAs and
+// dequantization; measured 1.15-1.25x faster than 4 at M = 4096.
+int a16_tiled_waves() {
+  const char *e = getenv("QG_A16_WAVES");
+  if (e && (atoi(e) == 4 || atoi(e) == 8)) return atoi(e);
+  return 8;
+}
+
 // Raster group of the tiled MoE launches (QG_MOE_GROUP_M overrides).
 static int moe_group_m() {
   const char *e = getenv("QG_MOE_GROUP_M");
@@ -447,7 +456,7 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   else if (v.kind == 3)
     he = launch_decode_a16(a, d, v, stream);
   else if (v.kind == 2)
-    he = launch_a16_tiled(a, d, v.bn, false, m, 0, ws, stream);
+    he = launch_a16_tiled(a, d, v.bn, false, m, 0, a16_tiled_waves(), ws, stream);
   else
     he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -543,7 +552,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
       he = launch_mx_tiled(a, kMoeTileRows, true, cap, mx_tiled_waves(), stream);
     } else {
       void *xs = (uint8_t *)ws + align_up((uint64_t)(2 + 2 * cap) * 4, 256);
-      he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, xs, stream);
+      he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, a16_tiled_waves(), xs, stream);
     }
     if (he != hipSuccess) return hip_status(he);
     a.moe_min_rows = min_rows;

@@ -153,7 +153,8 @@ int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // kernel.  ws holds (K / group) * m floats (a16_tiled_ws_bytes).
 // xs_rows: rows of X (dense: m; MoE: tokens or pairs, by the x row mode).
 hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
-                            int64_t xs_rows, int64_t tiles_cap, void *ws, hipStream_t s);
+                            int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, hipStream_t s);
+int a16_tiled_waves();  // QG_A16_WAVES (4 or 8), else the default
 uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m);
 // MoE tile list for the tiled kernels (experts with >= min_rows rows, bm-row
 // tiles): tiles[0] = count, then (expert, first sorted row) pairs.

@@ -7,7 +7,7 @@
 // matrix-core step.  Here the packed codes travel HBM -> LDS untouched (a
 // quarter of the bytes of a bf16 weight); each wave turns its columns' codes
 // into bf16 MFMA operands in registers, once per 128-K step, and reuses them
-// for all BM / 2 rows of its tile.
+// for all BM / WM rows of its tile.
 //
 // Arithmetic.  An offset-binary code u becomes the bf16 value 1 + u / MAG
 // (MAG = 16 for 4-bit, 8 for 3-bit codes: the code lands in the top mantissa
@@ -21,8 +21,10 @@
 // -(1 + z / MAG)) comes from a small pre-pass kernel that reads X once; the
 // dequantized weight is the exact real (u - z) * s.
 //
-// Tiling: a workgroup of 4 waves (2 x 2) computes a BM x 128 tile of Y, each
-// wave (BM / 2) x 64 as (BM / 32) x 4 blocks of 16 x 16.  K advances 128 per
+// Tiling: a workgroup of WM x 2 waves computes a BM x 128 tile of Y, each wave
+// (BM / WM) x 64 as (BM / WM / 16) x 4 blocks of 16 x 16; the default is 8
+// waves (WM = 4, two per SIMD, so one wave's waits hide behind the other's
+// work), the 4-wave form (WM = 2) is kept for comparison.  K advances 128 per
 // stage; one step uses
 //   A   BM rows x 128 bf16 (256 B per row, 16-byte chunks XOR-swizzled by
 //       the row's low 4 bits so the 16 rows of a fragment read hit distinct
@@ -47,11 +49,11 @@
 namespace qg {
 
 constexpr int kA16BN = 128;       // tile columns (8 packed n-tiles)
-constexpr int kA16Threads = 256;  // 4 waves
 constexpr int kLdsBytes = 160 * 1024;
 
-template <int BM, int BITS, bool ZP, int GROUP>
+template <int BM, int WM, int BITS, bool ZP, int GROUP>
 struct A16Cfg {
+  static constexpr int WAVES = 2 * WM;            // WM (M) x 2 (N)
   static constexpr int LB = BITS == 4 ? 16 : 12;  // packed bytes per lane per block
   static constexpr int BB = 64 * LB;              // packed bytes per 16 x 128 block
   static constexpr int GPB = 128 / GROUP;         // groups per 128-K step
@@ -75,9 +77,9 @@ struct A16Cfg {
   static constexpr int OFF_BRING = NA * A_STAGE;
   static constexpr int LDS = NA * A_STAGE + NB * B_STAGE;
   // loads per wave and stage
-  static constexpr int A_LOADS = BM / 16;             // 1-KB copies of A
+  static constexpr int A_LOADS = BM * 256 / 1024 / WAVES;            // 1-KB copies of A
   static constexpr int A_ISSUE = A_LOADS + GPB;
-  static constexpr int B_LOADS = BITS == 4 ? 2 : 6;   // 1-KB (4-bit) or 256-B (3-bit) copies
+  static constexpr int B_LOADS = (BITS == 4 ? 8 : 24) / WAVES;  // 1-KB (4-bit) or 256-B (3-bit) copies
   static constexpr int B_ISSUE = B_LOADS + 1 + (ZP ? 1 : 0);
   // Each step issues its activation loads, then its weight loads.  In steady
   // state, the loads issued after the later of stage kb's two groups: stage
@@ -85,7 +87,7 @@ struct A16Cfg {
   // weight ring is deeper (followed by that step's weight loads), in the same
   // step otherwise.
   static constexpr int AFTER_A = (NB > NA ? B_ISSUE : 0) + (NA - 2) * (A_ISSUE + B_ISSUE);
-  static constexpr int MI = BM / 32;                  // 16-row blocks per wave
+  static constexpr int MI = BM / WM / 16;             // 16-row blocks per wave
   static constexpr float MAG = BITS == 4 ? 16.f : 8.f;
   static constexpr int ZSYM = BITS == 4 ? 8 : 4;
   static_assert(NB >= 2 && NB >= NA, "weight ring too shallow");
@@ -102,10 +104,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BITS, bool ZP, int GROUP, bool MOE>
-__global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, const float *xs,
-                                                                 int xs_rows) {
-  using C = A16Cfg<BM, BITS, ZP, GROUP>;
+template <int BM, int WM, int BITS, bool ZP, int GROUP, bool MOE>
+__global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const float *xs,
+                                                             int xs_rows) {
+  using C = A16Cfg<BM, WM, BITS, ZP, GROUP>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,16 +135,16 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
     const int c = (lane & 15) ^ (row & 15);
     a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx * 2 + 16 * c);
   }
-  // B: 4-bit, copy i = block 2 wave + i; 3-bit, copy i = 256-byte piece
-  // 6 wave + i of the 8 blocks (three pieces per 768-byte block)
+  // B: 4-bit, copy i = block B_LOADS wave + i; 3-bit, copy i = 256-byte
+  // piece B_LOADS wave + i of the 8 blocks (three pieces per 768-byte block)
   uint32_t b_off[C::B_LOADS];
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i) {
     if constexpr (BITS == 4) {
-      const int blk = 2 * wave + i;
+      const int blk = C::B_LOADS * wave + i;
       b_off[i] = (uint32_t)(min(nt0 + blk, a.n_tiles - 1) * kbs) * 1024u + 16u * lane;
     } else {
-      const int piece = 6 * wave + i, blk = piece / 3;
+      const int piece = C::B_LOADS * wave + i, blk = piece / 3;
       b_off[i] = (uint32_t)(min(nt0 + blk, a.n_tiles - 1) * kbs) * 768u + 256u * (piece % 3) + 4u * lane;
     }
   }
@@ -169,9 +171,9 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i) {
       if constexpr (BITS == 4)
-        lds_dma16(wexp + b_off[i] + kb * 1024u, st + (2 * wave + i) * 1024);
+        lds_dma16(wexp + b_off[i] + kb * 1024u, st + (C::B_LOADS * wave + i) * 1024);
       else
-        lds_dma4(wexp + b_off[i] + kb * 768u, st + (6 * wave + i) * 256);
+        lds_dma4(wexp + b_off[i] + kb * 768u, st + (C::B_LOADS * wave + i) * 256);
     }
     const int g0 = kb * C::GPB;
     lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + (wave & 1) * 1024);
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
       }
 #pragma unroll
       for (int i = 0; i < C::MI; ++i) {
-        const int r0 = wm * (BM / 2) + 16 * i;
+        const int r0 = wm * (BM / WM) + 16 * i;
         const uint8_t *arow = st + (r0 + r16) * 256;
         u32x4 af[C::JPG];
 #pragma unroll
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(kA16Threads) void a16_tiled_kernel(GemmArgs a, cons
 
   // output through LDS (the ring is free once every wave is past its last stage)
   lds_barrier();
-  store_tile<C::MI, 4>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / 2),
+  store_tile<C::MI, 4>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / WM),
                        (nt0 + wn * 4) * 16, smem + wave * store_tile_lds_bytes<C::MI, 4>());
 }
 
@@ -292,10 +294,11 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *x, int6
   }
 }
 
-template <int BM, int BITS, bool ZP, int GROUP, bool MOE>
+template <int BM, int WM, int BITS, bool ZP, int GROUP, bool MOE>
 static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t tiles_cap, float *xs,
                                      hipStream_t s) {
-  using C = A16Cfg<BM, BITS, ZP, GROUP>;
+  using C = A16Cfg<BM, WM, BITS, ZP, GROUP>;
+  static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MI, 4>(), "epilogue LDS");
   const float factor = ZP ? 1.f : -(1.f + (float)C::ZSYM / C::MAG);
   const int64_t rows_blocks = (xs_rows + 3) / 4;
   hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3((unsigned)rows_blocks), dim3(256), 0, s,
@@ -307,34 +310,34 @@ static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, BITS, ZP, GROUP, MOE>,
+  e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, WM, BITS, ZP, GROUP, MOE>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((a16_tiled_kernel<BM, BITS, ZP, GROUP, MOE>), dim3((unsigned)(per_xcd * kXcds)),
-                     dim3(kA16Threads), lds, s, a, (const float *)xs, (int)xs_rows);
+  hipLaunchKernelGGL((a16_tiled_kernel<BM, WM, BITS, ZP, GROUP, MOE>), dim3((unsigned)(per_xcd * kXcds)),
+                     dim3(64 * C::WAVES), lds, s, a, (const float *)xs, (int)xs_rows);
   return hipGetLastError();
 }
 
-template <int BM, int BITS, bool ZP, bool MOE>
+template <int BM, int WM, int BITS, bool ZP, bool MOE>
 static hipError_t launch_group(const GemmArgs &a, int group, int64_t xs_rows, int64_t cap, float *xs,
                                hipStream_t s) {
   switch (group) {
-    case 32: return launch_a16_tiled_t<BM, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, s);
-    case 64: return launch_a16_tiled_t<BM, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, s);
-    case 128: return launch_a16_tiled_t<BM, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, s);
+    case 32: return launch_a16_tiled_t<BM, WM, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, s);
+    case 64: return launch_a16_tiled_t<BM, WM, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, s);
+    case 128: return launch_a16_tiled_t<BM, WM, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int BM, bool MOE>
+template <int BM, int WM, bool MOE>
 static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t xs_rows, int64_t cap,
                              float *xs, hipStream_t s) {
   const int g = d.group_size;
   switch (d.wtype) {
-    case QG_W_INT4: return launch_group<BM, 4, false, MOE>(a, g, xs_rows, cap, xs, s);
-    case QG_W_UINT4: return launch_group<BM, 4, true, MOE>(a, g, xs_rows, cap, xs, s);
-    case QG_W_INT3: return launch_group<BM, 3, false, MOE>(a, g, xs_rows, cap, xs, s);
-    case QG_W_UINT3: return launch_group<BM, 3, true, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_INT4: return launch_group<BM, WM, 4, false, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_UINT4: return launch_group<BM, WM, 4, true, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_INT3: return launch_group<BM, WM, 3, false, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_UINT3: return launch_group<BM, WM, 3, true, MOE>(a, g, xs_rows, cap, xs, s);
   }
   return hipErrorInvalidValue;
 }
@@ -344,14 +347,19 @@ uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m) {
 }
 
 // Dense: a.m rows in bm-row tiles.  MoE: the tile list a.tiles (capacity
-// tiles_cap) of 128-row tiles.
+// tiles_cap) of 128-row tiles.  waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2).
 hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
-                            int64_t xs_rows, int64_t tiles_cap, void *ws, hipStream_t s) {
+                            int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, hipStream_t s) {
   if (a.k % 128 != 0) return hipErrorInvalidValue;
   float *xs = (float *)ws;
-  if (moe) return launch_fmt<kMoeTileRows, true>(a, d, xs_rows, tiles_cap, xs, s);
-  return bm == 256 ? launch_fmt<256, false>(a, d, xs_rows, 0, xs, s)
-                   : launch_fmt<128, false>(a, d, xs_rows, 0, xs, s);
+  if (waves == 8) {
+    if (moe) return launch_fmt<kMoeTileRows, 4, true>(a, d, xs_rows, tiles_cap, xs, s);
+    return bm == 256 ? launch_fmt<256, 4, false>(a, d, xs_rows, 0, xs, s)
+                     : launch_fmt<128, 4, false>(a, d, xs_rows, 0, xs, s);
+  }
+  if (moe) return launch_fmt<kMoeTileRows, 2, true>(a, d, xs_rows, tiles_cap, xs, s);
+  return bm == 256 ? launch_fmt<256, 2, false>(a, d, xs_rows, 0, xs, s)
+                   : launch_fmt<128, 2, false>(a, d, xs_rows, 0, xs, s);
 }
 
 }  // namespace qg

@@ -35,21 +35,22 @@ def test_raster_visits_every_tile_once_for_oversized_grids():
         assert all(0 <= a < m and 0 <= b < n for a, b in live)
 
 
-def a16_rings(bm, bits, zp, group):
+def a16_rings(bm, bits, zp, group, waves=4):
     gpb = 128 // group
     a_stage = bm * 256 + gpb * bm * 4
     b_stage = 8 * 64 * (16 if bits == 4 else 12) + 128 * 16 + (128 * 4 if zp else 0)
     na = 3 if 3 * a_stage + 2 * b_stage <= LDS else 2
     nb = min(6, (LDS - na * a_stage) // b_stage)
-    a_issue = bm // 16 + gpb
-    b_issue = (2 if bits == 4 else 6) + 1 + (1 if zp else 0)
+    a_issue = bm * 256 // 1024 // waves + gpb
+    b_issue = (8 if bits == 4 else 24) // waves + 1 + (1 if zp else 0)
     after = (b_issue if nb > na else 0) + (na - 2) * (a_issue + b_issue)
     return na, nb, a_issue, b_issue, after, na * a_stage + nb * b_stage
 
 
 def test_a16_tiled_ring_waits_cover_each_stage():
-    for bm, bits, zp, group in itertools.product([128, 256], [3, 4], [False, True], [32, 64, 128]):
-        na, nb, ai, bi, after, lds = a16_rings(bm, bits, zp, group)
+    for bm, bits, zp, group, waves in itertools.product([128, 256], [3, 4], [False, True],
+                                                        [32, 64, 128], [4, 8]):
+        na, nb, ai, bi, after, lds = a16_rings(bm, bits, zp, group, waves)
         assert 2 <= na <= nb and lds <= LDS and after <= 63
         for kbs in range(1, 13):
             seq = []
