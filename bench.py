@@ -392,7 +392,7 @@ def main():
         for n, k in ((14336, 4096), (4096, 14336)):
             L = DenseWeights(qg, synth, torch, qg.W_INT4, n, k, 128, seed=60, copies=2)
             x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=61)
-            t = timed(torch, dense_launcher(qg, torch, L, x, None, 4096), 10, 2)
+            t = timed(torch, dense_launcher(qg, torch, L, x, None, 4096), 40, 10)
             fl = 2.0 * 4096 * n * k
             extra[f"w4a16_int4_M4096_N{n}_K{k}"] = {
                 "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
@@ -403,7 +403,7 @@ def main():
         for n in (3072, 14336):
             L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
             x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)
-            t = timed(torch, dense_launcher(qg, torch, L, x, xsc, 4096), 5, 1)
+            t = timed(torch, dense_launcher(qg, torch, L, x, xsc, 4096), 100, 20)
             fl = 2.0 * 4096 * n * 4096
             extra[f"w4a8_mx_M4096_N{n}_K4096"] = {
                 "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),

@@ -203,9 +203,11 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
 }
 
 // MoE: experts with at least this many rows go to the tiled kernels (128-row
-// tiles), the rest to the skinny kernel; 0 = skinny only.  Below ~64 rows a
-// 128-row tile wastes more matrix-core work than re-reading the expert's
-// weights per 16-row tile costs.  QG_MOE_TILED_MIN overrides (0 disables).
+// tiles); the rest to the small-tile form of the integer formats' tiled kernel
+// or (MXFP4) to the skinny kernel; 0 = skinny only.  QG_MOE_TILED_MIN
+// overrides (0 disables the tiled kernels).
+static bool moe_small_tiles(const qg_weight &w, int min_rows);
+
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
   if (d.k % 128 != 0 || d.num_experts > kMaxExperts) return 0;
@@ -217,7 +219,10 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
   int min_rows = 64;
   const char *e = getenv("QG_MOE_TILED_MIN");
   if (e && *e) min_rows = std::max(0, atoi(e));
-  if (min_rows <= 0 || pairs < min_rows) return 0;
+  if (min_rows <= 0) return 0;
+  // no expert can reach the threshold: all go to the small-tile form
+  // (integer formats) or the skinny kernel
+  if (pairs < min_rows && (mx || !moe_small_tiles(w, min_rows))) return 0;
   return min_rows;
 }
 
@@ -251,10 +256,37 @@ static int64_t moe_tiles_cap(const qg_weight &w, int64_t pairs, int min_rows) {
   return pairs / kMoeTileRows + std::min<int64_t>(w.desc.num_experts, pairs / min_rows) + 1;
 }
 
-// MoE workspace: [tile list][group row sums of X (integer formats)]
+// Rows of the small tiles: 64, or 32 (QG_MOE_SMALL_BM).
+static int moe_small_bm() {
+  const char *e = getenv("QG_MOE_SMALL_BM");
+  return (e && atoi(e) == 32) ? 32 : kMoeSmallTileRows;
+}
+
+// Small-tile list capacity (experts with 1 .. min_rows - 1 rows): one tile per
+// small-tile rows plus one partial tile per such expert.
+static int64_t moe_small_tiles_cap(const qg_weight &w, int64_t pairs) {
+  return pairs / moe_small_bm() + std::min<int64_t>(w.desc.num_experts, pairs) + 1;
+}
+
+// Integer formats: experts below the tiled threshold run the tiled kernel's
+// small-tile form (one pass over the expert's weights for all of its rows,
+// through the same deep LDS ring) instead of the skinny kernel, which re-reads
+// the weights per 16 rows and cannot keep enough bytes in flight with one
+// item per workgroup.  QG_MOE_SMALL=0 keeps them on the skinny kernel.
+static bool moe_small_tiles(const qg_weight &w, int min_rows) {
+  if (min_rows <= 0 || w.desc.wtype == QG_W_MXFP4) return false;
+  const char *e = getenv("QG_MOE_SMALL");
+  return !(e && *e && atoi(e) == 0);
+}
+
+static uint64_t moe_list_bytes(int64_t cap) { return align_up((uint64_t)(2 + 2 * cap) * 4, 256); }
+
+// MoE workspace: [tile list][small-tile list][group row sums of X (integer
+// formats)]
 static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_count, int min_rows) {
   if (min_rows <= 0) return 0;
-  uint64_t b = align_up((uint64_t)(2 + 2 * moe_tiles_cap(w, pairs, min_rows)) * 4, 256);
+  uint64_t b = moe_list_bytes(moe_tiles_cap(w, pairs, min_rows));
+  if (moe_small_tiles(w, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
   if (w.desc.wtype != QG_W_MXFP4) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
   return b;
 }
@@ -456,7 +488,7 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   else if (v.kind == 3)
     he = launch_decode_a16(a, d, v, stream);
   else if (v.kind == 2)
-    he = launch_a16_tiled(a, d, v.bn, false, m, 0, a16_tiled_waves(), ws, stream);
+    he = launch_a16_tiled(a, d, v.bn, false, m, 0, a16_tiled_waves(), ws, true, stream);
   else
     he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -542,8 +574,11 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   if (min_rows > 0) {
     // experts with >= min_rows rows: tile list, then the tiled kernel
     const int64_t cap = moe_tiles_cap(*w, pairs, min_rows);
+    const bool small = moe_small_tiles(*w, min_rows);
+    const int64_t cap_s = small ? moe_small_tiles_cap(*w, pairs) : 0;
     int32_t *tiles = (int32_t *)ws;
-    he = launch_moe_tiles(expert_offsets, d.num_experts, min_rows, kMoeTileRows, (int32_t)pairs,
+    int32_t *tiles_s = (int32_t *)((uint8_t *)ws + moe_list_bytes(cap));
+    he = launch_moe_tiles(expert_offsets, d.num_experts, min_rows, 0, kMoeTileRows, (int32_t)pairs,
                           (int32_t)cap, tiles, stream);
     if (he != hipSuccess) return hip_status(he);
     a.tiles = tiles;
@@ -551,8 +586,19 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     if (L.is_mx) {
       he = launch_mx_tiled(a, kMoeTileRows, true, cap, mx_tiled_waves(), stream);
     } else {
-      void *xs = (uint8_t *)ws + align_up((uint64_t)(2 + 2 * cap) * 4, 256);
-      he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, a16_tiled_waves(), xs, stream);
+      void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);
+      he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, a16_tiled_waves(), xs, true,
+                            stream);
+      if (he == hipSuccess && small) {
+        const int sbm = moe_small_bm();
+        he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
+                              (int32_t)cap_s, tiles_s, stream);
+        if (he != hipSuccess) return hip_status(he);
+        a.tiles = tiles_s;
+        a.group_m = 1;
+        he = launch_a16_tiled(a, d, sbm, true, x_rows_count, cap_s, 8, xs, false, stream);
+        return hip_status(he);  // every expert with rows is covered
+      }
     }
     if (he != hipSuccess) return hip_status(he);
     a.moe_min_rows = min_rows;

@@ -144,22 +144,30 @@ hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Varia
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                          int64_t max_tiles, hipStream_t s);
 // MoE launches of the tiled kernels walk the tile list a.tiles of capacity
-// tiles_cap, cut at kMoeTileRows rows.
+// tiles_cap, cut at kMoeTileRows rows; experts with fewer rows than the
+// tiled threshold go to the integer formats' small-tile form in one
+// kMoeSmallTileRows-row tile each.
 constexpr int kMoeTileRows = 128;
+constexpr int kMoeSmallTileRows = 64;
 hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, int waves,
                            hipStream_t s);
 int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // Integer formats at large M: group row sums of X into ws, then the tiled
 // kernel.  ws holds (K / group) * m floats (a16_tiled_ws_bytes).
 // xs_rows: rows of X (dense: m; MoE: tokens or pairs, by the x row mode).
+// sums = false skips the row sums (already in ws from an earlier launch on the
+// same X).
 hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
-                            int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, hipStream_t s);
+                            int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, bool sums,
+                            hipStream_t s);
 int a16_tiled_waves();  // QG_A16_WAVES (4 or 8), else the default
 uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m);
-// MoE tile list for the tiled kernels (experts with >= min_rows rows, bm-row
-// tiles): tiles[0] = count, then (expert, first sorted row) pairs.
-hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows, int32_t bm,
-                            int32_t pairs, int32_t capacity, int32_t *tiles, hipStream_t s);
+// MoE tile list for the tiled kernels (experts with min_rows <= rows <
+// max_rows, max_rows = 0 for no bound; bm-row tiles): tiles[0] = count, then
+// (expert, first sorted row) pairs.
+hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows,
+                            int32_t max_rows, int32_t bm, int32_t pairs, int32_t capacity,
+                            int32_t *tiles, hipStream_t s);
 hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,

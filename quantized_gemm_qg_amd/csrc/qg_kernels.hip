@@ -653,15 +653,15 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t *ids, int6
 // sorted row) per tile in expert order; at most `capacity` tiles are written
 // (counts are clamped to [0, pairs], so malformed offsets cannot overrun it).
 __global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t *offsets, int32_t experts,
-                                                         int32_t min_rows, int32_t bm, int32_t pairs,
-                                                         int32_t capacity, int32_t *tiles) {
+                                                         int32_t min_rows, int32_t max_rows, int32_t bm,
+                                                         int32_t pairs, int32_t capacity, int32_t *tiles) {
   __shared__ int wave_tot[16];
   const int tid = threadIdx.x, nth = blockDim.x;
   const int per = (experts + nth - 1) / nth;
   const int e0 = tid * per;
   auto ntiles = [&](int e) {
     const int c = min(max(offsets[e + 1] - offsets[e], 0), pairs);
-    return c >= min_rows ? (c + bm - 1) / bm : 0;
+    return c >= min_rows && (max_rows <= 0 || c < max_rows) ? (c + bm - 1) / bm : 0;
   };
   int local = 0;
   for (int e = e0; e < e0 + per && e < experts; ++e) local += ntiles(e);
@@ -839,10 +839,11 @@ hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Varian
   return launch_moe(a, d, v, max_tiles, s);
 }
 
-hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows, int32_t bm,
-                            int32_t pairs, int32_t capacity, int32_t *tiles, hipStream_t s) {
-  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, experts, min_rows, bm,
-                     pairs, capacity, tiles);
+hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows,
+                            int32_t max_rows, int32_t bm, int32_t pairs, int32_t capacity,
+                            int32_t *tiles, hipStream_t s) {
+  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, experts, min_rows,
+                     max_rows, bm, pairs, capacity, tiles);
   return hipGetLastError();
 }
 

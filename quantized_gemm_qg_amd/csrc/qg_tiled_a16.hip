@@ -51,16 +51,19 @@ namespace qg {
 constexpr int kA16BN = 128;       // tile columns (8 packed n-tiles)
 constexpr int kLdsBytes = 160 * 1024;
 
-template <int BM, int WM, int BITS, bool ZP, int GROUP>
+template <int BM, int WM, int WN, int BITS, bool ZP, int GROUP>
 struct A16Cfg {
-  static constexpr int WAVES = 2 * WM;            // WM (M) x 2 (N)
+  static constexpr int WAVES = WM * WN;           // WM (M) x WN (N)
+  static constexpr int NJ = 8 / WN;               // 16-column blocks per wave
   static constexpr int LB = BITS == 4 ? 16 : 12;  // packed bytes per lane per block
   static constexpr int BB = 64 * LB;              // packed bytes per 16 x 128 block
   static constexpr int GPB = 128 / GROUP;         // groups per 128-K step
   static constexpr int JPG = GROUP / 32;          // K32 MFMA steps per group
-  // activation ring stage: A tile, then the group row sums
+  // activation ring stage: A tile, then the group row sums (rows padded to 64:
+  // one 64-lane copy per group)
+  static constexpr int SXR = BM < 64 ? 64 : BM;
   static constexpr int A = BM * 256;
-  static constexpr int SX = GPB * BM * 4;
+  static constexpr int SX = GPB * SXR * 4;
   static constexpr int A_STAGE = A + SX;
   // weight ring stage: packed blocks, scales, zero points
   static constexpr int B = 8 * BB;
@@ -70,9 +73,13 @@ struct A16Cfg {
   static constexpr int OFF_SZ = OFF_SS + SS;
   static constexpr int B_STAGE = OFF_SZ + SZ;
   // ring depths: the weights come from HBM with little reuse across
-  // workgroups (MoE experts), so their ring runs as deep as LDS allows
-  static constexpr int NA = 3 * A_STAGE + 2 * B_STAGE <= kLdsBytes ? 3 : 2;
-  static constexpr int NB_FIT = (kLdsBytes - NA * A_STAGE) / B_STAGE;
+  // workgroups (MoE experts), so their ring runs as deep as LDS allows.  Small
+  // tiles (WM = 1) keep to half of LDS so that two workgroups share a CU: one
+  // fills its rings while the other computes (short-K layers spend much of a
+  // tile in the prologue).
+  static constexpr int LDS_CAP = WM == 1 ? kLdsBytes / 2 : kLdsBytes;
+  static constexpr int NA = WM == 1 ? 2 : (3 * A_STAGE + 2 * B_STAGE <= LDS_CAP ? 3 : 2);
+  static constexpr int NB_FIT = (LDS_CAP - NA * A_STAGE) / B_STAGE;
   static constexpr int NB = NB_FIT > 6 ? 6 : NB_FIT;
   static constexpr int OFF_BRING = NA * A_STAGE;
   static constexpr int LDS = NA * A_STAGE + NB * B_STAGE;
@@ -88,10 +95,13 @@ struct A16Cfg {
   // step otherwise.
   static constexpr int AFTER_A = (NB > NA ? B_ISSUE : 0) + (NA - 2) * (A_ISSUE + B_ISSUE);
   static constexpr int MI = BM / WM / 16;             // 16-row blocks per wave
+  // small tiles (one wave per 16 columns, every wave all BM rows) are for
+  // MoE experts with few rows: row blocks past the tile's rows are skipped
+  static constexpr bool SKIP_ROWS = WM == 1;
   static constexpr float MAG = BITS == 4 ? 16.f : 8.f;
   static constexpr int ZSYM = BITS == 4 ? 8 : 4;
   static_assert(NB >= 2 && NB >= NA, "weight ring too shallow");
-  static_assert(LDS <= kLdsBytes, "rings exceed LDS");
+  static_assert(LDS <= LDS_CAP, "rings exceed LDS");
   static_assert(AFTER_A <= 63, "vmcnt range");
 };
 
@@ -104,15 +114,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int WM, int BITS, bool ZP, int GROUP, bool MOE>
-__global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const float *xs,
-                                                             int xs_rows) {
-  using C = A16Cfg<BM, WM, BITS, ZP, GROUP>;
+template <int BM, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
+__global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, const float *xs,
+                                                                 int xs_rows) {
+  using C = A16Cfg<BM, WM, WN, BITS, ZP, GROUP>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int q = lane >> 4, r16 = lane & 15;
 
   TileRows tr;
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
   const int ncol = min(nt0 * 16 + 64 * (wave & 1) + lane, a.n_tiles * 16 - 1);
   const uint8_t *ss_src = wexp + a.scales_offset + (uint64_t)ncol * gp * 2;
   const uint32_t *sz_src = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
-  const int sx_row = 64 * (wave % (BM / 64)) + lane;
+  const int sx_row = 64 * (wave % (C::SXR / 64)) + lane;
   const float *sx_src = xs + tr.x(a, sx_row);
 
   auto issue_a = [&](int kb) {
@@ -164,7 +174,7 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
 #pragma unroll
     for (int gi = 0; gi < C::GPB; ++gi)
       lds_dma4(sx_src + (int64_t)(kb * C::GPB + gi) * xs_rows,
-               st + C::A + (gi * BM + 64 * (wave % (BM / 64))) * 4);
+               st + C::A + (gi * C::SXR + 64 * (wave % (C::SXR / 64))) * 4);
   };
   auto issue_b = [&](int kb) {
     uint8_t *st = smem + C::OFF_BRING + (kb % C::NB) * C::B_STAGE;
@@ -180,11 +190,11 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
     if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + (wave & 1) * 256);
   };
 
-  f32x4 acc[C::MI][4];
+  f32x4 acc[C::MI][C::NJ];
 #pragma unroll
   for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue: activations NA - 1 stages ahead, weights NB - 1 stages ahead
   for (int s = 0; s < C::NB - 1; ++s) {
@@ -209,11 +219,11 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
     const uint8_t *st = smem + (kb % C::NA) * C::A_STAGE;
     const uint8_t *sb = smem + C::OFF_BRING + (kb % C::NB) * C::B_STAGE;
 
-    // weight operands of the wave's 4 column blocks for the 4 K32 steps
-    u32x4 bw[4][4];
+    // weight operands of the wave's NJ column blocks for the 4 K32 steps
+    u32x4 bw[C::NJ][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int blk = wn * 4 + j;
+    for (int j = 0; j < C::NJ; ++j) {
+      const int blk = wn * C::NJ + j;
       u32x4 v;
       if constexpr (BITS == 4) {
         v = *(const u32x4 *)(sb + blk * 1024 + 16 * lane);
@@ -227,10 +237,10 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
 #pragma unroll
     for (int gi = 0; gi < C::GPB; ++gi) {
       const int gg = kb * C::GPB + gi;
-      float c1[4], zf[4];
+      float c1[C::NJ], zf[C::NJ];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = wn * 64 + 16 * j + r16;
+      for (int j = 0; j < C::NJ; ++j) {
+        const int col = wn * 16 * C::NJ + 16 * j + r16;
         const uint32_t sbits = *(const uint16_t *)(sb + C::OFF_SS + col * 16 + 2 * (gg & 7));
         c1[j] = C::MAG * bf16_bits_to_f32(sbits);
         int z = C::ZSYM;
@@ -241,21 +251,22 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
 #pragma unroll
       for (int i = 0; i < C::MI; ++i) {
         const int r0 = wm * (BM / WM) + 16 * i;
+        if (C::SKIP_ROWS && r0 >= tr.rows) continue;  // workgroup-uniform
         const uint8_t *arow = st + (r0 + r16) * 256;
         u32x4 af[C::JPG];
 #pragma unroll
         for (int ss = 0; ss < C::JPG; ++ss)
           af[ss] = *(const u32x4 *)(arow + 16 * ((4 * (gi * C::JPG + ss) + q) ^ r16));
-        const f32x4 sx = *(const f32x4 *)(st + C::A + (gi * BM + r0 + 4 * q) * 4);
-        f32x4 g[4];
+        const f32x4 sx = *(const f32x4 *)(st + C::A + (gi * C::SXR + r0 + 4 * q) * 4);
+        f32x4 g[C::NJ];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) g[j] = ZP ? sx * zf[j] : sx;
+        for (int j = 0; j < C::NJ; ++j) g[j] = ZP ? sx * zf[j] : sx;
 #pragma unroll
         for (int ss = 0; ss < C::JPG; ++ss)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) g[j] = mfma_bf16(af[ss], bw[j][gi * C::JPG + ss], g[j]);
+          for (int j = 0; j < C::NJ; ++j) g[j] = mfma_bf16(af[ss], bw[j][gi * C::JPG + ss], g[j]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < C::NJ; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(g[j][e], c1[j], acc[i][j][e]);
       }
@@ -264,8 +275,8 @@ __global__ __launch_bounds__(128 * WM) void a16_tiled_kernel(GemmArgs a, const f
 
   // output through LDS (the ring is free once every wave is past its last stage)
   lds_barrier();
-  store_tile<C::MI, 4>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / WM),
-                       (nt0 + wn * 4) * 16, smem + wave * store_tile_lds_bytes<C::MI, 4>());
+  store_tile<C::MI, C::NJ>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / WM),
+                           (nt0 + wn * C::NJ) * 16, smem + wave * store_tile_lds_bytes<C::MI, C::NJ>());
 }
 
 // Group row sums of bf16 X: xs[g * rows + r] = factor * (sum of x[r, g*GROUP ..
@@ -294,50 +305,53 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *x, int6
   }
 }
 
-template <int BM, int WM, int BITS, bool ZP, int GROUP, bool MOE>
+template <int BM, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
 static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t tiles_cap, float *xs,
-                                     hipStream_t s) {
-  using C = A16Cfg<BM, WM, BITS, ZP, GROUP>;
-  static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MI, 4>(), "epilogue LDS");
-  const float factor = ZP ? 1.f : -(1.f + (float)C::ZSYM / C::MAG);
-  const int64_t rows_blocks = (xs_rows + 3) / 4;
-  hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3((unsigned)rows_blocks), dim3(256), 0, s,
-                     (const uint16_t *)a.x, a.ldx, (int)xs_rows, a.k, factor, xs);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                                     bool sums, hipStream_t s) {
+  using C = A16Cfg<BM, WM, WN, BITS, ZP, GROUP>;
+  static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MI, C::NJ>(), "epilogue LDS");
+  hipError_t e;
+  if (sums) {
+    const float factor = ZP ? 1.f : -(1.f + (float)C::ZSYM / C::MAG);
+    const int64_t rows_blocks = (xs_rows + 3) / 4;
+    hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3((unsigned)rows_blocks), dim3(256), 0, s,
+                       (const uint16_t *)a.x, a.ldx, (int)xs_rows, a.k, factor, xs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
   const int64_t n_tiles_wg = (a.n_tiles + 7) / 8;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  e = hipFuncSetAttribute((const void *)a16_tiled_kernel<BM, WM, BITS, ZP, GROUP, MOE>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  auto kern = a16_tiled_kernel<BM, WM, WN, BITS, ZP, GROUP, MOE>;
+  e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((a16_tiled_kernel<BM, WM, BITS, ZP, GROUP, MOE>), dim3((unsigned)(per_xcd * kXcds)),
-                     dim3(64 * C::WAVES), lds, s, a, (const float *)xs, (int)xs_rows);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(64 * C::WAVES), lds, s, a,
+                     (const float *)xs, (int)xs_rows);
   return hipGetLastError();
 }
 
-template <int BM, int WM, int BITS, bool ZP, bool MOE>
+template <int BM, int WM, int WN, int BITS, bool ZP, bool MOE>
 static hipError_t launch_group(const GemmArgs &a, int group, int64_t xs_rows, int64_t cap, float *xs,
-                               hipStream_t s) {
+                               bool sums, hipStream_t s) {
   switch (group) {
-    case 32: return launch_a16_tiled_t<BM, WM, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, s);
-    case 64: return launch_a16_tiled_t<BM, WM, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, s);
-    case 128: return launch_a16_tiled_t<BM, WM, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, s);
+    case 32: return launch_a16_tiled_t<BM, WM, WN, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, sums, s);
+    case 64: return launch_a16_tiled_t<BM, WM, WN, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, sums, s);
+    case 128: return launch_a16_tiled_t<BM, WM, WN, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, sums, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int BM, int WM, bool MOE>
+template <int BM, int WM, int WN, bool MOE>
 static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t xs_rows, int64_t cap,
-                             float *xs, hipStream_t s) {
+                             float *xs, bool sums, hipStream_t s) {
   const int g = d.group_size;
   switch (d.wtype) {
-    case QG_W_INT4: return launch_group<BM, WM, 4, false, MOE>(a, g, xs_rows, cap, xs, s);
-    case QG_W_UINT4: return launch_group<BM, WM, 4, true, MOE>(a, g, xs_rows, cap, xs, s);
-    case QG_W_INT3: return launch_group<BM, WM, 3, false, MOE>(a, g, xs_rows, cap, xs, s);
-    case QG_W_UINT3: return launch_group<BM, WM, 3, true, MOE>(a, g, xs_rows, cap, xs, s);
+    case QG_W_INT4: return launch_group<BM, WM, WN, 4, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_UINT4: return launch_group<BM, WM, WN, 4, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_INT3: return launch_group<BM, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_UINT3: return launch_group<BM, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
   }
   return hipErrorInvalidValue;
 }
@@ -347,19 +361,25 @@ uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m) {
 }
 
 // Dense: a.m rows in bm-row tiles.  MoE: the tile list a.tiles (capacity
-// tiles_cap) of 128-row tiles.  waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2).
+// tiles_cap) of bm-row tiles, bm = 128 (large experts) or kMoeSmallTileRows
+// (small experts: 8 waves of 16 columns each).  waves: 4 (2 x 2, one per
+// SIMD) or 8 (4 x 2).  sums = false reuses the group row sums already in ws.
 hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
-                            int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, hipStream_t s) {
+                            int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, bool sums,
+                            hipStream_t s) {
   if (a.k % 128 != 0) return hipErrorInvalidValue;
   float *xs = (float *)ws;
+  if (moe && bm == 64) return launch_fmt<64, 1, 8, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+  if (moe && bm == 32) return launch_fmt<32, 1, 8, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+  if (moe && bm != kMoeTileRows) return hipErrorInvalidValue;
   if (waves == 8) {
-    if (moe) return launch_fmt<kMoeTileRows, 4, true>(a, d, xs_rows, tiles_cap, xs, s);
-    return bm == 256 ? launch_fmt<256, 4, false>(a, d, xs_rows, 0, xs, s)
-                     : launch_fmt<128, 4, false>(a, d, xs_rows, 0, xs, s);
+    if (moe) return launch_fmt<kMoeTileRows, 4, 2, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+    return bm == 256 ? launch_fmt<256, 4, 2, false>(a, d, xs_rows, 0, xs, sums, s)
+                     : launch_fmt<128, 4, 2, false>(a, d, xs_rows, 0, xs, sums, s);
   }
-  if (moe) return launch_fmt<kMoeTileRows, 2, true>(a, d, xs_rows, tiles_cap, xs, s);
-  return bm == 256 ? launch_fmt<256, 2, false>(a, d, xs_rows, 0, xs, s)
-                   : launch_fmt<128, 2, false>(a, d, xs_rows, 0, xs, s);
+  if (moe) return launch_fmt<kMoeTileRows, 2, 2, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+  return bm == 256 ? launch_fmt<256, 2, 2, false>(a, d, xs_rows, 0, xs, sums, s)
+                   : launch_fmt<128, 2, 2, false>(a, d, xs_rows, 0, xs, sums, s);
 }
 
 }  // namespace qg

@@ -60,12 +60,28 @@ def moe_reference(layer, xdq, ids, by_token, verbose=False):
     return oracle.moe_gemm(wdq, xdq, ids, rows_by_token=by_token)
 
 
-@pytest.mark.parametrize("tiled_min", ["0", "1", "12"])
+# (QG_MOE_TILED_MIN, QG_MOE_SMALL) per split of the experts between kernels
+SPLITS = {
+    "skinny": ("0", "1"),        # every expert on the skinny kernel
+    "tiled": ("1", "1"),         # every expert with a row on 128-row tiles
+    "mixed": ("12", "1"),        # >= 12 rows: 128-row tiles; fewer: small tiles (integer formats)
+    "mixed_skinny": ("12", "0"), # >= 12 rows: 128-row tiles; fewer: skinny kernel
+    "small": ("1000", "1"),      # integer formats: every expert on 64-row small tiles
+    "small32": ("1000", "1", "32"),  # the same on 32-row small tiles
+}
+
+
+@pytest.mark.parametrize("split", list(SPLITS))
 @pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_UINT3, qg.W_MXFP4])
-def test_moe_small_all_row_modes(monkeypatch, wtype, tiled_min):
-    """All row modes, with experts split between the kernels by row count:
-    skinny only (0), tiled only (1: every expert with a row), and mixed (12)."""
-    monkeypatch.setenv("QG_MOE_TILED_MIN", tiled_min)
+def test_moe_small_all_row_modes(monkeypatch, wtype, split):
+    """All row modes, with the experts split between the kernels by row count
+    (the small-tile form exists for the integer formats only; MXFP4 runs the
+    skinny kernel where they would use it)."""
+    if wtype == qg.W_MXFP4 and split in ("mixed_skinny", "small", "small32"):
+        pytest.skip("same dispatch as another split for MXFP4")
+    monkeypatch.setenv("QG_MOE_TILED_MIN", SPLITS[split][0])
+    monkeypatch.setenv("QG_MOE_SMALL", SPLITS[split][1])
+    monkeypatch.setenv("QG_MOE_SMALL_BM", SPLITS[split][2] if len(SPLITS[split]) > 2 else "64")
     t, e, topk, n, k = 37, 16, 4, 80, 640
     g = 32 if wtype == qg.W_MXFP4 else 128
     ids = synth.route(synth.rng(1, wtype), t, e, topk)
@@ -157,8 +173,9 @@ def test_moe_w4a8_128_experts_padding_shape(tokens):
 @pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_MXFP4])
 def test_moe_tiled_multi_tile_experts(wtype):
     """Skewed routing over 8 experts with hundreds of rows each: experts span
-    several 128-row tiles with a partial last tile; small experts stay on the
-    skinny kernel (default split).  N = 200 leaves a partial column tile."""
+    several 128-row tiles with a partial last tile; small experts take the
+    small-tile form (integer formats) or the skinny kernel (MXFP4), the default
+    split.  N = 200 leaves a partial column tile."""
     t, e, topk, n, k = 512, 8, 2, 200, 1024
     g = 32 if wtype == qg.W_MXFP4 else 64
     mx = wtype == qg.W_MXFP4

@@ -35,23 +35,28 @@ def test_raster_visits_every_tile_once_for_oversized_grids():
         assert all(0 <= a < m and 0 <= b < n for a, b in live)
 
 
-def a16_rings(bm, bits, zp, group, waves=4):
+def a16_rings(bm, bits, zp, group, waves=4, small=False):
+    """Ring depths and per-stage load counts of the integer-format tiled kernel
+    (small: one wave per 16 columns, rings within half of LDS)."""
     gpb = 128 // group
-    a_stage = bm * 256 + gpb * bm * 4
+    a_stage = bm * 256 + gpb * max(bm, 64) * 4
     b_stage = 8 * 64 * (16 if bits == 4 else 12) + 128 * 16 + (128 * 4 if zp else 0)
-    na = 3 if 3 * a_stage + 2 * b_stage <= LDS else 2
-    nb = min(6, (LDS - na * a_stage) // b_stage)
+    cap = LDS // 2 if small else LDS
+    na = 2 if small else (3 if 3 * a_stage + 2 * b_stage <= cap else 2)
+    nb = min(6, (cap - na * a_stage) // b_stage)
     a_issue = bm * 256 // 1024 // waves + gpb
     b_issue = (8 if bits == 4 else 24) // waves + 1 + (1 if zp else 0)
     after = (b_issue if nb > na else 0) + (na - 2) * (a_issue + b_issue)
-    return na, nb, a_issue, b_issue, after, na * a_stage + nb * b_stage
+    return na, nb, a_issue, b_issue, after, na * a_stage + nb * b_stage, cap
 
 
 def test_a16_tiled_ring_waits_cover_each_stage():
-    for bm, bits, zp, group, waves in itertools.product([128, 256], [3, 4], [False, True],
-                                                        [32, 64, 128], [4, 8]):
-        na, nb, ai, bi, after, lds = a16_rings(bm, bits, zp, group, waves)
-        assert 2 <= na <= nb and lds <= LDS and after <= 63
+    # 128- and 256-row tiles (4 or 8 waves) and the 32- and 64-row small tiles (8 waves)
+    shapes = [(bm, w, False) for bm in (128, 256) for w in (4, 8)] + [(32, 8, True), (64, 8, True)]
+    for (bm, waves, small), bits, zp, group in itertools.product(shapes, [3, 4], [False, True],
+                                                               [32, 64, 128]):
+        na, nb, ai, bi, after, lds, cap = a16_rings(bm, bits, zp, group, waves, small)
+        assert 2 <= na <= nb and lds <= cap and after <= 63
         for kbs in range(1, 13):
             seq = []
             for s in range(nb - 1):
@@ -89,3 +94,18 @@ def test_moe_tile_list_capacity_bounds_the_tiles():
         tiles = sum(-(-c // 128) for c in counts if c >= min_rows)
         cap = pairs // 128 + min(e, pairs // min_rows) + 1
         assert tiles <= cap
+
+
+def test_moe_small_tile_list_capacity_bounds_the_tiles():
+    """Small tiles (experts with 1 .. min_rows - 1 rows, 64-row tiles):
+    tiles <= pairs / 64 + min(E, pairs) + 1."""
+    import numpy as np
+    r = np.random.default_rng(1)
+    for _ in range(200):
+        e = int(r.integers(1, 300))
+        pairs = int(r.integers(1, 40000))
+        min_rows = int(r.choice([2, 12, 64, 1000]))
+        cuts = np.sort(r.integers(0, pairs + 1, e - 1))
+        counts = np.diff(np.concatenate([[0], cuts, [pairs]]))
+        tiles = sum(-(-c // 64) for c in counts if 1 <= c < min_rows)
+        assert tiles <= pairs // 64 + min(e, pairs) + 1
