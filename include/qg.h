@@ -67,7 +67,7 @@ extern "C" {
 #endif
 
 #define QG_ABI_VERSION 1
-#define QG_LAYOUT_VERSION 1
+#define QG_LAYOUT_VERSION 2
 
 typedef enum {
   QG_OK = 0,

@@ -20,7 +20,7 @@ S_BF16, S_E8M0 = 0, 1
 A_BF16, A_MXFP8 = 0, 1
 O_BF16, O_F32 = 0, 1
 ROWS_BY_TOKEN, ROWS_BY_PAIR, ROWS_SORTED = 0, 1, 2
-ABI_VERSION, LAYOUT_VERSION = 1, 1
+ABI_VERSION, LAYOUT_VERSION = 1, 2
 
 # every symbol include/qg.h declares
 EXPORTS = (

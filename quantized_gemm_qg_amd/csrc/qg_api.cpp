@@ -34,7 +34,8 @@ static bool env_variant(Variant *v) {
   if (sscanf(s, "%d,%d,%d,%d", &T, &KR, &W, &S) != 4) return false;
   if (T < 1 || KR < 1 || W < 1 || W > 16 || S < 1) return false;
   v->kind = 0;
-  v->bn = 0;
+  v->bm = 0;
+  v->tbn = 0;
   v->T = T;
   v->KR = KR;
   v->W = W;
@@ -78,7 +79,7 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
   const bool long_k = (k_blocks + KR - 1) / KR > 16;  // K gets split anyway
   while (!long_k && T > 1 && (int64_t)((n_tiles + T - 1) / T) * m_tiles < 128) T /= 2;
   KR = clamp_kr(d, T, KR);
-  Variant v{0, T, KR, 1, 1, 0};
+  Variant v{0, T, KR, 1, 1, 0, 0};
   const int64_t n_blocks = (n_tiles + T - 1) / T;
   const int waves_k = (k_blocks + KR - 1) / KR;
   int splits = 1;
@@ -106,6 +107,33 @@ static void sanitize(const qg_layer_desc &d, Variant *v) {
 // Large M: the LDS-tiled kernels, scaled MFMA for MX (BM x 256 tiles, from
 // M = 128) and bf16 MFMA for the integer formats (BM x 128 tiles, from M = 256,
 // where the 16-row skinny kernel stops being weight-bound).
+// Columns of the MX tiled kernel's workgroup tile.  One workgroup runs per CU
+// (the LDS ring fills it), so the tile count should fill whole rounds of the
+// 256 CUs: among 256, 224 and 192 columns take the one with the best
+// (round fill x column fill), discounted 3% per 32 columns below 256 for the
+// lower reuse of the activation tile.  QG_MX_BN overrides.
+static int mx_tile_cols(int64_t n, int64_t m, int bm) {
+  const char *e = getenv("QG_MX_BN");
+  if (mx_tiled_waves() != 8) return 256;  // the 4-wave form is built for 256 only
+  if (e && (atoi(e) == 192 || atoi(e) == 224 || atoi(e) == 256)) return atoi(e);
+  constexpr int kCus = 256;
+  const int64_t m_tiles = (m + bm - 1) / bm;
+  int best = 256;
+  double best_eff = 0.0;
+  for (int bn : {256, 224, 192}) {
+    const int64_t n_groups = (n + bn - 1) / bn;
+    const int64_t tiles = m_tiles * n_groups;
+    const int64_t rounds = (tiles + kCus - 1) / kCus;
+    const double eff = (double)tiles / (double)(rounds * kCus) * (double)n / (double)(n_groups * bn) *
+                       (1.0 - 0.03 * (256 - bn) / 32);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = bn;
+    }
+  }
+  return best;
+}
+
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   if (w.desc.k % 128 != 0) return false;
   const char *s = getenv("QG_TILED");
@@ -121,7 +149,7 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   int bm = m >= 256 ? 256 : 128;
   const char *b = getenv("QG_TILED_BM");
   if (b && (atoi(b) == 128 || atoi(b) == 256)) bm = atoi(b);
-  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm};
+  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, mx ? mx_tile_cols(w.desc.n, m, bm) : 128};
   return true;
 }
 
@@ -143,7 +171,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, Variant *v
   if ((int64_t)W * KR * gpb > w.groups_padded) return false;  // scale reads stay in the row
   const uint64_t lds = align_up((uint64_t)m * ((uint64_t)W * KR * 256 + 16), 256) + (uint64_t)W * T * m * 64;
   if (lds > 160 * 1024) return false;
-  *v = Variant{3, T, KR, W, 1, 0};
+  *v = Variant{3, T, KR, W, 1, 0, 0};
   return true;
 }
 
@@ -322,6 +350,7 @@ static void fill_weight(const qg_layer_desc *d, const Layout &L, void *dev, uint
 static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) {
   if (m <= 0) return 0;
   if (v.kind == 2) return a16_tiled_ws_bytes(w.desc, m);
+  if (v.kind == 1) return mx_tiled_ws_bytes(m, w.k_blocks);
   if (v.splits <= 1) return 0;
   const int64_t m_tiles = (m + 15) / 16;
   const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
@@ -484,11 +513,11 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
     a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
   }
   if (v.kind == 1)
-    he = launch_mx_tiled(a, v.bn, false, 0, mx_tiled_waves(), stream);
+    he = launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream);
   else if (v.kind == 3)
     he = launch_decode_a16(a, d, v, stream);
   else if (v.kind == 2)
-    he = launch_a16_tiled(a, d, v.bn, false, m, 0, a16_tiled_waves(), ws, true, stream);
+    he = launch_a16_tiled(a, d, v.bm, false, m, 0, a16_tiled_waves(), ws, true, stream);
   else
     he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -584,7 +613,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     a.tiles = tiles;
     a.group_m = moe_group_m();
     if (L.is_mx) {
-      he = launch_mx_tiled(a, kMoeTileRows, true, cap, mx_tiled_waves(), stream);
+      he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream);
     } else {
       void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);
       he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, a16_tiled_waves(), xs, true,
@@ -637,8 +666,7 @@ extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *b
   if (v.kind == 3)
     snprintf(buf, buf_bytes, "a16_decode T=%d KR=%d W=%d", v.T, v.KR, v.W);
   else if (v.kind == 1 || v.kind == 2)
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", L.is_mx ? "mx" : "a16", v.bn,
-             L.is_mx ? 256 : 128);
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", L.is_mx ? "mx" : "a16", v.bm, v.tbn);
   else
     snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
              v.KR, v.W, v.splits);

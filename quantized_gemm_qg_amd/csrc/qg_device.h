@@ -257,9 +257,11 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const TileRows &tr
     // the wave's own LDS accesses complete in order; this keeps the compiler
     // from moving the reads above the writes
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (int pass = 0; pass < (16 * cpr + 63) / 64; ++pass) {
+    for (int pass = 0; pass < (16 + rows_per_pass - 1) / rows_per_pass; ++pass) {
       const int rr = pass * rows_per_pass + lane / cpr, c = lane % cpr;
-      if (rr >= 16) continue;  // 16-column bf16 tiles: 32 lanes cover the block
+      // lanes past the pass's rows idle (cpr need not divide 64; 16-column
+      // bf16 tiles cover the block with 32 lanes)
+      if (lane >= rows_per_pass * cpr || rr >= 16) continue;
       const u32x4 v = *(const u32x4 *)(lds + rr * pitch + 16 * c);
       const int yr = yrow[16 * i + rr];
       const int col = col0 + c * (16 / el);

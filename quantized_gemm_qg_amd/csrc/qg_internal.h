@@ -22,9 +22,13 @@
 //     * e2m1 (block 1024 B, 16 B per lane): the lane's 32 codes k = 128 kb +
 //       32 q + e in standard order (two per byte, low nibble first), i.e. the
 //       16-B chunk of the standard row that one 16x16x128 scaled MFMA lane reads.
-//   scales  A16: bf16 [n_pad][groups_padded] (groups rounded up to 32);  MXFP4: e8m0 [n_pad][4][kb_pad]
-//           (byte (n, q, kb) scales k = 128 kb + 32 q .. +31), kb_pad = k_blocks
-//           rounded up to 4 so a lane reads four k-blocks' scales as one dword.
+//   scales  A16: bf16 [n_pad][groups_padded] (groups rounded up to 32).
+//           MXFP4: e8m0 in 256-byte units [n_tile][kb_pad / 4], each
+//           [16 columns c][4 quarters q][4 k-blocks]: byte (n, q, kb) scales
+//           k = 128 kb + 32 q .. +31 of column n = 16 n_tile + c; kb_pad =
+//           k_blocks rounded up to 4.  A lane reads four k-blocks' scales of
+//           its (column, quarter) as one dword, and 64 lanes read one unit
+//           (a whole n-tile) as 256 contiguous bytes.
 //   zeros   UINT formats: [n_pad][groups_padded / 8] uint32, group g in nibble
 //           g % 8 of word g / 8.
 //
@@ -90,6 +94,9 @@ struct GemmArgs {
   // activations / output
   const void *x;
   const uint8_t *x_scales;
+  // dense MX tiled kernel: the activation scales regrouped by K step,
+  // dword [kb * m + row] = the 4 e8m0 scales of row `row` in K step kb
+  const uint32_t *x_scales_t;
   int64_t ldx;
   void *y;
   int64_t ldy;
@@ -125,7 +132,8 @@ struct Variant {
   int KR;      // k-blocks per wave
   int W;       // waves per workgroup (split of K inside the workgroup)
   int splits;  // split of K across workgroups
-  int bn;      // tiled: workgroup tile rows (128 or 256); tiles are bn x 256 (MX) or bn x 128
+  int bm;      // tiled: workgroup tile rows (128 or 256)
+  int tbn;     // tiled: workgroup tile columns (MX: 192, 224 or 256; integer formats: 128)
 };
 
 Variant select_dense(const qg_weight &w, int64_t m);
@@ -149,8 +157,11 @@ hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Varian
 // kMoeSmallTileRows-row tile each.
 constexpr int kMoeTileRows = 128;
 constexpr int kMoeSmallTileRows = 64;
-hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, int waves,
-                           hipStream_t s);
+// Dense launches first regroup the activation scales by K step into ws
+// (mx_tiled_ws_bytes); MoE launches read them in place.
+hipError_t launch_mx_tiled(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
+                           void *ws, hipStream_t s);
+uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks);
 int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // Integer formats at large M: group row sums of X into ws, then the tiled
 // kernel.  ws holds (K / group) * m floats (a16_tiled_ws_bytes).

@@ -347,8 +347,10 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
   for (int t = 0; t < T; ++t) {
     const int n = min(nt0 + t, a.n_tiles - 1) * 16 + r16;
 #pragma unroll
-    for (int kb = 0; kb < KR; ++kb)
-      wsc[t][kb] = sbase[((uint64_t)n * 4 + q) * a.kb_pad + min(kb0 + kb, kbs - 1)];
+    for (int kb = 0; kb < KR; ++kb) {
+      const int b = min(kb0 + kb, kbs - 1);
+      wsc[t][kb] = sbase[((uint64_t)(n >> 4) * (a.kb_pad >> 2) + (b >> 2)) * 256 + ((n & 15) * 4 + q) * 4 + (b & 3)];
+    }
   }
   // keep every load above this point: the wave waits once for all of them
   __builtin_amdgcn_sched_barrier(0);

@@ -149,7 +149,9 @@ void repack_expert(const qg_layer_desc &d, const Layout &L, const uint8_t *codes
     for (int64_t n = 0; n < d.n; ++n)
       for (int i = 0; i < nb32; ++i) {
         const int kb = i / 4, q = i % 4;
-        dst[L.scales_offset + ((uint64_t)n * 4 + q) * L.kb_pad + kb] = scales[n * nb32 + i];
+        // 256-byte unit (n-tile, kb / 4): [16 columns][4 quarters][4 k-blocks]
+        const uint64_t unit = (uint64_t)(n / 16) * (L.kb_pad / 4) + kb / 4;
+        dst[L.scales_offset + unit * 256 + ((n % 16) * 4 + q) * 4 + kb % 4] = scales[n * nb32 + i];
       }
     return;
   }

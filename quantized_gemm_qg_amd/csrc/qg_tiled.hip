@@ -6,8 +6,9 @@
 // e8m0 block scales directly (v_mfma_scale_f32_16x16x128_f8f6f4), so nothing is
 // dequantized: the kernel only moves bytes.
 //
-// Tiling: a workgroup computes a BM x 256 tile of Y with WM x WN waves, each
-// (BM / WM) x (256 / WN) as blocks of 16 x 16.  The default is 8 waves (4 x 2,
+// Tiling: a workgroup computes a BM x BN tile of Y (BN = 256, or 224 / 192 so
+// that the tile count fills whole rounds of the 256 CUs) with WM x WN waves,
+// each (BM / WM) x (BN / WN) as blocks of 16 x 16.  The default is 8 waves (4 x 2,
 // two per SIMD, wave tile 64 x 128, 128 fp32 accumulators per lane): while one
 // wave of a SIMD waits on its LDS reads or the stage barrier, the other keeps
 // the matrix core busy; LDS traffic stays at 256 B per MFMA (16 KB per wave
@@ -19,14 +20,20 @@
 //   A   BM rows x 128 e4m3 bytes; each row's eight 16-byte chunks are stored
 //       in XOR-swizzled order (chunk c at slot c ^ (row & 7)) so the 16 rows
 //       of an MFMA fragment read hit all LDS banks without padding;
-//   B   16 packed weight blocks of 1 KB copied verbatim (the packed layout
-//       already stores each lane's 16-byte B operand contiguously);
-//   SA  the four e8m0 scales of each activation row for this K step;
-//   SW  for each of the 256 weight columns and quarters q, the dword holding
-//       its e8m0 scales of K steps kb & ~3 .. +3.
-// Every wave issues the same number of loads per stage, so "stage kb has
-// landed" is a wait until at most one stage of the wave's loads is
-// outstanding, followed by a workgroup barrier.  Inside a K step the next row
+//   B   BN / 16 packed weight blocks of 1 KB copied verbatim (the packed
+//       layout already stores each lane's 16-byte B operand contiguously);
+//   SA  the four e8m0 scales of each activation row for this K step (dense
+//       launches read them from a copy regrouped by K step, so one SA copy
+//       reads 256 contiguous bytes instead of a dword from each of 64 rows).
+// The weight scales change every fourth K step only: a separate two-slot ring
+// SW holds, for each of the BN weight columns and quarters q, the dword with
+// its e8m0 scales of K steps 4j .. 4j + 3, loaded with stage 4j.  (Scale loads
+// gather one dword per lane from as many cache lines, so they cost the
+// address unit far more than their bytes suggest.)  Each wave counts its own
+// loads: "stage kb has landed" is a wait until only the wave's loads of stage
+// kb + 1 are outstanding (where the blocks do not divide evenly, the last
+// waves copy the final block again, the same bytes to the same place; only the
+// first BM / 64 waves copy SA), followed by a workgroup barrier.  Inside a K step the next row
 // block's LDS reads are scheduled ahead of the current block's 8 MFMAs.
 //
 // Work order: workgroups are dealt round-robin to the 8 XCDs; the tile index
@@ -40,32 +47,37 @@
 
 namespace qg {
 
-constexpr int kTBN = 256;   // tile columns
 constexpr int kStages = 3;
 
-// BM x 256 tile, WM x WN waves, each wave (BM / WM) x (256 / WN)
-template <int BM, int WM, int WN>
+// BM x BN tile, WM x WN waves, each wave (BM / WM) x (BN / WN)
+template <int BM, int BN, int WM, int WN>
 struct MxCfg {
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NBLK = BN / 16;                      // packed n-tiles per tile
   static constexpr int A = BM * 128;
-  static constexpr int B = (kTBN / 16) * 1024;   // 16 KB
+  static constexpr int B = NBLK * 1024;
   static constexpr int SA = BM * 4;
-  static constexpr int SW = kTBN * 4 * 4;        // 4 KB
-  static constexpr int STAGE = A + B + SA + SW;
+  static constexpr int SW = BN * 4 * 4;                     // NBLK pieces of 256 B
+  static constexpr int STAGE = A + B + SA;
+  static constexpr int OFF_SW = 3 * STAGE;                  // the two SW slots
+  static constexpr int LDS = OFF_SW + 2 * SW;
   static constexpr int A_LOADS = BM * 128 / 1024 / WAVES;  // 1-KB copies of A per wave
-  static constexpr int B_LOADS = 16 / WAVES;                // 1-KB blocks of B per wave
-  static constexpr int SW_LOADS = 16 / WAVES;               // 256-B pieces of SW per wave
-  static constexpr int LOADS = A_LOADS + B_LOADS + 1 + SW_LOADS;  // + one SA piece
+  static constexpr int B_LOADS = (NBLK + WAVES - 1) / WAVES;  // 1-KB blocks of B per wave
+  static constexpr int SW_LOADS = B_LOADS;                  // 256-B pieces of SW per wave
+  static constexpr int SA_WAVES = BM / 64;                  // waves that copy a 256-B SA piece
+  static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int MB = BM / WM / 16;                   // 16-row blocks per wave
-  static constexpr int NB = kTBN / WN / 16;                 // 16-column blocks per wave
-  static_assert(A_LOADS >= 1 && B_LOADS >= 1 && SW_LOADS >= 1, "too many waves");
-  static_assert(WAVES >= BM / 64 || BM / 64 % WAVES == 0, "SA pieces");
+  static constexpr int NB = BN / WN / 16;                   // 16-column blocks per wave
+  static_assert(BN % (16 * WN) == 0, "column blocks per wave");
+  static_assert(A_LOADS >= 1 && BM * 128 % (1024 * WAVES) == 0, "A copies per wave");
+  static_assert(WAVES >= SA_WAVES, "SA pieces");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int WM, int WN, bool MOE>
+template <int BM, int BN, int WM, int WN, bool MOE>
 __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
-  using C = MxCfg<BM, WM, WN>;
+  using C = MxCfg<BM, BN, WM, WN>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,8 +88,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   TileRows tr;
   int tn;
   const uint8_t *wexp;
-  if (!tiled_work<BM>(a, MOE, (a.n_tiles * 16 + kTBN - 1) / kTBN, &tr, &tn, &wexp)) return;
-  const int nt0 = tn * (kTBN / 16);  // first 16-column n-tile
+  if (!tiled_work<BM>(a, MOE, (a.n_tiles + C::NBLK - 1) / C::NBLK, &tr, &tn, &wexp)) return;
+  const int nt0 = tn * C::NBLK;      // first 16-column n-tile
   const int kbs = a.k_blocks;
   const int kq = a.k >> 5;           // activation scale bytes per row
   const uint8_t *x = (const uint8_t *)a.x;
@@ -92,20 +104,26 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
   }
   const uint8_t *b_base = wexp + 16 * lane;
+  // copy i of this wave: tile block (and LDS slot) min(B_LOADS wave + i, NBLK - 1)
+  auto blk_of = [&](int i) { return min(wave * C::B_LOADS + i, C::NBLK - 1); };
   uint32_t b_blk[C::B_LOADS];  // first packed block of each of the wave's n-tiles
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i)
-    b_blk[i] = (uint32_t)min(nt0 + wave * C::B_LOADS + i, a.n_tiles - 1) * kbs;
-  // SA: BM rows of 4 bytes = BM / 64 pieces of 256 B; waves past them repeat
-  // earlier pieces (same bytes to the same place)
-  const int sa_piece = wave % (BM / 64);
-  const uint8_t *sa_src = a.x_scales + tr.x(a, sa_piece * 64 + lane) * kq;
+    b_blk[i] = (uint32_t)min(nt0 + blk_of(i), a.n_tiles - 1) * kbs;
+  // SA: BM rows of 4 bytes = BM / 64 pieces of 256 B, one per wave of the
+  // first BM / 64
+  const bool sa_wave = wave < C::SA_WAVES;
+  const int64_t sa_row = tr.x(a, (sa_wave ? wave : 0) * 64 + lane);
+  // per K step: + 4 bytes (MoE, rows of kq bytes) or + 4 m bytes (dense, by step)
+  const uint8_t *sa_src = MOE ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
+  const int64_t sa_step = MOE ? 4 : 4 * (int64_t)a.m;
   uint32_t sw_off[C::SW_LOADS];
 #pragma unroll
   for (int i = 0; i < C::SW_LOADS; ++i) {
-    const int e = (wave * C::SW_LOADS + i) * 64 + lane;  // (column, quarter) pair
-    const int n = min(nt0 * 16 + (e >> 2), a.n_tiles * 16 - 1);
-    sw_off[i] = (uint32_t)(((uint64_t)n * 4 + (e & 3)) * a.kb_pad);
+    // lane = (column, quarter) pair of the n-tile: dword `lane` of its 256-B
+    // scale unit for K steps 4j .. 4j + 3, at + 256 j
+    const int nt = min(nt0 + blk_of(i), a.n_tiles - 1);
+    sw_off[i] = (uint32_t)((uint64_t)nt * (a.kb_pad >> 2) * 256 + 4 * lane);
   }
 
   auto issue = [&](int kb, int buf) {
@@ -116,12 +134,13 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
       lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + (wave * C::B_LOADS + i) * 1024);
-    lds_dma4(sa_src + 4 * kb, st + C::A + C::B + sa_piece * 256);
-    const uint8_t *wk = wsc + (kb & ~3);
+      lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + blk_of(i) * 1024);
+    if (sa_wave) lds_dma4(sa_src + sa_step * kb, st + C::A + C::B + wave * 256);
+    if ((kb & 3) == 0) {
+      uint8_t *sws = smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW;
 #pragma unroll
-    for (int i = 0; i < C::SW_LOADS; ++i)
-      lds_dma4(wk + sw_off[i], st + C::A + C::B + C::SA + (wave * C::SW_LOADS + i) * 256);
+      for (int i = 0; i < C::SW_LOADS; ++i) lds_dma4(wsc + 64 * kb + sw_off[i], sws + blk_of(i) * 256);
+    }
   };
 
   f32x4 acc[C::MB][C::NB];
@@ -133,8 +152,16 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   issue(0, 0);
   if (kbs > 1) issue(1, 1);
   for (int kb = 0; kb < kbs; ++kb) {
+    // outstanding after stage kb: this wave's loads of stage kb + 1
     if (kb + 1 < kbs) {
-      QG_WAIT_VMCNT(C::LOADS);
+      const bool sw_next = ((kb + 1) & 3) == 0;
+      if (sa_wave) {
+        if (sw_next) QG_WAIT_VMCNT(C::AB_LOADS + 1 + C::SW_LOADS);
+        else QG_WAIT_VMCNT(C::AB_LOADS + 1);
+      } else {
+        if (sw_next) QG_WAIT_VMCNT(C::AB_LOADS + C::SW_LOADS);
+        else QG_WAIT_VMCNT(C::AB_LOADS);
+      }
     } else {
       QG_WAIT_VMCNT(0);
     }
@@ -148,7 +175,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
       const int blk = wn * C::NB + j;
       const u32x4 v = *(const u32x4 *)(st + C::A + blk * 1024 + 16 * lane);
       bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const uint32_t sw = *(const uint32_t *)(st + C::A + C::B + C::SA + ((blk * 16 + r16) * 4 + q) * 4);
+      const uint32_t sw = *(const uint32_t *)(smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW +
+                                              ((blk * 16 + r16) * 4 + q) * 4);
       bsc[j] = (int)((sw >> (8 * (kb & 3))) & 0xFFu);
     }
     auto read_a = [&](int i, i32x8 &af, int &asc) {
@@ -185,37 +213,67 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
                            (nt0 + wn * C::NB) * 16, smem + wave * store_tile_lds_bytes<C::MB, C::NB>());
 }
 
-template <int BM, int WM, int WN, bool MOE>
+// Activation scales regrouped by K step: out[kb * m + r] holds the 4 bytes of
+// row r's scales for K step kb (bytes 4 kb .. 4 kb + 3 of the row).
+__global__ __launch_bounds__(256) void mx_scales_by_step_kernel(const uint8_t *xs, int m, int kq,
+                                                                int kbs, uint32_t *out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)kbs * m) return;
+  const int r = (int)(i % m), kb = (int)(i / m);
+  const uint8_t *p = xs + (int64_t)r * kq + 4 * kb;
+  out[i] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+}
+
+uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) { return align_up((uint64_t)(m * k_blocks) * 4, 256); }
+
+template <int BM, int BN, int WM, int WN, bool MOE>
 static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
-  using C = MxCfg<BM, WM, WN>;
-  static_assert(kStages * C::STAGE >= C::WAVES * store_tile_lds_bytes<C::MB, C::NB>(), "epilogue LDS");
+  using C = MxCfg<BM, BN, WM, WN>;
+  static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MB, C::NB>(), "epilogue LDS");
   const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
-  const int64_t n_tiles_wg = (a.n_tiles * 16 + kTBN - 1) / kTBN;
+  const int64_t n_tiles_wg = (a.n_tiles + C::NBLK - 1) / C::NBLK;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const size_t lds = (size_t)kStages * C::STAGE;
-  hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BM, WM, WN, MOE>,
+  const size_t lds = (size_t)C::LDS;
+  hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BM, BN, WM, WN, MOE>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mx_tiled_kernel<BM, WM, WN, MOE>), dim3((unsigned)(per_xcd * kXcds)),
+  hipLaunchKernelGGL((mx_tiled_kernel<BM, BN, WM, WN, MOE>), dim3((unsigned)(per_xcd * kXcds)),
                      dim3(C::THREADS), lds, s, a);
   return hipGetLastError();
 }
 
-// Dense: bm-row tiles (128 or 256), tiles bm x 256.  MoE: the tile list a.tiles
-// (capacity tiles_cap) of kMoeTileRows-row tiles.  waves: 4 (2 x 2, one per
-// SIMD) or 8 (4 x 2, two per SIMD).
-hipError_t launch_mx_tiled(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, int waves,
-                           hipStream_t s) {
-  if (a.k % 128 != 0) return hipErrorInvalidValue;
-  if (waves == 8) {
-    if (moe) return launch_mx_tiled_bm<kMoeTileRows, 4, 2, true>(a, tiles_cap, s);
-    return bm == 256 ? launch_mx_tiled_bm<256, 4, 2, false>(a, 0, s)
-                     : launch_mx_tiled_bm<128, 4, 2, false>(a, 0, s);
+// Dense: bm-row tiles (128 or 256) of bn columns (192, 224 or 256 with 8
+// waves; 256 with 4).  MoE: the tile list a.tiles (capacity tiles_cap) of
+// kMoeTileRows x 256 tiles.  waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2, two
+// per SIMD).
+hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
+                           void *ws, hipStream_t s) {
+  if (a_in.k % 128 != 0) return hipErrorInvalidValue;
+  GemmArgs a = a_in;
+  if (!moe) {
+    if (!ws) return hipErrorInvalidValue;
+    const int64_t n = (int64_t)a.m * a.k_blocks;
+    hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       a.x_scales, a.m, a.k >> 5, a.k_blocks, (uint32_t *)ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.x_scales_t = (const uint32_t *)ws;
   }
-  if (moe) return launch_mx_tiled_bm<kMoeTileRows, 2, 2, true>(a, tiles_cap, s);
-  return bm == 256 ? launch_mx_tiled_bm<256, 2, 2, false>(a, 0, s)
-                   : launch_mx_tiled_bm<128, 2, 2, false>(a, 0, s);
+  if (waves == 8) {
+    if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true>(a, tiles_cap, s);
+    if (bm == 256) {
+      if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false>(a, 0, s);
+      if (bn == 224) return launch_mx_tiled_bm<256, 224, 4, 2, false>(a, 0, s);
+      return launch_mx_tiled_bm<256, 256, 4, 2, false>(a, 0, s);
+    }
+    if (bn == 192) return launch_mx_tiled_bm<128, 192, 4, 2, false>(a, 0, s);
+    if (bn == 224) return launch_mx_tiled_bm<128, 224, 4, 2, false>(a, 0, s);
+    return launch_mx_tiled_bm<128, 256, 4, 2, false>(a, 0, s);
+  }
+  if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 2, 2, true>(a, tiles_cap, s);
+  return bm == 256 ? launch_mx_tiled_bm<256, 256, 2, 2, false>(a, 0, s)
+                   : launch_mx_tiled_bm<128, 256, 2, 2, false>(a, 0, s);
 }
 
 }  // namespace qg

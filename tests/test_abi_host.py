@@ -131,7 +131,8 @@ def _unpack_packed(d, buf):
         for nn in range(n):
             for i in range(k // 32):
                 kb, q = divmod(i, 4)
-                sc[nn, i] = buf[L["s_off"] + (nn * 4 + q) * L["kb_pad"] + kb]
+                unit = (nn // 16) * (L["kb_pad"] // 4) + kb // 4
+                sc[nn, i] = buf[L["s_off"] + unit * 256 + ((nn % 16) * 4 + q) * 4 + kb % 4]
         return codes, sc, None
     s16 = np.frombuffer(bytes(buf[L["s_off"]:L["s_off"] + d.n * L["gpad"] * 2]), np.uint16)
     sc = s16.reshape(d.n, L["gpad"])[:, :G].astype(np.int64)

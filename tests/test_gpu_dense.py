@@ -165,11 +165,15 @@ def test_w4a8_mx_full_size_sampled_rows(nk):
     _check(layer, acts, m, rows=rows)
 
 
+@pytest.mark.parametrize("bn", ["256", "224", "192"])
 @pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (300, 200, 640), (777, 1040, 4096)])
-def test_mx_tiled_large_m_ragged(m, n, k):
-    """The LDS-tiled MX kernel (M >= 256) with partial row and column tiles."""
+def test_mx_tiled_large_m_ragged(monkeypatch, m, n, k, bn):
+    """The LDS-tiled MX kernel (M >= 256) with partial row and column tiles,
+    at each tile width (224 and 192 columns split their blocks unevenly over
+    the 8 waves)."""
+    monkeypatch.setenv("QG_MX_BN", bn)
     layer = Layer(qg.W_MXFP4, n, k, 32, seed=m)
-    assert "tiled" in qg.describe_dispatch(layer.w, m)
+    assert f"tiled BM=256 BN={bn}" in qg.describe_dispatch(layer.w, m)
     _check(layer, Acts(True, m, k, seed=m), m)
 
 

@@ -109,3 +109,53 @@ def test_moe_small_tile_list_capacity_bounds_the_tiles():
         counts = np.diff(np.concatenate([[0], cuts, [pairs]]))
         tiles = sum(-(-c // 64) for c in counts if 1 <= c < min_rows)
         assert tiles <= pairs // 64 + min(e, pairs) + 1
+
+
+def test_tile_epilogue_stores_every_row_chunk_once():
+    """The tiled kernels' epilogue moves a 16-row block of a wave tile of 16 NJ
+    columns out in passes: lane l takes 16-byte chunk l % cpr of row
+    pass * (64 // cpr) + l // cpr (cpr = chunks per row), lanes past the
+    pass's rows idle.  Every (row, chunk) must be stored exactly once for
+    every width the kernels use (NJ = 1 .. 8, bf16 and fp32 outputs), also
+    where cpr does not divide 64 (NJ = 3, 5, 6, 7)."""
+    for nj in range(1, 9):
+        for el in (2, 4):
+            cpr = 16 * nj * el // 16
+            rpp = 64 // cpr
+            seen = {}
+            for p in range((16 + rpp - 1) // rpp):
+                for lane in range(64):
+                    rr, c = p * rpp + lane // cpr, lane % cpr
+                    if lane >= rpp * cpr or rr >= 16:
+                        continue
+                    seen[(rr, c)] = seen.get((rr, c), 0) + 1
+            assert sorted(seen) == [(r, c) for r in range(16) for c in range(cpr)], (nj, el)
+            assert set(seen.values()) == {1}, (nj, el)
+
+
+def test_mx_tiled_waits_cover_each_stage():
+    """MX tiled kernel: stage kb = A_LOADS + B_LOADS copies, + 1 SA copy on the
+    first BM / 64 waves, + SW_LOADS weight-scale copies when kb % 4 == 0 (they
+    fill the scale ring slot of steps kb .. kb + 3).  Stages 0 and 1 go out in
+    the prologue, stage kb + 2 after the barrier of step kb; step kb waits
+    until only this wave's loads of stage kb + 1 are outstanding.  Replayed
+    per wave kind: every load of stage kb (and of the scale group of step kb)
+    has retired at the wait of step kb."""
+    for ab, swl in ((6, 2), (6, 2), (5, 2), (4, 1)):
+        for sa_wave in (True, False):
+            def stage(kb):
+                return [("AB", kb)] * ab + ([("SA", kb)] if sa_wave else []) + \
+                       ([("SW", kb)] * swl if kb % 4 == 0 else [])
+            for kbs in range(1, 14):
+                seq = stage(0) + (stage(1) if kbs > 1 else [])
+                for kb in range(kbs):
+                    if kb + 1 < kbs:
+                        w = ab + (1 if sa_wave else 0) + (swl if (kb + 1) % 4 == 0 else 0)
+                    else:
+                        w = 0
+                    assert w <= 63
+                    outstanding = seq[len(seq) - w:] if w else []
+                    assert all(t[1] != kb for t in outstanding), (ab, swl, sa_wave, kbs, kb)
+                    assert all(t[1] != kb - kb % 4 or t[0] != "SW" for t in outstanding)
+                    if kb + 2 < kbs:
+                        seq += stage(kb + 2)
