@@ -161,12 +161,15 @@ struct NoHook {
 // row's K values); its fragments are read at their MFMA instead of being held
 // in registers.  after_issue() runs once every global load of the wave has
 // been issued, before the first use of any.
-// vrows: valid rows of the tile; accumulator rows at or past it (row 4q + e
-// has e >= vrows for every lane) skip their group corrections.
-template <int BITS, bool ZP, int GROUP, int T, int KR, bool XL = false, typename Hook = NoHook>
+// ER: accumulator elements e < ER get their group corrections (row 4q + e of
+// lane group q).  ER = 1 serves a single-row tile (only row 0 is stored);
+// rows past the tile read a valid row, so the extra work of ER = 4 on them is
+// finite and never stored.
+template <int BITS, bool ZP, int GROUP, int T, int KR, bool XL = false, int ER = 4,
+          typename Hook = NoHook>
 __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
                                          const uint16_t *xrow, int nt0, int kb0, f32x4 (&acc)[T],
-                                         int vrows = 16, Hook after_issue = Hook()) {
+                                         Hook after_issue = Hook()) {
   constexpr int LB = BITS == 4 ? 16 : 12;    // packed bytes per lane per block
   constexpr int BB = 64 * LB;                // packed bytes per block
   constexpr int JPG = GROUP / 32;            // MFMAs per K-group
@@ -252,11 +255,10 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   // keep every load above this point: the wave waits once for all of them
   __builtin_amdgcn_sched_barrier(0);
   after_issue();
-  const bool kvalid = kb0 < kbs;  // wave-uniform; a wave entirely past K adds nothing
+  if (kb0 >= kbs) return;  // wave-uniform: a wave entirely past K adds nothing
   // scale s and zero point z of group g0 + i -> (MAG * s, -(MAG + z) * s)
   auto group_consts = [&](int t, int i, float &c1, float &c2) {
-    float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-    s = kvalid ? s : 0.f;
+    const float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
     int z = ZSYM;
     if constexpr (ZP) z = (int)((zw[t][i >> 3] >> (4 * ((g0 + i) & 7))) & 15u);
     c1 = MAG * s;
@@ -291,8 +293,7 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
         float c1, c2;
         group_consts(t, i, c1, c2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (e >= vrows) continue;  // wave-uniform
+        for (int e = 0; e < ER; ++e) {
           c[t][e] = __builtin_fmaf(xs[e], c2, c[t][e]);
           c[t][e] = __builtin_fmaf(g[e], c1, c[t][e]);
         }
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
         const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
         constexpr int BITS = (FMT <= 1) ? 4 : 3;
         constexpr bool ZP = (FMT == 1 || FMT == 3);
-        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc, it.rows, prefetch_next);
+        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc, prefetch_next);
       }
     } else {
       prefetch_next();
@@ -511,7 +512,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
 // the in-workgroup reduction (of the valid rows).  One workgroup per T
 // n-tiles.  Requires K % 512 == 0 (each 64-lane copy stays within a row) and
 // rows * (2K + 16) bytes of LDS.
-template <int FMT, int GROUP, int T, int KR>
+template <int FMT, int GROUP, int T, int KR, int ER>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   constexpr int BITS = (FMT <= 1) ? 4 : 3;
   constexpr bool ZP = (FMT == 1 || FMT == 3);
@@ -552,7 +553,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  a16_wave<BITS, ZP, GROUP, T, KR, true>(a, a.wbase, xrow, nt0, wave * KR, acc, rows, x_ready);
+  a16_wave<BITS, ZP, GROUP, T, KR, true, ER>(a, a.wbase, xrow, nt0, wave * KR, acc, x_ready);
 
   // 3. reduce the waves (valid rows only) and store
 #pragma unroll
@@ -767,7 +768,7 @@ static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream
   if (lds > 160 * 1024) return hipErrorInvalidValue;
 #define QG_DECODE_LAUNCH(TV, KRV)                                                            \
   {                                                                                          \
-    auto kern = decode_kernel<FMT, GROUP, TV, KRV>;                                          \
+    auto kern = a.m == 1 ? decode_kernel<FMT, GROUP, TV, KRV, 1> : decode_kernel<FMT, GROUP, TV, KRV, 4>; \
     hipError_t e = hipFuncSetAttribute((const void *)kern,                                   \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                           \
