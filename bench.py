@@ -171,6 +171,16 @@ def mx_acts_device(torch, rows, k, gen):
     return q.view(torch.uint8).view(rows, k).contiguous(), (e + 127).to(torch.uint8).contiguous()
 
 
+def moe_dispatch(ids, experts, mx, tiled_min=64):
+    """Which kernel serves which experts under the default split."""
+    counts = np.bincount(ids.ravel(), minlength=experts)
+    big = int((counts >= tiled_min).sum())
+    small = int(((counts > 0) & (counts < tiled_min)).sum())
+    fmt = "mx" if mx else "a16"
+    rest = f"mx_skinny for {small}" if mx else f"a16_tiled small tiles BM=64 for {small}"
+    return f"{fmt}_tiled BM=128 for {big} experts with >= {tiled_min} rows; {rest} smaller"
+
+
 def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters):
     mx = wtype == qg.W_MXFP4
     g = 32 if mx else 128
@@ -219,7 +229,7 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
            "sort_us": round(t_sort * 1e3, 2), "TFLOPS": round(tflops, 2),
            "weight_GBs": round(gbs, 1), "mfma_frac": round(tflops / peak, 4),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-           "dispatch": qg.describe_dispatch(up.ws[0], p)}
+           "dispatch": moe_dispatch(ids, experts, mx)}
     del up, down
     torch.cuda.empty_cache()
     print(f"[bench] {name} T={tokens}: {out}", file=sys.stderr, flush=True)
@@ -300,6 +310,35 @@ def pmc_workload(qg, synth, torch):
           f"({L.bytes} algorithmic bytes per launch), source hash {kernel_source_hash()}", flush=True)
 
 
+def bench_large_m(qg, synth, torch):
+    """W4A16 INT4 (g128) and W4A8 MXFP4 x MXFP8 dense GEMMs at M = 4096:
+    TFLOPS against the bf16 / fp8 dense MFMA peaks."""
+    extra = {}
+    for n, k in ((14336, 4096), (4096, 14336)):
+        L = DenseWeights(qg, synth, torch, qg.W_INT4, n, k, 128, seed=60, copies=2)
+        x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=61)
+        t = timed(torch, dense_launcher(qg, torch, L, x, None, 4096), 40, 10)
+        fl = 2.0 * 4096 * n * k
+        extra[f"w4a16_int4_M4096_N{n}_K{k}"] = {
+            "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+            "bf16_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
+        print(f"[bench] extra w4a16 N={n} K={k}: {extra[f'w4a16_int4_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
+        del L
+    for n in (3072, 14336):
+        L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
+        x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)
+        t = timed(torch, dense_launcher(qg, torch, L, x, xsc, 4096), 100, 20)
+        fl = 2.0 * 4096 * n * 4096
+        extra[f"w4a8_mx_M4096_N{n}_K4096"] = {
+            "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+            "fp8_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+            "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
+        print(f"[bench] extra mx N={n}: {extra[f'w4a8_mx_M4096_N{n}_K4096']}", file=sys.stderr, flush=True)
+        del L
+    return extra
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +346,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="primary decode workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--large-m", action="store_true",
+                    help="only the M=4096 dense GEMMs (for profiling the tiled kernels)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only run the copy calibration + decode kernel for rocprofv3 counter passes")
     args = ap.parse_args()
@@ -326,6 +367,9 @@ def main():
     torch.cuda.set_device(0)
     if args.pmc_workload:
         pmc_workload(qg, synth, torch)
+        return
+    if args.large_m:
+        print(json.dumps(bench_large_m(qg, synth, torch)), flush=True)
         return
 
     shapes = [(14336, 4096), (4096, 14336)]
@@ -389,28 +433,7 @@ def main():
                         "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "dispatch": qg.describe_dispatch(L.ws[0], mm)}
             print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
-        for n, k in ((14336, 4096), (4096, 14336)):
-            L = DenseWeights(qg, synth, torch, qg.W_INT4, n, k, 128, seed=60, copies=2)
-            x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=61)
-            t = timed(torch, dense_launcher(qg, torch, L, x, None, 4096), 40, 10)
-            fl = 2.0 * 4096 * n * k
-            extra[f"w4a16_int4_M4096_N{n}_K{k}"] = {
-                "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
-                "bf16_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
-                "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
-            print(f"[bench] extra w4a16 N={n} K={k}: {extra[f'w4a16_int4_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
-            del L
-        for n in (3072, 14336):
-            L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
-            x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)
-            t = timed(torch, dense_launcher(qg, torch, L, x, xsc, 4096), 100, 20)
-            fl = 2.0 * 4096 * n * 4096
-            extra[f"w4a8_mx_M4096_N{n}_K4096"] = {
-                "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
-                "fp8_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
-                "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
-            print(f"[bench] extra mx N={n}: {extra[f'w4a8_mx_M4096_N{n}_K4096']}", file=sys.stderr, flush=True)
-            del L
+        extra.update(bench_large_m(qg, synth, torch))
         moe = {}
         for tokens in (64, 4096):
             moe[f"w4a16_E256_top8_T{tokens}"] = bench_moe(
