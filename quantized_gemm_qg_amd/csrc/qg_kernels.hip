@@ -158,8 +158,8 @@ struct NoHook {
 };
 
 // XL: the activation row comes from LDS (xrow is an LDS address holding the
-// row's K values); its fragments are read at their MFMA instead of being held
-// in registers.  after_issue() runs once every global load of the wave has
+// row's K values from K = xk0 on); its fragments are read at their MFMA
+// instead of being held in registers.  after_issue() runs once every global load of the wave has
 // been issued, before the first use of any.
 // ER: accumulator elements e < ER get their group corrections (row 4q + e of
 // lane group q).  ER = 1 serves a single-row tile (only row 0 is stored);
@@ -169,7 +169,7 @@ template <int BITS, bool ZP, int GROUP, int T, int KR, bool XL = false, int ER =
           typename Hook = NoHook>
 __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
                                          const uint16_t *xrow, int nt0, int kb0, f32x4 (&acc)[T],
-                                         Hook after_issue = Hook()) {
+                                         Hook after_issue = Hook(), int xk0 = 0) {
   constexpr int LB = BITS == 4 ? 16 : 12;    // packed bytes per lane per block
   constexpr int BB = 64 * LB;                // packed bytes per block
   constexpr int JPG = GROUP / 32;            // MFMAs per K-group
@@ -228,7 +228,7 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   u32x4 xf[XL ? 1 : KR][4];
   auto xfrag = [&](int kb, int j) -> u32x4 {
     const int k = (kb0 + kb) * 128 + 32 * j + 8 * q;
-    if constexpr (XL) return *(const u32x4 *)(xrow + k);  // LDS row zero-padded past K
+    if constexpr (XL) return *(const u32x4 *)(xrow + (k - xk0));  // LDS row zero-padded past K
     return *(const u32x4 *)(xrow + (k < a.k ? k : 0));
   };
   if constexpr (!XL) {
@@ -500,6 +500,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
 
 // ---------------------------------------------------------------------------
 // dense decode (M <= 16 rows, integer formats): the workgroup covers all of K
+// (or 1 / splits of it)
 // ---------------------------------------------------------------------------
 //
 // The skinny kernel keeps every wave's activation fragments in registers (16
@@ -512,6 +513,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
 // the in-workgroup reduction (of the valid rows).  One workgroup per T
 // n-tiles.  Requires K % 512 == 0 (each 64-lane copy stays within a row) and
 // rows * (2K + 16) bytes of LDS.
+//
+// Long K with few n-tiles (one 14-wave workgroup per CU) leaves the
+// dequantization of the last-arriving blocks exposed; there a launch with
+// gridDim.y = splits > 1 gives each workgroup 1 / splits of K (its rows' K
+// range in LDS) and combines the splits as the skinny kernel does: fp32
+// partial tiles and a per-tile arrival counter, the last arriver sums the
+// splits in order and resets the counter.  Then W * KR * 128 must be a
+// multiple of 512 and the splits must all start inside K.
 template <int FMT, int GROUP, int T, int KR, int ER>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   constexpr int BITS = (FMT <= 1) ? 4 : 3;
@@ -522,22 +531,26 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   const int nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
   const int rows = a.m;                       // 1..16
-  const int kspan = nwaves * KR * 128;        // K covered by the waves (>= K)
+  const int kspan = nwaves * KR * 128;        // K covered by the waves of one split
   const int xpitch = kspan * 2 + 16;          // bytes per row in LDS (padded: bank spread)
   float *red = (float *)(dsm + ((rows * xpitch + 255) & ~255));  // [waves][T][rows][16]
+  __shared__ int last_flag;
   const int nt0 = blockIdx.x * T;
+  const int split = blockIdx.y;
+  const int ks0 = split * kspan;              // first K of this split (< K)
+  const int kk = min(kspan, a.k - ks0);       // K values of this split (a multiple of 512)
 
   // 1. activations -> LDS, 512 values (64 lanes x 16 B) per copy; columns
-  //    K .. kspan (a partial last wave) are zeros
-  const int per_row = a.k >> 9;
+  //    kk .. kspan (a partial last wave) are zeros
+  const int per_row = kk >> 9;
   for (int i = wave; i < rows * per_row; i += nwaves) {
     const int r = i / per_row, c0 = (i - r * per_row) << 9;
-    lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + c0 + lane * 8, dsm + r * xpitch + c0 * 2);
+    lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + ks0 + c0 + lane * 8, dsm + r * xpitch + c0 * 2);
   }
-  const int tail = (kspan - a.k) >> 3;  // 16-byte chunks per row
+  const int tail = (kspan - kk) >> 3;  // 16-byte chunks per row
   for (int i = threadIdx.x; i < rows * tail; i += blockDim.x) {
     const int r = i / tail;
-    *(u32x4 *)(dsm + r * xpitch + a.k * 2 + (i - r * tail) * 16) = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4 *)(dsm + r * xpitch + kk * 2 + (i - r * tail) * 16) = u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -553,7 +566,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  a16_wave<BITS, ZP, GROUP, T, KR, true, ER>(a, a.wbase, xrow, nt0, wave * KR, acc, x_ready);
+  a16_wave<BITS, ZP, GROUP, T, KR, true, ER>(a, a.wbase, xrow, nt0, (split * nwaves + wave) * KR, acc,
+                                             x_ready, ks0);
 
   // 3. reduce the waves (valid rows only) and store
 #pragma unroll
@@ -564,12 +578,46 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
       if (r < rows) red[((wave * T + t) * rows + r) * 16 + r16] = acc[t][e];
     }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < T * rows * 16; idx += blockDim.x) {
+  const int n_out = T * rows * 16;
+  if (gridDim.y == 1) {
+    for (int idx = threadIdx.x; idx < n_out; idx += blockDim.x) {
+      float sum = 0.f;
+      for (int w = 0; w < nwaves; ++w) sum += red[w * T * rows * 16 + idx];
+      const int t = idx / (rows * 16), r = (idx / 16) % rows, col = (nt0 + t) * 16 + (idx & 15);
+      if (col < a.n && nt0 + t < a.n_tiles) store_out(a.y, a.ldy, a.otype, r, col, sum);
+    }
+    return;
+  }
+  // split K: partial tile of this split (T * 256 floats per tile, element
+  // (t, r, c) at t * 256 + r * 16 + c), published by the counter add after
+  // the agent-scope stores have completed
+  float *part = a.partials + ((int64_t)split * gridDim.x + blockIdx.x) * (T * 256);
+  for (int idx = threadIdx.x; idx < n_out; idx += blockDim.x) {
     float sum = 0.f;
     for (int w = 0; w < nwaves; ++w) sum += red[w * T * rows * 16 + idx];
-    const int t = idx / (rows * 16), r = (idx / 16) % rows, col = (nt0 + t) * 16 + (idx & 15);
+    const int t = idx / (rows * 16), rc = idx - t * rows * 16;
+    __hip_atomic_store(part + t * 256 + rc, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (prev == gridDim.y - 1);
+  }
+  __syncthreads();
+  if (!last_flag) return;  // uniform across the workgroup
+  for (int idx = threadIdx.x; idx < n_out; idx += blockDim.x) {
+    const int t = idx / (rows * 16), rc = idx - t * rows * 16, r = rc / 16;
+    float sum = 0.f;
+    for (int sp = 0; sp < (int)gridDim.y; ++sp)
+      sum += __hip_atomic_load(a.partials + ((int64_t)sp * gridDim.x + blockIdx.x) * (T * 256) + t * 256 + rc,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int col = (nt0 + t) * 16 + (idx & 15);
     if (col < a.n && nt0 + t < a.n_tiles) store_out(a.y, a.ldy, a.otype, r, col, sum);
   }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Plain streaming kernels (measurement utilities): grid-stride 128-bit loads,
@@ -765,14 +813,14 @@ static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream
   const int n_blocks = (a.n_tiles + v.T - 1) / v.T;
   const size_t lds = (((size_t)a.m * ((size_t)v.W * v.KR * 256 + 16) + 255) & ~(size_t)255) +
                      (size_t)v.W * v.T * a.m * 16 * sizeof(float);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  if (lds > 160 * 1024 - 256) return hipErrorInvalidValue;  // (+ the kernel's static LDS)
 #define QG_DECODE_LAUNCH(TV, KRV)                                                            \
   {                                                                                          \
     auto kern = a.m == 1 ? decode_kernel<FMT, GROUP, TV, KRV, 1> : decode_kernel<FMT, GROUP, TV, KRV, 4>; \
     hipError_t e = hipFuncSetAttribute((const void *)kern,                                   \
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     if (e != hipSuccess) return e;                                                           \
-    hipLaunchKernelGGL(kern, dim3(n_blocks), dim3(64 * v.W), lds, s, a);                     \
+    hipLaunchKernelGGL(kern, dim3(n_blocks, v.splits), dim3(64 * v.W), lds, s, a);           \
     return hipGetLastError();                                                                \
   }
   // instances without register spills (a wave holds KR * 128 / GROUP group
@@ -782,6 +830,7 @@ static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream
     if (v.T == 2 && v.KR == 4) QG_DECODE_LAUNCH(2, 4)
   }
   if constexpr (GROUP == 128) {
+    if (v.T == 1 && v.KR == 4) QG_DECODE_LAUNCH(1, 4)
     if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
     if (v.T == 2 && v.KR == 8) QG_DECODE_LAUNCH(2, 8)
   }
@@ -801,7 +850,11 @@ static hipError_t launch_decode_f(const GemmArgs &a, int group, const Variant &v
 
 hipError_t launch_decode_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                              hipStream_t s) {
-  if (a.m < 1 || a.m > 16 || a.k % 512 != 0 || v.W * v.KR * 128 < a.k) return hipErrorInvalidValue;
+  if (a.m < 1 || a.m > 16 || a.k % 512 != 0 || v.splits < 1 || v.W * v.KR * 128 * v.splits < a.k)
+    return hipErrorInvalidValue;
+  if (v.splits > 1 && ((v.W * v.KR) % 4 != 0 || (v.splits - 1) * v.W * v.KR >= a.k_blocks ||
+                       !a.partials || !a.counters))
+    return hipErrorInvalidValue;
   switch (fmt_of(d)) {
     case 0: return launch_decode_f<0>(a, d.group_size, v, s);
     case 1: return launch_decode_f<1>(a, d.group_size, v, s);

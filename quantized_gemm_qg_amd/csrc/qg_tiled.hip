@@ -214,14 +214,26 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 }
 
 // Activation scales regrouped by K step: out[kb * m + r] holds the 4 bytes of
-// row r's scales for K step kb (bytes 4 kb .. 4 kb + 3 of the row).
+// row r's scales for K step kb (bytes 4 kb .. 4 kb + 3 of the row).  A
+// workgroup transposes 64 rows x 64 K steps through LDS: reads run along the
+// rows (consecutive threads, consecutive dwords of one row), writes along the
+// steps (consecutive threads, consecutive rows).
 __global__ __launch_bounds__(256) void mx_scales_by_step_kernel(const uint8_t *xs, int m, int kq,
                                                                 int kbs, uint32_t *out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)kbs * m) return;
-  const int r = (int)(i % m), kb = (int)(i / m);
-  const uint8_t *p = xs + (int64_t)r * kq + 4 * kb;
-  out[i] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+  __shared__ uint32_t tile[64][65];
+  const int r0 = blockIdx.x * 64, kb0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, kb = i & 63;
+    if (r0 + r < m && kb0 + kb < kbs) {
+      const uint8_t *p = xs + (int64_t)(r0 + r) * kq + 4 * (kb0 + kb);
+      tile[kb][r] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kb = i >> 6, r = i & 63;
+    if (r0 + r < m && kb0 + kb < kbs) out[(int64_t)(kb0 + kb) * m + r0 + r] = tile[kb][r];
+  }
 }
 
 uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) { return align_up((uint64_t)(m * k_blocks) * 4, 256); }
@@ -253,9 +265,8 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
   GemmArgs a = a_in;
   if (!moe) {
     if (!ws) return hipErrorInvalidValue;
-    const int64_t n = (int64_t)a.m * a.k_blocks;
-    hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       a.x_scales, a.m, a.k >> 5, a.k_blocks, (uint32_t *)ws);
+    hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((a.m + 63) / 64), (unsigned)((a.k_blocks + 63) / 64)),
+                       dim3(256), 0, s, a.x_scales, a.m, a.k >> 5, a.k_blocks, (uint32_t *)ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.x_scales_t = (const uint32_t *)ws;

@@ -258,10 +258,15 @@ def test_dispatch_table_covers_k():
                 if wt != qg.W_MXFP4:  # the group row sums of X live in the workspace
                     assert qg.gemm_workspace_size(w, m) >= (k // g) * m * 4
                 continue
-            if "decode" in s:  # activations in LDS, one workgroup over all of K
+            if "decode" in s:  # activations in LDS, one workgroup over all of K (or of a split)
                 assert wt != qg.W_MXFP4 and m <= 16 and k % 512 == 0, s
-                T, KR, W = (int(v) for v in re.findall(r"=(\d+)", s))
-                assert W * KR >= -(-k // 128) and 1 <= W <= 16, s
+                vals = [int(v) for v in re.findall(r"=(\d+)", s)]
+                T, KR, W = vals[:3]
+                S = vals[3] if len(vals) > 3 else 1
+                assert W * KR * S >= -(-k // 128) and 1 <= W <= 16, s
+                if S > 1:  # partials and arrival counters live in the workspace
+                    assert (S - 1) * W * KR < -(-k // 128) and (W * KR) % 4 == 0, s
+                    assert qg.gemm_workspace_size(w, m) >= S * -(-n // (16 * T)) * T * 256 * 4
                 continue
             T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
             assert W * KR * S >= -(-k // 128), s

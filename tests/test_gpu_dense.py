@@ -249,14 +249,17 @@ def test_w4a16_large_m_full_size_sampled_rows(nk):
 # dense decode kernel (integer formats, M <= 16, K % 512 == 0, rows in LDS)
 # ---------------------------------------------------------------------------
 
-DECODE_VARIANTS = {128: ["4,2", "2,4", "1,8", "2,8"], 64: ["4,2", "2,4"]}
+# "T,KR" or "T,KR,splits" (split K across workgroups)
+DECODE_VARIANTS = {128: ["4,2", "2,4", "1,4", "1,8", "2,8", "1,4,2", "1,4,3", "1,8,2", "2,4,2"],
+                   64: ["4,2", "2,4", "2,4,2"]}
 
 
 @pytest.mark.parametrize("wtype", A16)
 @pytest.mark.parametrize("group", [64, 128])
 def test_decode_kernel_variants(monkeypatch, wtype, group):
-    """Every compiled (T, KR) of the decode kernel; N = 200 leaves a partial
-    n-tile block, K = 1536 (12 blocks) a partial last wave for KR = 8."""
+    """Every compiled (T, KR) of the decode kernel, with and without a K
+    split; N = 200 leaves a partial n-tile block, K = 1536 (12 blocks) a
+    partial last wave for KR = 8 and a short last split."""
     layer = Layer(wtype, 200, 1536, group, seed=wtype * 10 + group + 1)
     for tune in DECODE_VARIANTS[group]:
         monkeypatch.setenv("QG_DECODE", tune)
@@ -264,6 +267,28 @@ def test_decode_kernel_variants(monkeypatch, wtype, group):
             assert "a16_decode" in qg.describe_dispatch(layer.w, m), (tune, m)
             print(f"  decode {tune} m={m}", flush=True)
             _check(layer, Acts(False, m, 1536, seed=m + group), m)
+
+
+def test_decode_split_k_reuses_workspace(monkeypatch):
+    """Split-K decode: the per-tile arrival counters return to zero, so one
+    workspace (zero-filled once) serves consecutive calls."""
+    monkeypatch.setenv("QG_DECODE", "1,4,2")
+    n, k = 200, 2048
+    layer = Layer(qg.W_UINT4, n, k, 128, seed=77)
+    m = 1
+    assert "splits=2" in qg.describe_dispatch(layer.w, m)
+    ws_bytes = qg.gemm_workspace_size(layer.w, m)
+    assert ws_bytes > 0
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    wdq = layer.wdq()
+    for call in range(3):
+        acts = Acts(False, m, k, seed=100 + call)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        qg.gemm(layer.w, acts.x, None, m, k, y, qg.O_F32, n, ws, ws_bytes)
+        torch.cuda.synchronize()
+        e = err(y, oracle.gemm(acts.xdq, wdq))
+        print(f"  call {call} err={e:.3e}", flush=True)
+        assert e <= tol_f32(False), (call, e)
 
 
 @pytest.mark.parametrize("wtype", A16)
