@@ -23,17 +23,19 @@
 //   B   BN / 16 packed weight blocks of 1 KB copied verbatim (the packed
 //       layout already stores each lane's 16-byte B operand contiguously);
 //   SA  the four e8m0 scales of each activation row for this K step (dense
-//       launches read them from a copy regrouped by K step, so one SA copy
-//       reads 256 contiguous bytes instead of a dword from each of 64 rows).
+//       launches read them from a copy regrouped by K step, so for 256-row
+//       tiles one 16-byte-per-lane copy moves all of them).
 // The weight scales change every fourth K step only: a separate two-slot ring
 // SW holds, for each of the BN weight columns and quarters q, the dword with
-// its e8m0 scales of K steps 4j .. 4j + 3, loaded with stage 4j.  (Scale loads
-// gather one dword per lane from as many cache lines, so they cost the
-// address unit far more than their bytes suggest.)  Each wave counts its own
-// loads: "stage kb has landed" is a wait until only the wave's loads of stage
-// kb + 1 are outstanding (where the blocks do not divide evenly, the last
-// waves copy the final block again, the same bytes to the same place; only the
-// first BM / 64 waves copy SA), followed by a workgroup barrier.  Inside a K step the next row
+// its e8m0 scales of K steps 4j .. 4j + 3, loaded with stage 4j as whole
+// 256-byte units (one per n-tile, four per 16-byte-per-lane copy).  Scale
+// copies of a dword per lane cost the load path about as much as a 1-KB copy,
+// so every scale copy here is a 16-byte one wherever the layout allows.  Each
+// wave counts its own loads: "stage kb has landed" is a wait until only the
+// wave's loads of stage kb + 1 are outstanding (where the blocks do not
+// divide evenly, the last waves copy the final block again, the same bytes to
+// the same place; SA and SW copies go to the first few waves), followed by a
+// workgroup barrier.  Inside a K step the next row
 // block's LDS reads are scheduled ahead of the current block's 8 MFMAs.
 //
 // Work order: workgroups are dealt round-robin to the 8 XCDs; the tile index
@@ -58,20 +60,20 @@ struct MxCfg {
   static constexpr int A = BM * 128;
   static constexpr int B = NBLK * 1024;
   static constexpr int SA = BM * 4;
-  static constexpr int SW = BN * 4 * 4;                     // NBLK pieces of 256 B
+  static constexpr int SW_PIECES = (NBLK + 3) / 4;          // 1-KB copies: 4 n-tiles' 256-B units each
+  static constexpr int SW = SW_PIECES * 1024;               // one slot (units past NBLK unused)
   static constexpr int STAGE = A + B + SA;
   static constexpr int OFF_SW = 3 * STAGE;                  // the two SW slots
   static constexpr int LDS = OFF_SW + 2 * SW;
   static constexpr int A_LOADS = BM * 128 / 1024 / WAVES;  // 1-KB copies of A per wave
   static constexpr int B_LOADS = (NBLK + WAVES - 1) / WAVES;  // 1-KB blocks of B per wave
-  static constexpr int SW_LOADS = B_LOADS;                  // 256-B pieces of SW per wave
   static constexpr int SA_WAVES = BM / 64;                  // waves that copy a 256-B SA piece
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int MB = BM / WM / 16;                   // 16-row blocks per wave
   static constexpr int NB = BN / WN / 16;                   // 16-column blocks per wave
   static_assert(BN % (16 * WN) == 0, "column blocks per wave");
   static_assert(A_LOADS >= 1 && BM * 128 % (1024 * WAVES) == 0, "A copies per wave");
-  static_assert(WAVES >= SA_WAVES, "SA pieces");
+  static_assert(WAVES >= SA_WAVES && WAVES >= SW_PIECES, "SA / SW pieces");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
@@ -110,21 +112,23 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i)
     b_blk[i] = (uint32_t)min(nt0 + blk_of(i), a.n_tiles - 1) * kbs;
-  // SA: BM rows of 4 bytes = BM / 64 pieces of 256 B, one per wave of the
-  // first BM / 64
-  const bool sa_wave = wave < C::SA_WAVES;
-  const int64_t sa_row = tr.x(a, (sa_wave ? wave : 0) * 64 + lane);
-  // per K step: + 4 bytes (MoE, rows of kq bytes) or + 4 m bytes (dense, by step)
+  // SA: BM rows of 4 bytes.  Dense 256-row tiles: one 1-KB copy by wave 0
+  // from the scales regrouped by K step (rows padded to 256, so the copy
+  // stays in the buffer; rows past M are never stored).  Otherwise BM / 64
+  // pieces of 256 B, one per wave of the first BM / 64, with rows clamped.
+  constexpr bool SA_X4 = !MOE && BM == 256;
+  const bool sa_wave = SA_X4 ? wave == 0 : wave < C::SA_WAVES;
+  const int64_t m_pad = ((int64_t)a.m + 255) & ~(int64_t)255;  // regrouped row stride
+  const int64_t sa_row = SA_X4 ? (int64_t)tr.base + 4 * lane : tr.x(a, (sa_wave ? wave : 0) * 64 + lane);
+  // per K step: + 4 bytes (MoE, rows of kq bytes) or + 4 m_pad bytes (dense, by step)
   const uint8_t *sa_src = MOE ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
-  const int64_t sa_step = MOE ? 4 : 4 * (int64_t)a.m;
-  uint32_t sw_off[C::SW_LOADS];
-#pragma unroll
-  for (int i = 0; i < C::SW_LOADS; ++i) {
-    // lane = (column, quarter) pair of the n-tile: dword `lane` of its 256-B
-    // scale unit for K steps 4j .. 4j + 3, at + 256 j
-    const int nt = min(nt0 + blk_of(i), a.n_tiles - 1);
-    sw_off[i] = (uint32_t)((uint64_t)nt * (a.kb_pad >> 2) * 256 + 4 * lane);
-  }
+  const int64_t sa_step = MOE ? 4 : 4 * m_pad;
+  // SW: copy p (by wave p < SW_PIECES) moves the 256-B units of n-tiles
+  // 4p .. 4p + 3 of the tile for K steps 4j .. 4j + 3 (unit of n-tile nt at
+  // nt * kb_pad / 4 * 256 + 256 j); lanes 16u .. 16u + 15 copy unit u
+  const bool sw_wave = wave < C::SW_PIECES;
+  const uint32_t sw_off = (uint32_t)((uint64_t)min(nt0 + 4 * wave + (lane >> 4), a.n_tiles - 1) *
+                                         (a.kb_pad >> 2) * 256 + 16 * (lane & 15));
 
   auto issue = [&](int kb, int buf) {
     uint8_t *st = smem + buf * C::STAGE;
@@ -135,12 +139,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
       lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + blk_of(i) * 1024);
-    if (sa_wave) lds_dma4(sa_src + sa_step * kb, st + C::A + C::B + wave * 256);
-    if ((kb & 3) == 0) {
-      uint8_t *sws = smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW;
-#pragma unroll
-      for (int i = 0; i < C::SW_LOADS; ++i) lds_dma4(wsc + 64 * kb + sw_off[i], sws + blk_of(i) * 256);
+    if (sa_wave) {
+      if constexpr (SA_X4)
+        lds_dma16(sa_src + sa_step * kb, st + C::A + C::B);
+      else
+        lds_dma4(sa_src + sa_step * kb, st + C::A + C::B + wave * 256);
     }
+    if ((kb & 3) == 0 && sw_wave)
+      lds_dma16(wsc + 64 * kb + sw_off, smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW + wave * 1024);
   };
 
   f32x4 acc[C::MB][C::NB];
@@ -154,13 +160,13 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   for (int kb = 0; kb < kbs; ++kb) {
     // outstanding after stage kb: this wave's loads of stage kb + 1
     if (kb + 1 < kbs) {
-      const bool sw_next = ((kb + 1) & 3) == 0;
-      if (sa_wave) {
-        if (sw_next) QG_WAIT_VMCNT(C::AB_LOADS + 1 + C::SW_LOADS);
-        else QG_WAIT_VMCNT(C::AB_LOADS + 1);
+      const int extra = (sa_wave ? 1 : 0) + ((((kb + 1) & 3) == 0 && sw_wave) ? 1 : 0);
+      if (extra == 0) {
+        QG_WAIT_VMCNT(C::AB_LOADS);
+      } else if (extra == 1) {
+        QG_WAIT_VMCNT(C::AB_LOADS + 1);
       } else {
-        if (sw_next) QG_WAIT_VMCNT(C::AB_LOADS + C::SW_LOADS);
-        else QG_WAIT_VMCNT(C::AB_LOADS);
+        QG_WAIT_VMCNT(C::AB_LOADS + 2);
       }
     } else {
       QG_WAIT_VMCNT(0);
@@ -213,13 +219,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
                            (nt0 + wn * C::NB) * 16, smem + wave * store_tile_lds_bytes<C::MB, C::NB>());
 }
 
-// Activation scales regrouped by K step: out[kb * m + r] holds the 4 bytes of
-// row r's scales for K step kb (bytes 4 kb .. 4 kb + 3 of the row).  A
+// Activation scales regrouped by K step: out[kb * m_pad + r] holds the 4 bytes
+// of row r's scales for K step kb (bytes 4 kb .. 4 kb + 3 of the row); m_pad =
+// m rounded up to 256 (rows m .. m_pad - 1 are not written).  A
 // workgroup transposes 64 rows x 64 K steps through LDS: reads run along the
 // rows (consecutive threads, consecutive dwords of one row), writes along the
 // steps (consecutive threads, consecutive rows).
-__global__ __launch_bounds__(256) void mx_scales_by_step_kernel(const uint8_t *xs, int m, int kq,
-                                                                int kbs, uint32_t *out) {
+__global__ __launch_bounds__(256) void mx_scales_by_step_kernel(const uint8_t *xs, int m, int64_t m_pad,
+                                                                int kq, int kbs, uint32_t *out) {
   __shared__ uint32_t tile[64][65];
   const int r0 = blockIdx.x * 64, kb0 = blockIdx.y * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
@@ -232,11 +239,13 @@ __global__ __launch_bounds__(256) void mx_scales_by_step_kernel(const uint8_t *x
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += 256) {
     const int kb = i >> 6, r = i & 63;
-    if (r0 + r < m && kb0 + kb < kbs) out[(int64_t)(kb0 + kb) * m + r0 + r] = tile[kb][r];
+    if (r0 + r < m && kb0 + kb < kbs) out[(int64_t)(kb0 + kb) * m_pad + r0 + r] = tile[kb][r];
   }
 }
 
-uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) { return align_up((uint64_t)(m * k_blocks) * 4, 256); }
+uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) {
+  return (uint64_t)((m + 255) & ~(int64_t)255) * (uint64_t)k_blocks * 4;
+}
 
 template <int BM, int BN, int WM, int WN, bool MOE>
 static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
@@ -266,7 +275,8 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
   if (!moe) {
     if (!ws) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((a.m + 63) / 64), (unsigned)((a.k_blocks + 63) / 64)),
-                       dim3(256), 0, s, a.x_scales, a.m, a.k >> 5, a.k_blocks, (uint32_t *)ws);
+                       dim3(256), 0, s, a.x_scales, a.m, ((int64_t)a.m + 255) & ~(int64_t)255, a.k >> 5,
+                       a.k_blocks, (uint32_t *)ws);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.x_scales_t = (const uint32_t *)ws;

@@ -134,28 +134,29 @@ def test_tile_epilogue_stores_every_row_chunk_once():
 
 
 def test_mx_tiled_waits_cover_each_stage():
-    """MX tiled kernel: stage kb = A_LOADS + B_LOADS copies, + 1 SA copy on the
-    first BM / 64 waves, + SW_LOADS weight-scale copies when kb % 4 == 0 (they
-    fill the scale ring slot of steps kb .. kb + 3).  Stages 0 and 1 go out in
-    the prologue, stage kb + 2 after the barrier of step kb; step kb waits
+    """MX tiled kernel: stage kb = A_LOADS + B_LOADS copies, + 1 SA copy on
+    the SA waves, + 1 weight-scale copy on the SW waves when kb % 4 == 0 (it
+    fills the scale ring slot of steps kb .. kb + 3).  Stages 0 and 1 go out
+    in the prologue, stage kb + 2 after the barrier of step kb; step kb waits
     until only this wave's loads of stage kb + 1 are outstanding.  Replayed
     per wave kind: every load of stage kb (and of the scale group of step kb)
     has retired at the wait of step kb."""
-    for ab, swl in ((6, 2), (6, 2), (5, 2), (4, 1)):
+    for ab in (6, 5, 4, 12):
         for sa_wave in (True, False):
-            def stage(kb):
-                return [("AB", kb)] * ab + ([("SA", kb)] if sa_wave else []) + \
-                       ([("SW", kb)] * swl if kb % 4 == 0 else [])
-            for kbs in range(1, 14):
-                seq = stage(0) + (stage(1) if kbs > 1 else [])
-                for kb in range(kbs):
-                    if kb + 1 < kbs:
-                        w = ab + (1 if sa_wave else 0) + (swl if (kb + 1) % 4 == 0 else 0)
-                    else:
-                        w = 0
-                    assert w <= 63
-                    outstanding = seq[len(seq) - w:] if w else []
-                    assert all(t[1] != kb for t in outstanding), (ab, swl, sa_wave, kbs, kb)
-                    assert all(t[1] != kb - kb % 4 or t[0] != "SW" for t in outstanding)
-                    if kb + 2 < kbs:
-                        seq += stage(kb + 2)
+            for sw_wave in (True, False):
+                def stage(kb):
+                    return [("AB", kb)] * ab + ([("SA", kb)] if sa_wave else []) + \
+                           ([("SW", kb)] if (kb % 4 == 0 and sw_wave) else [])
+                for kbs in range(1, 14):
+                    seq = stage(0) + (stage(1) if kbs > 1 else [])
+                    for kb in range(kbs):
+                        if kb + 1 < kbs:
+                            w = ab + (1 if sa_wave else 0) + (1 if ((kb + 1) % 4 == 0 and sw_wave) else 0)
+                        else:
+                            w = 0
+                        assert w <= 63
+                        outstanding = seq[len(seq) - w:] if w else []
+                        assert all(t[1] != kb for t in outstanding), (ab, sa_wave, sw_wave, kbs, kb)
+                        assert all(t[1] != kb - kb % 4 or t[0] != "SW" for t in outstanding)
+                        if kb + 2 < kbs:
+                            seq += stage(kb + 2)
