@@ -149,7 +149,12 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   int bm = m >= 256 ? 256 : 128;
   const char *b = getenv("QG_TILED_BM");
   if (b && (atoi(b) == 128 || atoi(b) == 256)) bm = atoi(b);
-  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, mx ? mx_tile_cols(w.desc.n, m, bm) : 128};
+  int bn = 128;
+  if (!mx && a16_tiled_bn() == 256) {
+    bm = 128;
+    bn = 256;
+  }
+  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, mx ? mx_tile_cols(w.desc.n, m, bm) : bn};
   return true;
 }
 
@@ -281,6 +286,16 @@ int a16_tiled_waves() {
   const char *e = getenv("QG_A16_WAVES");
   if (e && (atoi(e) == 4 || atoi(e) == 8)) return atoi(e);
   return 8;
+}
+
+// Columns of the integer-format tiled kernel's tile: 256 (with 128 rows, 2 x 4
+// waves) moves fewer activation bytes per flop than 256 x 128 and unpacks
+// each code for 2 waves instead of 4; measured 1.03-1.08x at M = 4096.
+// QG_A16_BN=128 keeps 128 columns (then QG_TILED_BM picks the rows).
+int a16_tiled_bn() {
+  if (a16_tiled_waves() != 8) return 128;
+  const char *e = getenv("QG_A16_BN");
+  return (e && atoi(e) == 128) ? 128 : 256;
 }
 
 // Raster group of the tiled MoE launches (QG_MOE_GROUP_M overrides).
@@ -528,7 +543,7 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   else if (v.kind == 3)
     he = launch_decode_a16(a, d, v, stream);
   else if (v.kind == 2)
-    he = launch_a16_tiled(a, d, v.bm, false, m, 0, a16_tiled_waves(), ws, true, stream);
+    he = launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), ws, true, stream);
   else
     he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
   return hip_status(he);
@@ -627,8 +642,8 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
       he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream);
     } else {
       void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);
-      he = launch_a16_tiled(a, d, kMoeTileRows, true, x_rows_count, cap, a16_tiled_waves(), xs, true,
-                            stream);
+      he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
+                            xs, true, stream);
       if (he == hipSuccess && small) {
         const int sbm = moe_small_bm();
         he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
@@ -636,7 +651,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
         if (he != hipSuccess) return hip_status(he);
         a.tiles = tiles_s;
         a.group_m = 1;
-        he = launch_a16_tiled(a, d, sbm, true, x_rows_count, cap_s, 8, xs, false, stream);
+        he = launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
         return hip_status(he);  // every expert with rows is covered
       }
     }

@@ -168,10 +168,11 @@ int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // xs_rows: rows of X (dense: m; MoE: tokens or pairs, by the x row mode).
 // sums = false skips the row sums (already in ws from an earlier launch on the
 // same X).
-hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
+hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, int bn, bool moe,
                             int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, bool sums,
                             hipStream_t s);
 int a16_tiled_waves();  // QG_A16_WAVES (4 or 8), else the default
+int a16_tiled_bn();     // tile columns of the integer-format tiled kernel (QG_A16_BN)
 uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m);
 // MoE tile list for the tiled kernels (experts with min_rows <= rows <
 // max_rows, max_rows = 0 for no bound; bm-row tiles): tiles[0] = count, then

@@ -48,13 +48,13 @@
 
 namespace qg {
 
-constexpr int kA16BN = 128;       // tile columns (8 packed n-tiles)
 constexpr int kLdsBytes = 160 * 1024;
 
-template <int BM, int WM, int WN, int BITS, bool ZP, int GROUP>
+template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP>
 struct A16Cfg {
   static constexpr int WAVES = WM * WN;           // WM (M) x WN (N)
-  static constexpr int NJ = 8 / WN;               // 16-column blocks per wave
+  static constexpr int NBLK = BN / 16;            // packed n-tiles per tile
+  static constexpr int NJ = NBLK / WN;            // 16-column blocks per wave
   static constexpr int LB = BITS == 4 ? 16 : 12;  // packed bytes per lane per block
   static constexpr int BB = 64 * LB;              // packed bytes per 16 x 128 block
   static constexpr int GPB = 128 / GROUP;         // groups per 128-K step
@@ -66,9 +66,10 @@ struct A16Cfg {
   static constexpr int SX = GPB * SXR * 4;
   static constexpr int A_STAGE = A + SX;
   // weight ring stage: packed blocks, scales, zero points
-  static constexpr int B = 8 * BB;
-  static constexpr int SS = kA16BN * 16;
-  static constexpr int SZ = ZP ? kA16BN * 4 : 0;
+  static constexpr int B = NBLK * BB;
+  static constexpr int SS = BN * 16;
+  static constexpr int SZ = ZP ? BN * 4 : 0;
+  static constexpr int SS_PIECES = BN / 64;       // 64-column copies of SS / SZ
   static constexpr int OFF_SS = B;
   static constexpr int OFF_SZ = OFF_SS + SS;
   static constexpr int B_STAGE = OFF_SZ + SZ;
@@ -78,7 +79,8 @@ struct A16Cfg {
   // fills its rings while the other computes (short-K layers spend much of a
   // tile in the prologue).
   static constexpr int LDS_CAP = WM == 1 ? kLdsBytes / 2 : kLdsBytes;
-  static constexpr int NA = WM == 1 ? 2 : (3 * A_STAGE + 2 * B_STAGE <= LDS_CAP ? 3 : 2);
+  // (256-column tiles: three weight stages at least when both rings fit)
+  static constexpr int NA = WM == 1 ? 2 : (3 * A_STAGE + (BN > 128 ? 3 : 2) * B_STAGE <= LDS_CAP ? 3 : 2);
   static constexpr int NB_FIT = (LDS_CAP - NA * A_STAGE) / B_STAGE;
   static constexpr int NB = NB_FIT > 6 ? 6 : NB_FIT;
   static constexpr int OFF_BRING = NA * A_STAGE;
@@ -86,7 +88,7 @@ struct A16Cfg {
   // loads per wave and stage
   static constexpr int A_LOADS = BM * 256 / 1024 / WAVES;            // 1-KB copies of A
   static constexpr int A_ISSUE = A_LOADS + GPB;
-  static constexpr int B_LOADS = (BITS == 4 ? 8 : 24) / WAVES;  // 1-KB (4-bit) or 256-B (3-bit) copies
+  static constexpr int B_LOADS = (BITS == 4 ? NBLK : 3 * NBLK) / WAVES;  // 1-KB (4-bit) or 256-B (3-bit) copies
   static constexpr int B_ISSUE = B_LOADS + 1 + (ZP ? 1 : 0);
   // Each step issues its activation loads, then its weight loads.  In steady
   // state, the loads issued after the later of stage kb's two groups: stage
@@ -114,10 +116,10 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
+template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
 __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, const float *xs,
                                                                  int xs_rows) {
-  using C = A16Cfg<BM, WM, WN, BITS, ZP, GROUP>;
+  using C = A16Cfg<BM, BN, WM, WN, BITS, ZP, GROUP>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -128,8 +130,8 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
   TileRows tr;
   int tn;
   const uint8_t *wexp;
-  if (!tiled_work<BM>(a, MOE, (a.n_tiles + 7) / 8, &tr, &tn, &wexp)) return;
-  const int nt0 = tn * 8;
+  if (!tiled_work<BM>(a, MOE, (a.n_tiles + C::NBLK - 1) / C::NBLK, &tr, &tn, &wexp)) return;
+  const int nt0 = tn * C::NBLK;
   const int kbs = a.k_blocks, gp = a.groups_padded;
   const uint32_t umask = sgpr_const(BITS == 4 ? 0x00780078u : 0x00700070u);
   const uint32_t umagic = vgpr_const(0x3F803F80u);
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
     a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx * 2 + 16 * c);
   }
   // B: 4-bit, copy i = block B_LOADS wave + i; 3-bit, copy i = 256-byte
-  // piece B_LOADS wave + i of the 8 blocks (three pieces per 768-byte block)
+  // piece B_LOADS wave + i of the NBLK blocks (three pieces per 768-byte block)
   uint32_t b_off[C::B_LOADS];
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i) {
@@ -158,8 +160,10 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
       b_off[i] = (uint32_t)(min(nt0 + blk, a.n_tiles - 1) * kbs) * 768u + 256u * (piece % 3) + 4u * lane;
     }
   }
-  // SS / SZ: column 64 (wave & 1) + lane of the tile (waves 2, 3 repeat 0, 1)
-  const int ncol = min(nt0 * 16 + 64 * (wave & 1) + lane, a.n_tiles * 16 - 1);
+  // SS / SZ: column 64 (wave % SS_PIECES) + lane of the tile (later waves
+  // repeat the first ones' copies: the same bytes to the same place)
+  const int ss_piece = wave % C::SS_PIECES;
+  const int ncol = min(nt0 * 16 + 64 * ss_piece + lane, a.n_tiles * 16 - 1);
   const uint8_t *ss_src = wexp + a.scales_offset + (uint64_t)ncol * gp * 2;
   const uint32_t *sz_src = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
   const int sx_row = 64 * (wave % (C::SXR / 64)) + lane;
@@ -186,8 +190,8 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
         lds_dma4(wexp + b_off[i] + kb * 768u, st + (C::B_LOADS * wave + i) * 256);
     }
     const int g0 = kb * C::GPB;
-    lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + (wave & 1) * 1024);
-    if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + (wave & 1) * 256);
+    lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + ss_piece * 1024);
+    if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + ss_piece * 256);
   };
 
   f32x4 acc[C::MI][C::NJ];
@@ -305,10 +309,10 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *x, int6
   }
 }
 
-template <int BM, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
+template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
 static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t tiles_cap, float *xs,
                                      bool sums, hipStream_t s) {
-  using C = A16Cfg<BM, WM, WN, BITS, ZP, GROUP>;
+  using C = A16Cfg<BM, BN, WM, WN, BITS, ZP, GROUP>;
   static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MI, C::NJ>(), "epilogue LDS");
   hipError_t e;
   if (sums) {
@@ -320,11 +324,11 @@ static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t
     if (e != hipSuccess) return e;
   }
   const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
-  const int64_t n_tiles_wg = (a.n_tiles + 7) / 8;
+  const int64_t n_tiles_wg = (a.n_tiles + C::NBLK - 1) / C::NBLK;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  auto kern = a16_tiled_kernel<BM, WM, WN, BITS, ZP, GROUP, MOE>;
+  auto kern = a16_tiled_kernel<BM, BN, WM, WN, BITS, ZP, GROUP, MOE>;
   e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(64 * C::WAVES), lds, s, a,
@@ -332,26 +336,26 @@ static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t
   return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int BITS, bool ZP, bool MOE>
+template <int BM, int BN, int WM, int WN, int BITS, bool ZP, bool MOE>
 static hipError_t launch_group(const GemmArgs &a, int group, int64_t xs_rows, int64_t cap, float *xs,
                                bool sums, hipStream_t s) {
   switch (group) {
-    case 32: return launch_a16_tiled_t<BM, WM, WN, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, sums, s);
-    case 64: return launch_a16_tiled_t<BM, WM, WN, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, sums, s);
-    case 128: return launch_a16_tiled_t<BM, WM, WN, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, sums, s);
+    case 32: return launch_a16_tiled_t<BM, BN, WM, WN, BITS, ZP, 32, MOE>(a, xs_rows, cap, xs, sums, s);
+    case 64: return launch_a16_tiled_t<BM, BN, WM, WN, BITS, ZP, 64, MOE>(a, xs_rows, cap, xs, sums, s);
+    case 128: return launch_a16_tiled_t<BM, BN, WM, WN, BITS, ZP, 128, MOE>(a, xs_rows, cap, xs, sums, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int BM, int WM, int WN, bool MOE>
+template <int BM, int BN, int WM, int WN, bool MOE>
 static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t xs_rows, int64_t cap,
                              float *xs, bool sums, hipStream_t s) {
   const int g = d.group_size;
   switch (d.wtype) {
-    case QG_W_INT4: return launch_group<BM, WM, WN, 4, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
-    case QG_W_UINT4: return launch_group<BM, WM, WN, 4, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
-    case QG_W_INT3: return launch_group<BM, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
-    case QG_W_UINT3: return launch_group<BM, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_INT4: return launch_group<BM, BN, WM, WN, 4, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_UINT4: return launch_group<BM, BN, WM, WN, 4, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_INT3: return launch_group<BM, BN, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_UINT3: return launch_group<BM, BN, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
   }
   return hipErrorInvalidValue;
 }
@@ -360,26 +364,34 @@ uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m) {
   return align_up((uint64_t)(d.k / d.group_size) * (uint64_t)m * 4, 256);
 }
 
-// Dense: a.m rows in bm-row tiles.  MoE: the tile list a.tiles (capacity
-// tiles_cap) of bm-row tiles, bm = 128 (large experts) or kMoeSmallTileRows
-// (small experts: 8 waves of 16 columns each).  waves: 4 (2 x 2, one per
-// SIMD) or 8 (4 x 2).  sums = false reuses the group row sums already in ws.
-hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, bool moe,
+// Dense: a.m rows in bm x bn tiles (256 x 128, 128 x 128 or 128 x 256).
+// MoE: the tile list a.tiles (capacity tiles_cap) of bm-row tiles, bm = 128
+// (large experts; 128 or 256 columns) or 64 / 32 (small experts: 8 waves of
+// 16 columns each).
+// waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2, or 2 x 4 for 256 columns).
+// sums = false reuses the group row sums already in ws.
+hipError_t launch_a16_tiled(const GemmArgs &a, const qg_layer_desc &d, int bm, int bn, bool moe,
                             int64_t xs_rows, int64_t tiles_cap, int waves, void *ws, bool sums,
                             hipStream_t s) {
   if (a.k % 128 != 0) return hipErrorInvalidValue;
   float *xs = (float *)ws;
-  if (moe && bm == 64) return launch_fmt<64, 1, 8, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
-  if (moe && bm == 32) return launch_fmt<32, 1, 8, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
-  if (moe && bm != kMoeTileRows) return hipErrorInvalidValue;
-  if (waves == 8) {
-    if (moe) return launch_fmt<kMoeTileRows, 4, 2, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
-    return bm == 256 ? launch_fmt<256, 4, 2, false>(a, d, xs_rows, 0, xs, sums, s)
-                     : launch_fmt<128, 4, 2, false>(a, d, xs_rows, 0, xs, sums, s);
+  if (moe) {
+    if (bm == 64) return launch_fmt<64, 128, 1, 8, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+    if (bm == 32) return launch_fmt<32, 128, 1, 8, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+    if (bm != kMoeTileRows) return hipErrorInvalidValue;
+    if (bn == 256 && waves == 8) return launch_fmt<kMoeTileRows, 256, 2, 4, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
+    return waves == 8 ? launch_fmt<kMoeTileRows, 128, 4, 2, true>(a, d, xs_rows, tiles_cap, xs, sums, s)
+                      : launch_fmt<kMoeTileRows, 128, 2, 2, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
   }
-  if (moe) return launch_fmt<kMoeTileRows, 2, 2, true>(a, d, xs_rows, tiles_cap, xs, sums, s);
-  return bm == 256 ? launch_fmt<256, 2, 2, false>(a, d, xs_rows, 0, xs, sums, s)
-                   : launch_fmt<128, 2, 2, false>(a, d, xs_rows, 0, xs, sums, s);
+  if (bn == 256) {
+    if (bm != 128 || waves != 8) return hipErrorInvalidValue;
+    return launch_fmt<128, 256, 2, 4, false>(a, d, xs_rows, 0, xs, sums, s);
+  }
+  if (waves == 8)
+    return bm == 256 ? launch_fmt<256, 128, 4, 2, false>(a, d, xs_rows, 0, xs, sums, s)
+                     : launch_fmt<128, 128, 4, 2, false>(a, d, xs_rows, 0, xs, sums, s);
+  return bm == 256 ? launch_fmt<256, 128, 2, 2, false>(a, d, xs_rows, 0, xs, sums, s)
+                   : launch_fmt<128, 128, 2, 2, false>(a, d, xs_rows, 0, xs, sums, s);
 }
 
 }  // namespace qg

@@ -193,24 +193,28 @@ def test_mx_tiled_identity_rows_exact():
 # LDS-tiled bf16-MFMA kernel for the integer formats (M >= 256)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bm", ["256", "128"])
+@pytest.mark.parametrize("tile", ["256x128", "128x128", "128x256"])
 @pytest.mark.parametrize("wtype", A16)
 @pytest.mark.parametrize("group", [32, 64, 128])
-def test_a16_tiled_formats_and_groups(monkeypatch, bm, wtype, group):
-    """Every integer format and group size through the tiled kernel, with a
-    partial row tile and a partial column tile (N = 200 is not a multiple of
-    the 128-column tile)."""
+def test_a16_tiled_formats_and_groups(monkeypatch, tile, wtype, group):
+    """Every integer format and group size through the tiled kernel at each
+    tile shape, with a partial row tile and a partial column tile (N = 200 is
+    not a multiple of the 128- or 256-column tile)."""
+    bm, bn = tile.split("x")
     monkeypatch.setenv("QG_TILED_BM", bm)
+    monkeypatch.setenv("QG_A16_BN", bn)
     layer = Layer(wtype, 200, 640, group, seed=wtype * 10 + group)
     m = 300
-    assert f"a16_tiled BM={bm}" in qg.describe_dispatch(layer.w, m)
+    assert f"a16_tiled BM={bm} BN={bn}" in qg.describe_dispatch(layer.w, m)
     _check(layer, Acts(False, m, 640, seed=m + group), m)
 
 
+@pytest.mark.parametrize("bn", ["128", "256"])
 @pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (512, 72, 128), (777, 1040, 4096)])
-def test_a16_tiled_ragged(m, n, k):
+def test_a16_tiled_ragged(monkeypatch, m, n, k, bn):
+    monkeypatch.setenv("QG_A16_BN", bn)
     layer = Layer(qg.W_UINT4, n, k, 128, seed=m)
-    assert "a16_tiled" in qg.describe_dispatch(layer.w, m)
+    assert f"a16_tiled BM={256 if bn == '128' else 128} BN={bn}" in qg.describe_dispatch(layer.w, m)
     _check(layer, Acts(False, m, k, seed=m), m)
 
 

@@ -60,14 +60,15 @@ def moe_reference(layer, xdq, ids, by_token, verbose=False):
     return oracle.moe_gemm(wdq, xdq, ids, rows_by_token=by_token)
 
 
-# (QG_MOE_TILED_MIN, QG_MOE_SMALL) per split of the experts between kernels
+# environment per split of the experts between kernels
 SPLITS = {
-    "skinny": ("0", "1"),        # every expert on the skinny kernel
-    "tiled": ("1", "1"),         # every expert with a row on 128-row tiles
-    "mixed": ("12", "1"),        # >= 12 rows: 128-row tiles; fewer: small tiles (integer formats)
-    "mixed_skinny": ("12", "0"), # >= 12 rows: 128-row tiles; fewer: skinny kernel
-    "small": ("1000", "1"),      # integer formats: every expert on 64-row small tiles
-    "small32": ("1000", "1", "32"),  # the same on 32-row small tiles
+    "skinny": {"QG_MOE_TILED_MIN": "0"},   # every expert on the skinny kernel
+    "tiled": {"QG_MOE_TILED_MIN": "1"},    # every expert with a row on 128-row tiles
+    "tiled_bn128": {"QG_MOE_TILED_MIN": "1", "QG_A16_BN": "128"},  # the same, 128-column tiles
+    "mixed": {"QG_MOE_TILED_MIN": "12"},   # >= 12 rows: 128-row tiles; fewer: small tiles (integer formats)
+    "mixed_skinny": {"QG_MOE_TILED_MIN": "12", "QG_MOE_SMALL": "0"},  # fewer: skinny kernel
+    "small": {"QG_MOE_TILED_MIN": "1000"},  # integer formats: every expert on 64-row small tiles
+    "small32": {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL_BM": "32"},  # the same on 32-row small tiles
 }
 
 
@@ -77,11 +78,10 @@ def test_moe_small_all_row_modes(monkeypatch, wtype, split):
     """All row modes, with the experts split between the kernels by row count
     (the small-tile form exists for the integer formats only; MXFP4 runs the
     skinny kernel where they would use it)."""
-    if wtype == qg.W_MXFP4 and split in ("mixed_skinny", "small", "small32"):
+    if wtype == qg.W_MXFP4 and split in ("tiled_bn128", "mixed_skinny", "small", "small32"):
         pytest.skip("same dispatch as another split for MXFP4")
-    monkeypatch.setenv("QG_MOE_TILED_MIN", SPLITS[split][0])
-    monkeypatch.setenv("QG_MOE_SMALL", SPLITS[split][1])
-    monkeypatch.setenv("QG_MOE_SMALL_BM", SPLITS[split][2] if len(SPLITS[split]) > 2 else "64")
+    for var, val in SPLITS[split].items():
+        monkeypatch.setenv(var, val)
     t, e, topk, n, k = 37, 16, 4, 80, 640
     g = 32 if wtype == qg.W_MXFP4 else 128
     ids = synth.route(synth.rng(1, wtype), t, e, topk)

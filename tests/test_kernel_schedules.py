@@ -35,27 +35,29 @@ def test_raster_visits_every_tile_once_for_oversized_grids():
         assert all(0 <= a < m and 0 <= b < n for a, b in live)
 
 
-def a16_rings(bm, bits, zp, group, waves=4, small=False):
+def a16_rings(bm, bits, zp, group, waves=4, small=False, bn=128):
     """Ring depths and per-stage load counts of the integer-format tiled kernel
     (small: one wave per 16 columns, rings within half of LDS)."""
     gpb = 128 // group
+    nblk = bn // 16
     a_stage = bm * 256 + gpb * max(bm, 64) * 4
-    b_stage = 8 * 64 * (16 if bits == 4 else 12) + 128 * 16 + (128 * 4 if zp else 0)
+    b_stage = nblk * 64 * (16 if bits == 4 else 12) + bn * 16 + (bn * 4 if zp else 0)
     cap = LDS // 2 if small else LDS
-    na = 2 if small else (3 if 3 * a_stage + 2 * b_stage <= cap else 2)
+    na = 2 if small else (3 if 3 * a_stage + (3 if bn > 128 else 2) * b_stage <= cap else 2)
     nb = min(6, (cap - na * a_stage) // b_stage)
     a_issue = bm * 256 // 1024 // waves + gpb
-    b_issue = (8 if bits == 4 else 24) // waves + 1 + (1 if zp else 0)
+    b_issue = (nblk if bits == 4 else 3 * nblk) // waves + 1 + (1 if zp else 0)
     after = (b_issue if nb > na else 0) + (na - 2) * (a_issue + b_issue)
     return na, nb, a_issue, b_issue, after, na * a_stage + nb * b_stage, cap
 
 
 def test_a16_tiled_ring_waits_cover_each_stage():
     # 128- and 256-row tiles (4 or 8 waves) and the 32- and 64-row small tiles (8 waves)
-    shapes = [(bm, w, False) for bm in (128, 256) for w in (4, 8)] + [(32, 8, True), (64, 8, True)]
-    for (bm, waves, small), bits, zp, group in itertools.product(shapes, [3, 4], [False, True],
-                                                               [32, 64, 128]):
-        na, nb, ai, bi, after, lds, cap = a16_rings(bm, bits, zp, group, waves, small)
+    shapes = [(bm, w, False, 128) for bm in (128, 256) for w in (4, 8)] + \
+             [(32, 8, True, 128), (64, 8, True, 128), (128, 8, False, 256)]
+    for (bm, waves, small, bn), bits, zp, group in itertools.product(shapes, [3, 4], [False, True],
+                                                                   [32, 64, 128]):
+        na, nb, ai, bi, after, lds, cap = a16_rings(bm, bits, zp, group, waves, small, bn)
         assert 2 <= na <= nb and lds <= cap and after <= 63
         for kbs in range(1, 13):
             seq = []
