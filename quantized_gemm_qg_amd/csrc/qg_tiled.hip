@@ -221,24 +221,26 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 
 // Activation scales regrouped by K step: out[kb * m_pad + r] holds the 4 bytes
 // of row r's scales for K step kb (bytes 4 kb .. 4 kb + 3 of the row); m_pad =
-// m rounded up to 256 (rows m .. m_pad - 1 are not written).  A
-// workgroup transposes 64 rows x 64 K steps through LDS: reads run along the
-// rows (consecutive threads, consecutive dwords of one row), writes along the
-// steps (consecutive threads, consecutive rows).
+// m rounded up to 256 (rows m .. m_pad - 1 are not written).  A workgroup
+// transposes 16 rows x 64 K steps through LDS (16 rows so that M = 4096 gives
+// 256 workgroups): reads run along the rows, writes along the steps.
 __global__ __launch_bounds__(256) void mx_scales_by_step_kernel(const uint8_t *xs, int m, int64_t m_pad,
                                                                 int kq, int kbs, uint32_t *out) {
-  __shared__ uint32_t tile[64][65];
-  const int r0 = blockIdx.x * 64, kb0 = blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+  __shared__ uint32_t tile[64][17];
+  const int r0 = blockIdx.x * 16, kb0 = blockIdx.y * 64;
+  const bool dword = ((uintptr_t)xs & 3) == 0;  // kq % 4 == 0, so every row is aligned too
+  for (int i = threadIdx.x; i < 16 * 64; i += 256) {
     const int r = i >> 6, kb = i & 63;
     if (r0 + r < m && kb0 + kb < kbs) {
       const uint8_t *p = xs + (int64_t)(r0 + r) * kq + 4 * (kb0 + kb);
-      tile[kb][r] = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) | ((uint32_t)p[3] << 24);
+      tile[kb][r] = dword ? *(const uint32_t *)p
+                          : ((uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16) |
+                             ((uint32_t)p[3] << 24));
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int kb = i >> 6, r = i & 63;
+  for (int i = threadIdx.x; i < 16 * 64; i += 256) {
+    const int kb = i >> 4, r = i & 15;
     if (r0 + r < m && kb0 + kb < kbs) out[(int64_t)(kb0 + kb) * m_pad + r0 + r] = tile[kb][r];
   }
 }
@@ -274,7 +276,7 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
   GemmArgs a = a_in;
   if (!moe) {
     if (!ws) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((a.m + 63) / 64), (unsigned)((a.k_blocks + 63) / 64)),
+    hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((a.m + 15) / 16), (unsigned)((a.k_blocks + 63) / 64)),
                        dim3(256), 0, s, a.x_scales, a.m, ((int64_t)a.m + 255) & ~(int64_t)255, a.k >> 5,
                        a.k_blocks, (uint32_t *)ws);
     const hipError_t e = hipGetLastError();
