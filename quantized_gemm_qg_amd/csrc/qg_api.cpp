@@ -250,7 +250,7 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
 // tiles); the rest to the small-tile form of the integer formats' tiled kernel
 // or (MXFP4) to the skinny kernel; 0 = skinny only.  QG_MOE_TILED_MIN
 // overrides (0 disables the tiled kernels).
-static bool moe_small_tiles(const qg_weight &w, int min_rows);
+static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
@@ -266,7 +266,7 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
   if (min_rows <= 0) return 0;
   // no expert can reach the threshold: all go to the small-tile form
   // (integer formats) or the skinny kernel
-  if (pairs < min_rows && (mx || !moe_small_tiles(w, min_rows))) return 0;
+  if (pairs < min_rows && !moe_small_tiles(w, pairs, min_rows)) return 0;
   return min_rows;
 }
 
@@ -322,15 +322,19 @@ static int64_t moe_small_tiles_cap(const qg_weight &w, int64_t pairs) {
   return pairs / moe_small_bm() + std::min<int64_t>(w.desc.num_experts, pairs) + 1;
 }
 
-// Integer formats: experts below the tiled threshold run the tiled kernel's
-// small-tile form (one pass over the expert's weights for all of its rows,
-// through the same deep LDS ring) instead of the skinny kernel, which re-reads
-// the weights per 16 rows and cannot keep enough bytes in flight with one
-// item per workgroup.  QG_MOE_SMALL=0 keeps them on the skinny kernel.
-static bool moe_small_tiles(const qg_weight &w, int min_rows) {
-  if (min_rows <= 0 || w.desc.wtype == QG_W_MXFP4) return false;
+// Experts below the tiled threshold run the tiled kernels' small-tile form
+// (one pass over the expert's weights for all of its rows, through the same
+// deep LDS ring) instead of the skinny kernel, which re-reads the weights per
+// 16 rows and cannot keep enough bytes in flight with one item per workgroup.
+// Below 256 pairs (a few tokens) the skinny kernel's K split across waves
+// keeps more loads in flight than the few small-tile workgroups, so it stays.
+// QG_MOE_SMALL=0 keeps small experts on the skinny kernel, =1 forces the
+// small tiles.
+static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows) {
+  if (min_rows <= 0) return false;
   const char *e = getenv("QG_MOE_SMALL");
-  return !(e && *e && atoi(e) == 0);
+  if (e && *e) return atoi(e) != 0;
+  return pairs >= 256;
 }
 
 static uint64_t moe_list_bytes(int64_t cap) { return align_up((uint64_t)(2 + 2 * cap) * 4, 256); }
@@ -340,7 +344,7 @@ static uint64_t moe_list_bytes(int64_t cap) { return align_up((uint64_t)(2 + 2 *
 static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_count, int min_rows) {
   if (min_rows <= 0) return 0;
   uint64_t b = moe_list_bytes(moe_tiles_cap(w, pairs, min_rows));
-  if (moe_small_tiles(w, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
+  if (moe_small_tiles(w, pairs, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
   if (w.desc.wtype != QG_W_MXFP4) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
   return b;
 }
@@ -629,7 +633,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   if (min_rows > 0) {
     // experts with >= min_rows rows: tile list, then the tiled kernel
     const int64_t cap = moe_tiles_cap(*w, pairs, min_rows);
-    const bool small = moe_small_tiles(*w, min_rows);
+    const bool small = moe_small_tiles(*w, pairs, min_rows);
     const int64_t cap_s = small ? moe_small_tiles_cap(*w, pairs) : 0;
     int32_t *tiles = (int32_t *)ws;
     int32_t *tiles_s = (int32_t *)((uint8_t *)ws + moe_list_bytes(cap));
@@ -638,24 +642,26 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     if (he != hipSuccess) return hip_status(he);
     a.tiles = tiles;
     a.group_m = moe_group_m();
-    if (L.is_mx) {
+    void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
+    if (L.is_mx)
       he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream);
-    } else {
-      void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);
+    else
       he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
                             xs, true, stream);
-      if (he == hipSuccess && small) {
-        const int sbm = moe_small_bm();
-        he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
-                              (int32_t)cap_s, tiles_s, stream);
-        if (he != hipSuccess) return hip_status(he);
-        a.tiles = tiles_s;
-        a.group_m = 1;
-        he = launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
-        return hip_status(he);  // every expert with rows is covered
-      }
-    }
     if (he != hipSuccess) return hip_status(he);
+    if (small) {
+      // the MX small tiles have 64 rows (QG_MOE_SMALL_BM applies to the
+      // integer formats; the list capacity covers either)
+      const int sbm = L.is_mx ? kMoeSmallTileRows : moe_small_bm();
+      he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
+                            (int32_t)cap_s, tiles_s, stream);
+      if (he != hipSuccess) return hip_status(he);
+      a.tiles = tiles_s;
+      a.group_m = 1;
+      he = L.is_mx ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream)
+                   : launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
+      return hip_status(he);  // every expert with rows is covered
+    }
     a.moe_min_rows = min_rows;
   }
   // the remaining (small) experts

@@ -196,6 +196,22 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     };
     i32x8 af[2];
     int asc[2];
+    if constexpr (WM == 1) {
+      // small tiles (MoE experts with few rows): row blocks past the tile's
+      // rows are skipped (workgroup-uniform)
+      const int mbv = min(C::MB, (tr.rows + 15) >> 4);
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        if (i < mbv) {
+          read_a(i, af[0], asc[0]);
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[0], bf[j], acc[i][j], 0, 4, 0,
+                                                                          asc[0], 0, bsc[j]);
+        }
+      }
+      continue;
+    }
     read_a(0, af[0], asc[0]);
     // B (2 NB reads) and A block 0 (3 reads) first
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NB + 3, 0);
@@ -268,7 +284,8 @@ static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipSt
 
 // Dense: bm-row tiles (128 or 256) of bn columns (192, 224 or 256 with 8
 // waves; 256 with 4).  MoE: the tile list a.tiles (capacity tiles_cap) of
-// kMoeTileRows x 256 tiles.  waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2, two
+// kMoeTileRows x 256 tiles, or (bm = 64, 8 waves) 64 x 128 small tiles, one
+// wave per 16 columns and all rows, for experts with few rows.  waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2, two
 // per SIMD).
 hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
                            void *ws, hipStream_t s) {
@@ -284,6 +301,7 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
     a.x_scales_t = (const uint32_t *)ws;
   }
   if (waves == 8) {
+    if (moe && bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true>(a, tiles_cap, s);
     if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true>(a, tiles_cap, s);
     if (bm == 256) {
       if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false>(a, 0, s);

@@ -65,10 +65,10 @@ SPLITS = {
     "skinny": {"QG_MOE_TILED_MIN": "0"},   # every expert on the skinny kernel
     "tiled": {"QG_MOE_TILED_MIN": "1"},    # every expert with a row on 128-row tiles
     "tiled_bn128": {"QG_MOE_TILED_MIN": "1", "QG_A16_BN": "128"},  # the same, 128-column tiles
-    "mixed": {"QG_MOE_TILED_MIN": "12"},   # >= 12 rows: 128-row tiles; fewer: small tiles (integer formats)
+    "mixed": {"QG_MOE_TILED_MIN": "12", "QG_MOE_SMALL": "1"},  # >= 12 rows: 128-row tiles; fewer: small tiles
     "mixed_skinny": {"QG_MOE_TILED_MIN": "12", "QG_MOE_SMALL": "0"},  # fewer: skinny kernel
-    "small": {"QG_MOE_TILED_MIN": "1000"},  # integer formats: every expert on 64-row small tiles
-    "small32": {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL_BM": "32"},  # the same on 32-row small tiles
+    "small": {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1"},  # every expert on 64-row small tiles
+    "small32": {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1", "QG_MOE_SMALL_BM": "32"},  # 32-row (integer formats)
 }
 
 
@@ -76,9 +76,8 @@ SPLITS = {
 @pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_UINT3, qg.W_MXFP4])
 def test_moe_small_all_row_modes(monkeypatch, wtype, split):
     """All row modes, with the experts split between the kernels by row count
-    (the small-tile form exists for the integer formats only; MXFP4 runs the
-    skinny kernel where they would use it)."""
-    if wtype == qg.W_MXFP4 and split in ("tiled_bn128", "mixed_skinny", "small", "small32"):
+    (128-row tiles, 64-row small tiles, the skinny kernel)."""
+    if wtype == qg.W_MXFP4 and split in ("tiled_bn128", "small32"):
         pytest.skip("same dispatch as another split for MXFP4")
     for var, val in SPLITS[split].items():
         monkeypatch.setenv(var, val)
@@ -174,8 +173,8 @@ def test_moe_w4a8_128_experts_padding_shape(tokens):
 def test_moe_tiled_multi_tile_experts(wtype):
     """Skewed routing over 8 experts with hundreds of rows each: experts span
     several 128-row tiles with a partial last tile; small experts take the
-    small-tile form (integer formats) or the skinny kernel (MXFP4), the default
-    split.  N = 200 leaves a partial column tile."""
+    small-tile form (the default split at 1024 pairs).  N = 200 leaves a
+    partial column tile."""
     t, e, topk, n, k = 512, 8, 2, 200, 1024
     g = 32 if wtype == qg.W_MXFP4 else 64
     mx = wtype == qg.W_MXFP4
