@@ -171,13 +171,14 @@ def mx_acts_device(torch, rows, k, gen):
     return q.view(torch.uint8).view(rows, k).contiguous(), (e + 127).to(torch.uint8).contiguous()
 
 
-def moe_dispatch(ids, experts, mx, tiled_min=64):
+def moe_dispatch(ids, experts, mx, tiled_min=64, small_min_pairs=256):
     """Which kernel serves which experts under the default split."""
     counts = np.bincount(ids.ravel(), minlength=experts)
     big = int((counts >= tiled_min).sum())
     small = int(((counts > 0) & (counts < tiled_min)).sum())
     fmt = "mx" if mx else "a16"
-    rest = f"mx_skinny for {small}" if mx else f"a16_tiled small tiles BM=64 for {small}"
+    rest = (f"{fmt}_tiled small tiles BM=64 for {small}" if ids.size >= small_min_pairs
+            else f"{fmt}_skinny for {small}")
     return f"{fmt}_tiled BM=128 for {big} experts with >= {tiled_min} rows; {rest} smaller"
 
 
