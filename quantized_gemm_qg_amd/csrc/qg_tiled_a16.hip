@@ -87,15 +87,19 @@ struct A16Cfg {
   static constexpr int LDS = NA * A_STAGE + NB * B_STAGE;
   // loads per wave and stage
   static constexpr int A_LOADS = BM * 256 / 1024 / WAVES;            // 1-KB copies of A
-  static constexpr int A_ISSUE = A_LOADS + GPB;
   static constexpr int B_LOADS = (BITS == 4 ? NBLK : 3 * NBLK) / WAVES;  // 1-KB (4-bit) or 256-B (3-bit) copies
-  static constexpr int B_ISSUE = B_LOADS + 1 + (ZP ? 1 : 0);
+  // the group row sums (SX) are copied by the first SXR / 64 waves, the
+  // scales and zero points (SS, SZ) by the first SS_PIECES: per-wave counts
+  static constexpr int SX_WAVES = SXR / 64;
+  static constexpr int A_ISSUE = A_LOADS + GPB;             // an SX wave
+  static constexpr int B_ISSUE = B_LOADS + 1 + (ZP ? 1 : 0);  // an SS wave
   // Each step issues its activation loads, then its weight loads.  In steady
   // state, the loads issued after the later of stage kb's two groups: stage
   // kb's weights went out in an earlier step than its activations when the
   // weight ring is deeper (followed by that step's weight loads), in the same
   // step otherwise.
-  static constexpr int AFTER_A = (NB > NA ? B_ISSUE : 0) + (NA - 2) * (A_ISSUE + B_ISSUE);
+  static constexpr int after(int ai, int bi) { return (NB > NA ? bi : 0) + (NA - 2) * (ai + bi); }
+  static constexpr int AFTER_A = after(A_ISSUE, B_ISSUE);   // the largest
   static constexpr int MI = BM / WM / 16;             // 16-row blocks per wave
   // small tiles (one wave per 16 columns, every wave all BM rows) are for
   // MoE experts with few rows: row blocks past the tile's rows are skipped
@@ -105,7 +109,25 @@ struct A16Cfg {
   static_assert(NB >= 2 && NB >= NA, "weight ring too shallow");
   static_assert(LDS <= LDS_CAP, "rings exceed LDS");
   static_assert(AFTER_A <= 63, "vmcnt range");
+  static_assert(SX_WAVES <= WAVES && SS_PIECES <= WAVES, "copy pieces");
 };
+
+// Wait of step kb for a wave that issues AI activation and BI weight copies
+// per stage: once at most after(AI, BI) loads are outstanding, both groups of
+// stage kb have landed (memory counters retire in issue order).  Near the end
+// fewer loads follow, so the wait is tightened, never loosened; in the
+// prologue more loads follow, so it is conservative.
+template <typename C, int AI, int BI>
+__device__ __forceinline__ void a16_stage_wait(int kb, int kbs) {
+  constexpr int AFTER = C::after(AI, BI);
+  if (kb + C::NB - 2 < kbs) {
+    QG_WAIT_VMCNT(AFTER);
+  } else if (C::NA == 3 && kb + 1 < kbs) {
+    QG_WAIT_VMCNT(AI);
+  } else {
+    QG_WAIT_VMCNT(0);
+  }
+}
 
 // Workgroup barrier that the compiler may not move LDS accesses across; the
 // memory-counter waits are explicit (QG_WAIT_VMCNT) so that loads of later
@@ -160,13 +182,12 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
       b_off[i] = (uint32_t)(min(nt0 + blk, a.n_tiles - 1) * kbs) * 768u + 256u * (piece % 3) + 4u * lane;
     }
   }
-  // SS / SZ: column 64 (wave % SS_PIECES) + lane of the tile (later waves
-  // repeat the first ones' copies: the same bytes to the same place)
-  const int ss_piece = wave % C::SS_PIECES;
-  const int ncol = min(nt0 * 16 + 64 * ss_piece + lane, a.n_tiles * 16 - 1);
+  // SS / SZ: wave w < SS_PIECES copies columns 64 w .. 64 w + 63 of the tile
+  const int ncol = min(nt0 * 16 + 64 * (wave % C::SS_PIECES) + lane, a.n_tiles * 16 - 1);
   const uint8_t *ss_src = wexp + a.scales_offset + (uint64_t)ncol * gp * 2;
   const uint32_t *sz_src = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
-  const int sx_row = 64 * (wave % (C::SXR / 64)) + lane;
+  const bool sx_wave = wave < C::SX_WAVES, ss_wave = wave < C::SS_PIECES;
+  const int sx_row = 64 * (sx_wave ? wave : 0) + lane;
   const float *sx_src = xs + tr.x(a, sx_row);
 
   auto issue_a = [&](int kb) {
@@ -175,10 +196,11 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
+    if (sx_wave) {
 #pragma unroll
-    for (int gi = 0; gi < C::GPB; ++gi)
-      lds_dma4(sx_src + (int64_t)(kb * C::GPB + gi) * xs_rows,
-               st + C::A + (gi * C::SXR + 64 * (wave % (C::SXR / 64))) * 4);
+      for (int gi = 0; gi < C::GPB; ++gi)
+        lds_dma4(sx_src + (int64_t)(kb * C::GPB + gi) * xs_rows, st + C::A + (gi * C::SXR + 64 * wave) * 4);
+    }
   };
   auto issue_b = [&](int kb) {
     uint8_t *st = smem + C::OFF_BRING + (kb % C::NB) * C::B_STAGE;
@@ -189,9 +211,11 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
       else
         lds_dma4(wexp + b_off[i] + kb * 768u, st + (C::B_LOADS * wave + i) * 256);
     }
-    const int g0 = kb * C::GPB;
-    lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + ss_piece * 1024);
-    if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + ss_piece * 256);
+    if (ss_wave) {
+      const int g0 = kb * C::GPB;
+      lds_dma16(ss_src + (g0 & ~7) * 2, st + C::OFF_SS + wave * 1024);
+      if constexpr (ZP) lds_dma4(sz_src + (g0 >> 3), st + C::OFF_SZ + wave * 256);
+    }
   };
 
   f32x4 acc[C::MI][C::NJ];
@@ -206,16 +230,12 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
     if (s < kbs) issue_b(s);
   }
   for (int kb = 0; kb < kbs; ++kb) {
-    // once at most AFTER_A loads are outstanding, both groups of stage kb have
-    // landed (memory counters retire in issue order).  Near the end fewer
-    // loads follow, so the wait is tightened, never loosened; in the prologue
-    // more loads follow, so it is conservative.
-    if (kb + C::NB - 2 < kbs) {
-      QG_WAIT_VMCNT(C::AFTER_A);
-    } else if (C::NA == 3 && kb + 1 < kbs) {
-      QG_WAIT_VMCNT(C::A_ISSUE);
+    if (sx_wave) {
+      if (ss_wave) a16_stage_wait<C, C::A_ISSUE, C::B_ISSUE>(kb, kbs);
+      else a16_stage_wait<C, C::A_ISSUE, C::B_LOADS>(kb, kbs);
     } else {
-      QG_WAIT_VMCNT(0);
+      if (ss_wave) a16_stage_wait<C, C::A_LOADS, C::B_ISSUE>(kb, kbs);
+      else a16_stage_wait<C, C::A_LOADS, C::B_LOADS>(kb, kbs);
     }
     lds_barrier();  // stage kb is in LDS; the buffers of stage kb - 1 are free
     if (kb + C::NA - 1 < kbs) issue_a(kb + C::NA - 1);

@@ -45,10 +45,16 @@ def a16_rings(bm, bits, zp, group, waves=4, small=False, bn=128):
     cap = LDS // 2 if small else LDS
     na = 2 if small else (3 if 3 * a_stage + (3 if bn > 128 else 2) * b_stage <= cap else 2)
     nb = min(6, (cap - na * a_stage) // b_stage)
-    a_issue = bm * 256 // 1024 // waves + gpb
-    b_issue = (nblk if bits == 4 else 3 * nblk) // waves + 1 + (1 if zp else 0)
-    after = (b_issue if nb > na else 0) + (na - 2) * (a_issue + b_issue)
-    return na, nb, a_issue, b_issue, after, na * a_stage + nb * b_stage, cap
+    a_loads = bm * 256 // 1024 // waves
+    b_loads = (nblk if bits == 4 else 3 * nblk) // waves
+    # per wave kind: the first waves also copy the row sums (+ gpb) and the
+    # scales / zero points (+ 1 + zp)
+    kinds = [(a_loads + sx, b_loads + ss) for sx in (0, gpb) for ss in (0, 1 + (1 if zp else 0))]
+    return na, nb, kinds, na * a_stage + nb * b_stage, cap
+
+
+def a16_after(na, nb, ai, bi):
+    return (bi if nb > na else 0) + (na - 2) * (ai + bi)
 
 
 def test_a16_tiled_ring_waits_cover_each_stage():
@@ -57,9 +63,11 @@ def test_a16_tiled_ring_waits_cover_each_stage():
              [(32, 8, True, 128), (64, 8, True, 128), (128, 8, False, 256)]
     for (bm, waves, small, bn), bits, zp, group in itertools.product(shapes, [3, 4], [False, True],
                                                                    [32, 64, 128]):
-        na, nb, ai, bi, after, lds, cap = a16_rings(bm, bits, zp, group, waves, small, bn)
-        assert 2 <= na <= nb and lds <= cap and after <= 63
-        for kbs in range(1, 13):
+        na, nb, kinds, lds, cap = a16_rings(bm, bits, zp, group, waves, small, bn)
+        assert 2 <= na <= nb and lds <= cap
+        for (ai, bi), kbs in itertools.product(kinds, range(1, 13)):
+            after = a16_after(na, nb, ai, bi)
+            assert after <= 63
             seq = []
             for s in range(nb - 1):
                 if s < na - 1 and s < kbs:
