@@ -51,20 +51,24 @@ namespace qg {
 
 constexpr int kStages = 3;
 
-// BM x BN tile, WM x WN waves, each wave (BM / WM) x (BN / WN)
-template <int BM, int BN, int WM, int WN>
+// BM x BN tile, WM x WN waves, each wave (BM / WM) x (BN / WN).  SAR: the
+// activation scales go to a two-slot ring of 4-step runs (16 bytes per row)
+// instead of 4 bytes per row in every stage.
+template <int BM, int BN, int WM, int WN, bool SAR>
 struct MxCfg {
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int NBLK = BN / 16;                      // packed n-tiles per tile
   static constexpr int A = BM * 128;
   static constexpr int B = NBLK * 1024;
-  static constexpr int SA = BM * 4;
+  static constexpr int SA = SAR ? 0 : BM * 4;
   static constexpr int SW_PIECES = (NBLK + 3) / 4;          // 1-KB copies: 4 n-tiles' 256-B units each
   static constexpr int SW = SW_PIECES * 1024;               // one slot (units past NBLK unused)
   static constexpr int STAGE = A + B + SA;
   static constexpr int OFF_SW = 3 * STAGE;                  // the two SW slots
-  static constexpr int LDS = OFF_SW + 2 * SW;
+  static constexpr int SAR_SLOT = SAR ? BM * 16 : 0;        // [row][4 steps x 4 bytes]
+  static constexpr int OFF_SAR = OFF_SW + 2 * SW;           // the two SA ring slots
+  static constexpr int LDS = OFF_SAR + 2 * SAR_SLOT;
   static constexpr int A_LOADS = BM * 128 / 1024 / WAVES;  // 1-KB copies of A per wave
   static constexpr int B_LOADS = (NBLK + WAVES - 1) / WAVES;  // 1-KB blocks of B per wave
   static constexpr int SA_WAVES = BM / 64;                  // waves that copy a 256-B SA piece
@@ -77,9 +81,9 @@ struct MxCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int WM, int WN, bool MOE>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR>
 __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
-  using C = MxCfg<BM, BN, WM, WN>;
+  using C = MxCfg<BM, BN, WM, WN, SAR>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -116,13 +120,17 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   // from the scales regrouped by K step (rows padded to 256, so the copy
   // stays in the buffer; rows past M are never stored).  Otherwise BM / 64
   // pieces of 256 B, one per wave of the first BM / 64, with rows clamped.
-  constexpr bool SA_X4 = !MOE && BM == 256;
+  // With SAR (K % 512 == 0 and 16-byte aligned scales) the first BM / 64
+  // waves copy, every fourth step, the 16 bytes of 4 steps of one row per
+  // lane straight from the row-major scales into the SA ring.
+  constexpr bool SA_X4 = !SAR && !MOE && BM == 256;
   const bool sa_wave = SA_X4 ? wave == 0 : wave < C::SA_WAVES;
   const int64_t m_pad = ((int64_t)a.m + 255) & ~(int64_t)255;  // regrouped row stride
   const int64_t sa_row = SA_X4 ? (int64_t)tr.base + 4 * lane : tr.x(a, (sa_wave ? wave : 0) * 64 + lane);
-  // per K step: + 4 bytes (MoE, rows of kq bytes) or + 4 m_pad bytes (dense, by step)
-  const uint8_t *sa_src = MOE ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
-  const int64_t sa_step = MOE ? 4 : 4 * m_pad;
+  // per K step: + 4 bytes (rows of kq bytes) or + 4 m_pad bytes (dense, regrouped by step)
+  const bool sa_rows = MOE || SAR;
+  const uint8_t *sa_src = sa_rows ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
+  const int64_t sa_step = sa_rows ? 4 : 4 * m_pad;
   // SW: copy p (by wave p < SW_PIECES) moves the 256-B units of n-tiles
   // 4p .. 4p + 3 of the tile for K steps 4j .. 4j + 3 (unit of n-tile nt at
   // nt * kb_pad / 4 * 256 + 256 j); lanes 16u .. 16u + 15 copy unit u
@@ -139,7 +147,10 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
       lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + blk_of(i) * 1024);
-    if (sa_wave) {
+    if constexpr (SAR) {
+      if ((kb & 3) == 0 && sa_wave)
+        lds_dma16(sa_src + sa_step * kb, smem + C::OFF_SAR + ((kb >> 2) & 1) * C::SAR_SLOT + wave * 1024);
+    } else if (sa_wave) {
       if constexpr (SA_X4)
         lds_dma16(sa_src + sa_step * kb, st + C::A + C::B);
       else
@@ -160,7 +171,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   for (int kb = 0; kb < kbs; ++kb) {
     // outstanding after stage kb: this wave's loads of stage kb + 1
     if (kb + 1 < kbs) {
-      const int extra = (sa_wave ? 1 : 0) + ((((kb + 1) & 3) == 0 && sw_wave) ? 1 : 0);
+      const bool ring_next = ((kb + 1) & 3) == 0;  // stage kb + 1 also fills the scale rings
+      const int extra = ((SAR ? ring_next : true) && sa_wave ? 1 : 0) + (ring_next && sw_wave ? 1 : 0);
       if (extra == 0) {
         QG_WAIT_VMCNT(C::AB_LOADS);
       } else if (extra == 1) {
@@ -192,7 +204,10 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
       const u32x4 hi = *(const u32x4 *)(ap + 16 * ((4 + q) ^ (row & 7)));
       af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                  (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      asc = st[C::A + C::B + 4 * row + q];
+      if constexpr (SAR)
+        asc = smem[C::OFF_SAR + ((kb >> 2) & 1) * C::SAR_SLOT + 16 * row + 4 * (kb & 3) + q];
+      else
+        asc = st[C::A + C::B + 4 * row + q];
     };
     i32x8 af[2];
     int asc[2];
@@ -265,32 +280,55 @@ uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) {
   return (uint64_t)((m + 255) & ~(int64_t)255) * (uint64_t)k_blocks * 4;
 }
 
-template <int BM, int BN, int WM, int WN, bool MOE>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR>
 static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
-  using C = MxCfg<BM, BN, WM, WN>;
+  using C = MxCfg<BM, BN, WM, WN, SAR>;
   static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MB, C::NB>(), "epilogue LDS");
   const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
   const int64_t n_tiles_wg = (a.n_tiles + C::NBLK - 1) / C::NBLK;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  hipError_t e = hipFuncSetAttribute((const void *)mx_tiled_kernel<BM, BN, WM, WN, MOE>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mx_tiled_kernel<BM, BN, WM, WN, MOE>), dim3((unsigned)(per_xcd * kXcds)),
-                     dim3(C::THREADS), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::THREADS), lds, s, a);
   return hipGetLastError();
+}
+
+template <bool SAR>
+static hipError_t launch_mx_shape(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
+                                  hipStream_t s) {
+  if (waves == 8) {
+    if (moe && bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, SAR>(a, tiles_cap, s);
+    if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true, SAR>(a, tiles_cap, s);
+    if (bm == 256) {
+      if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false, SAR>(a, 0, s);
+      if (bn == 224) return launch_mx_tiled_bm<256, 224, 4, 2, false, SAR>(a, 0, s);
+      return launch_mx_tiled_bm<256, 256, 4, 2, false, SAR>(a, 0, s);
+    }
+    if (bn == 192) return launch_mx_tiled_bm<128, 192, 4, 2, false, SAR>(a, 0, s);
+    if (bn == 224) return launch_mx_tiled_bm<128, 224, 4, 2, false, SAR>(a, 0, s);
+    return launch_mx_tiled_bm<128, 256, 4, 2, false, SAR>(a, 0, s);
+  }
+  if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 2, 2, true, SAR>(a, tiles_cap, s);
+  return bm == 256 ? launch_mx_tiled_bm<256, 256, 2, 2, false, SAR>(a, 0, s)
+                   : launch_mx_tiled_bm<128, 256, 2, 2, false, SAR>(a, 0, s);
 }
 
 // Dense: bm-row tiles (128 or 256) of bn columns (192, 224 or 256 with 8
 // waves; 256 with 4).  MoE: the tile list a.tiles (capacity tiles_cap) of
 // kMoeTileRows x 256 tiles, or (bm = 64, 8 waves) 64 x 128 small tiles, one
-// wave per 16 columns and all rows, for experts with few rows.  waves: 4 (2 x 2, one per SIMD) or 8 (4 x 2, two
-// per SIMD).
+// wave per 16 columns and all rows, for experts with few rows.  The
+// activation scales go through the SA ring when K % 512 == 0 and they are
+// 16-byte aligned; otherwise dense launches first regroup them by K step into
+// ws and MoE launches copy 4 bytes per row and step.
 hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
                            void *ws, hipStream_t s) {
   if (a_in.k % 128 != 0) return hipErrorInvalidValue;
   GemmArgs a = a_in;
+  const bool sar = a.k % 512 == 0 && ((uintptr_t)a.x_scales & 15) == 0;
+  if (sar) return launch_mx_shape<true>(a, bm, bn, moe, tiles_cap, waves, s);
   if (!moe) {
     if (!ws) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((a.m + 15) / 16), (unsigned)((a.k_blocks + 63) / 64)),
@@ -300,21 +338,7 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
     if (e != hipSuccess) return e;
     a.x_scales_t = (const uint32_t *)ws;
   }
-  if (waves == 8) {
-    if (moe && bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true>(a, tiles_cap, s);
-    if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true>(a, tiles_cap, s);
-    if (bm == 256) {
-      if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false>(a, 0, s);
-      if (bn == 224) return launch_mx_tiled_bm<256, 224, 4, 2, false>(a, 0, s);
-      return launch_mx_tiled_bm<256, 256, 4, 2, false>(a, 0, s);
-    }
-    if (bn == 192) return launch_mx_tiled_bm<128, 192, 4, 2, false>(a, 0, s);
-    if (bn == 224) return launch_mx_tiled_bm<128, 224, 4, 2, false>(a, 0, s);
-    return launch_mx_tiled_bm<128, 256, 4, 2, false>(a, 0, s);
-  }
-  if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 2, 2, true>(a, tiles_cap, s);
-  return bm == 256 ? launch_mx_tiled_bm<256, 256, 2, 2, false>(a, 0, s)
-                   : launch_mx_tiled_bm<128, 256, 2, 2, false>(a, 0, s);
+  return launch_mx_shape<false>(a, bm, bn, moe, tiles_cap, waves, s);
 }
 
 }  // namespace qg

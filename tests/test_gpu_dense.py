@@ -177,6 +177,27 @@ def test_mx_tiled_large_m_ragged(monkeypatch, m, n, k, bn):
     _check(layer, Acts(True, m, k, seed=m), m)
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 200, 1024), (256, 448, 4096)])
+def test_mx_tiled_unaligned_activation_scales(m, n, k):
+    """K % 512 == 0 with the activation scales at a 4-byte (not 16-byte)
+    aligned address: the tiled kernel falls back from its scale ring to the
+    scales regrouped by K step.  Checked against the oracle, and against the
+    same call on aligned scales bit for bit."""
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=k + n)
+    acts = Acts(True, m, k, seed=m + 5)
+    assert "mx_tiled" in qg.describe_dispatch(layer.w, m)
+    y_al = run_gemm(layer, acts, m, qg.O_F32)
+    buf = torch.zeros(acts.xs.numel() + 16, dtype=torch.uint8, device="cuda")
+    view = buf[4:4 + acts.xs.numel()].view(acts.xs.shape)
+    view.copy_(acts.xs)
+    assert view.data_ptr() % 16 == 4
+    acts.xs = view
+    y_un = run_gemm(layer, acts, m, qg.O_F32)
+    assert torch.equal(y_al, y_un)
+    e = err(y_un, oracle.gemm(acts.xdq, layer.wdq()))
+    assert e <= tol_f32(True), e
+
+
 def test_mx_tiled_identity_rows_exact():
     n, k, m = 64, 640, 256
     layer = Layer(qg.W_MXFP4, n, k, 32, seed=21)

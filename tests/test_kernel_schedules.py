@@ -151,22 +151,25 @@ def test_mx_tiled_waits_cover_each_stage():
     until only this wave's loads of stage kb + 1 are outstanding.  Replayed
     per wave kind: every load of stage kb (and of the scale group of step kb)
     has retired at the wait of step kb."""
-    for ab in (6, 5, 4, 12):
-        for sa_wave in (True, False):
-            for sw_wave in (True, False):
-                def stage(kb):
-                    return [("AB", kb)] * ab + ([("SA", kb)] if sa_wave else []) + \
-                           ([("SW", kb)] if (kb % 4 == 0 and sw_wave) else [])
-                for kbs in range(1, 14):
-                    seq = stage(0) + (stage(1) if kbs > 1 else [])
-                    for kb in range(kbs):
-                        if kb + 1 < kbs:
-                            w = ab + (1 if sa_wave else 0) + (1 if ((kb + 1) % 4 == 0 and sw_wave) else 0)
-                        else:
-                            w = 0
-                        assert w <= 63
-                        outstanding = seq[len(seq) - w:] if w else []
-                        assert all(t[1] != kb for t in outstanding), (ab, sa_wave, sw_wave, kbs, kb)
-                        assert all(t[1] != kb - kb % 4 or t[0] != "SW" for t in outstanding)
-                        if kb + 2 < kbs:
-                            seq += stage(kb + 2)
+    # sar: the activation scales also travel in a ring filled every fourth step
+    for ab, sa_wave, sw_wave, sar in itertools.product((6, 5, 4, 12), (True, False), (True, False),
+                                                       (False, True)):
+        def stage(kb):
+            return [("AB", kb)] * ab + ([("SA", kb)] if (sa_wave and (kb % 4 == 0 or not sar)) else []) + \
+                   ([("SW", kb)] if (kb % 4 == 0 and sw_wave) else [])
+        for kbs in range(1, 14):
+            seq = stage(0) + (stage(1) if kbs > 1 else [])
+            for kb in range(kbs):
+                if kb + 1 < kbs:
+                    ring_next = (kb + 1) % 4 == 0
+                    w = ab + (1 if (sa_wave and (ring_next or not sar)) else 0) + \
+                        (1 if (ring_next and sw_wave) else 0)
+                else:
+                    w = 0
+                assert w <= 63
+                outstanding = seq[len(seq) - w:] if w else []
+                assert all(t[1] != kb for t in outstanding), (ab, sa_wave, sw_wave, sar, kbs, kb)
+                # the ring slots of step kb were filled with stage kb - kb % 4
+                assert all(t[1] != kb - kb % 4 or t[0] not in ("SW", "SA") for t in outstanding)
+                if kb + 2 < kbs:
+                    seq += stage(kb + 2)
