@@ -18,8 +18,10 @@ launch duration, from HIP events around a run of back-to-back launches of that
 kernel alone on the launch stream.
 
 Unless --quick, the line also carries the other configurations ("extra"):
-INT3 and M = 4 / 16 decode, the W4A8 MXFP4 x MXFP8 GEMM at M = 4096, and the
-MoE grouped configurations (gate_up + down latency, the routing sort apart).
+INT3 and M = 4 / 16 decode, the W4A8 MXFP4 x MXFP8 GEMM at M = 4096, the
+activation-side kernels (bf16 -> MXFP8 quantization, the W4A8 GEMM fed from
+bf16, the MoE SiLU-gated product and top-k combine), and the MoE grouped
+configurations (gate_up + down latency, the routing sort apart).
 MoE weights are random bytes written straight into the packed layout on the
 device (uniform codes, |N(0, 0.02)| bf16 or e8m0 scales near 2^-7): the kernels
 read the same bytes a preprocessed checkpoint would give, and multi-GB expert
@@ -340,6 +342,78 @@ def bench_large_m(qg, synth, torch):
     return extra
 
 
+def bench_act(qg, synth, torch):
+    """Activation-side kernels at the hot path's shapes (HBM-bound; algorithmic
+    bytes read + written per call / time), and the W4A8 GEMM fed from bf16
+    activations (quantize + GEMM).  Inputs rotate over copies totalling more
+    than twice the MALL so each call reads from HBM."""
+    extra = {}
+    stream = torch.cuda.current_stream().cuda_stream
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(99)
+
+    def copies_for(nbytes):
+        return int(min(16, max(1, -(-2 * MALL_BYTES // nbytes))))
+
+    def record(name, t, nbytes, **kw):
+        gbs = nbytes / (t * 1e-3) / 1e9
+        extra[name] = {"us": round(t * 1e3, 2), "GBs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                       "bytes": int(nbytes), **kw}
+        print(f"[bench] {name}: {extra[name]}", file=sys.stderr, flush=True)
+
+    # bf16 -> MXFP8, M = 4096, K = 4096 (the W4A8 GEMM's activations)
+    m, k = 4096, 4096
+    nc = copies_for(m * k * 2)
+    xs = [torch.randn((m, k), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(nc)]
+    q = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((m, k // 32), dtype=torch.uint8, device="cuda")
+    t = timed(torch, lambda i: qg.quantize_mxfp8(xs[i % nc], m, k, k, q, k, qs, stream), 100, 10)
+    record("quantize_mxfp8_M4096_K4096", t, m * k * 3 + m * k // 32)
+    # W4A8 from bf16 activations: quantize, then the MXFP4 x MXFP8 GEMM
+    n = 14336
+    L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, k, 32, seed=50, copies=2)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    wsb = qg.gemm_workspace_size(L.ws[0], m)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def qgemm(i):
+        qg.quantize_mxfp8(xs[i % nc], m, k, k, q, k, qs, stream)
+        qg.gemm(L.ws[i % 2], q, qs, m, k, y, qg.O_BF16, n, ws, wsb, stream)
+    t = timed(torch, qgemm, 50, 10)
+    fl = 2.0 * m * n * k
+    extra[f"w4a8_from_bf16_M{m}_N{n}_K{k}"] = {
+        "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+        "fp8_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+        "steps": "qg_quantize_mxfp8 + qg_gemm"}
+    print(f"[bench] w4a8 from bf16: {extra[f'w4a8_from_bf16_M{m}_N{n}_K{k}']}", file=sys.stderr, flush=True)
+    del L, xs
+    # SiLU-gated product between gate_up and down at T = 4096, top-8 (32768 pairs)
+    p = 4096 * 8
+    for inter, mx in ((2048, False), (640, True)):
+        nc = copies_for(p * 2 * inter * 2)
+        gus = [torch.randn((p, 2 * inter), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(nc)]
+        h = torch.empty((p, inter), dtype=torch.uint8 if mx else torch.bfloat16, device="cuda")
+        hs = torch.empty((p, inter // 32), dtype=torch.uint8, device="cuda") if mx else None
+        ht = qg.A_MXFP8 if mx else qg.A_BF16
+        t = timed(torch, lambda i: qg.silu_mul(gus[i % nc], qg.O_BF16, p, inter, 2 * inter, h, ht, inter, hs,
+                                               stream), 50, 5)
+        out_bytes = p * inter + p * inter // 32 if mx else p * inter * 2
+        record(f"silu_mul_P{p}_I{inter}_{'mxfp8' if mx else 'bf16'}", t, p * 2 * inter * 2 + out_bytes)
+        del gus, h, hs
+    # weighted top-8 combine of the down projection's rows, T = 4096, N = 7168
+    tokens, topk, n = 4096, 8, 7168
+    nc = copies_for(tokens * topk * n * 2)
+    ys = [torch.randn((tokens * topk, n), device="cuda", generator=gen).to(torch.bfloat16) for _ in range(nc)]
+    w = torch.rand((tokens, topk), device="cuda", generator=gen)
+    o = torch.empty((tokens, n), dtype=torch.bfloat16, device="cuda")
+    t = timed(torch, lambda i: qg.moe_combine(ys[i % nc], qg.O_BF16, n, w, tokens, topk, n, None, o, qg.O_BF16, n,
+                                              stream), 50, 5)
+    record(f"moe_combine_T{tokens}_top{topk}_N{n}", t, tokens * topk * (n * 2 + 4) + tokens * n * 2)
+    del ys
+    torch.cuda.empty_cache()
+    return extra
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +423,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--large-m", action="store_true",
                     help="only the M=4096 dense GEMMs (for profiling the tiled kernels)")
+    ap.add_argument("--act", action="store_true",
+                    help="only the activation-side kernels (quantizer, SiLU-gated product, combine)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only run the copy calibration + decode kernel for rocprofv3 counter passes")
     args = ap.parse_args()
@@ -371,6 +447,9 @@ def main():
         return
     if args.large_m:
         print(json.dumps(bench_large_m(qg, synth, torch)), flush=True)
+        return
+    if args.act:
+        print(json.dumps(bench_act(qg, synth, torch)), flush=True)
         return
 
     shapes = [(14336, 4096), (4096, 14336)]
@@ -435,6 +514,7 @@ def main():
                         "dispatch": qg.describe_dispatch(L.ws[0], mm)}
             print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
         extra.update(bench_large_m(qg, synth, torch))
+        extra["activation"] = bench_act(qg, synth, torch)
         moe = {}
         for tokens in (64, 4096):
             moe[f"w4a16_E256_top8_T{tokens}"] = bench_moe(

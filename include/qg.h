@@ -207,6 +207,59 @@ qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, i
                       int64_t num_tokens, int32_t topk, void *y, int32_t otype, int32_t y_rows,
                       void *ws, uint64_t ws_bytes, hipStream_t stream);
 
+/* Activation quantization bf16 -> MXFP8 (announcement, section "Choosing the
+ * activation type": a deployment may run a layer with MXFP8 activations on a
+ * bf16 model, e.g. the MoE layers, so activations are quantized at run time
+ * before the W4A8 GEMM).  Per row, per block of 32 values along K, following
+ * the OCP Microscaling Formats v1.0 conversion: scale X = 2^(floor(log2
+ * max|v|) - 8) clamped to 2^-127 .. 2^127 (X = 1 for an all-zero block), stored
+ * as the e8m0 code log2(X) + 127; element = v / X rounded to the nearest e4m3
+ * value, ties to the even code, magnitudes beyond 448 saturated to 448, sign
+ * kept (a negative value that rounds to zero gives 0x80).  The result is
+ * exact (no fp32 rounding is involved for bf16 inputs).
+ *   x        device, bf16 [rows][ldx], 16-B aligned, ldx >= k, ldx % 8 == 0.
+ *   q        device, e4m3 bytes [rows][ldq], 8-B aligned, ldq >= k, ldq % 8 == 0.
+ *   q_scales device, e8m0 bytes [rows][k/32] (row stride k/32, the x_scales
+ *            layout of qg_gemm / qg_moe_gemm), any alignment.
+ * k % 32 != 0 or ld too small: QG_ERR_SHAPE.  rows == 0 or k == 0: no-op.
+ * NaN / Inf inputs give unspecified codes.  Asynchronous on `stream`. */
+qg_status qg_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q,
+                            int64_t ldq, void *q_scales, hipStream_t stream);
+
+/* SiLU-gated product of a fused gate/up projection (MoE output stage between
+ * gate_up and down; announcement, section "Shared CUDA components": scaling
+ * and bias work belongs to the output stage):
+ *   h[r][j] = silu(gu[r][j]) * gu[r][inter + j],  silu(v) = v / (1 + e^-v),
+ * for j < inter, computed in fp32 and rounded to bf16 (nearest-even).  With
+ * h_type QG_A_MXFP8 those bf16 values are then quantized exactly as
+ * qg_quantize_mxfp8 does, ready for an MXFP8 down projection.
+ *   gu       device, [rows][ldgu] of gu_type (QG_O_BF16 or QG_O_F32, i.e. the
+ *            gate_up GEMM's output type), 16-B aligned, ldgu >= 2*inter,
+ *            rows 16-B aligned (ldgu % 8 for bf16, % 4 for fp32).
+ *   h        device, [rows][ldh]: bf16 (16-B aligned, ldh % 8 == 0) or e4m3
+ *            bytes (8-B aligned, ldh % 8 == 0), ldh >= inter.
+ *   h_scales device, e8m0 [rows][inter/32] (QG_A_MXFP8 only, else ignored).
+ * inter % 8 (bf16 output) or % 32 (MXFP8 output) != 0: QG_ERR_SHAPE.
+ * rows == 0 is a no-op.  Asynchronous on `stream`. */
+qg_status qg_silu_mul(const void *gu, int32_t gu_type, int64_t rows, int64_t inter, int64_t ldgu,
+                      void *h, int32_t h_type, int64_t ldh, void *h_scales, hipStream_t stream);
+
+/* Weighted combine of each token's top-k expert rows (MoE output stage):
+ *   out[t][c] = sum_j topk_weights[t][j] * y[t*topk + j][c]  (+ bias[c])
+ * summed in fp32 over j = 0 .. topk-1 in order, then stored as out_type
+ * (bf16 nearest-even, or fp32).  y holds one row per pair p = t*topk + j, i.e.
+ * the QG_ROWS_BY_PAIR output of qg_moe_gemm.
+ *   y            device, [num_tokens*topk][ldy] of y_type (QG_O_BF16 / QG_O_F32),
+ *                16-B aligned rows.
+ *   topk_weights device, fp32 [num_tokens][topk], 4-B aligned.
+ *   bias         device, bf16 [n] (16-B aligned) or NULL.
+ *   out          device, [num_tokens][ldout] of out_type, 16-B aligned rows.
+ * n % 8 != 0 or ld too small: QG_ERR_SHAPE; topk < 1: QG_ERR_INVALID_ARGUMENT.
+ * num_tokens == 0 is a no-op.  out must not overlap y.  Asynchronous. */
+qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, const float *topk_weights,
+                         int64_t num_tokens, int32_t topk, int64_t n, const void *bias, void *out,
+                         int32_t out_type, int64_t ldout, hipStream_t stream);
+
 /* Measurement utilities, used for roofline calibration and cold-cache timing.
  * qg_stream_read reads `bytes` (a multiple of 16; src 16-B aligned, device)
  * with 128-bit loads and folds them into `sink` (device, at least 16 KiB, any

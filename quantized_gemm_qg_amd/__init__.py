@@ -27,7 +27,8 @@ EXPORTS = (
     "qg_packed_size", "qg_repack_host", "qg_preprocess", "qg_weight_bind",
     "qg_gemm_workspace_size", "qg_gemm", "qg_moe_workspace_size", "qg_moe_sort",
     "qg_moe_gemm", "qg_stream_read", "qg_stream_copy", "qg_describe_dispatch",
-    "qg_status_string", "qg_last_hip_error",
+    "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
+    "qg_moe_combine",
 )
 
 
@@ -83,6 +84,9 @@ def _load():
         "qg_describe_dispatch": (I32, [W, I64, ctypes.c_char_p, U64]),
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_last_hip_error": (I32, []),
+        "qg_quantize_mxfp8": (I32, [P, I64, I64, I64, P, I64, P, P]),
+        "qg_silu_mul": (I32, [P, I32, I64, I64, I64, P, I32, I64, P, P]),
+        "qg_moe_combine": (I32, [P, I32, I64, P, I64, I32, I64, P, P, I32, I64, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -220,3 +224,23 @@ def stream_read(src, nbytes: int, sink, stream=None) -> None:
 
 def stream_copy(dst, src, nbytes: int, stream=None) -> None:
     _check(_lib.qg_stream_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "qg_stream_copy")
+
+
+def quantize_mxfp8(x, rows: int, k: int, ldx: int, q, ldq: int, q_scales, stream=None) -> None:
+    """bf16 x [rows][ldx] -> e4m3 q [rows][ldq] + e8m0 q_scales [rows][k/32]."""
+    _check(_lib.qg_quantize_mxfp8(_ptr(x), rows, k, ldx, _ptr(q), ldq, _ptr(q_scales), _stream(stream)),
+           "qg_quantize_mxfp8")
+
+
+def silu_mul(gu, gu_type: int, rows: int, inter: int, ldgu: int, h, h_type: int, ldh: int,
+             h_scales=None, stream=None) -> None:
+    """h = silu(gu[:, :inter]) * gu[:, inter:2*inter] as bf16 (h_type A_BF16) or MXFP8 (A_MXFP8)."""
+    _check(_lib.qg_silu_mul(_ptr(gu), gu_type, rows, inter, ldgu, _ptr(h), h_type, ldh, _ptr(h_scales),
+                            _stream(stream)), "qg_silu_mul")
+
+
+def moe_combine(y, y_type: int, ldy: int, topk_weights, num_tokens: int, topk: int, n: int, bias, out,
+                out_type: int, ldout: int, stream=None) -> None:
+    """out[t] = sum_j topk_weights[t, j] * y[t*topk + j] (+ bias)."""
+    _check(_lib.qg_moe_combine(_ptr(y), y_type, ldy, _ptr(topk_weights), num_tokens, topk, n, _ptr(bias),
+                               _ptr(out), out_type, ldout, _stream(stream)), "qg_moe_combine")

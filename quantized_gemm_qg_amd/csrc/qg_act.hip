@@ -1,0 +1,245 @@
+// Activation-side kernels around the GEMMs: bf16 -> MXFP8 quantization of the
+// activations and the MoE output stage (SiLU-gated product of the fused
+// gate/up projection, weighted combine of a token's top-k expert rows).
+//
+// The announcement's section "Choosing the activation type" lets a deployment
+// run MoE layers with MXFP8 activations on a checkpoint whose activations are
+// bf16, so the activations are quantized at run time before the W4A8 GEMM;
+// its section "Shared CUDA components" puts scaling and bias additions in the
+// output stage.  Every kernel here is a single streaming pass bound by HBM:
+// one lane owns 8 consecutive values along the row (a 16-byte bf16 load), four
+// lanes own one 32-value MX block, and the block's largest magnitude is
+// combined across the four lanes with two DPP quad permutations.
+//
+// MXFP8 conversion (OCP Microscaling Formats v1.0, section 6.3): the block's
+// scale is X = 2^(floor(log2 max|v|) - 8), clamped to 2^-127 .. 2^127, X = 1 for
+// an all-zero block; each element is v / X rounded to the nearest e4m3 value,
+// ties to the even code, saturating at 448, keeping v's sign.  The inputs are
+// bf16, so floor(log2 max|v|) is the exponent field of the largest magnitude
+// pattern and v / X only moves the binary point: the rounding below works on
+// the bf16 bit fields with integer operations and is exact.
+#include <hip/hip_runtime.h>
+
+#include "qg_device.h"
+#include "qg_internal.h"
+
+namespace qg {
+
+namespace {
+
+// Scale exponent of a block whose largest magnitude has the bf16 pattern amax
+// (sign cleared): floor(log2) - 8, clamped at -127; 0 for an all-zero block.
+__device__ __forceinline__ int mx_block_exp(uint32_t amax) {
+  if (amax == 0) return 0;
+  return max((int)(amax >> 7) - 135, -127);  // subnormal maxima give -127 too
+}
+
+// e4m3 code of the bf16 pattern b times 2^-e: nearest value, ties to even,
+// saturating at 448 (0x7E), sign kept.
+__device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t b, int e) {
+  const uint32_t sign = (b >> 8) & 0x80u;
+  const uint32_t a = b & 0x7FFFu;
+  int eb = (int)(a >> 7);
+  uint32_t sig = a & 0x7Fu;  // significand, leading one at bit 7 once normalised
+  if (eb == 0) {
+    if (sig == 0) return sign;
+    eb = 1;  // subnormal: 0.m * 2^-126
+  } else {
+    sig |= 0x80u;
+  }
+  const int lz = __builtin_clz(sig) - 24;  // sig in [1, 255]
+  sig <<= lz;
+  int es = eb - lz - 127 - e;  // value = sig / 128 * 2^es
+  if (es >= -6) {
+    // normal e4m3: keep 4 significant bits (1.mmm)
+    uint32_t q = sig >> 4;
+    const uint32_t rem = sig & 15u;
+    q += (rem > 8u || (rem == 8u && (q & 1u))) ? 1u : 0u;
+    if (q == 16u) {
+      q = 8u;
+      ++es;
+    }
+    if (es > 8 || (es == 8 && q > 14u)) return sign | 0x7Eu;  // beyond 448
+    return sign | ((uint32_t)(es + 7) << 3) | (q & 7u);
+  }
+  // subnormal e4m3: multiples of 2^-9; value = sig * 2^(es + 2) of them
+  const int sh = -(es + 2);  // >= 5
+  if (sh > 9) return sign;   // below a quarter of a step
+  uint32_t q = sig >> sh;
+  const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
+  return sign | q;  // q == 8 is the smallest normal, code 0x08
+}
+
+// largest value over the lane's quad (lanes 4i .. 4i + 3)
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return v;
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Quantizes the 8 bf16 values of this lane (4 words, two values each, low
+// half first) as part of its quad's 32-value block: writes the 8 e4m3 codes
+// to q8 and, from the quad's first lane, the scale code to *scale.
+__device__ __forceinline__ void mx_store8(const uint32_t (&w)[4], uint8_t *q8, uint8_t *scale, bool first) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  amax = quad_max(amax);
+  const int e = mx_block_exp(amax);
+  uint32_t c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    c[h] = e4m3_of_bf16(w[2 * h] & 0xFFFFu, e) | (e4m3_of_bf16(w[2 * h] >> 16, e) << 8) |
+           (e4m3_of_bf16(w[2 * h + 1] & 0xFFFFu, e) << 16) | (e4m3_of_bf16(w[2 * h + 1] >> 16, e) << 24);
+  *(uint2 *)q8 = uint2{c[0], c[1]};
+  if (first) *scale = (uint8_t)(e + 127);
+}
+
+// 8 consecutive values of a bf16 or fp32 row as fp32
+__device__ __forceinline__ void load8_f32(const void *row, int64_t c8, bool f32, float (&v)[8]) {
+  if (f32) {
+    const u32x4 a = *((const u32x4 *)row + 2 * c8), b = *((const u32x4 *)row + 2 * c8 + 1);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  } else {
+    const u32x4 a = *((const u32x4 *)row + c8);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+}
+
+}  // namespace
+
+// bf16 rows [rows][ldx] -> e4m3 rows [rows][ldq] + e8m0 [rows][k / 32].
+// Unit u = (row, 8-value chunk c8); u runs over rows * k / 8 (a multiple of 4,
+// so a quad's units are all in range or all out of it).
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t *x, int64_t ldx, uint8_t *q,
+                                                             int64_t ldq, uint8_t *qs, int64_t k8,
+                                                             int64_t units) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool first = (threadIdx.x & 3) == 0;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
+    const int64_t row = u / k8, c8 = u - row * k8;
+    const u32x4 v = *(const u32x4 *)(x + row * ldx + 8 * c8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    mx_store8(w, q + row * ldq + 8 * c8, qs + row * (k8 >> 2) + (c8 >> 2), first);
+  }
+}
+
+// h[r][j] = silu(gu[r][j]) * gu[r][inter + j] for j < inter, in fp32, rounded
+// to bf16; MX: the bf16 values are then quantized to MXFP8 as above.
+template <bool MX>
+__global__ __launch_bounds__(256) void silu_mul_kernel(const void *gu, bool gu_f32, int64_t ldgu, int64_t inter,
+                                                       void *h, int64_t ldh, uint8_t *hs, int64_t i8,
+                                                       int64_t units) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool first = (threadIdx.x & 3) == 0;
+  const int esz = gu_f32 ? 4 : 2;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
+    const int64_t row = u / i8, c8 = u - row * i8;
+    const uint8_t *rp = (const uint8_t *)gu + row * ldgu * esz;
+    float g[8], up[8];
+    load8_f32(rp, c8, gu_f32, g);
+    load8_f32(rp + inter * esz, c8, gu_f32, up);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float h0 = g[2 * i] / (1.f + __expf(-g[2 * i])) * up[2 * i];
+      const float h1 = g[2 * i + 1] / (1.f + __expf(-g[2 * i + 1])) * up[2 * i + 1];
+      w[i] = f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
+    }
+    if constexpr (MX) {
+      mx_store8(w, (uint8_t *)h + row * ldh + 8 * c8, hs + row * (i8 >> 2) + (c8 >> 2), first);
+    } else {
+      *((u32x4 *)((uint16_t *)h + row * ldh) + c8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+// out[t][c] = sum_j wts[t][j] * y[t * topk + j][c] (+ bias[c]) in fp32, j in
+// order, stored as bf16 (RNE) or fp32.
+__global__ __launch_bounds__(256) void moe_combine_kernel(const void *y, bool y_f32, int64_t ldy, const float *wts,
+                                                          int topk, const uint16_t *bias, void *out, bool out_f32,
+                                                          int64_t ldo, int64_t n8, int64_t units) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int esz = y_f32 ? 4 : 2;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
+    const int64_t t = u / n8, c8 = u - t * n8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < topk; ++j) {
+      const float wj = wts[t * topk + j];
+      float v[8];
+      load8_f32((const uint8_t *)y + (t * topk + j) * ldy * esz, c8, y_f32, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+    }
+    if (bias) {
+      float b[8];
+      load8_f32(bias, c8, false, b);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += b[i];
+    }
+    if (out_f32) {
+      u32x4 *o = (u32x4 *)((float *)out + t * ldo) + 2 * c8;
+      o[0] = u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+      o[1] = u32x4{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]), __float_as_uint(acc[7])};
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_rne(acc[2 * i]) | (f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+      *((u32x4 *)((uint16_t *)out + t * ldo) + c8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+}
+
+static unsigned stream_grid(int64_t units) {
+  // one unit per lane per pass; at most 8 waves' worth of workgroups per CU
+  const int64_t want = (units + 255) / 256;
+  return (unsigned)std::min<int64_t>(std::max<int64_t>(want, 1), 256 * 32);
+}
+
+hipError_t launch_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
+                                 void *qs, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3(stream_grid(units)), dim3(256), 0, s, (const uint16_t *)x, ldx,
+                     (uint8_t *)q, ldq, (uint8_t *)qs, k / 8, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_mul(const void *gu, bool gu_f32, int64_t rows, int64_t inter, int64_t ldgu, bool mx,
+                           void *h, int64_t ldh, void *hs, hipStream_t s) {
+  const int64_t units = rows * (inter / 8);
+  if (units == 0) return hipSuccess;
+  if (mx)
+    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(stream_grid(units)), dim3(256), 0, s, gu, gu_f32, ldgu, inter,
+                       h, ldh, (uint8_t *)hs, inter / 8, units);
+  else
+    hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(stream_grid(units)), dim3(256), 0, s, gu, gu_f32, ldgu, inter,
+                       h, ldh, (uint8_t *)hs, inter / 8, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_combine(const void *y, bool y_f32, int64_t ldy, const float *wts, int64_t tokens, int topk,
+                              int64_t n, const void *bias, void *out, bool out_f32, int64_t ldo, hipStream_t s) {
+  const int64_t units = tokens * (n / 8);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(stream_grid(units)), dim3(256), 0, s, y, y_f32, ldy, wts, topk,
+                     (const uint16_t *)bias, out, out_f32, ldo, n / 8, units);
+  return hipGetLastError();
+}
+
+}  // namespace qg

@@ -688,6 +688,49 @@ extern "C" qg_status qg_stream_copy(void *dst, const void *src, uint64_t bytes,
   return hip_status(launch_stream_copy(dst, src, bytes, stream));
 }
 
+static bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+extern "C" qg_status qg_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q,
+                                       int64_t ldq, void *q_scales, hipStream_t stream) {
+  if (rows < 0 || k < 0) return QG_ERR_INVALID_ARGUMENT;
+  if (k % 32 != 0 || ldx < k || ldq < k) return QG_ERR_SHAPE;
+  if (rows == 0 || k == 0) return QG_OK;
+  if (!x || !q || !q_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || ldx % 8 != 0 || !aligned(q, 8) || ldq % 8 != 0) return QG_ERR_ALIGNMENT;
+  return hip_status(launch_quantize_mxfp8(x, rows, k, ldx, q, ldq, q_scales, stream));
+}
+
+extern "C" qg_status qg_silu_mul(const void *gu, int32_t gu_type, int64_t rows, int64_t inter, int64_t ldgu,
+                                 void *h, int32_t h_type, int64_t ldh, void *h_scales, hipStream_t stream) {
+  if (rows < 0 || inter < 0) return QG_ERR_INVALID_ARGUMENT;
+  if ((gu_type != QG_O_BF16 && gu_type != QG_O_F32) || (h_type != QG_A_BF16 && h_type != QG_A_MXFP8))
+    return QG_ERR_INVALID_ARGUMENT;
+  const bool mx = h_type == QG_A_MXFP8;
+  if (inter % (mx ? 32 : 8) != 0 || ldgu < 2 * inter || ldh < inter) return QG_ERR_SHAPE;
+  if (rows == 0 || inter == 0) return QG_OK;
+  if (!gu || !h || (mx && !h_scales)) return QG_ERR_INVALID_ARGUMENT;
+  const bool f32 = gu_type == QG_O_F32;
+  if (!aligned16(gu) || ldgu % (f32 ? 4 : 8) != 0) return QG_ERR_ALIGNMENT;
+  if (mx ? (!aligned(h, 8) || ldh % 8 != 0) : (!aligned16(h) || ldh % 8 != 0)) return QG_ERR_ALIGNMENT;
+  return hip_status(launch_silu_mul(gu, f32, rows, inter, ldgu, mx, h, ldh, h_scales, stream));
+}
+
+extern "C" qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, const float *topk_weights,
+                                    int64_t num_tokens, int32_t topk, int64_t n, const void *bias, void *out,
+                                    int32_t out_type, int64_t ldout, hipStream_t stream) {
+  if (num_tokens < 0 || n < 0 || topk < 1) return QG_ERR_INVALID_ARGUMENT;
+  if ((y_type != QG_O_BF16 && y_type != QG_O_F32) || (out_type != QG_O_BF16 && out_type != QG_O_F32))
+    return QG_ERR_INVALID_ARGUMENT;
+  if (n % 8 != 0 || ldy < n || ldout < n) return QG_ERR_SHAPE;
+  if (num_tokens == 0 || n == 0) return QG_OK;
+  if (!y || !topk_weights || !out) return QG_ERR_INVALID_ARGUMENT;
+  const bool yf = y_type == QG_O_F32, of = out_type == QG_O_F32;
+  if (!aligned16(y) || ldy % (yf ? 4 : 8) != 0 || !aligned16(out) || ldout % (of ? 4 : 8) != 0 ||
+      !aligned(topk_weights, 4) || (bias && !aligned16(bias)))
+    return QG_ERR_ALIGNMENT;
+  return hip_status(launch_moe_combine(y, yf, ldy, topk_weights, num_tokens, topk, n, bias, out, of, ldout, stream));
+}
+
 extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf,
                                           uint64_t buf_bytes) {
   Layout L;

@@ -182,6 +182,14 @@ hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min
                             int32_t *tiles, hipStream_t s);
 hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
+// Activation-side kernels (qg_act.hip): bf16 -> MXFP8, SiLU-gated product,
+// weighted top-k combine.  Shapes and alignment are validated by the callers.
+hipError_t launch_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
+                                 void *qs, hipStream_t s);
+hipError_t launch_silu_mul(const void *gu, bool gu_f32, int64_t rows, int64_t inter, int64_t ldgu, bool mx,
+                           void *h, int64_t ldh, void *hs, hipStream_t s);
+hipError_t launch_moe_combine(const void *y, bool y_f32, int64_t ldy, const float *wts, int64_t tokens, int topk,
+                              int64_t n, const void *bias, void *out, bool out_f32, int64_t ldo, hipStream_t s);
 hipError_t launch_moe_sort(const int32_t *ids, int64_t pairs, int32_t experts,
                            int32_t *sorted, int32_t *offsets, int32_t *ws_counts,
                            hipStream_t s);

@@ -312,3 +312,61 @@ def test_library_has_no_undefined_internal_symbols():
     out = subprocess.run([nm, "-D", "--undefined-only", qg.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     assert not [l for l in out.splitlines() if "_ZN2qg" in l], out
+
+
+def test_activation_entry_points_validate_before_launch():
+    S = 0
+    # no-ops
+    qg.quantize_mxfp8(None, 0, 64, 64, None, 64, None, stream=S)
+    qg.silu_mul(None, qg.O_BF16, 0, 64, 128, None, qg.A_BF16, 64, stream=S)
+    qg.moe_combine(None, qg.O_BF16, 64, None, 0, 2, 64, None, None, qg.O_BF16, 64, stream=S)
+    F = FAKE_DEV
+    q_cases = [
+        (dict(k=48), qg.QG_ERR_SHAPE),                  # K % 32
+        (dict(ldx=32), qg.QG_ERR_SHAPE),                # ldx < K
+        (dict(ldq=32), qg.QG_ERR_SHAPE),
+        (dict(x=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(qs=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(x=F + 8), qg.QG_ERR_ALIGNMENT),
+        (dict(ldx=68), qg.QG_ERR_ALIGNMENT),
+        (dict(q=F + 4), qg.QG_ERR_ALIGNMENT),
+        (dict(rows=-1), qg.QG_ERR_INVALID_ARGUMENT),
+    ]
+    for kw, status in q_cases:
+        a = dict(x=F, rows=4, k=64, ldx=64, q=F, ldq=64, qs=F)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.quantize_mxfp8(a["x"], a["rows"], a["k"], a["ldx"], a["q"], a["ldq"], a["qs"], stream=S)
+        assert e.value.status == status, kw
+    s_cases = [
+        (dict(inter=36), qg.QG_ERR_SHAPE),               # bf16 output needs inter % 8
+        (dict(inter=40, ht=qg.A_MXFP8), qg.QG_ERR_SHAPE),  # MXFP8 output needs inter % 32
+        (dict(ldgu=100), qg.QG_ERR_SHAPE),               # ldgu < 2 inter
+        (dict(gt=5), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(ht=qg.A_MXFP8), qg.QG_ERR_INVALID_ARGUMENT),  # scales missing
+        (dict(gu=F + 4), qg.QG_ERR_ALIGNMENT),
+        (dict(h=F + 8), qg.QG_ERR_ALIGNMENT),
+    ]
+    for kw, status in s_cases:
+        a = dict(gu=F, gt=qg.O_BF16, rows=4, inter=64, ldgu=128, h=F, ht=qg.A_BF16, ldh=64, hs=None)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.silu_mul(a["gu"], a["gt"], a["rows"], a["inter"], a["ldgu"], a["h"], a["ht"], a["ldh"], a["hs"],
+                        stream=S)
+        assert e.value.status == status, kw
+    c_cases = [
+        (dict(n=60), qg.QG_ERR_SHAPE),
+        (dict(topk=0), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(w=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(yt=3), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(bias=F + 2), qg.QG_ERR_ALIGNMENT),
+        (dict(out=F + 8), qg.QG_ERR_ALIGNMENT),
+        (dict(ldout=32), qg.QG_ERR_SHAPE),
+    ]
+    for kw, status in c_cases:
+        a = dict(y=F, yt=qg.O_BF16, ldy=64, w=F, t=4, topk=2, n=64, bias=None, out=F, ot=qg.O_BF16, ldout=64)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.moe_combine(a["y"], a["yt"], a["ldy"], a["w"], a["t"], a["topk"], a["n"], a["bias"], a["out"],
+                           a["ot"], a["ldout"], stream=S)
+        assert e.value.status == status, kw
