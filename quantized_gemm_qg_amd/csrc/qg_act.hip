@@ -16,8 +16,8 @@
 // an all-zero block; each element is v / X rounded to the nearest e4m3 value,
 // ties to the even code, saturating at 448, keeping v's sign.  The inputs are
 // bf16, so floor(log2 max|v|) is the exponent field of the largest magnitude
-// pattern and v / X only moves the binary point: the rounding below works on
-// the bf16 bit fields with integer operations and is exact.
+// and v / X only moves the binary point (exact in fp32); the one rounding is
+// the hardware's fp32 -> e4m3 conversion, nearest-even.
 #include <hip/hip_runtime.h>
 
 #include "qg_device.h"
@@ -27,48 +27,23 @@ namespace qg {
 
 namespace {
 
-// Scale exponent of a block whose largest magnitude has the bf16 pattern amax
-// (sign cleared): floor(log2) - 8, clamped at -127; 0 for an all-zero block.
+// Scale exponent of a block whose largest magnitude has the fp32 pattern amax
+// (a bf16 value widened, sign cleared): floor(log2) - 8, clamped at -127; 0
+// for an all-zero block.
 __device__ __forceinline__ int mx_block_exp(uint32_t amax) {
   if (amax == 0) return 0;
-  return max((int)(amax >> 7) - 135, -127);  // subnormal maxima give -127 too
+  return max((int)(amax >> 23) - 135, -127);  // subnormal maxima give -127 too
 }
 
-// e4m3 code of the bf16 pattern b times 2^-e: nearest value, ties to even,
-// saturating at 448 (0x7E), sign kept.
-__device__ __forceinline__ uint32_t e4m3_of_bf16(uint32_t b, int e) {
-  const uint32_t sign = (b >> 8) & 0x80u;
-  const uint32_t a = b & 0x7FFFu;
-  int eb = (int)(a >> 7);
-  uint32_t sig = a & 0x7Fu;  // significand, leading one at bit 7 once normalised
-  if (eb == 0) {
-    if (sig == 0) return sign;
-    eb = 1;  // subnormal: 0.m * 2^-126
-  } else {
-    sig |= 0x80u;
-  }
-  const int lz = __builtin_clz(sig) - 24;  // sig in [1, 255]
-  sig <<= lz;
-  int es = eb - lz - 127 - e;  // value = sig / 128 * 2^es
-  if (es >= -6) {
-    // normal e4m3: keep 4 significant bits (1.mmm)
-    uint32_t q = sig >> 4;
-    const uint32_t rem = sig & 15u;
-    q += (rem > 8u || (rem == 8u && (q & 1u))) ? 1u : 0u;
-    if (q == 16u) {
-      q = 8u;
-      ++es;
-    }
-    if (es > 8 || (es == 8 && q > 14u)) return sign | 0x7Eu;  // beyond 448
-    return sign | ((uint32_t)(es + 7) << 3) | (q & 7u);
-  }
-  // subnormal e4m3: multiples of 2^-9; value = sig * 2^(es + 2) of them
-  const int sh = -(es + 2);  // >= 5
-  if (sh > 9) return sign;   // below a quarter of a step
-  uint32_t q = sig >> sh;
-  const uint32_t rem = sig & ((1u << sh) - 1u), half = 1u << (sh - 1);
-  q += (rem > half || (rem == half && (q & 1u))) ? 1u : 0u;
-  return sign | q;  // q == 8 is the smallest normal, code 0x08
+// e4m3 codes of two values already divided by the block scale.  The division
+// by a power of two is exact for bf16 inputs (fp32 denormals are kept), the
+// clamp to +-448 gives the saturation (values in (448, 464) round to 448
+// anyway), and v_cvt_pk_fp8_f32 rounds to nearest-even into OCP e4m3; the
+// sign survives, so a negative value that rounds to zero becomes 0x80.
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  a = __builtin_amdgcn_fmed3f(a, -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(b, -448.f, 448.f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
 // largest value over the lane's quad (lanes 4i .. 4i + 3)
@@ -89,18 +64,34 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 // half first) as part of its quad's 32-value block: writes the 8 e4m3 codes
 // to q8 and, from the quad's first lane, the scale code to *scale.
 __device__ __forceinline__ void mx_store8(const uint32_t (&w)[4], uint8_t *q8, uint8_t *scale, bool first) {
-  uint32_t amax = 0;
+  float v[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  amax = quad_max(amax);
-  const int e = mx_block_exp(amax);
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  const int e = mx_block_exp(quad_max(__float_as_uint(m)));
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, e in [-127, 119]
   uint32_t c[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    c[h] = e4m3_of_bf16(w[2 * h] & 0xFFFFu, e) | (e4m3_of_bf16(w[2 * h] >> 16, e) << 8) |
-           (e4m3_of_bf16(w[2 * h + 1] & 0xFFFFu, e) << 16) | (e4m3_of_bf16(w[2 * h + 1] >> 16, e) << 24);
+    c[h] = e4m3_pair(v[4 * h] * inv, v[4 * h + 1] * inv) | (e4m3_pair(v[4 * h + 2] * inv, v[4 * h + 3] * inv) << 16);
   *(uint2 *)q8 = uint2{c[0], c[1]};
   if (first) *scale = (uint8_t)(e + 127);
+}
+
+// (row, chunk) of unit u with `per` chunks per row; 32-bit division whenever
+// the unit count allows (a 64-bit divide is a long instruction sequence)
+__device__ __forceinline__ void split_unit(int64_t u, int64_t per, bool wide, int64_t &row, int64_t &c) {
+  if (wide) {
+    row = u / per;
+  } else {
+    row = (int64_t)((uint32_t)u / (uint32_t)per);
+  }
+  c = u - row * per;
 }
 
 // 8 consecutive values of a bf16 or fp32 row as fp32
@@ -131,8 +122,10 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t *x, 
                                                              int64_t units) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const bool first = (threadIdx.x & 3) == 0;
+  const bool wide = units > 0xFFFFFFFFll;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    const int64_t row = u / k8, c8 = u - row * k8;
+    int64_t row, c8;
+    split_unit(u, k8, wide, row, c8);
     const u32x4 v = *(const u32x4 *)(x + row * ldx + 8 * c8);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     mx_store8(w, q + row * ldq + 8 * c8, qs + row * (k8 >> 2) + (c8 >> 2), first);
@@ -148,8 +141,10 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const void *gu, bool gu_f
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const bool first = (threadIdx.x & 3) == 0;
   const int esz = gu_f32 ? 4 : 2;
+  const bool wide = units > 0xFFFFFFFFll;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    const int64_t row = u / i8, c8 = u - row * i8;
+    int64_t row, c8;
+    split_unit(u, i8, wide, row, c8);
     const uint8_t *rp = (const uint8_t *)gu + row * ldgu * esz;
     float g[8], up[8];
     load8_f32(rp, c8, gu_f32, g);
@@ -176,8 +171,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const void *y, bool y_
                                                           int64_t ldo, int64_t n8, int64_t units) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int esz = y_f32 ? 4 : 2;
+  const bool wide = units > 0xFFFFFFFFll;
   for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    const int64_t t = u / n8, c8 = u - t * n8;
+    int64_t t, c8;
+    split_unit(u, n8, wide, t, c8);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < topk; ++j) {
       const float wj = wts[t * topk + j];
