@@ -513,6 +513,21 @@ def main():
                         "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "dispatch": qg.describe_dispatch(L.ws[0], mm)}
             print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
+        # the batch-invariant compute option at decode sizes (one kernel for every M)
+        for i, (n, k) in enumerate(shapes):
+            L = layers[i]
+            for mm in (1, 16):
+                x, _, _ = make_x(qg, synth, torch, False, mm, k, seed=40 + mm)
+                y = torch.empty((mm, n), dtype=torch.bfloat16, device="cuda")
+                wsb = qg.gemm_workspace_size_ex(L.ws[0], mm, qg.GEMM_BATCH_INVARIANT)
+                wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+                stream = torch.cuda.current_stream().cuda_stream
+                t = timed(torch, lambda j: qg.gemm_ex(L.ws[j % len(L.ws)], x, None, mm, k, y, qg.O_BF16, n, wsp, wsb,
+                                                      qg.GEMM_BATCH_INVARIANT, stream), 100, 10)
+                extra[f"batch_invariant_uint4_zp_M{mm}_N{n}_K{k}"] = {
+                    "us": round(t * 1e3, 2), "weight_GBs": round(L.bytes / (t * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        print(f"[bench] extra batch-invariant decode done", file=sys.stderr, flush=True)
         extra.update(bench_large_m(qg, synth, torch))
         extra["activation"] = bench_act(qg, synth, torch)
         moe = {}

@@ -173,6 +173,28 @@ qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64
                   hipStream_t stream);
 /* (ws, when needed, must hold zeros on entry; see qg_gemm_workspace_size.) */
 
+/* Compute options of qg_gemm_ex (the announcement's "Compute Config" names
+ * batch invariance among the compute options of a GEMM, section "Per-workload
+ * tuning and JIT compilation").
+ *   QG_GEMM_BATCH_INVARIANT: every output row is bit-identical whatever m is
+ *   (and whatever the other rows hold): the kernel and its reduction order
+ *   are chosen from (N, K) only, never from m.  Slower than the default at
+ *   small m (the large-M kernel serves every m when K % 128 == 0).  An
+ *   integer-format layer with m * K * 2 >= 2^31 returns QG_ERR_UNSUPPORTED
+ *   rather than switching kernels. */
+#define QG_GEMM_BATCH_INVARIANT 1u
+
+/* qg_gemm_workspace_size for the compute options `flags` (0 = qg_gemm's). */
+qg_status qg_gemm_workspace_size_ex(const qg_weight *w, int64_t m, uint32_t flags, uint64_t *bytes);
+
+/* qg_gemm with compute options `flags` (a combination of QG_GEMM_* bits;
+ * unknown bits: QG_ERR_INVALID_ARGUMENT).  flags == 0 is exactly qg_gemm.
+ * ws must hold qg_gemm_workspace_size_ex(w, m, flags) bytes, zero-filled once
+ * as for qg_gemm. */
+qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                     int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
+                     uint32_t flags, hipStream_t stream);
+
 /* Workspace bytes for qg_moe_sort and qg_moe_gemm with this many tokens (one
  * buffer of this size serves both; its contents on entry do not matter). */
 qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,

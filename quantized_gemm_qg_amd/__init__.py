@@ -28,8 +28,9 @@ EXPORTS = (
     "qg_gemm_workspace_size", "qg_gemm", "qg_moe_workspace_size", "qg_moe_sort",
     "qg_moe_gemm", "qg_stream_read", "qg_stream_copy", "qg_describe_dispatch",
     "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
-    "qg_moe_combine",
+    "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
 )
+GEMM_BATCH_INVARIANT = 1
 
 
 class QGError(RuntimeError):
@@ -87,6 +88,8 @@ def _load():
         "qg_quantize_mxfp8": (I32, [P, I64, I64, I64, P, I64, P, P]),
         "qg_silu_mul": (I32, [P, I32, I64, I64, I64, P, I32, I64, P, P]),
         "qg_moe_combine": (I32, [P, I32, I64, P, I64, I32, I64, P, P, I32, I64, P]),
+        "qg_gemm_workspace_size_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.POINTER(U64)]),
+        "qg_gemm_ex": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, ctypes.c_uint32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -183,6 +186,20 @@ def gemm_workspace_size(w: Weight, m: int) -> int:
     out = ctypes.c_uint64()
     _check(_lib.qg_gemm_workspace_size(ctypes.byref(w), m, ctypes.byref(out)), "qg_gemm_workspace_size")
     return out.value
+
+
+def gemm_workspace_size_ex(w: Weight, m: int, flags: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.qg_gemm_workspace_size_ex(ctypes.byref(w), m, flags, ctypes.byref(out)),
+           "qg_gemm_workspace_size_ex")
+    return out.value
+
+
+def gemm_ex(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, ws, ws_bytes: int,
+            flags: int, stream=None) -> None:
+    """qg_gemm with compute options (GEMM_BATCH_INVARIANT)."""
+    _check(_lib.qg_gemm_ex(ctypes.byref(w), _ptr(x), _ptr(x_scales), m, ldx, _ptr(y), otype, ldy,
+                           _ptr(ws), ws_bytes, flags, _stream(stream)), "qg_gemm_ex")
 
 
 def gemm(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, ws=None,

@@ -213,6 +213,21 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   return false;
 }
 
+// Batch-invariant dispatch: the variant depends on (N, K) only, so each
+// output row is reduced over K in one fixed order whatever M is.  The tiled
+// kernels (K % 128 == 0) sum every element in K-step order with a per-element
+// MFMA chain independent of the tile's position; the skinny kernel with a
+// variant fixed by (N, K) sums its waves' and splits' partials in index order.
+// Tile widths do not change any element's order; they are fixed anyway.
+static Variant select_dense_invariant(const qg_weight &w) {
+  const bool mx = w.desc.wtype == QG_W_MXFP4;
+  if (w.desc.k % 128 == 0 && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
+    const int bn = mx ? 256 : a16_tiled_bn();
+    return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
+  }
+  return skinny_for(w.desc, w.n_tiles, w.k_blocks, 1);
+}
+
 Variant select_dense(const qg_weight &w, int64_t m) {
   Variant v;
   if (tiled_for(w, m, &v)) return v;
@@ -488,24 +503,39 @@ extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
   return result;
 }
 
-extern "C" qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes) {
+static Variant dense_variant(const qg_weight &w, int64_t m, uint32_t flags) {
+  return (flags & QG_GEMM_BATCH_INVARIANT) ? select_dense_invariant(w) : select_dense(w, m);
+}
+
+extern "C" qg_status qg_gemm_workspace_size_ex(const qg_weight *w, int64_t m, uint32_t flags, uint64_t *bytes) {
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
-  if (!bytes || m < 0) return QG_ERR_INVALID_ARGUMENT;
-  *bytes = dense_ws_bytes(*w, select_dense(*w, m), m);
+  if (!bytes || m < 0 || (flags & ~(uint32_t)QG_GEMM_BATCH_INVARIANT) != 0) return QG_ERR_INVALID_ARGUMENT;
+  *bytes = dense_ws_bytes(*w, dense_variant(*w, m, flags), m);
   return QG_OK;
+}
+
+extern "C" qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes) {
+  return qg_gemm_workspace_size_ex(w, m, 0, bytes);
 }
 
 extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
                              int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws,
                              uint64_t ws_bytes, hipStream_t stream) {
+  return qg_gemm_ex(w, x, x_scales, m, ldx, y, otype, ldy, ws, ws_bytes, 0, stream);
+}
+
+extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                                int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws,
+                                uint64_t ws_bytes, uint32_t flags, hipStream_t stream) {
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
   const qg_layer_desc &d = w->desc;
   if (d.num_experts != 1) return QG_ERR_INVALID_ARGUMENT;
   if (m < 0 || (otype != QG_O_BF16 && otype != QG_O_F32)) return QG_ERR_INVALID_ARGUMENT;
+  if ((flags & ~(uint32_t)QG_GEMM_BATCH_INVARIANT) != 0) return QG_ERR_INVALID_ARGUMENT;
   if (m > (1ll << 30)) return QG_ERR_UNSUPPORTED;
   if (m == 0) return QG_OK;
   if (!x || !y) return QG_ERR_INVALID_ARGUMENT;
@@ -515,7 +545,10 @@ extern "C" qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_sc
   const int yel = otype == QG_O_F32 ? 4 : 2;
   if (!aligned16(x) || !aligned16(y) || (ldx * xel) % 16 != 0 || (ldy * yel) % 4 != 0)
     return QG_ERR_ALIGNMENT;
-  const Variant v = select_dense(*w, m);
+  const Variant v = dense_variant(*w, m, flags);
+  // the integer-format tiled kernel addresses X with 32-bit offsets; a
+  // batch-invariant call may not move to another kernel past that size
+  if (v.kind == 2 && (uint64_t)m * d.k * 2 >= (1ull << 31)) return QG_ERR_UNSUPPORTED;
   const uint64_t need = dense_ws_bytes(*w, v, m);
   if (need > 0) {
     if (!ws) return QG_ERR_INVALID_ARGUMENT;

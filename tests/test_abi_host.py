@@ -370,3 +370,17 @@ def test_activation_entry_points_validate_before_launch():
             qg.moe_combine(a["y"], a["yt"], a["ldy"], a["w"], a["t"], a["topk"], a["n"], a["bias"], a["out"],
                            a["ot"], a["ldout"], stream=S)
         assert e.value.status == status, kw
+
+
+def test_gemm_ex_flags_validated():
+    w = _bound(qg.layer_desc(qg.W_INT4, 256, 512, 128))
+    for bad in (2, 0x80000000):
+        with pytest.raises(qg.QGError) as e:
+            qg.gemm_workspace_size_ex(w, 4, bad)
+        assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+        with pytest.raises(qg.QGError) as e:
+            qg.gemm_ex(w, FAKE_DEV, None, 4, 512, FAKE_DEV, qg.O_BF16, 256, None, 0, bad, stream=0)
+        assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
+    # the invariant option sizes the large-M kernel's workspace at any M
+    assert qg.gemm_workspace_size_ex(w, 1, qg.GEMM_BATCH_INVARIANT) > 0
+    assert qg.gemm_workspace_size_ex(w, 1, 0) == qg.gemm_workspace_size(w, 1)
