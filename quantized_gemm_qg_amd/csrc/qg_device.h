@@ -15,6 +15,30 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(8))) int32_t i32x8;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 
+typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
+
+// The scaled f8f6f4 MFMA with its operand vectors sized by format: the LLVM
+// intrinsic is overloaded on them, and an e2m1 operand (32 codes per lane)
+// needs 4 registers where the clang builtin always passes 8.
+extern "C" __device__ f32x4 qg_mfma_scale_16x16x128_f8_f4(i32x8 a, i32x4 b, f32x4 c, int fmt_a, int fmt_b,
+                                                          int opsel_a, int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v8i32.v4i32");
+
+// acc += (e4m3 A, e8m0 scale sa) x (e2m1 B, e8m0 scale: byte SB of sb_word),
+// one 16x16x128 step; the instruction's scale byte select picks SB
+template <int SB>
+__device__ __forceinline__ f32x4 mfma_e4m3_e2m1(i32x8 a, i32x4 b, f32x4 c, int sa, int sb_word) {
+  return qg_mfma_scale_16x16x128_f8_f4(a, b, c, 0, 4, 0, sa, SB, sb_word);
+}
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+// acc (32 x 32) += A (32 x 16 bf16) x B (16 x 32 bf16)
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -222,12 +246,14 @@ constexpr int store_tile_lds_bytes() {
   return 16 * (16 * NJ * 4 + 16) + 16 * MI * 4;
 }
 
-template <int MI, int NJ, typename F>
-__device__ __forceinline__ void store_tile(const GemmArgs &a, const TileRows &tr, F &&acc_at,
-                                           int row0, int col0, uint8_t *lds) {
+// The store path of store_tile for any accumulator layout: write_slab(i, lds,
+// pitch, f32) writes the wave's 16-row slab i ([16][16 NJ] of fp32 or bf16 at
+// `pitch` bytes per row); the rows are then stored from LDS.
+template <int MI, int NJ, typename W>
+__device__ __forceinline__ void store_slabs(const GemmArgs &a, const TileRows &tr, W &&write_slab,
+                                            int row0, int col0, uint8_t *lds) {
   constexpr int WN = 16 * NJ;  // columns of the wave tile
   const int lane = threadIdx.x & 63;
-  const int q = lane >> 4, r16 = lane & 15;
   const bool f32 = a.otype == QG_O_F32;
   const int el = f32 ? 4 : 2;
   const int pitch = WN * el + 16;           // padded row pitch (bytes)
@@ -242,18 +268,7 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const TileRows &tr
   }
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const f32x4 v = acc_at(i, j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        uint8_t *p = lds + (4 * q + e) * pitch + (16 * j + r16) * el;
-        if (f32)
-          *(float *)p = v[e];
-        else
-          *(__bf16 *)p = (__bf16)v[e];
-      }
-    }
+    write_slab(i, lds, pitch, f32);
     // the wave's own LDS accesses complete in order; this keeps the compiler
     // from moving the reads above the writes
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -280,8 +295,37 @@ __device__ __forceinline__ void store_tile(const GemmArgs &a, const TileRows &tr
         }
       }
     }
-    asm volatile("" ::: "memory");  // next block's writes stay below these reads
+    asm volatile("" ::: "memory");  // next slab's writes stay below these reads
   }
+}
+
+// one fp32 / bf16 element of a slab in LDS
+__device__ __forceinline__ void slab_put(uint8_t *lds, int pitch, bool f32, int row, int col, float v) {
+  uint8_t *p = lds + row * pitch + col * (f32 ? 4 : 2);
+  if (f32)
+    *(float *)p = v;
+  else
+    *(__bf16 *)p = (__bf16)v;
+}
+
+// acc_at(i, j): the f32x4 of 16 x 16 block (i, j) in the 16x16 MFMA layout
+// (lane: column lane % 16, rows 4 (lane / 16) + e)
+template <int MI, int NJ, typename F>
+__device__ __forceinline__ void store_tile(const GemmArgs &a, const TileRows &tr, F &&acc_at,
+                                           int row0, int col0, uint8_t *lds) {
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, r16 = lane & 15;
+  store_slabs<MI, NJ>(
+      a, tr,
+      [&](int i, uint8_t *l, int pitch, bool f32) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const f32x4 v = acc_at(i, j);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) slab_put(l, pitch, f32, 4 * q + e, 16 * j + r16, v[e]);
+        }
+      },
+      row0, col0, lds);
 }
 
 }  // namespace qg

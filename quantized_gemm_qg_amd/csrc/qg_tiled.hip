@@ -44,6 +44,8 @@
 // rows and weight columns in that XCD's L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "qg_device.h"
 #include "qg_internal.h"
 
@@ -168,7 +170,13 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 
   issue(0, 0);
   if (kbs > 1) issue(1, 1);
-  for (int kb = 0; kb < kbs; ++kb) {
+  // the wave's B scale dwords of the current 4-step group (one byte per step,
+  // picked by the MFMA's scale byte select)
+  uint32_t swv[C::NB];
+  // one K step; S = kb % 4 is a compile-time constant (the loop below is
+  // unrolled by four) because the byte select is an instruction field
+  auto step = [&](int kb, auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
     // outstanding after stage kb: this wave's loads of stage kb + 1
     if (kb + 1 < kbs) {
       const bool ring_next = ((kb + 1) & 3) == 0;  // stage kb + 1 also fills the scale rings
@@ -186,16 +194,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();  // stage kb is in LDS; stage kb - 1 is free
     if (kb + 2 < kbs) issue(kb + 2, (kb + 2) % kStages);
     const uint8_t *st = smem + (kb % kStages) * C::STAGE;
-    i32x8 bf[C::NB];
-    int bsc[C::NB];
+    i32x4 bf[C::NB];
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
       const int blk = wn * C::NB + j;
       const u32x4 v = *(const u32x4 *)(st + C::A + blk * 1024 + 16 * lane);
-      bf[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-      const uint32_t sw = *(const uint32_t *)(smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW +
-                                              ((blk * 16 + r16) * 4 + q) * 4);
-      bsc[j] = (int)((sw >> (8 * (kb & 3))) & 0xFFu);
+      bf[j] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      if constexpr (S == 0)  // the SW slot of steps kb .. kb + 3 landed with stage kb
+        swv[j] = *(const uint32_t *)(smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW + ((blk * 16 + r16) * 4 + q) * 4);
     }
     auto read_a = [&](int i, i32x8 &af, int &asc) {
       const int row = wm * (BM / WM) + i * 16 + r16;
@@ -221,25 +227,29 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
           read_a(i, af[0], asc[0]);
 #pragma unroll
           for (int j = 0; j < C::NB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[0], bf[j], acc[i][j], 0, 4, 0,
-                                                                          asc[0], 0, bsc[j]);
+            acc[i][j] = mfma_e4m3_e2m1<S>(af[0], bf[j], acc[i][j], asc[0], (int)swv[j]);
         }
       }
-      continue;
+      return;
     }
     read_a(0, af[0], asc[0]);
-    // B (2 NB reads) and A block 0 (3 reads) first
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NB + 3, 0);
+    // B (NB reads, plus NB scale dwords every fourth step) and A block 0 (3 reads) first
+    __builtin_amdgcn_sched_group_barrier(0x100, (S == 0 ? 2 : 1) * C::NB + 3, 0);
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) {
       if (i + 1 < C::MB) read_a(i + 1, af[(i + 1) & 1], asc[(i + 1) & 1]);
 #pragma unroll
       for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], 0, 4,
-                                                                      0, asc[i & 1], 0, bsc[j]);
+        acc[i][j] = mfma_e4m3_e2m1<S>(af[i & 1], bf[j], acc[i][j], asc[i & 1], (int)swv[j]);
       if (i + 1 < C::MB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next block's reads
       __builtin_amdgcn_sched_group_barrier(0x008, C::NB, 0);                // this block's MFMAs
     }
+  };
+  for (int kb = 0; kb < kbs; kb += 4) {
+    step(kb, std::integral_constant<int, 0>{});
+    if (kb + 1 < kbs) step(kb + 1, std::integral_constant<int, 1>{});
+    if (kb + 2 < kbs) step(kb + 2, std::integral_constant<int, 2>{});
+    if (kb + 3 < kbs) step(kb + 3, std::integral_constant<int, 3>{});
   }
 
   // output through LDS (the ring is free once every wave is past its last stage)

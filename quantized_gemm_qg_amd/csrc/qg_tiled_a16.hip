@@ -101,6 +101,13 @@ struct A16Cfg {
   static constexpr int after(int ai, int bi) { return (NB > NA ? bi : 0) + (NA - 2) * (ai + bi); }
   static constexpr int AFTER_A = after(A_ISSUE, B_ISSUE);   // the largest
   static constexpr int MI = BM / WM / 16;             // 16-row blocks per wave
+  // wave tiles that are multiples of 32 x 32 run v_mfma_f32_32x32x16_bf16
+  // (measured on gfx950: 2.18 PFLOP/s sustained from registers, against
+  // 1.43 for 16x16x32); the small tiles (16-column waves) keep 16x16x32
+  static constexpr bool M32 = WM > 1 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0;
+  static constexpr int MB2 = BM / WM / 32;            // 32-row blocks per wave (M32)
+  static constexpr int NB2 = BN / WN / 32;            // 32-column blocks per wave (M32)
+  static constexpr int MPG = GROUP / 16;              // K16 MFMA steps per group (M32)
   // small tiles (one wave per 16 columns, every wave all BM rows) are for
   // MoE experts with few rows: row blocks past the tile's rows are skipped
   static constexpr bool SKIP_ROWS = WM == 1;
@@ -218,11 +225,19 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
     }
   };
 
-  f32x4 acc[C::MI][C::NJ];
+  f32x4 acc[C::M32 ? 1 : C::MI][C::M32 ? 1 : C::NJ];
+  f32x16 acc32[C::M32 ? C::MB2 : 1][C::M32 ? C::NB2 : 1];
+  if constexpr (C::M32) {
 #pragma unroll
-  for (int i = 0; i < C::MI; ++i)
+    for (int i = 0; i < C::MB2; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < C::NB2; ++j) acc32[i][j] = f32x16{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // prologue: activations NA - 1 stages ahead, weights NB - 1 stages ahead
   for (int s = 0; s < C::NB - 1; ++s) {
@@ -242,6 +257,80 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
     if (kb + C::NB - 1 < kbs) issue_b(kb + C::NB - 1);
     const uint8_t *st = smem + (kb % C::NA) * C::A_STAGE;
     const uint8_t *sb = smem + C::OFF_BRING + (kb % C::NB) * C::B_STAGE;
+
+    if constexpr (C::M32) {
+      // 32 x 32 blocks.  Lane l works on column / row l % 32 of a block and
+      // K16 half h = l / 32.  The B operand of K16 step m (k = 16 m + 8 h +
+      // 0..7 of the stage) is dword m / 2 of the packed lane slot with quarter
+      // 2 (m % 2) + h, i.e. slots (l % 16) + 16 h and that + 32 of the
+      // block's n-tile; A is 16-byte chunk 2 m + h of the row.  Accumulator
+      // element 4 ii + e holds row 8 ii + 4 h + e.
+      const int h = lane >> 5, c32 = lane & 31;
+      u32x4 bw[C::NB2][8];
+#pragma unroll
+      for (int j = 0; j < C::NB2; ++j) {
+        const int blk = 2 * (wn * C::NB2 + j) + (c32 >> 4);
+        const int slot = (c32 & 15) + 16 * h;
+        u32x4 v[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          if constexpr (BITS == 4) {
+            v[hh] = *(const u32x4 *)(sb + blk * 1024 + 16 * (slot + 32 * hh));
+          } else {
+            const uint32_t *p = (const uint32_t *)(sb + blk * 768 + 12 * (slot + 32 * hh));
+            v[hh] = u32x4{p[0], p[1], p[2], 0u};
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          bw[j][2 * jj] = unpack_br<BITS>(v[0], jj, umask, umagic);
+          bw[j][2 * jj + 1] = unpack_br<BITS>(v[1], jj, umask, umagic);
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < C::GPB; ++gi) {
+        const int gg = kb * C::GPB + gi;
+        float c1[C::NB2], zf[C::NB2];
+#pragma unroll
+        for (int j = 0; j < C::NB2; ++j) {
+          const int col = wn * 32 * C::NB2 + 32 * j + c32;
+          const uint32_t sbits = *(const uint16_t *)(sb + C::OFF_SS + col * 16 + 2 * (gg & 7));
+          c1[j] = C::MAG * bf16_bits_to_f32(sbits);
+          int z = C::ZSYM;
+          if constexpr (ZP) z = (int)((*(const uint32_t *)(sb + C::OFF_SZ + col * 4) >> (4 * (gg & 7))) & 15u);
+          zf[j] = ZP ? -(1.f + (float)z / C::MAG) : 1.f;
+        }
+#pragma unroll
+        for (int i = 0; i < C::MB2; ++i) {
+          const int r0 = wm * (BM / WM) + 32 * i;
+          const uint8_t *arow = st + (r0 + c32) * 256;
+          u32x4 af[C::MPG];
+#pragma unroll
+          for (int ss = 0; ss < C::MPG; ++ss)
+            af[ss] = *(const u32x4 *)(arow + 16 * ((2 * (gi * C::MPG + ss) + h) ^ (c32 & 15)));
+          f32x4 sxq[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii)
+            sxq[ii] = *(const f32x4 *)(st + C::A + (gi * C::SXR + r0 + 8 * ii + 4 * h) * 4);
+          f32x16 g[C::NB2];
+#pragma unroll
+          for (int j = 0; j < C::NB2; ++j)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) g[j][4 * ii + e] = ZP ? sxq[ii][e] * zf[j] : sxq[ii][e];
+#pragma unroll
+          for (int ss = 0; ss < C::MPG; ++ss)
+#pragma unroll
+            for (int j = 0; j < C::NB2; ++j) g[j] = mfma32_bf16(af[ss], bw[j][gi * C::MPG + ss], g[j]);
+#pragma unroll
+          for (int j = 0; j < C::NB2; ++j)
+#pragma unroll
+            for (int t = 0; t < 16; ++t) acc32[i][j][t] = __builtin_fmaf(g[j][t], c1[j], acc32[i][j][t]);
+        }
+      }
+      continue;
+    }
 
     // weight operands of the wave's NJ column blocks for the 4 K32 steps
     u32x4 bw[C::NJ][4];
@@ -299,8 +388,32 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
 
   // output through LDS (the ring is free once every wave is past its last stage)
   lds_barrier();
-  store_tile<C::MI, C::NJ>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / WM),
-                           (nt0 + wn * C::NJ) * 16, smem + wave * store_tile_lds_bytes<C::MI, C::NJ>());
+  if constexpr (C::M32) {
+    // 16-row slab s = rows 16 s .. 16 s + 15 of the wave tile: 32-row block
+    // s / 2, accumulator rows 8 ii + 4 h + e with ii in {2 (s % 2), 2 (s % 2) + 1}
+    const int h = lane >> 5, c32 = lane & 31;
+    store_slabs<C::MI, C::NJ>(
+        a, tr,
+        [&](int sl, uint8_t *l, int pitch, bool f32) {
+#pragma unroll
+          for (int i = 0; i < C::MB2; ++i) {
+            if (i != sl / 2) continue;
+#pragma unroll
+            for (int j = 0; j < C::NB2; ++j)
+#pragma unroll
+              for (int iq = 0; iq < 2; ++iq)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int ii = 2 * (sl & 1) + iq;
+                  slab_put(l, pitch, f32, 8 * iq + 4 * h + e, 32 * j + c32, acc32[i][j][4 * ii + e]);
+                }
+          }
+        },
+        wm * (BM / WM), (nt0 + wn * C::NJ) * 16, smem + wave * store_tile_lds_bytes<C::MI, C::NJ>());
+  } else {
+    store_tile<C::MI, C::NJ>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / WM),
+                             (nt0 + wn * C::NJ) * 16, smem + wave * store_tile_lds_bytes<C::MI, C::NJ>());
+  }
 }
 
 // Group row sums of bf16 X: xs[g * rows + r] = factor * (sum of x[r, g*GROUP ..
