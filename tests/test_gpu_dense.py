@@ -177,6 +177,18 @@ def test_mx_tiled_large_m_ragged(monkeypatch, m, n, k, bn):
     _check(layer, Acts(True, m, k, seed=m), m)
 
 
+@pytest.mark.parametrize("m", [256, 130])
+@pytest.mark.parametrize("k", [128, 256, 384, 896])
+def test_mx_tiled_short_k(m, k):
+    """1, 2, 3 and 7 K steps through the tiled MX kernel (256- and 128-row
+    tiles): its K loop runs four steps per trip (the weight-scale byte select
+    is an instruction field), so every remainder of the step count by 4 is
+    exercised."""
+    layer = Layer(qg.W_MXFP4, 136, k, 32, seed=k + m)
+    assert "mx_tiled" in qg.describe_dispatch(layer.w, m)
+    _check(layer, Acts(True, m, k, seed=k), m)
+
+
 @pytest.mark.parametrize("m,n,k", [(300, 200, 1024), (256, 448, 4096)])
 def test_mx_tiled_unaligned_activation_scales(m, n, k):
     """K % 512 == 0 with the activation scales at a 4-byte (not 16-byte)
