@@ -502,6 +502,24 @@ def main():
 
     if not args.quick:
         extra = {}
+        # the same decode step after qg_gemm_autotune of both GEMMs (candidates
+        # timed from cold caches: a 512 MiB read before every timed launch)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        tuned = []
+        for L, (x, _, _) in zip(layers, xs):
+            y = torch.empty((1, L.n), dtype=torch.bfloat16, device="cuda")
+            wsb = qg.gemm_autotune_workspace_size(L.ws[0], 1)
+            wst = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            tuned.append(qg.gemm_autotune(L.ws[0], x, None, 1, L.k, y, qg.O_BF16, L.n, wst, wsb, flush, flush.numel(), 10))
+        del flush
+        launchers_t = [dense_launcher(qg, torch, L, x, None, 1) for L, (x, _, _) in zip(layers, xs)]
+        ms_t = timed(torch, lambda i: [f(i) for f in launchers_t], args.steps, args.warmup)
+        extra["decode_step_autotuned"] = {
+            "us": round(ms_t * 1e3, 2), "weight_GBs": round(step_bytes / (ms_t * 1e-3) / 1e9, 1),
+            "hbm_frac": round(step_bytes / (ms_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "dispatch": [t[0] for t in tuned], "cold_cache_us": [round(t[1], 2) for t in tuned]}
+        print(f"[bench] autotuned decode step: {extra['decode_step_autotuned']}", file=sys.stderr, flush=True)
+        qg.autotune_reset()
         for wtype, name in ((qg.W_UINT4, "uint4_zp"), (qg.W_INT3, "int3")):
             for i, (n, k) in enumerate(shapes):
                 L = layers[i] if wtype == qg.W_UINT4 else DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=30 + i)

@@ -195,6 +195,38 @@ qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x_scales, in
                      int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
                      uint32_t flags, hipStream_t stream);
 
+/* Autotune of the dense tuning table (announcement, "Future plans": candidate
+ * configurations are benchmarked on the target device to find better
+ * execution parameters per workload, complementing the heuristics).
+ * qg_gemm_autotune runs the dense GEMM of this call once per candidate kernel
+ * variant (the heuristic's choice, the decode / skinny / tiled kernels' other
+ * compiled shapes that can serve m rows), times each with HIP events over
+ * `reps` launches (1..64) after one warm-up launch, and records the fastest in
+ * a process-wide table keyed by (wtype, group, N, K) and the M bucket of m
+ * (1, 2-4, 5-8, 9-16, 17-64, 65-256, 257-1024, > 1024).  From then on qg_gemm,
+ * qg_gemm_workspace_size and qg_describe_dispatch use that variant for every
+ * m of the bucket it can serve (otherwise the heuristics); batch-invariant
+ * calls ignore the table.  Query qg_gemm_workspace_size again after tuning:
+ * the tuned variant may need a different workspace.
+ *   x, x_scales, ldx, y, otype, ldy  as in qg_gemm; y is overwritten (the
+ *            result of the last candidate run).
+ *   ws       device, 256-B aligned, qg_gemm_autotune_workspace_size bytes;
+ *            contents on entry do not matter (the call clears what must
+ *            start at zero).  Not a qg_gemm workspace: it leaves scratch.
+ *   flush    optional device buffer (16-B aligned, flush_bytes a multiple of
+ *            16) read in full before every timed launch so that each launch
+ *            starts from cold caches (pass more than the 256 MB MALL), or NULL.
+ *   chosen   optional host buffer receiving the chosen variant's description;
+ *   chosen_us optional host float receiving its mean time per launch (us).
+ * Synchronizes `stream`.  Thread-safe (the table is guarded by a mutex). */
+qg_status qg_gemm_autotune_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes);
+qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                           int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
+                           const void *flush, uint64_t flush_bytes, int32_t reps, hipStream_t stream,
+                           char *chosen, uint64_t chosen_bytes, float *chosen_us);
+/* Forget every autotuned entry (back to the heuristics). */
+void qg_autotune_reset(void);
+
 /* Workspace bytes for qg_moe_sort and qg_moe_gemm with this many tokens (one
  * buffer of this size serves both; its contents on entry do not matter). */
 qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,

@@ -29,6 +29,7 @@ EXPORTS = (
     "qg_moe_gemm", "qg_stream_read", "qg_stream_copy", "qg_describe_dispatch",
     "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
+    "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset",
 )
 GEMM_BATCH_INVARIANT = 1
 
@@ -90,6 +91,10 @@ def _load():
         "qg_moe_combine": (I32, [P, I32, I64, P, I64, I32, I64, P, P, I32, I64, P]),
         "qg_gemm_workspace_size_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.POINTER(U64)]),
         "qg_gemm_ex": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, ctypes.c_uint32, P]),
+        "qg_gemm_autotune_workspace_size": (I32, [W, I64, ctypes.POINTER(U64)]),
+        "qg_gemm_autotune": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, P, U64, I32, P, ctypes.c_char_p, U64,
+                                   ctypes.POINTER(ctypes.c_float)]),
+        "qg_autotune_reset": (None, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -261,3 +266,26 @@ def moe_combine(y, y_type: int, ldy: int, topk_weights, num_tokens: int, topk: i
     """out[t] = sum_j topk_weights[t, j] * y[t*topk + j] (+ bias)."""
     _check(_lib.qg_moe_combine(_ptr(y), y_type, ldy, _ptr(topk_weights), num_tokens, topk, n, _ptr(bias),
                                _ptr(out), out_type, ldout, _stream(stream)), "qg_moe_combine")
+
+
+def gemm_autotune_workspace_size(w: Weight, m: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.qg_gemm_autotune_workspace_size(ctypes.byref(w), m, ctypes.byref(out)),
+           "qg_gemm_autotune_workspace_size")
+    return out.value
+
+
+def gemm_autotune(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, ws, ws_bytes: int,
+                  flush=None, flush_bytes: int = 0, reps: int = 10, stream=None) -> tuple[str, float]:
+    """Time the candidate variants of this dense GEMM and keep the fastest for
+    its (layer, M bucket); returns (description, mean us per launch)."""
+    buf = ctypes.create_string_buffer(256)
+    us = ctypes.c_float()
+    _check(_lib.qg_gemm_autotune(ctypes.byref(w), _ptr(x), _ptr(x_scales), m, ldx, _ptr(y), otype, ldy, _ptr(ws),
+                                 ws_bytes, _ptr(flush), flush_bytes, reps, _stream(stream), buf, 256,
+                                 ctypes.byref(us)), "qg_gemm_autotune")
+    return buf.value.decode(), us.value
+
+
+def autotune_reset() -> None:
+    _lib.qg_autotune_reset()

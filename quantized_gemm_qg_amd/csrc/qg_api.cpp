@@ -10,6 +10,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "qg_internal.h"
 
@@ -228,7 +230,93 @@ static Variant select_dense_invariant(const qg_weight &w) {
   return skinny_for(w.desc, w.n_tiles, w.k_blocks, 1);
 }
 
+// ---------------------------------------------------------------------------
+// Autotune table (announcement, "Future plans": benchmark candidate
+// configurations on the target device to find better execution parameters
+// per workload, complementing the heuristics).  qg_gemm_autotune times the
+// candidates of one (layer, M) and keeps the fastest here, per layer shape and
+// M bucket; select_dense consults it before its heuristics.
+// ---------------------------------------------------------------------------
+namespace {
+struct TuneEntry {
+  int32_t wtype, group, bucket;
+  int64_t n, k;
+  Variant v;
+};
+std::mutex g_tune_mu;
+std::vector<TuneEntry> g_tune;
+}  // namespace
+
+// M buckets of the table: 1, 2-4, 5-8, 9-16, 17-64, 65-256, 257-1024, > 1024
+static int m_bucket(int64_t m) {
+  static const int64_t edges[] = {1, 4, 8, 16, 64, 256, 1024};
+  int b = 0;
+  while (b < 7 && m > edges[b]) ++b;
+  return b;
+}
+
+static bool same_variant(const Variant &a, const Variant &b) {
+  return a.kind == b.kind && a.T == b.T && a.KR == b.KR && a.W == b.W && a.splits == b.splits && a.bm == b.bm &&
+         a.tbn == b.tbn;
+}
+
+// Whether v can serve m rows of w (a table entry serves every M of its bucket)
+static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
+  const qg_layer_desc &d = w.desc;
+  const bool mx = d.wtype == QG_W_MXFP4;
+  switch (v.kind) {
+    case 0:
+      return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 && covers(v, w.k_blocks);
+    case 1:
+      return mx && d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) &&
+             (v.tbn == 256 || (mx_tiled_waves() == 8 && (v.tbn == 192 || v.tbn == 224)));
+    case 2:
+      return !mx && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
+             (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31) &&
+             ((v.bm == 128 && v.tbn == 256 && a16_tiled_waves() == 8) || ((v.bm == 128 || v.bm == 256) && v.tbn == 128));
+    case 3: {
+      Variant t;
+      return !mx && m >= 1 && m <= 16 && d.k % 512 == 0 && decode_fits(w, m, v.T, v.KR, v.splits, &t) && t.W == v.W;
+    }
+  }
+  return false;
+}
+
+static bool tuned_lookup(const qg_weight &w, int64_t m, Variant *v) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  const int b = m_bucket(m);
+  for (const TuneEntry &e : g_tune)
+    if (e.wtype == w.desc.wtype && e.group == w.desc.group_size && e.n == w.desc.n && e.k == w.desc.k &&
+        e.bucket == b) {
+      if (!variant_valid(w, m, e.v)) return false;
+      *v = e.v;
+      return true;
+    }
+  return false;
+}
+
+static void tuned_store(const qg_weight &w, int64_t m, const Variant &v) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  const int b = m_bucket(m);
+  for (TuneEntry &e : g_tune)
+    if (e.wtype == w.desc.wtype && e.group == w.desc.group_size && e.n == w.desc.n && e.k == w.desc.k &&
+        e.bucket == b) {
+      e.v = v;
+      return;
+    }
+  g_tune.push_back(TuneEntry{w.desc.wtype, w.desc.group_size, b, w.desc.n, w.desc.k, v});
+}
+
+static Variant select_dense_heuristic(const qg_weight &w, int64_t m);
+
 Variant select_dense(const qg_weight &w, int64_t m) {
+  Variant v;
+  // experiment overrides win over the table
+  if (!getenv("QG_TUNE") && !getenv("QG_DECODE") && !getenv("QG_TILED") && tuned_lookup(w, m, &v)) return v;
+  return select_dense_heuristic(w, m);
+}
+
+static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
   Variant v;
   if (tiled_for(w, m, &v)) return v;
   if (!getenv("QG_TUNE") && decode_for(w, m, &v)) return v;
@@ -503,6 +591,37 @@ extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
   return result;
 }
 
+// One dense GEMM with variant v (arguments already validated; ws holds
+// dense_ws_bytes(w, v, m) bytes, its split-K counters zero).
+static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, const Variant &v, const void *x,
+                                       const void *x_scales, int64_t m, int64_t ldx, void *y, int32_t otype,
+                                       int64_t ldy, void *ws, hipStream_t stream) {
+  const qg_layer_desc &d = w.desc;
+  GemmArgs a;
+  base_args(w, &a);
+  a.x = x;
+  a.x_scales = (const uint8_t *)x_scales;
+  a.ldx = ldx;
+  a.y = y;
+  a.ldy = ldy;
+  a.otype = otype;
+  a.m = (int32_t)m;
+  a.splits = v.splits;
+  if (v.splits > 1) {
+    // counters start at zero (the caller zero-fills the workspace once) and
+    // every call leaves them at zero again
+    const int64_t m_tiles = (m + 15) / 16;
+    const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
+    const uint64_t cnt = (uint64_t)m_tiles * n_blocks;
+    a.counters = (uint32_t *)ws;
+    a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
+  }
+  if (v.kind == 1) return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream);
+  if (v.kind == 3) return launch_decode_a16(a, d, v, stream);
+  if (v.kind == 2) return launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), ws, true, stream);
+  return L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
+}
+
 static Variant dense_variant(const qg_weight &w, int64_t m, uint32_t flags) {
   return (flags & QG_GEMM_BATCH_INVARIANT) ? select_dense_invariant(w) : select_dense(w, m);
 }
@@ -555,35 +674,7 @@ extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x
     if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
     if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
   }
-  GemmArgs a;
-  base_args(*w, &a);
-  a.x = x;
-  a.x_scales = (const uint8_t *)x_scales;
-  a.ldx = ldx;
-  a.y = y;
-  a.ldy = ldy;
-  a.otype = otype;
-  a.m = (int32_t)m;
-  a.splits = v.splits;
-  hipError_t he = hipSuccess;
-  if (v.splits > 1) {
-    // counters start at zero (the caller zero-fills the workspace once) and
-    // every call leaves them at zero again
-    const int64_t m_tiles = (m + 15) / 16;
-    const int64_t n_blocks = (w->n_tiles + v.T - 1) / v.T;
-    const uint64_t cnt = (uint64_t)m_tiles * n_blocks;
-    a.counters = (uint32_t *)ws;
-    a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
-  }
-  if (v.kind == 1)
-    he = launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream);
-  else if (v.kind == 3)
-    he = launch_decode_a16(a, d, v, stream);
-  else if (v.kind == 2)
-    he = launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), ws, true, stream);
-  else
-    he = L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
-  return hip_status(he);
+  return hip_status(launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, ws, stream));
 }
 
 extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
@@ -764,6 +855,175 @@ extern "C" qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, 
   return hip_status(launch_moe_combine(y, yf, ldy, topk_weights, num_tokens, topk, n, bias, out, of, ldout, stream));
 }
 
+static void describe_variant(const Variant &v, bool mx, char *buf, uint64_t buf_bytes) {
+  if (v.kind == 3)
+    snprintf(buf, buf_bytes, v.splits > 1 ? "a16_decode T=%d KR=%d W=%d splits=%d" : "a16_decode T=%d KR=%d W=%d",
+             v.T, v.KR, v.W, v.splits);
+  else if (v.kind == 1 || v.kind == 2)
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", mx ? "mx" : "a16", v.bm, v.tbn);
+  else
+    snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", mx ? "mx" : "a16", v.T, v.KR, v.W, v.splits);
+}
+
+// Candidates of one dense (layer, M): the heuristic's choice first, then the
+// decode kernel's compiled (T, KR) pairs with 1, 2 or 4 K splits (integer
+// formats, M <= 16, K % 512 == 0), the skinny kernel's spill-free (T, KR)
+// with 1, 2, 4 or 8 K splits (M <= 256), and the tiled kernels' tile shapes
+// (K % 128 == 0).
+static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> *out) {
+  const qg_layer_desc &d = w.desc;
+  const bool mx = d.wtype == QG_W_MXFP4;
+  auto add = [&](const Variant &v) {
+    for (const Variant &u : *out)
+      if (same_variant(u, v)) return;
+    if (variant_valid(w, m, v)) out->push_back(v);
+  };
+  add(select_dense_heuristic(w, m));
+  if (!mx && m <= 16 && d.k % 512 == 0) {
+    static const int pairs[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}, {1, 4}};
+    for (const auto &p : pairs)
+      for (int S : {1, 2, 4}) {
+        Variant v;
+        if (decode_fits(w, m, p[0], p[1], S, &v)) add(v);
+      }
+  }
+  if (m <= 256) {
+    const int kbs = w.k_blocks;
+    for (int T : {1, 2, 4})
+      for (int KR : {1, 2, 4}) {
+        if (!variant_ok(d, T, KR)) continue;
+        const int waves_k = (kbs + KR - 1) / KR;
+        for (int S : {1, 2, 4, 8}) {
+          const int W = (waves_k + S - 1) / S;
+          if (W < 1 || W > 16) continue;
+          add(Variant{0, T, KR, W, (waves_k + W - 1) / W, 0, 0});
+        }
+      }
+  }
+  if (d.k % 128 == 0) {
+    if (mx) {
+      for (int bm : {128, 256})
+        for (int bn : {192, 224, 256}) add(Variant{1, 1, 1, 1, 1, bm, bn});
+    } else {
+      add(Variant{2, 1, 1, 1, 1, 128, 256});
+      add(Variant{2, 1, 1, 1, 1, 256, 128});
+      add(Variant{2, 1, 1, 1, 1, 128, 128});
+    }
+  }
+}
+
+constexpr int kTuneMaxReps = 64;
+constexpr uint64_t kTuneSinkBytes = 16384;
+
+// Autotune workspace: [split-K region (zero on entry, left zero)][tiled
+// kernels' scratch][flush sink], each 256-byte aligned.
+static void tune_ws_parts(const qg_weight &w, int64_t m, const std::vector<Variant> &c, uint64_t *split_bytes,
+                          uint64_t *tiled_bytes) {
+  *split_bytes = 0;
+  *tiled_bytes = 0;
+  for (const Variant &v : c) {
+    const uint64_t b = align_up(dense_ws_bytes(w, v, m), 256);
+    if (v.kind == 1 || v.kind == 2)
+      *tiled_bytes = std::max(*tiled_bytes, b);
+    else
+      *split_bytes = std::max(*split_bytes, b);
+  }
+}
+
+extern "C" qg_status qg_gemm_autotune_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (!bytes || m < 0 || w->desc.num_experts != 1) return QG_ERR_INVALID_ARGUMENT;
+  if (m == 0) {
+    *bytes = 0;
+    return QG_OK;
+  }
+  std::vector<Variant> c;
+  tune_candidates(*w, m, &c);
+  uint64_t sb, tb;
+  tune_ws_parts(*w, m, c, &sb, &tb);
+  *bytes = sb + tb + kTuneSinkBytes;
+  return QG_OK;
+}
+
+extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                                      int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
+                                      const void *flush, uint64_t flush_bytes, int32_t reps, hipStream_t stream,
+                                      char *chosen, uint64_t chosen_bytes, float *chosen_us) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  const qg_layer_desc &d = w->desc;
+  if (d.num_experts != 1 || m < 1 || reps < 1 || reps > kTuneMaxReps) return QG_ERR_INVALID_ARGUMENT;
+  if (otype != QG_O_BF16 && otype != QG_O_F32) return QG_ERR_INVALID_ARGUMENT;
+  if (m > (1ll << 30)) return QG_ERR_UNSUPPORTED;
+  if (!x || !y || !ws || (L.is_mx && !x_scales)) return QG_ERR_INVALID_ARGUMENT;
+  if (ldx < d.k || ldy < d.n) return QG_ERR_SHAPE;
+  const int xel = L.is_mx ? 1 : 2;
+  const int yel = otype == QG_O_F32 ? 4 : 2;
+  if (!aligned16(x) || !aligned16(y) || (ldx * xel) % 16 != 0 || (ldy * yel) % 4 != 0 ||
+      ((uintptr_t)ws & 255u) != 0)
+    return QG_ERR_ALIGNMENT;
+  if (flush && (flush_bytes % 16 != 0 || !aligned16(flush))) return QG_ERR_ALIGNMENT;
+  std::vector<Variant> cand;
+  tune_candidates(*w, m, &cand);
+  uint64_t sb, tb;
+  tune_ws_parts(*w, m, cand, &sb, &tb);
+  if (ws_bytes < sb + tb + kTuneSinkBytes) return QG_ERR_BUFFER_TOO_SMALL;
+  uint8_t *split_ws = (uint8_t *)ws, *tiled_ws = split_ws + sb, *sink = tiled_ws + tb;
+  // the split-K counters must start at zero; the rest is scratch
+  if (sb > 0) {
+    const hipError_t me = hipMemsetAsync(split_ws, 0, sb, stream);
+    if (me != hipSuccess) return hip_status(me);
+  }
+
+  hipEvent_t ev[2 * kTuneMaxReps];
+  int made = 0;
+  hipError_t he = hipSuccess;
+  for (; made < 2 * reps; ++made)
+    if ((he = hipEventCreate(&ev[made])) != hipSuccess) break;
+  int best = -1;
+  float best_us = 0.f;
+  for (size_t i = 0; he == hipSuccess && i < cand.size(); ++i) {
+    const Variant &v = cand[i];
+    void *vws = (v.kind == 1 || v.kind == 2) ? (void *)tiled_ws : (void *)split_ws;
+    auto run = [&]() { return launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, vws, stream); };
+    if (run() != hipSuccess) continue;  // an instance this shape does not compile to: skip it
+    for (int r = 0; r < reps && he == hipSuccess; ++r) {
+      if (flush && flush_bytes) he = launch_stream_read(flush, flush_bytes, sink, stream);
+      if (he == hipSuccess) he = hipEventRecord(ev[2 * r], stream);
+      if (he == hipSuccess) he = run();
+      if (he == hipSuccess) he = hipEventRecord(ev[2 * r + 1], stream);
+    }
+    if (he == hipSuccess) he = hipEventSynchronize(ev[2 * reps - 1]);
+    float total = 0.f;
+    for (int r = 0; r < reps && he == hipSuccess; ++r) {
+      float ms = 0.f;
+      he = hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]);
+      total += ms;
+    }
+    if (he != hipSuccess) break;
+    const float us = total * 1000.f / (float)reps;
+    if (best < 0 || us < best_us) {
+      best = (int)i;
+      best_us = us;
+    }
+  }
+  for (int e = 0; e < made; ++e) hipEventDestroy(ev[e]);
+  if (he != hipSuccess) return hip_status(he);
+  if (best < 0) return QG_ERR_UNSUPPORTED;
+  tuned_store(*w, m, cand[best]);
+  if (chosen && chosen_bytes) describe_variant(cand[best], L.is_mx, chosen, chosen_bytes);
+  if (chosen_us) *chosen_us = best_us;
+  return QG_OK;
+}
+
+extern "C" void qg_autotune_reset(void) {
+  std::lock_guard<std::mutex> lock(g_tune_mu);
+  g_tune.clear();
+}
+
 extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf,
                                           uint64_t buf_bytes) {
   Layout L;
@@ -771,13 +1031,6 @@ extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *b
   if (st != QG_OK) return st;
   if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
   const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
-  if (v.kind == 3)
-    snprintf(buf, buf_bytes, v.splits > 1 ? "a16_decode T=%d KR=%d W=%d splits=%d" : "a16_decode T=%d KR=%d W=%d",
-             v.T, v.KR, v.W, v.splits);
-  else if (v.kind == 1 || v.kind == 2)
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", L.is_mx ? "mx" : "a16", v.bm, v.tbn);
-  else
-    snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", L.is_mx ? "mx" : "a16", v.T,
-             v.KR, v.W, v.splits);
+  describe_variant(v, L.is_mx, buf, buf_bytes);
   return QG_OK;
 }

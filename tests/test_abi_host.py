@@ -22,7 +22,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_library_exports_every_declared_symbol():
     hdr = open(os.path.join(ROOT, "include", "qg.h")).read()
-    declared = set(re.findall(r"^(?:qg_status|const char \*|int32_t)\s*(qg_\w+)\(", hdr, re.M))
+    declared = set(re.findall(r"^(?:qg_status|const char \*|int32_t|void)\s*(qg_\w+)\(", hdr, re.M))
     assert declared == set(qg.EXPORTS)
     lib = ctypes.CDLL(qg.LIB_PATH)
     for name in declared:
@@ -384,3 +384,28 @@ def test_gemm_ex_flags_validated():
     # the invariant option sizes the large-M kernel's workspace at any M
     assert qg.gemm_workspace_size_ex(w, 1, qg.GEMM_BATCH_INVARIANT) > 0
     assert qg.gemm_workspace_size_ex(w, 1, 0) == qg.gemm_workspace_size(w, 1)
+
+
+def test_autotune_validates_before_launch():
+    w = _bound(qg.layer_desc(qg.W_UINT4, 256, 512, 128))
+    need = qg.gemm_autotune_workspace_size(w, 4)
+    assert need >= 16384
+    cases = [
+        (dict(reps=0), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(reps=65), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(m=0), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(x=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(ws=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(ws_bytes=100), qg.QG_ERR_BUFFER_TOO_SMALL),
+        (dict(ws=FAKE_DEV + 16), qg.QG_ERR_ALIGNMENT),
+        (dict(flush=FAKE_DEV + 4, flush_bytes=1 << 20), qg.QG_ERR_ALIGNMENT),
+        (dict(ldx=100), qg.QG_ERR_SHAPE),
+    ]
+    for kw, status in cases:
+        a = dict(x=FAKE_DEV, m=4, ldx=512, y=FAKE_DEV, ws=FAKE_DEV, ws_bytes=need, flush=None, flush_bytes=0, reps=3)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.gemm_autotune(w, a["x"], None, a["m"], a["ldx"], a["y"], qg.O_BF16, 256, a["ws"], a["ws_bytes"],
+                             a["flush"], a["flush_bytes"], a["reps"], stream=0)
+        assert e.value.status == status, kw
+    qg.autotune_reset()

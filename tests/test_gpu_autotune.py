@@ -1,0 +1,86 @@
+"""GPU tests of the dense autotune (qg_gemm_autotune): the fastest candidate
+is recorded for its (layer, M bucket), later qg_gemm calls in that bucket run
+it and still match the oracle, other buckets keep the heuristics, and
+qg_autotune_reset restores them.  The table is process-wide, so every test
+resets it when it ends."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_qg_amd as qg
+from gpu_harness import TOL_BF16, Acts, Layer, err, require_gpu, run_gemm, tol_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    qg.autotune_reset()
+    yield
+    qg.autotune_reset()
+
+
+def tune(layer, acts, m, flush=None, reps=4):
+    y = torch.empty((m, layer.n), dtype=torch.bfloat16, device="cuda")
+    wsb = qg.gemm_autotune_workspace_size(layer.w, m)
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")  # contents must not matter
+    fb = 0 if flush is None else flush.numel()
+    chosen, us = qg.gemm_autotune(layer.w, acts.x, acts.xs, m, layer.k, y, qg.O_BF16, layer.n, ws, wsb,
+                                  flush, fb, reps)
+    torch.cuda.synchronize()
+    return chosen, us
+
+
+@pytest.mark.parametrize("wtype,n,k,g,m", [(qg.W_UINT4, 4096, 14336, 128, 1), (qg.W_INT3, 2048, 4096, 128, 4),
+                                           (qg.W_MXFP4, 1024, 2048, 32, 200), (qg.W_INT4, 512, 1024, 64, 300)])
+def test_autotune_records_and_dispatches(wtype, n, k, g, m):
+    layer = Layer(wtype, n, k, g, seed=41)
+    acts = Acts(wtype == qg.W_MXFP4, m, k, seed=42)
+    other_m = 2000 if m < 1000 else 1
+    before_other = qg.describe_dispatch(layer.w, other_m)
+    flush = torch.empty(320 << 20, dtype=torch.uint8, device="cuda") if m == 1 else None
+    chosen, us = tune(layer, acts, m, flush)
+    print(f"  {wtype} N={n} K={k} M={m}: heuristic -> tuned {chosen} ({us:.2f} us)", flush=True)
+    assert us > 0
+    assert qg.describe_dispatch(layer.w, m) == chosen
+    assert qg.describe_dispatch(layer.w, other_m) == before_other  # another M bucket keeps the heuristics
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(layer.mx))):
+        y = run_gemm(layer, acts, m, otype)
+        e = err(y, oracle.gemm(acts.xdq, layer.wdq()))
+        assert e <= tol, (otype, e)
+    qg.autotune_reset()
+    assert qg.describe_dispatch(layer.w, other_m) == before_other
+
+
+def test_autotune_entry_serves_its_bucket_only_when_valid():
+    # a decode-kernel entry tuned at M = 1 (bucket "1") is not used for M = 2
+    # (bucket "2-4"); tuning M = 3 gives that bucket its own entry
+    layer = Layer(qg.W_UINT4, 4096, 4096, 128, seed=43)
+    acts = Acts(False, 4, 4096, seed=44)
+    h2 = qg.describe_dispatch(layer.w, 2)
+    a1 = Acts(False, 1, 4096, seed=45)
+    c1, _ = tune(layer, a1, 1)
+    assert qg.describe_dispatch(layer.w, 1) == c1
+    assert qg.describe_dispatch(layer.w, 2) == h2
+    c3, _ = tune(layer, acts, 3)
+    assert qg.describe_dispatch(layer.w, 2) == c3 and qg.describe_dispatch(layer.w, 4) == c3
+    y = run_gemm(layer, acts, 4, qg.O_F32)
+    assert err(y, oracle.gemm(acts.xdq, layer.wdq())) <= tol_f32(False)
+
+
+def test_batch_invariant_ignores_the_table():
+    layer = Layer(qg.W_INT4, 384, 1024, 128, seed=46)
+    acts = Acts(False, 64, 1024, seed=47)
+
+    def inv():
+        y = torch.empty((64, 384), dtype=torch.float32, device="cuda")
+        wsb = qg.gemm_workspace_size_ex(layer.w, 64, qg.GEMM_BATCH_INVARIANT)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        qg.gemm_ex(layer.w, acts.x, None, 64, 1024, y, qg.O_F32, 384, ws, wsb, qg.GEMM_BATCH_INVARIANT)
+        torch.cuda.synchronize()
+        return y.cpu()
+    before = inv()
+    tune(layer, acts, 64)
+    assert torch.equal(inv(), before)
