@@ -53,7 +53,7 @@ static bool env_variant(Variant *v) {
 // (T, KR) = (4, 2) for the integer formats, T * KR <= 8 but not (4, 4) for MX.
 static bool variant_ok(const qg_layer_desc &d, int T, int KR) {
   if ((T != 1 && T != 2 && T != 4) || (KR != 1 && KR != 2 && KR != 4)) return false;
-  if (d.wtype == QG_W_MXFP4) return T * KR <= 8 && !(T == 4 && KR == 4);
+  if (mx_a8(d)) return T * KR <= 8 && !(T == 4 && KR == 4);
   return T * KR <= 4 || (T == 4 && KR == 2);
 }
 
@@ -71,7 +71,7 @@ static int clamp_kr(const qg_layer_desc &d, int T, int kr) {
 // (which costs a partials round trip and a counter-clearing launch) unless N
 // alone gives too few workgroups.
 static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles) {
-  const bool mx = d.wtype == QG_W_MXFP4;
+  const bool mx = mx_a8(d);
   // T x KR per wave: 4 x 2 (integer formats), 2 x 4 (MX); fewer for short K.
   // Measured on the decode shapes: fewer, fuller workgroups beat more, emptier
   // ones (224 workgroups of 8 KB waves beat 448 of 4 KB), so T shrinks only
@@ -137,10 +137,10 @@ static int mx_tile_cols(int64_t n, int64_t m, int bm) {
 }
 
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
-  if (w.desc.k % 128 != 0) return false;
+  if (w.desc.k % 128 != 0 || fp4_a16(w.desc)) return false;
   const char *s = getenv("QG_TILED");
   if (s && *s == '0') return false;
-  const bool mx = w.desc.wtype == QG_W_MXFP4;
+  const bool mx = mx_a8(w.desc);
   // the integer-format kernel addresses X and the codes with 32-bit offsets
   if (!mx && ((uint64_t)m * w.desc.k * 2 >= (1ull << 31) ||
               (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31)))
@@ -188,7 +188,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
 
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
-  if (d.wtype == QG_W_MXFP4 || m < 1 || m > 16 || d.k % 512 != 0) return false;
+  if (mx_a8(d) || fp4_a16(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
   const char *e = getenv("QG_DECODE");
   if (e && *e == '0') return false;
   int T, KR, S = 1;
@@ -222,8 +222,8 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
 // variant fixed by (N, K) sums its waves' and splits' partials in index order.
 // Tile widths do not change any element's order; they are fixed anyway.
 static Variant select_dense_invariant(const qg_weight &w) {
-  const bool mx = w.desc.wtype == QG_W_MXFP4;
-  if (w.desc.k % 128 == 0 && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
+  const bool mx = mx_a8(w.desc);
+  if (w.desc.k % 128 == 0 && !fp4_a16(w.desc) && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
     const int bn = mx ? 256 : a16_tiled_bn();
     return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
   }
@@ -263,7 +263,7 @@ static bool same_variant(const Variant &a, const Variant &b) {
 // Whether v can serve m rows of w (a table entry serves every M of its bucket)
 static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
   const qg_layer_desc &d = w.desc;
-  const bool mx = d.wtype == QG_W_MXFP4;
+  const bool mx = mx_a8(d);
   switch (v.kind) {
     case 0:
       return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 && covers(v, w.k_blocks);
@@ -271,12 +271,12 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
       return mx && d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) &&
              (v.tbn == 256 || (mx_tiled_waves() == 8 && (v.tbn == 192 || v.tbn == 224)));
     case 2:
-      return !mx && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
+      return !mx && !fp4_a16(d) && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
              (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31) &&
              ((v.bm == 128 && v.tbn == 256 && a16_tiled_waves() == 8) || ((v.bm == 128 || v.bm == 256) && v.tbn == 128));
     case 3: {
       Variant t;
-      return !mx && m >= 1 && m <= 16 && d.k % 512 == 0 && decode_fits(w, m, v.T, v.KR, v.splits, &t) && t.W == v.W;
+      return !mx && !fp4_a16(d) && m >= 1 && m <= 16 && d.k % 512 == 0 && decode_fits(w, m, v.T, v.KR, v.splits, &t) && t.W == v.W;
     }
   }
   return false;
@@ -342,7 +342,7 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
   if (s.splits > 1) {
     // long K: the deepest spill-free wave (KR = 4), T reduced to fit
     s.KR = 4;
-    s.T = w.desc.wtype == QG_W_MXFP4 ? 2 : 1;
+    s.T = mx_a8(w.desc) ? 2 : 1;
     s.W = std::min(16, (w.k_blocks + s.KR - 1) / s.KR);
     s.splits = 1;
   }
@@ -357,8 +357,8 @@ static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
-  if (d.k % 128 != 0 || d.num_experts > kMaxExperts) return 0;
-  const bool mx = d.wtype == QG_W_MXFP4;
+  if (d.k % 128 != 0 || d.num_experts > kMaxExperts || fp4_a16(d)) return 0;  // skinny kernel only
+  const bool mx = mx_a8(d);
   // 32-bit offsets inside the kernels
   if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
       (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31))
@@ -448,7 +448,7 @@ static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_c
   if (min_rows <= 0) return 0;
   uint64_t b = moe_list_bytes(moe_tiles_cap(w, pairs, min_rows));
   if (moe_small_tiles(w, pairs, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
-  if (w.desc.wtype != QG_W_MXFP4) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
+  if (!mx_a8(w.desc)) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
   return b;
 }
 
@@ -563,7 +563,7 @@ extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
   hipError_t he = hipHostMalloc(&stage, stage_bytes, hipHostMallocDefault);
   if (he != hipSuccess) return hip_status(he);
   uint64_t cb = (uint64_t)desc->n * desc->k * L.bits / 8;
-  uint64_t sb = (uint64_t)desc->n * (desc->k / desc->group_size) * (L.is_mx ? 1 : 2);
+  uint64_t sb = (uint64_t)desc->n * (desc->k / desc->group_size) * ((L.is_mx || L.fp4) ? 1 : 2);  // e8m0 / bf16
   uint64_t zb = L.has_zp ? (uint64_t)desc->n * (desc->k / desc->group_size) : 0;
   qg_status result = QG_OK;
   for (int64_t e0 = 0; e0 < expert_count; e0 += (int64_t)chunk_experts) {
@@ -872,7 +872,7 @@ static void describe_variant(const Variant &v, bool mx, char *buf, uint64_t buf_
 // (K % 128 == 0).
 static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> *out) {
   const qg_layer_desc &d = w.desc;
-  const bool mx = d.wtype == QG_W_MXFP4;
+  const bool mx = mx_a8(d);
   auto add = [&](const Variant &v) {
     for (const Variant &u : *out)
       if (same_variant(u, v)) return;

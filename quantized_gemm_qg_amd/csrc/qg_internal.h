@@ -45,6 +45,12 @@
 
 namespace qg {
 
+// MXFP4 weights with MXFP8 activations run the MX kernels (codes straight
+// into the scaled MFMA); with bf16 activations they run the integer-format
+// skinny kernel, the codes dequantized to exact bf16 by the fp4 conversion.
+inline bool mx_a8(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_MXFP8; }
+inline bool fp4_a16(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_BF16; }
+
 constexpr int kTileN = 16;    // N per tile
 constexpr int kBlockK = 128;  // K per block
 
@@ -56,7 +62,8 @@ struct Layout {
   int kb_pad = 0;         // k_blocks rounded up to 4
   int bits = 0;
   bool has_zp = false;
-  bool is_mx = false;
+  bool is_mx = false;     // MX kernels (MXFP4 x MXFP8)
+  bool fp4 = false;       // MXFP4 weights x bf16 activations (integer-format layout, bf16 scales)
   uint64_t block_bytes = 0;
   uint64_t codes_bytes = 0;
   uint64_t scales_offset = 0;

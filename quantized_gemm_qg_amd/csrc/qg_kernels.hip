@@ -165,11 +165,15 @@ struct NoHook {
 // lane group q).  ER = 1 serves a single-row tile (only row 0 is stored);
 // rows past the tile read a valid row, so the extra work of ER = 4 on them is
 // finite and never stored.
+// FP4: the codes are e2m1 in standard order (group 32, no zero point) and the
+// scales bf16 powers of two; each MFMA operand is the exact bf16 e2m1 x scale
+// from the fp4 -> bf16 conversion, so the MFMA accumulates into acc directly.
 template <int BITS, bool ZP, int GROUP, int T, int KR, bool XL = false, int ER = 4,
-          typename Hook = NoHook>
+          typename Hook = NoHook, bool FP4 = false>
 __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
                                          const uint16_t *xrow, int nt0, int kb0, f32x4 (&acc)[T],
                                          Hook after_issue = Hook(), int xk0 = 0) {
+  static_assert(!FP4 || (BITS == 4 && !ZP && GROUP == 32), "fp4 codes: 4-bit, group 32, no zero point");
   constexpr int LB = BITS == 4 ? 16 : 12;    // packed bytes per lane per block
   constexpr int BB = 64 * LB;                // packed bytes per block
   constexpr int JPG = GROUP / 32;            // MFMAs per K-group
@@ -276,6 +280,30 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
     u32x4 xk[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xk[j] = XL ? xfrag(kb, j) : xf[XL ? 0 : kb][j];
+    if constexpr (FP4) {
+      // one K-group per MFMA: operand = e2m1 x 2^(e - 127), exact in bf16.
+      // The conversion takes its scale as a power of two (a 0.0 scale acts as
+      // 2^-127), so a padding group's zero scale does not zero the operand:
+      // k-blocks past K (clamped re-reads of the last block, against
+      // activations clamped to k = 0) are skipped instead (wave-uniform);
+      // padding inside the last block holds code 0, which converts to 0.
+      if (kb0 + kb >= kbs) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = kb * GPB + j;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+          const uint32_t wd = wq[t][kb][j];
+          const u32x4 b = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 0)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 2)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, s, 3))};
+          c[t] = mfma_bf16(xk[j], b, c[t]);
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int gi = 0; gi < GPB; ++gi) {
       // 4. group row sums of X on the matrix core (B = all ones)
@@ -381,7 +409,8 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
 template <int FMT, int GROUP, int T, int KR>
 __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int moe,
                                                                 int64_t total_items_dense) {
-  // FMT: 0 INT4 sym, 1 INT4 + zp, 2 INT3 sym, 3 INT3 + zp, 4 MXFP4 x MXFP8
+  // FMT: 0 INT4 sym, 1 INT4 + zp, 2 INT3 sym, 3 INT3 + zp, 4 MXFP4 x MXFP8,
+  // 5 MXFP4 x bf16
   extern __shared__ float red[];  // [waves][T][256]: sized by the launcher
   __shared__ int prefix[kMaxExperts + 1];
   __shared__ int last_flag;
@@ -431,9 +460,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
         mx_wave<T, KR>(a, wexp, xrow, xsrow, nt0, kb0, acc, prefetch_next);
       } else {
         const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
-        constexpr int BITS = (FMT <= 1) ? 4 : 3;
+        constexpr int BITS = (FMT <= 1 || FMT == 5) ? 4 : 3;
         constexpr bool ZP = (FMT == 1 || FMT == 3);
-        a16_wave<BITS, ZP, GROUP, T, KR>(a, wexp, xrow, nt0, kb0, acc, prefetch_next);
+        a16_wave<BITS, ZP, GROUP, T, KR, false, 4, decltype(prefetch_next), FMT == 5>(a, wexp, xrow, nt0, kb0, acc,
+                                                                                     prefetch_next);
       }
     } else {
       prefetch_next();
@@ -764,8 +794,8 @@ static hipError_t launch_skinny(const GemmArgs &a, const Variant &v, bool moe, i
 template <int FMT>
 static hipError_t launch_fmt(const GemmArgs &a, int group, const Variant &v, bool moe,
                              int64_t grid, int64_t items, hipStream_t s) {
-  if constexpr (FMT == 4) {
-    return launch_skinny<4, 32>(a, v, moe, grid, items, s);
+  if constexpr (FMT >= 4) {
+    return group == 32 ? launch_skinny<FMT, 32>(a, v, moe, grid, items, s) : hipErrorInvalidValue;
   } else {
     switch (group) {
       case 32: return launch_skinny<FMT, 32>(a, v, moe, grid, items, s);
@@ -782,7 +812,7 @@ static int fmt_of(const qg_layer_desc &d) {
     case QG_W_UINT4: return 1;
     case QG_W_INT3: return 2;
     case QG_W_UINT3: return 3;
-    default: return 4;
+    default: return fp4_a16(d) ? 5 : 4;
   }
 }
 
@@ -795,6 +825,7 @@ static hipError_t launch_any(const GemmArgs &a, const qg_layer_desc &d, const Va
     case 1: return launch_fmt<1>(a, d.group_size, v, moe, grid, items, s);
     case 2: return launch_fmt<2>(a, d.group_size, v, moe, grid, items, s);
     case 3: return launch_fmt<3>(a, d.group_size, v, moe, grid, items, s);
+    case 5: return launch_fmt<5>(a, d.group_size, v, moe, grid, items, s);
     default: return launch_fmt<4>(a, d.group_size, v, moe, grid, items, s);
   }
 }

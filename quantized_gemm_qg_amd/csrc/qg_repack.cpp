@@ -30,10 +30,12 @@ qg_status make_layout(const qg_layer_desc *d, Layout *out) {
     L.bits = (d->wtype == QG_W_INT4 || d->wtype == QG_W_UINT4) ? 4 : 3;
     L.has_zp = (d->wtype == QG_W_UINT4 || d->wtype == QG_W_UINT3);
   } else {
-    if (d->stype != QG_S_E8M0 || d->atype != QG_A_MXFP8 || d->group_size != 32)
-      return QG_ERR_UNSUPPORTED;
+    if (d->stype != QG_S_E8M0 || d->group_size != 32) return QG_ERR_UNSUPPORTED;
     L.bits = 4;
-    L.is_mx = true;
+    // MXFP8 activations: the MX layout; bf16 activations: the 4-bit integer
+    // layout with each e8m0 scale stored as its (exact) bf16 power of two
+    L.is_mx = d->atype == QG_A_MXFP8;
+    L.fp4 = d->atype == QG_A_BF16;
   }
   L.n_tiles = (int)((d->n + kTileN - 1) / kTileN);
   L.k_blocks = (int)((d->k + kBlockK - 1) / kBlockK);
@@ -71,10 +73,14 @@ static inline uint32_t read_bits(const uint8_t *row, uint64_t bitpos, int bits) 
   return v;
 }
 
+// fp4: e2m1 codes keep their standard order inside the dword (byte i = codes
+// 2i, 2i + 1, low nibble first: the order the fp4 -> bf16 pair conversion
+// produces its two values in); integer codes go to the nibble slots above.
 static void repack_codes_int4(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
                               uint8_t *dst) {
   const uint64_t row_bytes = (uint64_t)d.k / 2;
   const uint32_t flip = (d.wtype == QG_W_INT4) ? 0x88888888u : 0u;
+  const bool natural = L.fp4;
   for (int64_t n = 0; n < d.n; ++n) {
     const uint8_t *row = codes + n * row_bytes;
     const int t = (int)(n / kTileN), ln = (int)(n % kTileN);
@@ -83,8 +89,12 @@ static void repack_codes_int4(const qg_layer_desc &d, const Layout &L, const uin
       uint32_t w;
       memcpy(&w, row + k0 / 2, 4);
       uint32_t out = 0;
-      for (int e = 0; e < 8; ++e) out |= ((w >> (4 * e)) & 15u) << (4 * slot_of(e));
-      out ^= flip;
+      if (natural) {
+        out = w;
+      } else {
+        for (int e = 0; e < 8; ++e) out |= ((w >> (4 * e)) & 15u) << (4 * slot_of(e));
+        out ^= flip;
+      }
       const int kb = (int)(k0 / kBlockK), kk = (int)(k0 % kBlockK);
       const int j = kk / 32, q = (kk % 32) / 8;
       const int lane = ln + 16 * q;
@@ -159,8 +169,18 @@ void repack_expert(const qg_layer_desc &d, const Layout &L, const uint8_t *codes
     repack_codes_int4(d, L, codes, dst);
   else
     repack_codes_int3(d, L, codes, dst);
-  const uint16_t *s16 = (const uint16_t *)scales;
   uint16_t *ds = (uint16_t *)(dst + L.scales_offset);
+  if (L.fp4) {
+    // e8m0 code c -> bf16 2^(c - 127): exponent field c (c = 0: the subnormal
+    // 2^-127 = mantissa bit 6; c = 255: NaN)
+    for (int64_t n = 0; n < d.n; ++n)
+      for (int g = 0; g < L.groups; ++g) {
+        const uint8_t c = scales[n * L.groups + g];
+        ds[n * L.groups_padded + g] = c == 0 ? 0x0040 : c == 255 ? 0x7FC0 : (uint16_t)(c << 7);
+      }
+    return;
+  }
+  const uint16_t *s16 = (const uint16_t *)scales;
   for (int64_t n = 0; n < d.n; ++n)
     for (int g = 0; g < L.groups; ++g) ds[n * L.groups_padded + g] = s16[n * L.groups + g];
   if (L.has_zp) {
@@ -176,7 +196,7 @@ void repack_expert(const qg_layer_desc &d, const Layout &L, const uint8_t *codes
 static void std_sizes(const qg_layer_desc &d, const Layout &L, uint64_t *codes, uint64_t *scales,
                       uint64_t *zeros) {
   *codes = (uint64_t)d.n * d.k * L.bits / 8;
-  *scales = (uint64_t)d.n * (d.k / d.group_size) * (L.is_mx ? 1 : 2);
+  *scales = (uint64_t)d.n * (d.k / d.group_size) * ((L.is_mx || L.fp4) ? 1 : 2);
   *zeros = L.has_zp ? (uint64_t)d.n * (d.k / d.group_size) : 0;
 }
 

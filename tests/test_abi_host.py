@@ -42,7 +42,7 @@ def _desc(**kw):
     (dict(n=0), qg.QG_ERR_SHAPE),
     (dict(group_size=256, k=512), qg.QG_ERR_UNSUPPORTED),
     (dict(atype=qg.A_MXFP8), qg.QG_ERR_UNSUPPORTED),     # INT4 x MXFP8: no kernel
-    (dict(wtype=qg.W_MXFP4, group_size=32, atype=qg.A_BF16), qg.QG_ERR_UNSUPPORTED),
+    (dict(wtype=qg.W_MXFP4, group_size=64, atype=qg.A_BF16), qg.QG_ERR_UNSUPPORTED),
     (dict(wtype=qg.W_MXFP4, group_size=128), qg.QG_ERR_UNSUPPORTED),
     (dict(stype=qg.S_E8M0), qg.QG_ERR_UNSUPPORTED),
     (dict(wtype=9), qg.QG_ERR_INVALID_ARGUMENT),
@@ -409,3 +409,33 @@ def test_autotune_validates_before_launch():
                              a["flush"], a["flush_bytes"], a["reps"], stream=0)
         assert e.value.status == status, kw
     qg.autotune_reset()
+
+
+def test_repack_fp4_bf16_layout():
+    """MXFP4 weights for bf16 activations: e2m1 codes in the 4-bit integer
+    lane order with standard nibble order, e8m0 scales stored as bf16 powers
+    of two (read back here by an independent decoder of that layout)."""
+    n, k = 40, 384
+    desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_BF16)
+    codes_std, sc, raw = synth.mx_weights(synth.rng(3, 1), n, k)
+    sc = sc.copy()
+    sc[0, 0], sc[1, 1] = 0, 255  # the subnormal and NaN codes
+    dst = np.zeros(qg.packed_size(desc), np.uint8)
+    qg.repack_host(desc, codes_std, sc, None, dst)
+    w = _bound(desc)
+    kbs, gp = w.k_blocks, w.groups_padded
+    for nn in range(n):
+        t, ln = divmod(nn, 16)
+        for kk in range(k):
+            kb, r = divmod(kk, 128)
+            j, q, e = r // 32, (r % 32) // 8, kk % 8
+            lane = ln + 16 * q
+            off = (t * kbs + kb) * 1024 + lane * 16 + 4 * j
+            dword = int.from_bytes(dst[off:off + 4].tobytes(), "little")
+            assert (dword >> (4 * e)) & 15 == raw[nn, kk], (nn, kk)
+    s16 = dst[w.scales_offset:w.scales_offset + w.n_tiles * 16 * gp * 2].view(np.uint16).reshape(-1, gp)
+    for nn in range(n):
+        for g in range(k // 32):
+            c = int(sc[nn, g])
+            expect = 0x0040 if c == 0 else 0x7FC0 if c == 255 else c << 7
+            assert s16[nn, g] == expect, (nn, g)

@@ -1,0 +1,97 @@
+"""GPU parity of MXFP4 weights x bf16 activations (e2m1 codes, e8m0 scale per
+32 along K, bf16 activations) through the C ABI against the CPU oracle.
+
+The kernels turn each code into the exact bf16 value e2m1 x 2^(e - 127) and
+run the bf16 MFMA on it, so the fp32 accumulators meet the integer formats'
+1e-5 normwise bound and one-hot rows return the dequantized weights bit for
+bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_gemm_qg_amd as qg
+import synth
+from gpu_harness import TOL_BF16, TOL_F32, Acts, require_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+class Fp4Layer:
+    def __init__(self, n, k, seed, experts=1):
+        self.n, self.k, self.experts = n, k, experts
+        self.desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_BF16, num_experts=experts)
+        self.buf = torch.empty(qg.packed_size(self.desc), dtype=torch.uint8, device="cuda")
+        self.std = []
+        for e in range(experts):
+            codes, sc, _ = synth.mx_weights(synth.rng(seed, 500 + e), n, k)
+            self.std.append((codes, sc))
+            self.w = qg.preprocess(self.desc, codes, sc, None, self.buf, expert_begin=e, expert_count=1)
+
+    def wdq(self, e=0):
+        codes, sc = self.std[e]
+        return oracle.dequant_weights(qg.W_MXFP4, codes, sc, None, self.k, 32)
+
+
+def run(layer, x, m, otype):
+    y = torch.empty((m, layer.n), dtype=torch.float32 if otype == qg.O_F32 else torch.bfloat16, device="cuda")
+    wsb = qg.gemm_workspace_size(layer.w, m)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    qg.gemm(layer.w, x, None, m, layer.k, y, otype, layer.n, ws, wsb)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 256, 512), (1, 200, 640), (37, 136, 544), (300, 264, 1024),
+                                   (4, 4096, 14336), (1, 14336, 4096)])
+def test_fp4_bf16_dense(m, n, k):
+    layer = Fp4Layer(n, k, seed=m + n)
+    acts = Acts(False, m, k, seed=k)
+    print(f"  M={m} N={n} K={k}: {qg.describe_dispatch(layer.w, m)}", flush=True)
+    assert "a16_skinny" in qg.describe_dispatch(layer.w, m)
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
+        e = oracle.normwise_error(run(layer, acts.x, m, otype), yref)
+        assert e <= tol, (otype, e)
+
+
+def test_fp4_bf16_identity_rows_exact():
+    n, k, m = 136, 640, 16
+    layer = Fp4Layer(n, k, seed=5)
+    wdq = layer.wdq()
+    for c0 in range(0, k, 16 * 8):
+        bits = np.zeros((m, k), np.uint16)
+        cols = c0 + np.arange(m) * 7 % 128
+        bits[np.arange(m), cols] = 0x3F80
+        y = run(layer, to_dev(bits), m, qg.O_F32)
+        for i in range(m):
+            ref = wdq[:, cols[i]]
+            bad = np.nonzero(y[i] != ref)[0]
+            assert bad.size == 0, (c0, i, bad.size, bad[:4].tolist(), y[i][bad[:4]].tolist(), ref[bad[:4]].tolist(),
+                                   float(np.max(np.abs(y[i] - ref))))
+
+
+def test_fp4_bf16_moe():
+    experts, topk, t, n, k = 8, 2, 40, 256, 512
+    layer = Fp4Layer(n, k, seed=7, experts=experts)
+    r = synth.rng(8, 0)
+    ids = synth.route(r, t, experts, topk)
+    acts = Acts(False, t, k, seed=9)
+    d_ids = to_dev(ids.astype(np.int32))
+    sorted_ids = torch.empty(t * topk, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
+    wsb = qg.moe_workspace_size(layer.w, t, topk)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    qg.moe_sort(d_ids, t, topk, experts, sorted_ids, offsets, ws, wsb)
+    y = torch.empty((t * topk, n), dtype=torch.float32, device="cuda")
+    qg.moe_gemm(layer.w, acts.x, None, qg.ROWS_BY_TOKEN, sorted_ids, offsets, t, topk, y, qg.O_F32,
+                qg.ROWS_BY_PAIR, ws, wsb)
+    torch.cuda.synchronize()
+    yref = oracle.moe_gemm(layer.wdq, acts.xdq, ids, rows_by_token=True)
+    e = oracle.normwise_error(y.cpu().numpy().astype(np.float64), yref)
+    assert e <= TOL_F32, e
