@@ -531,6 +531,29 @@ def main():
                         "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "dispatch": qg.describe_dispatch(L.ws[0], mm)}
             print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
+        # MXFP4 weights x bf16 activations at the decode shapes
+        for i, (n, k) in enumerate(shapes):
+            r = synth.rng(70 + i, 1)
+            codes, sc, _ = synth.mx_weights(r, n, k)
+            desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_BF16)
+            size = qg.packed_size(desc)
+            bufs = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
+            wts = [qg.preprocess(desc, codes, sc, None, b) for b in bufs]
+            wbytes = weight_bytes(n, k, 4, 32, False, 1)
+            for mm in (1, 16):
+                x, _, _ = make_x(qg, synth, torch, False, mm, k, seed=40 + mm)
+                y = torch.empty((mm, n), dtype=torch.bfloat16, device="cuda")
+                wsb = qg.gemm_workspace_size(wts[0], mm)
+                wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+                stream = torch.cuda.current_stream().cuda_stream
+                t = timed(torch, lambda j: qg.gemm(wts[j % ROTATE], x, None, mm, k, y, qg.O_BF16, n, wsp, wsb, stream),
+                          100, 10)
+                extra[f"mxfp4_bf16_M{mm}_N{n}_K{k}"] = {
+                    "us": round(t * 1e3, 2), "weight_GBs": round(wbytes / (t * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(wbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "dispatch": qg.describe_dispatch(wts[0], mm)}
+            del bufs, wts
+        print(f"[bench] extra MXFP4 x bf16 decode done", file=sys.stderr, flush=True)
         # the batch-invariant compute option at decode sizes (one kernel for every M)
         for i, (n, k) in enumerate(shapes):
             L = layers[i]
