@@ -328,6 +328,25 @@ def bench_large_m(qg, synth, torch):
             "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
         print(f"[bench] extra w4a16 N={n} K={k}: {extra[f'w4a16_int4_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
         del L
+    # MXFP4 weights x bf16 activations (tiled kernel, exact bf16 operands)
+    n, k = 14336, 4096
+    codes, sc, _ = synth.mx_weights(synth.rng(80, 1), n, k)
+    desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_BF16)
+    bufs = [torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    wts = [qg.preprocess(desc, codes, sc, None, b) for b in bufs]
+    x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=81)
+    y = torch.empty((4096, n), dtype=torch.bfloat16, device="cuda")
+    wsb = qg.gemm_workspace_size(wts[0], 4096)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    t = timed(torch, lambda i: qg.gemm(wts[i % 2], x, None, 4096, k, y, qg.O_BF16, n, ws, wsb, stream), 40, 10)
+    fl = 2.0 * 4096 * n * k
+    extra[f"mxfp4_bf16_M4096_N{n}_K{k}"] = {
+        "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+        "bf16_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+        "dispatch": qg.describe_dispatch(wts[0], 4096)}
+    print(f"[bench] extra mxfp4 x bf16: {extra[f'mxfp4_bf16_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
+    del bufs, wts
     for n in (3072, 14336):
         L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
         x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)

@@ -137,7 +137,7 @@ static int mx_tile_cols(int64_t n, int64_t m, int bm) {
 }
 
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
-  if (w.desc.k % 128 != 0 || fp4_a16(w.desc)) return false;
+  if (w.desc.k % 128 != 0) return false;
   const char *s = getenv("QG_TILED");
   if (s && *s == '0') return false;
   const bool mx = mx_a8(w.desc);
@@ -223,7 +223,7 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
 // Tile widths do not change any element's order; they are fixed anyway.
 static Variant select_dense_invariant(const qg_weight &w) {
   const bool mx = mx_a8(w.desc);
-  if (w.desc.k % 128 == 0 && !fp4_a16(w.desc) && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
+  if (w.desc.k % 128 == 0 && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
     const int bn = mx ? 256 : a16_tiled_bn();
     return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
   }
@@ -271,7 +271,7 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
       return mx && d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) &&
              (v.tbn == 256 || (mx_tiled_waves() == 8 && (v.tbn == 192 || v.tbn == 224)));
     case 2:
-      return !mx && !fp4_a16(d) && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
+      return !mx && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
              (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31) &&
              ((v.bm == 128 && v.tbn == 256 && a16_tiled_waves() == 8) || ((v.bm == 128 || v.bm == 256) && v.tbn == 128));
     case 3: {

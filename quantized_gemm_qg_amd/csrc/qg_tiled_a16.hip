@@ -145,10 +145,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
+// FP4: MXFP4 weights x bf16 activations (e2m1 codes in standard nibble order,
+// group 32, bf16 power-of-two scales): each B operand is the exact bf16
+// e2m1 x scale from the fp4 conversion, so the MFMAs accumulate straight into
+// the output accumulators (no group row sums, no per-group FMA).
+template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE, bool FP4 = false>
 __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, const float *xs,
                                                                  int xs_rows) {
   using C = A16Cfg<BM, BN, WM, WN, BITS, ZP, GROUP>;
+  static_assert(!FP4 || (C::M32 && BITS == 4 && !ZP && GROUP == 32), "fp4 codes: 32 x 32 tiles, group 32");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,9 +198,9 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
   const int ncol = min(nt0 * 16 + 64 * (wave % C::SS_PIECES) + lane, a.n_tiles * 16 - 1);
   const uint8_t *ss_src = wexp + a.scales_offset + (uint64_t)ncol * gp * 2;
   const uint32_t *sz_src = (const uint32_t *)(wexp + a.zeros_offset) + (uint64_t)ncol * (gp >> 3);
-  const bool sx_wave = wave < C::SX_WAVES, ss_wave = wave < C::SS_PIECES;
+  const bool sx_wave = !FP4 && wave < C::SX_WAVES, ss_wave = wave < C::SS_PIECES;  // FP4: no row sums
   const int sx_row = 64 * (sx_wave ? wave : 0) + lane;
-  const float *sx_src = xs + tr.x(a, sx_row);
+  const float *sx_src = FP4 ? xs : xs + tr.x(a, sx_row);
 
   auto issue_a = [&](int kb) {
     uint8_t *st = smem + (kb % C::NA) * C::A_STAGE;
@@ -281,11 +286,44 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
             v[hh] = u32x4{p[0], p[1], p[2], 0u};
           }
         }
+        if constexpr (FP4) {
+          // dword jj of both slots holds K-group kb * GPB + jj of column col
+          const int col = wn * 32 * C::NB2 + 32 * j + c32;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          bw[j][2 * jj] = unpack_br<BITS>(v[0], jj, umask, umagic);
-          bw[j][2 * jj + 1] = unpack_br<BITS>(v[1], jj, umask, umagic);
+          for (int jj = 0; jj < 4; ++jj) {
+            const int gg = kb * C::GPB + jj;
+            const float sc = bf16_bits_to_f32(*(const uint16_t *)(sb + C::OFF_SS + col * 16 + 2 * (gg & 7)));
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint32_t wd = v[hh][jj];
+              bw[j][2 * jj + hh] =
+                  u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2)),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 3))};
+            }
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            bw[j][2 * jj] = unpack_br<BITS>(v[0], jj, umask, umagic);
+            bw[j][2 * jj + 1] = unpack_br<BITS>(v[1], jj, umask, umagic);
+          }
         }
+      }
+      if constexpr (FP4) {
+#pragma unroll
+        for (int i = 0; i < C::MB2; ++i) {
+          const int r0 = wm * (BM / WM) + 32 * i;
+          const uint8_t *arow = st + (r0 + c32) * 256;
+#pragma unroll
+          for (int mm = 0; mm < 8; ++mm) {
+            const u32x4 af = *(const u32x4 *)(arow + 16 * ((2 * mm + h) ^ (c32 & 15)));
+#pragma unroll
+            for (int j = 0; j < C::NB2; ++j) acc32[i][j] = mfma32_bf16(af, bw[j][mm], acc32[i][j]);
+          }
+        }
+        continue;
       }
 #pragma unroll
       for (int gi = 0; gi < C::GPB; ++gi) {
@@ -442,13 +480,13 @@ __global__ __launch_bounds__(256) void group_sums_kernel(const uint16_t *x, int6
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE>
+template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE, bool FP4 = false>
 static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t tiles_cap, float *xs,
                                      bool sums, hipStream_t s) {
   using C = A16Cfg<BM, BN, WM, WN, BITS, ZP, GROUP>;
   static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MI, C::NJ>(), "epilogue LDS");
   hipError_t e;
-  if (sums) {
+  if (sums && !FP4) {
     const float factor = ZP ? 1.f : -(1.f + (float)C::ZSYM / C::MAG);
     const int64_t rows_blocks = (xs_rows + 3) / 4;
     hipLaunchKernelGGL(group_sums_kernel<GROUP>, dim3((unsigned)rows_blocks), dim3(256), 0, s,
@@ -461,7 +499,7 @@ static hipError_t launch_a16_tiled_t(const GemmArgs &a, int64_t xs_rows, int64_t
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  auto kern = a16_tiled_kernel<BM, BN, WM, WN, BITS, ZP, GROUP, MOE>;
+  auto kern = a16_tiled_kernel<BM, BN, WM, WN, BITS, ZP, GROUP, MOE, FP4>;
   e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(64 * C::WAVES), lds, s, a,
@@ -489,6 +527,12 @@ static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t 
     case QG_W_UINT4: return launch_group<BM, BN, WM, WN, 4, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_INT3: return launch_group<BM, BN, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_UINT3: return launch_group<BM, BN, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_MXFP4:
+      // MXFP4 x bf16: dense tiles of 32 x 32 wave blocks only
+      if constexpr (!MOE && WM > 1 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0) {
+        if (fp4_a16(d) && g == 32) return launch_a16_tiled_t<BM, BN, WM, WN, 4, false, 32, false, true>(a, xs_rows, cap, xs, false, s);
+      }
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

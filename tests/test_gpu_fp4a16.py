@@ -53,7 +53,7 @@ def test_fp4_bf16_dense(m, n, k):
     layer = Fp4Layer(n, k, seed=m + n)
     acts = Acts(False, m, k, seed=k)
     print(f"  M={m} N={n} K={k}: {qg.describe_dispatch(layer.w, m)}", flush=True)
-    assert "a16_skinny" in qg.describe_dispatch(layer.w, m)
+    assert ("a16_tiled" if m >= 256 and k % 128 == 0 else "a16_skinny") in qg.describe_dispatch(layer.w, m)
     yref = oracle.gemm(acts.xdq, layer.wdq())
     for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
         e = oracle.normwise_error(run(layer, acts.x, m, otype), yref)
@@ -95,3 +95,53 @@ def test_fp4_bf16_moe():
     yref = oracle.moe_gemm(layer.wdq, acts.xdq, ids, rows_by_token=True)
     e = oracle.normwise_error(y.cpu().numpy().astype(np.float64), yref)
     assert e <= TOL_F32, e
+
+
+@pytest.mark.parametrize("tile", ["128x256", "256x128", "128x128"])
+def test_fp4_bf16_tiled_shapes(monkeypatch, tile):
+    """The LDS-tiled kernel (M >= 256) at each dense tile shape, with partial
+    row and column tiles."""
+    bm, bn = tile.split("x")
+    monkeypatch.setenv("QG_TILED_BM", bm)
+    monkeypatch.setenv("QG_A16_BN", bn)
+    m, n, k = 300, 200, 640
+    layer = Fp4Layer(n, k, seed=11)
+    assert f"a16_tiled BM={bm} BN={bn}" in qg.describe_dispatch(layer.w, m)
+    acts = Acts(False, m, k, seed=12)
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
+        e = oracle.normwise_error(run(layer, acts.x, m, otype), yref)
+        assert e <= tol, (otype, e)
+
+
+def test_fp4_bf16_tiled_identity_rows_exact():
+    n, k, m = 136, 640, 320
+    layer = Fp4Layer(n, k, seed=13)
+    wdq = layer.wdq()
+    bits = np.zeros((m, k), np.uint16)
+    cols = (np.arange(m) * 2 + 1) % k
+    bits[np.arange(m), cols] = 0x3F80
+    assert "a16_tiled" in qg.describe_dispatch(layer.w, m)
+    y = run(layer, to_dev(bits), m, qg.O_F32)
+    for i in range(m):
+        assert np.array_equal(y[i], wdq[:, cols[i]]), i
+
+
+def test_fp4_bf16_batch_invariant_rows():
+    n, k, mfull = 264, 1024, 300
+    layer = Fp4Layer(n, k, seed=15)
+    acts = Acts(False, mfull, k, seed=16)
+
+    def inv(rows):
+        x = acts.x.index_select(0, torch.as_tensor(rows, device="cuda")).contiguous()
+        y = torch.empty((len(rows), n), dtype=torch.float32, device="cuda")
+        wsb = qg.gemm_workspace_size_ex(layer.w, len(rows), qg.GEMM_BATCH_INVARIANT)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        qg.gemm_ex(layer.w, x, None, len(rows), k, y, qg.O_F32, n, ws, wsb, qg.GEMM_BATCH_INVARIANT)
+        torch.cuda.synchronize()
+        return y.cpu()
+    full = inv(list(range(mfull)))
+    assert oracle.normwise_error(full.numpy().astype(np.float64), oracle.gemm(acts.xdq, layer.wdq())) <= TOL_F32
+    for m in (1, 5, 64, 257):
+        rows = list(range(3, 3 + m))
+        assert torch.equal(inv(rows).view(torch.int32), full[rows].view(torch.int32)), m
