@@ -357,7 +357,7 @@ static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
-  if (d.k % 128 != 0 || d.num_experts > kMaxExperts || fp4_a16(d)) return 0;  // skinny kernel only
+  if (d.k % 128 != 0 || d.num_experts > kMaxExperts) return 0;
   const bool mx = mx_a8(d);
   // 32-bit offsets inside the kernels
   if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
@@ -434,7 +434,8 @@ static int64_t moe_small_tiles_cap(const qg_weight &w, int64_t pairs) {
 // QG_MOE_SMALL=0 keeps small experts on the skinny kernel, =1 forces the
 // small tiles.
 static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows) {
-  if (min_rows <= 0) return false;
+  // (MXFP4 x bf16: no small-tile form; its smaller experts run the skinny kernel)
+  if (min_rows <= 0 || fp4_a16(w.desc)) return false;
   const char *e = getenv("QG_MOE_SMALL");
   if (e && *e) return atoi(e) != 0;
   return pairs >= 256;

@@ -528,9 +528,9 @@ static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t 
     case QG_W_INT3: return launch_group<BM, BN, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_UINT3: return launch_group<BM, BN, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_MXFP4:
-      // MXFP4 x bf16: dense tiles of 32 x 32 wave blocks only
-      if constexpr (!MOE && WM > 1 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0) {
-        if (fp4_a16(d) && g == 32) return launch_a16_tiled_t<BM, BN, WM, WN, 4, false, 32, false, true>(a, xs_rows, cap, xs, false, s);
+      // MXFP4 x bf16: tiles of 32 x 32 wave blocks (not the 16-column small tiles)
+      if constexpr (WM > 1 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0) {
+        if (fp4_a16(d) && g == 32) return launch_a16_tiled_t<BM, BN, WM, WN, 4, false, 32, MOE, true>(a, xs_rows, cap, xs, false, s);
       }
       return hipErrorInvalidValue;
   }

@@ -76,8 +76,14 @@ def test_fp4_bf16_identity_rows_exact():
                                    float(np.max(np.abs(y[i] - ref))))
 
 
-def test_fp4_bf16_moe():
-    experts, topk, t, n, k = 8, 2, 40, 256, 512
+@pytest.mark.parametrize("t,tiled_min", [(40, None), (256, None), (256, "1"), (256, "0")])
+def test_fp4_bf16_moe(monkeypatch, t, tiled_min):
+    """Grouped MXFP4 x bf16: few tokens (skinny kernel), a skewed batch whose
+    large experts take the 128-row tiled kernel and the rest the skinny kernel,
+    every expert on the tiled kernel (QG_MOE_TILED_MIN=1) and none (=0)."""
+    if tiled_min is not None:
+        monkeypatch.setenv("QG_MOE_TILED_MIN", tiled_min)
+    experts, topk, n, k = 8, 2, 256, 512
     layer = Fp4Layer(n, k, seed=7, experts=experts)
     r = synth.rng(8, 0)
     ids = synth.route(r, t, experts, topk)
