@@ -128,7 +128,14 @@ def fill_packed_random(qg, torch, w, buf, gen):
                                                device="cuda", generator=gen)
     n_pad = w.n_tiles * 16
     so = w.scales_offset
-    if d.wtype == qg.W_MXFP4:
+    if d.wtype == qg.W_MXFP4 and d.atype == qg.A_BF16:
+        # bf16 powers of two 2^(e - 127), e near 120, in the integer formats' scale layout
+        gp, G = w.groups_padded, k // 32
+        s16 = v[:, so:so + n_pad * gp * 2].clone().view(torch.int16).view(E, n_pad, gp)
+        e8 = torch.randint(118, 123, (E, n, G), dtype=torch.int16, device="cuda", generator=gen)
+        s16[:, :n, :G] = e8 << 7
+        v[:, so:so + n_pad * gp * 2] = s16.view(E, -1).view(torch.uint8)
+    elif d.wtype == qg.W_MXFP4:
         kb_pad = -(-w.k_blocks // 4) * 4
         sc = v[:, so:so + n_pad * 4 * kb_pad].view(E, n_pad, 4, kb_pad)
         sc[:, :n, :, :k // 128] = torch.randint(118, 123, (E, n, 4, k // 128), dtype=torch.uint8,
@@ -149,9 +156,9 @@ def fill_packed_random(qg, torch, w, buf, gen):
 
 
 class MoELayer:
-    def __init__(self, qg, torch, wtype, experts, n, k, copies, gen):
+    def __init__(self, qg, torch, wtype, experts, n, k, copies, gen, atype=None):
         g = 32 if wtype == qg.W_MXFP4 else 128
-        desc = qg.layer_desc(wtype, n, k, g, num_experts=experts)
+        desc = qg.layer_desc(wtype, n, k, g, num_experts=experts, atype=atype)
         size = qg.packed_size(desc)
         self.n, self.k, self.ws = n, k, []
         self.bufs = []
@@ -184,19 +191,20 @@ def moe_dispatch(ids, experts, mx, tiled_min=64, small_min_pairs=256):
     return f"{fmt}_tiled BM=128 for {big} experts with >= {tiled_min} rows; {rest} smaller"
 
 
-def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters):
-    mx = wtype == qg.W_MXFP4
-    g = 32 if mx else 128
+def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters, atype=None):
+    fp4 = wtype == qg.W_MXFP4 and atype == qg.A_BF16  # MXFP4 weights x bf16 activations
+    mx = wtype == qg.W_MXFP4 and not fp4
+    g = 32 if wtype == qg.W_MXFP4 else 128
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
     ids = synth.route(synth.rng(7, tokens), tokens, experts, topk)
     active = int(np.unique(ids).size)
     p = tokens * topk
-    touched = active * (weight_bytes(n1, k1, 4, g, False, 1 if mx else 2) +
-                        weight_bytes(n2, k2, 4, g, False, 1 if mx else 2))
+    sb = 1 if wtype == qg.W_MXFP4 else 2
+    touched = active * (weight_bytes(n1, k1, 4, g, False, sb) + weight_bytes(n2, k2, 4, g, False, sb))
     copies = int(min(16, max(1, -(-2 * MALL_BYTES // touched))))
-    up = MoELayer(qg, torch, wtype, experts, n1, k1, copies, gen)
-    down = MoELayer(qg, torch, wtype, experts, n2, k2, copies, gen)
+    up = MoELayer(qg, torch, wtype, experts, n1, k1, copies, gen, atype)
+    down = MoELayer(qg, torch, wtype, experts, n2, k2, copies, gen, atype)
     d_ids = torch.from_numpy(ids).cuda()
     sorted_ids = torch.empty(p, dtype=torch.int32, device="cuda")
     offsets = torch.empty(experts + 1, dtype=torch.int32, device="cuda")
@@ -595,6 +603,10 @@ def main():
             moe[f"w4a16_E256_top8_T{tokens}"] = bench_moe(
                 qg, synth, torch, "moe_w4a16", qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, tokens,
                 iters=5 if tokens > 64 else 30)
+        for tokens in (64, 4096):
+            moe[f"w4a16_mxfp4_E256_top8_T{tokens}"] = bench_moe(
+                qg, synth, torch, "moe_w4a16_mxfp4", qg.W_MXFP4, 256, 8, 4096, 7168, 7168, 2048, tokens,
+                iters=5 if tokens > 64 else 30, atype=qg.A_BF16)
         for tokens in (1, 64, 512, 4096):
             moe[f"w4a8_E128_top8_T{tokens}"] = bench_moe(
                 qg, synth, torch, "moe_w4a8", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,

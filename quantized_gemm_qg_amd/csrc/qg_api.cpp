@@ -434,8 +434,7 @@ static int64_t moe_small_tiles_cap(const qg_weight &w, int64_t pairs) {
 // QG_MOE_SMALL=0 keeps small experts on the skinny kernel, =1 forces the
 // small tiles.
 static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows) {
-  // (MXFP4 x bf16: no small-tile form; its smaller experts run the skinny kernel)
-  if (min_rows <= 0 || fp4_a16(w.desc)) return false;
+  if (min_rows <= 0) return false;
   const char *e = getenv("QG_MOE_SMALL");
   if (e && *e) return atoi(e) != 0;
   return pairs >= 256;

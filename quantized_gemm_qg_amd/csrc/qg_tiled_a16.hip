@@ -153,7 +153,7 @@ template <int BM, int BN, int WM, int WN, int BITS, bool ZP, int GROUP, bool MOE
 __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, const float *xs,
                                                                  int xs_rows) {
   using C = A16Cfg<BM, BN, WM, WN, BITS, ZP, GROUP>;
-  static_assert(!FP4 || (C::M32 && BITS == 4 && !ZP && GROUP == 32), "fp4 codes: 32 x 32 tiles, group 32");
+  static_assert(!FP4 || (BITS == 4 && !ZP && GROUP == 32), "fp4 codes: 4-bit, group 32");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -382,8 +382,37 @@ __global__ __launch_bounds__(64 * WM * WN) void a16_tiled_kernel(GemmArgs a, con
         const uint32_t *p = (const uint32_t *)(sb + blk * 768 + 12 * lane);
         v = u32x4{p[0], p[1], p[2], 0u};
       }
+      if constexpr (FP4) {
+        // K32 step s is K-group kb * GPB + s of column col
+        const int col = wn * 16 * C::NJ + 16 * j + r16;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bw[j][s] = unpack_br<BITS>(v, s, umask, umagic);
+        for (int s = 0; s < 4; ++s) {
+          const int gg = kb * C::GPB + s;
+          const float sc = bf16_bits_to_f32(*(const uint16_t *)(sb + C::OFF_SS + col * 16 + 2 * (gg & 7)));
+          bw[j][s] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v[s], sc, 0)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v[s], sc, 1)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v[s], sc, 2)),
+                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v[s], sc, 3))};
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bw[j][s] = unpack_br<BITS>(v, s, umask, umagic);
+      }
+    }
+    if constexpr (FP4) {
+#pragma unroll
+      for (int i = 0; i < C::MI; ++i) {
+        const int r0 = wm * (BM / WM) + 16 * i;
+        if (C::SKIP_ROWS && r0 >= tr.rows) continue;  // workgroup-uniform
+        const uint8_t *arow = st + (r0 + r16) * 256;
+#pragma unroll
+        for (int ss = 0; ss < 4; ++ss) {
+          const u32x4 af = *(const u32x4 *)(arow + 16 * ((4 * ss + q) ^ r16));
+#pragma unroll
+          for (int j = 0; j < C::NJ; ++j) acc[i][j] = mfma_bf16(af, bw[j][ss], acc[i][j]);
+        }
+      }
+      continue;
     }
 #pragma unroll
     for (int gi = 0; gi < C::GPB; ++gi) {
@@ -527,11 +556,8 @@ static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t 
     case QG_W_UINT4: return launch_group<BM, BN, WM, WN, 4, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_INT3: return launch_group<BM, BN, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_UINT3: return launch_group<BM, BN, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
-    case QG_W_MXFP4:
-      // MXFP4 x bf16: tiles of 32 x 32 wave blocks (not the 16-column small tiles)
-      if constexpr (WM > 1 && (BM / WM) % 32 == 0 && (BN / WN) % 32 == 0) {
-        if (fp4_a16(d) && g == 32) return launch_a16_tiled_t<BM, BN, WM, WN, 4, false, 32, MOE, true>(a, xs_rows, cap, xs, false, s);
-      }
+    case QG_W_MXFP4:  // MXFP4 x bf16
+      if (fp4_a16(d) && g == 32) return launch_a16_tiled_t<BM, BN, WM, WN, 4, false, 32, MOE, true>(a, xs_rows, cap, xs, false, s);
       return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;

@@ -76,13 +76,17 @@ def test_fp4_bf16_identity_rows_exact():
                                    float(np.max(np.abs(y[i] - ref))))
 
 
-@pytest.mark.parametrize("t,tiled_min", [(40, None), (256, None), (256, "1"), (256, "0")])
-def test_fp4_bf16_moe(monkeypatch, t, tiled_min):
+@pytest.mark.parametrize("t,env", [(40, {}), (256, {}), (256, {"QG_MOE_TILED_MIN": "1"}),
+                                   (256, {"QG_MOE_TILED_MIN": "0"}),
+                                   (256, {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1"}),
+                                   (256, {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1", "QG_MOE_SMALL_BM": "32"})])
+def test_fp4_bf16_moe(monkeypatch, t, env):
     """Grouped MXFP4 x bf16: few tokens (skinny kernel), a skewed batch whose
-    large experts take the 128-row tiled kernel and the rest the skinny kernel,
-    every expert on the tiled kernel (QG_MOE_TILED_MIN=1) and none (=0)."""
-    if tiled_min is not None:
-        monkeypatch.setenv("QG_MOE_TILED_MIN", tiled_min)
+    large experts take the 128-row tiled kernel and the rest the 64-row small
+    tiles, every expert on 128-row tiles, none on tiles, and every expert on
+    64- or 32-row small tiles."""
+    for key, val in env.items():
+        monkeypatch.setenv(key, val)
     experts, topk, n, k = 8, 2, 256, 512
     layer = Fp4Layer(n, k, seed=7, experts=experts)
     r = synth.rng(8, 0)
