@@ -41,7 +41,7 @@
  *   scales : [N][K/g]: bf16 bit patterns (A16 formats) or e8m0 bytes (MXFP4).
  *   zeros  : [N][K/g] uint8 in 0..2^b-1 for UINT-b formats, NULL otherwise.
  * Activations: x is [rows][ldx] row-major: bf16, or e4m3 bytes (MXFP8) with
- * x_scales [rows][K/32] e8m0 bytes (row stride K/32).  y is [rows][ldy]
+ * x_scales [rows][K/32] e8m0 bytes (row stride K/32), per desc.atype.  y is [rows][ldy]
  * row-major, bf16 or fp32.
  *
  * Numerics (the contract the CPU oracle checks):
@@ -99,8 +99,11 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
 
 /* Layer + compute description ("Layer Config" / "Compute Config" of the
  * announcement's tuning section).  Supported (wtype, stype, atype, group):
- *   INT4/UINT4/INT3/UINT3, BF16 scales, BF16 activations, group 32 or 128;
- *   MXFP4, E8M0 scales, MXFP8 activations, group 32.
+ *   INT4/UINT4/INT3/UINT3, BF16 scales, BF16 activations, group 32, 64 or 128;
+ *   MXFP4, E8M0 scales, MXFP8 activations, group 32 (W4A8 on the scaled MFMA);
+ *   MXFP4, E8M0 scales, BF16 activations, group 32 (each code dequantized in
+ *   the kernel to the exact bf16 e2m1 * 2^(e-127); the announcement's
+ *   "Choosing the activation type": MXFP4 checkpoints on a bf16 compute path).
  * Other valid combinations return QG_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t abi_version; /* must be QG_ABI_VERSION */
