@@ -169,9 +169,11 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
 // one, "0" disables the kernel.
 static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Variant *v) {
   const int g = w.desc.group_size;
-  const bool compiled = (g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
-                                      (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
-                        (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)));
+  const bool compiled = fp4_a16(w.desc)
+                            ? (g == 32 && T == 1 && (KR == 4 || KR == 8))
+                            : (g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
+                                            (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
+                                  (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)));
   if (!compiled || S < 1 || S > 8) return false;
   const int kbs = w.k_blocks;
   const int W = (kbs + KR * S - 1) / (KR * S);
@@ -188,7 +190,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
 
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
-  if (mx_a8(d) || fp4_a16(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
+  if (mx_a8(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
   const char *e = getenv("QG_DECODE");
   if (e && *e == '0') return false;
   int T, KR, S = 1;
@@ -276,7 +278,7 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
              ((v.bm == 128 && v.tbn == 256 && a16_tiled_waves() == 8) || ((v.bm == 128 || v.bm == 256) && v.tbn == 128));
     case 3: {
       Variant t;
-      return !mx && !fp4_a16(d) && m >= 1 && m <= 16 && d.k % 512 == 0 && decode_fits(w, m, v.T, v.KR, v.splits, &t) && t.W == v.W;
+      return !mx && m >= 1 && m <= 16 && d.k % 512 == 0 && decode_fits(w, m, v.T, v.KR, v.splits, &t) && t.W == v.W;
     }
   }
   return false;

@@ -553,7 +553,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
 // multiple of 512 and the splits must all start inside K.
 template <int FMT, int GROUP, int T, int KR, int ER>
 __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
-  constexpr int BITS = (FMT <= 1) ? 4 : 3;
+  constexpr int BITS = (FMT <= 1 || FMT == 5) ? 4 : 3;  // FMT 5: MXFP4 codes x bf16
   constexpr bool ZP = (FMT == 1 || FMT == 3);
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   const int lane = threadIdx.x & 63;
@@ -596,8 +596,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  a16_wave<BITS, ZP, GROUP, T, KR, true, ER>(a, a.wbase, xrow, nt0, (split * nwaves + wave) * KR, acc,
-                                             x_ready, ks0);
+  a16_wave<BITS, ZP, GROUP, T, KR, true, ER, decltype(x_ready), FMT == 5>(
+      a, a.wbase, xrow, nt0, (split * nwaves + wave) * KR, acc, x_ready, ks0);
 
   // 3. reduce the waves (valid rows only) and store
 #pragma unroll
@@ -865,6 +865,11 @@ static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream
     if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
     if (v.T == 2 && v.KR == 8) QG_DECODE_LAUNCH(2, 8)
   }
+  // MXFP4 x bf16 (group 32: 4 scales per k-block, 16 dwords at KR = 8)
+  if constexpr (FMT == 5 && GROUP == 32) {
+    if (v.T == 1 && v.KR == 4) QG_DECODE_LAUNCH(1, 4)
+    if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
+  }
 #undef QG_DECODE_LAUNCH
   return hipErrorInvalidValue;
 }
@@ -891,6 +896,7 @@ hipError_t launch_decode_a16(const GemmArgs &a, const qg_layer_desc &d, const Va
     case 1: return launch_decode_f<1>(a, d.group_size, v, s);
     case 2: return launch_decode_f<2>(a, d.group_size, v, s);
     case 3: return launch_decode_f<3>(a, d.group_size, v, s);
+    case 5: return d.group_size == 32 ? launch_decode_g<5, 32>(a, v, s) : hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
 }

@@ -48,12 +48,14 @@ def run(layer, x, m, otype):
 
 
 @pytest.mark.parametrize("m,n,k", [(16, 256, 512), (1, 200, 640), (37, 136, 544), (300, 264, 1024),
-                                   (4, 4096, 14336), (1, 14336, 4096)])
+                                   (4, 4096, 14336), (1, 14336, 4096), (8, 264, 1536), (3, 72, 512)])
 def test_fp4_bf16_dense(m, n, k):
     layer = Fp4Layer(n, k, seed=m + n)
     acts = Acts(False, m, k, seed=k)
     print(f"  M={m} N={n} K={k}: {qg.describe_dispatch(layer.w, m)}", flush=True)
-    assert ("a16_tiled" if m >= 256 and k % 128 == 0 else "a16_skinny") in qg.describe_dispatch(layer.w, m)
+    expect = ("a16_tiled" if m >= 256 and k % 128 == 0 else
+              "a16_decode" if m <= 8 and k % 512 == 0 else "a16_skinny")
+    assert expect in qg.describe_dispatch(layer.w, m)
     yref = oracle.gemm(acts.xdq, layer.wdq())
     for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
         e = oracle.normwise_error(run(layer, acts.x, m, otype), yref)
@@ -155,3 +157,26 @@ def test_fp4_bf16_batch_invariant_rows():
     for m in (1, 5, 64, 257):
         rows = list(range(3, 3 + m))
         assert torch.equal(inv(rows).view(torch.int32), full[rows].view(torch.int32)), m
+
+
+@pytest.mark.parametrize("decode", ["1,8", "1,4", "1,8,2"])
+def test_fp4_bf16_decode_identity_rows_exact(monkeypatch, decode):
+    """One-hot rows through the decode kernel (activations in LDS; with and
+    without a K split) return the dequantized weights bit for bit."""
+    monkeypatch.setenv("QG_DECODE", decode)
+    n, k, m = 72, 2048, 8
+    layer = Fp4Layer(n, k, seed=17)
+    assert "a16_decode" in qg.describe_dispatch(layer.w, m)
+    wdq = layer.wdq()
+    for c0 in range(0, k, 512):
+        bits = np.zeros((m, k), np.uint16)
+        cols = c0 + (np.arange(m) * 37) % 512
+        bits[np.arange(m), cols] = 0x3F80
+        wsb = qg.gemm_workspace_size(layer.w, m)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        qg.gemm(layer.w, to_dev(bits), None, m, k, y, qg.O_F32, n, ws, wsb)
+        torch.cuda.synchronize()
+        y = y.cpu().numpy().astype(np.float64)
+        for i in range(m):
+            assert np.array_equal(y[i], wdq[:, cols[i]]), (c0, i)
