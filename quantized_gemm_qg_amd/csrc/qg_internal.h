@@ -22,7 +22,13 @@
 //     * e2m1 (block 1024 B, 16 B per lane): the lane's 32 codes k = 128 kb +
 //       32 q + e in standard order (two per byte, low nibble first), i.e. the
 //       16-B chunk of the standard row that one 16x16x128 scaled MFMA lane reads.
-//   scales  A16: bf16 [n_pad][groups_padded] (groups rounded up to 32).
+//     * e2m1 for bf16 activations: the 4-bit integer lane order above (dword
+//       j = the codes of bf16 MFMA j) with the eight codes in standard order
+//       (byte i = codes 2i, 2i + 1, low nibble first), the order the
+//       fp4 -> bf16 pair conversion emits.
+//   scales  A16: bf16 [n_pad][groups_padded] (groups rounded up to 32); for
+//           e2m1 with bf16 activations each e8m0 code c is stored as the bf16
+//           2^(c - 127) (c = 0: 0x0040).
 //           MXFP4: e8m0 in 256-byte units [n_tile][kb_pad / 4], each
 //           [16 columns c][4 quarters q][4 k-blocks]: byte (n, q, kb) scales
 //           k = 128 kb + 32 q .. +31 of column n = 16 n_tile + c; kb_pad =
