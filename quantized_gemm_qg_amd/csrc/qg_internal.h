@@ -1,7 +1,7 @@
 // Internal declarations shared by the host side of libqg (validation, repack,
 // dispatch) and the HIP kernel launchers.  Not part of the public ABI.
 //
-// Packed layout, version 1 (one section per expert, each part 256-B aligned):
+// Packed layout, version 2 (QG_LAYOUT_VERSION; one section per expert, each part 256-B aligned):
 //
 //   codes   k-blocks of 128 along K, n-tiles of 16 along N, block (t, kb) at
 //           byte ((t * k_blocks) + kb) * block_bytes.  Inside a block, lane
