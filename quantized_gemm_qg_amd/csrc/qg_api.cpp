@@ -169,11 +169,11 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
 // one, "0" disables the kernel.
 static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Variant *v) {
   const int g = w.desc.group_size;
-  const bool compiled = fp4_a16(w.desc)
-                            ? (g == 32 && T == 1 && (KR == 4 || KR == 8))
-                            : (g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
-                                            (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
-                                  (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)));
+  const bool compiled = (g == 32 && T == 1 && (KR == 4 || KR == 8)) ||
+                        (!fp4_a16(w.desc) &&
+                         ((g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
+                                        (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
+                          (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)))));
   if (!compiled || S < 1 || S > 8) return false;
   const int kbs = w.k_blocks;
   const int W = (kbs + KR * S - 1) / (KR * S);

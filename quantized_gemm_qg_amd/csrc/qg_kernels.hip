@@ -865,8 +865,8 @@ static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream
     if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
     if (v.T == 2 && v.KR == 8) QG_DECODE_LAUNCH(2, 8)
   }
-  // MXFP4 x bf16 (group 32: 4 scales per k-block, 16 dwords at KR = 8)
-  if constexpr (FMT == 5 && GROUP == 32) {
+  // group 32 (4 scales per k-block: 16 dwords at KR = 8), one n-tile per wave
+  if constexpr (GROUP == 32) {
     if (v.T == 1 && v.KR == 4) QG_DECODE_LAUNCH(1, 4)
     if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
   }

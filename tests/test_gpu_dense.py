@@ -288,11 +288,12 @@ def test_w4a16_large_m_full_size_sampled_rows(nk):
 
 # "T,KR" or "T,KR,splits" (split K across workgroups)
 DECODE_VARIANTS = {128: ["4,2", "2,4", "1,4", "1,8", "2,8", "1,4,2", "1,4,3", "1,8,2", "2,4,2"],
-                   64: ["4,2", "2,4", "2,4,2"]}
+                   64: ["4,2", "2,4", "2,4,2"],
+                   32: ["1,4", "1,8", "1,4,2", "1,8,2"]}
 
 
 @pytest.mark.parametrize("wtype", A16)
-@pytest.mark.parametrize("group", [64, 128])
+@pytest.mark.parametrize("group", [32, 64, 128])
 def test_decode_kernel_variants(monkeypatch, wtype, group):
     """Every compiled (T, KR) of the decode kernel, with and without a K
     split; N = 200 leaves a partial n-tile block, K = 1536 (12 blocks) a
@@ -328,11 +329,12 @@ def test_decode_split_k_reuses_workspace(monkeypatch):
         assert e <= tol_f32(False), (call, e)
 
 
+@pytest.mark.parametrize("group", [32, 128])
 @pytest.mark.parametrize("wtype", A16)
-def test_decode_kernel_identity_rows_exact(monkeypatch, wtype):
+def test_decode_kernel_identity_rows_exact(monkeypatch, wtype, group):
     monkeypatch.setenv("QG_DECODE", "1,8")  # 16 rows: past the default row limit
     n, k = 72, 1024
-    layer = Layer(wtype, n, k, 128, seed=31)
+    layer = Layer(wtype, n, k, group, seed=31)
     wdq = layer.wdq()
     ks = [0, 1, 31, 32, 127, 128, 255, 511, 512, 513, 767, 896, 1000, 1023, 300, 700]
     m = len(ks)
