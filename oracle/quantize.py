@@ -16,6 +16,13 @@ this module (see ``oracle/__init__.py``); the library never does.
   to zero gives the code 0x80 (e4m3 -0).
   Written here as a search over the 127 non-negative finite e4m3 values, which
   are decoded from their bit fields by ``formats.decode_e4m3``.
+* bf16 -> MXFP4 (announcement, section "W8A8 / W4A8 / W4A4": MXFP4 on both
+  operands).  The same OCP rule with e2m1 elements: emax_elem = 2 (the largest
+  e2m1 value is 6 = 1.5 * 2^2), elements rounded to the nearest of the eight
+  non-negative e2m1 values, ties to the even code, saturated at 6, sign kept
+  (a negative value that rounds to zero gives code 0x8).  Codes are returned
+  one per element; ``pack_e2m1`` puts two per byte, element 2i in the low
+  nibble of byte i.
 * MoE output stage (announcement, section "Shared CUDA components": scaling
   and bias additions can be fused into the output stage; MoE layers route each
   token to top-k experts):
@@ -91,6 +98,62 @@ def quantize_mxfp8_bf16(x_bits: np.ndarray):
 def dequantize_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """Real values of MXFP8 rows: e4m3(code) * 2^(scale - 127), blocks of 32."""
     v = F.decode_e4m3(codes)
+    s = F.decode_e8m0(scales)
+    return v * np.repeat(s, 32, axis=-1)
+
+
+E2M1_EMAX = 2          # largest e2m1 binade: 6 = 1.5 * 2^2
+
+
+def e2m1_nearest(v: np.ndarray) -> np.ndarray:
+    """e2m1 code of each real v: nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to
+    the even code, |v| > 6 saturated to 6, sign (bit 3) taken from v
+    (including -0.0)."""
+    v = np.asarray(v, dtype=np.float64)
+    codes = np.arange(8, dtype=np.int64)
+    vals = F.decode_e2m1(codes)                          # increasing with the code
+    a = np.minimum(np.abs(v), vals[-1])
+    d = np.abs(a[..., None] - vals)                      # distance to every value
+    best = d.min(axis=-1, keepdims=True)
+    tied = d == best                                      # one or two nearest codes
+    even = tied & (codes % 2 == 0)
+    mag = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tied, axis=-1))
+    sign = np.signbit(v).astype(np.int64)
+    return ((sign << 3) | mag).astype(np.uint8)
+
+
+def quantize_mxfp4(x: np.ndarray):
+    """MXFP4 quantization of real rows [rows, K] (K % 32 == 0) along K.
+
+    Returns (codes uint8 [rows, K], one e2m1 code per element,
+    scales uint8 [rows, K/32] e8m0)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, k = x.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    blk = x.reshape(rows, k // 32, 32)
+    e = mx_block_exponent(np.abs(blk).max(axis=-1), E2M1_EMAX)
+    scaled = blk * np.exp2(-e.astype(np.float64))[..., None]   # exact: power-of-two scale
+    codes = e2m1_nearest(scaled).reshape(rows, k)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def quantize_mxfp4_bf16(x_bits: np.ndarray):
+    """quantize_mxfp4 of bf16 bit patterns (uint16 [rows, K])."""
+    return quantize_mxfp4(F.decode_bf16(x_bits))
+
+
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis: element 2i in the low
+    nibble of byte i, element 2i + 1 in the high nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] & 15) | ((c[..., 1::2] & 15) << 4)
+
+
+def dequantize_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Real values of MXFP4 rows (one code per element): e2m1(code) *
+    2^(scale - 127), blocks of 32."""
+    v = F.decode_e2m1(codes)
     s = F.decode_e8m0(scales)
     return v * np.repeat(s, 32, axis=-1)
 

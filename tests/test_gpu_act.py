@@ -33,7 +33,7 @@ def _gpu():
     require_gpu()
 
 
-def gpu_quantize(xbits: np.ndarray, ldx=None, ldq=None):
+def gpu_quantize(xbits: np.ndarray, ldx=None, ldq=None, qs_off=0):
     rows, k = xbits.shape
     ldx = ldx or k
     ldq = ldq or k
@@ -41,11 +41,16 @@ def gpu_quantize(xbits: np.ndarray, ldx=None, ldq=None):
     xpad[:, :k] = xbits
     x = to_dev(xpad)
     q = torch.full((rows, ldq), 0xAA, dtype=torch.uint8, device="cuda")
-    qs = torch.full((rows, k // 32), 0xAA, dtype=torch.uint8, device="cuda")
+    # qs_off places the scale array at an odd or 2-byte offset; the bytes
+    # around it must stay untouched
+    qbuf = torch.full((rows * (k // 32) + 2 * qs_off,), 0xAA, dtype=torch.uint8, device="cuda")
+    qs = qbuf[qs_off:qs_off + rows * (k // 32)].view(rows, k // 32)
     qg.quantize_mxfp8(x, rows, k, ldx, q, ldq, qs)
     torch.cuda.synchronize()
     qn = q.cpu().numpy()
     assert np.all(qn[:, k:] == 0xAA)  # padding columns untouched
+    qb = qbuf.cpu().numpy()
+    assert np.all(qb[:qs_off] == 0xAA) and np.all(qb[qs_off + rows * (k // 32):] == 0xAA)
     return qn[:, :k], qs.cpu().numpy()
 
 
@@ -93,11 +98,12 @@ def test_quantize_every_scale_exponent():
     check_quantize(z)
 
 
-@pytest.mark.parametrize("rows,k,ldx,ldq", [(1, 32, None, None), (3, 96, 104, 104), (37, 4096, None, 4112),
-                                            (4096, 4096, None, None)])
-def test_quantize_normal_rows(rows, k, ldx, ldq):
+@pytest.mark.parametrize("rows,k,ldx,ldq,qs_off", [(1, 32, None, None, 0), (3, 96, 104, 104, 0),
+                                                   (37, 4096, None, 4112, 0), (4096, 4096, None, None, 0),
+                                                   (5, 1024, None, None, 1), (9, 1536, None, None, 2)])
+def test_quantize_normal_rows(rows, k, ldx, ldq, qs_off):
     r = synth.rng(23, rows)
-    check_quantize(synth.x_bf16(r, rows, k), ldx=ldx, ldq=ldq)
+    check_quantize(synth.x_bf16(r, rows, k), ldx=ldx, ldq=ldq, qs_off=qs_off)
 
 
 def test_quantize_then_w4a8_gemm():
@@ -161,8 +167,8 @@ def test_silu_mul_bf16(f32, rows, inter, ldgu):
 
 
 @pytest.mark.parametrize("f32", [False, True])
-def test_silu_mul_mxfp8(f32):
-    rows, inter = 256, 640
+@pytest.mark.parametrize("rows,inter", [(256, 640), (96, 2048)])
+def test_silu_mul_mxfp8(f32, rows, inter):
     g, gv = _gu(rows, inter, f32, 26)
     c, s = _silu_gpu(g, f32, rows, inter, True)
     deq = Q.dequantize_mxfp8(c, s)

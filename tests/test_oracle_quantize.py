@@ -1,10 +1,10 @@
-"""Pins of the oracle's MXFP8 quantizer and MoE output stage (CPU only).
+"""Pins of the oracle's MXFP8 / MXFP4 quantizers and MoE output stage (CPU only).
 
 Each pin ties ``oracle.quantize`` to something other than itself: hand-worked
 cases of the OCP MX conversion rule, an exact round trip of representable
-blocks, a brute-force nearest-value search over every finite e4m3 value, the
-input generator's independent quantizer (grid-step arithmetic), closed forms
-of SiLU and torch's float64 SiLU.
+blocks, a brute-force nearest-value search over every finite e4m3 / e2m1
+value, the input generator's independent quantizer (grid-step arithmetic),
+closed forms of SiLU and torch's float64 SiLU.
 """
 import os
 
@@ -15,11 +15,12 @@ from oracle import formats as F
 from oracle import quantize as Q
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxfp8_quantize_cases.txt")
+GOLDEN4 = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_quantize_cases.txt")
 
 
-def _cases():
+def _cases(path=GOLDEN):
     out = []
-    for line in open(GOLDEN):
+    for line in open(path):
         line = line.strip()
         if not line or line.startswith("#"):
             continue
@@ -130,6 +131,69 @@ def test_dequantized_error_bounds():
     # and within 2^-4 relative for unsaturated values in the normal range
     big = (np.abs(x) >= 2.0 ** -6 * xs) & ~sat
     assert np.all(np.abs(d - x)[big] <= 2.0 ** -4 * np.abs(x)[big])
+
+
+@pytest.mark.parametrize("case", _cases(GOLDEN4), ids=lambda c: c[0])
+def test_mxfp4_hand_worked_cases(case):
+    _, x, scale, codes = case
+    c, s = Q.quantize_mxfp4(x[None, :])
+    assert int(s[0, 0]) == scale
+    np.testing.assert_array_equal(c[0], codes)
+
+
+def test_mxfp4_representable_blocks_round_trip():
+    # e2m1 values times 2^E with one element of magnitude 4 or 6 (the top
+    # binade [4, 8)): the scale rule gives back E and every code exactly
+    r = np.random.default_rng(16)
+    codes = r.integers(0, 16, size=(400, 32)).astype(np.uint8)
+    pos = r.integers(0, 32, size=400)
+    codes[np.arange(400), pos] = (r.integers(6, 8, size=400) | (r.integers(0, 2, size=400) << 3)).astype(np.uint8)
+    e = r.integers(-125, 126, size=400)
+    x = F.decode_e2m1(codes) * np.exp2(e.astype(np.float64))[:, None]
+    c, s = Q.quantize_mxfp4(x.reshape(100, 128))
+    np.testing.assert_array_equal(s.reshape(400), (e + 127).astype(np.uint8))
+    np.testing.assert_array_equal(c.reshape(400, 32), codes)   # -0 stays 0x8
+
+
+def test_e2m1_nearest_by_brute_force_and_midpoints():
+    r = np.random.default_rng(17)
+    v = np.concatenate([r.normal(0, 2, 4000), r.uniform(-8, 8, 4000)])
+    codes = Q.e2m1_nearest(v)
+    allv = F.decode_e2m1(np.arange(16))
+    got = F.decode_e2m1(codes.astype(np.int64))
+    clipped = np.clip(v, -6, 6)
+    best = np.abs(allv[None, :] - clipped[:, None]).min(axis=1)
+    np.testing.assert_array_equal(np.abs(got - clipped), best)
+    assert np.all(((codes >> 3) & 1) == np.signbit(v))
+    # the midpoints between consecutive non-negative values go to the even code
+    vals = F.decode_e2m1(np.arange(8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    lo = np.arange(7)
+    np.testing.assert_array_equal(Q.e2m1_nearest(mids), np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint8))
+
+
+def test_mxfp4_agrees_with_grid_step_quantizer_and_bounds():
+    import synth
+    r = np.random.default_rng(18)
+    xb = synth.x_bf16(r, 64, 512)
+    xv = F.decode_bf16(xb)
+    c1, s1 = Q.quantize_mxfp4_bf16(xb)
+    c2, s2 = synth.mx_quantize(xv, "e2m1")
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(c1, c2)
+    # scale rule: the block maximum lies in [4 X, 8 X)
+    amax = np.abs(xv.reshape(64, 16, 32)).max(axis=-1)
+    ratio = amax / F.decode_e8m0(s1)
+    assert np.all((ratio >= 4) & (ratio < 8))
+    # error: half the largest step (2 X) where unsaturated, < 2 X above 6 X
+    d = Q.dequantize_mxfp4(c1, s1)
+    xs = np.repeat(F.decode_e8m0(s1), 32, axis=-1)
+    sat = np.abs(xv) > 6 * xs
+    assert np.all(np.abs(d - xv)[~sat] <= 1 * xs[~sat])
+    assert np.all(np.abs(d - xv)[sat] < 2 * xs[sat])
+    # packing: element 2i in the low nibble of byte i
+    p = Q.pack_e2m1(c1)
+    np.testing.assert_array_equal(p, synth.pack_codes(c1, 4))
 
 
 def test_silu_closed_forms():
