@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "fp4": 10100.0}
 METRIC = "TFLOPS at M=4096 (W4A16, W4A8-MXFP4) + weight GB/s at M=1 decode, 1 GPU"
 ROTATE = 8
 MALL_BYTES = 256 << 20
@@ -366,6 +366,28 @@ def bench_large_m(qg, synth, torch):
             "dispatch": qg.describe_dispatch(L.ws[0], 4096)}
         print(f"[bench] extra mx N={n}: {extra[f'w4a8_mx_M4096_N{n}_K4096']}", file=sys.stderr, flush=True)
         del L
+    # W4A4: MXFP4 weights x MXFP4 activations (the same MX tiled kernel with
+    # e2m1 A operands; fp4 dense MFMA peak)
+    for n in (3072, 14336):
+        k = 4096
+        codes, sc, _ = synth.mx_weights(synth.rng(82, n), n, k)
+        desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_MXFP4)
+        bufs = [torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda") for _ in range(2)]
+        wts = [qg.preprocess(desc, codes, sc, None, b) for b in bufs]
+        xc = torch.randint(0, 256, (4096, k // 2), dtype=torch.uint8, device="cuda")
+        xs = torch.randint(118, 128, (4096, k // 32), dtype=torch.uint8, device="cuda")
+        y = torch.empty((4096, n), dtype=torch.bfloat16, device="cuda")
+        wsb = qg.gemm_workspace_size(wts[0], 4096)
+        ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream().cuda_stream
+        t = timed(torch, lambda i: qg.gemm(wts[i % 2], xc, xs, 4096, k, y, qg.O_BF16, n, ws, wsb, stream), 100, 20)
+        fl = 2.0 * 4096 * n * k
+        extra[f"w4a4_mx_M4096_N{n}_K{k}"] = {
+            "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+            "fp4_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp4"], 4),
+            "dispatch": qg.describe_dispatch(wts[0], 4096)}
+        print(f"[bench] extra w4a4 N={n}: {extra[f'w4a4_mx_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
+        del bufs, wts
     return extra
 
 

@@ -40,7 +40,9 @@
  *            e2m1 uses bit 3 as its sign.
  *   scales : [N][K/g]: bf16 bit patterns (A16 formats) or e8m0 bytes (MXFP4).
  *   zeros  : [N][K/g] uint8 in 0..2^b-1 for UINT-b formats, NULL otherwise.
- * Activations: x is [rows][ldx] row-major: bf16, or e4m3 bytes (MXFP8) with
+ * Activations: x is [rows][ldx] row-major: bf16, e4m3 bytes (MXFP8), or e2m1
+ * codes two per byte (MXFP4: element k in the low nibble of byte k/2 when k is
+ * even, the high nibble when odd; ldx counts elements), the MX types with
  * x_scales [rows][K/32] e8m0 bytes (row stride K/32), per desc.atype.  y is [rows][ldy]
  * row-major, bf16 or fp32.
  *
@@ -50,7 +52,7 @@
  *     s the group's bf16 scale.  Kernels form sum_k x*(q - z) per K-group with
  *     bf16 MFMA (codes are exact in bf16) and apply s per group in fp32.
  *   - MXFP4 x MXFP8: e2m1 * 2^(e-127) times e4m3 * 2^(ea-127), exact operands
- *     into gfx950 scaled MFMA.
+ *     into gfx950 scaled MFMA; MXFP4 x MXFP4 likewise with e2m1 activations.
  *   - fp32 accumulation; QG_O_BF16 output is the fp32 result rounded to
  *     nearest-even; QG_O_F32 exposes the fp32 accumulators.
  */
@@ -88,7 +90,7 @@ typedef enum {
 } qg_wtype;
 
 typedef enum { QG_S_BF16 = 0, QG_S_E8M0 = 1 } qg_stype;
-typedef enum { QG_A_BF16 = 0, QG_A_MXFP8 = 1 } qg_atype;
+typedef enum { QG_A_BF16 = 0, QG_A_MXFP8 = 1, QG_A_MXFP4 = 2 } qg_atype;
 typedef enum { QG_O_BF16 = 0, QG_O_F32 = 1 } qg_otype;
 
 /* How MoE rows are addressed.  A pair p = t*topk + j is token t's j-th expert
@@ -103,7 +105,10 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
  *   MXFP4, E8M0 scales, MXFP8 activations, group 32 (W4A8 on the scaled MFMA);
  *   MXFP4, E8M0 scales, BF16 activations, group 32 (each code dequantized in
  *   the kernel to the exact bf16 e2m1 * 2^(e-127); the announcement's
- *   "Choosing the activation type": MXFP4 checkpoints on a bf16 compute path).
+ *   "Choosing the activation type": MXFP4 checkpoints on a bf16 compute path);
+ *   MXFP4, E8M0 scales, MXFP4 activations, group 32, K % 128 == 0, dense
+ *   layers only (W4A4: both operands e2m1 into the scaled MFMA; the
+ *   announcement's "W8A8 / W4A8 / W4A4" section runs all three MX pairings).
  * Other valid combinations return QG_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t abi_version; /* must be QG_ABI_VERSION */
@@ -164,9 +169,14 @@ qg_status qg_weight_bind(const qg_layer_desc *desc, void *dst_dev, uint64_t dst_
 qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes);
 
 /* Dense GEMM: y[m][n] = x[m][:K] * dequant(W)^T.
- *   x        device, [m][ldx] bf16 or e4m3 bytes (per desc.atype), 16-B aligned,
- *            ldx >= K and ldx*elem_size a multiple of 16 bytes.
- *   x_scales device, [m][K/32] e8m0 (MXFP8 only, else ignored / may be NULL).
+ *   x        device, [m][ldx] bf16, e4m3 bytes or e2m1 nibble pairs (per
+ *            desc.atype), 16-B aligned, ldx >= K and the row pitch (ldx
+ *            elements) a multiple of 16 bytes (ldx % 32 == 0 for MXFP4).
+ *   x_scales device, [m][K/32] e8m0 (MX activations only, else ignored / may
+ *            be NULL).
+ * The MX large-M kernel addresses X with 32-bit offsets: an MX call whose
+ * activation rows span 4 GiB or more (m * row pitch) returns
+ * QG_ERR_UNSUPPORTED.
  *   y        device, [m][ldy] of otype, 16-B aligned, ldy >= N.
  *   ws       device workspace of at least qg_gemm_workspace_size bytes
  *            (may be NULL when that size is 0).
@@ -281,6 +291,25 @@ qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, i
  * k % 32 != 0 or ld too small: QG_ERR_SHAPE.  rows == 0 or k == 0: no-op.
  * NaN / Inf inputs give unspecified codes.  Asynchronous on `stream`. */
 qg_status qg_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q,
+                            int64_t ldq, void *q_scales, hipStream_t stream);
+
+/* bf16 activations -> MXFP4 (e2m1 codes + e8m0 scales), the input of a W4A4
+ * GEMM (announcement, section "W8A8 / W4A8 / W4A4": MXFP4 on both operands).
+ * Per row, per block of 32 values along K, the OCP Microscaling Formats v1.0
+ * conversion with e2m1's largest power of two, 2^2: scale X = 2^(floor(log2
+ * max|v|) - 2) clamped to 2^-127 .. 2^127 (X = 1 for an all-zero block),
+ * stored as the e8m0 code log2(X) + 127; element = v / X rounded to the
+ * nearest e2m1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6), ties to the even code,
+ * magnitudes beyond 6 saturated to 6, sign kept (a negative value that rounds
+ * to zero gives code 0x8).  Exact for bf16 inputs (no fp32 rounding).
+ *   x        device, bf16 [rows][ldx], 16-B aligned, ldx >= k, ldx % 8 == 0.
+ *   q        device, e2m1 nibble pairs [rows][ldq elements] (element j in the
+ *            low nibble of byte j/2 when j is even), 4-B aligned, ldq >= k,
+ *            ldq % 8 == 0.
+ *   q_scales device, e8m0 bytes [rows][k/32] (row stride k/32), any alignment.
+ * k % 32 != 0 or ld too small: QG_ERR_SHAPE.  rows == 0 or k == 0: no-op.
+ * NaN / Inf inputs give unspecified codes.  Asynchronous on `stream`. */
+qg_status qg_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q,
                             int64_t ldq, void *q_scales, hipStream_t stream);
 
 /* SiLU-gated product of a fused gate/up projection (MoE output stage between

@@ -17,7 +17,7 @@ QG_OK, QG_ERR_INVALID_ARGUMENT, QG_ERR_SHAPE, QG_ERR_ALIGNMENT = 0, 1, 2, 3
 QG_ERR_UNSUPPORTED, QG_ERR_BUFFER_TOO_SMALL, QG_ERR_HIP = 4, 5, 6
 W_INT4, W_UINT4, W_INT3, W_UINT3, W_MXFP4 = 0, 1, 2, 3, 4
 S_BF16, S_E8M0 = 0, 1
-A_BF16, A_MXFP8 = 0, 1
+A_BF16, A_MXFP8, A_MXFP4 = 0, 1, 2
 O_BF16, O_F32 = 0, 1
 ROWS_BY_TOKEN, ROWS_BY_PAIR, ROWS_SORTED = 0, 1, 2
 ABI_VERSION, LAYOUT_VERSION = 1, 2
@@ -29,7 +29,7 @@ EXPORTS = (
     "qg_moe_gemm", "qg_stream_read", "qg_stream_copy", "qg_describe_dispatch",
     "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
-    "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset",
+    "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset", "qg_quantize_mxfp4",
 )
 GEMM_BATCH_INVARIANT = 1
 
@@ -87,6 +87,7 @@ def _load():
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_last_hip_error": (I32, []),
         "qg_quantize_mxfp8": (I32, [P, I64, I64, I64, P, I64, P, P]),
+        "qg_quantize_mxfp4": (I32, [P, I64, I64, I64, P, I64, P, P]),
         "qg_silu_mul": (I32, [P, I32, I64, I64, I64, P, I32, I64, P, P]),
         "qg_moe_combine": (I32, [P, I32, I64, P, I64, I32, I64, P, P, I32, I64, P]),
         "qg_gemm_workspace_size_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.POINTER(U64)]),
@@ -252,6 +253,12 @@ def quantize_mxfp8(x, rows: int, k: int, ldx: int, q, ldq: int, q_scales, stream
     """bf16 x [rows][ldx] -> e4m3 q [rows][ldq] + e8m0 q_scales [rows][k/32]."""
     _check(_lib.qg_quantize_mxfp8(_ptr(x), rows, k, ldx, _ptr(q), ldq, _ptr(q_scales), _stream(stream)),
            "qg_quantize_mxfp8")
+
+
+def quantize_mxfp4(x, rows: int, k: int, ldx: int, q, ldq: int, q_scales, stream=None) -> None:
+    """bf16 x [rows][ldx] -> e2m1 q [rows][ldq elements, two per byte] + e8m0 q_scales [rows][k/32]."""
+    _check(_lib.qg_quantize_mxfp4(_ptr(x), rows, k, ldx, _ptr(q), ldq, _ptr(q_scales), _stream(stream)),
+           "qg_quantize_mxfp4")
 
 
 def silu_mul(gu, gu_type: int, rows: int, inter: int, ldgu: int, h, h_type: int, ldh: int,

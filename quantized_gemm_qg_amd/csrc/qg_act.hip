@@ -18,6 +18,11 @@
 // bf16, so floor(log2 max|v|) is the exponent field of the largest magnitude
 // and v / X only moves the binary point (exact in fp32); the one rounding is
 // the hardware's fp32 -> e4m3 conversion, nearest-even.
+//
+// MXFP4 conversion (for W4A4, the announcement's section "W8A8 / W4A8 /
+// W4A4"): the same rule with e2m1 elements, X = 2^(floor(log2 max|v|) - 2), the
+// element rounded to the nearest of the eight e2m1 magnitudes by comparisons
+// against their midpoints (no hardware conversion involved).
 #include <hip/hip_runtime.h>
 
 #include "qg_device.h"
@@ -83,6 +88,43 @@ __device__ __forceinline__ void mx_store8(const uint32_t (&w)[4], uint8_t *q8, u
   if (first) *scale = (uint8_t)(e + 127);
 }
 
+// e2m1 code (sign in bit 3) of v already divided by its block scale: the
+// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturated at
+// 6.  Each comparison is against a midpoint between neighbouring values, `>`
+// where the lower neighbour's code is even and `>=` where the upper one's is;
+// the division by the power-of-two scale is exact, so no rounding precedes
+// the comparisons.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float m = fabsf(v);
+  const uint32_t mag = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
+                       (uint32_t)(m > 5.f);
+  return mag | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// MXFP4 form of mx_store8: the block scale is 2^(floor(log2 max|v|) - 2)
+// (e2m1's largest value 6 lies in [4, 8)); the 8 codes go out as one dword,
+// value i in bits 4i .. 4i + 3.
+__device__ __forceinline__ void mx4_store8(const uint32_t (&w)[4], uint8_t *q4, uint8_t *scale, bool first) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  const uint32_t amax = quad_max(__float_as_uint(m));
+  const int e = amax == 0 ? 0 : max((int)(amax >> 23) - 129, -127);  // bf16 maxima: e <= 125
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);      // 2^-e
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c |= e2m1_code(v[i] * inv) << (4 * i);
+  *(uint32_t *)q4 = c;
+  if (first) *scale = (uint8_t)(e + 127);
+}
+
 // (row, chunk) of unit u with `per` chunks per row; 32-bit division whenever
 // the unit count allows (a 64-bit divide is a long instruction sequence)
 __device__ __forceinline__ void split_unit(int64_t u, int64_t per, bool wide, int64_t &row, int64_t &c) {
@@ -113,6 +155,23 @@ __device__ __forceinline__ void load8_f32(const void *row, int64_t c8, bool f32,
 }
 
 }  // namespace
+
+// bf16 rows [rows][ldx] -> e2m1 rows [rows][ldq elements, two per byte] +
+// e8m0 [rows][k / 32]; units as in quantize_mxfp8_kernel.
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const uint16_t *x, int64_t ldx, uint8_t *q,
+                                                             int64_t ldq, uint8_t *qs, int64_t k8,
+                                                             int64_t units) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const bool first = (threadIdx.x & 3) == 0;
+  const bool wide = units > 0xFFFFFFFFll;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
+    int64_t row, c8;
+    split_unit(u, k8, wide, row, c8);
+    const u32x4 v = *(const u32x4 *)(x + row * ldx + 8 * c8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    mx4_store8(w, q + row * (ldq >> 1) + 4 * c8, qs + row * (k8 >> 2) + (c8 >> 2), first);
+  }
+}
 
 // bf16 rows [rows][ldx] -> e4m3 rows [rows][ldq] + e8m0 [rows][k / 32].
 // Unit u = (row, 8-value chunk c8); u runs over rows * k / 8 (a multiple of 4,
@@ -213,6 +272,15 @@ hipError_t launch_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t
   const int64_t units = rows * (k / 8);
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3(stream_grid(units)), dim3(256), 0, s, (const uint16_t *)x, ldx,
+                     (uint8_t *)q, ldq, (uint8_t *)qs, k / 8, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
+                                 void *qs, hipStream_t s) {
+  const int64_t units = rows * (k / 8);
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(stream_grid(units)), dim3(256), 0, s, (const uint16_t *)x, ldx,
                      (uint8_t *)q, ldq, (uint8_t *)qs, k / 8, units);
   return hipGetLastError();
 }

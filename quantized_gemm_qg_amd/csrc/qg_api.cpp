@@ -140,12 +140,13 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   if (w.desc.k % 128 != 0) return false;
   const char *s = getenv("QG_TILED");
   if (s && *s == '0') return false;
-  const bool mx = mx_a8(w.desc);
+  const bool mx = mx_a8(w.desc) || mx_a4(w.desc);
   // the integer-format kernel addresses X and the codes with 32-bit offsets
   if (!mx && ((uint64_t)m * w.desc.k * 2 >= (1ull << 31) ||
               (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31)))
     return false;
-  if (m < (mx ? 128 : 256)) return false;
+  // (W4A4 has only the MX tiled kernel, which serves every M)
+  if (m < (mx_a4(w.desc) ? 1 : mx ? 128 : 256)) return false;
   // 256-row tiles halve the weight re-reads and win at every measured shape
   // once M fills them; 128-row tiles for M in [128, 256)
   int bm = m >= 256 ? 256 : 128;
@@ -190,7 +191,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
 
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
-  if (mx_a8(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
+  if (mx_a8(d) || mx_a4(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
   const char *e = getenv("QG_DECODE");
   if (e && *e == '0') return false;
   int T, KR, S = 1;
@@ -224,7 +225,7 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
 // variant fixed by (N, K) sums its waves' and splits' partials in index order.
 // Tile widths do not change any element's order; they are fixed anyway.
 static Variant select_dense_invariant(const qg_weight &w) {
-  const bool mx = mx_a8(w.desc);
+  const bool mx = mx_a8(w.desc) || mx_a4(w.desc);  // (W4A4 layers have K % 128 == 0)
   if (w.desc.k % 128 == 0 && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
     const int bn = mx ? 256 : a16_tiled_bn();
     return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
@@ -265,7 +266,8 @@ static bool same_variant(const Variant &a, const Variant &b) {
 // Whether v can serve m rows of w (a table entry serves every M of its bucket)
 static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
   const qg_layer_desc &d = w.desc;
-  const bool mx = mx_a8(d);
+  const bool mx = mx_a8(d) || mx_a4(d);
+  if (mx_a4(d) && v.kind != 1) return false;  // W4A4: the MX tiled kernel only
   switch (v.kind) {
     case 0:
       return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 && covers(v, w.k_blocks);
@@ -320,6 +322,11 @@ Variant select_dense(const qg_weight &w, int64_t m) {
 
 static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
   Variant v;
+  if (mx_a4(w.desc)) {
+    // the one kernel with e2m1 activations (whatever QG_TILED says)
+    const int bm = m >= 256 ? 256 : 128;
+    return Variant{1, 1, 1, 1, 1, bm, mx_tile_cols(w.desc.n, m, bm)};
+  }
   if (tiled_for(w, m, &v)) return v;
   if (!getenv("QG_TUNE") && decode_for(w, m, &v)) return v;
   if (env_variant(&v)) {
@@ -595,6 +602,12 @@ extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
 
 // One dense GEMM with variant v (arguments already validated; ws holds
 // dense_ws_bytes(w, v, m) bytes, its split-K counters zero).
+// Row pitch of the activations in bytes: ldx elements of bf16, e4m3 or (two
+// per byte) e2m1.
+static uint64_t x_pitch(const Layout &L, int64_t ldx) {
+  return L.a4 ? (uint64_t)ldx / 2 : (uint64_t)ldx * (L.is_mx ? 1 : 2);
+}
+
 static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, const Variant &v, const void *x,
                                        const void *x_scales, int64_t m, int64_t ldx, void *y, int32_t otype,
                                        int64_t ldy, void *ws, hipStream_t stream) {
@@ -618,7 +631,10 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
     a.counters = (uint32_t *)ws;
     a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
   }
-  if (v.kind == 1) return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream);
+  if (v.kind == 1) {
+    if (L.a4) a.ldx = ldx / 2;  // the kernel addresses e2m1 rows in bytes
+    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream, L.a4);
+  }
   if (v.kind == 3) return launch_decode_a16(a, d, v, stream);
   if (v.kind == 2) return launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), ws, true, stream);
   return L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
@@ -662,14 +678,14 @@ extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x
   if (!x || !y) return QG_ERR_INVALID_ARGUMENT;
   if (L.is_mx && !x_scales) return QG_ERR_INVALID_ARGUMENT;
   if (ldx < d.k || ldy < d.n) return QG_ERR_SHAPE;
-  const int xel = L.is_mx ? 1 : 2;
   const int yel = otype == QG_O_F32 ? 4 : 2;
-  if (!aligned16(x) || !aligned16(y) || (ldx * xel) % 16 != 0 || (ldy * yel) % 4 != 0)
+  if (!aligned16(x) || !aligned16(y) || x_pitch(L, ldx) % 16 != 0 || (L.a4 && (ldx & 1)) || (ldy * yel) % 4 != 0)
     return QG_ERR_ALIGNMENT;
   const Variant v = dense_variant(*w, m, flags);
-  // the integer-format tiled kernel addresses X with 32-bit offsets; a
-  // batch-invariant call may not move to another kernel past that size
+  // the tiled kernels address X with 32-bit offsets; a batch-invariant call
+  // may not move to another kernel past that size
   if (v.kind == 2 && (uint64_t)m * d.k * 2 >= (1ull << 31)) return QG_ERR_UNSUPPORTED;
+  if (v.kind == 1 && (uint64_t)m * x_pitch(L, ldx) >= (1ull << 32)) return QG_ERR_UNSUPPORTED;
   const uint64_t need = dense_ws_bytes(*w, v, m);
   if (need > 0) {
     if (!ws) return QG_ERR_INVALID_ARGUMENT;
@@ -685,6 +701,7 @@ extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_token
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
   if (!bytes || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
+  if (L.a4) return QG_ERR_UNSUPPORTED;  // W4A4 is dense only
   const int64_t pairs = num_tokens * topk;
   // the sort's need, or the grouped GEMM's with X indexed by pair (the larger
   // of the two x row counts)
@@ -719,6 +736,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   const qg_layer_desc &d = w->desc;
   if (num_tokens < 0 || topk <= 0 || (otype != QG_O_BF16 && otype != QG_O_F32))
     return QG_ERR_INVALID_ARGUMENT;
+  if (L.a4) return QG_ERR_UNSUPPORTED;  // W4A4 is dense only
   if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
   if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
   if (d.num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
@@ -826,6 +844,16 @@ extern "C" qg_status qg_quantize_mxfp8(const void *x, int64_t rows, int64_t k, i
   return hip_status(launch_quantize_mxfp8(x, rows, k, ldx, q, ldq, q_scales, stream));
 }
 
+extern "C" qg_status qg_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q,
+                                       int64_t ldq, void *q_scales, hipStream_t stream) {
+  if (rows < 0 || k < 0) return QG_ERR_INVALID_ARGUMENT;
+  if (k % 32 != 0 || ldx < k || ldq < k) return QG_ERR_SHAPE;
+  if (rows == 0 || k == 0) return QG_OK;
+  if (!x || !q || !q_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || ldx % 8 != 0 || !aligned(q, 4) || ldq % 8 != 0) return QG_ERR_ALIGNMENT;
+  return hip_status(launch_quantize_mxfp4(x, rows, k, ldx, q, ldq, q_scales, stream));
+}
+
 extern "C" qg_status qg_silu_mul(const void *gu, int32_t gu_type, int64_t rows, int64_t inter, int64_t ldgu,
                                  void *h, int32_t h_type, int64_t ldh, void *h_scales, hipStream_t stream) {
   if (rows < 0 || inter < 0) return QG_ERR_INVALID_ARGUMENT;
@@ -874,7 +902,7 @@ static void describe_variant(const Variant &v, bool mx, char *buf, uint64_t buf_
 // (K % 128 == 0).
 static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> *out) {
   const qg_layer_desc &d = w.desc;
-  const bool mx = mx_a8(d);
+  const bool mx = mx_a8(d) || mx_a4(d);
   auto add = [&](const Variant &v) {
     for (const Variant &u : *out)
       if (same_variant(u, v)) return;
@@ -962,11 +990,11 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (m > (1ll << 30)) return QG_ERR_UNSUPPORTED;
   if (!x || !y || !ws || (L.is_mx && !x_scales)) return QG_ERR_INVALID_ARGUMENT;
   if (ldx < d.k || ldy < d.n) return QG_ERR_SHAPE;
-  const int xel = L.is_mx ? 1 : 2;
   const int yel = otype == QG_O_F32 ? 4 : 2;
-  if (!aligned16(x) || !aligned16(y) || (ldx * xel) % 16 != 0 || (ldy * yel) % 4 != 0 ||
+  if (!aligned16(x) || !aligned16(y) || x_pitch(L, ldx) % 16 != 0 || (L.a4 && (ldx & 1)) || (ldy * yel) % 4 != 0 ||
       ((uintptr_t)ws & 255u) != 0)
     return QG_ERR_ALIGNMENT;
+  if (L.is_mx && (uint64_t)m * x_pitch(L, ldx) >= (1ull << 32)) return QG_ERR_UNSUPPORTED;
   if (flush && (flush_bytes % 16 != 0 || !aligned16(flush))) return QG_ERR_ALIGNMENT;
   std::vector<Variant> cand;
   tune_candidates(*w, m, &cand);

@@ -56,6 +56,9 @@ namespace qg {
 // skinny kernel, the codes dequantized to exact bf16 by the fp4 conversion.
 inline bool mx_a8(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_MXFP8; }
 inline bool fp4_a16(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_BF16; }
+// MXFP4 weights with MXFP4 activations (W4A4): the MX layout, the large-M MX
+// kernel with e2m1 A operands, dense layers only.
+inline bool mx_a4(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_MXFP4; }
 
 constexpr int kTileN = 16;    // N per tile
 constexpr int kBlockK = 128;  // K per block
@@ -68,7 +71,8 @@ struct Layout {
   int kb_pad = 0;         // k_blocks rounded up to 4
   int bits = 0;
   bool has_zp = false;
-  bool is_mx = false;     // MX kernels (MXFP4 x MXFP8)
+  bool is_mx = false;     // MX kernels (MXFP4 x MXFP8, or x MXFP4 with a4)
+  bool a4 = false;        // MXFP4 activations (two e2m1 codes per byte)
   bool fp4 = false;       // MXFP4 weights x bf16 activations (integer-format layout, bf16 scales)
   uint64_t block_bytes = 0;
   uint64_t codes_bytes = 0;
@@ -172,8 +176,10 @@ constexpr int kMoeTileRows = 128;
 constexpr int kMoeSmallTileRows = 64;
 // Dense launches first regroup the activation scales by K step into ws
 // (mx_tiled_ws_bytes); MoE launches read them in place.
+// a4: the activations are e2m1 (a.ldx then counts bytes, K / 2 per row
+// minimum); dense only.
 hipError_t launch_mx_tiled(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
-                           void *ws, hipStream_t s);
+                           void *ws, hipStream_t s, bool a4 = false);
 uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks);
 int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // Integer formats at large M: group row sums of X into ws, then the tiled
@@ -197,6 +203,8 @@ hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipSt
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 // Activation-side kernels (qg_act.hip): bf16 -> MXFP8, SiLU-gated product,
 // weighted top-k combine.  Shapes and alignment are validated by the callers.
+hipError_t launch_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
+                                 void *qs, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
                                  void *qs, hipStream_t s);
 hipError_t launch_silu_mul(const void *gu, bool gu_f32, int64_t rows, int64_t inter, int64_t ldgu, bool mx,

@@ -19,7 +19,7 @@ qg_status make_layout(const qg_layer_desc *d, Layout *out) {
   if (d->abi_version != QG_ABI_VERSION) return QG_ERR_INVALID_ARGUMENT;
   if (d->wtype < QG_W_INT4 || d->wtype > QG_W_MXFP4) return QG_ERR_INVALID_ARGUMENT;
   if (d->stype < QG_S_BF16 || d->stype > QG_S_E8M0) return QG_ERR_INVALID_ARGUMENT;
-  if (d->atype < QG_A_BF16 || d->atype > QG_A_MXFP8) return QG_ERR_INVALID_ARGUMENT;
+  if (d->atype < QG_A_BF16 || d->atype > QG_A_MXFP4) return QG_ERR_INVALID_ARGUMENT;
   if (d->n <= 0 || d->k <= 0 || d->num_experts <= 0 || d->group_size <= 0) return QG_ERR_SHAPE;
   if (d->n > (1 << 24) || d->k > (1 << 24) || d->num_experts > 4096) return QG_ERR_UNSUPPORTED;
   if (d->k % 32 != 0 || d->k % d->group_size != 0) return QG_ERR_SHAPE;
@@ -32,9 +32,13 @@ qg_status make_layout(const qg_layer_desc *d, Layout *out) {
   } else {
     if (d->stype != QG_S_E8M0 || d->group_size != 32) return QG_ERR_UNSUPPORTED;
     L.bits = 4;
-    // MXFP8 activations: the MX layout; bf16 activations: the 4-bit integer
-    // layout with each e8m0 scale stored as its (exact) bf16 power of two
-    L.is_mx = d->atype == QG_A_MXFP8;
+    // MXFP8 or MXFP4 activations: the MX layout (W4A4 only for dense layers
+    // with K % 128 == 0: the large-M MX kernel serves it); bf16 activations:
+    // the 4-bit integer layout with each e8m0 scale stored as its (exact) bf16
+    // power of two
+    if (d->atype == QG_A_MXFP4 && (d->num_experts != 1 || d->k % kBlockK != 0)) return QG_ERR_UNSUPPORTED;
+    L.is_mx = d->atype == QG_A_MXFP8 || d->atype == QG_A_MXFP4;
+    L.a4 = d->atype == QG_A_MXFP4;
     L.fp4 = d->atype == QG_A_BF16;
   }
   L.n_tiles = (int)((d->n + kTileN - 1) / kTileN);

@@ -38,6 +38,13 @@
 // workgroup barrier.  Inside a K step the next row
 // block's LDS reads are scheduled ahead of the current block's 8 MFMAs.
 //
+// W4A4 (A4: MXFP4 activations, the announcement's "W8A8 / W4A8 / W4A4"
+// section): the same kernel with e2m1 A operands.  A row holds 64 bytes per K
+// step, a lane's operand is the 16 bytes of K 32q .. 32q + 31 (the layout the
+// packed weights use for B), and each row's four 16-byte chunks sit at slot
+// c ^ ((row >> 1) & 3), so the eight lanes of one LDS read phase (rows r .. r
+// + 7, one chunk) cover all 128 bytes of a bank row.
+//
 // Work order: workgroups are dealt round-robin to the 8 XCDs; the tile index
 // is remapped so each XCD owns a contiguous range of a grouped (GM m-tiles at
 // a time) raster, so the tiles running together on one XCD share activation
@@ -53,15 +60,26 @@ namespace qg {
 
 constexpr int kStages = 3;
 
+// acc += (e2m1 A, e8m0 scale sa) x (e2m1 B, e8m0 scale: byte SB of sb_word)
+extern "C" __device__ f32x4 qg_mfma_scale_16x16x128_f4_f4(i32x4 a, i32x4 b, f32x4 c, int fmt_a, int fmt_b,
+                                                          int opsel_a, int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
+
+template <int SB>
+__device__ __forceinline__ f32x4 mfma_e2m1_e2m1(i32x4 a, i32x4 b, f32x4 c, int sa, int sb_word) {
+  return qg_mfma_scale_16x16x128_f4_f4(a, b, c, 4, 4, 0, sa, SB, sb_word);
+}
+
 // BM x BN tile, WM x WN waves, each wave (BM / WM) x (BN / WN).  SAR: the
 // activation scales go to a two-slot ring of 4-step runs (16 bytes per row)
-// instead of 4 bytes per row in every stage.
-template <int BM, int BN, int WM, int WN, bool SAR>
+// instead of 4 bytes per row in every stage.  A4: e2m1 activations.
+template <int BM, int BN, int WM, int WN, bool SAR, bool A4 = false>
 struct MxCfg {
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int NBLK = BN / 16;                      // packed n-tiles per tile
-  static constexpr int A = BM * 128;
+  static constexpr int AROW = A4 ? 64 : 128;                // A bytes per row and K step
+  static constexpr int A = BM * AROW;
   static constexpr int B = NBLK * 1024;
   static constexpr int SA = SAR ? 0 : BM * 4;
   static constexpr int SW_PIECES = (NBLK + 3) / 4;          // 1-KB copies: 4 n-tiles' 256-B units each
@@ -71,21 +89,22 @@ struct MxCfg {
   static constexpr int SAR_SLOT = SAR ? BM * 16 : 0;        // [row][4 steps x 4 bytes]
   static constexpr int OFF_SAR = OFF_SW + 2 * SW;           // the two SA ring slots
   static constexpr int LDS = OFF_SAR + 2 * SAR_SLOT;
-  static constexpr int A_LOADS = BM * 128 / 1024 / WAVES;  // 1-KB copies of A per wave
+  static constexpr int A_LOADS = BM * AROW / 1024 / WAVES;  // 1-KB copies of A per wave
   static constexpr int B_LOADS = (NBLK + WAVES - 1) / WAVES;  // 1-KB blocks of B per wave
   static constexpr int SA_WAVES = BM / 64;                  // waves that copy a 256-B SA piece
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int MB = BM / WM / 16;                   // 16-row blocks per wave
   static constexpr int NB = BN / WN / 16;                   // 16-column blocks per wave
   static_assert(BN % (16 * WN) == 0, "column blocks per wave");
-  static_assert(A_LOADS >= 1 && BM * 128 % (1024 * WAVES) == 0, "A copies per wave");
+  static_assert(A_LOADS >= 1 && BM * AROW % (1024 * WAVES) == 0, "A copies per wave");
   static_assert(WAVES >= SA_WAVES && WAVES >= SW_PIECES, "SA / SW pieces");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int WM, int WN, bool MOE, bool SAR>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4>
 __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
-  using C = MxCfg<BM, BN, WM, WN, SAR>;
+  using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
+  static_assert(!(A4 && MOE), "e2m1 activations: dense launches only");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -107,9 +126,16 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   uint32_t a_off[C::A_LOADS];
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
-    const int row = 8 * (wave * C::A_LOADS + i) + (lane >> 3);
-    const int c = (lane & 7) ^ (row & 7);
-    a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
+    if constexpr (A4) {
+      // 16 rows of 4 chunks per copy: lane -> row lane / 4, slot lane % 4
+      const int row = 16 * (wave * C::A_LOADS + i) + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 1) & 3);
+      a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
+    } else {
+      const int row = 8 * (wave * C::A_LOADS + i) + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7);
+      a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
+    }
   }
   const uint8_t *b_base = wexp + 16 * lane;
   // copy i of this wave: tile block (and LDS slot) min(B_LOADS wave + i, NBLK - 1)
@@ -142,7 +168,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 
   auto issue = [&](int kb, int buf) {
     uint8_t *st = smem + buf * C::STAGE;
-    const uint8_t *xk = x + kb * 128;
+    const uint8_t *xk = x + kb * C::AROW;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
       lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
@@ -203,19 +229,31 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
       if constexpr (S == 0)  // the SW slot of steps kb .. kb + 3 landed with stage kb
         swv[j] = *(const uint32_t *)(smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW + ((blk * 16 + r16) * 4 + q) * 4);
     }
-    auto read_a = [&](int i, i32x8 &af, int &asc) {
+    using AFrag = std::conditional_t<A4, i32x4, i32x8>;
+    auto read_a = [&](int i, AFrag &af, int &asc) {
       const int row = wm * (BM / WM) + i * 16 + r16;
-      const uint8_t *ap = st + row * 128;
-      const u32x4 lo = *(const u32x4 *)(ap + 16 * (q ^ (row & 7)));
-      const u32x4 hi = *(const u32x4 *)(ap + 16 * ((4 + q) ^ (row & 7)));
-      af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const uint8_t *ap = st + row * C::AROW;
+      if constexpr (A4) {
+        const u32x4 v = *(const u32x4 *)(ap + 16 * (q ^ ((row >> 1) & 3)));
+        af = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      } else {
+        const u32x4 lo = *(const u32x4 *)(ap + 16 * (q ^ (row & 7)));
+        const u32x4 hi = *(const u32x4 *)(ap + 16 * ((4 + q) ^ (row & 7)));
+        af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
       if constexpr (SAR)
         asc = smem[C::OFF_SAR + ((kb >> 2) & 1) * C::SAR_SLOT + 16 * row + 4 * (kb & 3) + q];
       else
         asc = st[C::A + C::B + 4 * row + q];
     };
-    i32x8 af[2];
+    auto mma = [&](const AFrag &af, const i32x4 &bf, f32x4 c, int sa, int sb) {
+      if constexpr (A4)
+        return mfma_e2m1_e2m1<S>(af, bf, c, sa, sb);
+      else
+        return mfma_e4m3_e2m1<S>(af, bf, c, sa, sb);
+    };
+    AFrag af[2];
     int asc[2];
     if constexpr (WM == 1) {
       // small tiles (MoE experts with few rows): row blocks past the tile's
@@ -227,21 +265,23 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
           read_a(i, af[0], asc[0]);
 #pragma unroll
           for (int j = 0; j < C::NB; ++j)
-            acc[i][j] = mfma_e4m3_e2m1<S>(af[0], bf[j], acc[i][j], asc[0], (int)swv[j]);
+            acc[i][j] = mma(af[0], bf[j], acc[i][j], asc[0], (int)swv[j]);
         }
       }
       return;
     }
     read_a(0, af[0], asc[0]);
-    // B (NB reads, plus NB scale dwords every fourth step) and A block 0 (3 reads) first
-    __builtin_amdgcn_sched_group_barrier(0x100, (S == 0 ? 2 : 1) * C::NB + 3, 0);
+    // B (NB reads, plus NB scale dwords every fourth step) and A block 0 (3
+    // reads; 2 for e2m1) first
+    constexpr int AR = A4 ? 2 : 3;
+    __builtin_amdgcn_sched_group_barrier(0x100, (S == 0 ? 2 : 1) * C::NB + AR, 0);
 #pragma unroll
     for (int i = 0; i < C::MB; ++i) {
       if (i + 1 < C::MB) read_a(i + 1, af[(i + 1) & 1], asc[(i + 1) & 1]);
 #pragma unroll
       for (int j = 0; j < C::NB; ++j)
-        acc[i][j] = mfma_e4m3_e2m1<S>(af[i & 1], bf[j], acc[i][j], asc[i & 1], (int)swv[j]);
-      if (i + 1 < C::MB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // next block's reads
+        acc[i][j] = mma(af[i & 1], bf[j], acc[i][j], asc[i & 1], (int)swv[j]);
+      if (i + 1 < C::MB) __builtin_amdgcn_sched_group_barrier(0x100, AR, 0);  // next block's reads
       __builtin_amdgcn_sched_group_barrier(0x008, C::NB, 0);                // this block's MFMAs
     }
   };
@@ -290,16 +330,16 @@ uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) {
   return (uint64_t)((m + 255) & ~(int64_t)255) * (uint64_t)k_blocks * 4;
 }
 
-template <int BM, int BN, int WM, int WN, bool MOE, bool SAR>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4 = false>
 static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
-  using C = MxCfg<BM, BN, WM, WN, SAR>;
+  using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
   static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MB, C::NB>(), "epilogue LDS");
   const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
   const int64_t n_tiles_wg = (a.n_tiles + C::NBLK - 1) / C::NBLK;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR>;
+  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR, A4>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::THREADS), lds, s, a);
@@ -326,19 +366,38 @@ static hipError_t launch_mx_shape(const GemmArgs &a, int bm, int bn, bool moe, i
                    : launch_mx_tiled_bm<128, 256, 2, 2, false, SAR>(a, 0, s);
 }
 
+// Dense e2m1 activations: the same tile shapes as dense MXFP8.
+template <bool SAR>
+static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, int waves, hipStream_t s) {
+  if (waves == 8) {
+    if (bm == 256) {
+      if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false, SAR, true>(a, 0, s);
+      if (bn == 224) return launch_mx_tiled_bm<256, 224, 4, 2, false, SAR, true>(a, 0, s);
+      return launch_mx_tiled_bm<256, 256, 4, 2, false, SAR, true>(a, 0, s);
+    }
+    if (bn == 192) return launch_mx_tiled_bm<128, 192, 4, 2, false, SAR, true>(a, 0, s);
+    if (bn == 224) return launch_mx_tiled_bm<128, 224, 4, 2, false, SAR, true>(a, 0, s);
+    return launch_mx_tiled_bm<128, 256, 4, 2, false, SAR, true>(a, 0, s);
+  }
+  return bm == 256 ? launch_mx_tiled_bm<256, 256, 2, 2, false, SAR, true>(a, 0, s)
+                   : launch_mx_tiled_bm<128, 256, 2, 2, false, SAR, true>(a, 0, s);
+}
+
 // Dense: bm-row tiles (128 or 256) of bn columns (192, 224 or 256 with 8
 // waves; 256 with 4).  MoE: the tile list a.tiles (capacity tiles_cap) of
 // kMoeTileRows x 256 tiles, or (bm = 64, 8 waves) 64 x 128 small tiles, one
 // wave per 16 columns and all rows, for experts with few rows.  The
 // activation scales go through the SA ring when K % 512 == 0 and they are
 // 16-byte aligned; otherwise dense launches first regroup them by K step into
-// ws and MoE launches copy 4 bytes per row and step.
+// ws and MoE launches copy 4 bytes per row and step.  a4: e2m1 activations
+// (dense only; a.ldx in bytes).
 hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
-                           void *ws, hipStream_t s) {
-  if (a_in.k % 128 != 0) return hipErrorInvalidValue;
+                           void *ws, hipStream_t s, bool a4) {
+  if (a_in.k % 128 != 0 || (a4 && moe)) return hipErrorInvalidValue;
   GemmArgs a = a_in;
   const bool sar = a.k % 512 == 0 && ((uintptr_t)a.x_scales & 15) == 0;
-  if (sar) return launch_mx_shape<true>(a, bm, bn, moe, tiles_cap, waves, s);
+  if (sar) return a4 ? launch_mx_shape_a4<true>(a, bm, bn, waves, s)
+                     : launch_mx_shape<true>(a, bm, bn, moe, tiles_cap, waves, s);
   if (!moe) {
     if (!ws) return hipErrorInvalidValue;
     hipLaunchKernelGGL(mx_scales_by_step_kernel, dim3((unsigned)((a.m + 15) / 16), (unsigned)((a.k_blocks + 63) / 64)),
@@ -348,7 +407,8 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
     if (e != hipSuccess) return e;
     a.x_scales_t = (const uint32_t *)ws;
   }
-  return launch_mx_shape<false>(a, bm, bn, moe, tiles_cap, waves, s);
+  return a4 ? launch_mx_shape_a4<false>(a, bm, bn, waves, s)
+            : launch_mx_shape<false>(a, bm, bn, moe, tiles_cap, waves, s);
 }
 
 }  // namespace qg

@@ -44,10 +44,10 @@ class Layer:
     """A (possibly multi-expert) quantized weight in standard format plus its
     packed device copy."""
 
-    def __init__(self, wtype, n, k, group, seed=0, experts=1, active=None):
+    def __init__(self, wtype, n, k, group, seed=0, experts=1, active=None, atype=None):
         self.wtype, self.n, self.k, self.group, self.experts = wtype, n, k, group, experts
         self.mx = wtype == qg.W_MXFP4
-        self.desc = qg.layer_desc(wtype, n, k, group, num_experts=experts)
+        self.desc = qg.layer_desc(wtype, n, k, group, atype=atype, num_experts=experts)
         self.buf = torch.empty(qg.packed_size(self.desc), dtype=torch.uint8, device="cuda")
         self.std = {}
         ids = range(experts) if active is None else sorted(set(int(e) for e in active))

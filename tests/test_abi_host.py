@@ -46,6 +46,10 @@ def _desc(**kw):
     (dict(wtype=qg.W_MXFP4, group_size=128), qg.QG_ERR_UNSUPPORTED),
     (dict(stype=qg.S_E8M0), qg.QG_ERR_UNSUPPORTED),
     (dict(wtype=9), qg.QG_ERR_INVALID_ARGUMENT),
+    (dict(atype=3), qg.QG_ERR_INVALID_ARGUMENT),
+    (dict(atype=qg.A_MXFP4), qg.QG_ERR_UNSUPPORTED),     # INT4 x MXFP4: no kernel
+    (dict(wtype=qg.W_MXFP4, group_size=32, atype=qg.A_MXFP4, k=544), qg.QG_ERR_UNSUPPORTED),  # W4A4: K % 128
+    (dict(wtype=qg.W_MXFP4, group_size=32, atype=qg.A_MXFP4, num_experts=2), qg.QG_ERR_UNSUPPORTED),  # dense only
 ])
 def test_descriptor_validation(kw, status):
     with pytest.raises(qg.QGError) as e:
@@ -439,3 +443,54 @@ def test_repack_fp4_bf16_layout():
             c = int(sc[nn, g])
             expect = 0x0040 if c == 0 else 0x7FC0 if c == 255 else c << 7
             assert s16[nn, g] == expect, (nn, g)
+
+
+def test_w4a4_host_logic():
+    d = qg.layer_desc(qg.W_MXFP4, 256, 512, 32, atype=qg.A_MXFP4)
+    # the weight layout is the W4A8 one
+    assert qg.packed_size(d) == qg.packed_size(qg.layer_desc(qg.W_MXFP4, 256, 512, 32))
+    w = _bound(d)
+    # the MX tiled kernel at every M, with its scales scratch
+    for m in (1, 7, 130, 4096):
+        assert qg.describe_dispatch(w, m).startswith("mx_tiled"), m
+        assert qg.gemm_workspace_size(w, m) > 0
+    assert qg.describe_dispatch(w, 1) == qg.describe_dispatch(w, 1)
+    F, S = FAKE_DEV, 0
+    cases = [
+        (dict(ldx=513), qg.QG_ERR_ALIGNMENT),      # odd: half a byte per row
+        (dict(ldx=528), qg.QG_ERR_ALIGNMENT),      # 264-byte rows
+        (dict(ldx=500), qg.QG_ERR_SHAPE),
+        (dict(xs=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(m=1 << 24, ldx=512), qg.QG_ERR_UNSUPPORTED),  # 4 GiB of e2m1 rows
+    ]
+    for kw, status in cases:
+        a = dict(m=4, ldx=512, xs=F)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.gemm(w, F, a["xs"], a["m"], a["ldx"], F, qg.O_BF16, 256, F, 1 << 40, stream=S)
+        assert e.value.status == status, kw
+    # MXFP8 rows spanning 4 GiB are refused too (32-bit activation offsets)
+    w8 = _bound(qg.layer_desc(qg.W_MXFP4, 256, 1024, 32))
+    with pytest.raises(qg.QGError) as e:
+        qg.gemm(w8, F, F, 1 << 22, 1024, F, qg.O_BF16, 256, F, 1 << 40, stream=S)
+    assert e.value.status == qg.QG_ERR_UNSUPPORTED
+    # MoE calls on a W4A4 layer
+    with pytest.raises(qg.QGError) as e:
+        qg.moe_workspace_size(w, 16, 1)
+    assert e.value.status == qg.QG_ERR_UNSUPPORTED
+    # quantizer validation
+    qg.quantize_mxfp4(None, 0, 64, 64, None, 64, None, stream=S)
+    q_cases = [
+        (dict(k=48), qg.QG_ERR_SHAPE),
+        (dict(ldq=32), qg.QG_ERR_SHAPE),
+        (dict(qs=None), qg.QG_ERR_INVALID_ARGUMENT),
+        (dict(q=F + 2), qg.QG_ERR_ALIGNMENT),
+        (dict(ldq=68), qg.QG_ERR_ALIGNMENT),
+        (dict(x=F + 8), qg.QG_ERR_ALIGNMENT),
+    ]
+    for kw, status in q_cases:
+        a = dict(x=F, rows=4, k=64, ldx=64, q=F, ldq=64, qs=F)
+        a.update(kw)
+        with pytest.raises(qg.QGError) as e:
+            qg.quantize_mxfp4(a["x"], a["rows"], a["k"], a["ldx"], a["q"], a["ldq"], a["qs"], stream=S)
+        assert e.value.status == status, kw
