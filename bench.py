@@ -603,6 +603,32 @@ def main():
                     "dispatch": qg.describe_dispatch(wts[0], mm)}
             del bufs, wts
         print(f"[bench] extra MXFP4 x bf16 decode done", file=sys.stderr, flush=True)
+        # MXFP4 weights x MX activations at the decode shapes: W4A8 (MXFP8) on
+        # the MX skinny kernel, W4A4 (MXFP4) widened to e4m3 in the workspace
+        # and then the same kernel (the widening launch is inside the timing)
+        for i, (n, k) in enumerate(shapes):
+            codes, sc, _ = synth.mx_weights(synth.rng(70 + i, 1), n, k)
+            wbytes = weight_bytes(n, k, 4, 32, False, 1)
+            for atype, name in ((qg.A_MXFP8, "w4a8_mx"), (qg.A_MXFP4, "w4a4_mx")):
+                desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=atype)
+                bufs = [torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda") for _ in range(ROTATE)]
+                wts = [qg.preprocess(desc, codes, sc, None, b) for b in bufs]
+                for mm in (1, 16):
+                    xb = k if atype == qg.A_MXFP8 else k // 2
+                    xm = torch.randint(0, 256, (mm, xb), dtype=torch.uint8, device="cuda")
+                    xms = torch.randint(118, 128, (mm, k // 32), dtype=torch.uint8, device="cuda")
+                    y = torch.empty((mm, n), dtype=torch.bfloat16, device="cuda")
+                    wsb = qg.gemm_workspace_size(wts[0], mm)
+                    wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+                    stream = torch.cuda.current_stream().cuda_stream
+                    t = timed(torch, lambda j: qg.gemm(wts[j % ROTATE], xm, xms, mm, k, y, qg.O_BF16, n, wsp, wsb,
+                                                        stream), 100, 10)
+                    extra[f"{name}_M{mm}_N{n}_K{k}"] = {
+                        "us": round(t * 1e3, 2), "weight_GBs": round(wbytes / (t * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(wbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "dispatch": qg.describe_dispatch(wts[0], mm)}
+                del bufs, wts
+        print(f"[bench] extra MX-activation decode done", file=sys.stderr, flush=True)
         # the batch-invariant compute option at decode sizes (one kernel for every M)
         for i, (n, k) in enumerate(shapes):
             L = layers[i]

@@ -53,7 +53,7 @@ static bool env_variant(Variant *v) {
 // (T, KR) = (4, 2) for the integer formats, T * KR <= 8 but not (4, 4) for MX.
 static bool variant_ok(const qg_layer_desc &d, int T, int KR) {
   if ((T != 1 && T != 2 && T != 4) || (KR != 1 && KR != 2 && KR != 4)) return false;
-  if (mx_a8(d)) return T * KR <= 8 && !(T == 4 && KR == 4);
+  if (mx_a8(d) || mx_a4(d)) return T * KR <= 8 && !(T == 4 && KR == 4);
   return T * KR <= 4 || (T == 4 && KR == 2);
 }
 
@@ -71,7 +71,7 @@ static int clamp_kr(const qg_layer_desc &d, int T, int kr) {
 // (which costs a partials round trip and a counter-clearing launch) unless N
 // alone gives too few workgroups.
 static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles) {
-  const bool mx = mx_a8(d);
+  const bool mx = mx_a8(d) || mx_a4(d);
   // T x KR per wave: 4 x 2 (integer formats), 2 x 4 (MX); fewer for short K.
   // Measured on the decode shapes: fewer, fuller workgroups beat more, emptier
   // ones (224 workgroups of 8 KB waves beat 448 of 4 KB), so T shrinks only
@@ -267,7 +267,7 @@ static bool same_variant(const Variant &a, const Variant &b) {
 static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
   const qg_layer_desc &d = w.desc;
   const bool mx = mx_a8(d) || mx_a4(d);
-  if (mx_a4(d) && v.kind != 1) return false;  // W4A4: the MX tiled kernel only
+  if (mx_a4(d) && v.kind != 1 && v.kind != 0) return false;  // W4A4: MX tiled, or MX skinny on widened rows
   switch (v.kind) {
     case 0:
       return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 && covers(v, w.k_blocks);
@@ -323,9 +323,13 @@ Variant select_dense(const qg_weight &w, int64_t m) {
 static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
   Variant v;
   if (mx_a4(w.desc)) {
-    // the one kernel with e2m1 activations (whatever QG_TILED says)
-    const int bm = m >= 256 ? 256 : 128;
-    return Variant{1, 1, 1, 1, 1, bm, mx_tile_cols(w.desc.n, m, bm)};
+    // from 128 rows the tiled kernel with e2m1 operands; below, the MXFP8
+    // skinny kernel on the rows widened exactly to e4m3 in the workspace
+    if (m >= 128) {
+      const int bm = m >= 256 ? 256 : 128;
+      return Variant{1, 1, 1, 1, 1, bm, mx_tile_cols(w.desc.n, m, bm)};
+    }
+    return skinny_for(w.desc, w.n_tiles, w.k_blocks, (m + 15) / 16);
   }
   if (tiled_for(w, m, &v)) return v;
   if (!getenv("QG_TUNE") && decode_for(w, m, &v)) return v;
@@ -489,16 +493,25 @@ static void fill_weight(const qg_layer_desc *d, const Layout &L, void *dev, uint
   out->zeros_offset = L.has_zp ? L.zeros_offset : 0;
 }
 
-static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) {
-  if (m <= 0) return 0;
-  if (v.kind == 2) return a16_tiled_ws_bytes(w.desc, m);
-  if (v.kind == 1) return mx_tiled_ws_bytes(m, w.k_blocks);
+// Split-K counters (256-byte aligned) and fp32 partial tiles of a skinny or
+// decode launch; a multiple of 256 bytes.
+static uint64_t split_region_bytes(const qg_weight &w, const Variant &v, int64_t m) {
   if (v.splits <= 1) return 0;
   const int64_t m_tiles = (m + 15) / 16;
   const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
   const uint64_t counters = align_up((uint64_t)m_tiles * n_blocks * 4, 256);
   const uint64_t partials = (uint64_t)v.splits * m_tiles * n_blocks * (uint64_t)v.T * 256 * 4;
   return counters + partials;
+}
+
+static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) {
+  if (m <= 0) return 0;
+  if (v.kind == 2) return a16_tiled_ws_bytes(w.desc, m);
+  if (v.kind == 1) return mx_tiled_ws_bytes(m, w.k_blocks);
+  const uint64_t split = split_region_bytes(w, v, m);
+  // W4A4 through the skinny kernel: the rows widened to e4m3 follow
+  if (mx_a4(w.desc) && v.kind == 0) return split + align_up((uint64_t)m * w.desc.k, 256);
+  return split;
 }
 
 static void base_args(const qg_weight &w, GemmArgs *a) {
@@ -634,6 +647,16 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
   if (v.kind == 1) {
     if (L.a4) a.ldx = ldx / 2;  // the kernel addresses e2m1 rows in bytes
     return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream, L.a4);
+  }
+  if (L.a4) {
+    // the split-K region (zero) first, then the rows widened to e4m3 (scratch):
+    // same values under the same scales for the MXFP8 skinny kernel
+    uint8_t *x8 = (uint8_t *)ws + split_region_bytes(w, v, m);
+    const hipError_t e = launch_widen_e2m1(x, m, d.k, ldx / 2, x8, d.k, stream);
+    if (e != hipSuccess) return e;
+    a.x = x8;
+    a.ldx = d.k;
+    return launch_dense_mx(a, d, v, stream);
   }
   if (v.kind == 3) return launch_decode_a16(a, d, v, stream);
   if (v.kind == 2) return launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), ws, true, stream);

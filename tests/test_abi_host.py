@@ -450,11 +450,17 @@ def test_w4a4_host_logic():
     # the weight layout is the W4A8 one
     assert qg.packed_size(d) == qg.packed_size(qg.layer_desc(qg.W_MXFP4, 256, 512, 32))
     w = _bound(d)
-    # the MX tiled kernel at every M, with its scales scratch
-    for m in (1, 7, 130, 4096):
+    # from 128 rows the MX tiled kernel (its scales scratch in the
+    # workspace); below, the MX skinny kernel on rows widened to e4m3 in the
+    # workspace (at least m * K bytes)
+    for m in (1, 7, 127):
+        assert qg.describe_dispatch(w, m).startswith("mx_skinny"), m
+        assert qg.gemm_workspace_size(w, m) >= m * 512
+    for m in (128, 130, 4096):
         assert qg.describe_dispatch(w, m).startswith("mx_tiled"), m
         assert qg.gemm_workspace_size(w, m) > 0
-    assert qg.describe_dispatch(w, 1) == qg.describe_dispatch(w, 1)
+    # the batch-invariant option keeps the tiled kernel at every M
+    assert qg.gemm_workspace_size_ex(w, 1, qg.GEMM_BATCH_INVARIANT) == qg.gemm_workspace_size(w, 256) // 256 * 256
     F, S = FAKE_DEV, 0
     cases = [
         (dict(ldx=513), qg.QG_ERR_ALIGNMENT),      # odd: half a byte per row

@@ -6,8 +6,9 @@ C ABI, against the CPU oracle.
   bit with the oracle (packed two per byte) over every finite bf16 pattern,
   over blocks whose maxima walk every scale exponent of the bf16 range, and
   on N(0, 1) rows with padded leading dimensions.
-* qg_gemm on W4A4 layers: the MX tiled kernel at every M (one row to several
-  256-row tiles), ragged N, K % 512 != 0 (scales regrouped by K step) and
+* qg_gemm on W4A4 layers: below 128 rows the rows widened exactly to e4m3
+  for the MX skinny kernel, from 128 the MX tiled kernel on e2m1 operands;
+  ragged N, K % 512 != 0 (scales regrouped by K step) and
   == 0 (scale ring), padded rows, unaligned scales; bf16 output within
   TOL_BF16 and fp32 within the scaled MFMA's bound (TOL_F32_MX) of the
   float64 product of the exact operands.
@@ -132,12 +133,34 @@ def check_a4(layer, acts, m):
         assert torch.isfinite(y.float()).all()
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 256, 512), (7, 136, 384), (130, 300, 1024), (300, 1000, 2048),
+@pytest.mark.parametrize("m,n,k", [(1, 256, 512), (7, 136, 384), (33, 300, 1024), (127, 512, 2048),
+                                   (1, 4096, 14336), (4, 14336, 4096), (130, 300, 1024), (300, 1000, 2048),
                                    (513, 448, 640), (256, 512, 4096)])
 def test_w4a4_gemm(m, n, k):
+    """Below 128 rows the rows are widened to e4m3 in the workspace for the
+    MX skinny kernel (long K: split over workgroups); from 128 the tiled
+    kernel takes the e2m1 operands directly."""
     layer = a4_layer(n, k, seed=m + n)
-    assert qg.describe_dispatch(layer.w, m).startswith("mx_tiled")
+    assert qg.describe_dispatch(layer.w, m).startswith("mx_skinny" if m < 128 else "mx_tiled")
     check_a4(layer, A4(m, k, seed=m + k), m)
+
+
+def test_w4a4_skinny_padded_rows_repeat_calls():
+    """Padded e2m1 rows through the widening path, two calls on one
+    workspace (its split-K counters must be left at zero), then a smaller M."""
+    n, k = 512, 8192
+    layer = a4_layer(n, k, seed=53)
+    ws_bytes = qg.gemm_workspace_size(layer.w, 16)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    print(f"  dispatch {qg.describe_dispatch(layer.w, 16)}", flush=True)
+    for m in (16, 16, 3):
+        acts = A4(m, k, seed=54 + m, ldx=k + 96)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        qg.gemm(layer.w, acts.x, acts.xs, m, acts.ldx, y, qg.O_F32, n, ws, ws_bytes)
+        torch.cuda.synchronize()
+        e = oracle.normwise_error(y.cpu().numpy().astype(np.float64), oracle.gemm(acts.xdq, layer.wdq()))
+        print(f"  m={m} err={e:.3e}", flush=True)
+        assert e <= TOL_F32_MX
 
 
 @pytest.mark.parametrize("m,k", [(300, 128), (300, 256), (130, 384), (257, 896)])
@@ -174,7 +197,9 @@ def test_w4a4_batch_invariant():
         assert torch.equal(y, y_big[rows]), m
 
 
-def test_w4a4_autotune_picks_mx_tiled():
+def test_w4a4_autotune():
+    """The tuner times the MX tiled kernel and the skinny kernel on widened
+    rows; whichever it keeps serves the next calls, within parity."""
     m, n, k = 64, 512, 1024
     layer = a4_layer(n, k, seed=49)
     acts = A4(m, k, seed=50)
@@ -185,7 +210,7 @@ def test_w4a4_autotune_picks_mx_tiled():
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
         desc, us = qg.gemm_autotune(layer.w, acts.x, acts.xs, m, k, y, qg.O_BF16, n, ws, ws_bytes, reps=3)
         print(f"  chose {desc} ({us:.2f} us)", flush=True)
-        assert desc.startswith("mx_tiled") and us > 0
+        assert desc.startswith(("mx_tiled", "mx_skinny")) and us > 0
         assert qg.describe_dispatch(layer.w, m) == desc
         check_a4(layer, acts, m)
     finally:
