@@ -216,6 +216,8 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
     if mx:
         x, xs = mx_acts_device(torch, tokens, k1, gen)
         h, hs = mx_acts_device(torch, p, k2, gen)
+        if atype == qg.A_MXFP4:  # two e2m1 codes per byte
+            x, h = x[:, :k1 // 2].contiguous(), h[:, :k2 // 2].contiguous()
     else:
         x = torch.randn((tokens, k1), device="cuda", generator=gen).to(torch.bfloat16)
         h = torch.randn((p, k2), device="cuda", generator=gen).to(torch.bfloat16)
@@ -659,6 +661,10 @@ def main():
             moe[f"w4a8_E128_top8_T{tokens}"] = bench_moe(
                 qg, synth, torch, "moe_w4a8", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
                 iters=5 if tokens > 512 else 30)
+        for tokens in (64, 4096):
+            moe[f"w4a4_E128_top8_T{tokens}"] = bench_moe(
+                qg, synth, torch, "moe_w4a4", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
+                iters=5 if tokens > 512 else 30, atype=qg.A_MXFP4)
         extra["moe"] = moe
         out["extra"] = extra
 

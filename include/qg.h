@@ -106,9 +106,12 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
  *   MXFP4, E8M0 scales, BF16 activations, group 32 (each code dequantized in
  *   the kernel to the exact bf16 e2m1 * 2^(e-127); the announcement's
  *   "Choosing the activation type": MXFP4 checkpoints on a bf16 compute path);
- *   MXFP4, E8M0 scales, MXFP4 activations, group 32, K % 128 == 0, dense
- *   layers only (W4A4: both operands e2m1 into the scaled MFMA; the
- *   announcement's "W8A8 / W4A8 / W4A4" section runs all three MX pairings).
+ *   MXFP4, E8M0 scales, MXFP4 activations, group 32, K % 128 == 0 (W4A4, the
+ *   announcement's "W8A8 / W4A8 / W4A4" section: dense calls from 128 rows
+ *   put both e2m1 operands into the scaled MFMA; below 128 rows, and in
+ *   qg_moe_gemm, the activation rows are first widened to e4m3 in the
+ *   workspace -- every e2m1 value is an e4m3 value under the same scale --
+ *   and the W4A8 kernels run on them).
  * Other valid combinations return QG_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t abi_version; /* must be QG_ABI_VERSION */
@@ -265,8 +268,8 @@ qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, int32_t topk,
  * x, x_scales, y as in qg_gemm with ldx = K and ldy = N (dense rows).
  * ws: device, 256-B aligned, at least qg_moe_workspace_size bytes (holds the
  * tile list of the large-expert kernel and, for integer formats, the group
- * row sums of x; overwritten by every call, so calls sharing one ws must be
- * ordered on one stream).
+ * row sums of x, for W4A4 the rows of x widened to e4m3; overwritten by every
+ * call, so calls sharing one ws must be ordered on one stream).
  * More than 1024 experts: QG_ERR_UNSUPPORTED (here and in qg_moe_sort).
  * Asynchronous on `stream`. */
 qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, int32_t x_rows,

@@ -718,18 +718,28 @@ extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x
   return hip_status(launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, ws, stream));
 }
 
+// The weight as the kernels see it: a W4A4 layer runs as W4A8 (the packed
+// layout is the same) on its activation rows widened exactly to e4m3.
+static qg_weight mx_kernel_weight(const qg_weight &w, const Layout &L) {
+  qg_weight k = w;
+  if (L.a4) k.desc.atype = QG_A_MXFP8;
+  return k;
+}
+
 extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
                                            uint64_t *bytes) {
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
   if (!bytes || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
-  if (L.a4) return QG_ERR_UNSUPPORTED;  // W4A4 is dense only
   const int64_t pairs = num_tokens * topk;
   // the sort's need, or the grouped GEMM's with X indexed by pair (the larger
-  // of the two x row counts)
-  *bytes = std::max<uint64_t>(align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256),
-                              moe_ws_bytes(*w, pairs, pairs, moe_tiled_min_rows(*w, pairs, pairs)));
+  // of the two x row counts); W4A4: the MXFP8 path's need, then the rows
+  // widened to e4m3
+  const qg_weight wk = mx_kernel_weight(*w, L);
+  uint64_t gemm = moe_ws_bytes(wk, pairs, pairs, moe_tiled_min_rows(wk, pairs, pairs));
+  if (L.a4) gemm = align_up(gemm, 256) + (uint64_t)pairs * w->desc.k;
+  *bytes = std::max<uint64_t>(align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256), gemm);
   return QG_OK;
 }
 
@@ -756,10 +766,11 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
-  const qg_layer_desc &d = w->desc;
+  // W4A4: everything below runs the W4A8 path on rows widened into ws
+  const qg_weight wk = mx_kernel_weight(*w, L);
+  const qg_layer_desc &d = wk.desc;
   if (num_tokens < 0 || topk <= 0 || (otype != QG_O_BF16 && otype != QG_O_F32))
     return QG_ERR_INVALID_ARGUMENT;
-  if (L.a4) return QG_ERR_UNSUPPORTED;  // W4A4 is dense only
   if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
   if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
   if (d.num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
@@ -768,22 +779,29 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   if (pairs == 0) return QG_OK;
   if (!x || !y || !sorted_pair_ids || !expert_offsets) return QG_ERR_INVALID_ARGUMENT;
   if (L.is_mx && !x_scales) return QG_ERR_INVALID_ARGUMENT;
-  const int xel = L.is_mx ? 1 : 2;
   const int yel = otype == QG_O_F32 ? 4 : 2;
-  if (!aligned16(x) || !aligned16(y) || (d.k * xel) % 16 != 0 || (d.n * yel) % 4 != 0)
+  if (!aligned16(x) || !aligned16(y) || x_pitch(L, d.k) % 16 != 0 || (d.n * yel) % 4 != 0)
     return QG_ERR_ALIGNMENT;
-  const Variant v = select_moe(*w, pairs);
-  if (!covers(v, w->k_blocks)) return QG_ERR_UNSUPPORTED;  // K too long for one workgroup
+  const Variant v = select_moe(wk, pairs);
+  if (!covers(v, wk.k_blocks)) return QG_ERR_UNSUPPORTED;  // K too long for one workgroup
   const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
-  const int min_rows = moe_tiled_min_rows(*w, pairs, x_rows_count);
-  const uint64_t need = moe_ws_bytes(*w, pairs, x_rows_count, min_rows);
+  const int min_rows = moe_tiled_min_rows(wk, pairs, x_rows_count);
+  const uint64_t need_k = moe_ws_bytes(wk, pairs, x_rows_count, min_rows);
+  const uint64_t wide_off = align_up(need_k, 256);
+  const uint64_t need = L.a4 ? wide_off + (uint64_t)x_rows_count * d.k : need_k;
   if (need > 0) {
     if (!ws) return QG_ERR_INVALID_ARGUMENT;
     if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
     if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
   }
+  if (L.a4) {
+    uint8_t *x8 = (uint8_t *)ws + wide_off;
+    const hipError_t we = launch_widen_e2m1(x, x_rows_count, d.k, d.k / 2, x8, d.k, stream);
+    if (we != hipSuccess) return hip_status(we);
+    x = x8;
+  }
   GemmArgs a;
-  base_args(*w, &a);
+  base_args(wk, &a);
   a.x = x;
   a.x_scales = (const uint8_t *)x_scales;
   a.ldx = d.k;
@@ -799,9 +817,9 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   hipError_t he = hipSuccess;
   if (min_rows > 0) {
     // experts with >= min_rows rows: tile list, then the tiled kernel
-    const int64_t cap = moe_tiles_cap(*w, pairs, min_rows);
-    const bool small = moe_small_tiles(*w, pairs, min_rows);
-    const int64_t cap_s = small ? moe_small_tiles_cap(*w, pairs) : 0;
+    const int64_t cap = moe_tiles_cap(wk, pairs, min_rows);
+    const bool small = moe_small_tiles(wk, pairs, min_rows);
+    const int64_t cap_s = small ? moe_small_tiles_cap(wk, pairs) : 0;
     int32_t *tiles = (int32_t *)ws;
     int32_t *tiles_s = (int32_t *)((uint8_t *)ws + moe_list_bytes(cap));
     he = launch_moe_tiles(expert_offsets, d.num_experts, min_rows, 0, kMoeTileRows, (int32_t)pairs,

@@ -32,11 +32,10 @@ qg_status make_layout(const qg_layer_desc *d, Layout *out) {
   } else {
     if (d->stype != QG_S_E8M0 || d->group_size != 32) return QG_ERR_UNSUPPORTED;
     L.bits = 4;
-    // MXFP8 or MXFP4 activations: the MX layout (W4A4 only for dense layers
-    // with K % 128 == 0: the large-M MX kernel serves it); bf16 activations:
-    // the 4-bit integer layout with each e8m0 scale stored as its (exact) bf16
-    // power of two
-    if (d->atype == QG_A_MXFP4 && (d->num_experts != 1 || d->k % kBlockK != 0)) return QG_ERR_UNSUPPORTED;
+    // MXFP8 or MXFP4 activations: the MX layout (W4A4 needs K % 128 == 0,
+    // the MX tiled kernel's K step); bf16 activations: the 4-bit integer
+    // layout with each e8m0 scale stored as its (exact) bf16 power of two
+    if (d->atype == QG_A_MXFP4 && d->k % kBlockK != 0) return QG_ERR_UNSUPPORTED;
     L.is_mx = d->atype == QG_A_MXFP8 || d->atype == QG_A_MXFP4;
     L.a4 = d->atype == QG_A_MXFP4;
     L.fp4 = d->atype == QG_A_BF16;

@@ -13,6 +13,8 @@ C ABI, against the CPU oracle.
   TOL_BF16 and fp32 within the scaled MFMA's bound (TOL_F32_MX) of the
   float64 product of the exact operands.
 * Batch invariance, the autotuner's choice, and the quantize -> GEMM chain.
+* W4A4 MoE (rows widened to e4m3 in the workspace, then the W4A8 grouped
+  kernels) in every row mode and every split of the experts between kernels.
 """
 import numpy as np
 import pytest
@@ -237,3 +239,56 @@ def test_quantize4_then_w4a4_gemm():
     e_q = oracle.normwise_error(y.float().cpu().numpy().astype(np.float64),
                                 oracle.gemm(F.decode_bf16(xb), layer.wdq()))
     assert e_q < 0.5
+
+
+# ---------------------------------------------------------------------------
+# W4A4 MoE: the activation rows widened to e4m3 in the workspace, then the
+# W4A8 grouped kernels (every split of the experts between them)
+# ---------------------------------------------------------------------------
+
+def _moe_a4_layer(n, k, experts, seed):
+    return Layer(qg.W_MXFP4, n, k, 32, seed=seed, experts=experts, atype=qg.A_MXFP4)
+
+
+@pytest.mark.parametrize("split", ["skinny", "tiled", "mixed", "mixed_skinny", "small"])
+def test_w4a4_moe_all_row_modes(monkeypatch, split):
+    from test_gpu_moe import SPLITS, moe_reference, run_moe, sort_on_gpu
+    for var, val in SPLITS[split].items():
+        monkeypatch.setenv(var, val)
+    t, e, topk, n, k = 37, 16, 4, 80, 640
+    ids = synth.route(synth.rng(60, 0), t, e, topk)
+    layer = _moe_a4_layer(n, k, e, seed=61)
+    sorted_ids, offsets = sort_on_gpu(ids, e, layer)
+    acts = A4(t, k, seed=62)
+    ref = moe_reference(layer, acts.xdq, ids, True)
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
+        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+        err = oracle.normwise_error(y, ref)
+        print(f"  {split} by-token otype={otype} err={err:.3e}", flush=True)
+        assert err <= tol
+    h = A4(t * topk, k, seed=63)
+    y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
+    s = sorted_ids.cpu().numpy()
+    assert oracle.normwise_error(y, moe_reference(layer, h.xdq, ids, False)[s]) <= TOL_F32_MX
+    y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, qg.O_F32)
+    inv = np.empty_like(s)
+    inv[s] = np.arange(s.size)
+    ref2 = np.stack([h.xdq[inv[p]] @ layer.wdq(int(ids.reshape(-1)[p])).T for p in range(t * topk)])
+    assert oracle.normwise_error(y, ref2) <= TOL_F32_MX
+
+
+def test_w4a4_moe_multi_tile_experts():
+    """Skewed routing, experts over several 128-row tiles (tiled kernel) and
+    small ones (small tiles), N = 200 with a partial column tile."""
+    from test_gpu_moe import moe_reference, run_moe, sort_on_gpu
+    t, e, topk, n, k = 512, 8, 2, 200, 1024
+    ids = synth.route(synth.rng(64, 0), t, e, topk)
+    layer = _moe_a4_layer(n, k, e, seed=65)
+    sorted_ids, offsets = sort_on_gpu(ids, e, layer)
+    acts = A4(t, k, seed=66)
+    ref = moe_reference(layer, acts.xdq, ids, True)
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
+        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+        err = oracle.normwise_error(y, ref)
+        print(f"  multi-tile otype={otype} err={err:.3e}", flush=True)
+        assert err <= tol
