@@ -108,10 +108,11 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
  *   "Choosing the activation type": MXFP4 checkpoints on a bf16 compute path);
  *   MXFP4, E8M0 scales, MXFP4 activations, group 32, K % 128 == 0 (W4A4, the
  *   announcement's "W8A8 / W4A8 / W4A4" section: dense calls from 128 rows
- *   put both e2m1 operands into the scaled MFMA; below 128 rows, and in
- *   qg_moe_gemm, the activation rows are first widened to e4m3 in the
- *   workspace -- every e2m1 value is an e4m3 value under the same scale --
- *   and the W4A8 kernels run on them).
+ *   put both e2m1 operands into the scaled MFMA; below 128 rows the W4A8
+ *   skinny kernel widens each activation fragment to e4m3 in registers, and
+ *   qg_moe_gemm first widens the activation rows to e4m3 in the workspace --
+ *   every e2m1 value is an e4m3 value under the same scale -- and runs the
+ *   W4A8 grouped kernels on them).
  * Other valid combinations return QG_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t abi_version; /* must be QG_ABI_VERSION */

@@ -323,8 +323,8 @@ Variant select_dense(const qg_weight &w, int64_t m) {
 static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
   Variant v;
   if (mx_a4(w.desc)) {
-    // from 128 rows the tiled kernel with e2m1 operands; below, the MXFP8
-    // skinny kernel on the rows widened exactly to e4m3 in the workspace
+    // from 128 rows the tiled kernel with e2m1 operands; below, the MX skinny
+    // kernel, which widens each e2m1 fragment exactly to e4m3 in registers
     if (m >= 128) {
       const int bm = m >= 256 ? 256 : 128;
       return Variant{1, 1, 1, 1, 1, bm, mx_tile_cols(w.desc.n, m, bm)};
@@ -508,10 +508,7 @@ static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) 
   if (m <= 0) return 0;
   if (v.kind == 2) return a16_tiled_ws_bytes(w.desc, m);
   if (v.kind == 1) return mx_tiled_ws_bytes(m, w.k_blocks);
-  const uint64_t split = split_region_bytes(w, v, m);
-  // W4A4 through the skinny kernel: the rows widened to e4m3 follow
-  if (mx_a4(w.desc) && v.kind == 0) return split + align_up((uint64_t)m * w.desc.k, 256);
-  return split;
+  return split_region_bytes(w, v, m);
 }
 
 static void base_args(const qg_weight &w, GemmArgs *a) {
@@ -649,13 +646,8 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
     return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream, L.a4);
   }
   if (L.a4) {
-    // the split-K region (zero) first, then the rows widened to e4m3 (scratch):
-    // same values under the same scales for the MXFP8 skinny kernel
-    uint8_t *x8 = (uint8_t *)ws + split_region_bytes(w, v, m);
-    const hipError_t e = launch_widen_e2m1(x, m, d.k, ldx / 2, x8, d.k, stream);
-    if (e != hipSuccess) return e;
-    a.x = x8;
-    a.ldx = d.k;
+    // the MX skinny kernel widens the e2m1 fragments to e4m3 in registers
+    a.ldx = ldx / 2;
     return launch_dense_mx(a, d, v, stream);
   }
   if (v.kind == 3) return launch_decode_a16(a, d, v, stream);

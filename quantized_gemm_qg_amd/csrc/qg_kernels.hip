@@ -332,8 +332,22 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   for (int t = 0; t < T; ++t) acc[t] = c[t];
 }
 
-// MXFP4 weights x MXFP8 activations: one scaled MFMA per 16x128 block.
-template <int T, int KR, typename Hook = NoHook>
+// Four e2m1 codes (the low 16 bits of h, code i in bits 4i .. 4i + 3) -> the
+// four e4m3 bytes of the same values: every e2m1 magnitude (0, 0.5, 1, 1.5, 2,
+// 3, 4, 6) is an e4m3 value, looked up in an 8-byte table with v_perm_b32
+// (selector bytes 0-3 pick bytes of the second operand, 4-7 of the first);
+// the sign moves from bit 3 to bit 7.
+__device__ __forceinline__ uint32_t e2m1x4_to_e4m3(uint32_t h) {
+  const uint32_t n = (h & 0xFu) | ((h & 0xF0u) << 4) | ((h & 0xF00u) << 8) | ((h & 0xF000u) << 12);
+  const uint32_t mag = __builtin_amdgcn_perm(0x4C484440u, 0x3C383000u, n & 0x07070707u);
+  return mag | ((n & 0x08080808u) << 4);
+}
+
+// MXFP4 weights x MXFP8 activations: one scaled MFMA per 16x128 block.  A4:
+// the activation rows hold e2m1 codes (two per byte, xrow in bytes of those
+// rows); each fragment is widened to e4m3 in registers (same values, same
+// block scales).
+template <int T, int KR, typename Hook = NoHook, bool A4 = false>
 __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
                                         const uint8_t *xrow, const uint8_t *xsrow, int nt0, int kb0,
                                         f32x4 (&acc)[T], Hook after_issue = Hook()) {
@@ -352,8 +366,18 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
   for (int kb = 0; kb < KR; ++kb) {
     const int k0 = (kb0 + kb) * 128;
     const int klo = k0 + 16 * q, khi = k0 + 64 + 16 * q;
-    const u32x4 lo = *(const u32x4 *)(xrow + (klo < a.k ? klo : 0));
-    const u32x4 hi = *(const u32x4 *)(xrow + (khi < a.k ? khi : 0));
+    u32x4 lo, hi;
+    if constexpr (A4) {
+      const uint2 l4 = *(const uint2 *)(xrow + ((klo < a.k ? klo : 0) >> 1));
+      const uint2 h4 = *(const uint2 *)(xrow + ((khi < a.k ? khi : 0) >> 1));
+      lo = u32x4{e2m1x4_to_e4m3(l4.x), e2m1x4_to_e4m3(l4.x >> 16), e2m1x4_to_e4m3(l4.y),
+                 e2m1x4_to_e4m3(l4.y >> 16)};
+      hi = u32x4{e2m1x4_to_e4m3(h4.x), e2m1x4_to_e4m3(h4.x >> 16), e2m1x4_to_e4m3(h4.y),
+                 e2m1x4_to_e4m3(h4.y >> 16)};
+    } else {
+      lo = *(const u32x4 *)(xrow + (klo < a.k ? klo : 0));
+      hi = *(const u32x4 *)(xrow + (khi < a.k ? khi : 0));
+    }
     const int kb32 = (k0 >> 5) + q;
     const int sc = xsrow[kb32 < (a.k >> 5) ? kb32 : 0];
     const bool lo_ok = klo < a.k, hi_ok = khi < a.k;
@@ -410,7 +434,7 @@ template <int FMT, int GROUP, int T, int KR>
 __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int moe,
                                                                 int64_t total_items_dense) {
   // FMT: 0 INT4 sym, 1 INT4 + zp, 2 INT3 sym, 3 INT3 + zp, 4 MXFP4 x MXFP8,
-  // 5 MXFP4 x bf16
+  // 5 MXFP4 x bf16, 6 MXFP4 x MXFP4 (activations widened to e4m3 in registers)
   extern __shared__ float red[];  // [waves][T][256]: sized by the launcher
   __shared__ int prefix[kMaxExperts + 1];
   __shared__ int last_flag;
@@ -454,10 +478,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = {0.f, 0.f, 0.f, 0.f};
     if (kb0 < a.k_blocks) {
-      if constexpr (FMT == 4) {
+      if constexpr (FMT == 4 || FMT == 6) {
         const uint8_t *xrow = (const uint8_t *)a.x + xr * a.ldx;
         const uint8_t *xsrow = a.x_scales + xr * (int64_t)(a.k >> 5);
-        mx_wave<T, KR>(a, wexp, xrow, xsrow, nt0, kb0, acc, prefetch_next);
+        mx_wave<T, KR, decltype(prefetch_next), FMT == 6>(a, wexp, xrow, xsrow, nt0, kb0, acc, prefetch_next);
       } else {
         const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
         constexpr int BITS = (FMT <= 1 || FMT == 5) ? 4 : 3;
@@ -812,7 +836,7 @@ static int fmt_of(const qg_layer_desc &d) {
     case QG_W_UINT4: return 1;
     case QG_W_INT3: return 2;
     case QG_W_UINT3: return 3;
-    default: return fp4_a16(d) ? 5 : 4;
+    default: return fp4_a16(d) ? 5 : mx_a4(d) ? 6 : 4;
   }
 }
 
@@ -826,6 +850,7 @@ static hipError_t launch_any(const GemmArgs &a, const qg_layer_desc &d, const Va
     case 2: return launch_fmt<2>(a, d.group_size, v, moe, grid, items, s);
     case 3: return launch_fmt<3>(a, d.group_size, v, moe, grid, items, s);
     case 5: return launch_fmt<5>(a, d.group_size, v, moe, grid, items, s);
+    case 6: return launch_fmt<6>(a, d.group_size, v, moe, grid, items, s);
     default: return launch_fmt<4>(a, d.group_size, v, moe, grid, items, s);
   }
 }

@@ -450,11 +450,13 @@ def test_w4a4_host_logic():
     assert qg.packed_size(d) == qg.packed_size(qg.layer_desc(qg.W_MXFP4, 256, 512, 32))
     w = _bound(d)
     # from 128 rows the MX tiled kernel (its scales scratch in the
-    # workspace); below, the MX skinny kernel on rows widened to e4m3 in the
-    # workspace (at least m * K bytes)
+    # workspace); below, the MX skinny kernel (e2m1 fragments widened to e4m3
+    # in registers), with the W4A8 layer's workspace
+    w8 = _bound(qg.layer_desc(qg.W_MXFP4, 256, 512, 32))
     for m in (1, 7, 127):
         assert qg.describe_dispatch(w, m).startswith("mx_skinny"), m
-        assert qg.gemm_workspace_size(w, m) >= m * 512
+        assert qg.describe_dispatch(w, m) == qg.describe_dispatch(w8, m)
+        assert qg.gemm_workspace_size(w, m) == qg.gemm_workspace_size(w8, m)
     for m in (128, 130, 4096):
         assert qg.describe_dispatch(w, m).startswith("mx_tiled"), m
         assert qg.gemm_workspace_size(w, m) > 0
@@ -475,9 +477,9 @@ def test_w4a4_host_logic():
             qg.gemm(w, F, a["xs"], a["m"], a["ldx"], F, qg.O_BF16, 256, F, 1 << 40, stream=S)
         assert e.value.status == status, kw
     # MXFP8 rows spanning 4 GiB are refused too (32-bit activation offsets)
-    w8 = _bound(qg.layer_desc(qg.W_MXFP4, 256, 1024, 32))
+    w8k = _bound(qg.layer_desc(qg.W_MXFP4, 256, 1024, 32))
     with pytest.raises(qg.QGError) as e:
-        qg.gemm(w8, F, F, 1 << 22, 1024, F, qg.O_BF16, 256, F, 1 << 40, stream=S)
+        qg.gemm(w8k, F, F, 1 << 22, 1024, F, qg.O_BF16, 256, F, 1 << 40, stream=S)
     assert e.value.status == qg.QG_ERR_UNSUPPORTED
     # W4A4 MoE: the W4A8 path's workspace plus the pairs' rows widened to e4m3
     dm4 = qg.layer_desc(qg.W_MXFP4, 256, 512, 32, atype=qg.A_MXFP4, num_experts=8)

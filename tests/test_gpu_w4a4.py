@@ -6,8 +6,9 @@ C ABI, against the CPU oracle.
   bit with the oracle (packed two per byte) over every finite bf16 pattern,
   over blocks whose maxima walk every scale exponent of the bf16 range, and
   on N(0, 1) rows with padded leading dimensions.
-* qg_gemm on W4A4 layers: below 128 rows the rows widened exactly to e4m3
-  for the MX skinny kernel, from 128 the MX tiled kernel on e2m1 operands;
+* qg_gemm on W4A4 layers: below 128 rows the MX skinny kernel, which widens
+  each e2m1 fragment exactly to e4m3 in registers, from 128 the MX tiled
+  kernel on e2m1 operands;
   ragged N, K % 512 != 0 (scales regrouped by K step) and
   == 0 (scale ring), padded rows, unaligned scales; bf16 output within
   TOL_BF16 and fp32 within the scaled MFMA's bound (TOL_F32_MX) of the
@@ -139,16 +140,16 @@ def check_a4(layer, acts, m):
                                    (1, 4096, 14336), (4, 14336, 4096), (130, 300, 1024), (300, 1000, 2048),
                                    (513, 448, 640), (256, 512, 4096)])
 def test_w4a4_gemm(m, n, k):
-    """Below 128 rows the rows are widened to e4m3 in the workspace for the
-    MX skinny kernel (long K: split over workgroups); from 128 the tiled
-    kernel takes the e2m1 operands directly."""
+    """Below 128 rows the MX skinny kernel widens the e2m1 fragments to e4m3
+    in registers (long K: split over workgroups); from 128 the tiled kernel
+    takes the e2m1 operands directly."""
     layer = a4_layer(n, k, seed=m + n)
     assert qg.describe_dispatch(layer.w, m).startswith("mx_skinny" if m < 128 else "mx_tiled")
     check_a4(layer, A4(m, k, seed=m + k), m)
 
 
 def test_w4a4_skinny_padded_rows_repeat_calls():
-    """Padded e2m1 rows through the widening path, two calls on one
+    """Padded e2m1 rows through the skinny kernel, two calls on one
     workspace (its split-K counters must be left at zero), then a smaller M."""
     n, k = 512, 8192
     layer = a4_layer(n, k, seed=53)
@@ -200,8 +201,8 @@ def test_w4a4_batch_invariant():
 
 
 def test_w4a4_autotune():
-    """The tuner times the MX tiled kernel and the skinny kernel on widened
-    rows; whichever it keeps serves the next calls, within parity."""
+    """The tuner times the MX tiled kernel and the skinny kernel; whichever
+    it keeps serves the next calls, within parity."""
     m, n, k = 64, 512, 1024
     layer = a4_layer(n, k, seed=49)
     acts = A4(m, k, seed=50)
