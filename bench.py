@@ -45,6 +45,7 @@ PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "fp4": 10100.0}
 METRIC = "TFLOPS at M=4096 (W4A16, W4A8-MXFP4) + weight GB/s at M=1 decode, 1 GPU"
 ROTATE = 8
 MALL_BYTES = 256 << 20
+WARM_MS = 50.0  # minimum untimed back-to-back work before each timed configuration
 
 
 def weight_bytes(n: int, k: int, bits: int, group: int, zp: bool, scale_bytes: int = 2) -> int:
@@ -87,12 +88,22 @@ def make_x(qg, synth, torch, mx, m, k, seed):
     return torch.from_numpy(b.view(np.int16)).cuda(), None, b
 
 
-def timed(torch, launch, iters, warmup):
+def timed(torch, launch, iters, warmup, warm_ms=WARM_MS):
     """Mean ms per call of `launch(i)` over `iters` back-to-back calls, HIP
-    events at both ends on the current stream."""
+    events at both ends on the current stream.  Untimed first: `warmup` calls,
+    then more until at least `warm_ms` of back-to-back work has run (the GPU's
+    clocks take about 25 ms of sustained load to settle; the first
+    milliseconds run up to 15 % slower)."""
+    t0 = time.perf_counter()
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    i = warmup
+    while (time.perf_counter() - t0) * 1e3 < warm_ms:
+        for _ in range(8):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(iters):
@@ -469,7 +480,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    # 2500 decode steps are about 50 ms of back-to-back work: the clocks settle
+    ap.add_argument("--warmup", type=int, default=2500)
     ap.add_argument("--quick", action="store_true", help="primary decode workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--large-m", action="store_true",
@@ -514,7 +526,7 @@ def main():
             f(i)
 
     # timed region: K steps bracketed by a synchronize and events on both sides
-    ms_step = timed(torch, step, args.steps, args.warmup)
+    ms_step = timed(torch, step, args.steps, args.warmup, warm_ms=0)  # exactly W warmup steps
     step_bytes = sum(L.bytes for L in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     # per-kernel average launch durations (each kernel alone, back to back)
