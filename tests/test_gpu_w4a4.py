@@ -293,3 +293,40 @@ def test_w4a4_moe_multi_tile_experts():
         err = oracle.normwise_error(y, ref)
         print(f"  multi-tile otype={otype} err={err:.3e}", flush=True)
         assert err <= tol
+
+
+@pytest.mark.parametrize("nk", [(3072, 4096), (14336, 4096)])
+def test_w4a4_full_size_sampled_rows(nk):
+    """(4096, N, 4096) W4A4 at the benchmarked sizes, in the benchmarked
+    launch: every output computed, 96 sampled rows (first and last included)
+    against the oracle, which computes those rows only."""
+    n, k = nk
+    m = 4096
+    print(f"w4a4 M={m} N={n} K={k}", flush=True)
+    layer = a4_layer(n, k, seed=13)
+    acts = A4(m, k, seed=13)
+    assert qg.describe_dispatch(layer.w, m).startswith("mx_tiled BM=256")
+    rows = np.sort(synth.rng(0, 98).choice(m, 96, replace=False))
+    rows[0], rows[-1] = 0, m - 1
+    yref = oracle.gemm(acts.xdq[rows], layer.wdq())
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
+        y = run_a4(layer, acts, m, otype)
+        e = oracle.normwise_error(y[rows].float().cpu().numpy().astype(np.float64), yref)
+        print(f"  otype={otype} err={e:.3e}", flush=True)
+        assert e <= tol
+        assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("env", [{"QG_MX_BN": "256"}, {"QG_MX_BN": "224"}, {"QG_MX_BN": "192"},
+                                 {"QG_MX_WAVES": "4"}], ids=lambda e: "-".join(f"{k}={v}" for k, v in e.items()))
+@pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (300, 200, 640), (777, 1040, 4096)])
+def test_w4a4_tiled_ragged_every_shape(monkeypatch, env, m, n, k):
+    """Every compiled form of the e2m1-operand tiled kernel (256-, 224- and
+    192-column tiles with 8 waves; 256 with 4) on partial row and column
+    tiles."""
+    for var, val in env.items():
+        monkeypatch.setenv(var, val)
+    layer = a4_layer(n, k, seed=m + 1)
+    bn = env.get("QG_MX_BN", "256")
+    assert f"mx_tiled BM=256 BN={bn}" == qg.describe_dispatch(layer.w, m)
+    check_a4(layer, A4(m, k, seed=m + 2), m)
