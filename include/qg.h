@@ -108,11 +108,10 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
  *   "Choosing the activation type": MXFP4 checkpoints on a bf16 compute path);
  *   MXFP4, E8M0 scales, MXFP4 activations, group 32, K % 128 == 0 (W4A4, the
  *   announcement's "W8A8 / W4A8 / W4A4" section: dense calls from 128 rows
- *   put both e2m1 operands into the scaled MFMA; below 128 rows the W4A8
- *   skinny kernel widens each activation fragment to e4m3 in registers, and
- *   qg_moe_gemm first widens the activation rows to e4m3 in the workspace --
- *   every e2m1 value is an e4m3 value under the same scale -- and runs the
- *   W4A8 grouped kernels on them).
+ *   put both e2m1 operands into the scaled MFMA, and so do qg_moe_gemm's
+ *   tiled kernels; the skinny kernel (dense below 128 rows, MoE experts with
+ *   few rows) widens each activation fragment to e4m3 in registers -- every
+ *   e2m1 value is an e4m3 value under the same scale).
  * Other valid combinations return QG_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t abi_version; /* must be QG_ABI_VERSION */
@@ -269,8 +268,8 @@ qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, int32_t topk,
  * x, x_scales, y as in qg_gemm with ldx = K and ldy = N (dense rows).
  * ws: device, 256-B aligned, at least qg_moe_workspace_size bytes (holds the
  * tile list of the large-expert kernel and, for integer formats, the group
- * row sums of x, for W4A4 the rows of x widened to e4m3; overwritten by every
- * call, so calls sharing one ws must be ordered on one stream).
+ * row sums of x; overwritten by every call, so calls sharing one ws must be
+ * ordered on one stream).
  * More than 1024 experts: QG_ERR_UNSUPPORTED (here and in qg_moe_sort).
  * Asynchronous on `stream`. */
 qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales, int32_t x_rows,

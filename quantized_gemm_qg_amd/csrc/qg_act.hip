@@ -173,31 +173,6 @@ __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const uint16_t *x, 
   }
 }
 
-// e2m1 rows [rows][ldx4 bytes] -> e4m3 rows [rows][ldx8 bytes], value for
-// value: every e2m1 magnitude (0, 0.5, 1, 1.5, 2, 3, 4, 6) is an e4m3 value, so
-// under the same e8m0 block scale the MXFP8 row holds exactly the MXFP4 row's
-// values.  Unit u = (row, 8 codes: one dword in, two dwords out).
-__global__ __launch_bounds__(256) void widen_e2m1_kernel(const uint8_t *x4, int64_t ldx4, uint8_t *x8,
-                                                         int64_t ldx8, int64_t k8, int64_t units) {
-  // e4m3 bits of the e2m1 magnitudes 0..7 (exponent bias 7), four per dword
-  constexpr uint32_t kLo = 0x3C383000u, kHi = 0x4C484440u;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const bool wide = units > 0xFFFFFFFFll;
-  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += stride) {
-    int64_t row, c8;
-    split_unit(u, k8, wide, row, c8);
-    const uint32_t c = *(const uint32_t *)(x4 + row * ldx4 + 4 * c8);
-    uint32_t out[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t code = (c >> (4 * i)) & 15u, mag = code & 7u;
-      const uint32_t bits = (((mag < 4 ? kLo : kHi) >> (8 * (mag & 3))) & 0xFFu) | ((code & 8u) << 4);
-      out[i >> 2] |= bits << (8 * (i & 3));
-    }
-    *(uint2 *)(x8 + row * ldx8 + 8 * c8) = uint2{out[0], out[1]};
-  }
-}
-
 // bf16 rows [rows][ldx] -> e4m3 rows [rows][ldq] + e8m0 [rows][k / 32].
 // Unit u = (row, 8-value chunk c8); u runs over rows * k / 8 (a multiple of 4,
 // so a quad's units are all in range or all out of it).
@@ -307,15 +282,6 @@ hipError_t launch_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(stream_grid(units)), dim3(256), 0, s, (const uint16_t *)x, ldx,
                      (uint8_t *)q, ldq, (uint8_t *)qs, k / 8, units);
-  return hipGetLastError();
-}
-
-hipError_t launch_widen_e2m1(const void *x4, int64_t rows, int64_t k, int64_t ldx4, void *x8, int64_t ldx8,
-                             hipStream_t s) {
-  const int64_t units = rows * (k / 8);
-  if (units == 0) return hipSuccess;
-  hipLaunchKernelGGL(widen_e2m1_kernel, dim3(stream_grid(units)), dim3(256), 0, s, (const uint8_t *)x4, ldx4,
-                     (uint8_t *)x8, ldx8, k / 8, units);
   return hipGetLastError();
 }
 

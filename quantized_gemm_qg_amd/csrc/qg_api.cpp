@@ -710,8 +710,9 @@ extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x
   return hip_status(launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, ws, stream));
 }
 
-// The weight as the kernels see it: a W4A4 layer runs as W4A8 (the packed
-// layout is the same) on its activation rows widened exactly to e4m3.
+// The weight as the MoE dispatch sees it: a W4A4 layer takes W4A8's kernel
+// choices and workspace (the packed layout is the same); its launches then
+// read e2m1 rows (the tiled kernel's A4 form, the skinny kernel's FMT 6).
 static qg_weight mx_kernel_weight(const qg_weight &w, const Layout &L) {
   qg_weight k = w;
   if (L.a4) k.desc.atype = QG_A_MXFP8;
@@ -726,11 +727,9 @@ extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_token
   if (!bytes || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
   const int64_t pairs = num_tokens * topk;
   // the sort's need, or the grouped GEMM's with X indexed by pair (the larger
-  // of the two x row counts); W4A4: the MXFP8 path's need, then the rows
-  // widened to e4m3
+  // of the two x row counts); W4A4 needs what W4A8 does
   const qg_weight wk = mx_kernel_weight(*w, L);
-  uint64_t gemm = moe_ws_bytes(wk, pairs, pairs, moe_tiled_min_rows(wk, pairs, pairs));
-  if (L.a4) gemm = align_up(gemm, 256) + (uint64_t)pairs * w->desc.k;
+  const uint64_t gemm = moe_ws_bytes(wk, pairs, pairs, moe_tiled_min_rows(wk, pairs, pairs));
   *bytes = std::max<uint64_t>(align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256), gemm);
   return QG_OK;
 }
@@ -758,7 +757,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
-  // W4A4: everything below runs the W4A8 path on rows widened into ws
+  // W4A4: W4A8's dispatch, launched on e2m1 rows
   const qg_weight wk = mx_kernel_weight(*w, L);
   const qg_layer_desc &d = wk.desc;
   if (num_tokens < 0 || topk <= 0 || (otype != QG_O_BF16 && otype != QG_O_F32))
@@ -778,25 +777,17 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   if (!covers(v, wk.k_blocks)) return QG_ERR_UNSUPPORTED;  // K too long for one workgroup
   const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
   const int min_rows = moe_tiled_min_rows(wk, pairs, x_rows_count);
-  const uint64_t need_k = moe_ws_bytes(wk, pairs, x_rows_count, min_rows);
-  const uint64_t wide_off = align_up(need_k, 256);
-  const uint64_t need = L.a4 ? wide_off + (uint64_t)x_rows_count * d.k : need_k;
+  const uint64_t need = moe_ws_bytes(wk, pairs, x_rows_count, min_rows);
   if (need > 0) {
     if (!ws) return QG_ERR_INVALID_ARGUMENT;
     if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
     if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
   }
-  if (L.a4) {
-    uint8_t *x8 = (uint8_t *)ws + wide_off;
-    const hipError_t we = launch_widen_e2m1(x, x_rows_count, d.k, d.k / 2, x8, d.k, stream);
-    if (we != hipSuccess) return hip_status(we);
-    x = x8;
-  }
   GemmArgs a;
   base_args(wk, &a);
   a.x = x;
   a.x_scales = (const uint8_t *)x_scales;
-  a.ldx = d.k;
+  a.ldx = L.a4 ? d.k / 2 : d.k;  // bytes of an e2m1 row
   a.y = y;
   a.ldy = d.n;
   a.otype = otype;
@@ -821,7 +812,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     a.group_m = moe_group_m();
     void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
     if (L.is_mx)
-      he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream);
+      he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream, L.a4);
     else
       he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
                             xs, true, stream);
@@ -835,7 +826,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
       if (he != hipSuccess) return hip_status(he);
       a.tiles = tiles_s;
       a.group_m = 1;
-      he = L.is_mx ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream)
+      he = L.is_mx ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4)
                    : launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
       return hip_status(he);  // every expert with rows is covered
     }
@@ -843,7 +834,9 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   }
   // the remaining (small) experts
   const int64_t max_tiles = (pairs + 15) / 16 + d.num_experts;
-  he = L.is_mx ? launch_moe_mx(a, d, v, max_tiles, stream) : launch_moe_a16(a, d, v, max_tiles, stream);
+  // (the skinny kernel's format comes from the layer's own description:
+  // FMT 6 widens e2m1 fragments in registers)
+  he = L.is_mx ? launch_moe_mx(a, w->desc, v, max_tiles, stream) : launch_moe_a16(a, d, v, max_tiles, stream);
   return hip_status(he);
 }
 

@@ -203,10 +203,6 @@ hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipSt
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 // Activation-side kernels (qg_act.hip): bf16 -> MXFP8, SiLU-gated product,
 // weighted top-k combine.  Shapes and alignment are validated by the callers.
-// e2m1 rows (ldx4 bytes apart) -> the same values as e4m3 rows (ldx8 bytes
-// apart); k % 8 == 0, 4-byte aligned input rows, 8-byte aligned output rows.
-hipError_t launch_widen_e2m1(const void *x4, int64_t rows, int64_t k, int64_t ldx4, void *x8, int64_t ldx8,
-                             hipStream_t s);
 hipError_t launch_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
                                  void *qs, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,

@@ -89,14 +89,18 @@ struct MxCfg {
   static constexpr int SAR_SLOT = SAR ? BM * 16 : 0;        // [row][4 steps x 4 bytes]
   static constexpr int OFF_SAR = OFF_SW + 2 * SW;           // the two SA ring slots
   static constexpr int LDS = OFF_SAR + 2 * SAR_SLOT;
-  static constexpr int A_LOADS = BM * AROW / 1024 / WAVES;  // 1-KB copies of A per wave
+  static constexpr int A_COPIES = BM * AROW / 1024;          // 1-KB copies of A per stage
+  // per wave; where they do not divide evenly (e2m1 64-row tiles: 4 copies,
+  // 8 waves) the last waves repeat the final copy, the same bytes to the
+  // same place
+  static constexpr int A_LOADS = (A_COPIES + WAVES - 1) / WAVES;
   static constexpr int B_LOADS = (NBLK + WAVES - 1) / WAVES;  // 1-KB blocks of B per wave
   static constexpr int SA_WAVES = BM / 64;                  // waves that copy a 256-B SA piece
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int MB = BM / WM / 16;                   // 16-row blocks per wave
   static constexpr int NB = BN / WN / 16;                   // 16-column blocks per wave
   static_assert(BN % (16 * WN) == 0, "column blocks per wave");
-  static_assert(A_LOADS >= 1 && BM * AROW % (1024 * WAVES) == 0, "A copies per wave");
+  static_assert(A_COPIES >= 1 && BM * AROW % 1024 == 0, "A copies");
   static_assert(WAVES >= SA_WAVES && WAVES >= SW_PIECES, "SA / SW pieces");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
@@ -104,7 +108,6 @@ struct MxCfg {
 template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4>
 __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
-  static_assert(!(A4 && MOE), "e2m1 activations: dense launches only");
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -124,15 +127,16 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
 
   // per-lane source offsets (32-bit, added to wave-uniform bases at issue)
   uint32_t a_off[C::A_LOADS];
+  auto a_copy = [&](int i) { return min(wave * C::A_LOADS + i, C::A_COPIES - 1); };
 #pragma unroll
   for (int i = 0; i < C::A_LOADS; ++i) {
     if constexpr (A4) {
       // 16 rows of 4 chunks per copy: lane -> row lane / 4, slot lane % 4
-      const int row = 16 * (wave * C::A_LOADS + i) + (lane >> 2);
+      const int row = 16 * a_copy(i) + (lane >> 2);
       const int c = (lane & 3) ^ ((row >> 1) & 3);
       a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
     } else {
-      const int row = 8 * (wave * C::A_LOADS + i) + (lane >> 3);
+      const int row = 8 * a_copy(i) + (lane >> 3);
       const int c = (lane & 7) ^ (row & 7);
       a_off[i] = (uint32_t)(tr.x(a, row) * a.ldx + 16 * c);
     }
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     const uint8_t *xk = x + kb * C::AROW;
 #pragma unroll
     for (int i = 0; i < C::A_LOADS; ++i)
-      lds_dma16(xk + a_off[i], st + (wave * C::A_LOADS + i) * 1024);
+      lds_dma16(xk + a_off[i], st + a_copy(i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
       lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + blk_of(i) * 1024);
@@ -366,9 +370,15 @@ static hipError_t launch_mx_shape(const GemmArgs &a, int bm, int bn, bool moe, i
                    : launch_mx_tiled_bm<128, 256, 2, 2, false, SAR>(a, 0, s);
 }
 
-// Dense e2m1 activations: the same tile shapes as dense MXFP8.
+// e2m1 activations: the same tile shapes as MXFP8.
 template <bool SAR>
-static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, int waves, hipStream_t s) {
+static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
+                                     hipStream_t s) {
+  if (moe) {
+    if (waves == 8 && bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, SAR, true>(a, tiles_cap, s);
+    if (waves == 8) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true, SAR, true>(a, tiles_cap, s);
+    return launch_mx_tiled_bm<kMoeTileRows, 256, 2, 2, true, SAR, true>(a, tiles_cap, s);
+  }
   if (waves == 8) {
     if (bm == 256) {
       if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false, SAR, true>(a, 0, s);
@@ -390,13 +400,13 @@ static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, int wave
 // activation scales go through the SA ring when K % 512 == 0 and they are
 // 16-byte aligned; otherwise dense launches first regroup them by K step into
 // ws and MoE launches copy 4 bytes per row and step.  a4: e2m1 activations
-// (dense only; a.ldx in bytes).
+// (a.ldx in bytes).
 hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
                            void *ws, hipStream_t s, bool a4) {
-  if (a_in.k % 128 != 0 || (a4 && moe)) return hipErrorInvalidValue;
+  if (a_in.k % 128 != 0) return hipErrorInvalidValue;
   GemmArgs a = a_in;
   const bool sar = a.k % 512 == 0 && ((uintptr_t)a.x_scales & 15) == 0;
-  if (sar) return a4 ? launch_mx_shape_a4<true>(a, bm, bn, waves, s)
+  if (sar) return a4 ? launch_mx_shape_a4<true>(a, bm, bn, moe, tiles_cap, waves, s)
                      : launch_mx_shape<true>(a, bm, bn, moe, tiles_cap, waves, s);
   if (!moe) {
     if (!ws) return hipErrorInvalidValue;
@@ -407,7 +417,7 @@ hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64
     if (e != hipSuccess) return e;
     a.x_scales_t = (const uint32_t *)ws;
   }
-  return a4 ? launch_mx_shape_a4<false>(a, bm, bn, waves, s)
+  return a4 ? launch_mx_shape_a4<false>(a, bm, bn, moe, tiles_cap, waves, s)
             : launch_mx_shape<false>(a, bm, bn, moe, tiles_cap, waves, s);
 }
 

@@ -14,8 +14,9 @@ C ABI, against the CPU oracle.
   TOL_BF16 and fp32 within the scaled MFMA's bound (TOL_F32_MX) of the
   float64 product of the exact operands.
 * Batch invariance, the autotuner's choice, and the quantize -> GEMM chain.
-* W4A4 MoE (rows widened to e4m3 in the workspace, then the W4A8 grouped
-  kernels) in every row mode and every split of the experts between kernels.
+* W4A4 MoE (W4A8's dispatch on e2m1 rows: the tiled kernel's e2m1 form,
+  its 64-row small tiles, the skinny kernel's in-register widening) in every
+  row mode and every split of the experts between kernels.
 """
 import numpy as np
 import pytest
@@ -243,8 +244,8 @@ def test_quantize4_then_w4a4_gemm():
 
 
 # ---------------------------------------------------------------------------
-# W4A4 MoE: the activation rows widened to e4m3 in the workspace, then the
-# W4A8 grouped kernels (every split of the experts between them)
+# W4A4 MoE: W4A8's dispatch on e2m1 rows (every split of the experts between
+# the tiled kernel, its small tiles and the skinny kernel)
 # ---------------------------------------------------------------------------
 
 def _moe_a4_layer(n, k, experts, seed):
