@@ -252,10 +252,11 @@ def _moe_a4_layer(n, k, experts, seed):
     return Layer(qg.W_MXFP4, n, k, 32, seed=seed, experts=experts, atype=qg.A_MXFP4)
 
 
-@pytest.mark.parametrize("split", ["skinny", "tiled", "mixed", "mixed_skinny", "small"])
+@pytest.mark.parametrize("split", ["skinny", "tiled", "tiled_4waves", "mixed", "mixed_skinny", "small"])
 def test_w4a4_moe_all_row_modes(monkeypatch, split):
     from test_gpu_moe import SPLITS, moe_reference, run_moe, sort_on_gpu
-    for var, val in SPLITS[split].items():
+    env = dict(SPLITS["tiled"], QG_MX_WAVES="4") if split == "tiled_4waves" else SPLITS[split]
+    for var, val in env.items():
         monkeypatch.setenv(var, val)
     t, e, topk, n, k = 37, 16, 4, 80, 640
     ids = synth.route(synth.rng(60, 0), t, e, topk)
