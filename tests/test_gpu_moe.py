@@ -194,9 +194,11 @@ def test_moe_tiled_multi_tile_experts(wtype):
     assert oracle.normwise_error(y, moe_reference(layer, h.xdq, ids, False)[s]) <= tol_f32(mx)
 
 
-def _moe_sampled(wtype, experts, topk, n, k, tokens, seed, by_token, n_experts_checked=12):
+def _moe_sampled(wtype, experts, topk, n, k, tokens, seed, by_token, n_experts_checked=12, atype=None,
+                 make_acts=None):
     """Full-size grouped GEMM; the oracle checks every pair of a sample of
-    experts (the largest, the smallest and some in between)."""
+    experts (the largest, the smallest and some in between).  atype /
+    make_acts(rows, k, seed): another activation type and its inputs."""
     g = 32 if wtype == qg.W_MXFP4 else 128
     mx = wtype == qg.W_MXFP4
     ids = synth.route(synth.rng(seed, 1), tokens, experts, topk)
@@ -207,10 +209,10 @@ def _moe_sampled(wtype, experts, topk, n, k, tokens, seed, by_token, n_experts_c
                                      order[np.linspace(0, order.size - 1, n_experts_checked - 8).astype(int)]]))
     print(f"moe wtype={wtype} E={experts} T={tokens} N={n} K={k} active={active.size} "
           f"max rows={counts.max()} checked experts={pick.tolist()}", flush=True)
-    layer = Layer(wtype, n, k, g, seed=seed, experts=experts, active=active)
+    layer = Layer(wtype, n, k, g, seed=seed, experts=experts, active=active, atype=atype)
     sorted_ids, offsets = sort_on_gpu(ids, experts, layer)
     rows = tokens if by_token else tokens * topk
-    acts = Acts(mx, rows, k, seed=seed + 1)
+    acts = make_acts(rows, k, seed + 1) if make_acts else Acts(mx, rows, k, seed=seed + 1)
     y = run_moe(layer, acts, sorted_ids, offsets, tokens, topk,
                 qg.ROWS_BY_TOKEN if by_token else qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR, qg.O_BF16)
     flat = ids.reshape(-1)

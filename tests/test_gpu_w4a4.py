@@ -332,3 +332,13 @@ def test_w4a4_tiled_ragged_every_shape(monkeypatch, env, m, n, k):
     bn = env.get("QG_MX_BN", "256")
     assert f"mx_tiled BM=256 BN={bn}" == qg.describe_dispatch(layer.w, m)
     check_a4(layer, A4(m, k, seed=m + 2), m)
+
+
+@pytest.mark.parametrize("nk,by_token", [((1280, 4096), True), ((4096, 640), False)])
+def test_w4a4_moe_128_experts_t4096_sampled(nk, by_token):
+    """The benchmarked W4A4 MoE layer (E = 128, top-8, T = 4096; gate_up by
+    token, down by pair) at full size: every pair of a sample of experts
+    against the oracle."""
+    from test_gpu_moe import _moe_sampled
+    _moe_sampled(qg.W_MXFP4, 128, 8, nk[0], nk[1], 4096, seed=63, by_token=by_token, atype=qg.A_MXFP4,
+                 make_acts=lambda rows, k, seed: A4(rows, k, seed))
