@@ -406,8 +406,8 @@ def bench_large_m(qg, synth, torch):
 
 def bench_act(qg, synth, torch):
     """Activation-side kernels at the hot path's shapes (HBM-bound; algorithmic
-    bytes read + written per call / time), and the W4A8 GEMM fed from bf16
-    activations (quantize + GEMM).  Inputs rotate over copies totalling more
+    bytes read + written per call / time), and the W4A8 / W4A4 GEMMs fed from
+    bf16 activations (quantize + GEMM).  Inputs rotate over copies totalling more
     than twice the MALL so each call reads from HBM."""
     extra = {}
     stream = torch.cuda.current_stream().cuda_stream
@@ -448,7 +448,28 @@ def bench_act(qg, synth, torch):
         "fp8_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
         "steps": "qg_quantize_mxfp8 + qg_gemm"}
     print(f"[bench] w4a8 from bf16: {extra[f'w4a8_from_bf16_M{m}_N{n}_K{k}']}", file=sys.stderr, flush=True)
-    del L, xs
+    del L
+    # bf16 -> MXFP4 (2 B read, 1/2 + 1/32 B written per value), then W4A4
+    q4 = torch.empty((m, k // 2), dtype=torch.uint8, device="cuda")
+    t = timed(torch, lambda i: qg.quantize_mxfp4(xs[i % nc], m, k, k, q4, k, qs, stream), 100, 10)
+    record("quantize_mxfp4_M4096_K4096", t, m * k * 2 + m * k // 2 + m * k // 32)
+    codes, sc, _ = synth.mx_weights(synth.rng(50, 1), n, k)
+    desc4 = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_MXFP4)
+    bufs4 = [torch.empty(qg.packed_size(desc4), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    w4 = [qg.preprocess(desc4, codes, sc, None, b) for b in bufs4]
+    wsb4 = qg.gemm_workspace_size(w4[0], m)
+    ws4 = torch.zeros(max(wsb4, 1), dtype=torch.uint8, device="cuda")
+
+    def qgemm4(i):
+        qg.quantize_mxfp4(xs[i % nc], m, k, k, q4, k, qs, stream)
+        qg.gemm(w4[i % 2], q4, qs, m, k, y, qg.O_BF16, n, ws4, wsb4, stream)
+    t = timed(torch, qgemm4, 50, 10)
+    extra[f"w4a4_from_bf16_M{m}_N{n}_K{k}"] = {
+        "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+        "fp4_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp4"], 4),
+        "steps": "qg_quantize_mxfp4 + qg_gemm"}
+    print(f"[bench] w4a4 from bf16: {extra[f'w4a4_from_bf16_M{m}_N{n}_K{k}']}", file=sys.stderr, flush=True)
+    del bufs4, w4, xs
     # SiLU-gated product between gate_up and down at T = 4096, top-8 (32768 pairs)
     p = 4096 * 8
     for inter, mx in ((2048, False), (640, True)):
