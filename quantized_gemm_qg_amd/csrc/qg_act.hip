@@ -21,8 +21,8 @@
 //
 // MXFP4 conversion (for W4A4, the announcement's section "W8A8 / W4A8 /
 // W4A4"): the same rule with e2m1 elements, X = 2^(floor(log2 max|v|) - 2), the
-// element rounded to the nearest of the eight e2m1 magnitudes by comparisons
-// against their midpoints (no hardware conversion involved).
+// element rounded by the hardware's fp32 -> e2m1 conversion (nearest, ties to
+// even, sign kept; the clamp to +-6 gives the saturation).
 #include <hip/hip_runtime.h>
 
 #include "qg_device.h"
@@ -88,20 +88,6 @@ __device__ __forceinline__ void mx_store8(const uint32_t (&w)[4], uint8_t *q8, u
   if (first) *scale = (uint8_t)(e + 127);
 }
 
-// e2m1 code (sign in bit 3) of v already divided by its block scale: the
-// nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code, saturated at
-// 6.  Each comparison is against a midpoint between neighbouring values, `>`
-// where the lower neighbour's code is even and `>=` where the upper one's is;
-// the division by the power-of-two scale is exact, so no rounding precedes
-// the comparisons.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const float m = fabsf(v);
-  const uint32_t mag = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
-                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) +
-                       (uint32_t)(m > 5.f);
-  return mag | ((__float_as_uint(v) >> 28) & 8u);
-}
-
 // MXFP4 form of mx_store8: the block scale is 2^(floor(log2 max|v|) - 2)
 // (e2m1's largest value 6 lies in [4, 8)); the 8 codes go out as one dword,
 // value i in bits 4i .. 4i + 3.
@@ -118,9 +104,18 @@ __device__ __forceinline__ void mx4_store8(const uint32_t (&w)[4], uint8_t *q4, 
   const uint32_t amax = quad_max(__float_as_uint(m));
   const int e = amax == 0 ? 0 : max((int)(amax >> 23) - 129, -127);  // bf16 maxima: e <= 125
   const float inv = __uint_as_float((uint32_t)(127 - e) << 23);      // 2^-e
-  uint32_t c = 0;
+  // v_cvt_scalef32_pk_fp4_f32 rounds each pair (scale 1: the values are
+  // already divided by X, exactly) to the nearest e2m1, ties to even, sign
+  // kept, the first value in the low nibble of byte i; the clamp to +-6
+  // gives the saturation
+  float s8[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c |= e2m1_code(v[i] * inv) << (4 * i);
+  for (int i = 0; i < 8; ++i) s8[i] = __builtin_amdgcn_fmed3f(v[i] * inv, -6.f, 6.f);
+  uint32_t c = 0;
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, s8[0], s8[1], 1.f, 0);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, s8[2], s8[3], 1.f, 1);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, s8[4], s8[5], 1.f, 2);
+  c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c, s8[6], s8[7], 1.f, 3);
   *(uint32_t *)q4 = c;
   if (first) *scale = (uint8_t)(e + 127);
 }
