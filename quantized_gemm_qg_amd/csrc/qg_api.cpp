@@ -267,7 +267,7 @@ static bool same_variant(const Variant &a, const Variant &b) {
 static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
   const qg_layer_desc &d = w.desc;
   const bool mx = mx_a8(d) || mx_a4(d);
-  if (mx_a4(d) && v.kind != 1 && v.kind != 0) return false;  // W4A4: MX tiled, or MX skinny on widened rows
+  if (mx_a4(d) && v.kind != 1 && v.kind != 0) return false;  // W4A4: the MX tiled or MX skinny kernel
   switch (v.kind) {
     case 0:
       return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 && covers(v, w.k_blocks);
