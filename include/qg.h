@@ -165,10 +165,15 @@ qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes, const void
 qg_status qg_weight_bind(const qg_layer_desc *desc, void *dst_dev, uint64_t dst_bytes,
                          qg_weight *out);
 
-/* Workspace bytes qg_gemm needs for `m` rows (0 when none is needed).  A
- * workspace must be zero-filled once before its first use (e.g. with
- * hipMemsetAsync); every completed qg_gemm call leaves it zero-filled again, so
- * one workspace serves any sequence of calls ordered on one stream. */
+/* Workspace bytes qg_gemm needs for `m` rows (0 when none is needed).
+ * Layout of a dense workspace: the first 64 KiB hold the arrival counters of
+ * split-K launches (one per output tile; a launch that splits K counts its
+ * workgroups in and leaves the counters at zero again), and the bytes after
+ * them are scratch (fp32 partial tiles, the large-M kernels' pre-pass
+ * results) whose contents never matter.  So a workspace must be zero-filled
+ * once before its first use (its first 64 KiB suffice) and then serves any
+ * sequence of qg_gemm / qg_gemm_ex calls -- any layer, any m -- ordered on one
+ * stream, provided it holds the size each call asks for. */
 qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes);
 
 /* Dense GEMM: y[m][n] = x[m][:K] * dequant(W)^T.
@@ -243,6 +248,22 @@ qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const void *x_scal
 /* Forget every autotuned entry (back to the heuristics). */
 void qg_autotune_reset(void);
 
+/* Experiment overrides of the tuning table, for tests and parameter sweeps
+ * (production code sets none).  At the first dispatch of the process the
+ * library reads the environment variables of these names once; after that
+ * only these calls change them.  name is one of QG_TUNE ("T,KR,W,splits": the
+ * skinny kernel with these parameters), QG_DECODE ("0" disables the decode
+ * kernel, "T,KR[,splits]" picks an instance), QG_TILED ("0" disables the
+ * large-M kernels), QG_TILED_BM, QG_MX_BN, QG_MX_WAVES, QG_A16_WAVES,
+ * QG_A16_BN, QG_MOE_TILED_MIN, QG_MOE_GROUP_M, QG_MOE_SMALL_BM, QG_MOE_SMALL,
+ * QG_GROUP_M; value NULL or "" clears the override.  An unknown name returns
+ * QG_ERR_INVALID_ARGUMENT.  A value outside an override's range is ignored
+ * (the heuristic applies).  Thread-safe; a dispatch sees the overrides before
+ * or after a concurrent change, never a mix.  qg_clear_overrides clears all
+ * (the environment is not read again). */
+qg_status qg_set_override(const char *name, const char *value);
+void qg_clear_overrides(void);
+
 /* Workspace bytes for qg_moe_sort and qg_moe_gemm with this many tokens (one
  * buffer of this size serves both; its contents on entry do not matter). */
 qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
@@ -262,6 +283,8 @@ qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, int32_t topk,
                       void *ws, uint64_t ws_bytes, hipStream_t stream);
 
 /* Grouped GEMM over the sorted pairs: for every pair p routed to expert e,
+ * (any K that is a multiple of 32 and of the group; long K loops inside the
+ * kernels' workgroups)
  *   y[row_y(p)] = x[row_x(p)] * dequant(W[e])^T
  * with row_x given by x_rows (BY_TOKEN: p / topk; BY_PAIR: p; SORTED: the
  * pair's position in sorted_pair_ids) and row_y by y_rows (BY_PAIR or SORTED).
@@ -359,9 +382,13 @@ qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, const float
 qg_status qg_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t stream);
 qg_status qg_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t stream);
 
-/* Name of the kernel variant the tuning table selects for `m` rows (dense) and
- * the tile parameters, written as a NUL-terminated string into buf. */
+/* Name of the kernel variant the tuning table selects for `m` rows (dense) or
+ * `m` pairs (MoE: the skinny kernel's variant for experts with few rows) and
+ * the tile parameters, written as a NUL-terminated string into buf.
+ * qg_describe_dispatch_ex does the same for the compute options `flags` of
+ * qg_gemm_ex (dense layers only). */
 qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf, uint64_t buf_bytes);
+qg_status qg_describe_dispatch_ex(const qg_weight *w, int64_t m, uint32_t flags, char *buf, uint64_t buf_bytes);
 
 /* Static description of a status code (never NULL). */
 const char *qg_status_string(qg_status status);

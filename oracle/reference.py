@@ -153,10 +153,14 @@ def moe_gemm(expert_weights, x_rows: np.ndarray, topk_ids: np.ndarray,
 # ----------------------------------------------------------------------------
 
 def round_bf16(y: np.ndarray) -> np.ndarray:
-    """Round float64 to the nearest-even bf16 value (normal range), as float64."""
+    """Round float64 to the nearest-even bf16 value, as float64.
+
+    bf16 keeps 8 significant bits and binary32's exponent range, so below the
+    smallest normal 2^-126 its spacing stays 2^-133 (subnormals).  Values past
+    the largest finite bf16 are not expected here."""
     y = np.asarray(y, dtype=np.float64)
     m, e = np.frexp(y)          # y = m * 2^e, 0.5 <= |m| < 1
-    quantum = np.ldexp(1.0, e - 8)  # 8 significant bits
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))  # 8 significant bits, subnormal floor
     return np.where(y == 0, 0.0, np.rint(y / quantum) * quantum)
 
 

@@ -30,6 +30,7 @@ EXPORTS = (
     "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
     "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset", "qg_quantize_mxfp4",
+    "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex",
 )
 GEMM_BATCH_INVARIANT = 1
 
@@ -84,6 +85,7 @@ def _load():
         "qg_stream_read": (I32, [P, U64, P, P]),
         "qg_stream_copy": (I32, [P, P, U64, P]),
         "qg_describe_dispatch": (I32, [W, I64, ctypes.c_char_p, U64]),
+        "qg_describe_dispatch_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.c_char_p, U64]),
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_last_hip_error": (I32, []),
         "qg_quantize_mxfp8": (I32, [P, I64, I64, I64, P, I64, P, P]),
@@ -96,6 +98,8 @@ def _load():
         "qg_gemm_autotune": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, P, U64, I32, P, ctypes.c_char_p, U64,
                                    ctypes.POINTER(ctypes.c_float)]),
         "qg_autotune_reset": (None, []),
+        "qg_set_override": (I32, [ctypes.c_char_p, ctypes.c_char_p]),
+        "qg_clear_overrides": (None, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -235,9 +239,9 @@ def moe_gemm(w: Weight, x, x_scales, x_rows: int, sorted_pair_ids, expert_offset
                             otype, y_rows, _ptr(ws), ws_bytes, _stream(stream)), "qg_moe_gemm")
 
 
-def describe_dispatch(w: Weight, m: int) -> str:
+def describe_dispatch(w: Weight, m: int, flags: int = 0) -> str:
     buf = ctypes.create_string_buffer(256)
-    _check(_lib.qg_describe_dispatch(ctypes.byref(w), m, buf, 256), "qg_describe_dispatch")
+    _check(_lib.qg_describe_dispatch_ex(ctypes.byref(w), m, flags, buf, 256), "qg_describe_dispatch_ex")
     return buf.value.decode()
 
 
@@ -296,3 +300,13 @@ def gemm_autotune(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: 
 
 def autotune_reset() -> None:
     _lib.qg_autotune_reset()
+
+
+def set_override(name: str, value: str | None) -> None:
+    """Experiment override of the tuning table (QG_TUNE, QG_DECODE, ...); None clears it."""
+    _check(_lib.qg_set_override(name.encode(), None if value is None else str(value).encode()),
+           "qg_set_override")
+
+
+def clear_overrides() -> None:
+    _lib.qg_clear_overrides()

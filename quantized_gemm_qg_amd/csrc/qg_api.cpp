@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -28,20 +29,119 @@ static qg_status hip_status(hipError_t e) {
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Optional override for experiments: QG_TUNE="T,KR,W,splits".
+// ---------------------------------------------------------------------------
+// Experiment overrides of the tuning table.  The QG_* environment variables
+// are read once, at the first dispatch; qg_set_override changes them later.
+// Dispatch reads one immutable snapshot through an atomic pointer, so the
+// per-call path neither parses strings nor touches the environment, and a
+// concurrent qg_set_override never tears a read (replaced snapshots are kept
+// until the process ends: they are few and small).
+// ---------------------------------------------------------------------------
+namespace {
+struct Overrides {
+  bool tune = false;  // QG_TUNE "T,KR,W,splits": the skinny kernel with these parameters
+  int tune_v[4] = {0, 0, 0, 0};
+  bool decode_off = false;  // QG_DECODE "0"
+  int decode_n = 0;         // QG_DECODE "T,KR[,splits]": number of fields parsed (2 or 3)
+  int decode_v[3] = {0, 0, 1};
+  bool tiled_off = false;   // QG_TILED "0"
+  bool tiled_set = false;   // QG_TILED present (any value): the autotune table is bypassed
+  int tiled_bm = 0;         // QG_TILED_BM: 128 or 256
+  int mx_bn = 0;            // QG_MX_BN: 192, 224 or 256
+  int mx_waves = 0;         // QG_MX_WAVES: 4 or 8
+  int a16_waves = 0;        // QG_A16_WAVES: 4 or 8
+  int a16_bn = 0;           // QG_A16_BN: 128
+  int moe_tiled_min = -1;   // QG_MOE_TILED_MIN: >= 0 (0 disables the tiled MoE kernels)
+  int moe_group_m = 0;      // QG_MOE_GROUP_M: 1..64
+  int moe_small_bm = 0;     // QG_MOE_SMALL_BM: 32
+  int moe_small = -1;       // QG_MOE_SMALL: 0 or 1
+  int group_m = 0;          // QG_GROUP_M: 1..64
+};
+
+const char *const kOverrideNames[] = {"QG_TUNE", "QG_DECODE", "QG_TILED", "QG_TILED_BM", "QG_MX_BN",
+                                      "QG_MX_WAVES", "QG_A16_WAVES", "QG_A16_BN", "QG_MOE_TILED_MIN",
+                                      "QG_MOE_GROUP_M", "QG_MOE_SMALL_BM", "QG_MOE_SMALL", "QG_GROUP_M"};
+
+// Applies one named override to o (value NULL or "" clears it).  Returns
+// false for an unknown name.
+bool apply_override(Overrides *o, const char *name, const char *val) {
+  const bool set = val && *val;
+  const int iv = set ? atoi(val) : 0;
+  if (!strcmp(name, "QG_TUNE")) {
+    int T, KR, W, S;
+    o->tune = set && sscanf(val, "%d,%d,%d,%d", &T, &KR, &W, &S) == 4 && T >= 1 && KR >= 1 && W >= 1 &&
+              W <= 16 && S >= 1;
+    if (o->tune) {
+      o->tune_v[0] = T; o->tune_v[1] = KR; o->tune_v[2] = W; o->tune_v[3] = S;
+    }
+  } else if (!strcmp(name, "QG_DECODE")) {
+    o->decode_off = set && *val == '0';
+    o->decode_n = 0;
+    int T, KR, S = 1;
+    if (set && !o->decode_off) {
+      const int n = sscanf(val, "%d,%d,%d", &T, &KR, &S);
+      if (n >= 2) {
+        o->decode_n = n;
+        o->decode_v[0] = T; o->decode_v[1] = KR; o->decode_v[2] = n == 3 ? S : 1;
+      }
+    }
+  } else if (!strcmp(name, "QG_TILED")) {
+    o->tiled_set = set;
+    o->tiled_off = set && *val == '0';
+  } else if (!strcmp(name, "QG_TILED_BM")) {
+    o->tiled_bm = (iv == 128 || iv == 256) ? iv : 0;
+  } else if (!strcmp(name, "QG_MX_BN")) {
+    o->mx_bn = (iv == 192 || iv == 224 || iv == 256) ? iv : 0;
+  } else if (!strcmp(name, "QG_MX_WAVES")) {
+    o->mx_waves = (iv == 4 || iv == 8) ? iv : 0;
+  } else if (!strcmp(name, "QG_A16_WAVES")) {
+    o->a16_waves = (iv == 4 || iv == 8) ? iv : 0;
+  } else if (!strcmp(name, "QG_A16_BN")) {
+    o->a16_bn = iv == 128 ? 128 : 0;
+  } else if (!strcmp(name, "QG_MOE_TILED_MIN")) {
+    o->moe_tiled_min = set ? std::max(0, iv) : -1;
+  } else if (!strcmp(name, "QG_MOE_GROUP_M")) {
+    o->moe_group_m = (iv >= 1 && iv <= 64) ? iv : 0;
+  } else if (!strcmp(name, "QG_MOE_SMALL_BM")) {
+    o->moe_small_bm = iv == 32 ? 32 : 0;
+  } else if (!strcmp(name, "QG_MOE_SMALL")) {
+    o->moe_small = set ? (iv != 0) : -1;
+  } else if (!strcmp(name, "QG_GROUP_M")) {
+    o->group_m = (iv >= 1 && iv <= 64) ? iv : 0;
+  } else {
+    return false;
+  }
+  return true;
+}
+
+std::atomic<const Overrides *> g_overrides{nullptr};
+std::mutex g_overrides_mu;
+
+const Overrides *overrides_from_env() {
+  Overrides *o = new Overrides();
+  for (const char *name : kOverrideNames) apply_override(o, name, getenv(name));
+  return o;
+}
+}  // namespace
+
+// The current override snapshot (the environment's on first use).
+static const Overrides &ov() {
+  const Overrides *o = g_overrides.load(std::memory_order_acquire);
+  if (o) return *o;
+  std::lock_guard<std::mutex> lock(g_overrides_mu);
+  o = g_overrides.load(std::memory_order_relaxed);
+  if (!o) {
+    o = overrides_from_env();
+    g_overrides.store(o, std::memory_order_release);
+  }
+  return *o;
+}
+
+// QG_TUNE: the skinny kernel with explicit (T, KR, W, splits).
 static bool env_variant(Variant *v) {
-  const char *s = getenv("QG_TUNE");
-  if (!s || !*s) return false;
-  int T, KR, W, S;
-  if (sscanf(s, "%d,%d,%d,%d", &T, &KR, &W, &S) != 4) return false;
-  if (T < 1 || KR < 1 || W < 1 || W > 16 || S < 1) return false;
-  v->kind = 0;
-  v->bm = 0;
-  v->tbn = 0;
-  v->T = T;
-  v->KR = KR;
-  v->W = W;
-  v->splits = S;
+  const Overrides &o = ov();
+  if (!o.tune) return false;
+  *v = Variant{0, o.tune_v[0], o.tune_v[1], o.tune_v[2], o.tune_v[3], 0, 0};
   return true;
 }
 
@@ -93,12 +193,21 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
     ++splits;
   v.W = (waves_k + splits - 1) / splits;
   v.splits = (waves_k + v.W - 1) / v.W;
+  // a cross-workgroup split needs one arrival counter per output tile in the
+  // workspace's counter prefix; past that the workgroup loops over K instead
+  if (v.splits > 1 && n_blocks * m_tiles > kMaxSplitCounters) {
+    v.KR = clamp_kr(d, v.T, 4);
+    v.W = std::min(16, (k_blocks + v.KR - 1) / v.KR);
+    v.splits = 1;
+  }
   return v;
 }
 
-// A variant must cover every k-block: W * KR * splits >= k_blocks.
-static bool covers(const Variant &v, int k_blocks) {
-  return (int64_t)v.W * v.KR * v.splits >= k_blocks;
+// Split-K arrival counters of a dense launch (one per output tile), or 0.
+static int64_t split_counters(const qg_weight &w, const Variant &v, int64_t m) {
+  if (v.splits <= 1) return 0;
+  const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
+  return v.kind == 3 ? n_blocks : ((m + 15) / 16) * n_blocks;
 }
 
 static void sanitize(const qg_layer_desc &d, Variant *v) {
@@ -115,9 +224,8 @@ static void sanitize(const qg_layer_desc &d, Variant *v) {
 // (round fill x column fill), discounted 3% per 32 columns below 256 for the
 // lower reuse of the activation tile.  QG_MX_BN overrides.
 static int mx_tile_cols(int64_t n, int64_t m, int bm) {
-  const char *e = getenv("QG_MX_BN");
   if (mx_tiled_waves() != 8) return 256;  // the 4-wave form is built for 256 only
-  if (e && (atoi(e) == 192 || atoi(e) == 224 || atoi(e) == 256)) return atoi(e);
+  if (ov().mx_bn) return ov().mx_bn;
   constexpr int kCus = 256;
   const int64_t m_tiles = (m + bm - 1) / bm;
   int best = 256;
@@ -138,8 +246,7 @@ static int mx_tile_cols(int64_t n, int64_t m, int bm) {
 
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   if (w.desc.k % 128 != 0) return false;
-  const char *s = getenv("QG_TILED");
-  if (s && *s == '0') return false;
+  if (ov().tiled_off) return false;
   const bool mx = mx_a8(w.desc) || mx_a4(w.desc);
   // the integer-format kernel addresses X and the codes with 32-bit offsets
   if (!mx && ((uint64_t)m * w.desc.k * 2 >= (1ull << 31) ||
@@ -150,8 +257,7 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   // 256-row tiles halve the weight re-reads and win at every measured shape
   // once M fills them; 128-row tiles for M in [128, 256)
   int bm = m >= 256 ? 256 : 128;
-  const char *b = getenv("QG_TILED_BM");
-  if (b && (atoi(b) == 128 || atoi(b) == 256)) bm = atoi(b);
+  if (ov().tiled_bm) bm = ov().tiled_bm;
   int bn = 128;
   if (!mx && a16_tiled_bn() == 256) {
     bm = 128;
@@ -183,6 +289,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
   if (S > 1 && ((W * KR) % 4 != 0 || (S - 1) * W * KR >= kbs)) return false;
   const int gpb = 128 / w.desc.group_size;
   if ((int64_t)W * KR * S * gpb > w.groups_padded) return false;  // scale reads stay in the row
+  if (S > 1 && (w.n_tiles + T - 1) / T > kMaxSplitCounters) return false;  // one counter per column block
   const uint64_t lds = align_up((uint64_t)m * ((uint64_t)W * KR * 256 + 16), 256) + (uint64_t)W * T * m * 64;
   if (lds > 160 * 1024 - 256) return false;  // (+ the kernel's static LDS)
   *v = Variant{3, T, KR, W, S, 0, 0};
@@ -192,10 +299,9 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
   if (mx_a8(d) || mx_a4(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
-  const char *e = getenv("QG_DECODE");
-  if (e && *e == '0') return false;
-  int T, KR, S = 1;
-  if (e && sscanf(e, "%d,%d,%d", &T, &KR, &S) >= 2) return decode_fits(w, m, T, KR, S, v);
+  const Overrides &o = ov();
+  if (o.decode_off) return false;
+  if (o.decode_n >= 2) return decode_fits(w, m, o.decode_v[0], o.decode_v[1], o.decode_v[2], v);
   // Measured on the decode shapes: one n-tile and 8 k-blocks per wave wins
   // (small workgroups start and drain independently, which hides the
   // dequantization behind the weight stream); at 16 rows the skinny kernel's
@@ -230,7 +336,15 @@ static Variant select_dense_invariant(const qg_weight &w) {
     const int bn = mx ? 256 : a16_tiled_bn();
     return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
   }
-  return skinny_for(w.desc, w.n_tiles, w.k_blocks, 1);
+  // the skinny kernel with the workgroup looping over K: the reduction order
+  // (passes in K order per wave, then the waves in index order) depends on
+  // (N, K) only
+  Variant v = skinny_for(w.desc, w.n_tiles, w.k_blocks, 1);
+  if (v.splits > 1) {
+    v.W = std::min(16, (w.k_blocks + v.KR - 1) / v.KR);
+    v.splits = 1;
+  }
+  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -242,7 +356,7 @@ static Variant select_dense_invariant(const qg_weight &w) {
 // ---------------------------------------------------------------------------
 namespace {
 struct TuneEntry {
-  int32_t wtype, group, bucket;
+  int32_t wtype, atype, group, bucket;
   int64_t n, k;
   Variant v;
 };
@@ -270,7 +384,8 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
   if (mx_a4(d) && v.kind != 1 && v.kind != 0) return false;  // W4A4: the MX tiled or MX skinny kernel
   switch (v.kind) {
     case 0:
-      return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 && covers(v, w.k_blocks);
+      return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 &&
+             split_counters(w, v, m) <= kMaxSplitCounters;
     case 1:
       return mx && d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) &&
              (v.tbn == 256 || (mx_tiled_waves() == 8 && (v.tbn == 192 || v.tbn == 224)));
@@ -290,8 +405,8 @@ static bool tuned_lookup(const qg_weight &w, int64_t m, Variant *v) {
   std::lock_guard<std::mutex> lock(g_tune_mu);
   const int b = m_bucket(m);
   for (const TuneEntry &e : g_tune)
-    if (e.wtype == w.desc.wtype && e.group == w.desc.group_size && e.n == w.desc.n && e.k == w.desc.k &&
-        e.bucket == b) {
+    if (e.wtype == w.desc.wtype && e.atype == w.desc.atype && e.group == w.desc.group_size && e.n == w.desc.n &&
+        e.k == w.desc.k && e.bucket == b) {
       if (!variant_valid(w, m, e.v)) return false;
       *v = e.v;
       return true;
@@ -303,12 +418,12 @@ static void tuned_store(const qg_weight &w, int64_t m, const Variant &v) {
   std::lock_guard<std::mutex> lock(g_tune_mu);
   const int b = m_bucket(m);
   for (TuneEntry &e : g_tune)
-    if (e.wtype == w.desc.wtype && e.group == w.desc.group_size && e.n == w.desc.n && e.k == w.desc.k &&
-        e.bucket == b) {
+    if (e.wtype == w.desc.wtype && e.atype == w.desc.atype && e.group == w.desc.group_size && e.n == w.desc.n &&
+        e.k == w.desc.k && e.bucket == b) {
       e.v = v;
       return;
     }
-  g_tune.push_back(TuneEntry{w.desc.wtype, w.desc.group_size, b, w.desc.n, w.desc.k, v});
+  g_tune.push_back(TuneEntry{w.desc.wtype, w.desc.atype, w.desc.group_size, b, w.desc.n, w.desc.k, v});
 }
 
 static Variant select_dense_heuristic(const qg_weight &w, int64_t m);
@@ -316,7 +431,8 @@ static Variant select_dense_heuristic(const qg_weight &w, int64_t m);
 Variant select_dense(const qg_weight &w, int64_t m) {
   Variant v;
   // experiment overrides win over the table
-  if (!getenv("QG_TUNE") && !getenv("QG_DECODE") && !getenv("QG_TILED") && tuned_lookup(w, m, &v)) return v;
+  const Overrides &o = ov();
+  if (!o.tune && !o.decode_off && o.decode_n == 0 && !o.tiled_set && tuned_lookup(w, m, &v)) return v;
   return select_dense_heuristic(w, m);
 }
 
@@ -325,17 +441,23 @@ static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
   if (mx_a4(w.desc)) {
     // from 128 rows the tiled kernel with e2m1 operands; below, the MX skinny
     // kernel, which widens each e2m1 fragment exactly to e4m3 in registers
-    if (m >= 128) {
-      const int bm = m >= 256 ? 256 : 128;
+    if (m >= 128 && !ov().tiled_off) {
+      const int bm = ov().tiled_bm ? ov().tiled_bm : m >= 256 ? 256 : 128;
       return Variant{1, 1, 1, 1, 1, bm, mx_tile_cols(w.desc.n, m, bm)};
+    }
+    if (env_variant(&v)) {
+      sanitize(w.desc, &v);
+      if (split_counters(w, v, m) > kMaxSplitCounters) v.splits = 1;
+      return v;
     }
     return skinny_for(w.desc, w.n_tiles, w.k_blocks, (m + 15) / 16);
   }
   if (tiled_for(w, m, &v)) return v;
-  if (!getenv("QG_TUNE") && decode_for(w, m, &v)) return v;
+  if (!ov().tune && decode_for(w, m, &v)) return v;
   if (env_variant(&v)) {
     sanitize(w.desc, &v);
-    while (!covers(v, w.k_blocks)) ++v.splits;
+    // (K beyond W * KR * splits blocks: the workgroups loop over K)
+    if (split_counters(w, v, m) > kMaxSplitCounters) v.splits = 1;
     return v;
   }
   const int64_t m_tiles = (m + 15) / 16;
@@ -349,10 +471,11 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
     v.splits = 1;
     return v;
   }
-  // the grouped kernel keeps K inside one workgroup (no cross-workgroup split)
+  // the grouped kernel keeps K inside one workgroup (no cross-workgroup
+  // split); past 16 waves of KR blocks the workgroup loops over K
   const int64_t m_tiles = std::max<int64_t>(1, (pairs + 15) / 16);
   Variant s = skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles);
-  if (s.splits > 1) {
+  if (s.splits > 1 || (int64_t)s.W * s.KR < w.k_blocks) {
     // long K: the deepest spill-free wave (KR = 4), T reduced to fit
     s.KR = 4;
     s.T = mx_a8(w.desc) ? 2 : 1;
@@ -377,8 +500,7 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
       (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31))
     return 0;
   int min_rows = 64;
-  const char *e = getenv("QG_MOE_TILED_MIN");
-  if (e && *e) min_rows = std::max(0, atoi(e));
+  if (ov().moe_tiled_min >= 0) min_rows = ov().moe_tiled_min;
   if (min_rows <= 0) return 0;
   // no expert can reach the threshold: all go to the small-tile form
   // (integer formats) or the skinny kernel
@@ -390,18 +512,14 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
 // the matrix core fed while the other wave of the SIMD waits on LDS reads or
 // the stage barrier; measured 1.3x faster than 4 at M = 4096.
 int mx_tiled_waves() {
-  const char *e = getenv("QG_MX_WAVES");
-  if (e && (atoi(e) == 4 || atoi(e) == 8)) return atoi(e);
-  return 8;
+  return ov().mx_waves ? ov().mx_waves : 8;
 }
 
 // Waves of the integer-format tiled kernel: 8 (4 x 2, two per SIMD, wave
 // tile (BM / 4) x 64) hides one wave's waits behind the other's MFMAs and
 // dequantization; measured 1.15-1.25x faster than 4 at M = 4096.
 int a16_tiled_waves() {
-  const char *e = getenv("QG_A16_WAVES");
-  if (e && (atoi(e) == 4 || atoi(e) == 8)) return atoi(e);
-  return 8;
+  return ov().a16_waves ? ov().a16_waves : 8;
 }
 
 // Columns of the integer-format tiled kernel's tile: 256 (with 128 rows, 2 x 4
@@ -410,14 +528,12 @@ int a16_tiled_waves() {
 // QG_A16_BN=128 keeps 128 columns (then QG_TILED_BM picks the rows).
 int a16_tiled_bn() {
   if (a16_tiled_waves() != 8) return 128;
-  const char *e = getenv("QG_A16_BN");
-  return (e && atoi(e) == 128) ? 128 : 256;
+  return ov().a16_bn == 128 ? 128 : 256;
 }
 
 // Raster group of the tiled MoE launches (QG_MOE_GROUP_M overrides).
 static int moe_group_m() {
-  const char *e = getenv("QG_MOE_GROUP_M");
-  return (e && atoi(e) >= 1 && atoi(e) <= 64) ? atoi(e) : 1;
+  return ov().moe_group_m ? ov().moe_group_m : 1;
 }
 
 // Tile-list capacity: one tile per 128 rows plus one partial tile per expert
@@ -428,8 +544,7 @@ static int64_t moe_tiles_cap(const qg_weight &w, int64_t pairs, int min_rows) {
 
 // Rows of the small tiles: 64, or 32 (QG_MOE_SMALL_BM).
 static int moe_small_bm() {
-  const char *e = getenv("QG_MOE_SMALL_BM");
-  return (e && atoi(e) == 32) ? 32 : kMoeSmallTileRows;
+  return ov().moe_small_bm == 32 ? 32 : kMoeSmallTileRows;
 }
 
 // Small-tile list capacity (experts with 1 .. min_rows - 1 rows): one tile per
@@ -448,8 +563,7 @@ static int64_t moe_small_tiles_cap(const qg_weight &w, int64_t pairs) {
 // small tiles.
 static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows) {
   if (min_rows <= 0) return false;
-  const char *e = getenv("QG_MOE_SMALL");
-  if (e && *e) return atoi(e) != 0;
+  if (ov().moe_small >= 0) return ov().moe_small != 0;
   return pairs >= 256;
 }
 
@@ -493,22 +607,20 @@ static void fill_weight(const qg_layer_desc *d, const Layout &L, void *dev, uint
   out->zeros_offset = L.has_zp ? L.zeros_offset : 0;
 }
 
-// Split-K counters (256-byte aligned) and fp32 partial tiles of a skinny or
-// decode launch; a multiple of 256 bytes.
-static uint64_t split_region_bytes(const qg_weight &w, const Variant &v, int64_t m) {
-  if (v.splits <= 1) return 0;
-  const int64_t m_tiles = (m + 15) / 16;
-  const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
-  const uint64_t counters = align_up((uint64_t)m_tiles * n_blocks * 4, 256);
-  const uint64_t partials = (uint64_t)v.splits * m_tiles * n_blocks * (uint64_t)v.T * 256 * 4;
-  return counters + partials;
-}
-
+// Dense workspace layout: [split-K arrival counters, kSplitCounterBytes]
+// [fp32 partial tiles of a split launch, or the tiled kernels' scratch].
+// The counter prefix sits at the same place for every layer and M and is
+// never written by anything but the counters, which every split launch
+// leaves at zero; so one workspace, zero-filled once, serves any sequence of
+// calls on one stream.  Launches that use neither need no workspace.
 static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) {
   if (m <= 0) return 0;
-  if (v.kind == 2) return a16_tiled_ws_bytes(w.desc, m);
-  if (v.kind == 1) return mx_tiled_ws_bytes(m, w.k_blocks);
-  return split_region_bytes(w, v, m);
+  if (v.kind == 2) return kSplitCounterBytes + a16_tiled_ws_bytes(w.desc, m);
+  if (v.kind == 1) return kSplitCounterBytes + mx_tiled_ws_bytes(m, w.k_blocks);
+  if (v.splits <= 1) return 0;
+  const int64_t m_tiles = v.kind == 3 ? 1 : (m + 15) / 16;
+  const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
+  return kSplitCounterBytes + (uint64_t)v.splits * m_tiles * n_blocks * (uint64_t)v.T * 256 * 4;
 }
 
 static void base_args(const qg_weight &w, GemmArgs *a) {
@@ -525,8 +637,7 @@ static void base_args(const qg_weight &w, GemmArgs *a) {
   a->k = (int32_t)w.desc.k;
   a->splits = 1;
   // raster group of the dense tiled launches (QG_GROUP_M overrides)
-  const char *g = getenv("QG_GROUP_M");
-  a->group_m = (g && atoi(g) >= 1 && atoi(g) <= 64) ? atoi(g) : 4;
+  a->group_m = ov().group_m ? ov().group_m : 4;
 }
 
 }  // namespace qg
@@ -632,18 +743,16 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
   a.otype = otype;
   a.m = (int32_t)m;
   a.splits = v.splits;
+  // counters start at zero (the caller zero-fills the workspace once) and
+  // every call leaves them at zero again; the scratch behind them is free
+  void *scratch = ws ? (void *)((uint8_t *)ws + kSplitCounterBytes) : nullptr;
   if (v.splits > 1) {
-    // counters start at zero (the caller zero-fills the workspace once) and
-    // every call leaves them at zero again
-    const int64_t m_tiles = (m + 15) / 16;
-    const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
-    const uint64_t cnt = (uint64_t)m_tiles * n_blocks;
     a.counters = (uint32_t *)ws;
-    a.partials = (float *)((uint8_t *)ws + align_up(cnt * 4, 256));
+    a.partials = (float *)scratch;
   }
   if (v.kind == 1) {
     if (L.a4) a.ldx = ldx / 2;  // the kernel addresses e2m1 rows in bytes
-    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), ws, stream, L.a4);
+    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), scratch, stream, L.a4);
   }
   if (L.a4) {
     // the MX skinny kernel widens the e2m1 fragments to e4m3 in registers
@@ -651,7 +760,7 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
     return launch_dense_mx(a, d, v, stream);
   }
   if (v.kind == 3) return launch_decode_a16(a, d, v, stream);
-  if (v.kind == 2) return launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), ws, true, stream);
+  if (v.kind == 2) return launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), scratch, true, stream);
   return L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
 }
 
@@ -774,7 +883,6 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   if (!aligned16(x) || !aligned16(y) || x_pitch(L, d.k) % 16 != 0 || (d.n * yel) % 4 != 0)
     return QG_ERR_ALIGNMENT;
   const Variant v = select_moe(wk, pairs);
-  if (!covers(v, wk.k_blocks)) return QG_ERR_UNSUPPORTED;  // K too long for one workgroup
   const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
   const int min_rows = moe_tiled_min_rows(wk, pairs, x_rows_count);
   const uint64_t need = moe_ws_bytes(wk, pairs, x_rows_count, min_rows);
@@ -911,14 +1019,18 @@ extern "C" qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, 
   return hip_status(launch_moe_combine(y, yf, ldy, topk_weights, num_tokens, topk, n, bias, out, of, ldout, stream));
 }
 
-static void describe_variant(const Variant &v, bool mx, char *buf, uint64_t buf_bytes) {
+static void describe_variant(const Variant &v, bool mx, int k_blocks, char *buf, uint64_t buf_bytes) {
   if (v.kind == 3)
     snprintf(buf, buf_bytes, v.splits > 1 ? "a16_decode T=%d KR=%d W=%d splits=%d" : "a16_decode T=%d KR=%d W=%d",
              v.T, v.KR, v.W, v.splits);
   else if (v.kind == 1 || v.kind == 2)
     snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", mx ? "mx" : "a16", v.bm, v.tbn);
-  else
-    snprintf(buf, buf_bytes, "%s_skinny T=%d KR=%d W=%d splits=%d", mx ? "mx" : "a16", v.T, v.KR, v.W, v.splits);
+  else {
+    // (K beyond W * KR * splits blocks: the workgroups loop over K)
+    const int span = v.W * v.KR * v.splits, passes = (k_blocks + span - 1) / span;
+    snprintf(buf, buf_bytes, passes > 1 ? "%s_skinny T=%d KR=%d W=%d splits=%d passes=%d" : "%s_skinny T=%d KR=%d W=%d splits=%d",
+             mx ? "mx" : "a16", v.T, v.KR, v.W, v.splits, passes);
+  }
 }
 
 // Candidates of one dense (layer, M): the heuristic's choice first, then the
@@ -971,19 +1083,13 @@ static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> 
 constexpr int kTuneMaxReps = 64;
 constexpr uint64_t kTuneSinkBytes = 16384;
 
-// Autotune workspace: [split-K region (zero on entry, left zero)][tiled
-// kernels' scratch][flush sink], each 256-byte aligned.
-static void tune_ws_parts(const qg_weight &w, int64_t m, const std::vector<Variant> &c, uint64_t *split_bytes,
-                          uint64_t *tiled_bytes) {
-  *split_bytes = 0;
-  *tiled_bytes = 0;
-  for (const Variant &v : c) {
-    const uint64_t b = align_up(dense_ws_bytes(w, v, m), 256);
-    if (v.kind == 1 || v.kind == 2)
-      *tiled_bytes = std::max(*tiled_bytes, b);
-    else
-      *split_bytes = std::max(*split_bytes, b);
-  }
+// Autotune workspace: a dense workspace for every candidate (the counter
+// prefix, cleared by the call, then the largest candidate's partials or
+// scratch), then the flush sink.
+static uint64_t tune_ws_dense_bytes(const qg_weight &w, int64_t m, const std::vector<Variant> &c) {
+  uint64_t b = kSplitCounterBytes;
+  for (const Variant &v : c) b = std::max(b, align_up(dense_ws_bytes(w, v, m), 256));
+  return b;
 }
 
 extern "C" qg_status qg_gemm_autotune_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes) {
@@ -997,9 +1103,7 @@ extern "C" qg_status qg_gemm_autotune_workspace_size(const qg_weight *w, int64_t
   }
   std::vector<Variant> c;
   tune_candidates(*w, m, &c);
-  uint64_t sb, tb;
-  tune_ws_parts(*w, m, c, &sb, &tb);
-  *bytes = sb + tb + kTuneSinkBytes;
+  *bytes = tune_ws_dense_bytes(*w, m, c) + kTuneSinkBytes;
   return QG_OK;
 }
 
@@ -1024,15 +1128,13 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (flush && (flush_bytes % 16 != 0 || !aligned16(flush))) return QG_ERR_ALIGNMENT;
   std::vector<Variant> cand;
   tune_candidates(*w, m, &cand);
-  uint64_t sb, tb;
-  tune_ws_parts(*w, m, cand, &sb, &tb);
-  if (ws_bytes < sb + tb + kTuneSinkBytes) return QG_ERR_BUFFER_TOO_SMALL;
-  uint8_t *split_ws = (uint8_t *)ws, *tiled_ws = split_ws + sb, *sink = tiled_ws + tb;
-  // the split-K counters must start at zero; the rest is scratch
-  if (sb > 0) {
-    const hipError_t me = hipMemsetAsync(split_ws, 0, sb, stream);
-    if (me != hipSuccess) return hip_status(me);
-  }
+  const uint64_t db = tune_ws_dense_bytes(*w, m, cand);
+  if (ws_bytes < db + kTuneSinkBytes) return QG_ERR_BUFFER_TOO_SMALL;
+  uint8_t *sink = (uint8_t *)ws + db;
+  // the split-K counters must start at zero; the rest is scratch (this call
+  // synchronizes its stream, so it is never part of a captured graph)
+  const hipError_t me = hipMemsetAsync(ws, 0, kSplitCounterBytes, stream);
+  if (me != hipSuccess) return hip_status(me);
 
   hipEvent_t ev[2 * kTuneMaxReps];
   int made = 0;
@@ -1043,8 +1145,7 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   float best_us = 0.f;
   for (size_t i = 0; he == hipSuccess && i < cand.size(); ++i) {
     const Variant &v = cand[i];
-    void *vws = (v.kind == 1 || v.kind == 2) ? (void *)tiled_ws : (void *)split_ws;
-    auto run = [&]() { return launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, vws, stream); };
+    auto run = [&]() { return launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, ws, stream); };
     if (run() != hipSuccess) continue;  // an instance this shape does not compile to: skip it
     for (int r = 0; r < reps && he == hipSuccess; ++r) {
       if (flush && flush_bytes) he = launch_stream_read(flush, flush_bytes, sink, stream);
@@ -1070,9 +1171,28 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (he != hipSuccess) return hip_status(he);
   if (best < 0) return QG_ERR_UNSUPPORTED;
   tuned_store(*w, m, cand[best]);
-  if (chosen && chosen_bytes) describe_variant(cand[best], L.is_mx, chosen, chosen_bytes);
+  if (chosen && chosen_bytes) describe_variant(cand[best], L.is_mx, w->k_blocks, chosen, chosen_bytes);
   if (chosen_us) *chosen_us = best_us;
   return QG_OK;
+}
+
+extern "C" qg_status qg_set_override(const char *name, const char *value) {
+  if (!name) return QG_ERR_INVALID_ARGUMENT;
+  ov();  // the environment's snapshot exists from here on
+  std::lock_guard<std::mutex> lock(g_overrides_mu);
+  Overrides *o = new Overrides(*g_overrides.load(std::memory_order_relaxed));
+  if (!apply_override(o, name, value)) {
+    delete o;
+    return QG_ERR_INVALID_ARGUMENT;
+  }
+  g_overrides.store(o, std::memory_order_release);
+  return QG_OK;
+}
+
+extern "C" void qg_clear_overrides(void) {
+  ov();
+  std::lock_guard<std::mutex> lock(g_overrides_mu);
+  g_overrides.store(new Overrides(), std::memory_order_release);
 }
 
 extern "C" void qg_autotune_reset(void) {
@@ -1080,13 +1200,19 @@ extern "C" void qg_autotune_reset(void) {
   g_tune.clear();
 }
 
-extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf,
-                                          uint64_t buf_bytes) {
+extern "C" qg_status qg_describe_dispatch_ex(const qg_weight *w, int64_t m, uint32_t flags, char *buf,
+                                             uint64_t buf_bytes) {
   Layout L;
   qg_status st = check_weight(w, &L);
   if (st != QG_OK) return st;
-  if (!buf || buf_bytes == 0 || m < 0) return QG_ERR_INVALID_ARGUMENT;
-  const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : select_dense(*w, m);
-  describe_variant(v, L.is_mx, buf, buf_bytes);
+  if (!buf || buf_bytes == 0 || m < 0 || (flags & ~(uint32_t)QG_GEMM_BATCH_INVARIANT) != 0)
+    return QG_ERR_INVALID_ARGUMENT;
+  if (flags && w->desc.num_experts > 1) return QG_ERR_INVALID_ARGUMENT;
+  const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : dense_variant(*w, m, flags);
+  describe_variant(v, L.is_mx, w->k_blocks, buf, buf_bytes);
   return QG_OK;
+}
+
+extern "C" qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf, uint64_t buf_bytes) {
+  return qg_describe_dispatch_ex(w, m, 0, buf, buf_bytes);
 }

@@ -141,6 +141,12 @@ struct GemmArgs {
 
 constexpr int kMaxExperts = 1024;  // LDS-resident per-expert tables
 
+// Dense workspaces begin with the arrival counters of split-K launches (one
+// uint32 per output tile, left at zero by every launch); partial tiles and
+// the tiled kernels' scratch follow this prefix.
+constexpr uint64_t kSplitCounterBytes = 64 * 1024;
+constexpr int64_t kMaxSplitCounters = (int64_t)(kSplitCounterBytes / 4);
+
 // One entry of the tuning table: a kernel variant and its tile parameters.
 struct Variant {
   int kind;    // 0 = skinny (16-row tiles, weights streamed to VGPRs), 1 = MX tiled (LDS),

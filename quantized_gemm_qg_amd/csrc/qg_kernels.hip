@@ -425,6 +425,16 @@ __device__ __forceinline__ void mx_wave(const GemmArgs &a, const uint8_t *wexp,
   }
 }
 
+// Waits 16 wait states with the accumulators as operands, so the wait sits
+// between the MFMAs that write them and every later read.
+__device__ __forceinline__ void mfma_drain(f32x4 (&acc)[1]) { asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0])); }
+__device__ __forceinline__ void mfma_drain(f32x4 (&acc)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
+}
+__device__ __forceinline__ void mfma_drain(f32x4 (&acc)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+}
+
 // ---------------------------------------------------------------------------
 // the kernel: a loop over work items (one item per workgroup for dense
 // launches; a persistent grid for MoE)
@@ -460,12 +470,16 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
     const Item first = decode_item(a, moe != 0, blockIdx.x, n_blocks, total_tiles, prefix);
     nxt_xr = (int)x_row_of(a, moe != 0, first, r16 < first.rows ? r16 : 0);
   }
+  // K blocks one pass of the launch covers; beyond that every workgroup
+  // loops over K (pass p, split s, wave w takes blocks from ((p * splits + s)
+  // * waves + w) * KR), accumulating in registers
+  const int span = nwaves * KR * a.splits;
+  const int passes = (a.k_blocks + span - 1) / span;
   for (int64_t item = blockIdx.x; item < total_items; item += gridDim.x) {
     const Item it = decode_item(a, moe != 0, item, n_blocks, total_tiles, prefix);
     const int64_t xr = nxt_xr;
     const uint8_t *wexp = a.wbase + (uint64_t)it.expert * a.expert_stride;
     const int nt0 = it.nb * T;
-    const int kb0 = (it.split * nwaves + wave) * KR;
     auto prefetch_next = [&]() {
       const int64_t next = item + gridDim.x;
       if (next < total_items) {  // workgroup-uniform
@@ -477,21 +491,32 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
     f32x4 acc[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) acc[t] = {0.f, 0.f, 0.f, 0.f};
-    if (kb0 < a.k_blocks) {
-      if constexpr (FMT == 4 || FMT == 6) {
-        const uint8_t *xrow = (const uint8_t *)a.x + xr * a.ldx;
-        const uint8_t *xsrow = a.x_scales + xr * (int64_t)(a.k >> 5);
-        mx_wave<T, KR, decltype(prefetch_next), FMT == 6>(a, wexp, xrow, xsrow, nt0, kb0, acc, prefetch_next);
+    for (int p = 0; p < passes; ++p) {
+      const int kb0 = ((p * a.splits + it.split) * nwaves + wave) * KR;
+      // the next item's rows are resolved once, behind the first pass's loads
+      auto hook = [&]() {
+        if (p == 0) prefetch_next();
+      };
+      if (kb0 < a.k_blocks) {
+        if constexpr (FMT == 4 || FMT == 6) {
+          const uint8_t *xrow = (const uint8_t *)a.x + xr * a.ldx;
+          const uint8_t *xsrow = a.x_scales + xr * (int64_t)(a.k >> 5);
+          mx_wave<T, KR, decltype(hook), FMT == 6>(a, wexp, xrow, xsrow, nt0, kb0, acc, hook);
+        } else {
+          const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
+          constexpr int BITS = (FMT <= 1 || FMT == 5) ? 4 : 3;
+          constexpr bool ZP = (FMT == 1 || FMT == 3);
+          a16_wave<BITS, ZP, GROUP, T, KR, false, 4, decltype(hook), FMT == 5>(a, wexp, xrow, nt0, kb0, acc, hook);
+        }
       } else {
-        const uint16_t *xrow = (const uint16_t *)a.x + xr * a.ldx;
-        constexpr int BITS = (FMT <= 1 || FMT == 5) ? 4 : 3;
-        constexpr bool ZP = (FMT == 1 || FMT == 3);
-        a16_wave<BITS, ZP, GROUP, T, KR, false, 4, decltype(prefetch_next), FMT == 5>(a, wexp, xrow, nt0, kb0, acc,
-                                                                                     prefetch_next);
+        hook();
       }
-    } else {
-      prefetch_next();
     }
+
+    // The last MFMA of the K loop may still be writing acc: the compiler
+    // does not count its write-back latency across the loop's exit, so the
+    // wait is explicit (16 wait states; the MFMAs here need at most 12)
+    mfma_drain(acc);
 
     // reduce the K-split waves of the workgroup in a fixed order
 #pragma unroll

@@ -10,3 +10,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture
+def override():
+    """Set tuning-table overrides (QG_TUNE, QG_DECODE, ...) through the library
+    for one test; all are cleared afterwards."""
+    import quantized_gemm_qg_amd as qg
+
+    yield qg.set_override
+    qg.clear_overrides()

@@ -258,8 +258,8 @@ def test_dispatch_table_covers_k():
             if "tiled" in s:  # LDS-tiled large-M paths: loop over all of K
                 assert m >= 128 and k % 128 == 0, s
                 assert ("mx_" in s) == (wt == qg.W_MXFP4), s
-                if wt != qg.W_MXFP4:  # the group row sums of X live in the workspace
-                    assert qg.gemm_workspace_size(w, m) >= (k // g) * m * 4
+                if wt != qg.W_MXFP4:  # the group row sums of X live behind the counter prefix
+                    assert qg.gemm_workspace_size(w, m) >= 65536 + (k // g) * m * 4
                 continue
             if "decode" in s:  # activations in LDS, one workgroup over all of K (or of a split)
                 assert wt != qg.W_MXFP4 and m <= 16 and k % 512 == 0, s
@@ -267,9 +267,9 @@ def test_dispatch_table_covers_k():
                 T, KR, W = vals[:3]
                 S = vals[3] if len(vals) > 3 else 1
                 assert W * KR * S >= -(-k // 128) and 1 <= W <= 16, s
-                if S > 1:  # partials and arrival counters live in the workspace
+                if S > 1:  # arrival counters (prefix) and partials live in the workspace
                     assert (S - 1) * W * KR < -(-k // 128) and (W * KR) % 4 == 0, s
-                    assert qg.gemm_workspace_size(w, m) >= S * -(-n // (16 * T)) * T * 256 * 4
+                    assert qg.gemm_workspace_size(w, m) >= 65536 + S * -(-n // (16 * T)) * T * 256 * 4
                 continue
             T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
             assert W * KR * S >= -(-k // 128), s
@@ -294,7 +294,8 @@ def test_binding_maps_a_single_hip_runtime():
 
 def test_moe_dispatch_covers_configured_shapes():
     """The grouped kernel keeps K in one workgroup: every configured expert
-    shape (gate_up and down of both MoE configurations) must be covered."""
+    shape (gate_up and down of both MoE configurations) is covered in one
+    pass of the workgroup's waves."""
     for wt, n, k, g, e in [(qg.W_INT4, 4096, 7168, 128, 256), (qg.W_INT4, 7168, 2048, 128, 256),
                            (qg.W_MXFP4, 1280, 4096, 32, 128), (qg.W_MXFP4, 4096, 640, 32, 128)]:
         w = _bound(qg.layer_desc(wt, n, k, g, num_experts=e))
@@ -504,3 +505,48 @@ def test_w4a4_host_logic():
         with pytest.raises(qg.QGError) as e:
             qg.quantize_mxfp4(a["x"], a["rows"], a["k"], a["ldx"], a["q"], a["ldq"], a["qs"], stream=S)
         assert e.value.status == status, kw
+
+
+def test_long_k_dispatch_loops_inside_the_workgroup():
+    """K past one pass of a workgroup's waves (MoE: 16 waves x 4 blocks = 8192)
+    is served by looping over K, never rejected: the MoE dispatch at K = 14336
+    and a dense layer whose split-K counters would not fit the workspace's
+    counter prefix."""
+    for wt, g in ((qg.W_INT4, 128), (qg.W_MXFP4, 32)):
+        w = _bound(qg.layer_desc(wt, 256, 14336, g, num_experts=32))
+        for pairs in (8, 16, 200):
+            s = qg.describe_dispatch(w, pairs)
+            T, KR, W, S, P = (int(v) for v in re.findall(r"=(\d+)", s))
+            assert S == 1 and W <= 16 and W * KR * P >= 112 and W * KR * (P - 1) < 112, s
+        assert qg.moe_workspace_size(w, 4096, 8) > 0
+    # K % 128 != 0 (no large-M kernel), long K, many rows: no cross-workgroup
+    # split (its counters would exceed the 64 KiB prefix), the workgroups loop
+    w = _bound(qg.layer_desc(qg.W_INT4, 14336, 14336 + 32, 32))
+    s = qg.describe_dispatch(w, 4096)
+    assert "splits=1 passes=" in s, s
+    assert qg.gemm_workspace_size(w, 4096) == 0
+    # and at 16 rows the split is kept (16 x 896 / T counters fit)
+    assert "splits=1" not in qg.describe_dispatch(w, 16)
+
+
+def test_overrides_through_the_library():
+    """Experiment overrides are set through qg_set_override (the environment is
+    read once per process), and clearing them restores the heuristics."""
+    w = _bound(qg.layer_desc(qg.W_UINT4, 4096, 14336, 128))
+    base = qg.describe_dispatch(w, 1)
+    assert base.startswith("a16_decode")
+    try:
+        qg.set_override("QG_DECODE", "0")
+        assert qg.describe_dispatch(w, 1).startswith("a16_skinny")
+        qg.set_override("QG_DECODE", "2,8")
+        assert qg.describe_dispatch(w, 1).startswith("a16_decode T=2 KR=8")
+        qg.set_override("QG_DECODE", None)
+        assert qg.describe_dispatch(w, 1) == base
+        qg.set_override("QG_TUNE", "1,2,8,2")
+        assert qg.describe_dispatch(w, 4) == "a16_skinny T=1 KR=2 W=8 splits=2 passes=4"
+        with pytest.raises(qg.QGError):
+            qg.set_override("QG_NOT_A_KNOB", "1")
+    finally:
+        qg.clear_overrides()
+    assert qg.describe_dispatch(w, 1) == base
+

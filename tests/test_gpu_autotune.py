@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import quantized_gemm_qg_amd as qg
-from gpu_harness import TOL_BF16, Acts, Layer, err, require_gpu, run_gemm, tol_f32
+from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, check_mx_f32, err, require_gpu, run_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,13 @@ def test_autotune_records_and_dispatches(wtype, n, k, g, m):
     assert us > 0
     assert qg.describe_dispatch(layer.w, m) == chosen
     assert qg.describe_dispatch(layer.w, other_m) == before_other  # another M bucket keeps the heuristics
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(layer.mx))):
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
         y = run_gemm(layer, acts, m, otype)
         e = err(y, oracle.gemm(acts.xdq, layer.wdq()))
-        assert e <= tol, (otype, e)
+        if otype == qg.O_F32 and layer.mx:
+            check_mx_f32(layer, acts, m, y)   # the tuned variant's own accumulation
+        else:
+            assert e <= tol, (otype, e)
     qg.autotune_reset()
     assert qg.describe_dispatch(layer.w, other_m) == before_other
 
@@ -67,7 +70,7 @@ def test_autotune_entry_serves_its_bucket_only_when_valid():
     c3, _ = tune(layer, acts, 3)
     assert qg.describe_dispatch(layer.w, 2) == c3 and qg.describe_dispatch(layer.w, 4) == c3
     y = run_gemm(layer, acts, 4, qg.O_F32)
-    assert err(y, oracle.gemm(acts.xdq, layer.wdq())) <= tol_f32(False)
+    assert err(y, oracle.gemm(acts.xdq, layer.wdq())) <= TOL_F32
 
 
 def test_batch_invariant_ignores_the_table():
@@ -84,3 +87,18 @@ def test_batch_invariant_ignores_the_table():
     before = inv()
     tune(layer, acts, 64)
     assert torch.equal(inv(), before)
+
+
+def test_autotune_entries_are_per_activation_type():
+    """Two MXFP4 layers of one shape, one with MXFP8 and one with bf16
+    activations: tuning one leaves the other on its heuristics."""
+    n, k, m = 1024, 2048, 200
+    a8 = Layer(qg.W_MXFP4, n, k, 32, seed=48)
+    a16 = Layer(qg.W_MXFP4, n, k, 32, seed=48, atype=qg.A_BF16)
+    h16 = qg.describe_dispatch(a16.w, m)
+    chosen, _ = tune(a8, Acts(True, m, k, seed=49), m)
+    assert qg.describe_dispatch(a8.w, m) == chosen
+    assert qg.describe_dispatch(a16.w, m) == h16
+    acts = Acts(False, m, k, seed=50)
+    y = run_gemm(a16, acts, m, qg.O_F32)
+    assert err(y, oracle.gemm(acts.xdq, a16.wdq())) <= TOL_F32

@@ -15,7 +15,7 @@ import torch
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, err, require_gpu, run_gemm, tol_f32
+from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, assert_bf16_is_rne, check_mx_f32, err, require_gpu, run_gemm
 
 pytestmark = pytest.mark.gpu
 
@@ -28,8 +28,13 @@ def _gpu():
 
 
 def _check(layer, acts, m, rows=None):
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(layer.mx))):
-        y = run_gemm(layer, acts, m, otype)
+    """bf16 outputs against the oracle (normwise); fp32 outputs against the
+    oracle (integer formats: normwise) or, for MX layers, bit for bit
+    against the block-scaled MFMA model (the normwise error is printed); the
+    bf16 output against RNE of the fp32 one (bit for bit)."""
+    ys = {}
+    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
+        y = ys[otype] = run_gemm(layer, acts, m, otype)
         if rows is None:
             yref = oracle.gemm(acts.xdq, layer.wdq())
             e = err(y, yref)
@@ -37,8 +42,12 @@ def _check(layer, acts, m, rows=None):
             yref = oracle.gemm(acts.xdq[rows], layer.wdq())
             e = oracle.normwise_error(y[rows].float().cpu().numpy().astype(np.float64), yref)
         print(f"  otype={otype} err={e:.3e}", flush=True)
-        assert e <= tol, (otype, e)
         assert torch.isfinite(y.float()).all()
+        if otype == qg.O_F32 and layer.mx:
+            check_mx_f32(layer, acts, m, y, rows=rows)
+        else:
+            assert e <= tol, (otype, e)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
 
 
 def test_tiny_w4a16_config():
@@ -88,7 +97,7 @@ def test_ragged_shapes(m):
     _check(mxl, Acts(True, m, 640, seed=m), m)
 
 
-def test_split_k_path_matches(monkeypatch):
+def test_split_k_path_matches(override):
     """K split across workgroups: one zero-filled workspace serves consecutive
     calls with different split counts (the counters reset themselves)."""
     layer = Layer(qg.W_UINT4, 64, 4096, 128, seed=3)
@@ -97,7 +106,7 @@ def test_split_k_path_matches(monkeypatch):
         acts = Acts(False, m, 4096, seed=3)
         ref = oracle.gemm(acts.xdq, layer.wdq())
         for tune in ("1,2,4,4", "1,1,2,16", "2,2,4,4", "4,2,8,2", "1,4,1,8"):
-            monkeypatch.setenv("QG_TUNE", tune)
+            override("QG_TUNE", tune)
             assert int(qg.describe_dispatch(layer.w, m).split("splits=")[1]) > 1
             need = qg.gemm_workspace_size(layer.w, m)
             assert 0 < need <= ws.numel()
@@ -109,12 +118,12 @@ def test_split_k_path_matches(monkeypatch):
             assert int(ws[:4 * 64].view(torch.int32).abs().sum()) == 0  # counters back at zero
 
 
-def test_tuning_variants_agree(monkeypatch):
+def test_tuning_variants_agree(override):
     layer = Layer(qg.W_INT3, 64, 2048, 128, seed=4)
     acts = Acts(False, 7, 2048, seed=4)
     ref = oracle.gemm(acts.xdq, layer.wdq())
     for tune in ("1,1,16,1", "1,2,8,1", "1,4,4,1", "2,4,4,1", "2,1,16,1", "1,8,2,1"):
-        monkeypatch.setenv("QG_TUNE", tune)
+        override("QG_TUNE", tune)
         y = run_gemm(layer, acts, 7, qg.O_F32)
         assert err(y, ref) <= TOL_F32, tune
 
@@ -167,11 +176,11 @@ def test_w4a8_mx_full_size_sampled_rows(nk):
 
 @pytest.mark.parametrize("bn", ["256", "224", "192"])
 @pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (300, 200, 640), (777, 1040, 4096)])
-def test_mx_tiled_large_m_ragged(monkeypatch, m, n, k, bn):
+def test_mx_tiled_large_m_ragged(override, m, n, k, bn):
     """The LDS-tiled MX kernel (M >= 256) with partial row and column tiles,
     at each tile width (224 and 192 columns split their blocks unevenly over
     the 8 waves)."""
-    monkeypatch.setenv("QG_MX_BN", bn)
+    override("QG_MX_BN", bn)
     layer = Layer(qg.W_MXFP4, n, k, 32, seed=m)
     assert f"tiled BM=256 BN={bn}" in qg.describe_dispatch(layer.w, m)
     _check(layer, Acts(True, m, k, seed=m), m)
@@ -206,8 +215,7 @@ def test_mx_tiled_unaligned_activation_scales(m, n, k):
     acts.xs = view
     y_un = run_gemm(layer, acts, m, qg.O_F32)
     assert torch.equal(y_al, y_un)
-    e = err(y_un, oracle.gemm(acts.xdq, layer.wdq()))
-    assert e <= tol_f32(True), e
+    check_mx_f32(layer, acts, m, y_un)
 
 
 def test_mx_tiled_identity_rows_exact():
@@ -229,13 +237,13 @@ def test_mx_tiled_identity_rows_exact():
 @pytest.mark.parametrize("tile", ["256x128", "128x128", "128x256"])
 @pytest.mark.parametrize("wtype", A16)
 @pytest.mark.parametrize("group", [32, 64, 128])
-def test_a16_tiled_formats_and_groups(monkeypatch, tile, wtype, group):
+def test_a16_tiled_formats_and_groups(override, tile, wtype, group):
     """Every integer format and group size through the tiled kernel at each
     tile shape, with a partial row tile and a partial column tile (N = 200 is
     not a multiple of the 128- or 256-column tile)."""
     bm, bn = tile.split("x")
-    monkeypatch.setenv("QG_TILED_BM", bm)
-    monkeypatch.setenv("QG_A16_BN", bn)
+    override("QG_TILED_BM", bm)
+    override("QG_A16_BN", bn)
     layer = Layer(wtype, 200, 640, group, seed=wtype * 10 + group)
     m = 300
     assert f"a16_tiled BM={bm} BN={bn}" in qg.describe_dispatch(layer.w, m)
@@ -244,8 +252,8 @@ def test_a16_tiled_formats_and_groups(monkeypatch, tile, wtype, group):
 
 @pytest.mark.parametrize("bn", ["128", "256"])
 @pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (512, 72, 128), (777, 1040, 4096)])
-def test_a16_tiled_ragged(monkeypatch, m, n, k, bn):
-    monkeypatch.setenv("QG_A16_BN", bn)
+def test_a16_tiled_ragged(override, m, n, k, bn):
+    override("QG_A16_BN", bn)
     layer = Layer(qg.W_UINT4, n, k, 128, seed=m)
     assert f"a16_tiled BM={256 if bn == '128' else 128} BN={bn}" in qg.describe_dispatch(layer.w, m)
     _check(layer, Acts(False, m, k, seed=m), m)
@@ -294,23 +302,23 @@ DECODE_VARIANTS = {128: ["4,2", "2,4", "1,4", "1,8", "2,8", "1,4,2", "1,4,3", "1
 
 @pytest.mark.parametrize("wtype", A16)
 @pytest.mark.parametrize("group", [32, 64, 128])
-def test_decode_kernel_variants(monkeypatch, wtype, group):
+def test_decode_kernel_variants(override, wtype, group):
     """Every compiled (T, KR) of the decode kernel, with and without a K
     split; N = 200 leaves a partial n-tile block, K = 1536 (12 blocks) a
     partial last wave for KR = 8 and a short last split."""
     layer = Layer(wtype, 200, 1536, group, seed=wtype * 10 + group + 1)
     for tune in DECODE_VARIANTS[group]:
-        monkeypatch.setenv("QG_DECODE", tune)
+        override("QG_DECODE", tune)
         for m in (1, 3, 16):
             assert "a16_decode" in qg.describe_dispatch(layer.w, m), (tune, m)
             print(f"  decode {tune} m={m}", flush=True)
             _check(layer, Acts(False, m, 1536, seed=m + group), m)
 
 
-def test_decode_split_k_reuses_workspace(monkeypatch):
+def test_decode_split_k_reuses_workspace(override):
     """Split-K decode: the per-tile arrival counters return to zero, so one
     workspace (zero-filled once) serves consecutive calls."""
-    monkeypatch.setenv("QG_DECODE", "1,4,2")
+    override("QG_DECODE", "1,4,2")
     n, k = 200, 2048
     layer = Layer(qg.W_UINT4, n, k, 128, seed=77)
     m = 1
@@ -326,13 +334,13 @@ def test_decode_split_k_reuses_workspace(monkeypatch):
         torch.cuda.synchronize()
         e = err(y, oracle.gemm(acts.xdq, wdq))
         print(f"  call {call} err={e:.3e}", flush=True)
-        assert e <= tol_f32(False), (call, e)
+        assert e <= TOL_F32, (call, e)
 
 
 @pytest.mark.parametrize("group", [32, 128])
 @pytest.mark.parametrize("wtype", A16)
-def test_decode_kernel_identity_rows_exact(monkeypatch, wtype, group):
-    monkeypatch.setenv("QG_DECODE", "1,8")  # 16 rows: past the default row limit
+def test_decode_kernel_identity_rows_exact(override, wtype, group):
+    override("QG_DECODE", "1,8")  # 16 rows: past the default row limit
     n, k = 72, 1024
     layer = Layer(wtype, n, k, group, seed=31)
     wdq = layer.wdq()
@@ -346,3 +354,108 @@ def test_decode_kernel_identity_rows_exact(monkeypatch, wtype, group):
     y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
     for i, kk in enumerate(ks):
         assert np.array_equal(y[i].astype(np.float64), wdq[:, kk]), kk
+
+
+# ---------------------------------------------------------------------------
+# one workspace shared by calls of different kernels, layers and M
+# ---------------------------------------------------------------------------
+
+def _gemm_ws(layer, acts, m, ws, otype=qg.O_F32):
+    need = qg.gemm_workspace_size(layer.w, m)
+    assert need <= ws.numel(), (need, ws.numel())
+    y = torch.empty((m, layer.n), dtype=torch.float32 if otype == qg.O_F32 else torch.bfloat16, device="cuda")
+    qg.gemm(layer.w, acts.x, acts.xs, m, layer.k, y, otype, layer.n, ws, ws.numel())
+    torch.cuda.synchronize()
+    return y
+
+
+def test_workspace_shared_by_prefill_and_split_decode():
+    """The headline layer (UINT4 + zero points, g128, N = 4096, K = 14336):
+    M = 4096 runs the tiled kernel (group row sums written to the workspace's
+    scratch), then M = 1 runs the split-K decode kernel on the same workspace
+    (its arrival counters sit in the workspace's counter prefix), then both
+    once more.  Every result against the oracle; the counters end at zero."""
+    n, k = 4096, 14336
+    layer = Layer(qg.W_UINT4, n, k, 128, seed=81)
+    assert "a16_tiled" in qg.describe_dispatch(layer.w, 4096)
+    assert "splits=2" in qg.describe_dispatch(layer.w, 1), qg.describe_dispatch(layer.w, 1)
+    ws = torch.zeros(max(qg.gemm_workspace_size(layer.w, 4096), qg.gemm_workspace_size(layer.w, 1)),
+                     dtype=torch.uint8, device="cuda")
+    big = Acts(False, 4096, k, seed=82)
+    rows = np.array([0, 1, 777, 2048, 4095])
+    ref_big = oracle.gemm(big.xdq[rows], layer.wdq())
+    for rnd in range(2):
+        y = _gemm_ws(layer, big, 4096, ws)
+        e = oracle.normwise_error(y[rows].cpu().numpy().astype(np.float64), ref_big)
+        print(f"  round {rnd} M=4096 err={e:.3e}", flush=True)
+        assert e <= TOL_F32
+        for seed in (83, 84):
+            small = Acts(False, 1, k, seed=seed + rnd)
+            y = _gemm_ws(layer, small, 1, ws)
+            e = err(y, oracle.gemm(small.xdq, layer.wdq()))
+            print(f"  round {rnd} M=1 err={e:.3e}", flush=True)
+            assert e <= TOL_F32
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
+def test_workspace_shared_by_mx_tiled_scratch_and_split_skinny():
+    """An MX layer with K % 512 != 0: the tiled kernel (M = 256) first regroups
+    the activation scales by K step into the workspace's scratch; the skinny
+    kernel at M = 1 then splits K across workgroups on the same workspace, and
+    another layer's split call follows."""
+    k = 8320  # 65 K steps of 128
+    a = Layer(qg.W_MXFP4, 512, k, 32, seed=85)
+    b = Layer(qg.W_MXFP4, 1040, k, 32, seed=86)
+    assert "mx_tiled" in qg.describe_dispatch(a.w, 256)
+    for L in (a, b):
+        assert int(qg.describe_dispatch(L.w, 1).split("splits=")[1]) > 1, qg.describe_dispatch(L.w, 1)
+    need = max(qg.gemm_workspace_size(L.w, m) for L in (a, b) for m in (1, 256))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rnd in range(2):
+        for L, m in ((a, 256), (a, 1), (b, 1), (b, 256), (a, 1)):
+            acts = Acts(True, m, k, seed=87 + m + rnd)
+            y = _gemm_ws(L, acts, m, ws)
+            print(f"  N={L.n} M={m} err={err(y, oracle.gemm(acts.xdq, L.wdq())):.3e}", flush=True)
+            check_mx_f32(L, acts, m, y)
+    assert int(ws[:65536].view(torch.int32).abs().sum()) == 0
+
+
+def test_skinny_loops_over_long_k(override):
+    """K beyond one pass of the workgroup (W * KR * splits < K blocks): the
+    workgroups loop over K.  Integer and MX formats, dense."""
+    for wtype, g, mx in ((qg.W_UINT4, 128, False), (qg.W_INT3, 64, False), (qg.W_MXFP4, 32, True)):
+        layer = Layer(wtype, 80, 5120, g, seed=88)
+        override("QG_TUNE", "2,2,4,1")  # 8 of 40 K blocks per pass: five passes
+        m = 19
+        assert "W=4 splits=1" in qg.describe_dispatch(layer.w, m)
+        _check(layer, Acts(mx, m, 5120, seed=89), m)
+
+
+@pytest.mark.parametrize("mnk", [(21, 200, 1024), (64, 512, 1024)])
+@pytest.mark.parametrize("atype", ["mxfp8", "mxfp4"])
+def test_mx_skinny_every_variant(override, atype, mnk):
+    """Every compiled (T, KR) of the MX skinny kernel, with one wave per
+    block up to 8 waves and a cross-workgroup split, for MXFP8 and MXFP4
+    (widened in registers) activations."""
+    from test_gpu_w4a4 import A4, check_a4
+    m, n, k = mnk
+    a4 = atype == "mxfp4"
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=90, atype=qg.A_MXFP4 if a4 else None)
+    acts = A4(m, k, seed=91) if a4 else Acts(True, m, k, seed=91)
+    bad = []
+    for T in (1, 2, 4):
+        for KR in (1, 2, 4):
+            if T * KR > 8 or (T, KR) == (4, 4):
+                continue
+            for W, S in ((8 // KR, 1), (max(1, 4 // KR), 2), (1, 8 // KR)):
+                tune = f"{T},{KR},{W},{S}"
+                override("QG_TUNE", tune)
+                print(f"  {atype} {tune}: {qg.describe_dispatch(layer.w, m)}", flush=True)
+                try:
+                    if a4:
+                        check_a4(layer, acts, m)
+                    else:
+                        _check(layer, acts, m)
+                except AssertionError as e:
+                    bad.append((tune, str(e)[:120]))
+    assert not bad, bad

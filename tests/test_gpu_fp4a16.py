@@ -12,7 +12,7 @@ import torch
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import TOL_BF16, TOL_F32, Acts, require_gpu, to_dev
+from gpu_harness import TOL_BF16, TOL_F32, Acts, assert_bf16_is_rne, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -57,9 +57,11 @@ def test_fp4_bf16_dense(m, n, k):
               "a16_decode" if m <= 8 and k % 512 == 0 else "a16_skinny")
     assert expect in qg.describe_dispatch(layer.w, m)
     yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {}
     for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
-        e = oracle.normwise_error(run(layer, acts.x, m, otype), yref)
+        e = oracle.normwise_error(ys.setdefault(otype, run(layer, acts.x, m, otype)), yref)
         assert e <= tol, (otype, e)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
 
 
 def test_fp4_bf16_identity_rows_exact():
@@ -82,13 +84,13 @@ def test_fp4_bf16_identity_rows_exact():
                                    (256, {"QG_MOE_TILED_MIN": "0"}),
                                    (256, {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1"}),
                                    (256, {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1", "QG_MOE_SMALL_BM": "32"})])
-def test_fp4_bf16_moe(monkeypatch, t, env):
+def test_fp4_bf16_moe(override, t, env):
     """Grouped MXFP4 x bf16: few tokens (skinny kernel), a skewed batch whose
     large experts take the 128-row tiled kernel and the rest the 64-row small
     tiles, every expert on 128-row tiles, none on tiles, and every expert on
     64- or 32-row small tiles."""
     for key, val in env.items():
-        monkeypatch.setenv(key, val)
+        override(key, val)
     experts, topk, n, k = 8, 2, 256, 512
     layer = Fp4Layer(n, k, seed=7, experts=experts)
     r = synth.rng(8, 0)
@@ -110,20 +112,22 @@ def test_fp4_bf16_moe(monkeypatch, t, env):
 
 
 @pytest.mark.parametrize("tile", ["128x256", "256x128", "128x128"])
-def test_fp4_bf16_tiled_shapes(monkeypatch, tile):
+def test_fp4_bf16_tiled_shapes(override, tile):
     """The LDS-tiled kernel (M >= 256) at each dense tile shape, with partial
     row and column tiles."""
     bm, bn = tile.split("x")
-    monkeypatch.setenv("QG_TILED_BM", bm)
-    monkeypatch.setenv("QG_A16_BN", bn)
+    override("QG_TILED_BM", bm)
+    override("QG_A16_BN", bn)
     m, n, k = 300, 200, 640
     layer = Fp4Layer(n, k, seed=11)
     assert f"a16_tiled BM={bm} BN={bn}" in qg.describe_dispatch(layer.w, m)
     acts = Acts(False, m, k, seed=12)
     yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {}
     for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32)):
-        e = oracle.normwise_error(run(layer, acts.x, m, otype), yref)
+        e = oracle.normwise_error(ys.setdefault(otype, run(layer, acts.x, m, otype)), yref)
         assert e <= tol, (otype, e)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
 
 
 def test_fp4_bf16_tiled_identity_rows_exact():
@@ -160,10 +164,10 @@ def test_fp4_bf16_batch_invariant_rows():
 
 
 @pytest.mark.parametrize("decode", ["1,8", "1,4", "1,8,2"])
-def test_fp4_bf16_decode_identity_rows_exact(monkeypatch, decode):
+def test_fp4_bf16_decode_identity_rows_exact(override, decode):
     """One-hot rows through the decode kernel (activations in LDS; with and
     without a K split) return the dequantized weights bit for bit."""
-    monkeypatch.setenv("QG_DECODE", decode)
+    override("QG_DECODE", decode)
     n, k, m = 72, 2048, 8
     layer = Fp4Layer(n, k, seed=17)
     assert "a16_decode" in qg.describe_dispatch(layer.w, m)

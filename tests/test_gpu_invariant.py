@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import quantized_gemm_qg_amd as qg
-from gpu_harness import TOL_BF16, Acts, Layer, require_gpu, tol_f32
+from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, assert_mx_f32, mx_codes, require_gpu
 
 pytestmark = pytest.mark.gpu
 INV = qg.GEMM_BATCH_INVARIANT
@@ -42,9 +42,13 @@ def test_rows_do_not_depend_on_m(wtype, k, g):
     for otype in (qg.O_F32, qg.O_BF16):
         full = run(layer, acts, list(range(mfull)), otype, INV)
         yref = oracle.gemm(acts.xdq, layer.wdq())
-        tol = tol_f32(layer.mx) if otype == qg.O_F32 else TOL_BF16
         e = oracle.normwise_error(full.float().cpu().numpy().astype(np.float64), yref)
-        assert e <= tol, e
+        if otype == qg.O_F32 and layer.mx:
+            wc, wsc = mx_codes(layer)
+            assert_mx_f32(full, acts.codes, acts.scales, wc, wsc, "e4m3", [qg.describe_dispatch(layer.w, mfull, INV)],
+                          what="batch-invariant")
+        else:
+            assert e <= (TOL_F32 if otype == qg.O_F32 else TOL_BF16), e
         fb = full.view(torch.int32 if otype == qg.O_F32 else torch.int16).cpu()
         r = np.random.default_rng(33)
         for m in (1, 3, 16, 17, 64, 129, 255, 256):

@@ -8,7 +8,7 @@ import torch
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import TOL_BF16, Acts, Layer, require_gpu, to_dev, tol_f32
+from gpu_harness import TOL_BF16, TOL_F32, Acts, Layer, assert_bf16_is_rne, check_moe_mx_f32, require_gpu, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,18 @@ def run_moe(layer, acts, sorted_ids, offsets, t, topk, x_rows, y_rows, otype):
     return y.float().cpu().numpy().astype(np.float64)
 
 
+def check_f32(layer, acts, ids, y, ref, x_rows, y_rows, sorted_ids=None):
+    """An fp32 grouped-GEMM output: integer formats within TOL_F32 of the
+    oracle (normwise); MX layers bit for bit against the block-scaled MFMA
+    model, expert by expert (the normwise error is printed)."""
+    e = oracle.normwise_error(y, ref)
+    print(f"  fp32 normwise err {e:.3e}", flush=True)
+    if layer.mx:
+        check_moe_mx_f32(layer, acts.codes, acts.scales, "e4m3", ids, y, x_rows, y_rows, sorted_ids)
+    else:
+        assert e <= TOL_F32, e
+
+
 def moe_reference(layer, xdq, ids, by_token, verbose=False):
     def wdq(e):
         if verbose:
@@ -74,13 +86,13 @@ SPLITS = {
 
 @pytest.mark.parametrize("split", list(SPLITS))
 @pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_INT3, qg.W_UINT3, qg.W_MXFP4])
-def test_moe_small_all_row_modes(monkeypatch, wtype, split):
+def test_moe_small_all_row_modes(override, wtype, split):
     """All row modes, with the experts split between the kernels by row count
     (128-row tiles, 64-row small tiles, the skinny kernel)."""
     if wtype == qg.W_MXFP4 and split in ("tiled_bn128", "small32"):
         pytest.skip("same dispatch as another split for MXFP4")
     for var, val in SPLITS[split].items():
-        monkeypatch.setenv(var, val)
+        override(var, val)
     t, e, topk, n, k = 37, 16, 4, 80, 640
     g = 32 if wtype == qg.W_MXFP4 else 128
     ids = synth.route(synth.rng(1, wtype), t, e, topk)
@@ -91,15 +103,18 @@ def test_moe_small_all_row_modes(monkeypatch, wtype, split):
     # gate/up style: rows by token
     acts = Acts(mx, t, k, seed=3)
     ref = moe_reference(layer, acts.xdq, ids, True)
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(mx))):
-        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
-        assert oracle.normwise_error(y, ref) <= tol
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        ys[otype] = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+    assert oracle.normwise_error(ys[qg.O_BF16], ref) <= TOL_BF16
+    check_f32(layer, acts, ids, ys[qg.O_F32], ref, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
     # down style: rows by pair, output in sorted order
     h = Acts(mx, t * topk, k, seed=4)
     ref_pair = moe_reference(layer, h.xdq, ids, False)
     y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
     s = sorted_ids.cpu().numpy()
-    assert oracle.normwise_error(y, ref_pair[s]) <= tol_f32(mx)
+    check_f32(layer, h, ids, y, ref_pair[s], qg.ROWS_BY_PAIR, qg.ROWS_SORTED, sorted_ids)
     # sorted input rows
     hs = Acts(mx, t * topk, k, seed=4)
     y = run_moe(layer, hs, sorted_ids, offsets, t, topk, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, qg.O_F32)
@@ -107,7 +122,7 @@ def test_moe_small_all_row_modes(monkeypatch, wtype, split):
     inv = np.empty_like(s)
     inv[s] = np.arange(s.size)
     ref2 = np.stack([hs.xdq[inv[p]] @ layer.wdq(int(ids.reshape(-1)[p])).T for p in range(t * topk)])
-    assert oracle.normwise_error(y, ref2) <= tol_f32(mx)
+    check_f32(layer, hs, ids, y, ref2, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, sorted_ids)
 
 
 def test_moe_empty_and_single_row_experts():
@@ -119,7 +134,7 @@ def test_moe_empty_and_single_row_experts():
     check_sort(ids, e, sorted_ids, offsets)
     acts = Acts(False, t, k, seed=7)
     y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, qg.O_F32)
-    assert oracle.normwise_error(y, moe_reference(layer, acts.xdq, ids, True)) <= tol_f32(False)
+    assert oracle.normwise_error(y, moe_reference(layer, acts.xdq, ids, True)) <= TOL_F32
 
 
 def test_moe_sort_zero_tokens_and_out_of_range_ids():
@@ -132,6 +147,14 @@ def test_moe_sort_zero_tokens_and_out_of_range_ids():
     offs = offsets.cpu().numpy()
     assert offs.tolist() == [0, 1, 1, 2, 2]
     assert sorted(sorted_ids.cpu().numpy()[:2].tolist()) == [0, 3]
+
+
+def _expert_sample(ids, n=8):
+    """The most and the least loaded experts and some in between."""
+    counts = np.bincount(np.asarray(ids).ravel())
+    act = np.nonzero(counts)[0]
+    order = act[np.argsort(-counts[act], kind="stable")]
+    return np.unique(np.concatenate([order[:3], order[-3:], order[np.linspace(0, order.size - 1, n - 6).astype(int)]]))
 
 
 def _moe_full(wtype, experts, topk, n1, k1, n2, k2, tokens, seed):
@@ -147,24 +170,38 @@ def _moe_full(wtype, experts, topk, n1, k1, n2, k2, tokens, seed):
     sorted_ids, offsets = sort_on_gpu(ids, experts, up)
     check_sort(ids, experts, sorted_ids, offsets)
     x = Acts(mx, tokens, k1, seed=seed + 1)
-    y = run_moe(up, x, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, qg.O_BF16)
-    e1 = oracle.normwise_error(y, moe_reference(up, x.xdq, ids, True, verbose=True))
+    ref = moe_reference(up, x.xdq, ids, True, verbose=True)
+    ys = {o: run_moe(up, x, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, o)
+          for o in (qg.O_BF16, qg.O_F32)}
+    e1 = [oracle.normwise_error(ys[o], ref) for o in (qg.O_BF16, qg.O_F32)]
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    if mx:
+        check_moe_mx_f32(up, x.codes, x.scales, "e4m3", ids, ys[qg.O_F32], qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR,
+                         experts=_expert_sample(ids))
     up.drop_wdq()
-    del up
+    del up, ref
     down = Layer(wtype, n2, k2, g, seed=seed + 7, experts=experts, active=active)
     print("  down weights ready", flush=True)
     h = Acts(mx, tokens * topk, k2, seed=seed + 2)
-    y = run_moe(down, h, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR, qg.O_BF16)
-    e2 = oracle.normwise_error(y, moe_reference(down, h.xdq, ids, False, verbose=True))
-    print(f"  gate_up err={e1:.3e} down err={e2:.3e}", flush=True)
-    assert e1 <= TOL_BF16 and e2 <= TOL_BF16
+    ref = moe_reference(down, h.xdq, ids, False, verbose=True)
+    ys = {o: run_moe(down, h, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR, o)
+          for o in (qg.O_BF16, qg.O_F32)}
+    e2 = [oracle.normwise_error(ys[o], ref) for o in (qg.O_BF16, qg.O_F32)]
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    if mx:
+        check_moe_mx_f32(down, h.codes, h.scales, "e4m3", ids, ys[qg.O_F32], qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR,
+                         experts=_expert_sample(ids))
+    print(f"  gate_up err bf16/fp32={e1[0]:.3e}/{e1[1]:.3e} down err={e2[0]:.3e}/{e2[1]:.3e}", flush=True)
+    assert e1[0] <= TOL_BF16 and e2[0] <= TOL_BF16
+    if not mx:
+        assert e1[1] <= TOL_F32 and e2[1] <= TOL_F32
 
 
 def test_moe_w4a16_256_experts_t64():
     _moe_full(qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, 64, seed=40)
 
 
-@pytest.mark.parametrize("tokens", [1, 64])
+@pytest.mark.parametrize("tokens", [1, 64, 512])
 def test_moe_w4a8_128_experts_padding_shape(tokens):
     _moe_full(qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens, seed=50)
 
@@ -185,13 +222,17 @@ def test_moe_tiled_multi_tile_experts(wtype):
     sorted_ids, offsets = sort_on_gpu(ids, e, layer)
     acts = Acts(mx, t, k, seed=10)
     ref = moe_reference(layer, acts.xdq, ids, True)
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, tol_f32(mx))):
-        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
-        assert oracle.normwise_error(y, ref) <= tol
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        ys[otype] = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+    assert oracle.normwise_error(ys[qg.O_BF16], ref) <= TOL_BF16
+    check_f32(layer, acts, ids, ys[qg.O_F32], ref, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
     h = Acts(mx, t * topk, k, seed=11)
     y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
     s = sorted_ids.cpu().numpy()
-    assert oracle.normwise_error(y, moe_reference(layer, h.xdq, ids, False)[s]) <= tol_f32(mx)
+    check_f32(layer, h, ids, y, moe_reference(layer, h.xdq, ids, False)[s], qg.ROWS_BY_PAIR, qg.ROWS_SORTED,
+              sorted_ids)
 
 
 def _moe_sampled(wtype, experts, topk, n, k, tokens, seed, by_token, n_experts_checked=12, atype=None,
@@ -239,3 +280,32 @@ def test_moe_w4a16_256_experts_t4096_down_sampled():
 @pytest.mark.parametrize("nk,by_token", [((1280, 4096), True), ((4096, 640), False)])
 def test_moe_w4a8_128_experts_t4096_sampled(nk, by_token):
     _moe_sampled(qg.W_MXFP4, 128, 8, nk[0], nk[1], 4096, seed=62, by_token=by_token)
+
+
+@pytest.mark.parametrize("tokens,topk", [(4, 4), (64, 4), (4096, 2)])
+@pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_MXFP4])
+def test_moe_long_k(tokens, topk, wtype):
+    """K = 14336 (a down projection of a 14336-wide expert): few tokens run the
+    skinny kernel, whose workgroups then loop over K; 64 tokens the small
+    tiles; 4096 tokens the 128-row tiles and the small tiles.  Every pair
+    against the oracle, bf16 and fp32 outputs."""
+    experts, n, k = 32, 256, 14336
+    g = 32 if wtype == qg.W_MXFP4 else 128
+    mx = wtype == qg.W_MXFP4
+    ids = synth.route(synth.rng(70, tokens), tokens, experts, topk)
+    layer = Layer(wtype, n, k, g, seed=71, experts=experts, active=np.unique(ids))
+    print(f"  T={tokens} dispatch {qg.describe_dispatch(layer.w, tokens * topk)}", flush=True)
+    sorted_ids, offsets = sort_on_gpu(ids, experts, layer)
+    h = Acts(mx, tokens * topk, k, seed=72)
+    ref = moe_reference(layer, h.xdq, ids, False)
+    ys = {o: run_moe(layer, h, sorted_ids, offsets, tokens, topk, qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR, o)
+          for o in (qg.O_BF16, qg.O_F32)}
+    e = [oracle.normwise_error(ys[o], ref) for o in (qg.O_BF16, qg.O_F32)]
+    print(f"  err bf16 {e[0]:.3e} fp32 {e[1]:.3e}", flush=True)
+    assert e[0] <= TOL_BF16
+    if mx:
+        check_moe_mx_f32(layer, h.codes, h.scales, "e4m3", ids, ys[qg.O_F32], qg.ROWS_BY_PAIR, qg.ROWS_BY_PAIR,
+                         experts=_expert_sample(ids))
+    else:
+        assert e[1] <= TOL_F32
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])

@@ -11,8 +11,8 @@ C ABI, against the CPU oracle.
   kernel on e2m1 operands;
   ragged N, K % 512 != 0 (scales regrouped by K step) and
   == 0 (scale ring), padded rows, unaligned scales; bf16 output within
-  TOL_BF16 and fp32 within the scaled MFMA's bound (TOL_F32_MX) of the
-  float64 product of the exact operands.
+  TOL_BF16 of the float64 product of the exact operands, fp32 output bit
+  for bit equal to the block-scaled MFMA model (tests/mx_mfma_model.py).
 * Batch invariance, the autotuner's choice, and the quantize -> GEMM chain.
 * W4A4 MoE (W4A8's dispatch on e2m1 rows: the tiled kernel's e2m1 form,
   its 64-row small tiles, the skinny kernel's in-register widening) in every
@@ -25,7 +25,7 @@ import torch
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import TOL_BF16, TOL_F32_MX, Layer, require_gpu, to_dev
+from gpu_harness import TOL_BF16, Layer, assert_bf16_is_rne, check_moe_mx_f32, check_mx_f32, require_gpu, to_dev
 from oracle import formats as F
 from oracle import quantize as Q
 
@@ -105,6 +105,7 @@ class A4:
     def __init__(self, m, k, seed, ldx=None):
         r = synth.rng(seed, 44)
         codes, self.scales = synth.mx_quantize(r.normal(0.0, 1.0, size=(m, k)), "e2m1")
+        self.codes, self.a4 = codes, True
         self.xdq = Q.dequantize_mxfp4(codes, self.scales)
         ldx = ldx or k
         packed = np.zeros((m, ldx // 2), dtype=np.uint8)
@@ -127,14 +128,21 @@ def run_a4(layer, acts, m, otype, flags=0):
     return y
 
 
-def check_a4(layer, acts, m):
+def check_a4(layer, acts, m, flags=0):
+    """bf16 output against the oracle (normwise), fp32 output bit for bit
+    against the block-scaled MFMA model, bf16 == RNE(fp32)."""
     yref = oracle.gemm(acts.xdq, layer.wdq())
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
-        y = run_a4(layer, acts, m, otype)
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        y = ys[otype] = run_a4(layer, acts, m, otype, flags)
         e = oracle.normwise_error(y.float().cpu().numpy().astype(np.float64), yref)
         print(f"  m={m} n={layer.n} k={layer.k} otype={otype} err={e:.3e}", flush=True)
-        assert e <= tol, (otype, e)
         assert torch.isfinite(y.float()).all()
+        if otype == qg.O_BF16:
+            assert e <= TOL_BF16, (otype, e)
+        elif not flags:
+            check_mx_f32(layer, acts, m, y)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 256, 512), (7, 136, 384), (33, 300, 1024), (127, 512, 2048),
@@ -164,7 +172,7 @@ def test_w4a4_skinny_padded_rows_repeat_calls():
         torch.cuda.synchronize()
         e = oracle.normwise_error(y.cpu().numpy().astype(np.float64), oracle.gemm(acts.xdq, layer.wdq()))
         print(f"  m={m} err={e:.3e}", flush=True)
-        assert e <= TOL_F32_MX
+        check_mx_f32(layer, acts, m, y)
 
 
 @pytest.mark.parametrize("m,k", [(300, 128), (300, 256), (130, 384), (257, 896)])
@@ -253,31 +261,31 @@ def _moe_a4_layer(n, k, experts, seed):
 
 
 @pytest.mark.parametrize("split", ["skinny", "tiled", "tiled_4waves", "mixed", "mixed_skinny", "small"])
-def test_w4a4_moe_all_row_modes(monkeypatch, split):
+def test_w4a4_moe_all_row_modes(override, split):
     from test_gpu_moe import SPLITS, moe_reference, run_moe, sort_on_gpu
     env = dict(SPLITS["tiled"], QG_MX_WAVES="4") if split == "tiled_4waves" else SPLITS[split]
     for var, val in env.items():
-        monkeypatch.setenv(var, val)
+        override(var, val)
     t, e, topk, n, k = 37, 16, 4, 80, 640
     ids = synth.route(synth.rng(60, 0), t, e, topk)
     layer = _moe_a4_layer(n, k, e, seed=61)
     sorted_ids, offsets = sort_on_gpu(ids, e, layer)
     acts = A4(t, k, seed=62)
     ref = moe_reference(layer, acts.xdq, ids, True)
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
-        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        y = ys[otype] = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
         err = oracle.normwise_error(y, ref)
         print(f"  {split} by-token otype={otype} err={err:.3e}", flush=True)
-        assert err <= tol
+        if otype == qg.O_BF16:
+            assert err <= TOL_BF16
+    check_moe_mx_f32(layer, acts.codes, acts.scales, "e2m1", ids, ys[qg.O_F32], qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
     h = A4(t * topk, k, seed=63)
     y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, qg.O_F32)
-    s = sorted_ids.cpu().numpy()
-    assert oracle.normwise_error(y, moe_reference(layer, h.xdq, ids, False)[s]) <= TOL_F32_MX
+    check_moe_mx_f32(layer, h.codes, h.scales, "e2m1", ids, y, qg.ROWS_BY_PAIR, qg.ROWS_SORTED, sorted_ids)
     y = run_moe(layer, h, sorted_ids, offsets, t, topk, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, qg.O_F32)
-    inv = np.empty_like(s)
-    inv[s] = np.arange(s.size)
-    ref2 = np.stack([h.xdq[inv[p]] @ layer.wdq(int(ids.reshape(-1)[p])).T for p in range(t * topk)])
-    assert oracle.normwise_error(y, ref2) <= TOL_F32_MX
+    check_moe_mx_f32(layer, h.codes, h.scales, "e2m1", ids, y, qg.ROWS_SORTED, qg.ROWS_BY_PAIR, sorted_ids)
 
 
 def test_w4a4_moe_multi_tile_experts():
@@ -290,11 +298,15 @@ def test_w4a4_moe_multi_tile_experts():
     sorted_ids, offsets = sort_on_gpu(ids, e, layer)
     acts = A4(t, k, seed=66)
     ref = moe_reference(layer, acts.xdq, ids, True)
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
-        y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        y = ys[otype] = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, otype)
         err = oracle.normwise_error(y, ref)
         print(f"  multi-tile otype={otype} err={err:.3e}", flush=True)
-        assert err <= tol
+        if otype == qg.O_BF16:
+            assert err <= TOL_BF16
+    check_moe_mx_f32(layer, acts.codes, acts.scales, "e2m1", ids, ys[qg.O_F32], qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR)
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
 
 
 @pytest.mark.parametrize("nk", [(3072, 4096), (14336, 4096)])
@@ -311,23 +323,28 @@ def test_w4a4_full_size_sampled_rows(nk):
     rows = np.sort(synth.rng(0, 98).choice(m, 96, replace=False))
     rows[0], rows[-1] = 0, m - 1
     yref = oracle.gemm(acts.xdq[rows], layer.wdq())
-    for otype, tol in ((qg.O_BF16, TOL_BF16), (qg.O_F32, TOL_F32_MX)):
-        y = run_a4(layer, acts, m, otype)
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        y = ys[otype] = run_a4(layer, acts, m, otype)
         e = oracle.normwise_error(y[rows].float().cpu().numpy().astype(np.float64), yref)
         print(f"  otype={otype} err={e:.3e}", flush=True)
-        assert e <= tol
         assert torch.isfinite(y.float()).all()
+        if otype == qg.O_BF16:
+            assert e <= TOL_BF16
+        else:
+            check_mx_f32(layer, acts, m, y, rows=rows[:48])
+    assert_bf16_is_rne(ys[qg.O_BF16][rows], ys[qg.O_F32][rows])
 
 
 @pytest.mark.parametrize("env", [{"QG_MX_BN": "256"}, {"QG_MX_BN": "224"}, {"QG_MX_BN": "192"},
                                  {"QG_MX_WAVES": "4"}], ids=lambda e: "-".join(f"{k}={v}" for k, v in e.items()))
 @pytest.mark.parametrize("m,n,k", [(256, 128, 1024), (300, 200, 640), (777, 1040, 4096)])
-def test_w4a4_tiled_ragged_every_shape(monkeypatch, env, m, n, k):
+def test_w4a4_tiled_ragged_every_shape(override, env, m, n, k):
     """Every compiled form of the e2m1-operand tiled kernel (256-, 224- and
     192-column tiles with 8 waves; 256 with 4) on partial row and column
     tiles."""
     for var, val in env.items():
-        monkeypatch.setenv(var, val)
+        override(var, val)
     layer = a4_layer(n, k, seed=m + 1)
     bn = env.get("QG_MX_BN", "256")
     assert f"mx_tiled BM=256 BN={bn}" == qg.describe_dispatch(layer.w, m)

@@ -224,5 +224,14 @@ def test_round_bf16_and_normwise_error():
     got = oracle.round_bf16(y)
     lib = torch.from_numpy(y.astype(np.float32)).to(torch.bfloat16).double().numpy()
     assert np.array_equal(got, lib)
+    # binary32 subnormals and the normal/subnormal boundary, every tie case
+    bits = np.concatenate([r.integers(1, 0x00800000, 3000, dtype=np.uint32),
+                           r.integers(0x00700000, 0x00900000, 2000, dtype=np.uint32),
+                           np.arange(0x00007FF0, 0x00008010, dtype=np.uint32)])
+    bits = np.concatenate([bits, bits | 0x80000000])
+    ys = bits.view(np.float32)
+    got = oracle.round_bf16(ys.astype(np.float64))
+    lib = torch.from_numpy(ys.copy()).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, lib)
     assert oracle.normwise_error(np.array([1.0, 2.0]), np.array([1.0, 2.5])) == pytest.approx(0.2)
     assert oracle.normwise_error(np.zeros(3), np.zeros(3)) == 0.0
