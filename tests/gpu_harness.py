@@ -149,15 +149,20 @@ def assert_mx_f32(y, a_codes, a_scales, w_codes, w_scales, afmt, dispatches, row
     r_idx = np.asarray(rows) if rows is not None else _sample(yv.shape[0], max_rows, 1)
     c_idx = _sample(yv.shape[1], max_cols, 2)
     got = yv[np.ix_(r_idx, c_idx)]
+    report = []
     for disp in dispatches:
         pred = MM.predict(a_codes[r_idx], a_scales[r_idx], w_codes[c_idx], w_scales[c_idx], afmt, disp)
-        if np.array_equal(pred, got):
-            print(f"  {what} fp32 == block-scaled MFMA model ({disp}) on {got.size} outputs", flush=True)
+        diff = pred != got
+        n_diff = int(diff.sum())
+        # one-ulp differences are allowed in at most 1 of 1000 outputs
+        ulps = np.abs(got[diff].astype(np.float64) - pred[diff]) / np.spacing(np.abs(pred[diff]))
+        if n_diff == 0 or (n_diff <= max(1, got.size // 1000) and np.all(ulps <= 1.0)):
+            print(f"  {what} fp32 == block-scaled MFMA model ({disp}) on {got.size - n_diff} of {got.size} outputs"
+                  + (f", {n_diff} one ulp apart" if n_diff else ""), flush=True)
             return
-    bad = np.argwhere(pred != got)
-    raise AssertionError(f"{what}: {bad.shape[0]} of {got.size} fp32 outputs differ from the model "
-                         f"({dispatches}); first {tuple(bad[0])}: {float(got[tuple(bad[0])]).hex()} vs "
-                         f"{float(pred[tuple(bad[0])]).hex()}")
+        first = tuple(np.argwhere(diff)[0])
+        report.append(f"{disp}: {n_diff} differ, first {first}: {float(got[first]).hex()} vs {float(pred[first]).hex()}")
+    raise AssertionError(f"{what}: fp32 outputs of {got.size} sampled differ from the model: " + "; ".join(report))
 
 
 def moe_mx_forms(layer, pairs):
