@@ -194,6 +194,23 @@ qg_status qg_gemm(const qg_weight *w, const void *x, const void *x_scales, int64
                   hipStream_t stream);
 /* (ws, when needed, must hold zeros on entry; see qg_gemm_workspace_size.) */
 
+/* qg_gemm for callers that cannot allocate memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels, with the workspace replaced by a static device array of
+ * QG_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends.  The call allocates nothing (no hipMalloc / hipFree, no
+ * allocating library call); on its first use on a device it looks the
+ * array's address up and clears its split-K counter prefix with a kernel on
+ * `stream`.  Every call on one GPU shares that GPU's array and the array
+ * keeps the last call's contents: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  A call
+ * whose kernels would need more scratch than the array holds returns
+ * QG_ERR_BUFFER_TOO_SMALL before launching anything (qg_gemm with a caller
+ * workspace serves it).  Arguments and all other errors as in qg_gemm. */
+#define QG_NOALLOC_SCRATCH_BYTES (8u << 20)
+qg_status qg_gemm_noalloc(const qg_weight *w, const void *x, const void *x_scales, int64_t m, int64_t ldx,
+                          void *y, int32_t otype, int64_t ldy, hipStream_t stream);
+
 /* Compute options of qg_gemm_ex (the announcement's "Compute Config" names
  * batch invariance among the compute options of a GEMM, section "Per-workload
  * tuning and JIT compilation").

@@ -30,8 +30,9 @@ EXPORTS = (
     "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
     "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset", "qg_quantize_mxfp4",
-    "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex",
+    "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex", "qg_gemm_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 8 << 20
 GEMM_BATCH_INVARIANT = 1
 
 
@@ -94,6 +95,7 @@ def _load():
         "qg_moe_combine": (I32, [P, I32, I64, P, I64, I32, I64, P, P, I32, I64, P]),
         "qg_gemm_workspace_size_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.POINTER(U64)]),
         "qg_gemm_ex": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, ctypes.c_uint32, P]),
+        "qg_gemm_noalloc": (I32, [W, P, P, I64, I64, P, I32, I64, P]),
         "qg_gemm_autotune_workspace_size": (I32, [W, I64, ctypes.POINTER(U64)]),
         "qg_gemm_autotune": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, P, U64, I32, P, ctypes.c_char_p, U64,
                                    ctypes.POINTER(ctypes.c_float)]),
@@ -210,6 +212,12 @@ def gemm_ex(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, w
     """qg_gemm with compute options (GEMM_BATCH_INVARIANT)."""
     _check(_lib.qg_gemm_ex(ctypes.byref(w), _ptr(x), _ptr(x_scales), m, ldx, _ptr(y), otype, ldy,
                            _ptr(ws), ws_bytes, flags, _stream(stream)), "qg_gemm_ex")
+
+
+def gemm_noalloc(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, stream=None) -> None:
+    """qg_gemm with the library's static device scratch instead of a workspace."""
+    _check(_lib.qg_gemm_noalloc(ctypes.byref(w), _ptr(x), _ptr(x_scales), m, ldx, _ptr(y), otype, ldy,
+                                _stream(stream)), "qg_gemm_noalloc")
 
 
 def gemm(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: int, ws=None,

@@ -819,6 +819,64 @@ extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x
   return hip_status(launch_dense_variant(*w, L, v, x, x_scales, m, ldx, y, otype, ldy, ws, stream));
 }
 
+// ---------------------------------------------------------------------------
+// qg_gemm without a caller workspace: the scratch (split-K counters, partial
+// tiles, the large-M kernels' pre-pass results) is a static device array.
+// Its host-side name is only a stand-in: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[QG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+__global__ void zero_fill_kernel(uint32_t *p, uint64_t words) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The scratch array of the current device: its address on first use there,
+// with the split-K counter prefix cleared on `stream` by a fill kernel (not a
+// memset node, so a first call inside graph capture stays correct).
+static qg_status noalloc_scratch(hipStream_t stream, void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return QG_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!ptr) return QG_ERR_HIP;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(64), dim3(256), 0, stream, (uint32_t *)ptr, kSplitCounterBytes / 4);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QG_OK;
+}
+
+extern "C" qg_status qg_gemm_noalloc(const qg_weight *w, const void *x, const void *x_scales, int64_t m,
+                                     int64_t ldx, void *y, int32_t otype, int64_t ldy, hipStream_t stream) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (m < 0) return QG_ERR_INVALID_ARGUMENT;
+  // the scratch this call needs must fit the static array
+  if (m > 0 && dense_ws_bytes(*w, dense_variant(*w, m, 0), m) > QG_NOALLOC_SCRATCH_BYTES)
+    return QG_ERR_BUFFER_TOO_SMALL;
+  if (m == 0) return qg_gemm_ex(w, x, x_scales, m, ldx, y, otype, ldy, nullptr, 0, 0, stream);
+  void *ws = nullptr;
+  st = noalloc_scratch(stream, &ws);
+  if (st != QG_OK) return st;
+  return qg_gemm_ex(w, x, x_scales, m, ldx, y, otype, ldy, ws, QG_NOALLOC_SCRATCH_BYTES, 0, stream);
+}
+
 // The weight as the MoE dispatch sees it: a W4A4 layer takes W4A8's kernel
 // choices and workspace (the packed layout is the same); its launches then
 // read e2m1 rows (the tiled kernel's A4 form, the skinny kernel's FMT 6).

@@ -550,3 +550,15 @@ def test_overrides_through_the_library():
         qg.clear_overrides()
     assert qg.describe_dispatch(w, 1) == base
 
+
+
+def test_noalloc_validates_before_any_device_call():
+    """qg_gemm_noalloc: m == 0 is a no-op, and a call whose kernels would need
+    more scratch than the static array holds is refused before any device
+    call (host logic only)."""
+    w = _bound(qg.layer_desc(qg.W_INT4, 1024, 14336, 128))
+    qg.gemm_noalloc(w, None, None, 0, 14336, None, qg.O_BF16, 1024, stream=0)
+    assert qg.gemm_workspace_size(w, 32768) > qg.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(qg.QGError) as e:
+        qg.gemm_noalloc(w, FAKE_DEV, None, 32768, 14336, FAKE_DEV, qg.O_BF16, 1024, stream=0)
+    assert e.value.status == qg.QG_ERR_BUFFER_TOO_SMALL
