@@ -260,6 +260,32 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   __builtin_amdgcn_sched_barrier(0);
   after_issue();
   if (kb0 >= kbs) return;  // wave-uniform: a wave entirely past K adds nothing
+  // One row in LDS (ER = 1): the group row sums of the wave's NG groups come
+  // from the LDS copy once, lane l summing values 16 l .. 16 l + 15 of the
+  // wave's K range with dot products against ones, GROUP / 16 lanes per group
+  // combined by butterfly; group i's sum is then read from lane i * GROUP / 16
+  // into a scalar.  (With more rows the MFMA against all-ones gives the sums
+  // of 16 rows at once.)
+  constexpr bool XS_LDS = XL && ER == 1 && !FP4;
+  float xsum_lane = 0.f;
+  if constexpr (XS_LDS) {
+    // the wave's KR blocks are KR * 8 lanes' worth (KR * 128 values)
+    if (KR == 8 || lane < KR * 8) {
+      const u32x4 *xp = (const u32x4 *)(xrow + (kb0 * 128 - xk0) + 16 * lane);
+      const u32x4 v0 = xp[0], v1 = xp[1];
+      const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // (element copied out first: a bit cast of a vector element lvalue
+        // reads element 0)
+        const uint32_t d0 = v0[e], d1 = v1[e];
+        xsum_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d0), one2, xsum_lane, false);
+        xsum_lane = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d1), one2, xsum_lane, false);
+      }
+    }
+#pragma unroll
+    for (int off = 1; off < GROUP / 16; off <<= 1) xsum_lane += __shfl_xor(xsum_lane, off);
+  }
   // scale s and zero point z of group g0 + i -> (MAG * s, -(MAG + z) * s)
   auto group_consts = [&](int t, int i, float &c1, float &c2) {
     const float s = bf16_bits_to_f32((sw[t][i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
@@ -306,11 +332,17 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
     }
 #pragma unroll
     for (int gi = 0; gi < GPB; ++gi) {
-      // 4. group row sums of X on the matrix core (B = all ones)
-      f32x4 xs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xk[j], ones, xs);
       const int i = kb * GPB + gi;
+      // 4. group row sums of X: from the lanes' dot products (one row), or
+      //    on the matrix core (B = all ones)
+      f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (XS_LDS) {
+        xs[0] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, xsum_lane),
+                                                                    i * (GROUP / 16)));
+      } else {
+#pragma unroll
+        for (int j = gi * JPG; j < (gi + 1) * JPG; ++j) xs = mfma_bf16(xk[j], ones, xs);
+      }
       // 5. dequantize + MFMA + per-group scaling
 #pragma unroll
       for (int t = 0; t < T; ++t) {
