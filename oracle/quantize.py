@@ -23,6 +23,15 @@ this module (see ``oracle/__init__.py``); the library never does.
   (a negative value that rounds to zero gives code 0x8).  Codes are returned
   one per element; ``pack_e2m1`` puts two per byte, element 2i in the low
   nibble of byte i.
+* bf16 -> FP8 with fp32 scales (announcement, section "End to end": W4A8
+  serving with per-token FP8 activations; section "W8A8 / W4A8 / W4A4": FP8
+  with block-wise scaling).  The pages name the granularity only, so the rule
+  is the plain one, in fp32 arithmetic: per block (a whole row for per-token
+  scaling, 128 consecutive values of a row for block scaling) with largest
+  magnitude a, the scale is s = fl32(a / 448) (448 = the largest e4m3 value;
+  s = 1 for an all-zero block), and each element is e4m3 of fl32(v / s),
+  nearest with ties to the even code, saturated at 448, sign kept.  fl32 is
+  IEEE binary32 division, rounded to nearest-even.
 * MoE output stage (announcement, section "Shared CUDA components": scaling
   and bias additions can be fused into the output stage; MoE layers route each
   token to top-k experts):
@@ -156,6 +165,39 @@ def dequantize_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     v = F.decode_e2m1(codes)
     s = F.decode_e8m0(scales)
     return v * np.repeat(s, 32, axis=-1)
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_fp8(x: np.ndarray, block: int | None = None):
+    """FP8 quantization of rows [rows, K] of fp32-representable reals.
+
+    block = None: one scale per row (per token); block = B: one scale per B
+    consecutive values (the last block of a row may be shorter).  Returns
+    (codes uint8 [rows, K] e4m3, scales float32 [rows] or [rows, ceil(K/B)])."""
+    x = np.asarray(x, dtype=np.float64)
+    x32 = x.astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), x, equal_nan=True):
+        raise ValueError("inputs must be exact in fp32")
+    rows, k = x.shape
+    b = k if block is None else block
+    nb = -(-k // b)
+    xp = np.zeros((rows, nb * b), np.float32)
+    xp[:, :k] = x32
+    blk = xp.reshape(rows, nb, b)
+    amax = np.abs(blk).max(axis=-1)                                   # exact
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)              # IEEE fp32 division
+    s = np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+    q = (blk / s[..., None]).astype(np.float32)                       # IEEE fp32 division
+    # keep -0.0 of negative zeros: the division preserves the sign
+    codes = e4m3_nearest(q.astype(np.float64)).reshape(rows, nb * b)[:, :k]
+    return codes, (s[:, 0] if block is None else s)
+
+
+def quantize_fp8_bf16(x_bits: np.ndarray, block: int | None = None):
+    """quantize_fp8 of bf16 bit patterns (uint16 [rows, K])."""
+    return quantize_fp8(F.decode_bf16(x_bits), block)
 
 
 def silu(v: np.ndarray) -> np.ndarray:

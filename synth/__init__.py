@@ -26,8 +26,10 @@ import numpy as np
 
 # Weight-type names shared with the C header (values match ``qg_wtype``).
 W_INT4, W_UINT4, W_INT3, W_UINT3, W_MXFP4 = 0, 1, 2, 3, 4
-WTYPE_BITS = {W_INT4: 4, W_UINT4: 4, W_INT3: 3, W_UINT3: 3, W_MXFP4: 4}
-WTYPE_HAS_ZP = {W_INT4: False, W_UINT4: True, W_INT3: False, W_UINT3: True, W_MXFP4: False}
+W_INT8, W_UINT8, W_INT2, W_UINT2, W_INT1, W_UINT1, W_E0M3, W_E0M7, W_FP8 = 5, 6, 7, 8, 9, 10, 11, 12, 13
+WTYPE_BITS = {W_INT4: 4, W_UINT4: 4, W_INT3: 3, W_UINT3: 3, W_MXFP4: 4, W_INT8: 8, W_UINT8: 8, W_INT2: 2,
+              W_UINT2: 2, W_INT1: 1, W_UINT1: 1, W_E0M3: 4, W_E0M7: 8, W_FP8: 8}
+WTYPE_HAS_ZP = {w: w in (W_UINT4, W_UINT3, W_UINT8, W_UINT2, W_UINT1) for w in WTYPE_BITS}
 
 
 def rng(seed: int, *stream: int) -> np.random.Generator:
@@ -85,12 +87,53 @@ def int_weights(r: np.random.Generator, n: int, k: int, wtype: int, group: int,
     bits = WTYPE_BITS[wtype]
     lead = (n,) if experts is None else (experts, n)
     assert k % group == 0
-    raw = r.integers(0, 1 << bits, size=lead + (k,), dtype=np.uint8)  # code bits
+    if wtype == W_FP8:
+        # e4m3 codes of N(0, 1) values (finite: NaN codes never drawn)
+        raw = _encode_e4m3(np.copysign(_round_to_grid(np.abs(r.normal(0.0, 1.0, size=lead + (k,))), "e4m3"),
+                                       r.choice([-1.0, 1.0], size=lead + (k,))))
+    else:
+        raw = r.integers(0, 1 << bits, size=lead + (k,), dtype=np.uint8)  # code bits
     sc = scales_bf16(r, lead + (k // group,))
     zp = None
     if WTYPE_HAS_ZP[wtype]:
         zp = r.integers(0, 1 << bits, size=lead + (k // group,), dtype=np.uint8)
     return pack_codes(raw, bits), sc, zp, raw
+
+
+def fp8_block_weights(r: np.random.Generator, n: int, k: int, experts: int | None = None,
+                      sigma: float = 0.02):
+    """W8A8 weights: e4m3 codes [.., N, K] (one byte per element) of N(0,
+    sigma^2) values over fp32 scales, one per 128 x 128 block
+    ([.., ceil(N/128), ceil(K/128)]): each block's scale is its largest
+    magnitude / 448 (1 for an all-zero block), the codes the nearest-even
+    e4m3 of value / scale."""
+    lead = (n,) if experts is None else (experts, n)
+    w = r.normal(0.0, sigma, size=lead + (k,))
+    nb, kb = -(-n // 128), -(-k // 128)
+    wp = np.zeros(lead[:-1] + (nb * 128, kb * 128))
+    wp[..., :n, :k] = w
+    blk = wp.reshape(lead[:-1] + (nb, 128, kb, 128))
+    amax = np.abs(blk).max(axis=(-3, -1))
+    sc = np.where(amax > 0, amax / _E4M3_MAX, 1.0).astype(np.float32)
+    full = np.repeat(np.repeat(sc.astype(np.float64), 128, axis=-2), 128, axis=-1)
+    v = wp / full
+    codes = _encode_e4m3(np.copysign(_round_to_grid(np.abs(v), "e4m3"), v))[..., :n, :k]
+    return np.ascontiguousarray(codes), sc
+
+
+def fp8_activations(r: np.random.Generator, m: int, k: int, block: int | None, sigma: float = 1.0):
+    """e4m3 activations [m, k] over fp32 scales, one per row (block None) or
+    per row and ``block`` values: scale = block max / 448, codes nearest-even."""
+    x = r.normal(0.0, sigma, size=(m, k))
+    b = k if block is None else block
+    nb = -(-k // b)
+    xp = np.zeros((m, nb * b))
+    xp[:, :k] = x
+    amax = np.abs(xp.reshape(m, nb, b)).max(axis=-1)
+    sc = np.where(amax > 0, amax / _E4M3_MAX, 1.0).astype(np.float32)
+    v = xp / np.repeat(sc.astype(np.float64), b, axis=-1)
+    codes = _encode_e4m3(np.copysign(_round_to_grid(np.abs(v), "e4m3"), v))[:, :k]
+    return np.ascontiguousarray(codes), (sc[:, 0] if block is None else sc)
 
 
 def int4_weights_packed(r: np.random.Generator, n: int, k: int, wtype: int, group: int):

@@ -78,7 +78,7 @@ def test_bf16_matches_torch():
     assert _same(got, lib)
 
 
-@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_int_decode_matches_sign_extension(bits):
     c = np.arange(1 << bits)
     got = F.decode_int(c, bits)
@@ -109,7 +109,7 @@ def test_e0m7_identity_with_int8_without_minus_128():
     assert set(int4.tolist()) - set(e03.tolist()) == {-8.0}
 
 
-@pytest.mark.parametrize("bits", [3, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_unpack_bitstream_matches_numpy_unpackbits(bits):
     r = np.random.default_rng(7)
     k = 96
@@ -120,7 +120,7 @@ def test_unpack_bitstream_matches_numpy_unpackbits(bits):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 8])
 def test_pack_codes_roundtrip(bits):
     r = np.random.default_rng(3)
     codes = r.integers(0, 1 << bits, size=(4, 7, 256), dtype=np.uint8)

@@ -23,7 +23,14 @@ def _x_small_ints(r, m, k, lo=-3, hi=4):
     return synth.f32_to_bf16_bits(vals), vals.astype(np.float64)
 
 
-@pytest.mark.parametrize("wtype", [oracle.W_INT4, oracle.W_UINT4, oracle.W_INT3, oracle.W_UINT3])
+A16_WTYPES = [oracle.W_INT4, oracle.W_UINT4, oracle.W_INT3, oracle.W_UINT3, oracle.W_INT8, oracle.W_UINT8,
+              oracle.W_INT2, oracle.W_UINT2, oracle.W_INT1, oracle.W_UINT1, oracle.W_E0M3, oracle.W_E0M7,
+              oracle.W_FP8]
+INT_WTYPES = [oracle.W_INT4, oracle.W_UINT4, oracle.W_INT3, oracle.W_UINT3, oracle.W_INT8, oracle.W_UINT8,
+              oracle.W_INT2, oracle.W_UINT2, oracle.W_INT1, oracle.W_UINT1]
+
+
+@pytest.mark.parametrize("wtype", A16_WTYPES)
 def test_fraction_bruteforce_equals_fp64_a16(wtype):
     r = np.random.default_rng(100 + wtype)
     m, n, k, g = 3, 5, 64, 32
@@ -53,7 +60,7 @@ def test_fraction_bruteforce_equals_fp64_mx():
             assert Fraction(float(y[i, j])) == exact[i][j]  # dyadic, short span: exact
 
 
-@pytest.mark.parametrize("wtype", [oracle.W_INT4, oracle.W_UINT4, oracle.W_INT3, oracle.W_UINT3])
+@pytest.mark.parametrize("wtype", INT_WTYPES)
 def test_unit_scales_reduce_to_integer_gemm(wtype):
     """All scales 1.0 -> an integer GEMM, checked with numpy int64 on raw codes."""
     r = np.random.default_rng(300 + wtype)
@@ -71,6 +78,94 @@ def test_unit_scales_reduce_to_integer_gemm(wtype):
         w = ((raw << sh).view(np.int8) >> sh).astype(np.int64)
     ref = xv.astype(np.int64) @ w.T
     assert np.array_equal(y, ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("wtype,bits", [(oracle.W_E0M3, 4), (oracle.W_E0M7, 8)])
+def test_e0m_unit_scales_reduce_to_integer_gemm(wtype, bits):
+    """Announcement, "Quantization support": e0m codes are sign + magnitude in
+    integer units.  With unit scales the GEMM is an integer GEMM on
+    v = c for c < 2^(b-1) and v = 2^(b-1) - c otherwise (the magnitude
+    negated), written here without bit masks."""
+    r = np.random.default_rng(310 + wtype)
+    m, n, k, g = 3, 6, 256, 64
+    codes, sc, zp, raw = synth.int_weights(r, n, k, wtype, g)
+    assert zp is None
+    sc = np.full_like(sc, BF16_ONE)
+    xb, xv = _x_small_ints(r, m, k)
+    y = oracle.qg_gemm(wtype, codes, sc, None, n, k, g, oracle.A_BF16, xb)
+    half = 1 << (bits - 1)
+    raw = raw.astype(np.int64)
+    w = np.where(raw < half, raw, half - raw)
+    assert np.array_equal(y, (xv.astype(np.int64) @ w.T).astype(np.float64))
+
+
+def test_fp8_weights_unit_scales_reduce_to_value_table_gemm():
+    """e4m3 weights with bf16 scale 1.0: a GEMM on torch's e4m3 values."""
+    r = np.random.default_rng(320)
+    m, n, k, g = 3, 5, 128, 32
+    codes, sc, _, raw = synth.int_weights(r, n, k, oracle.W_FP8, g)
+    assert np.array_equal(codes, raw)            # 8-bit codes: one byte each
+    sc = np.full_like(sc, BF16_ONE)
+    xb, xv = _x_small_ints(r, m, k)
+    y = oracle.qg_gemm(oracle.W_FP8, codes, sc, None, n, k, g, oracle.A_BF16, xb)
+    wv = torch.from_numpy(raw.copy()).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(y, xv @ wv.T)
+
+
+def test_fp8_block_closed_form():
+    """W8A8 (announcement, "W8A8 / W4A8 / W4A4": FP8 with block-wise
+    scaling): all codes 1.0 (0x38), activation scales 2^a[r, kb], weight
+    scales 2^b[nb, kb] -> Y[r, n] = sum_kb 128 * 2^(a[r, kb] + b[n // 128, kb]).
+    N = 200 has a partial second block of rows, K = 384 three blocks; a
+    swapped block index or a per-column (not per-128-rows) weight scale fails."""
+    m, n, k = 3, 200, 384
+    a = np.array([[0, 1, 2], [3, -1, 0], [2, 2, -3]])
+    b = np.array([[1, 0, -2], [0, 4, 1]])
+    x = np.full((m, k), 0x38, np.uint8)
+    w = np.full((n, k), 0x38, np.uint8)
+    xs = np.exp2(a).astype(np.float32)
+    ws = np.exp2(b).astype(np.float32)
+    y = oracle.qg_gemm(oracle.W_FP8, w, ws, None, n, k, 128, oracle.A_FP8_BLOCK, x, xs)
+    for r_ in range(m):
+        for j in range(n):
+            assert y[r_, j] == sum(128 * 2.0 ** (a[r_, kb] + b[j // 128, kb]) for kb in range(3))
+
+
+def test_fp8_block_fraction_bruteforce_and_orientation():
+    """Random W8A8 operands at distinct M, N, K: float64 equals the exact
+    rational sum of e4m3(a) s_a[r, k // 128] e4m3(w) s_w[n // 128, k // 128]
+    term by term."""
+    r = synth.rng(0, 7)
+    m, n, k = 2, 130, 256
+    wc, ws = synth.fp8_block_weights(r, n, k)
+    xc, xs = synth.fp8_activations(r, m, k, 128)
+    y = oracle.qg_gemm(oracle.W_FP8, wc, ws, None, n, k, 128, oracle.A_FP8_BLOCK, xc, xs)
+    e4 = {c: Fraction(float(v)) for c, v in enumerate(
+        torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().tolist()) if v == v}
+    for i in range(m):
+        for j in (0, 1, 127, 128, 129):
+            terms = [e4[int(xc[i, kk])] * Fraction(float(xs[i, kk // 128])) * e4[int(wc[j, kk])] *
+                     Fraction(float(ws[j // 128, kk // 128])) for kk in range(k)]
+            # float64 summation error: at most k ulps of the sum of magnitudes
+            bound = k * Fraction(2) ** -52 * sum(abs(t) for t in terms)
+            assert abs(Fraction(float(y[i, j])) - sum(terms)) <= bound
+
+
+def test_per_token_fp8_w4a8_fraction_bruteforce():
+    """MXFP4 weights x per-token FP8 activations (announcement, "End to
+    end"): Y[r, n] = s_r * sum_k e4m3(a[r, k]) * e2m1(w[n, k]) 2^(e[n, k // 32] - 127),
+    exactly (a one-scale row check catches a scale applied per column)."""
+    r = synth.rng(0, 8)
+    m, n, k = 3, 4, 64
+    wc, wsc, wraw = synth.mx_weights(r, n, k)
+    xc, xs = synth.fp8_activations(r, m, k, None)
+    y = oracle.qg_gemm(oracle.W_MXFP4, wc, wsc, None, n, k, 32, oracle.A_FP8_TOKEN, xc, xs)
+    e4 = torch.from_numpy(xc.copy()).view(torch.float8_e4m3fn).double().numpy()
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(float(e4[i, kk])) * Fraction(float(F.decode_e2m1(wraw[j, kk]))) *
+                        Fraction(2) ** (int(wsc[j, kk // 32]) - 127) for kk in range(k))
+            assert Fraction(float(y[i, j])) == Fraction(float(xs[i])) * exact
 
 
 def test_closed_form_constant_codes_zero_point_and_groups():

@@ -13,6 +13,7 @@ import pytest
 
 from oracle import formats as F
 from oracle import quantize as Q
+import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxfp8_quantize_cases.txt")
 GOLDEN4 = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_quantize_cases.txt")
@@ -217,3 +218,95 @@ def test_combine_cases():
     np.testing.assert_array_equal(out_b, out + [[1, -1]])
     # topk = 1 with unit weights is the identity
     np.testing.assert_array_equal(Q.moe_combine(y, np.ones((6, 1)), 1), y)
+
+
+# ---------------------------------------------------------------------------
+# FP8 with fp32 scales (per token, per 128 values)
+# ---------------------------------------------------------------------------
+
+GOLDEN_FP8 = os.path.join(os.path.dirname(__file__), "golden", "fp8_quantize_cases.txt")
+
+
+def _fp8_cases():
+    out = []
+    for line in open(GOLDEN_FP8):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        name, vals, scale, codes = [p.strip() for p in line.split("|")]
+        x = np.zeros(8)
+        c = np.zeros(8, dtype=np.uint8)
+        for tok in vals.split():
+            i, v = tok.split("=")
+            x[int(i)] = float(v)
+        for tok in codes.split():
+            i, v = tok.split("=")
+            c[int(i)] = int(v, 16)
+        out.append((name, x, float(scale), c))
+    return out
+
+
+@pytest.mark.parametrize("case", _fp8_cases(), ids=lambda c: c[0])
+def test_fp8_hand_worked_cases(case):
+    _, x, scale, codes = case
+    c, s = Q.quantize_fp8(x[None, :])
+    assert s.dtype == np.float32 and float(s[0]) == scale
+    np.testing.assert_array_equal(c[0], codes)
+
+
+def _torch_fp8(x, block):
+    """The same rule through torch's fp32 arithmetic and its e4m3 cast."""
+    import torch
+    t = torch.from_numpy(np.asarray(x, np.float32))
+    rows, k = t.shape
+    b = k if block is None else block
+    nb = -(-k // b)
+    tp = torch.zeros((rows, nb * b), dtype=torch.float32)
+    tp[:, :k] = t
+    blk = tp.view(rows, nb, b)
+    amax = blk.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (blk / s[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(rows, nb * b)[:, :k]
+    return q.numpy(), (s[:, 0] if block is None else s).numpy()
+
+
+@pytest.mark.parametrize("block", [None, 128])
+def test_fp8_matches_torch_route(block):
+    """Random bf16 rows over a wide range of magnitudes, K not a multiple of
+    the block: codes and scales equal torch's fp32 division and e4m3 cast."""
+    r = np.random.default_rng(21)
+    x = r.normal(0, 1, size=(64, 320)) * np.exp2(r.integers(-20, 20, size=(64, 1)))
+    x[3] = 0.0
+    x[5, :130] = 0.0
+    xb = synth.f32_to_bf16_bits(x.astype(np.float32))
+    c, s = Q.quantize_fp8_bf16(xb, block)
+    ct, st = _torch_fp8(F.decode_bf16(xb), block)
+    np.testing.assert_array_equal(s, st)
+    np.testing.assert_array_equal(c, ct)
+
+
+def test_fp8_round_trip_of_representable_rows():
+    """Rows of e4m3 values times 2^E with one element at +-448: the scale is
+    exactly 2^E and every code comes back."""
+    r = np.random.default_rng(22)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    codes = r.choice(finite, size=(200, 64)).astype(np.uint8)
+    codes[np.arange(200), r.integers(0, 64, size=200)] = r.choice([0x7E, 0xFE], size=200)
+    e = r.integers(-100, 100, size=200)
+    x = F.decode_e4m3(codes) * np.exp2(e.astype(np.float64))[:, None]
+    c, s = Q.quantize_fp8(x)
+    np.testing.assert_array_equal(s, np.exp2(e).astype(np.float32))
+    # +-0 codes come back as +-0 (0x00 / 0x80)
+    np.testing.assert_array_equal(c, codes)
+
+
+def test_fp8_block_scales_are_per_128():
+    """Block scaling equals per-token scaling of each 128-value slice."""
+    r = np.random.default_rng(23)
+    x = synth.f32_to_bf16_bits(r.normal(0, 1, size=(5, 384)).astype(np.float32))
+    c, s = Q.quantize_fp8_bf16(x, 128)
+    assert s.shape == (5, 3)
+    for kb in range(3):
+        ck, sk = Q.quantize_fp8_bf16(x[:, 128 * kb:128 * kb + 128])
+        np.testing.assert_array_equal(c[:, 128 * kb:128 * kb + 128], ck)
+        np.testing.assert_array_equal(s[:, kb], sk)
