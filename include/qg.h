@@ -37,20 +37,25 @@
  *   codes  : [N][K] row-major, each row an LSB-first bitstream of b-bit codes
  *            (code k sits in bits [b*k, b*k+b) of the row; rows are K*b/8
  *            bytes).  INT-b codes are two's complement, UINT-b codes are plain,
- *            e2m1 uses bit 3 as its sign.
- *   scales : [N][K/g]: bf16 bit patterns (A16 formats) or e8m0 bytes (MXFP4).
+ *            e2m1 uses bit 3 as its sign, e0m codes bit b-1, e4m3 bit 7.
+ *   scales : [N][K/g]: bf16 bit patterns (A16 formats) or e8m0 bytes (MXFP4);
+ *            W8A8: fp32 [ceil(N/128)][K/128].
  *   zeros  : [N][K/g] uint8 in 0..2^b-1 for UINT-b formats, NULL otherwise.
  * Activations: x is [rows][ldx] row-major: bf16, e4m3 bytes (MXFP8), or e2m1
  * codes two per byte (MXFP4: element k in the low nibble of byte k/2 when k is
  * even, the high nibble when odd; ldx counts elements), the MX types with
- * x_scales [rows][K/32] e8m0 bytes (row stride K/32), per desc.atype.  y is [rows][ldy]
- * row-major, bf16 or fp32.
+ * x_scales [rows][K/32] e8m0 bytes (row stride K/32), per desc.atype; e4m3
+ * bytes with fp32 x_scales [rows] (FP8_TOKEN) or [rows][K/128] (FP8_BLOCK).
+ * y is [rows][ldy] row-major, bf16 or fp32.
  *
  * Numerics (the contract the CPU oracle checks):
  *   - A16 formats: the dequantized weight is the exact real (q - z) * s, with
  *     q the decoded code, z the group's zero point (0 for signed formats) and
  *     s the group's bf16 scale.  Kernels form sum_k x*(q - z) per K-group with
  *     bf16 MFMA (codes are exact in bf16) and apply s per group in fp32.
+ *   - Per-token FP8: y[r] = s_r * sum_k e4m3(a[r,k]) * Wdq[n,k] (MXFP4 Wdq).
+ *   - W8A8: sum over 128-K blocks kb of sa[r][kb] * sw[n/128][kb] * the
+ *     block's sum of e4m3 products, each block's partial scaled in fp32.
  *   - MXFP4 x MXFP8: e2m1 * 2^(e-127) times e4m3 * 2^(ea-127), exact operands
  *     into gfx950 scaled MFMA; MXFP4 x MXFP4 likewise with e2m1 activations.
  *   - fp32 accumulation; QG_O_BF16 output is the fp32 result rounded to
@@ -82,15 +87,27 @@ typedef enum {
 } qg_status;
 
 typedef enum {
-  QG_W_INT4 = 0,  /* signed two's complement [-8, 7], no zero point */
-  QG_W_UINT4 = 1, /* unsigned [0, 15] with a uint4 zero point per group */
-  QG_W_INT3 = 2,  /* signed two's complement [-4, 3], no zero point */
-  QG_W_UINT3 = 3, /* unsigned [0, 7] with a zero point per group */
-  QG_W_MXFP4 = 4  /* OCP e2m1 with one e8m0 scale per 32 along K */
+  QG_W_INT4 = 0,   /* signed two's complement [-8, 7], no zero point */
+  QG_W_UINT4 = 1,  /* unsigned [0, 15] with a uint4 zero point per group */
+  QG_W_INT3 = 2,   /* signed two's complement [-4, 3], no zero point */
+  QG_W_UINT3 = 3,  /* unsigned [0, 7] with a zero point per group */
+  QG_W_MXFP4 = 4,  /* OCP e2m1 with one e8m0 scale per 32 along K */
+  QG_W_INT8 = 5,   /* signed two's complement [-128, 127], no zero point */
+  QG_W_UINT8 = 6,  /* unsigned [0, 255] with a uint8 zero point per group */
+  QG_W_INT2 = 7,   /* signed two's complement [-2, 1], no zero point */
+  QG_W_UINT2 = 8,  /* unsigned [0, 3] with a zero point per group */
+  QG_W_INT1 = 9,   /* signed two's complement 1-bit: code 0 = 0, code 1 = -1 */
+  QG_W_UINT1 = 10, /* unsigned [0, 1] with a zero point per group */
+  QG_W_E0M3 = 11,  /* zero-exponent float: sign bit 3, magnitude bits 0..2 (-7..7) */
+  QG_W_E0M7 = 12,  /* zero-exponent float: sign bit 7, magnitude bits 0..6 (-127..127) */
+  QG_W_FP8 = 13    /* OCP e4m3 (one byte per weight) */
 } qg_wtype;
 
-typedef enum { QG_S_BF16 = 0, QG_S_E8M0 = 1 } qg_stype;
-typedef enum { QG_A_BF16 = 0, QG_A_MXFP8 = 1, QG_A_MXFP4 = 2 } qg_atype;
+typedef enum { QG_S_BF16 = 0, QG_S_E8M0 = 1, QG_S_F32 = 2 } qg_stype;
+/* FP8_TOKEN: e4m3 bytes with one fp32 scale per row (x_scales [rows]).
+ * FP8_BLOCK: e4m3 bytes with one fp32 scale per row and 128 K (x_scales
+ * [rows][K/128], row stride K/128). */
+typedef enum { QG_A_BF16 = 0, QG_A_MXFP8 = 1, QG_A_MXFP4 = 2, QG_A_FP8_TOKEN = 3, QG_A_FP8_BLOCK = 4 } qg_atype;
 typedef enum { QG_O_BF16 = 0, QG_O_F32 = 1 } qg_otype;
 
 /* How MoE rows are addressed.  A pair p = t*topk + j is token t's j-th expert
@@ -102,6 +119,21 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
 /* Layer + compute description ("Layer Config" / "Compute Config" of the
  * announcement's tuning section).  Supported (wtype, stype, atype, group):
  *   INT4/UINT4/INT3/UINT3, BF16 scales, BF16 activations, group 32, 64 or 128;
+ *   INT8/UINT8/INT2/UINT2/INT1/UINT1, E0M3/E0M7 and FP8 (e4m3), BF16 scales,
+ *   BF16 activations, group 32, 64 or 128 (the announcement's "WnA16"
+ *   section: integer and floating-point weights of 1 to 8 bits on the shared
+ *   dequantize-and-compute path; e0m codes, section "Quantization support",
+ *   hold the values of INT4 without -8 / INT8 without -128 and are stored as
+ *   those integers; the LDS-tiled large-M kernels serve the 4- and 3-bit
+ *   formats and E0M3, the others run the 16-row skinny kernel at every M);
+ *   MXFP4, E8M0 scales, FP8_TOKEN activations, group 32 (W4A8 with per-token
+ *   FP8 activations, section "End to end": the scaled MFMA with unit
+ *   activation block scales, each output row times its row's fp32 scale;
+ *   skinny kernel);
+ *   FP8 (e4m3), F32 scales, FP8_BLOCK activations, group 128 (W8A8 with
+ *   block-wise scaling, section "W8A8 / W4A8 / W4A4": one fp32 scale per
+ *   128 x 128 block of W, scales [N/128 rounded up][K/128]; K % 128 == 0;
+ *   skinny kernel);
  *   MXFP4, E8M0 scales, MXFP8 activations, group 32 (W4A8 on the scaled MFMA);
  *   MXFP4, E8M0 scales, BF16 activations, group 32 (each code dequantized in
  *   the kernel to the exact bf16 e2m1 * 2^(e-127); the announcement's
@@ -180,8 +212,9 @@ qg_status qg_gemm_workspace_size(const qg_weight *w, int64_t m, uint64_t *bytes)
  *   x        device, [m][ldx] bf16, e4m3 bytes or e2m1 nibble pairs (per
  *            desc.atype), 16-B aligned, ldx >= K and the row pitch (ldx
  *            elements) a multiple of 16 bytes (ldx % 32 == 0 for MXFP4).
- *   x_scales device, [m][K/32] e8m0 (MX activations only, else ignored / may
- *            be NULL).
+ *   x_scales device, [m][K/32] e8m0 (MX activations), fp32 [m] (FP8_TOKEN)
+ *            or fp32 [m][K/128] (FP8_BLOCK), 4-B aligned for fp32; ignored /
+ *            may be NULL for bf16 activations.
  * The MX large-M kernel addresses X with 32-bit offsets: an MX call whose
  * activation rows span 4 GiB or more (m * row pitch) returns
  * QG_ERR_UNSUPPORTED.
@@ -354,6 +387,24 @@ qg_status qg_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx,
  * NaN / Inf inputs give unspecified codes.  Asynchronous on `stream`. */
 qg_status qg_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q,
                             int64_t ldq, void *q_scales, hipStream_t stream);
+
+/* bf16 activations -> e4m3 with fp32 scales: per token (block == 0, one scale
+ * per row; the announcement's section "End to end" serves W4A8 with per-token
+ * FP8 activations) or per 128 values of a row (block == 128, the W8A8 input;
+ * section "W8A8 / W4A8 / W4A4").  Per block with largest magnitude a (a
+ * bf16 value, exact in fp32): scale s = a / 448 in IEEE fp32 (nearest-even;
+ * s = 1 for an all-zero block); code = e4m3 of the fp32 quotient v / s
+ * (IEEE division), nearest with ties to the even code, saturated at 448, sign
+ * kept (a negative value that rounds to zero gives 0x80).
+ *   x        device, bf16 [rows][ldx], 16-B aligned, ldx >= k, ldx % 8 == 0.
+ *   q        device, e4m3 bytes [rows][ldq], 16-B aligned, ldq >= k, ldq % 16 == 0.
+ *   q_scales device, fp32 [rows] (block 0) or [rows][ceil(k/128)] (block 128,
+ *            row stride ceil(k/128)), 4-B aligned.
+ * k % 8 != 0 or ld too small: QG_ERR_SHAPE; block not 0 or 128:
+ * QG_ERR_INVALID_ARGUMENT.  rows == 0 or k == 0: no-op.  NaN / Inf inputs give
+ * unspecified codes.  Asynchronous on `stream`. */
+qg_status qg_quantize_fp8(const void *x, int64_t rows, int64_t k, int64_t ldx, int32_t block, void *q,
+                          int64_t ldq, float *q_scales, hipStream_t stream);
 
 /* SiLU-gated product of a fused gate/up projection (MoE output stage between
  * gate_up and down; announcement, section "Shared CUDA components": scaling

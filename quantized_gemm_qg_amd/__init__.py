@@ -16,8 +16,9 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqg.so")
 QG_OK, QG_ERR_INVALID_ARGUMENT, QG_ERR_SHAPE, QG_ERR_ALIGNMENT = 0, 1, 2, 3
 QG_ERR_UNSUPPORTED, QG_ERR_BUFFER_TOO_SMALL, QG_ERR_HIP = 4, 5, 6
 W_INT4, W_UINT4, W_INT3, W_UINT3, W_MXFP4 = 0, 1, 2, 3, 4
-S_BF16, S_E8M0 = 0, 1
-A_BF16, A_MXFP8, A_MXFP4 = 0, 1, 2
+W_INT8, W_UINT8, W_INT2, W_UINT2, W_INT1, W_UINT1, W_E0M3, W_E0M7, W_FP8 = 5, 6, 7, 8, 9, 10, 11, 12, 13
+S_BF16, S_E8M0, S_F32 = 0, 1, 2
+A_BF16, A_MXFP8, A_MXFP4, A_FP8_TOKEN, A_FP8_BLOCK = 0, 1, 2, 3, 4
 O_BF16, O_F32 = 0, 1
 ROWS_BY_TOKEN, ROWS_BY_PAIR, ROWS_SORTED = 0, 1, 2
 ABI_VERSION, LAYOUT_VERSION = 1, 2
@@ -30,7 +31,7 @@ EXPORTS = (
     "qg_status_string", "qg_last_hip_error", "qg_quantize_mxfp8", "qg_silu_mul",
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
     "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset", "qg_quantize_mxfp4",
-    "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex", "qg_gemm_noalloc",
+    "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex", "qg_gemm_noalloc", "qg_quantize_fp8",
 )
 NOALLOC_SCRATCH_BYTES = 8 << 20
 GEMM_BATCH_INVARIANT = 1
@@ -91,6 +92,7 @@ def _load():
         "qg_last_hip_error": (I32, []),
         "qg_quantize_mxfp8": (I32, [P, I64, I64, I64, P, I64, P, P]),
         "qg_quantize_mxfp4": (I32, [P, I64, I64, I64, P, I64, P, P]),
+        "qg_quantize_fp8": (I32, [P, I64, I64, I64, I32, P, I64, P, P]),
         "qg_silu_mul": (I32, [P, I32, I64, I64, I64, P, I32, I64, P, P]),
         "qg_moe_combine": (I32, [P, I32, I64, P, I64, I32, I64, P, P, I32, I64, P]),
         "qg_gemm_workspace_size_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.POINTER(U64)]),
@@ -152,9 +154,10 @@ def last_hip_error() -> int:
 def layer_desc(wtype: int, n: int, k: int, group_size: int, atype: int | None = None,
                num_experts: int = 1, stype: int | None = None) -> LayerDesc:
     mx = wtype == W_MXFP4
-    return LayerDesc(ABI_VERSION, wtype, S_E8M0 if stype is None and mx else (stype or S_BF16),
-                     group_size, (A_MXFP8 if mx else A_BF16) if atype is None else atype,
-                     num_experts, n, k)
+    atype = (A_MXFP8 if mx else A_BF16) if atype is None else atype
+    if stype is None:
+        stype = S_E8M0 if mx else S_F32 if atype == A_FP8_BLOCK else S_BF16
+    return LayerDesc(ABI_VERSION, wtype, stype, group_size, atype, num_experts, n, k)
 
 
 def packed_size(desc: LayerDesc) -> int:
@@ -265,6 +268,13 @@ def quantize_mxfp8(x, rows: int, k: int, ldx: int, q, ldq: int, q_scales, stream
     """bf16 x [rows][ldx] -> e4m3 q [rows][ldq] + e8m0 q_scales [rows][k/32]."""
     _check(_lib.qg_quantize_mxfp8(_ptr(x), rows, k, ldx, _ptr(q), ldq, _ptr(q_scales), _stream(stream)),
            "qg_quantize_mxfp8")
+
+
+def quantize_fp8(x, rows: int, k: int, ldx: int, block: int, q, ldq: int, q_scales, stream=None) -> None:
+    """bf16 x [rows][ldx] -> e4m3 q [rows][ldq] + fp32 q_scales: [rows] (block 0, per token) or
+    [rows][ceil(k/128)] (block 128)."""
+    _check(_lib.qg_quantize_fp8(_ptr(x), rows, k, ldx, block, _ptr(q), ldq, _ptr(q_scales), _stream(stream)),
+           "qg_quantize_fp8")
 
 
 def quantize_mxfp4(x, rows: int, k: int, ldx: int, q, ldq: int, q_scales, stream=None) -> None:

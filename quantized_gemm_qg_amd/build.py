@@ -20,7 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqg.so")
-SOURCES = ["qg_api.cpp", "qg_repack.cpp", "qg_kernels.hip", "qg_tiled.hip", "qg_tiled_a16.hip", "qg_act.hip"]
+SOURCES = ["qg_api.cpp", "qg_repack.cpp", "qg_kernels.hip", "qg_formats.hip", "qg_tiled.hip", "qg_tiled_a16.hip",
+           "qg_act.hip"]
 ARCH = os.environ.get("QG_OFFLOAD_ARCH", "gfx950")
 
 

@@ -186,6 +186,92 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t *x, 
   }
 }
 
+// FP8 with fp32 scales.  The scale of a block with largest magnitude a is
+// s = a / 448 (IEEE fp32 division; 1 for an all-zero block) and each element
+// becomes e4m3 of the fp32 quotient v / s (IEEE division, then the
+// nearest-even e4m3 of e4m3_pair, saturated at 448).
+__device__ __forceinline__ float fp8_block_scale(float amax) { return amax > 0.f ? amax / 448.f : 1.f; }
+
+__device__ __forceinline__ uint2 fp8_store8(const float (&v)[8], float s) {
+  uint32_t c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    c[h] = e4m3_pair(v[4 * h] / s, v[4 * h + 1] / s) | (e4m3_pair(v[4 * h + 2] / s, v[4 * h + 3] / s) << 16);
+  return uint2{c[0], c[1]};
+}
+
+__device__ __forceinline__ void load8_bf16(const uint16_t *p, bool ok, float (&v)[8]) {
+  u32x4 a = {0u, 0u, 0u, 0u};
+  if (ok) a = *(const u32x4 *)p;
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+
+// Blocks of 128 values: 16 lanes per block (8 values, one 16-byte load each),
+// the block maximum combined over the 16 lanes by butterfly.  Unit u = (row,
+// block b); a block past K's end holds fewer values (k % 8 == 0), the lanes
+// beyond it load nothing and count as zeros.
+__global__ __launch_bounds__(256) void quantize_fp8_block_kernel(const uint16_t *x, int64_t ldx, int64_t k,
+                                                                 uint8_t *q, int64_t ldq, float *qs, int64_t kb,
+                                                                 int64_t units) {
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 16);
+  const int sub = threadIdx.x & 15;
+  const bool wide = units > 0xFFFFFFFFll;
+  // every lane of a 16-lane group runs the same iterations (u is uniform in the group)
+  for (int64_t u = (int64_t)blockIdx.x * (blockDim.x / 16) + threadIdx.x / 16; u < units; u += stride) {
+    int64_t row, b;
+    split_unit(u, kb, wide, row, b);
+    const int64_t c = b * 128 + 8 * sub;
+    const bool ok = c < k;
+    float v[8];
+    load8_bf16(x + row * ldx + c, ok, v);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float s = fp8_block_scale(m);
+    if (ok) *(uint2 *)(q + row * ldq + c) = fp8_store8(v, s);
+    if (sub == 0) qs[row * kb + b] = s;
+  }
+}
+
+// One scale per row: a workgroup per row (grid-stride over rows), the row
+// maximum reduced over the workgroup, then the row quantized in a second pass
+// over its values (from L2).
+__global__ __launch_bounds__(256) void quantize_fp8_row_kernel(const uint16_t *x, int64_t ldx, int64_t k,
+                                                               uint8_t *q, int64_t ldq, float *qs, int64_t rows) {
+  __shared__ float wave_max[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const uint16_t *xr = x + row * ldx;
+    float m = 0.f;
+    for (int64_t c = 8 * (int64_t)threadIdx.x; c < k; c += 8 * (int64_t)blockDim.x) {
+      float v[8];
+      load8_bf16(xr + c, true, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) wave_max[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+    __syncthreads();  // wave_max is rewritten for the next row
+    const float s = fp8_block_scale(m);
+    for (int64_t c = 8 * (int64_t)threadIdx.x; c < k; c += 8 * (int64_t)blockDim.x) {
+      float v[8];
+      load8_bf16(xr + c, true, v);
+      *(uint2 *)(q + row * ldq + c) = fp8_store8(v, s);
+    }
+    if (threadIdx.x == 0) qs[row] = s;
+  }
+}
+
 // h[r][j] = silu(gu[r][j]) * gu[r][inter + j] for j < inter, in fp32, rounded
 // to bf16; MX: the bf16 values are then quantized to MXFP8 as above.
 template <bool MX>
@@ -277,6 +363,22 @@ hipError_t launch_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_mxfp4_kernel, dim3(stream_grid(units)), dim3(256), 0, s, (const uint16_t *)x, ldx,
                      (uint8_t *)q, ldq, (uint8_t *)qs, k / 8, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void *x, int64_t rows, int64_t k, int64_t ldx, int block, void *q,
+                               int64_t ldq, float *qs, hipStream_t s) {
+  if (rows == 0 || k == 0) return hipSuccess;
+  if (block == 0) {
+    const unsigned grid = (unsigned)std::min<int64_t>(rows, 256 * 8);
+    hipLaunchKernelGGL(quantize_fp8_row_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t *)x, ldx, k,
+                       (uint8_t *)q, ldq, qs, rows);
+  } else {
+    const int64_t kb = (k + 127) / 128, units = rows * kb;
+    const unsigned grid = (unsigned)std::min<int64_t>((units + 15) / 16, 256 * 32);
+    hipLaunchKernelGGL(quantize_fp8_block_kernel, dim3(grid), dim3(256), 0, s, (const uint16_t *)x, ldx, k,
+                       (uint8_t *)q, ldq, qs, kb, units);
+  }
   return hipGetLastError();
 }
 

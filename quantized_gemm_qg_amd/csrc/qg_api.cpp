@@ -153,8 +153,18 @@ static bool env_variant(Variant *v) {
 // (T, KR) = (4, 2) for the integer formats, T * KR <= 8 but not (4, 4) for MX.
 static bool variant_ok(const qg_layer_desc &d, int T, int KR) {
   if ((T != 1 && T != 2 && T != 4) || (KR != 1 && KR != 2 && KR != 4)) return false;
-  if (mx_a8(d) || mx_a4(d)) return T * KR <= 8 && !(T == 4 && KR == 4);
+  if (mx_a8(d) || mx_a4(d) || mx_tok(d)) return T * KR <= 8 && !(T == 4 && KR == 4);
+  // 1-, 2-, 8-bit integers, e4m3 weights, W8A8: T <= 2 (fewer instances);
+  // spill-free: T * KR <= 2 for 8-bit slices (8 registers per block) and for
+  // group 32 (16 scales per block), 4 otherwise
+  if (ext_a16(d) || w8a8(d)) return T <= 2 && T * KR <= ext_wave_cap(d);
   return T * KR <= 4 || (T == 4 && KR == 2);
+}
+
+// Formats with a decode-kernel instance (bf16 activations, A16 formats)
+static bool decode_capable(const qg_layer_desc &d) {
+  const int f = kernel_fmt(d);
+  return f <= 3 || f == 5 || ext_a16(d);
 }
 
 static int clamp_kr(const qg_layer_desc &d, int T, int kr) {
@@ -171,12 +181,14 @@ static int clamp_kr(const qg_layer_desc &d, int T, int kr) {
 // (which costs a partials round trip and a counter-clearing launch) unless N
 // alone gives too few workgroups.
 static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles) {
-  const bool mx = mx_a8(d) || mx_a4(d);
-  // T x KR per wave: 4 x 2 (integer formats), 2 x 4 (MX); fewer for short K.
+  const bool mx = mx_a8(d) || mx_a4(d) || mx_tok(d);
+  // T x KR per wave: 4 x 2 (integer formats), 2 x 4 (MX), 2 x 2 (1-, 2-,
+  // 8-bit integers, e4m3 weights, W8A8); fewer for short K.
   // Measured on the decode shapes: fewer, fuller workgroups beat more, emptier
   // ones (224 workgroups of 8 KB waves beat 448 of 4 KB), so T shrinks only
   // when N alone would leave more than half of the CUs idle.
-  int T = mx ? 2 : 4, KR = mx ? 4 : 2;
+  const bool narrow = ext_a16(d) || w8a8(d);
+  int T = mx || narrow ? 2 : 4, KR = mx ? 4 : 2;
   while (KR > 1 && KR > k_blocks) KR /= 2;
   const bool long_k = (k_blocks + KR - 1) / KR > 16;  // K gets split anyway
   while (!long_k && T > 1 && (int64_t)((n_tiles + T - 1) / T) * m_tiles < 128) T /= 2;
@@ -245,7 +257,7 @@ static int mx_tile_cols(int64_t n, int64_t m, int bm) {
 }
 
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
-  if (w.desc.k % 128 != 0) return false;
+  if (w.desc.k % 128 != 0 || !has_tiled(w.desc)) return false;
   if (ov().tiled_off) return false;
   const bool mx = mx_a8(w.desc) || mx_a4(w.desc);
   // the integer-format kernel addresses X and the codes with 32-bit offsets
@@ -276,11 +288,14 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
 // one, "0" disables the kernel.
 static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Variant *v) {
   const int g = w.desc.group_size;
-  const bool compiled = (g == 32 && T == 1 && (KR == 4 || KR == 8)) ||
-                        (!fp4_a16(w.desc) &&
-                         ((g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
-                                        (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
-                          (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)))));
+  if (!decode_capable(w.desc)) return false;
+  // (1-, 2-, 8-bit integers and e4m3 weights: T = 1, KR = 4 or 8)
+  const bool compiled = ext_a16(w.desc) ? (T == 1 && (KR == 4 || KR == 8))
+                        : (g == 32 && T == 1 && (KR == 4 || KR == 8)) ||
+                              (!fp4_a16(w.desc) &&
+                               ((g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
+                                              (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
+                                (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)))));
   if (!compiled || S < 1 || S > 8) return false;
   const int kbs = w.k_blocks;
   const int W = (kbs + KR * S - 1) / (KR * S);
@@ -298,7 +313,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
 
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
-  if (mx_a8(d) || mx_a4(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
+  if (!decode_capable(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
   const Overrides &o = ov();
   if (o.decode_off) return false;
   if (o.decode_n >= 2) return decode_fits(w, m, o.decode_v[0], o.decode_v[1], o.decode_v[2], v);
@@ -307,9 +322,10 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   // dequantization behind the weight stream); at 16 rows the skinny kernel's
   // register-resident fragments win, so the decode kernel stops at 8 rows.
   if (m > 8) return false;
-  static const int pairs[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
+  static const int pairs_int[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
+  static const int pairs_ext[][2] = {{1, 8}, {1, 4}, {1, 4}, {1, 4}};
   const int kbs = w.k_blocks;
-  for (const auto &p : pairs) {
+  for (const auto &p : ext_a16(d) ? pairs_ext : pairs_int) {
     if ((kbs + p[1] - 1) / p[1] > 16) continue;
     if ((w.n_tiles + p[0] - 1) / p[0] < 200 && p[0] > 1) continue;
     if (decode_fits(w, m, p[0], p[1], 1, v)) {
@@ -332,7 +348,8 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
 // Tile widths do not change any element's order; they are fixed anyway.
 static Variant select_dense_invariant(const qg_weight &w) {
   const bool mx = mx_a8(w.desc) || mx_a4(w.desc);  // (W4A4 layers have K % 128 == 0)
-  if (w.desc.k % 128 == 0 && (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
+  if (has_tiled(w.desc) && w.desc.k % 128 == 0 &&
+      (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
     const int bn = mx ? 256 : a16_tiled_bn();
     return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
   }
@@ -390,7 +407,7 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
       return mx && d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) &&
              (v.tbn == 256 || (mx_tiled_waves() == 8 && (v.tbn == 192 || v.tbn == 224)));
     case 2:
-      return !mx && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
+      return !mx && has_tiled(d) && d.k % 128 == 0 && (uint64_t)m * d.k * 2 < (1ull << 31) &&
              (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31) &&
              ((v.bm == 128 && v.tbn == 256 && a16_tiled_waves() == 8) || ((v.bm == 128 || v.bm == 256) && v.tbn == 128));
     case 3: {
@@ -477,8 +494,8 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
   Variant s = skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles);
   if (s.splits > 1 || (int64_t)s.W * s.KR < w.k_blocks) {
     // long K: the deepest spill-free wave (KR = 4), T reduced to fit
-    s.KR = 4;
-    s.T = mx_a8(w.desc) ? 2 : 1;
+    s.T = (mx_a8(w.desc) || mx_tok(w.desc)) ? 2 : 1;
+    s.KR = clamp_kr(w.desc, s.T, 4);
     s.W = std::min(16, (w.k_blocks + s.KR - 1) / s.KR);
     s.splits = 1;
   }
@@ -493,7 +510,7 @@ static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
-  if (d.k % 128 != 0 || d.num_experts > kMaxExperts) return 0;
+  if (d.k % 128 != 0 || d.num_experts > kMaxExperts || !has_tiled(d)) return 0;
   const bool mx = mx_a8(d);
   // 32-bit offsets inside the kernels
   if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
@@ -692,9 +709,8 @@ extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
   void *stage = nullptr;
   hipError_t he = hipHostMalloc(&stage, stage_bytes, hipHostMallocDefault);
   if (he != hipSuccess) return hip_status(he);
-  uint64_t cb = (uint64_t)desc->n * desc->k * L.bits / 8;
-  uint64_t sb = (uint64_t)desc->n * (desc->k / desc->group_size) * ((L.is_mx || L.fp4) ? 1 : 2);  // e8m0 / bf16
-  uint64_t zb = L.has_zp ? (uint64_t)desc->n * (desc->k / desc->group_size) : 0;
+  uint64_t cb, sb, zb;
+  std_sizes(*desc, L, &cb, &sb, &zb);
   qg_status result = QG_OK;
   for (int64_t e0 = 0; e0 < expert_count; e0 += (int64_t)chunk_experts) {
     const int cnt = (int)std::min<int64_t>((int64_t)chunk_experts, expert_count - e0);
@@ -726,7 +742,7 @@ extern "C" qg_status qg_preprocess(const qg_layer_desc *desc, const void *codes,
 // Row pitch of the activations in bytes: ldx elements of bf16, e4m3 or (two
 // per byte) e2m1.
 static uint64_t x_pitch(const Layout &L, int64_t ldx) {
-  return L.a4 ? (uint64_t)ldx / 2 : (uint64_t)ldx * (L.is_mx ? 1 : 2);
+  return L.a4 ? (uint64_t)ldx / 2 : (uint64_t)ldx * (L.x8 ? 1 : 2);
 }
 
 static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, const Variant &v, const void *x,
@@ -800,8 +816,9 @@ extern "C" qg_status qg_gemm_ex(const qg_weight *w, const void *x, const void *x
   if (m > (1ll << 30)) return QG_ERR_UNSUPPORTED;
   if (m == 0) return QG_OK;
   if (!x || !y) return QG_ERR_INVALID_ARGUMENT;
-  if (L.is_mx && !x_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (L.xs_kind && !x_scales) return QG_ERR_INVALID_ARGUMENT;
   if (ldx < d.k || ldy < d.n) return QG_ERR_SHAPE;
+  if (L.xs_kind >= 2 && ((uintptr_t)x_scales & 3u) != 0) return QG_ERR_ALIGNMENT;
   const int yel = otype == QG_O_F32 ? 4 : 2;
   if (!aligned16(x) || !aligned16(y) || x_pitch(L, ldx) % 16 != 0 || (L.a4 && (ldx & 1)) || (ldy * yel) % 4 != 0)
     return QG_ERR_ALIGNMENT;
@@ -936,7 +953,8 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   if (pairs > (1ll << 30)) return QG_ERR_UNSUPPORTED;
   if (pairs == 0) return QG_OK;
   if (!x || !y || !sorted_pair_ids || !expert_offsets) return QG_ERR_INVALID_ARGUMENT;
-  if (L.is_mx && !x_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (L.xs_kind && !x_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (L.xs_kind >= 2 && ((uintptr_t)x_scales & 3u) != 0) return QG_ERR_ALIGNMENT;
   const int yel = otype == QG_O_F32 ? 4 : 2;
   if (!aligned16(x) || !aligned16(y) || x_pitch(L, d.k) % 16 != 0 || (d.n * yel) % 4 != 0)
     return QG_ERR_ALIGNMENT;
@@ -1046,6 +1064,17 @@ extern "C" qg_status qg_quantize_mxfp4(const void *x, int64_t rows, int64_t k, i
   return hip_status(launch_quantize_mxfp4(x, rows, k, ldx, q, ldq, q_scales, stream));
 }
 
+extern "C" qg_status qg_quantize_fp8(const void *x, int64_t rows, int64_t k, int64_t ldx, int32_t block, void *q,
+                                     int64_t ldq, float *q_scales, hipStream_t stream) {
+  if (rows < 0 || k < 0 || (block != 0 && block != 128)) return QG_ERR_INVALID_ARGUMENT;
+  if (k % 8 != 0 || ldx < k || ldq < k) return QG_ERR_SHAPE;
+  if (rows == 0 || k == 0) return QG_OK;
+  if (!x || !q || !q_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || ldx % 8 != 0 || !aligned16(q) || ldq % 16 != 0 || !aligned(q_scales, 4))
+    return QG_ERR_ALIGNMENT;
+  return hip_status(launch_quantize_fp8(x, rows, k, ldx, block, q, ldq, q_scales, stream));
+}
+
 extern "C" qg_status qg_silu_mul(const void *gu, int32_t gu_type, int64_t rows, int64_t inter, int64_t ldgu,
                                  void *h, int32_t h_type, int64_t ldh, void *h_scales, hipStream_t stream) {
   if (rows < 0 || inter < 0) return QG_ERR_INVALID_ARGUMENT;
@@ -1077,7 +1106,10 @@ extern "C" qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, 
   return hip_status(launch_moe_combine(y, yf, ldy, topk_weights, num_tokens, topk, n, bias, out, of, ldout, stream));
 }
 
-static void describe_variant(const Variant &v, bool mx, int k_blocks, char *buf, uint64_t buf_bytes) {
+static void describe_variant(const Variant &v, const Layout &L, int k_blocks, char *buf, uint64_t buf_bytes) {
+  const bool mx = L.is_mx;
+  // skinny-kernel family: MX (also per-token FP8 activations), W8A8, A16
+  const char *fam = L.mx_pack ? "mx" : L.f8 ? "f8" : "a16";
   if (v.kind == 3)
     snprintf(buf, buf_bytes, v.splits > 1 ? "a16_decode T=%d KR=%d W=%d splits=%d" : "a16_decode T=%d KR=%d W=%d",
              v.T, v.KR, v.W, v.splits);
@@ -1087,7 +1119,7 @@ static void describe_variant(const Variant &v, bool mx, int k_blocks, char *buf,
     // (K beyond W * KR * splits blocks: the workgroups loop over K)
     const int span = v.W * v.KR * v.splits, passes = (k_blocks + span - 1) / span;
     snprintf(buf, buf_bytes, passes > 1 ? "%s_skinny T=%d KR=%d W=%d splits=%d passes=%d" : "%s_skinny T=%d KR=%d W=%d splits=%d",
-             mx ? "mx" : "a16", v.T, v.KR, v.W, v.splits, passes);
+             fam, v.T, v.KR, v.W, v.splits, passes);
   }
 }
 
@@ -1176,8 +1208,9 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (d.num_experts != 1 || m < 1 || reps < 1 || reps > kTuneMaxReps) return QG_ERR_INVALID_ARGUMENT;
   if (otype != QG_O_BF16 && otype != QG_O_F32) return QG_ERR_INVALID_ARGUMENT;
   if (m > (1ll << 30)) return QG_ERR_UNSUPPORTED;
-  if (!x || !y || !ws || (L.is_mx && !x_scales)) return QG_ERR_INVALID_ARGUMENT;
+  if (!x || !y || !ws || (L.xs_kind && !x_scales)) return QG_ERR_INVALID_ARGUMENT;
   if (ldx < d.k || ldy < d.n) return QG_ERR_SHAPE;
+  if (L.xs_kind >= 2 && ((uintptr_t)x_scales & 3u) != 0) return QG_ERR_ALIGNMENT;
   const int yel = otype == QG_O_F32 ? 4 : 2;
   if (!aligned16(x) || !aligned16(y) || x_pitch(L, ldx) % 16 != 0 || (L.a4 && (ldx & 1)) || (ldy * yel) % 4 != 0 ||
       ((uintptr_t)ws & 255u) != 0)
@@ -1229,7 +1262,7 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (he != hipSuccess) return hip_status(he);
   if (best < 0) return QG_ERR_UNSUPPORTED;
   tuned_store(*w, m, cand[best]);
-  if (chosen && chosen_bytes) describe_variant(cand[best], L.is_mx, w->k_blocks, chosen, chosen_bytes);
+  if (chosen && chosen_bytes) describe_variant(cand[best], L, w->k_blocks, chosen, chosen_bytes);
   if (chosen_us) *chosen_us = best_us;
   return QG_OK;
 }
@@ -1267,7 +1300,7 @@ extern "C" qg_status qg_describe_dispatch_ex(const qg_weight *w, int64_t m, uint
     return QG_ERR_INVALID_ARGUMENT;
   if (flags && w->desc.num_experts > 1) return QG_ERR_INVALID_ARGUMENT;
   const Variant v = w->desc.num_experts > 1 ? select_moe(*w, m) : dense_variant(*w, m, flags);
-  describe_variant(v, L.is_mx, w->k_blocks, buf, buf_bytes);
+  describe_variant(v, L, w->k_blocks, buf, buf_bytes);
   return QG_OK;
 }
 

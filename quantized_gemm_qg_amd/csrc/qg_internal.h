@@ -16,9 +16,20 @@
 //       holds MFMA j's eight codes in bits 0..2 of the same nibble slots; the
 //       eight codes of MFMA 3 are spread over the slots' bit 3, bit b of a code
 //       living in dword b.
+//     * 8-bit integer and e4m3 weights x bf16 (block 2048 B, 32 B per lane =
+//       8 dwords): bytes 8 j .. 8 j + 7 hold MFMA j's codes e = 0..7 in order.
+//     * 2-bit integer (block 512 B, 8 B per lane): dword j / 2 holds MFMAs j
+//       and j + 1 (j even); code e of MFMA j in 2-bit slot 4 (j % 2) + e / 2 +
+//       8 (e % 2).
+//     * 1-bit integer (block 256 B, 4 B per lane): code e of MFMA j in bit
+//       4 j + e / 2 + 16 (e % 2).
 //     * Integer codes are stored offset-binary (u = c + 2^(b-1) for signed
 //       formats), so every integer format computes (u - z) with z = 2^(b-1)
-//       implied for signed formats.
+//       implied for signed formats; e0m3 / e0m7 codes (sign and magnitude)
+//       become the offset-binary code of their value, u = v + 8 / v + 128.
+//     * W8A8 e4m3 (block 2048 B, 32 B per lane): the lane's bytes are K 16 q
+//       .. 16 q + 15 and 64 + 16 q .. 64 + 16 q + 15 of the block for column
+//       n = 16 t + l % 16 (the scaled MFMA's 8-bit operand).
 //     * e2m1 (block 1024 B, 16 B per lane): the lane's 32 codes k = 128 kb +
 //       32 q + e in standard order (two per byte, low nibble first), i.e. the
 //       16-B chunk of the standard row that one 16x16x128 scaled MFMA lane reads.
@@ -35,8 +46,11 @@
 //           k_blocks rounded up to 4.  A lane reads four k-blocks' scales of
 //           its (column, quarter) as one dword, and 64 lanes read one unit
 //           (a whole n-tile) as 256 contiguous bytes.
+//           W8A8: fp32 [n_tile][kb_pad], the scale of the 128 x 128 block
+//           holding n-tile n_tile and k-block kb.
 //   zeros   UINT formats: [n_pad][groups_padded / 8] uint32, group g in nibble
-//           g % 8 of word g / 8.
+//           g % 8 of word g / 8; UINT8: [n_pad][groups_padded / 4] uint32,
+//           group g in byte g % 4 of word g / 4.
 //
 // Padding (n >= N, k >= K) holds code 0 with scale 0 (A16) or scale code 0
 // (MX), so padded weights are exactly zero; kernels also zero activations
@@ -59,6 +73,49 @@ inline bool fp4_a16(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.
 // MXFP4 weights with MXFP4 activations (W4A4): the MX layout, the large-M MX
 // kernel with e2m1 A operands, dense layers only.
 inline bool mx_a4(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_MXFP4; }
+// MXFP4 weights with per-token FP8 activations: the MX layout, the MX skinny
+// kernel with unit activation block scales and the row scale in the output.
+inline bool mx_tok(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.atype == QG_A_FP8_TOKEN; }
+// W8A8 FP8 with block scales (e4m3 x e4m3, fp32 scales)
+inline bool w8a8(const qg_layer_desc &d) { return d.wtype == QG_W_FP8 && d.atype == QG_A_FP8_BLOCK; }
+
+// Kernel format of a layer (the FMT of the skinny and decode kernels, see
+// FmtTraits in qg_wave.h).  e0m3 weights are stored as offset-binary INT4 and
+// e0m7 as offset-binary INT8 (the same values), so they run those formats.
+inline int kernel_fmt(const qg_layer_desc &d) {
+  switch (d.wtype) {
+    case QG_W_INT4: case QG_W_E0M3: return 0;
+    case QG_W_UINT4: return 1;
+    case QG_W_INT3: return 2;
+    case QG_W_UINT3: return 3;
+    case QG_W_INT8: case QG_W_E0M7: return 7;
+    case QG_W_UINT8: return 8;
+    case QG_W_INT2: return 9;
+    case QG_W_UINT2: return 10;
+    case QG_W_INT1: return 11;
+    case QG_W_UINT1: return 12;
+    case QG_W_FP8: return d.atype == QG_A_FP8_BLOCK ? 15 : 13;
+    default: return fp4_a16(d) ? 5 : mx_a4(d) ? 6 : mx_tok(d) ? 14 : 4;
+  }
+}
+// Formats of a16x_wave (1-, 2-, 8-bit integers, e4m3 weights; bf16 activations)
+inline bool ext_a16(const qg_layer_desc &d) {
+  const int f = kernel_fmt(d);
+  return f >= 7 && f <= 13;
+}
+// Largest T * KR of a spill-free skinny wave for the formats of a16x_wave
+// and W8A8 (T <= 2): 2 for 8-bit slices and for group 32, else 4.
+inline int ext_wave_cap(const qg_layer_desc &d) {
+  const int f = kernel_fmt(d);
+  return (f == 7 || f == 8 || f == 13 || (f >= 7 && f <= 13 && d.group_size == 32)) ? 2 : 4;
+}
+// Formats served by the LDS-tiled kernels (large M, MoE tiles): the 4- and
+// 3-bit integer formats (e0m3 included), MXFP4 with bf16, MXFP8 or MXFP4
+// activations.  The others run the skinny kernel at every M.
+inline bool has_tiled(const qg_layer_desc &d) {
+  const int f = kernel_fmt(d);
+  return f <= 6;
+}
 
 constexpr int kTileN = 16;    // N per tile
 constexpr int kBlockK = 128;  // K per block
@@ -72,8 +129,12 @@ struct Layout {
   int bits = 0;
   bool has_zp = false;
   bool is_mx = false;     // MX kernels (MXFP4 x MXFP8, or x MXFP4 with a4)
+  bool mx_pack = false;   // MX code and scale layout (is_mx, or per-token FP8 activations)
   bool a4 = false;        // MXFP4 activations (two e2m1 codes per byte)
   bool fp4 = false;       // MXFP4 weights x bf16 activations (integer-format layout, bf16 scales)
+  bool f8 = false;        // W8A8: e4m3 codes in the 8-bit MFMA operand layout, fp32 block scales
+  bool x8 = false;        // one byte per activation element (e4m3)
+  int xs_kind = 0;        // activation scales: 0 none, 1 e8m0 per 32, 2 fp32 per row, 3 fp32 per row and 128 K
   uint64_t block_bytes = 0;
   uint64_t codes_bytes = 0;
   uint64_t scales_offset = 0;
@@ -88,6 +149,9 @@ inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
 // Validates a descriptor; fills the layout on success.
 qg_status make_layout(const qg_layer_desc *d, Layout *out);
+
+// Bytes of one expert's standard-format codes, scales and zero points.
+void std_sizes(const qg_layer_desc &d, const Layout &L, uint64_t *codes, uint64_t *scales, uint64_t *zeros);
 
 // Host repack of one expert's standard-format tensors into its packed section.
 void repack_expert(const qg_layer_desc &d, const Layout &L, const uint8_t *codes,
@@ -164,6 +228,11 @@ Variant select_moe(const qg_weight &w, int64_t pairs);
 
 hipError_t launch_dense_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                             hipStream_t s);
+// Skinny and decode instances of the formats 7 .. 15 (qg_formats.hip): the
+// same contracts as the launches above for those formats.
+hipError_t launch_skinny_ext(const GemmArgs &a, int fmt, int group, const Variant &v, bool moe, int64_t grid,
+                             int64_t items, hipStream_t s);
+hipError_t launch_decode_ext(const GemmArgs &a, int fmt, int group, const Variant &v, hipStream_t s);
 hipError_t launch_dense_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                            hipStream_t s);
 // Dense decode for the integer formats (m <= 16, K % 512 == 0): activations
@@ -213,6 +282,9 @@ hipError_t launch_quantize_mxfp4(const void *x, int64_t rows, int64_t k, int64_t
                                  void *qs, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const void *x, int64_t rows, int64_t k, int64_t ldx, void *q, int64_t ldq,
                                  void *qs, hipStream_t s);
+// bf16 -> e4m3 with fp32 scales per row (block 0) or per 128 values (block 128)
+hipError_t launch_quantize_fp8(const void *x, int64_t rows, int64_t k, int64_t ldx, int block, void *q,
+                               int64_t ldq, float *qs, hipStream_t s);
 hipError_t launch_silu_mul(const void *gu, bool gu_f32, int64_t rows, int64_t inter, int64_t ldgu, bool mx,
                            void *h, int64_t ldh, void *hs, hipStream_t s);
 hipError_t launch_moe_combine(const void *y, bool y_f32, int64_t ldy, const float *wts, int64_t tokens, int topk,

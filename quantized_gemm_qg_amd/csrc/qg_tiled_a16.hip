@@ -552,7 +552,9 @@ static hipError_t launch_fmt(const GemmArgs &a, const qg_layer_desc &d, int64_t 
                              float *xs, bool sums, hipStream_t s) {
   const int g = d.group_size;
   switch (d.wtype) {
-    case QG_W_INT4: return launch_group<BM, BN, WM, WN, 4, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
+    case QG_W_INT4:
+    case QG_W_E0M3:  // stored as offset-binary INT4
+      return launch_group<BM, BN, WM, WN, 4, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_UINT4: return launch_group<BM, BN, WM, WN, 4, true, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_INT3: return launch_group<BM, BN, WM, WN, 3, false, MOE>(a, g, xs_rows, cap, xs, sums, s);
     case QG_W_UINT3: return launch_group<BM, BN, WM, WN, 3, true, MOE>(a, g, xs_rows, cap, xs, sums, s);

@@ -45,8 +45,16 @@ def _desc(**kw):
     (dict(wtype=qg.W_MXFP4, group_size=64, atype=qg.A_BF16), qg.QG_ERR_UNSUPPORTED),
     (dict(wtype=qg.W_MXFP4, group_size=128), qg.QG_ERR_UNSUPPORTED),
     (dict(stype=qg.S_E8M0), qg.QG_ERR_UNSUPPORTED),
-    (dict(wtype=9), qg.QG_ERR_INVALID_ARGUMENT),
-    (dict(atype=3), qg.QG_ERR_INVALID_ARGUMENT),
+    (dict(wtype=14), qg.QG_ERR_INVALID_ARGUMENT),
+    (dict(atype=5), qg.QG_ERR_INVALID_ARGUMENT),
+    (dict(stype=3), qg.QG_ERR_INVALID_ARGUMENT),
+    (dict(wtype=qg.W_INT8, stype=qg.S_E8M0), qg.QG_ERR_UNSUPPORTED),
+    (dict(wtype=qg.W_INT2, atype=qg.A_FP8_TOKEN), qg.QG_ERR_UNSUPPORTED),
+    (dict(atype=qg.A_FP8_BLOCK), qg.QG_ERR_UNSUPPORTED),               # INT4 x block FP8: no kernel
+    (dict(wtype=qg.W_FP8, atype=qg.A_FP8_BLOCK, group_size=64), qg.QG_ERR_UNSUPPORTED),   # W8A8: 128
+    (dict(wtype=qg.W_FP8, atype=qg.A_FP8_BLOCK, stype=qg.S_BF16), qg.QG_ERR_UNSUPPORTED),  # W8A8: fp32 scales
+    (dict(wtype=qg.W_FP8, atype=qg.A_FP8_TOKEN), qg.QG_ERR_UNSUPPORTED),
+    (dict(wtype=qg.W_MXFP4, group_size=32, atype=qg.A_FP8_BLOCK), qg.QG_ERR_UNSUPPORTED),
     (dict(atype=qg.A_MXFP4), qg.QG_ERR_UNSUPPORTED),     # INT4 x MXFP4: no kernel
     (dict(wtype=qg.W_MXFP4, group_size=32, atype=qg.A_MXFP4, k=544), qg.QG_ERR_UNSUPPORTED),  # W4A4: K % 128
 ])
@@ -64,32 +72,43 @@ def test_bad_abi_version():
     assert e.value.status == qg.QG_ERR_INVALID_ARGUMENT
 
 
+BITS = {qg.W_INT4: 4, qg.W_UINT4: 4, qg.W_INT3: 3, qg.W_UINT3: 3, qg.W_MXFP4: 4, qg.W_INT8: 8, qg.W_UINT8: 8,
+        qg.W_INT2: 2, qg.W_UINT2: 2, qg.W_INT1: 1, qg.W_UINT1: 1, qg.W_E0M3: 4, qg.W_E0M7: 8, qg.W_FP8: 8}
+ZP_TYPES = (qg.W_UINT4, qg.W_UINT3, qg.W_UINT8, qg.W_UINT2, qg.W_UINT1)
+
+
 def _layout(d):
     n_tiles = -(-d.n // 16)
     k_blocks = -(-d.k // 128)
     gpad = -(-(k_blocks * 128 // d.group_size) // 32) * 32
     kb_pad = -(-k_blocks // 4) * 4
-    bits = 3 if d.wtype in (qg.W_INT3, qg.W_UINT3) else 4
-    mx = d.wtype == qg.W_MXFP4
-    zp = d.wtype in (qg.W_UINT4, qg.W_UINT3)
-    bb = 1024 if bits == 4 else 768
+    bits = BITS[d.wtype]
+    mx = d.wtype == qg.W_MXFP4 and d.atype != qg.A_BF16
+    f8 = d.atype == qg.A_FP8_BLOCK
+    zp = d.wtype in ZP_TYPES
+    bb = 256 * bits
     codes = n_tiles * k_blocks * bb
     al = lambda v: -(-v // 256) * 256  # noqa: E731
     s_off = al(codes)
-    s_bytes = n_tiles * 16 * 4 * kb_pad if mx else n_tiles * 16 * gpad * 2
+    s_bytes = n_tiles * 16 * 4 * kb_pad if mx else n_tiles * kb_pad * 4 if f8 else n_tiles * 16 * gpad * 2
     end = s_off + s_bytes
     z_off = 0
     if zp:
         z_off = al(end)
-        end = z_off + n_tiles * 16 * (gpad // 8) * 4
-    return dict(n_tiles=n_tiles, k_blocks=k_blocks, gpad=gpad, kb_pad=kb_pad, bits=bits, mx=mx,
+        end = z_off + (n_tiles * 16 * gpad if bits == 8 else n_tiles * 16 * (gpad // 8) * 4)
+    return dict(n_tiles=n_tiles, k_blocks=k_blocks, gpad=gpad, kb_pad=kb_pad, bits=bits, mx=mx, f8=f8,
                 zp=zp, bb=bb, s_off=s_off, z_off=z_off, stride=al(end))
 
 
 def test_packed_size_formula():
     for d in (_desc(), _desc(wtype=qg.W_UINT4, n=14336, k=4096),
               _desc(wtype=qg.W_INT3, n=40, k=640, group_size=32),
-              _desc(wtype=qg.W_MXFP4, n=1280, k=640, group_size=32, num_experts=3)):
+              _desc(wtype=qg.W_MXFP4, n=1280, k=640, group_size=32, num_experts=3),
+              _desc(wtype=qg.W_UINT8, n=200, k=640, group_size=64),
+              _desc(wtype=qg.W_UINT2, n=40, k=384, group_size=32, num_experts=2),
+              _desc(wtype=qg.W_INT1, n=17, k=256),
+              _desc(wtype=qg.W_FP8, n=300, k=512, atype=qg.A_FP8_BLOCK),
+              _desc(wtype=qg.W_MXFP4, n=64, k=256, group_size=32, atype=qg.A_FP8_TOKEN)):
         assert qg.packed_size(d) == _layout(d)["stride"] * d.num_experts
 
 
@@ -113,13 +132,35 @@ def _unpack_packed(d, buf):
                 byte = buf[blk + (ln + 16 * q) * 16 + e // 2]
                 codes[nn, kk] = (byte >> (4 * (e % 2))) & 15
                 continue
+            if L["f8"]:
+                half, rr = divmod(r, 64)
+                q, i = divmod(rr, 16)
+                codes[nn, kk] = buf[blk + (ln + 16 * q) * 32 + 16 * half + i]
+                continue
             j, rr = divmod(r, 32)
             q, e = divmod(rr, 8)
             lane = ln + 16 * q
+            if L["bits"] in (8, 2, 1):
+                nb = L["bits"]
+                base = blk + lane * 4 * nb
+                if nb == 8:
+                    u = buf[base + 8 * j + e]
+                else:
+                    word, slot = (j // 2, 4 * (j % 2) + e // 2 + 8 * (e % 2)) if nb == 2 else \
+                        (0, 4 * j + e // 2 + 16 * (e % 2))
+                    w = int.from_bytes(bytes(buf[base + 4 * word: base + 4 * word + 4]), "little")
+                    u = (w >> (nb * slot)) & ((1 << nb) - 1)
+                half_v = 1 << (nb - 1)
+                if d.wtype in (qg.W_INT8, qg.W_INT2, qg.W_INT1):
+                    u ^= half_v                       # back to the two's complement code
+                elif d.wtype == qg.W_E0M7:
+                    u = int(u) - half_v               # the value (checked against the e0m decode)
+                codes[nn, kk] = u
+                continue
             if L["bits"] == 4:
                 w = int.from_bytes(bytes(buf[blk + lane * 16 + 4 * j: blk + lane * 16 + 4 * j + 4]), "little")
                 u = (w >> (4 * _slot(e))) & 15
-                codes[nn, kk] = u ^ 8 if d.wtype == qg.W_INT4 else u
+                codes[nn, kk] = u ^ 8 if d.wtype == qg.W_INT4 else u - 8 if d.wtype == qg.W_E0M3 else u
             else:
                 ws = [int.from_bytes(bytes(buf[blk + lane * 12 + 4 * b: blk + lane * 12 + 4 * b + 4]), "little")
                       for b in range(3)]
@@ -129,6 +170,9 @@ def _unpack_packed(d, buf):
                     u = sum(((ws[b] >> (4 * _slot(e) + 3)) & 1) << b for b in range(3))
                 codes[nn, kk] = u ^ 4 if d.wtype == qg.W_INT3 else u
     G = k // d.group_size
+    if L["f8"]:
+        f = np.frombuffer(bytes(buf[L["s_off"]:L["s_off"] + L["n_tiles"] * L["kb_pad"] * 4]), np.float32)
+        return codes, f.reshape(L["n_tiles"], L["kb_pad"]), None
     if L["mx"]:
         sc = np.zeros((n, k // 32), np.int64)
         for nn in range(n):
@@ -140,7 +184,10 @@ def _unpack_packed(d, buf):
     s16 = np.frombuffer(bytes(buf[L["s_off"]:L["s_off"] + d.n * L["gpad"] * 2]), np.uint16)
     sc = s16.reshape(d.n, L["gpad"])[:, :G].astype(np.int64)
     zp = None
-    if L["zp"]:
+    if L["zp"] and L["bits"] == 8:
+        zb = np.frombuffer(bytes(buf[L["z_off"]:L["z_off"] + d.n * L["gpad"]]), np.uint8)
+        zp = zb.reshape(d.n, L["gpad"])[:, :G].astype(np.int64)
+    elif L["zp"]:
         words = np.frombuffer(bytes(buf[L["z_off"]:L["z_off"] + d.n * L["gpad"] // 2]), np.uint32)
         words = words.reshape(d.n, L["gpad"] // 8).astype(np.int64)
         zp = np.array([[(words[nn, g // 8] >> (4 * (g % 8))) & 15 for g in range(G)]
@@ -150,7 +197,10 @@ def _unpack_packed(d, buf):
 
 @pytest.mark.parametrize("wtype,n,k,g", [
     (qg.W_INT4, 40, 256, 128), (qg.W_UINT4, 33, 640, 64), (qg.W_INT3, 20, 384, 128),
-    (qg.W_UINT3, 16, 256, 32), (qg.W_MXFP4, 24, 640, 32)])
+    (qg.W_UINT3, 16, 256, 32), (qg.W_MXFP4, 24, 640, 32), (qg.W_INT8, 20, 384, 128),
+    (qg.W_UINT8, 18, 256, 64), (qg.W_INT2, 33, 384, 32), (qg.W_UINT2, 16, 256, 128),
+    (qg.W_INT1, 21, 256, 64), (qg.W_UINT1, 16, 384, 32), (qg.W_E0M3, 17, 256, 128),
+    (qg.W_E0M7, 19, 256, 64), (qg.W_FP8, 20, 256, 32)])
 def test_repack_roundtrip(wtype, n, k, g):
     r = synth.rng(42, wtype)
     d = qg.layer_desc(wtype, n, k, g)
@@ -162,13 +212,33 @@ def test_repack_roundtrip(wtype, n, k, g):
     buf = np.zeros(qg.packed_size(d), np.uint8)
     qg.repack_host(d, codes, sc, zp, buf)
     got_c, got_s, got_z = _unpack_packed(d, buf)
-    assert np.array_equal(got_c, raw.astype(np.int64))
+    want = raw.astype(np.int64)
+    if wtype in (qg.W_E0M3, qg.W_E0M7):
+        # sign and magnitude, written out without the oracle: the packed code holds the value
+        half = 1 << (synth.WTYPE_BITS[wtype] - 1)
+        want = np.where(want < half, want, half - want)
+    assert np.array_equal(got_c, want)
     assert np.array_equal(got_s, sc.astype(np.int64))
     if zp is not None:
         assert np.array_equal(got_z, zp.astype(np.int64))
     # padding beyond N is zero
     L = _layout(d)
     assert not buf[L["stride"]:].any()
+
+
+def test_repack_roundtrip_w8a8():
+    r = synth.rng(43, 1)
+    n, k = 300, 384
+    d = qg.layer_desc(qg.W_FP8, n, k, 128, atype=qg.A_FP8_BLOCK)
+    codes, sc = synth.fp8_block_weights(r, n, k)
+    buf = np.zeros(qg.packed_size(d), np.uint8)
+    qg.repack_host(d, codes, sc, None, buf)
+    got_c, got_s, _ = _unpack_packed(d, buf)
+    assert np.array_equal(got_c, codes.astype(np.int64))
+    L = _layout(d)
+    for t in range(L["n_tiles"]):
+        assert np.array_equal(got_s[t, :L["k_blocks"]], sc[16 * t // 128])
+        assert not got_s[t, L["k_blocks"]:].any()
 
 
 def test_repack_selected_experts_only():

@@ -151,3 +151,19 @@ def test_chains_follow_the_kernels_order():
     assert np.array_equal(two, (np.float32(0) + lo + hi).astype(np.float32))
     # passes: one wave of KR = 1 over 4 steps chains them in order like gemm_chain
     assert np.array_equal(full, M.gemm_waves(a, sa, w, sw, "e4m3", kr=1, waves=1))
+
+
+def test_w8a8_chain_within_its_bound_of_the_exact_oracle():
+    """The W8A8 chain (e4m3 x e4m3 steps, fp32 block scales) stays within
+    w8a8_error_bound of the exact oracle product for every wave layout."""
+    r = synth.rng(12, 1)
+    m, n, k = 6, 40, 512
+    wc, ws = synth.fp8_block_weights(r, n, k)
+    xc, xs = synth.fp8_activations(r, m, k, 128)
+    exact = oracle.qg_gemm(oracle.W_FP8, wc, ws, None, n, k, 128, oracle.A_FP8_BLOCK, xc, xs)
+    wcol = ws[np.arange(n) // 128]                     # each column's block scales
+    bound = M.w8a8_error_bound(xc, xs, wc, wcol)
+    assert np.all(bound < 1e-3 * np.abs(exact).max())  # the bound is tight enough to test
+    for kr, waves, splits in ((4, 1, 1), (1, 4, 1), (2, 1, 2), (1, 2, 2), (1, 1, 1)):
+        y = M.gemm_w8a8(xc, xs, wc, wcol, kr, waves, splits)
+        assert np.all(np.abs(y - exact) <= bound), (kr, waves, splits)
