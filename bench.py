@@ -70,13 +70,17 @@ class DenseWeights:
         self.std = (codes, sc, zp)
         desc = qg.layer_desc(wtype, n, k, group)
         size = qg.packed_size(desc)
-        self.bufs, self.ws = [], []
-        for _ in range(copies):
-            b = torch.empty(size, dtype=torch.uint8, device="cuda")
-            self.ws.append(qg.preprocess(desc, codes, sc, zp, b))
-            self.bufs.append(b)
         bits = 3 if wtype in (qg.W_INT3, qg.W_UINT3) else 4
         self.bytes = weight_bytes(n, k, bits, group, zp is not None, 1 if wtype == qg.W_MXFP4 else 2)
+        if copies is None:  # cold: the rotation spans twice the MALL
+            copies = max(2, -(-2 * MALL_BYTES // self.bytes))
+        # one host repack; the other copies are device copies of the packed bytes
+        first = torch.empty(size, dtype=torch.uint8, device="cuda")
+        self.bufs, self.ws = [first], [qg.preprocess(desc, codes, sc, zp, first)]
+        for _ in range(copies - 1):
+            b = first.clone()
+            self.ws.append(qg.weight_bind(desc, b, size))
+            self.bufs.append(b)
 
 
 def make_x(qg, synth, torch, mx, m, k, seed):
@@ -191,15 +195,17 @@ def mx_acts_device(torch, rows, k, gen):
     return q.view(torch.uint8).view(rows, k).contiguous(), (e + 127).to(torch.uint8).contiguous()
 
 
-def moe_dispatch(ids, experts, mx, tiled_min=64, small_min_pairs=256):
-    """Which kernel serves which experts under the default split."""
+def moe_dispatch(qg, w, ids, experts):
+    """The library's MoE dispatch rule for this routing, with the number of
+    experts on each side of its row threshold."""
+    import re
+    rule = qg.describe_moe_dispatch(w, ids.shape[0], ids.shape[1])
+    m = re.search(r">= (\d+) rows", rule)
+    if not m:
+        return rule
     counts = np.bincount(ids.ravel(), minlength=experts)
-    big = int((counts >= tiled_min).sum())
-    small = int(((counts > 0) & (counts < tiled_min)).sum())
-    fmt = "mx" if mx else "a16"
-    rest = (f"{fmt}_tiled small tiles BM=64 for {small}" if ids.size >= small_min_pairs
-            else f"{fmt}_skinny for {small}")
-    return f"{fmt}_tiled BM=128 for {big} experts with >= {tiled_min} rows; {rest} smaller"
+    thr = int(m.group(1))
+    return f"{rule} ({int((counts >= thr).sum())} / {int(((counts > 0) & (counts < thr)).sum())} experts)"
 
 
 def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters, atype=None):
@@ -253,11 +259,37 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
            "sort_us": round(t_sort * 1e3, 2), "TFLOPS": round(tflops, 2),
            "weight_GBs": round(gbs, 1), "mfma_frac": round(tflops / peak, 4),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-           "dispatch": moe_dispatch(ids, experts, mx)}
+           "dispatch": moe_dispatch(qg, up.ws[0], ids, experts)}
     del up, down
     torch.cuda.empty_cache()
     print(f"[bench] {name} T={tokens}: {out}", file=sys.stderr, flush=True)
     return out
+
+
+def bench_stream_ceiling(qg, torch, nbytes=30507008):
+    """Plain qg_stream_read of one decode GEMM's weight bytes (30.5 MB), the
+    buffers rotating over twice the MALL: the practical single-launch read
+    rate that bounds the decode kernels."""
+    copies = max(2, -(-2 * MALL_BYTES // nbytes))
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    sink = torch.zeros(16384, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    t = timed(torch, lambda i: qg.stream_read(bufs[i % copies], nbytes, sink, stream), 200, 20)
+    out = {"bytes": nbytes, "us": round(t * 1e3, 2), "GBs": round(nbytes / (t * 1e-3) / 1e9, 1),
+           "hbm_frac": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "copies": copies}
+    print(f"[bench] stream-read ceiling: {out}", file=sys.stderr, flush=True)
+    del bufs
+    return out
+
+
+def bench_moe_large(qg, synth, torch):
+    """The MoE configurations at T = 4096 only (for profiling)."""
+    return {
+        "w4a16_E256_top8_T4096": bench_moe(qg, synth, torch, "moe_w4a16", qg.W_INT4, 256, 8, 4096, 7168, 7168,
+                                           2048, 4096, iters=5),
+        "w4a8_E128_top8_T4096": bench_moe(qg, synth, torch, "moe_w4a8", qg.W_MXFP4, 128, 8, 1280, 4096, 4096,
+                                          640, 4096, iters=5),
+    }
 
 
 def cpu_baseline(oracle, shapes, budget_s=15.0):
@@ -284,7 +316,7 @@ def cpu_baseline(oracle, shapes, budget_s=15.0):
 # the traffic summary under profiles/).  Used only while the kernel sources
 # still hash to what was measured.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_w4a16_m1_hbm_traffic.md")
-KERNEL_SOURCES = ["qg_kernels.hip", "qg_device.h", "qg_internal.h"]
+KERNEL_SOURCES = ["qg_kernels.hip", "qg_wave.h", "qg_device.h", "qg_internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -334,12 +366,26 @@ def pmc_workload(qg, synth, torch):
           f"({L.bytes} algorithmic bytes per launch), source hash {kernel_source_hash()}", flush=True)
 
 
+def cold_copies(qg, torch, desc, codes, sc, nbytes):
+    """Packed copies of one weight whose rotation spans twice the MALL (each
+    launch reads its weights from HBM): one host repack, device copies."""
+    copies = max(2, -(-2 * MALL_BYTES // nbytes))
+    first = torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda")
+    bufs, wts = [first], [qg.preprocess(desc, codes, sc, None, first)]
+    for _ in range(copies - 1):
+        b = first.clone()
+        bufs.append(b)
+        wts.append(qg.weight_bind(desc, b, b.numel()))
+    return bufs, wts
+
+
 def bench_large_m(qg, synth, torch):
     """W4A16 INT4 (g128) and W4A8 MXFP4 x MXFP8 dense GEMMs at M = 4096:
-    TFLOPS against the bf16 / fp8 dense MFMA peaks."""
+    TFLOPS against the bf16 / fp8 dense MFMA peaks.  Weights rotate over
+    copies spanning twice the MALL, so every launch reads them from HBM."""
     extra = {}
     for n, k in ((14336, 4096), (4096, 14336)):
-        L = DenseWeights(qg, synth, torch, qg.W_INT4, n, k, 128, seed=60, copies=2)
+        L = DenseWeights(qg, synth, torch, qg.W_INT4, n, k, 128, seed=60, copies=None)
         x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=61)
         t = timed(torch, dense_launcher(qg, torch, L, x, None, 4096), 40, 10)
         fl = 2.0 * 4096 * n * k
@@ -353,14 +399,14 @@ def bench_large_m(qg, synth, torch):
     n, k = 14336, 4096
     codes, sc, _ = synth.mx_weights(synth.rng(80, 1), n, k)
     desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_BF16)
-    bufs = [torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda") for _ in range(2)]
-    wts = [qg.preprocess(desc, codes, sc, None, b) for b in bufs]
+    bufs, wts = cold_copies(qg, torch, desc, codes, sc, weight_bytes(n, k, 4, 32, False, 1))
+    nw = len(wts)
     x, _, _ = make_x(qg, synth, torch, False, 4096, k, seed=81)
     y = torch.empty((4096, n), dtype=torch.bfloat16, device="cuda")
     wsb = qg.gemm_workspace_size(wts[0], 4096)
     ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
-    t = timed(torch, lambda i: qg.gemm(wts[i % 2], x, None, 4096, k, y, qg.O_BF16, n, ws, wsb, stream), 40, 10)
+    t = timed(torch, lambda i: qg.gemm(wts[i % nw], x, None, 4096, k, y, qg.O_BF16, n, ws, wsb, stream), 40, 10)
     fl = 2.0 * 4096 * n * k
     extra[f"mxfp4_bf16_M4096_N{n}_K{k}"] = {
         "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
@@ -369,7 +415,7 @@ def bench_large_m(qg, synth, torch):
     print(f"[bench] extra mxfp4 x bf16: {extra[f'mxfp4_bf16_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
     del bufs, wts
     for n in (3072, 14336):
-        L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=2)
+        L = DenseWeights(qg, synth, torch, qg.W_MXFP4, n, 4096, 32, seed=50, copies=None)
         x, xsc, _ = make_x(qg, synth, torch, True, 4096, 4096, seed=51)
         t = timed(torch, dense_launcher(qg, torch, L, x, xsc, 4096), 100, 20)
         fl = 2.0 * 4096 * n * 4096
@@ -385,15 +431,15 @@ def bench_large_m(qg, synth, torch):
         k = 4096
         codes, sc, _ = synth.mx_weights(synth.rng(82, n), n, k)
         desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_MXFP4)
-        bufs = [torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda") for _ in range(2)]
-        wts = [qg.preprocess(desc, codes, sc, None, b) for b in bufs]
+        bufs, wts = cold_copies(qg, torch, desc, codes, sc, weight_bytes(n, k, 4, 32, False, 1))
+        nw = len(wts)
         xc = torch.randint(0, 256, (4096, k // 2), dtype=torch.uint8, device="cuda")
         xs = torch.randint(118, 128, (4096, k // 32), dtype=torch.uint8, device="cuda")
         y = torch.empty((4096, n), dtype=torch.bfloat16, device="cuda")
         wsb = qg.gemm_workspace_size(wts[0], 4096)
         ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
         stream = torch.cuda.current_stream().cuda_stream
-        t = timed(torch, lambda i: qg.gemm(wts[i % 2], xc, xs, 4096, k, y, qg.O_BF16, n, ws, wsb, stream), 100, 20)
+        t = timed(torch, lambda i: qg.gemm(wts[i % nw], xc, xs, 4096, k, y, qg.O_BF16, n, ws, wsb, stream), 100, 20)
         fl = 2.0 * 4096 * n * k
         extra[f"w4a4_mx_M4096_N{n}_K{k}"] = {
             "us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
@@ -509,6 +555,10 @@ def main():
                     help="only the M=4096 dense GEMMs (for profiling the tiled kernels)")
     ap.add_argument("--act", action="store_true",
                     help="only the activation-side kernels (quantizer, SiLU-gated product, combine)")
+    ap.add_argument("--moe", action="store_true",
+                    help="only the MoE configurations at T=4096 (for profiling the grouped kernels)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only the plain stream-read ceiling at one decode GEMM's weight bytes")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only run the copy calibration + decode kernel for rocprofv3 counter passes")
     args = ap.parse_args()
@@ -534,6 +584,12 @@ def main():
         return
     if args.act:
         print(json.dumps(bench_act(qg, synth, torch)), flush=True)
+        return
+    if args.moe:
+        print(json.dumps(bench_moe_large(qg, synth, torch)), flush=True)
+        return
+    if args.ceiling:
+        print(json.dumps(bench_stream_ceiling(qg, torch)), flush=True)
         return
 
     shapes = [(14336, 4096), (4096, 14336)]
@@ -679,6 +735,7 @@ def main():
                     "us": round(t * 1e3, 2), "weight_GBs": round(L.bytes / (t * 1e-3) / 1e9, 1),
                     "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         print(f"[bench] extra batch-invariant decode done", file=sys.stderr, flush=True)
+        extra["stream_read_ceiling"] = bench_stream_ceiling(qg, torch)
         extra.update(bench_large_m(qg, synth, torch))
         extra["activation"] = bench_act(qg, synth, torch)
         moe = {}

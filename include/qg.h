@@ -458,6 +458,13 @@ qg_status qg_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t
 qg_status qg_describe_dispatch(const qg_weight *w, int64_t m, char *buf, uint64_t buf_bytes);
 qg_status qg_describe_dispatch_ex(const qg_weight *w, int64_t m, uint32_t flags, char *buf, uint64_t buf_bytes);
 
+/* The MoE dispatch of qg_moe_gemm for num_tokens * topk pairs, as text:
+ * which kernel serves experts by row count (the tiled kernels' row threshold,
+ * the small-tile form or the skinny kernel's variant below it).  Which
+ * experts fall on which side depends on the routing (device data). */
+qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_tokens, int32_t topk, char *buf,
+                                   uint64_t buf_bytes);
+
 /* Static description of a status code (never NULL). */
 const char *qg_status_string(qg_status status);
 

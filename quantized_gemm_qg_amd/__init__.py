@@ -32,6 +32,7 @@ EXPORTS = (
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
     "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset", "qg_quantize_mxfp4",
     "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex", "qg_gemm_noalloc", "qg_quantize_fp8",
+    "qg_describe_moe_dispatch",
 )
 NOALLOC_SCRATCH_BYTES = 8 << 20
 GEMM_BATCH_INVARIANT = 1
@@ -88,6 +89,7 @@ def _load():
         "qg_stream_copy": (I32, [P, P, U64, P]),
         "qg_describe_dispatch": (I32, [W, I64, ctypes.c_char_p, U64]),
         "qg_describe_dispatch_ex": (I32, [W, I64, ctypes.c_uint32, ctypes.c_char_p, U64]),
+        "qg_describe_moe_dispatch": (I32, [W, I64, I32, ctypes.c_char_p, U64]),
         "qg_status_string": (ctypes.c_char_p, [I32]),
         "qg_last_hip_error": (I32, []),
         "qg_quantize_mxfp8": (I32, [P, I64, I64, I64, P, I64, P, P]),
@@ -253,6 +255,12 @@ def moe_gemm(w: Weight, x, x_scales, x_rows: int, sorted_pair_ids, expert_offset
 def describe_dispatch(w: Weight, m: int, flags: int = 0) -> str:
     buf = ctypes.create_string_buffer(256)
     _check(_lib.qg_describe_dispatch_ex(ctypes.byref(w), m, flags, buf, 256), "qg_describe_dispatch_ex")
+    return buf.value.decode()
+
+
+def describe_moe_dispatch(w: Weight, num_tokens: int, topk: int) -> str:
+    buf = ctypes.create_string_buffer(256)
+    _check(_lib.qg_describe_moe_dispatch(ctypes.byref(w), num_tokens, topk, buf, 256), "qg_describe_moe_dispatch")
     return buf.value.decode()
 
 

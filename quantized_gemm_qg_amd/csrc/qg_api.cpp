@@ -1024,6 +1024,32 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   return hip_status(he);
 }
 
+static void describe_variant(const Variant &v, const Layout &L, int k_blocks, char *buf, uint64_t buf_bytes);
+
+extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_tokens, int32_t topk, char *buf,
+                                              uint64_t buf_bytes) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (!buf || buf_bytes == 0 || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
+  const qg_weight wk = mx_kernel_weight(*w, L);
+  const int64_t pairs = num_tokens * topk;
+  const Variant v = select_moe(wk, std::max<int64_t>(pairs, 1));
+  char skinny[96];
+  describe_variant(v, L, w->k_blocks, skinny, sizeof skinny);
+  const int min_rows = pairs > 0 ? moe_tiled_min_rows(wk, pairs, pairs) : 0;
+  const char *fam = L.is_mx ? "mx" : "a16";
+  if (min_rows <= 0)
+    snprintf(buf, buf_bytes, "%s for every expert", skinny);
+  else if (moe_small_tiles(wk, pairs, min_rows))
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
+             kMoeTileRows, min_rows, fam, L.is_mx ? kMoeSmallTileRows : moe_small_bm());
+  else
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s below", fam, kMoeTileRows, min_rows,
+             skinny);
+  return QG_OK;
+}
+
 extern "C" qg_status qg_stream_read(const void *src, uint64_t bytes, void *sink,
                                     hipStream_t stream) {
   if (bytes == 0) return QG_OK;
