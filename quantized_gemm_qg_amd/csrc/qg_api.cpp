@@ -317,25 +317,31 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const Overrides &o = ov();
   if (o.decode_off) return false;
   if (o.decode_n >= 2) return decode_fits(w, m, o.decode_v[0], o.decode_v[1], o.decode_v[2], v);
-  // Measured on the decode shapes: one n-tile and 8 k-blocks per wave wins
-  // (small workgroups start and drain independently, which hides the
-  // dequantization behind the weight stream); at 16 rows the skinny kernel's
-  // register-resident fragments win, so the decode kernel stops at 8 rows.
-  if (m > 8) return false;
-  static const int pairs_int[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
+  // Measured on the decode shapes (N x K = 14336 x 4096 and 4096 x 14336,
+  // UINT4 and INT3, M = 1 .. 16): at one row one n-tile and 8 k-blocks per
+  // wave wins; from two rows two n-tiles of 4 k-blocks (the activation
+  // fragments read from LDS serve both tiles: 14336 x 4096 at M = 8 9.6 us
+  // against 12.1 us, at M = 16 12.6 against 17.9 us for the skinny kernel)
+  // wherever N gives enough workgroups; rows that do not fit LDS over all of
+  // K take a K split in two (4096 x 14336 at M = 8: 14.7 against 20.8 us on
+  // the skinny kernel), else the skinny kernel.
+  static const int pairs_one[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
+  static const int pairs_rows[][2] = {{2, 4}, {1, 8}, {2, 8}, {4, 2}};
   static const int pairs_ext[][2] = {{1, 8}, {1, 4}, {1, 4}, {1, 4}};
   const int kbs = w.k_blocks;
-  for (const auto &p : ext_a16(d) ? pairs_ext : pairs_int) {
+  for (const auto &p : ext_a16(d) ? pairs_ext : m == 1 ? pairs_one : pairs_rows) {
     if ((kbs + p[1] - 1) / p[1] > 16) continue;
     if ((w.n_tiles + p[0] - 1) / p[0] < 200 && p[0] > 1) continue;
     if (decode_fits(w, m, p[0], p[1], 1, v)) {
-      // long K over few column tiles (fewer than two workgroups per CU, each
-      // more than 8 waves): two K halves per tile measured 3 % faster
-      // (4096 x 14336: 10.94 -> 10.55 us at M = 1)
+      // a K split only when the column tiles leave CUs idle: the split's
+      // partial round trip (store, counter, reload) costs about 1.5 us
+      // (4096 x 14336 at M = 1: 7.9 us in one workgroup per tile, 9.4 us
+      // with two K halves)
       Variant s;
-      if ((w.n_tiles + v->T - 1) / v->T < 512 && v->W > 8 && decode_fits(w, m, v->T, v->KR, 2, &s)) *v = s;
+      if ((w.n_tiles + v->T - 1) / v->T < 192 && v->W > 8 && decode_fits(w, m, v->T, v->KR, 2, &s)) *v = s;
       return true;
     }
+    if (m > 1 && decode_fits(w, m, p[0], p[1], 2, v)) return true;  // rows too long for LDS: K halves
   }
   return false;
 }

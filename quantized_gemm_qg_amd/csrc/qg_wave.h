@@ -157,6 +157,13 @@ struct FmtTraits {
   static constexpr bool SWAP = FMT == 15;       // accumulator lane (q, r16) = (columns 4q + e, row r16)
 };
 
+// Weight blocks a decode-kernel wave keeps in flight (see a16_wave): 4 of its
+// KR = 8 blocks; every block at once elsewhere.
+template <bool XL, int KR>
+constexpr int a16_pipe_depth() {
+  return XL && KR > 4 ? 4 : KR;
+}
+
 // XL: the activation row comes from LDS (xrow is an LDS address holding the
 // row's K values from K = xk0 on); its fragments are read at their MFMA
 // instead of being held in registers.  after_issue() runs once every global load of the wave has
@@ -241,10 +248,14 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
 #pragma unroll
       for (int j = 0; j < 4; ++j) xf[kb][j] = xfrag(kb, j);
   }
-  // 3. weight slices, in the order the MFMAs consume them
+  // 3. weight slices, in the order the MFMAs consume them.  XL (the decode
+  //    kernel): DP blocks go out first and block kb + DP right after block
+  //    kb's work, so the wave computes while the CU's memory queue drains
+  //    (a wave that issued all its loads up front sat blocked on the full
+  //    queue until its last load went out); otherwise every block at once.
+  constexpr int DP = a16_pipe_depth<XL, KR>();
   u32x4 wq[T][KR];
-#pragma unroll
-  for (int kb = 0; kb < KR; ++kb)
+  auto issue = [&](int kb) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int nt = min(nt0 + t, a.n_tiles - 1), b = min(kb0 + kb, kbs - 1);
@@ -256,7 +267,10 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
         wq[t][kb] = u32x4{load_stream(p32), load_stream(p32 + 1), load_stream(p32 + 2), 0u};
       }
     }
-  // keep every load above this point: the wave waits once for all of them
+  };
+#pragma unroll
+  for (int kb = 0; kb < DP; ++kb) issue(kb);
+  // keep these loads above this point (the hook's waits count them)
   __builtin_amdgcn_sched_barrier(0);
   after_issue();
   if (kb0 >= kbs) return;  // wave-uniform: a wave entirely past K adds nothing
@@ -306,6 +320,16 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
     u32x4 xk[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xk[j] = XL ? xfrag(kb, j) : xf[XL ? 0 : kb][j];
+    // the next block's loads go out once this block's operands are read
+    auto issue_next = [&]() {
+      if constexpr (DP < KR) {
+        if (kb + DP < KR) {
+          __builtin_amdgcn_sched_barrier(0);
+          issue(kb + DP);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
     if constexpr (FP4) {
       // one K-group per MFMA: operand = e2m1 x 2^(e - 127), exact in bf16.
       // The conversion takes its scale as a power of two (a 0.0 scale acts as
@@ -313,7 +337,10 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
       // k-blocks past K (clamped re-reads of the last block, against
       // activations clamped to k = 0) are skipped instead (wave-uniform);
       // padding inside the last block holds code 0, which converts to 0.
-      if (kb0 + kb >= kbs) continue;
+      if (kb0 + kb >= kbs) {
+        issue_next();
+        continue;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = kb * GPB + j;
@@ -328,6 +355,7 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
           c[t] = mfma_bf16(xk[j], b, c[t]);
         }
       }
+      issue_next();
       continue;
     }
 #pragma unroll
@@ -359,6 +387,7 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
         }
       }
     }
+    issue_next();
   }
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = c[t];
@@ -923,7 +952,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
   const int q = lane >> 4, r16 = lane & 15;
-  const int rows = a.m;                       // 1..16
+  const int rows = ER == 1 ? 1 : a.m;         // 1..16 (ER = 1: a single row)
   const int kspan = nwaves * KR * 128;        // K covered by the waves of one split
   const int xpitch = kspan * 2 + 16;          // bytes per row in LDS (padded: bank spread)
   float *red = (float *)(dsm + ((rows * xpitch + 255) & ~255));  // [waves][T][rows][16]
@@ -934,29 +963,49 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   const int kk = min(kspan, a.k - ks0);       // K values of this split (a multiple of 512)
 
   // 1. activations -> LDS, 512 values (64 lanes x 16 B) per copy; columns
-  //    kk .. kspan (a partial last wave) are zeros
-  const int per_row = kk >> 9;
-  for (int i = wave; i < rows * per_row; i += nwaves) {
-    const int r = i / per_row, c0 = (i - r * per_row) << 9;
-    lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + ks0 + c0 + lane * 8, dsm + r * xpitch + c0 * 2);
-  }
-  const int tail = (kspan - kk) >> 3;  // 16-byte chunks per row
-  for (int i = threadIdx.x; i < rows * tail; i += blockDim.x) {
-    const int r = i / tail;
-    *(u32x4 *)(dsm + r * xpitch + kk * 2 + (i - r * tail) * 16) = u32x4{0u, 0u, 0u, 0u};
+  //    kk .. kspan (a partial last wave) are zeros.  With KR >= 4 each wave
+  //    copies the K range it reads itself (KR / 4 copies per row), so it only
+  //    waits for its own copies; with fewer blocks per wave the waves copy
+  //    the rows together and meet at a barrier.
+  constexpr bool OWN_X = KR >= 4;
+  if constexpr (OWN_X) {
+    const int kw = wave * KR * 128;  // the wave's first K (within the split)
+#pragma unroll
+    for (int c = 0; c < KR / 4; ++c) {
+      const int c0 = kw + c * 512;
+      for (int r = 0; r < rows; ++r) {
+        if (c0 < kk)  // wave-uniform
+          lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + ks0 + c0 + lane * 8, dsm + r * xpitch + c0 * 2);
+        else
+          *(u32x4 *)(dsm + r * xpitch + c0 * 2 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  } else {
+    const int per_row = kk >> 9;
+    for (int i = wave; i < rows * per_row; i += nwaves) {
+      const int r = i / per_row, c0 = (i - r * per_row) << 9;
+      lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + ks0 + c0 + lane * 8, dsm + r * xpitch + c0 * 2);
+    }
+    const int tail = (kspan - kk) >> 3;  // 16-byte chunks per row
+    for (int i = threadIdx.x; i < rows * tail; i += blockDim.x) {
+      const int r = i / tail;
+      *(u32x4 *)(dsm + r * xpitch + kk * 2 + (i - r * tail) * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. weights (all loads in flight), then the wait that covers the copies
-  //    above: at least T * KR weight loads were issued after them
+  // 2. weights (the first loads in flight), then the wait that covers the
+  //    copies above: at least T * (blocks issued) weight loads went out after
+  //    them
   f32x4 acc[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) acc[t] = {0.f, 0.f, 0.f, 0.f};
   const uint16_t *xrow = (const uint16_t *)(dsm + min(r16, rows - 1) * xpitch);
+  constexpr int ISSUED = FmtTraits<FMT>::EXT ? KR : a16_pipe_depth<true, KR>();
   auto x_ready = [&]() {
-    QG_WAIT_VMCNT(T * KR);
+    QG_WAIT_VMCNT(T * ISSUED);
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
+    if constexpr (!OWN_X) __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
   if constexpr (FmtTraits<FMT>::EXT)

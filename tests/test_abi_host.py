@@ -344,9 +344,12 @@ def test_dispatch_table_covers_k():
             T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
             assert W * KR * S >= -(-k // 128), s
             assert 1 <= W <= 16
-    # a split-K layout asks for a workspace
-    w = _bound(qg.layer_desc(qg.W_INT4, 4096, 14336, 32))
+    # a split-K layout (long K over too few column tiles to fill the CUs)
+    # asks for a workspace
+    w = _bound(qg.layer_desc(qg.W_INT4, 1024, 14336, 32))
+    assert "splits=2" in qg.describe_dispatch(w, 1)
     assert qg.gemm_workspace_size(w, 1) > 0
+    assert "splits" not in qg.describe_dispatch(_bound(qg.layer_desc(qg.W_UINT4, 4096, 14336, 128)), 1)
     assert qg.gemm_workspace_size(_bound(qg.layer_desc(qg.W_UINT4, 14336, 4096, 128)), 1) == 0
 
 

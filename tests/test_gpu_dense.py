@@ -369,12 +369,15 @@ def _gemm_ws(layer, acts, m, ws, otype=qg.O_F32):
     return y
 
 
-def test_workspace_shared_by_prefill_and_split_decode():
+def test_workspace_shared_by_prefill_and_split_decode(override):
     """The headline layer (UINT4 + zero points, g128, N = 4096, K = 14336):
     M = 4096 runs the tiled kernel (group row sums written to the workspace's
-    scratch), then M = 1 runs the split-K decode kernel on the same workspace
-    (its arrival counters sit in the workspace's counter prefix), then both
-    once more.  Every result against the oracle; the counters end at zero."""
+    scratch), then M = 1 runs the decode kernel split in two along K (forced:
+    the heuristic keeps this shape in one workgroup per tile) on the same
+    workspace (its arrival counters sit in the workspace's counter prefix),
+    then both once more.  Every result against the oracle; the counters end
+    at zero."""
+    override("QG_DECODE", "1,8,2")
     n, k = 4096, 14336
     layer = Layer(qg.W_UINT4, n, k, 128, seed=81)
     assert "a16_tiled" in qg.describe_dispatch(layer.w, 4096)

@@ -54,7 +54,7 @@ def test_fp4_bf16_dense(m, n, k):
     acts = Acts(False, m, k, seed=k)
     print(f"  M={m} N={n} K={k}: {qg.describe_dispatch(layer.w, m)}", flush=True)
     expect = ("a16_tiled" if m >= 256 and k % 128 == 0 else
-              "a16_decode" if m <= 8 and k % 512 == 0 else "a16_skinny")
+              "a16_decode" if m <= 16 and k % 512 == 0 else "a16_skinny")
     assert expect in qg.describe_dispatch(layer.w, m)
     yref = oracle.gemm(acts.xdq, layer.wdq())
     ys = {}
