@@ -44,6 +44,8 @@ struct Overrides {
   bool decode_off = false;  // QG_DECODE "0"
   int decode_n = 0;         // QG_DECODE "T,KR[,splits]": number of fields parsed (2 or 3)
   int decode_v[3] = {0, 0, 1};
+  int wide = -1;            // QG_DECODE_WIDE: "0" off, "W,KR" the wide decode form, unset: heuristics
+  int wide_v[2] = {16, 8};
   bool tiled_off = false;   // QG_TILED "0"
   bool tiled_set = false;   // QG_TILED present (any value): the autotune table is bypassed
   int tiled_bm = 0;         // QG_TILED_BM: 128 or 256
@@ -58,7 +60,7 @@ struct Overrides {
   int group_m = 0;          // QG_GROUP_M: 1..64
 };
 
-const char *const kOverrideNames[] = {"QG_TUNE", "QG_DECODE", "QG_TILED", "QG_TILED_BM", "QG_MX_BN",
+const char *const kOverrideNames[] = {"QG_TUNE", "QG_DECODE", "QG_DECODE_WIDE", "QG_TILED", "QG_TILED_BM", "QG_MX_BN",
                                       "QG_MX_WAVES", "QG_A16_WAVES", "QG_A16_BN", "QG_MOE_TILED_MIN",
                                       "QG_MOE_GROUP_M", "QG_MOE_SMALL_BM", "QG_MOE_SMALL", "QG_GROUP_M"};
 
@@ -84,6 +86,15 @@ bool apply_override(Overrides *o, const char *name, const char *val) {
         o->decode_n = n;
         o->decode_v[0] = T; o->decode_v[1] = KR; o->decode_v[2] = n == 3 ? S : 1;
       }
+    }
+  } else if (!strcmp(name, "QG_DECODE_WIDE")) {
+    int W, KR;
+    o->wide = -1;
+    if (set && *val == '0') {
+      o->wide = 0;
+    } else if (set && sscanf(val, "%d,%d", &W, &KR) == 2 && W >= 1 && W <= 16 && (KR == 8 || KR == 16)) {
+      o->wide = 1;
+      o->wide_v[0] = W; o->wide_v[1] = KR;
     }
   } else if (!strcmp(name, "QG_TILED")) {
     o->tiled_set = set;
@@ -218,6 +229,7 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
 // Split-K arrival counters of a dense launch (one per output tile), or 0.
 static int64_t split_counters(const qg_weight &w, const Variant &v, int64_t m) {
   if (v.splits <= 1) return 0;
+  if (v.kind == 4) return (w.n_tiles + v.W - 1) / v.W;  // wide decode: one per column group
   const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
   return v.kind == 3 ? n_blocks : ((m + 15) / 16) * n_blocks;
 }
@@ -311,12 +323,35 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
   return true;
 }
 
+// Wide decode form (2 .. 16 rows, K % 512 == 0): W waves along N, one K slice
+// of KR blocks per workgroup, ceil(K / (KR * 128)) slices.  Instances: KR 8 or
+// 16 for the decode-capable formats and groups, KR 8 only for the 8-bit
+// slices (e4m3 and 8-bit integers: 16 blocks of them in flight spill).
+static bool decode_wide_fits(const qg_weight &w, int64_t m, int W, int KR, Variant *v) {
+  const qg_layer_desc &d = w.desc;
+  if (!decode_capable(d) || m < 2 || m > 16 || d.k % 512 != 0 || W < 1 || W > 16 || (KR != 8 && KR != 16))
+    return false;
+  const int f = kernel_fmt(d);
+  if (KR == 16 && (f == 7 || f == 8 || f == 13)) return false;
+  // a slice's NG = KR * 128 / group scales are read as one run starting at a
+  // multiple of NG, which stays inside the row's padded groups only if NG
+  // divides them (always for NG <= 32: the padding is to a multiple of 32)
+  const int ng = KR * (128 / d.group_size);
+  if (w.groups_padded % ng != 0) return false;
+  if (fp4_a16(d) && d.group_size != 32) return false;
+  const int S = (w.k_blocks + KR - 1) / KR;
+  if (S > 1 && (w.n_tiles + W - 1) / W > kMaxSplitCounters) return false;
+  *v = Variant{4, 1, KR, W, S, 0, 0};
+  return true;
+}
+
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
   if (!decode_capable(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
   const Overrides &o = ov();
   if (o.decode_off) return false;
   if (o.decode_n >= 2) return decode_fits(w, m, o.decode_v[0], o.decode_v[1], o.decode_v[2], v);
+  if (o.wide == 1) return decode_wide_fits(w, m, o.wide_v[0], o.wide_v[1], v);
   // Measured on the decode shapes (N x K = 14336 x 4096 and 4096 x 14336,
   // UINT4 and INT3, M = 1 .. 16): at one row one n-tile and 8 k-blocks per
   // wave wins; from two rows two n-tiles of 4 k-blocks (the activation
@@ -341,9 +376,14 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
       if ((w.n_tiles + v->T - 1) / v->T < 192 && v->W > 8 && decode_fits(w, m, v->T, v->KR, 2, &s)) *v = s;
       return true;
     }
-    if (m > 1 && decode_fits(w, m, p[0], p[1], 2, v)) return true;  // rows too long for LDS: K halves
+    // rows too long for LDS over all of K: the wide form, which copies each
+    // K slice once per 8 column tiles (4096 x 14336, UINT4: 10.6 us at M = 8
+    // against 14.1 us for two K halves in this form, 11.3 us at M = 16
+    // against 20.6 us on the skinny kernel), else K halves
+    if (m > 1 && (decode_wide_fits(w, m, 8, 16, v) || decode_wide_fits(w, m, 8, 8, v))) return true;
+    if (m > 1 && decode_fits(w, m, p[0], p[1], 2, v)) return true;
   }
-  return false;
+  return m > 1 && (decode_wide_fits(w, m, 8, 16, v) || decode_wide_fits(w, m, 8, 8, v));
 }
 
 // Batch-invariant dispatch: the variant depends on (N, K) only, so each
@@ -419,6 +459,10 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
     case 3: {
       Variant t;
       return !mx && m >= 1 && m <= 16 && d.k % 512 == 0 && decode_fits(w, m, v.T, v.KR, v.splits, &t) && t.W == v.W;
+    }
+    case 4: {
+      Variant t;
+      return decode_wide_fits(w, m, v.W, v.KR, &t) && t.splits == v.splits;
     }
   }
   return false;
@@ -641,6 +685,8 @@ static uint64_t dense_ws_bytes(const qg_weight &w, const Variant &v, int64_t m) 
   if (v.kind == 2) return kSplitCounterBytes + a16_tiled_ws_bytes(w.desc, m);
   if (v.kind == 1) return kSplitCounterBytes + mx_tiled_ws_bytes(m, w.k_blocks);
   if (v.splits <= 1) return 0;
+  if (v.kind == 4)  // wide decode: a 16 x 16 partial per wave, slice and column group
+    return kSplitCounterBytes + (uint64_t)v.splits * ((w.n_tiles + v.W - 1) / v.W) * v.W * 256 * 4;
   const int64_t m_tiles = v.kind == 3 ? 1 : (m + 15) / 16;
   const int64_t n_blocks = (w.n_tiles + v.T - 1) / v.T;
   return kSplitCounterBytes + (uint64_t)v.splits * m_tiles * n_blocks * (uint64_t)v.T * 256 * 4;
@@ -782,6 +828,7 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
     return launch_dense_mx(a, d, v, stream);
   }
   if (v.kind == 3) return launch_decode_a16(a, d, v, stream);
+  if (v.kind == 4) return launch_decode_wide(a, d, v, stream);
   if (v.kind == 2) return launch_a16_tiled(a, d, v.bm, v.tbn, false, m, 0, a16_tiled_waves(), scratch, true, stream);
   return L.is_mx ? launch_dense_mx(a, d, v, stream) : launch_dense_a16(a, d, v, stream);
 }
@@ -1145,6 +1192,8 @@ static void describe_variant(const Variant &v, const Layout &L, int k_blocks, ch
   if (v.kind == 3)
     snprintf(buf, buf_bytes, v.splits > 1 ? "a16_decode T=%d KR=%d W=%d splits=%d" : "a16_decode T=%d KR=%d W=%d",
              v.T, v.KR, v.W, v.splits);
+  else if (v.kind == 4)
+    snprintf(buf, buf_bytes, "a16_decode_wide KR=%d W=%d splits=%d", v.KR, v.W, v.splits);
   else if (v.kind == 1 || v.kind == 2)
     snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", mx ? "mx" : "a16", v.bm, v.tbn);
   else {
@@ -1175,6 +1224,11 @@ static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> 
       for (int S : {1, 2, 4}) {
         Variant v;
         if (decode_fits(w, m, p[0], p[1], S, &v)) add(v);
+      }
+    for (int W : {8, 16})
+      for (int KR : {8, 16}) {
+        Variant v;
+        if (decode_wide_fits(w, m, W, KR, &v)) add(v);
       }
   }
   if (m <= 256) {

@@ -136,6 +136,10 @@ __device__ __forceinline__ void lds_dma4(const void *g, void *l) {
 
 // s_waitcnt with vmcnt <= n (n <= 63), expcnt and lgkmcnt unconstrained
 #define QG_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// Wait for this wave's LDS writes (and scalar loads) only: a bare s_barrier
+// does not wait for them, so LDS stores that other waves read after one are
+// waited for first.
+#define QG_WAIT_LGKMCNT0() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
 
 constexpr int kXcds = 8;  // L2 domains; workgroup ids are dealt round-robin over them
 

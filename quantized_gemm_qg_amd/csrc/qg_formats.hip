@@ -12,7 +12,8 @@
 // Kept in a translation unit of their own so the library's sources compile in
 // parallel.  Skinny instances: the spill-free (T, KR) of the host's
 // variant_ok; group 32, 64 or 128 for the bf16-activation formats, 32 for
-// the per-token MX format, 128 for W8A8.  Decode: (T, KR) = (1, 4), (1, 8).
+// the per-token MX format, 128 for W8A8.  Decode: (T, KR) = (1, 4), (1, 8);
+// wide decode: KR = 8, and 16 below 8-bit slices.
 #include <hip/hip_runtime.h>
 
 #include "qg_device.h"
@@ -115,6 +116,48 @@ hipError_t launch_decode_ext(const GemmArgs &a, int fmt, int group, const Varian
     case 11: return launch_decode_groups<11>(a, group, v, s);
     case 12: return launch_decode_groups<12>(a, group, v, s);
     case 13: return launch_decode_groups<13>(a, group, v, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int FMT, int GROUP>
+static hipError_t launch_decode_wide_x(const GemmArgs &a, const Variant &v, hipStream_t s) {
+  if (a.m < 2 || a.m > 16 || a.k % 512 != 0 || v.W < 1 || v.W > kMaxWaves || v.splits < 1 ||
+      v.splits * v.KR < a.k_blocks || (v.splits > 1 && (!a.partials || !a.counters)))
+    return hipErrorInvalidValue;
+  const unsigned groups = (unsigned)((a.n_tiles + v.W - 1) / v.W);
+  const size_t lds = (size_t)a.m * ((size_t)v.KR * 256 + 16);
+  auto launch = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(groups, v.splits), dim3(64 * v.W), lds, s, a);
+    return hipGetLastError();
+  };
+  if (v.KR == 8) return launch(decode_wide_kernel<FMT, GROUP, 8, 4>);
+  if constexpr (FmtTraits<FMT>::BITS < 8)  // (16 blocks of 8-bit slices in flight spill)
+    if (v.KR == 16) return launch(decode_wide_kernel<FMT, GROUP, 16, 4>);
+  return hipErrorInvalidValue;
+}
+
+template <int FMT>
+static hipError_t launch_decode_wide_groups(const GemmArgs &a, int group, const Variant &v, hipStream_t s) {
+  switch (group) {
+    case 32: return launch_decode_wide_x<FMT, 32>(a, v, s);
+    case 64: return launch_decode_wide_x<FMT, 64>(a, v, s);
+    case 128: return launch_decode_wide_x<FMT, 128>(a, v, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_wide_ext(const GemmArgs &a, int fmt, int group, const Variant &v, hipStream_t s) {
+  switch (fmt) {
+    case 7: return launch_decode_wide_groups<7>(a, group, v, s);
+    case 8: return launch_decode_wide_groups<8>(a, group, v, s);
+    case 9: return launch_decode_wide_groups<9>(a, group, v, s);
+    case 10: return launch_decode_wide_groups<10>(a, group, v, s);
+    case 11: return launch_decode_wide_groups<11>(a, group, v, s);
+    case 12: return launch_decode_wide_groups<12>(a, group, v, s);
+    case 13: return launch_decode_wide_groups<13>(a, group, v, s);
   }
   return hipErrorInvalidValue;
 }

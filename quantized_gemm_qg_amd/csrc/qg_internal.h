@@ -214,7 +214,8 @@ constexpr int64_t kMaxSplitCounters = (int64_t)(kSplitCounterBytes / 4);
 // One entry of the tuning table: a kernel variant and its tile parameters.
 struct Variant {
   int kind;    // 0 = skinny (16-row tiles, weights streamed to VGPRs), 1 = MX tiled (LDS),
-               // 2 = integer-format tiled (LDS, bf16 MFMA), 3 = decode (activations in LDS)
+               // 2 = integer-format tiled (LDS, bf16 MFMA), 3 = decode (activations in LDS),
+               // 4 = wide decode (waves along N over one K slice, activations in LDS)
   int T;       // n-tiles per wave
   int KR;      // k-blocks per wave
   int W;       // waves per workgroup (split of K inside the workgroup)
@@ -239,6 +240,10 @@ hipError_t launch_dense_mx(const GemmArgs &a, const qg_layer_desc &d, const Vari
 // staged in LDS, one workgroup per v.T n-tiles over all of K (v.W * v.KR * 128 >= K).
 hipError_t launch_decode_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                              hipStream_t s);
+// Wide decode form (kind 4; 2 <= m <= 16, K % 512 == 0): v.W waves along N
+// per workgroup, one K slice of v.KR blocks each, v.splits slices.
+hipError_t launch_decode_wide(const GemmArgs &a, const qg_layer_desc &d, const Variant &v, hipStream_t s);
+hipError_t launch_decode_wide_ext(const GemmArgs &a, int fmt, int group, const Variant &v, hipStream_t s);
 hipError_t launch_moe_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                           int64_t max_tiles, hipStream_t s);
 hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,

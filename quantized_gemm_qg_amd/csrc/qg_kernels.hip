@@ -283,6 +283,45 @@ hipError_t launch_decode_a16(const GemmArgs &a, const qg_layer_desc &d, const Va
   return hipErrorInvalidValue;
 }
 
+template <int FMT, int GROUP>
+static hipError_t launch_decode_wide_g(const GemmArgs &a, const Variant &v, hipStream_t s) {
+  if (a.m < 2 || a.m > 16 || a.k % 512 != 0 || v.W < 1 || v.W > kMaxWaves || v.splits < 1 ||
+      v.splits * v.KR < a.k_blocks || (v.splits > 1 && (!a.partials || !a.counters)))
+    return hipErrorInvalidValue;
+  const unsigned groups = (unsigned)((a.n_tiles + v.W - 1) / v.W);
+  const size_t lds = (size_t)a.m * ((size_t)v.KR * 256 + 16);
+  auto launch = [&](auto kern) -> hipError_t {
+    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(groups, v.splits), dim3(64 * v.W), lds, s, a);
+    return hipGetLastError();
+  };
+  if (v.KR == 8) return launch(decode_wide_kernel<FMT, GROUP, 8, 4>);
+  if (v.KR == 16) return launch(decode_wide_kernel<FMT, GROUP, 16, 4>);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_wide(const GemmArgs &a, const qg_layer_desc &d, const Variant &v, hipStream_t s) {
+  const int fmt = kernel_fmt(d);
+  if (fmt >= 7) return launch_decode_wide_ext(a, fmt, d.group_size, v, s);
+  const int g = d.group_size;
+  switch (fmt) {
+#define QG_WIDE_FMT(F)                                                 \
+  case F:                                                              \
+    if (g == 32) return launch_decode_wide_g<F, 32>(a, v, s);          \
+    if (g == 64) return launch_decode_wide_g<F, 64>(a, v, s);          \
+    if (g == 128) return launch_decode_wide_g<F, 128>(a, v, s);        \
+    return hipErrorInvalidValue;
+    QG_WIDE_FMT(0)
+    QG_WIDE_FMT(1)
+    QG_WIDE_FMT(2)
+    QG_WIDE_FMT(3)
+#undef QG_WIDE_FMT
+    case 5: return g == 32 ? launch_decode_wide_g<5, 32>(a, v, s) : hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_dense_a16(const GemmArgs &a, const qg_layer_desc &d, const Variant &v,
                             hipStream_t s) {
   return launch_dense(a, d, v, s);

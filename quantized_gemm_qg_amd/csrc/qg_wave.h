@@ -39,6 +39,44 @@ __device__ __forceinline__ void store_out(void *y, int64_t ldy, int otype, int64
   }
 }
 
+// Sum in split order of the n >= 1 fp32 partials p[0], p[stride], ...,
+// read with agent-scope loads (written by other workgroups): the loads go out
+// eight at a time, unconditionally (indices past n re-read the last partial,
+// which is not added), so the combine costs one memory round trip per eight
+// splits instead of one per split.
+__device__ __forceinline__ float sum_partials(const float *p, int64_t stride, int n) {
+  float sum = 0.f;
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = __hip_atomic_load(p + min(s0 + j, n - 1) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum = s0 + j < n ? sum + v[j] : sum;
+  }
+  return sum;
+}
+
+// sum_partials of four values at once (p + e * 64, e = 0..3): all 32 loads of
+// a group of eight splits go out before the first add.
+__device__ __forceinline__ f32x4 sum_partials4(const float *p, int64_t stride, int n) {
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    float v[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        v[j][e] = __hip_atomic_load(p + min(s0 + j, n - 1) * stride + e * 64, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sum[e] = s0 + j < n ? sum[e] + v[j][e] : sum[e];
+  }
+  return sum;
+}
+
 // ---------------------------------------------------------------------------
 // work-item decoding shared by the dense and MoE launches
 // ---------------------------------------------------------------------------
@@ -281,6 +319,7 @@ __device__ __forceinline__ void a16_wave(const GemmArgs &a, const uint8_t *wexp,
   // into a scalar.  (With more rows the MFMA against all-ones gives the sums
   // of 16 rows at once.)
   constexpr bool XS_LDS = XL && ER == 1 && !FP4;
+  static_assert(!XS_LDS || KR <= 8, "one row: a wave's K range spans at most its 64 lanes x 16 values");
   float xsum_lane = 0.f;
   if constexpr (XS_LDS) {
     // the wave's KR blocks are KR * 8 lanes' worth (KR * 128 values)
@@ -897,9 +936,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void skinny_kernel(GemmArgs a, int 
       for (int idx = threadIdx.x; idx < T * 256; idx += blockDim.x) {
         float s = 0.f;
         if (out_row(idx) < it.rows)
-          for (int sp = 0; sp < a.splits; ++sp)
-            s += __hip_atomic_load(a.partials + ((int64_t)sp * m_tiles * n_blocks + tile) * (T * 256) + idx,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s = sum_partials(a.partials + tile * (T * 256) + idx, m_tiles * n_blocks * (T * 256), a.splits);
         red[idx] = s;
       }
       if (threadIdx.x == 0)
@@ -991,6 +1028,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
       const int r = i / tail;
       *(u32x4 *)(dsm + r * xpitch + kk * 2 + (i - r * tail) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
+    QG_WAIT_LGKMCNT0();  // the zeros, before the barrier that publishes them
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1055,10 +1093,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   if (!last_flag) return;  // uniform across the workgroup
   for (int idx = threadIdx.x; idx < n_out; idx += blockDim.x) {
     const int t = idx / (rows * 16), rc = idx - t * rows * 16, r = rc / 16;
-    float sum = 0.f;
-    for (int sp = 0; sp < (int)gridDim.y; ++sp)
-      sum += __hip_atomic_load(a.partials + ((int64_t)sp * gridDim.x + blockIdx.x) * (T * 256) + t * 256 + rc,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const float sum = sum_partials(a.partials + (int64_t)blockIdx.x * (T * 256) + t * 256 + rc,
+                                   (int64_t)gridDim.x * (T * 256), (int)gridDim.y);
     const int col = (nt0 + t) * 16 + (idx & 15);
     if (col < a.n && nt0 + t < a.n_tiles) store_out(a.y, a.ldy, a.otype, r, col, sum);
   }
@@ -1066,5 +1102,109 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
     __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+
+
+// ---------------------------------------------------------------------------
+// dense decode, wide form (2 .. 16 rows): the workgroup's waves run along N
+// ---------------------------------------------------------------------------
+//
+// The form above copies its rows over the whole K range of the workgroup, for
+// every column tile: at 16 rows and K = 14336 that is 459 KB per workgroup,
+// 117 MB over the launch against 30.5 MB of weights.  Here the W waves of a
+// workgroup take W consecutive n-tiles (one each) over one K slice of KR
+// blocks, and the rows' slice is copied into LDS once for all of them:
+// gridDim.y = ceil(K / (KR * 128)) slices, each workgroup's activation copy
+// rows * KR * 256 bytes (4096 x 14336 at 16 rows: 7.3 MB in all).  The
+// waves copy the slice together and issue their first weight loads, then wait
+// for their copies and meet at a barrier; each wave then runs the decode wave
+// body on its n-tile (pipelined weight loads) and writes its 16 x 16 tile:
+// directly with one slice, else as an fp32 partial, combined in slice order
+// by the last workgroup of the column group to arrive (per-group arrival
+// counter, reset by that workgroup).  Requires K % 512 == 0.
+template <int FMT, int GROUP, int KR, int ER>
+__global__ __launch_bounds__(kMaxWaves * 64) void decode_wide_kernel(GemmArgs a) {
+  constexpr int BITS = FmtTraits<FMT>::BITS;
+  constexpr bool ZP = FmtTraits<FMT>::ZP;
+  constexpr int KS = KR * 128;       // K values of one slice
+  constexpr int XP = KS * 2 + 16;    // LDS bytes per row (padded: bank spread)
+  constexpr int PER_ROW = KS / 512;  // 64-lane copies per row
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  __shared__ int last_flag;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int q = lane >> 4, r16 = lane & 15;
+  const int rows = ER == 1 ? 1 : a.m;
+  const int nt0 = blockIdx.x * nwaves + wave;  // this wave's n-tile (past N: clamped loads, no stores)
+  const int split = blockIdx.y;
+  const int ks0 = split * KS;
+  const int kk = min(KS, a.k - ks0);           // a multiple of 512
+
+  // 1. the rows' K slice -> LDS (zeros past K), the copies shared out over
+  //    the waves
+  for (int i = wave; i < rows * PER_ROW; i += nwaves) {
+    const int r = i / PER_ROW, c0 = (i % PER_ROW) * 512;
+    if (c0 < kk)  // wave-uniform
+      lds_dma16((const uint16_t *)a.x + (int64_t)r * a.ldx + ks0 + c0 + lane * 8, dsm + r * XP + c0 * 2);
+    else
+      *(u32x4 *)(dsm + r * XP + c0 * 2 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+  QG_WAIT_LGKMCNT0();  // the zeros, before the barrier that publishes them
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. the wave's n-tile over the slice: its first weight loads go out, then
+  //    it waits for its own copies (issued before them) and meets the other
+  //    waves at a barrier, after which every copy of the slice has landed
+  f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  const uint16_t *xrow = (const uint16_t *)(dsm + min(r16, rows - 1) * XP);
+  constexpr int ISSUED = FmtTraits<FMT>::EXT ? KR : a16_pipe_depth<true, KR>();
+  auto x_ready = [&]() {
+    QG_WAIT_VMCNT(ISSUED);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  if constexpr (FmtTraits<FMT>::EXT)
+    a16x_wave<FMT, GROUP, 1, KR, true, ER, decltype(x_ready)>(a, a.wbase, xrow, nt0, split * KR, acc, x_ready,
+                                                              ks0);
+  else
+    a16_wave<BITS, ZP, GROUP, 1, KR, true, ER, decltype(x_ready), FMT == 5>(a, a.wbase, xrow, nt0, split * KR,
+                                                                            acc, x_ready, ks0);
+
+  // 3. store: element (e, lane) is row 4 (lane / 16) + e, column lane % 16 of the tile
+  const int col = nt0 * 16 + r16;
+  const bool col_ok = nt0 < a.n_tiles && col < a.n;
+  if (gridDim.y == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * q + e;
+      if (r < rows && col_ok) store_out(a.y, a.ldy, a.otype, r, col, acc[0][e]);
+    }
+    return;
+  }
+  float *part = a.partials + (((int64_t)split * gridDim.x + blockIdx.x) * nwaves + wave) * 256;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    __hip_atomic_store(part + e * 64 + lane, acc[0][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(a.counters + blockIdx.x, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    last_flag = (prev == gridDim.y - 1);
+  }
+  __syncthreads();
+  if (!last_flag) return;  // uniform across the workgroup
+  const f32x4 sum = sum_partials4(a.partials + ((int64_t)blockIdx.x * nwaves + wave) * 256 + lane,
+                                  (int64_t)gridDim.x * nwaves * 256, (int)gridDim.y);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int r = 4 * q + e;
+    const float v = sum[e];  // (element copied out: see the bit-cast note in a16_wave)
+    if (r < rows && col_ok) store_out(a.y, a.ldy, a.otype, r, col, v);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.counters + blockIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 }  // namespace qg

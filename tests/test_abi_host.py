@@ -331,6 +331,14 @@ def test_dispatch_table_covers_k():
                 if wt != qg.W_MXFP4:  # the group row sums of X live behind the counter prefix
                     assert qg.gemm_workspace_size(w, m) >= 65536 + (k // g) * m * 4
                 continue
+            if "decode_wide" in s:  # K slices of KR blocks, W column tiles per workgroup
+                assert wt != qg.W_MXFP4 and 2 <= m <= 16 and k % 512 == 0, s
+                KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
+                kb = -(-k // 128)
+                assert S == -(-kb // KR) and 1 <= W <= 16, s
+                if S > 1:  # arrival counters (prefix) and partials live in the workspace
+                    assert qg.gemm_workspace_size(w, m) >= 65536 + S * -(-n // (16 * W)) * W * 256 * 4
+                continue
             if "decode" in s:  # activations in LDS, one workgroup over all of K (or of a split)
                 assert wt != qg.W_MXFP4 and m <= 16 and k % 512 == 0, s
                 vals = [int(v) for v in re.findall(r"=(\d+)", s)]

@@ -156,7 +156,7 @@ def test_decode_full_size(wtype, nk):
     n, k = nk
     print(f"decode wtype={wtype} N={n} K={k}", flush=True)
     layer = Layer(wtype, n, k, 128, seed=11)
-    for m in (1, 4, 16):
+    for m in (1, 4, 8, 16):
         _check(layer, Acts(False, m, k, seed=20 + m), m)
 
 
@@ -354,6 +354,56 @@ def test_decode_kernel_identity_rows_exact(override, wtype, group):
     y = run_gemm(layer, acts, m, qg.O_F32).cpu().numpy()
     for i, kk in enumerate(ks):
         assert np.array_equal(y[i].astype(np.float64), wdq[:, kk]), kk
+
+
+# wide decode form: "W,KR" = column tiles (waves) per workgroup, k-blocks per
+# K slice
+WIDE_VARIANTS = ["8,8", "8,16", "16,8", "3,16"]
+
+
+@pytest.mark.parametrize("wtype", A16)
+@pytest.mark.parametrize("group", [32, 128])
+def test_decode_wide_variants(override, wtype, group):
+    """The wide decode form.  N = 200 is 13 n-tiles (a partial last column
+    group, a ragged last tile); K = 2560 is 20 k-blocks (KR = 8: three slices,
+    the last half full; KR = 16: two, the last short), K = 1024 one slice at
+    KR = 8 (direct stores), K = 4096 two full slices at KR = 16.  Rows 2, 7
+    and 16."""
+    for k in (2560, 1024, 4096):
+        layer = Layer(wtype, 200, k, group, seed=wtype * 7 + group + k)
+        for tune in WIDE_VARIANTS:
+            override("QG_DECODE_WIDE", tune)
+            for m in (2, 7, 16):
+                d = qg.describe_dispatch(layer.w, m)
+                if tune.endswith(",16") and group == 32 and k != 4096:
+                    # a slice's 64 group scales must divide the row's padded
+                    # groups (32 at K = 1024, 96 at K = 2560)
+                    assert "a16_decode_wide" not in d, d
+                    continue
+                assert "a16_decode_wide" in d, (tune, m, d)
+                print(f"  wide {tune} k={k} m={m}: {d}", flush=True)
+                _check(layer, Acts(False, m, k, seed=m + group + k), m)
+
+
+def test_decode_wide_split_reuses_workspace(override):
+    """Wide form over several K slices: the per-group arrival counters return
+    to zero, so one workspace (zero-filled once) serves consecutive calls of
+    different row counts."""
+    override("QG_DECODE_WIDE", "8,8")
+    n, k = 200, 3072
+    layer = Layer(qg.W_UINT4, n, k, 128, seed=78)
+    wdq = layer.wdq()
+    ws_bytes = max(qg.gemm_workspace_size(layer.w, m) for m in (16, 5))
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    for call, m in enumerate((16, 5, 16)):
+        assert "splits=3" in qg.describe_dispatch(layer.w, m)
+        acts = Acts(False, m, k, seed=200 + call)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        qg.gemm(layer.w, acts.x, None, m, k, y, qg.O_F32, n, ws, ws_bytes)
+        torch.cuda.synchronize()
+        e = err(y, oracle.gemm(acts.xdq, wdq))
+        print(f"  call {call} m={m} err={e:.3e}", flush=True)
+        assert e <= TOL_F32, (call, e)
 
 
 # ---------------------------------------------------------------------------

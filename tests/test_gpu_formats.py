@@ -81,6 +81,26 @@ def test_wna16_dispatch():
         assert ("tiled" in big) == (wtype == qg.W_E0M3), (wtype, big)
 
 
+@pytest.mark.parametrize("group", [32, 128])
+@pytest.mark.parametrize("wtype", A16_EXT)
+def test_wna16_decode_wide(override, wtype, group):
+    """The wide decode form (column tiles along the workgroup's waves, K in
+    slices): N = 200 (a partial last column group), K = 2560 (20 k-blocks:
+    three slices of 8, the last half full, or two of 16, the last short);
+    16-block slices only below 8-bit codes."""
+    layer = Layer(wtype, 200, 2560, group, seed=90 + wtype + group)
+    bits8 = wtype in (qg.W_INT8, qg.W_UINT8, qg.W_E0M7, qg.W_FP8)
+    for tune in ("8,8", "8,16", "5,8"):
+        override("QG_DECODE_WIDE", tune)
+        for m in (2, 16):
+            d = qg.describe_dispatch(layer.w, m)
+            if tune == "8,16" and (bits8 or group == 32):  # (g32: 64 scales per slice, 96 per row)
+                assert "a16_decode_wide" not in d, d
+                continue
+            assert "a16_decode_wide" in d, (tune, m, d)
+            _check_a16(layer, m, seed=95 + m)
+
+
 def test_wna16_long_k_decode_split():
     """INT8 and INT2 at the long-K decode shape (N = 4096, K = 14336, M = 1)."""
     for wtype in (qg.W_INT8, qg.W_UINT2):
