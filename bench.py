@@ -316,7 +316,7 @@ def cpu_baseline(oracle, shapes, budget_s=15.0):
 # the traffic summary under profiles/).  Used only while the kernel sources
 # still hash to what was measured.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_w4a16_m1_hbm_traffic.md")
-KERNEL_SOURCES = ["qg_kernels.hip", "qg_wave.h", "qg_device.h", "qg_internal.h"]
+KERNEL_SOURCES = ["qg_kernels.hip", "qg_wave.h", "qg_device.h", "qg_internal.h", "qg_formats.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -347,7 +347,9 @@ def measured_traffic():
 def pmc_workload(qg, synth, torch):
     """A short run for rocprofv3 counter passes: qg_stream_copy of 256 MiB
     (three launches, the calibration), then the dominant decode kernel (dense
-    W4A16 UINT4 + zp, M=1, N=4096, K=14336) 20 times on rotating weight copies."""
+    W4A16 UINT4 + zp, M=1, N=4096, K=14336) 20 times on rotating weight
+    copies, then the 16-row decode GEMMs (UINT4 + zp and INT3, both decode
+    shapes) 20 times each."""
     n_copy = 256 << 20
     src = torch.empty(n_copy, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
@@ -364,6 +366,42 @@ def pmc_workload(qg, synth, torch):
     torch.cuda.synchronize()
     print(f"pmc workload: copy {n_copy} B x3, decode N=4096 K=14336 M=1 x20 "
           f"({L.bytes} algorithmic bytes per launch), source hash {kernel_source_hash()}", flush=True)
+    del L
+    for wtype, name in ((qg.W_UINT4, "uint4_zp"), (qg.W_INT3, "int3")):
+        for i, (n, k) in enumerate([(14336, 4096), (4096, 14336)]):
+            L = DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=30 + i)
+            x, _, _ = make_x(qg, synth, torch, False, 16, k, seed=56)
+            f = dense_launcher(qg, torch, L, x, None, 16)
+            for j in range(20):
+                f(j)
+            torch.cuda.synchronize()
+            print(f"pmc workload: decode {name} N={n} K={k} M=16 x20 ({L.bytes} algorithmic weight bytes, "
+                  f"{16 * k * 2} activation bytes, {16 * n * 2} output bytes per launch): "
+                  f"{qg.describe_dispatch(L.ws[0], 16)}", flush=True)
+            del L
+
+
+def bench_decode_rows(qg, synth, torch, shapes, layers=None):
+    """Dense W4A16 decode (UINT4 + zp and INT3, group 128) at M = 1, 4, 8, 16
+    on both decode shapes: per-GEMM time, weight GB/s and the M / M=1 time
+    ratio.  `layers`: the UINT4 weights already on the device, if any."""
+    out = {}
+    for wtype, name in ((qg.W_UINT4, "uint4_zp"), (qg.W_INT3, "int3")):
+        for i, (n, k) in enumerate(shapes):
+            L = (layers[i] if wtype == qg.W_UINT4 and layers is not None
+                 else DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=(0 if wtype == qg.W_UINT4 else 30) + i))
+            t1 = None
+            for mm in (1, 4, 8, 16):
+                x, _, _ = make_x(qg, synth, torch, False, mm, k, seed=40 + mm)
+                t = timed(torch, dense_launcher(qg, torch, L, x, None, mm), 100, 10)
+                t1 = t if mm == 1 else t1
+                out[f"decode_{name}_M{mm}_N{n}_K{k}"] = {
+                    "us": round(t * 1e3, 2), "weight_GBs": round(L.bytes / (t * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "vs_M1": round(t / t1, 3), "dispatch": qg.describe_dispatch(L.ws[0], mm)}
+            del L
+        print(f"[bench] decode rows {name} done", file=sys.stderr, flush=True)
+    return out
 
 
 def cold_copies(qg, torch, desc, codes, sc, nbytes):
@@ -559,6 +597,8 @@ def main():
                     help="only the MoE configurations at T=4096 (for profiling the grouped kernels)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only the plain stream-read ceiling at one decode GEMM's weight bytes")
+    ap.add_argument("--decode-rows", action="store_true",
+                    help="only the dense W4A16 decode GEMMs at M = 1, 4, 8, 16 (UINT4 + zp and INT3)")
     ap.add_argument("--pmc-workload", action="store_true",
                     help="only run the copy calibration + decode kernel for rocprofv3 counter passes")
     args = ap.parse_args()
@@ -591,8 +631,11 @@ def main():
     if args.ceiling:
         print(json.dumps(bench_stream_ceiling(qg, torch)), flush=True)
         return
-
     shapes = [(14336, 4096), (4096, 14336)]
+    if args.decode_rows:
+        print(json.dumps(bench_decode_rows(qg, synth, torch, shapes)), flush=True)
+        return
+
     print(f"[bench] preparing decode weights {shapes} x{ROTATE} copies", file=sys.stderr, flush=True)
     layers = [DenseWeights(qg, synth, torch, qg.W_UINT4, n, k, 128, seed=i) for i, (n, k) in enumerate(shapes)]
     xs = [make_x(qg, synth, torch, False, 1, k, seed=10 + i) for i, (_, k) in enumerate(shapes)]
@@ -660,17 +703,7 @@ def main():
             "dispatch": [t[0] for t in tuned], "cold_cache_us": [round(t[1], 2) for t in tuned]}
         print(f"[bench] autotuned decode step: {extra['decode_step_autotuned']}", file=sys.stderr, flush=True)
         qg.autotune_reset()
-        for wtype, name in ((qg.W_UINT4, "uint4_zp"), (qg.W_INT3, "int3")):
-            for i, (n, k) in enumerate(shapes):
-                L = layers[i] if wtype == qg.W_UINT4 else DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=30 + i)
-                for mm in (1, 4, 16):
-                    x, _, _ = make_x(qg, synth, torch, False, mm, k, seed=40 + mm)
-                    t = timed(torch, dense_launcher(qg, torch, L, x, None, mm), 100, 10)
-                    extra[f"decode_{name}_M{mm}_N{n}_K{k}"] = {
-                        "us": round(t * 1e3, 2), "weight_GBs": round(L.bytes / (t * 1e-3) / 1e9, 1),
-                        "hbm_frac": round(L.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                        "dispatch": qg.describe_dispatch(L.ws[0], mm)}
-            print(f"[bench] extra decode {name} done", file=sys.stderr, flush=True)
+        extra.update(bench_decode_rows(qg, synth, torch, shapes, layers))
         # MXFP4 weights x bf16 activations at the decode shapes
         for i, (n, k) in enumerate(shapes):
             r = synth.rng(70 + i, 1)
@@ -694,9 +727,9 @@ def main():
                     "dispatch": qg.describe_dispatch(wts[0], mm)}
             del bufs, wts
         print(f"[bench] extra MXFP4 x bf16 decode done", file=sys.stderr, flush=True)
-        # MXFP4 weights x MX activations at the decode shapes: W4A8 (MXFP8) on
-        # the MX skinny kernel, W4A4 (MXFP4) widened to e4m3 in the workspace
-        # and then the same kernel (the widening launch is inside the timing)
+        # MXFP4 weights x MX activations at the decode shapes: W4A8 (MXFP8) and
+        # W4A4 (MXFP4) on the MX skinny kernel, which widens W4A4's e2m1
+        # activation fragments to e4m3 in registers (one launch per GEMM)
         for i, (n, k) in enumerate(shapes):
             codes, sc, _ = synth.mx_weights(synth.rng(70 + i, 1), n, k)
             wbytes = weight_bytes(n, k, 4, 32, False, 1)
