@@ -70,8 +70,8 @@ class DenseWeights:
         self.std = (codes, sc, zp)
         desc = qg.layer_desc(wtype, n, k, group)
         size = qg.packed_size(desc)
-        bits = 3 if wtype in (qg.W_INT3, qg.W_UINT3) else 4
-        self.bytes = weight_bytes(n, k, bits, group, zp is not None, 1 if wtype == qg.W_MXFP4 else 2)
+        self.bytes = weight_bytes(n, k, synth.WTYPE_BITS[wtype], group, zp is not None,
+                                  1 if wtype == qg.W_MXFP4 else 2)
         if copies is None:  # cold: the rotation spans twice the MALL
             copies = max(2, -(-2 * MALL_BYTES // self.bytes))
         # one host repack; the other copies are device copies of the packed bytes
@@ -404,6 +404,67 @@ def bench_decode_rows(qg, synth, torch, shapes, layers=None):
     return out
 
 
+def bench_formats(qg, synth, torch, shapes):
+    """The further weight and activation formats at the decode shapes: WnA16
+    integer and e4m3 weights (group 128, bf16 activations) at M = 1 and 16;
+    W8A8 block FP8 and MXFP4 x per-token FP8 at M = 1, 16 and 256 (both on
+    the skinny kernel).  Weight bytes per GEMM / time, and TFLOPS."""
+    out = {}
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def run(name, ws, x, xs, m, n, k, nbytes):
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        wsb = qg.gemm_workspace_size(ws[0], m)
+        wsp = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+        t = timed(torch, lambda j: qg.gemm(ws[j % len(ws)], x, xs, m, k, y, qg.O_BF16, n, wsp, wsb, stream),
+                  100, 10)
+        out[name] = {"us": round(t * 1e3, 2), "weight_GBs": round(nbytes / (t * 1e-3) / 1e9, 1),
+                     "hbm_frac": round(nbytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "TFLOPS": round(2.0 * m * n * k / (t * 1e-3) / 1e12, 2),
+                     "dispatch": qg.describe_dispatch(ws[0], m)}
+
+    for wtype, name in ((qg.W_INT8, "int8"), (qg.W_UINT2, "uint2_zp"), (qg.W_INT1, "int1"), (qg.W_FP8, "e4m3")):
+        for i, (n, k) in enumerate(shapes):
+            L = DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=90 + i)
+            for mm in (1, 16):
+                x, _, _ = make_x(qg, synth, torch, False, mm, k, seed=40 + mm)
+                run(f"{name}_bf16_M{mm}_N{n}_K{k}", L.ws, x, None, mm, n, k, L.bytes)
+            del L
+        print(f"[bench] formats {name} done", file=sys.stderr, flush=True)
+    for i, (n, k) in enumerate(shapes):
+        # W8A8: e4m3 weights, fp32 scale per 128 x 128 block; e4m3 activations,
+        # fp32 scale per row and 128 K
+        codes, sc = synth.fp8_block_weights(synth.rng(95 + i, 1), n, k)
+        desc = qg.layer_desc(qg.W_FP8, n, k, 128, atype=qg.A_FP8_BLOCK)
+        first = torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda")
+        bufs, ws = [first], [qg.preprocess(desc, codes, sc, None, first)]
+        for _ in range(ROTATE - 1):
+            bufs.append(first.clone())
+            ws.append(qg.weight_bind(desc, bufs[-1], first.numel()))
+        nbytes = n * k + sc.size * 4
+        for mm in (1, 16, 256):
+            c, s_ = synth.fp8_activations(synth.rng(96, mm), mm, k, 128)
+            run(f"w8a8_block_fp8_M{mm}_N{n}_K{k}", ws, torch.from_numpy(c).cuda(), torch.from_numpy(s_).cuda(),
+                mm, n, k, nbytes)
+        del bufs, ws
+        # MXFP4 weights x FP8 activations with one fp32 scale per row
+        mc, msc, _ = synth.mx_weights(synth.rng(97 + i, 1), n, k)
+        desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=qg.A_FP8_TOKEN)
+        first = torch.empty(qg.packed_size(desc), dtype=torch.uint8, device="cuda")
+        bufs, ws = [first], [qg.preprocess(desc, mc, msc, None, first)]
+        for _ in range(ROTATE - 1):
+            bufs.append(first.clone())
+            ws.append(qg.weight_bind(desc, bufs[-1], first.numel()))
+        nbytes = weight_bytes(n, k, 4, 32, False, 1)
+        for mm in (1, 16, 256):
+            c, s_ = synth.fp8_activations(synth.rng(98, mm), mm, k, None)
+            run(f"w4a8_fp8_token_M{mm}_N{n}_K{k}", ws, torch.from_numpy(c).cuda(), torch.from_numpy(s_).cuda(),
+                mm, n, k, nbytes)
+        del bufs, ws
+    print(f"[bench] formats W8A8 / per-token W4A8 done", file=sys.stderr, flush=True)
+    return out
+
+
 def cold_copies(qg, torch, desc, codes, sc, nbytes):
     """Packed copies of one weight whose rotation spans twice the MALL (each
     launch reads its weights from HBM): one host repack, device copies."""
@@ -597,6 +658,8 @@ def main():
                     help="only the MoE configurations at T=4096 (for profiling the grouped kernels)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only the plain stream-read ceiling at one decode GEMM's weight bytes")
+    ap.add_argument("--formats", action="store_true",
+                    help="only the further formats (WnA16 integer / e4m3 weights, W8A8, per-token W4A8)")
     ap.add_argument("--decode-rows", action="store_true",
                     help="only the dense W4A16 decode GEMMs at M = 1, 4, 8, 16 (UINT4 + zp and INT3)")
     ap.add_argument("--pmc-workload", action="store_true",
@@ -634,6 +697,9 @@ def main():
     shapes = [(14336, 4096), (4096, 14336)]
     if args.decode_rows:
         print(json.dumps(bench_decode_rows(qg, synth, torch, shapes)), flush=True)
+        return
+    if args.formats:
+        print(json.dumps(bench_formats(qg, synth, torch, shapes)), flush=True)
         return
 
     print(f"[bench] preparing decode weights {shapes} x{ROTATE} copies", file=sys.stderr, flush=True)
@@ -704,6 +770,7 @@ def main():
         print(f"[bench] autotuned decode step: {extra['decode_step_autotuned']}", file=sys.stderr, flush=True)
         qg.autotune_reset()
         extra.update(bench_decode_rows(qg, synth, torch, shapes, layers))
+        extra["formats"] = bench_formats(qg, synth, torch, shapes)
         # MXFP4 weights x bf16 activations at the decode shapes
         for i, (n, k) in enumerate(shapes):
             r = synth.rng(70 + i, 1)

@@ -125,7 +125,8 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
  *   dequantize-and-compute path; e0m codes, section "Quantization support",
  *   hold the values of INT4 without -8 / INT8 without -128 and are stored as
  *   those integers; the LDS-tiled large-M kernels serve the 4- and 3-bit
- *   formats and E0M3, the others run the 16-row skinny kernel at every M);
+ *   formats and E0M3; the others run the decode kernels up to 16 rows when
+ *   K % 512 == 0 and the 16-row skinny kernel otherwise);
  *   MXFP4, E8M0 scales, FP8_TOKEN activations, group 32 (W4A8 with per-token
  *   FP8 activations, section "End to end": the scaled MFMA with unit
  *   activation block scales, each output row times its row's fp32 scale;

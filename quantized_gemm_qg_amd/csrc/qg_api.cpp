@@ -360,6 +360,16 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   // wherever N gives enough workgroups; rows that do not fit LDS over all of
   // K take a K split in two (4096 x 14336 at M = 8: 14.7 against 20.8 us on
   // the skinny kernel), else the skinny kernel.
+  // 1-, 2- and 8-bit integer and e4m3 weights run one n-tile per decode
+  // workgroup, which copies its rows for every tile: from 8 rows (9 for the
+  // 8-bit slices) the wide form wins (14336 x 4096 at M = 16: UINT2 10.8
+  // against 19.9 us, INT8 18.5 against 24.8 us; at M = 8 UINT2 10.3 against
+  // 11.2 us, INT8 17.9 against 17.0 us)
+  if (ext_a16(d)) {
+    const int f = kernel_fmt(d);
+    const bool bits8 = f == 7 || f == 8 || f == 13;
+    if (m >= (bits8 ? 9 : 8) && decode_wide_fits(w, m, bits8 ? 4 : 8, 8, v)) return true;
+  }
   static const int pairs_one[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
   static const int pairs_rows[][2] = {{2, 4}, {1, 8}, {2, 8}, {4, 2}};
   static const int pairs_ext[][2] = {{1, 8}, {1, 4}, {1, 4}, {1, 4}};
