@@ -271,7 +271,7 @@ static int mx_tile_cols(int64_t n, int64_t m, int bm) {
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   if (w.desc.k % 128 != 0 || !has_tiled(w.desc)) return false;
   if (ov().tiled_off) return false;
-  const bool mx = mx_a8(w.desc) || mx_a4(w.desc);
+  const bool mx = mx_tiled_fmt(w.desc);
   // the integer-format kernel addresses X and the codes with 32-bit offsets
   if (!mx && ((uint64_t)m * w.desc.k * 2 >= (1ull << 31) ||
               (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31)))
@@ -403,7 +403,7 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
 // variant fixed by (N, K) sums its waves' and splits' partials in index order.
 // Tile widths do not change any element's order; they are fixed anyway.
 static Variant select_dense_invariant(const qg_weight &w) {
-  const bool mx = mx_a8(w.desc) || mx_a4(w.desc);  // (W4A4 layers have K % 128 == 0)
+  const bool mx = mx_tiled_fmt(w.desc);  // (W4A4 layers have K % 128 == 0)
   if (has_tiled(w.desc) && w.desc.k % 128 == 0 &&
       (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
     const int bn = mx ? 256 : a16_tiled_bn();
@@ -453,7 +453,7 @@ static bool same_variant(const Variant &a, const Variant &b) {
 // Whether v can serve m rows of w (a table entry serves every M of its bucket)
 static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
   const qg_layer_desc &d = w.desc;
-  const bool mx = mx_a8(d) || mx_a4(d);
+  const bool mx = mx_tiled_fmt(d);
   if (mx_a4(d) && v.kind != 1 && v.kind != 0) return false;  // W4A4: the MX tiled or MX skinny kernel
   switch (v.kind) {
     case 0:
@@ -571,7 +571,7 @@ static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
   if (d.k % 128 != 0 || d.num_experts > kMaxExperts || !has_tiled(d)) return 0;
-  const bool mx = mx_a8(d);
+  const bool mx = mx_a8(d) || mx_tok(d);  // one byte per activation element
   // 32-bit offsets inside the kernels
   if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
       (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31))
@@ -652,7 +652,7 @@ static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_c
   if (min_rows <= 0) return 0;
   uint64_t b = moe_list_bytes(moe_tiles_cap(w, pairs, min_rows));
   if (moe_small_tiles(w, pairs, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
-  if (!mx_a8(w.desc)) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
+  if (!mx_a8(w.desc) && !mx_tok(w.desc)) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
   return b;
 }
 
@@ -830,7 +830,7 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
   }
   if (v.kind == 1) {
     if (L.a4) a.ldx = ldx / 2;  // the kernel addresses e2m1 rows in bytes
-    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), scratch, stream, L.a4);
+    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), scratch, stream, L.a4, mx_tok(d));
   }
   if (L.a4) {
     // the MX skinny kernel widens the e2m1 fragments to e4m3 in registers
@@ -1058,8 +1058,8 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     a.tiles = tiles;
     a.group_m = moe_group_m();
     void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
-    if (L.is_mx)
-      he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream, L.a4);
+    if (L.mx_pack)
+      he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream, L.a4, mx_tok(d));
     else
       he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
                             xs, true, stream);
@@ -1067,13 +1067,13 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     if (small) {
       // the MX small tiles have 64 rows (QG_MOE_SMALL_BM applies to the
       // integer formats; the list capacity covers either)
-      const int sbm = L.is_mx ? kMoeSmallTileRows : moe_small_bm();
+      const int sbm = L.mx_pack ? kMoeSmallTileRows : moe_small_bm();
       he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
                             (int32_t)cap_s, tiles_s, stream);
       if (he != hipSuccess) return hip_status(he);
       a.tiles = tiles_s;
       a.group_m = 1;
-      he = L.is_mx ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4)
+      he = L.mx_pack ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4, mx_tok(d))
                    : launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
       return hip_status(he);  // every expert with rows is covered
     }
@@ -1101,12 +1101,12 @@ extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_to
   char skinny[96];
   describe_variant(v, L, w->k_blocks, skinny, sizeof skinny);
   const int min_rows = pairs > 0 ? moe_tiled_min_rows(wk, pairs, pairs) : 0;
-  const char *fam = L.is_mx ? "mx" : "a16";
+  const char *fam = L.mx_pack ? "mx" : "a16";
   if (min_rows <= 0)
     snprintf(buf, buf_bytes, "%s for every expert", skinny);
   else if (moe_small_tiles(wk, pairs, min_rows))
     snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
-             kMoeTileRows, min_rows, fam, L.is_mx ? kMoeSmallTileRows : moe_small_bm());
+             kMoeTileRows, min_rows, fam, L.mx_pack ? kMoeSmallTileRows : moe_small_bm());
   else
     snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s below", fam, kMoeTileRows, min_rows,
              skinny);
@@ -1196,7 +1196,7 @@ extern "C" qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, 
 }
 
 static void describe_variant(const Variant &v, const Layout &L, int k_blocks, char *buf, uint64_t buf_bytes) {
-  const bool mx = L.is_mx;
+  const bool mx = L.mx_pack;  // (the MX tiled kernel also serves per-token FP8 activations)
   // skinny-kernel family: MX (also per-token FP8 activations), W8A8, A16
   const char *fam = L.mx_pack ? "mx" : L.f8 ? "f8" : "a16";
   if (v.kind == 3)
@@ -1221,7 +1221,7 @@ static void describe_variant(const Variant &v, const Layout &L, int k_blocks, ch
 // (K % 128 == 0).
 static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> *out) {
   const qg_layer_desc &d = w.desc;
-  const bool mx = mx_a8(d) || mx_a4(d);
+  const bool mx = mx_tiled_fmt(d);
   auto add = [&](const Variant &v) {
     for (const Variant &u : *out)
       if (same_variant(u, v)) return;
@@ -1311,7 +1311,7 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (!aligned16(x) || !aligned16(y) || x_pitch(L, ldx) % 16 != 0 || (L.a4 && (ldx & 1)) || (ldy * yel) % 4 != 0 ||
       ((uintptr_t)ws & 255u) != 0)
     return QG_ERR_ALIGNMENT;
-  if (L.is_mx && (uint64_t)m * x_pitch(L, ldx) >= (1ull << 32)) return QG_ERR_UNSUPPORTED;
+  if (L.mx_pack && (uint64_t)m * x_pitch(L, ldx) >= (1ull << 32)) return QG_ERR_UNSUPPORTED;
   if (flush && (flush_bytes % 16 != 0 || !aligned16(flush))) return QG_ERR_ALIGNMENT;
   std::vector<Variant> cand;
   tune_candidates(*w, m, &cand);

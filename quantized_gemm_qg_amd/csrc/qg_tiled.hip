@@ -38,6 +38,11 @@
 // workgroup barrier.  Inside a K step the next row
 // block's LDS reads are scheduled ahead of the current block's 8 MFMAs.
 //
+// Per-token FP8 activations (RS; the announcement's "End to end" section
+// serves W4A8 with them): e4m3 A operands under a unit block scale (code
+// 127), no SA copies, and each output row multiplied by its row's fp32 scale
+// in the epilogue.
+//
 // W4A4 (A4: MXFP4 activations, the announcement's "W8A8 / W4A8 / W4A4"
 // section): the same kernel with e2m1 A operands.  A row holds 64 bytes per K
 // step, a lane's operand is the 16 bytes of K 32q .. 32q + 31 (the layout the
@@ -105,8 +110,9 @@ struct MxCfg {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4, bool RS>
 __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
+  static_assert(!RS || (!SAR && !A4), "per-token scales: e4m3 rows, no activation scale ring");
   using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
@@ -156,12 +162,12 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   // waves copy, every fourth step, the 16 bytes of 4 steps of one row per
   // lane straight from the row-major scales into the SA ring.
   constexpr bool SA_X4 = !SAR && !MOE && BM == 256;
-  const bool sa_wave = SA_X4 ? wave == 0 : wave < C::SA_WAVES;
+  const bool sa_wave = !RS && (SA_X4 ? wave == 0 : wave < C::SA_WAVES);
   const int64_t m_pad = ((int64_t)a.m + 255) & ~(int64_t)255;  // regrouped row stride
   const int64_t sa_row = SA_X4 ? (int64_t)tr.base + 4 * lane : tr.x(a, (sa_wave ? wave : 0) * 64 + lane);
   // per K step: + 4 bytes (rows of kq bytes) or + 4 m_pad bytes (dense, regrouped by step)
   const bool sa_rows = MOE || SAR;
-  const uint8_t *sa_src = sa_rows ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
+  const uint8_t *sa_src = RS ? nullptr : sa_rows ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
   const int64_t sa_step = sa_rows ? 4 : 4 * m_pad;
   // SW: copy p (by wave p < SW_PIECES) moves the 256-B units of n-tiles
   // 4p .. 4p + 3 of the tile for K steps 4j .. 4j + 3 (unit of n-tile nt at
@@ -246,7 +252,9 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
         af = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
       }
-      if constexpr (SAR)
+      if constexpr (RS)
+        asc = 127;  // unit scale: the row's fp32 scale is applied to the output
+      else if constexpr (SAR)
         asc = smem[C::OFF_SAR + ((kb >> 2) & 1) * C::SAR_SLOT + 16 * row + 4 * (kb & 3) + q];
       else
         asc = st[C::A + C::B + 4 * row + q];
@@ -296,12 +304,31 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     if (kb + 3 < kbs) step(kb + 3, std::integral_constant<int, 3>{});
   }
 
+  // per-token FP8: the fp32 scales of the lane's output rows (4 (lane / 16)
+  // + e of each 16-row block; rows past the tile read the last row's)
+  float rsc[RS ? C::MB : 1][4];
+  if constexpr (RS) {
+#pragma unroll
+    for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        rsc[i][e] = ((const float *)a.x_scales)[tr.x(a, wm * (BM / WM) + i * 16 + 4 * q + e)];
+  }
   // output through LDS (the ring is free once every wave is past its last stage)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  store_tile<C::MB, C::NB>(a, tr, [&](int i, int j) { return acc[i][j]; }, wm * (BM / WM),
-                           (nt0 + wn * C::NB) * 16, smem + wave * store_tile_lds_bytes<C::MB, C::NB>());
+  store_tile<C::MB, C::NB>(a, tr,
+                           [&](int i, int j) {
+                             f32x4 v = acc[i][j];
+                             if constexpr (RS) {
+#pragma unroll
+                               for (int e = 0; e < 4; ++e) v[e] *= rsc[i][e];
+                             }
+                             return v;
+                           },
+                           wm * (BM / WM), (nt0 + wn * C::NB) * 16,
+                           smem + wave * store_tile_lds_bytes<C::MB, C::NB>());
 }
 
 // Activation scales regrouped by K step: out[kb * m_pad + r] holds the 4 bytes
@@ -334,7 +361,7 @@ uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) {
   return (uint64_t)((m + 255) & ~(int64_t)255) * (uint64_t)k_blocks * 4;
 }
 
-template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4 = false>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4 = false, bool RS = false>
 static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
   using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
   static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MB, C::NB>(), "epilogue LDS");
@@ -343,7 +370,7 @@ static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipSt
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR, A4>;
+  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR, A4, RS>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::THREADS), lds, s, a);
@@ -393,6 +420,22 @@ static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, bool moe
                    : launch_mx_tiled_bm<128, 256, 2, 2, false, SAR, true>(a, 0, s);
 }
 
+// Per-token FP8 activations: the 8-wave shapes of MXFP8, no scale ring.
+static hipError_t launch_mx_shape_rs(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, hipStream_t s) {
+  if (moe) {
+    if (bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, false, false, true>(a, tiles_cap, s);
+    return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true, false, false, true>(a, tiles_cap, s);
+  }
+  if (bm == 256) {
+    if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false, false, false, true>(a, 0, s);
+    if (bn == 224) return launch_mx_tiled_bm<256, 224, 4, 2, false, false, false, true>(a, 0, s);
+    return launch_mx_tiled_bm<256, 256, 4, 2, false, false, false, true>(a, 0, s);
+  }
+  if (bn == 192) return launch_mx_tiled_bm<128, 192, 4, 2, false, false, false, true>(a, 0, s);
+  if (bn == 224) return launch_mx_tiled_bm<128, 224, 4, 2, false, false, false, true>(a, 0, s);
+  return launch_mx_tiled_bm<128, 256, 4, 2, false, false, false, true>(a, 0, s);
+}
+
 // Dense: bm-row tiles (128 or 256) of bn columns (192, 224 or 256 with 8
 // waves; 256 with 4).  MoE: the tile list a.tiles (capacity tiles_cap) of
 // kMoeTileRows x 256 tiles, or (bm = 64, 8 waves) 64 x 128 small tiles, one
@@ -400,10 +443,12 @@ static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, bool moe
 // activation scales go through the SA ring when K % 512 == 0 and they are
 // 16-byte aligned; otherwise dense launches first regroup them by K step into
 // ws and MoE launches copy 4 bytes per row and step.  a4: e2m1 activations
-// (a.ldx in bytes).
+// (a.ldx in bytes).  rs: per-token FP8 activations (8 waves whatever `waves`
+// says).
 hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
-                           void *ws, hipStream_t s, bool a4) {
+                           void *ws, hipStream_t s, bool a4, bool rs) {
   if (a_in.k % 128 != 0) return hipErrorInvalidValue;
+  if (rs) return a4 ? hipErrorInvalidValue : launch_mx_shape_rs(a_in, bm, bn, moe, tiles_cap, s);
   GemmArgs a = a_in;
   const bool sar = a.k % 512 == 0 && ((uintptr_t)a.x_scales & 15) == 0;
   if (sar) return a4 ? launch_mx_shape_a4<true>(a, bm, bn, moe, tiles_cap, waves, s)

@@ -166,9 +166,19 @@ def assert_mx_f32(y, a_codes, a_scales, w_codes, w_scales, afmt, dispatches, row
 
 
 def moe_mx_forms(layer, pairs):
-    """The kernel forms an MX grouped GEMM may run an expert on: the tiled
-    kernels (one MFMA chain over K) or the skinny kernel's variant."""
-    return ["mx_tiled", qg.describe_dispatch(layer.w, pairs)]
+    """The kernel forms an MX grouped GEMM of `pairs` rows may run an expert
+    on, from the library's MoE dispatch description: the tiled kernels (one
+    MFMA chain over K) and the skinny kernel's variant for the experts below
+    the tiled threshold."""
+    forms = []
+    for part in qg.describe_moe_dispatch(layer.w, pairs, 1).split(";"):
+        part = part.strip()
+        if "skinny" in part:
+            forms.append(part.split(" for ")[0].replace(" below", ""))
+        elif "tiled" in part and "mx_tiled" not in forms:
+            forms.append("mx_tiled")
+    assert forms, pairs
+    return forms
 
 
 def check_mx_f32(layer, acts, m, y, rows=None, what=""):

@@ -12,8 +12,8 @@ import mx_mfma_model as MM
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import (TOL_BF16, TOL_F32, Acts, Layer, assert_bf16_is_rne, err, mx_codes, require_gpu,
-                         run_gemm, to_dev)
+from gpu_harness import (TOL_BF16, TOL_F32, Acts, Layer, assert_bf16_is_rne, err, moe_mx_forms, mx_codes,
+                         require_gpu, run_gemm, to_dev)
 from oracle import quantize as Q
 
 pytestmark = pytest.mark.gpu
@@ -170,9 +170,12 @@ def _tok_model(layer, acts, rows, cols, dispatch):
     return (part * acts.scales[rows][:, None].astype(np.float32)).astype(np.float32)
 
 
-@pytest.mark.parametrize("m", [1, 16, 100])
+@pytest.mark.parametrize("m", [1, 16, 100, 128, 300])
 @pytest.mark.parametrize("nk", [(512, 1024), (200, 640)])
 def test_w4a8_per_token_dense(m, nk):
+    """Below 128 rows the MX skinny kernel, from 128 rows the MX tiled kernel
+    (256-row tiles from 256 rows; 300 rows leave a ragged second tile), each
+    with unit activation block scales and the row scale on the output."""
     n, k = nk
     layer = Layer(qg.W_MXFP4, n, k, 32, seed=90, atype=qg.A_FP8_TOKEN)
     acts = TokActs(m, k, seed=91 + m)
@@ -184,6 +187,7 @@ def test_w4a8_per_token_dense(m, nk):
         print(f"  M={m} N={n} K={k} otype={otype} err={err(ys[otype], yref):.3e} ({disp})", flush=True)
     assert err(ys[qg.O_BF16], yref) <= TOL_BF16
     assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    assert ("mx_tiled" in disp) == (m >= 128), disp
     rows = np.arange(m)
     cols = np.arange(n)
     want = _tok_model(layer, acts, rows, cols, disp)
@@ -194,8 +198,12 @@ def test_w4a8_per_token_dense(m, nk):
     assert int(diff.sum()) <= max(1, got.size // 1000) and np.all(ulps <= 1.0)
 
 
-def test_w4a8_per_token_moe():
-    t, e, topk, n, k = 33, 8, 4, 128, 512
+@pytest.mark.parametrize("t", [33, 300])
+def test_w4a8_per_token_moe(t):
+    """33 tokens x top-4 (132 pairs, every expert on the skinny kernel) and
+    300 x top-4 (1200 pairs over 8 experts: the 128-row tiles of the MX tiled
+    kernel)."""
+    e, topk, n, k = 8, 4, 128, 512
     ids = synth.route(synth.rng(6, 1), t, e, topk)
     layer = Layer(qg.W_MXFP4, n, k, 32, seed=7, experts=e, atype=qg.A_FP8_TOKEN)
     acts = TokActs(t, k, seed=8)
@@ -206,18 +214,22 @@ def test_w4a8_per_token_moe():
     print(f"  bf16 err {eb:.3e} fp32 err {ef:.3e}", flush=True)
     assert eb <= TOL_BF16
     assert np.array_equal(yb, oracle.round_bf16(yf))
-    # fp32 rows against the model, expert by expert (the MoE skinny variant)
+    # fp32 rows against the model, expert by expert (one of the kernel forms
+    # the MoE dispatch names for this pair count)
     flat = ids.reshape(-1)
-    disp = qg.describe_dispatch(layer.w, flat.size)
+    forms = moe_mx_forms(layer, flat.size)
+    print(f"  MoE dispatch: {qg.describe_moe_dispatch(layer.w, t, topk)}", flush=True)
     for ex in np.unique(flat):
         pairs = np.nonzero(flat == ex)[0]
         wc, ws = mx_codes(layer, int(ex))
         ones = np.full((pairs.size, k // 32), 127, np.uint8)
-        part = MM.predict(acts.codes[pairs // topk], ones, wc, ws, "e4m3", disp)
-        want = (part * acts.scales[pairs // topk][:, None].astype(np.float32)).astype(np.float32)
         got = yf[pairs].astype(np.float32)
-        n_diff = int((got != want).sum())
-        assert n_diff <= max(1, got.size // 1000), (ex, n_diff)
+        diffs = []
+        for disp in forms:
+            part = MM.predict(acts.codes[pairs // topk], ones, wc, ws, "e4m3", disp)
+            want = (part * acts.scales[pairs // topk][:, None].astype(np.float32)).astype(np.float32)
+            diffs.append(int((got != want).sum()))
+        assert min(diffs) <= max(1, got.size // 1000), (ex, forms, diffs)
 
 
 # ---------------------------------------------------------------------------
