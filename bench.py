@@ -711,12 +711,14 @@ def main():
         for f in launchers:
             f(i)
 
+    # per-kernel average launch durations (each kernel alone, back to back,
+    # after at least 50 ms of its own launches); measured first, so the
+    # step below also starts on settled clocks
+    per_kernel_ms = [timed(torch, f, args.steps, 5) for f in launchers]
     # timed region: K steps bracketed by a synchronize and events on both sides
     ms_step = timed(torch, step, args.steps, args.warmup, warm_ms=0)  # exactly W warmup steps
     step_bytes = sum(L.bytes for L in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
-    # per-kernel average launch durations (each kernel alone, back to back)
-    per_kernel_ms = [timed(torch, f, args.steps, 5) for f in launchers]
     dom = int(np.argmax(per_kernel_ms))
     achieved = layers[dom].bytes / (per_kernel_ms[dom] * 1e-3) / 1e9
     print(f"[bench] decode step {ms_step * 1e3:.2f} us, {value:.0f} GB/s", file=sys.stderr, flush=True)
