@@ -135,15 +135,22 @@ def fill_packed_random(qg, torch, w, buf, gen):
     d = w.desc
     E, n, k = d.num_experts, d.n, d.k
     v = buf.view(E, w.expert_stride)
-    bits = 3 if d.wtype in (qg.W_INT3, qg.W_UINT3) else 4
-    codes_bytes = w.n_tiles * w.k_blocks * (1024 if bits == 4 else 768)
+    block = {3: 768, 4: 1024, 8: 2048}[8 if d.wtype == qg.W_FP8 else 3 if d.wtype in (qg.W_INT3, qg.W_UINT3) else 4]
+    codes_bytes = w.n_tiles * w.k_blocks * block
     for e0 in range(0, E, 16):  # bounded temporaries
         e1 = min(E, e0 + 16)
-        v[e0:e1, :codes_bytes] = torch.randint(0, 256, (e1 - e0, codes_bytes), dtype=torch.uint8,
-                                               device="cuda", generator=gen)
+        c = torch.randint(0, 256, (e1 - e0, codes_bytes), dtype=torch.uint8, device="cuda", generator=gen)
+        if d.wtype == qg.W_FP8:  # no e4m3 NaN codes (S.1111.111)
+            c[(c & 0x7F) == 0x7F] -= 1
+        v[e0:e1, :codes_bytes] = c
     n_pad = w.n_tiles * 16
     so = w.scales_offset
-    if d.wtype == qg.W_MXFP4 and d.atype == qg.A_BF16:
+    if d.wtype == qg.W_FP8:
+        # W8A8: fp32 block scales [n_tile][kb_pad] near 2e-2 / 448
+        kb_pad = -(-w.k_blocks // 4) * 4
+        sc = torch.rand((E, w.n_tiles * kb_pad), device="cuda", generator=gen) * 4e-5 + 2e-5
+        v[:, so:so + w.n_tiles * kb_pad * 4] = sc.view(torch.uint8).view(E, -1)
+    elif d.wtype == qg.W_MXFP4 and d.atype == qg.A_BF16:
         # bf16 powers of two 2^(e - 127), e near 120, in the integer formats' scale layout
         gp, G = w.groups_padded, k // 32
         s16 = v[:, so:so + n_pad * gp * 2].clone().view(torch.int16).view(E, n_pad, gp)
@@ -208,9 +215,20 @@ def moe_dispatch(qg, w, ids, experts):
     return f"{rule} ({int((counts >= thr).sum())} / {int(((counts > 0) & (counts < thr)).sum())} experts)"
 
 
+def fp8_acts_device(torch, rows, k, block, gen):
+    """e4m3 activations from N(0, 1) with fp32 scales per row (block None) or
+    per row and 128 K (values near the range a per-block amax / 448 gives)."""
+    q = torch.randn((rows, k), device="cuda", generator=gen).to(torch.float8_e4m3fn)
+    cols = 1 if block is None else k // block
+    s = torch.rand((rows, cols), device="cuda", generator=gen) * 4e-3 + 6e-3
+    return q.view(torch.uint8).contiguous(), (s[:, 0] if block is None else s).contiguous()
+
+
 def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters, atype=None):
     fp4 = wtype == qg.W_MXFP4 and atype == qg.A_BF16  # MXFP4 weights x bf16 activations
-    mx = wtype == qg.W_MXFP4 and not fp4
+    tok = atype == qg.A_FP8_TOKEN                       # MXFP4 weights x per-token FP8
+    f8 = wtype == qg.W_FP8                              # W8A8 block FP8
+    mx = wtype == qg.W_MXFP4 and not fp4 and not tok
     g = 32 if wtype == qg.W_MXFP4 else 128
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
@@ -218,7 +236,10 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
     active = int(np.unique(ids).size)
     p = tokens * topk
     sb = 1 if wtype == qg.W_MXFP4 else 2
-    touched = active * (weight_bytes(n1, k1, 4, g, False, sb) + weight_bytes(n2, k2, 4, g, False, sb))
+    if f8:
+        touched = active * (n1 * k1 + n2 * k2 + 4 * (-(-n1 // 128) * (k1 // 128) + -(-n2 // 128) * (k2 // 128)))
+    else:
+        touched = active * (weight_bytes(n1, k1, 4, g, False, sb) + weight_bytes(n2, k2, 4, g, False, sb))
     copies = int(min(16, max(1, -(-2 * MALL_BYTES // touched))))
     up = MoELayer(qg, torch, wtype, experts, n1, k1, copies, gen, atype)
     down = MoELayer(qg, torch, wtype, experts, n2, k2, copies, gen, atype)
@@ -230,7 +251,10 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
     stream = torch.cuda.current_stream().cuda_stream
     t_sort = timed(torch, lambda i: qg.moe_sort(d_ids, tokens, topk, experts, sorted_ids, offsets,
                                                 ws, wsb, stream), iters, 3)
-    if mx:
+    if tok or f8:
+        x, xs = fp8_acts_device(torch, tokens, k1, 128 if f8 else None, gen)
+        h, hs = fp8_acts_device(torch, p, k2, 128 if f8 else None, gen)
+    elif mx:
         x, xs = mx_acts_device(torch, tokens, k1, gen)
         h, hs = mx_acts_device(torch, p, k2, gen)
         if atype == qg.A_MXFP4:  # two e2m1 codes per byte
@@ -253,7 +277,7 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
     flops = 2.0 * p * (n1 * k1 + n2 * k2)
     tflops = flops / (t * 1e-3) / 1e12
     gbs = touched / (t * 1e-3) / 1e9
-    peak = PEAK_TFLOPS["fp8" if mx else "bf16"]
+    peak = PEAK_TFLOPS["fp8" if (mx or tok or f8) else "bf16"]
     out = {"tokens": tokens, "active_experts": active, "weight_copies": copies,
            "gate_up_us": round(t_up * 1e3, 2), "down_us": round(t_dn * 1e3, 2),
            "sort_us": round(t_sort * 1e3, 2), "TFLOPS": round(tflops, 2),
@@ -290,6 +314,20 @@ def bench_moe_large(qg, synth, torch):
         "w4a8_E128_top8_T4096": bench_moe(qg, synth, torch, "moe_w4a8", qg.W_MXFP4, 128, 8, 1280, 4096, 4096,
                                           640, 4096, iters=5),
     }
+
+
+def bench_moe_formats(qg, synth, torch):
+    """W8A8 block FP8 and MXFP4 x per-token FP8 on the E = 128 top-8 MoE
+    layer (gate_up 1280 x 4096, down 4096 x 640 per expert), T = 1 .. 4096."""
+    out = {}
+    for tokens in (1, 64, 512, 4096):
+        out[f"w8a8_block_fp8_E128_top8_T{tokens}"] = bench_moe(
+            qg, synth, torch, "moe_w8a8", qg.W_FP8, 128, 8, 1280, 4096, 4096, 640, tokens,
+            iters=5 if tokens > 512 else 30, atype=qg.A_FP8_BLOCK)
+        out[f"w4a8_fp8_token_E128_top8_T{tokens}"] = bench_moe(
+            qg, synth, torch, "moe_w4a8_token", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
+            iters=5 if tokens > 512 else 30, atype=qg.A_FP8_TOKEN)
+    return out
 
 
 def cpu_baseline(oracle, shapes, budget_s=15.0):
@@ -546,6 +584,36 @@ def bench_large_m(qg, synth, torch):
             "dispatch": qg.describe_dispatch(wts[0], 4096)}
         print(f"[bench] extra w4a4 N={n}: {extra[f'w4a4_mx_M4096_N{n}_K{k}']}", file=sys.stderr, flush=True)
         del bufs, wts
+    # W8A8 block FP8 and MXFP4 x per-token FP8 on the tiled kernel (fp8 peak)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(83)
+    stream = torch.cuda.current_stream().cuda_stream
+    for n in (3072, 14336):
+        k = 4096
+        for name, atype in (("w8a8_block_fp8", qg.A_FP8_BLOCK), ("w4a8_fp8_token", qg.A_FP8_TOKEN)):
+            if atype == qg.A_FP8_BLOCK:
+                codes, sc = synth.fp8_block_weights(synth.rng(84, n), n, k)
+                desc = qg.layer_desc(qg.W_FP8, n, k, 128, atype=atype)
+                nbytes = n * k + sc.size * 4
+            else:
+                codes, sc, _ = synth.mx_weights(synth.rng(85, n), n, k)
+                desc = qg.layer_desc(qg.W_MXFP4, n, k, 32, atype=atype)
+                nbytes = weight_bytes(n, k, 4, 32, False, 1)
+            bufs, wts = cold_copies(qg, torch, desc, codes, sc, nbytes)
+            nw = len(wts)
+            xc, xs = fp8_acts_device(torch, 4096, k, 128 if atype == qg.A_FP8_BLOCK else None, gen)
+            y = torch.empty((4096, n), dtype=torch.bfloat16, device="cuda")
+            wsb = qg.gemm_workspace_size(wts[0], 4096)
+            ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+            t = timed(torch, lambda i: qg.gemm(wts[i % nw], xc, xs, 4096, k, y, qg.O_BF16, n, ws, wsb, stream),
+                      100, 20)
+            fl = 2.0 * 4096 * n * k
+            key = f"{name}_M4096_N{n}_K{k}"
+            extra[key] = {"us": round(t * 1e3, 1), "TFLOPS": round(fl / (t * 1e-3) / 1e12, 2),
+                          "fp8_frac": round(fl / (t * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4),
+                          "dispatch": qg.describe_dispatch(wts[0], 4096)}
+            print(f"[bench] extra {key}: {extra[key]}", file=sys.stderr, flush=True)
+            del bufs, wts
     return extra
 
 
@@ -658,6 +726,8 @@ def main():
                     help="only the MoE configurations at T=4096 (for profiling the grouped kernels)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only the plain stream-read ceiling at one decode GEMM's weight bytes")
+    ap.add_argument("--moe-formats", action="store_true",
+                    help="only the W8A8 and per-token W4A8 MoE configurations")
     ap.add_argument("--formats", action="store_true",
                     help="only the further formats (WnA16 integer / e4m3 weights, W8A8, per-token W4A8)")
     ap.add_argument("--decode-rows", action="store_true",
@@ -690,6 +760,9 @@ def main():
         return
     if args.moe:
         print(json.dumps(bench_moe_large(qg, synth, torch)), flush=True)
+        return
+    if args.moe_formats:
+        print(json.dumps(bench_moe_formats(qg, synth, torch)), flush=True)
         return
     if args.ceiling:
         print(json.dumps(bench_stream_ceiling(qg, torch)), flush=True)
@@ -857,6 +930,7 @@ def main():
             moe[f"w4a4_E128_top8_T{tokens}"] = bench_moe(
                 qg, synth, torch, "moe_w4a4", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
                 iters=5 if tokens > 512 else 30, atype=qg.A_MXFP4)
+        moe.update(bench_moe_formats(qg, synth, torch))
         extra["moe"] = moe
         out["extra"] = extra
 

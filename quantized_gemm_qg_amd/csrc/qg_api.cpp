@@ -287,7 +287,8 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
     bm = 128;
     bn = 256;
   }
-  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, mx ? mx_tile_cols(w.desc.n, m, bm) : bn};
+  // (W8A8: 128-column tiles, the only width its 2-KB weight blocks fit)
+  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, w8a8(w.desc) ? 128 : mx ? mx_tile_cols(w.desc.n, m, bm) : bn};
   return true;
 }
 
@@ -406,7 +407,7 @@ static Variant select_dense_invariant(const qg_weight &w) {
   const bool mx = mx_tiled_fmt(w.desc);  // (W4A4 layers have K % 128 == 0)
   if (has_tiled(w.desc) && w.desc.k % 128 == 0 &&
       (mx || (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31))) {
-    const int bn = mx ? 256 : a16_tiled_bn();
+    const int bn = w8a8(w.desc) ? 128 : mx ? 256 : a16_tiled_bn();
     return Variant{mx ? 1 : 2, 1, 1, 1, 1, (mx || bn == 256) ? 128 : 256, bn};
   }
   // the skinny kernel with the workgroup looping over K: the reduction order
@@ -460,6 +461,7 @@ static bool variant_valid(const qg_weight &w, int64_t m, const Variant &v) {
       return variant_ok(d, v.T, v.KR) && v.W >= 1 && v.W <= 16 && v.splits >= 1 &&
              split_counters(w, v, m) <= kMaxSplitCounters;
     case 1:
+      if (w8a8(d)) return d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) && v.tbn == 128;
       return mx && d.k % 128 == 0 && (v.bm == 128 || v.bm == 256) &&
              (v.tbn == 256 || (mx_tiled_waves() == 8 && (v.tbn == 192 || v.tbn == 224)));
     case 2:
@@ -571,7 +573,7 @@ static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
   if (d.k % 128 != 0 || d.num_experts > kMaxExperts || !has_tiled(d)) return 0;
-  const bool mx = mx_a8(d) || mx_tok(d);  // one byte per activation element
+  const bool mx = mx_a8(d) || mx_tok(d) || w8a8(d);  // one byte per activation element
   // 32-bit offsets inside the kernels
   if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
       (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31))
@@ -652,7 +654,7 @@ static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_c
   if (min_rows <= 0) return 0;
   uint64_t b = moe_list_bytes(moe_tiles_cap(w, pairs, min_rows));
   if (moe_small_tiles(w, pairs, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
-  if (!mx_a8(w.desc) && !mx_tok(w.desc)) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
+  if (!mx_a8(w.desc) && !mx_tok(w.desc) && !w8a8(w.desc)) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
   return b;
 }
 
@@ -830,7 +832,7 @@ static hipError_t launch_dense_variant(const qg_weight &w, const Layout &L, cons
   }
   if (v.kind == 1) {
     if (L.a4) a.ldx = ldx / 2;  // the kernel addresses e2m1 rows in bytes
-    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), scratch, stream, L.a4, mx_tok(d));
+    return launch_mx_tiled(a, v.bm, v.tbn, false, 0, mx_tiled_waves(), scratch, stream, L.a4, mx_tok(d), L.f8);
   }
   if (L.a4) {
     // the MX skinny kernel widens the e2m1 fragments to e4m3 in registers
@@ -1058,8 +1060,9 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     a.tiles = tiles;
     a.group_m = moe_group_m();
     void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
-    if (L.mx_pack)
-      he = launch_mx_tiled(a, kMoeTileRows, 256, true, cap, mx_tiled_waves(), nullptr, stream, L.a4, mx_tok(d));
+    if (L.mx_pack || L.f8)
+      he = launch_mx_tiled(a, kMoeTileRows, L.f8 ? 128 : 256, true, cap, mx_tiled_waves(), nullptr, stream, L.a4,
+                           mx_tok(d), L.f8);
     else
       he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
                             xs, true, stream);
@@ -1067,13 +1070,13 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     if (small) {
       // the MX small tiles have 64 rows (QG_MOE_SMALL_BM applies to the
       // integer formats; the list capacity covers either)
-      const int sbm = L.mx_pack ? kMoeSmallTileRows : moe_small_bm();
+      const int sbm = (L.mx_pack || L.f8) ? kMoeSmallTileRows : moe_small_bm();
       he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
                             (int32_t)cap_s, tiles_s, stream);
       if (he != hipSuccess) return hip_status(he);
       a.tiles = tiles_s;
       a.group_m = 1;
-      he = L.mx_pack ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4, mx_tok(d))
+      he = (L.mx_pack || L.f8) ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4, mx_tok(d), L.f8)
                    : launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
       return hip_status(he);  // every expert with rows is covered
     }
@@ -1101,12 +1104,12 @@ extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_to
   char skinny[96];
   describe_variant(v, L, w->k_blocks, skinny, sizeof skinny);
   const int min_rows = pairs > 0 ? moe_tiled_min_rows(wk, pairs, pairs) : 0;
-  const char *fam = L.mx_pack ? "mx" : "a16";
+  const char *fam = L.f8 ? "f8" : L.mx_pack ? "mx" : "a16";
   if (min_rows <= 0)
     snprintf(buf, buf_bytes, "%s for every expert", skinny);
   else if (moe_small_tiles(wk, pairs, min_rows))
     snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
-             kMoeTileRows, min_rows, fam, L.mx_pack ? kMoeSmallTileRows : moe_small_bm());
+             kMoeTileRows, min_rows, fam, (L.mx_pack || L.f8) ? kMoeSmallTileRows : moe_small_bm());
   else
     snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s below", fam, kMoeTileRows, min_rows,
              skinny);
@@ -1196,7 +1199,7 @@ extern "C" qg_status qg_moe_combine(const void *y, int32_t y_type, int64_t ldy, 
 }
 
 static void describe_variant(const Variant &v, const Layout &L, int k_blocks, char *buf, uint64_t buf_bytes) {
-  const bool mx = L.mx_pack;  // (the MX tiled kernel also serves per-token FP8 activations)
+  const bool mx = L.mx_pack || L.f8;  // (the MX tiled kernel also serves per-token FP8 and W8A8)
   // skinny-kernel family: MX (also per-token FP8 activations), W8A8, A16
   const char *fam = L.mx_pack ? "mx" : L.f8 ? "f8" : "a16";
   if (v.kind == 3)
@@ -1205,7 +1208,7 @@ static void describe_variant(const Variant &v, const Layout &L, int k_blocks, ch
   else if (v.kind == 4)
     snprintf(buf, buf_bytes, "a16_decode_wide KR=%d W=%d splits=%d", v.KR, v.W, v.splits);
   else if (v.kind == 1 || v.kind == 2)
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", mx ? "mx" : "a16", v.bm, v.tbn);
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d", L.f8 ? "f8" : mx ? "mx" : "a16", v.bm, v.tbn);
   else {
     // (K beyond W * KR * splits blocks: the workgroups loop over K)
     const int span = v.W * v.KR * v.splits, passes = (k_blocks + span - 1) / span;
@@ -1257,7 +1260,7 @@ static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> 
   if (d.k % 128 == 0) {
     if (mx) {
       for (int bm : {128, 256})
-        for (int bn : {192, 224, 256}) add(Variant{1, 1, 1, 1, 1, bm, bn});
+        for (int bn : {128, 192, 224, 256}) add(Variant{1, 1, 1, 1, 1, bm, bn});  // (variant_valid filters)
     } else {
       add(Variant{2, 1, 1, 1, 1, 128, 256});
       add(Variant{2, 1, 1, 1, 1, 256, 128});
@@ -1311,7 +1314,7 @@ extern "C" qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const v
   if (!aligned16(x) || !aligned16(y) || x_pitch(L, ldx) % 16 != 0 || (L.a4 && (ldx & 1)) || (ldy * yel) % 4 != 0 ||
       ((uintptr_t)ws & 255u) != 0)
     return QG_ERR_ALIGNMENT;
-  if (L.mx_pack && (uint64_t)m * x_pitch(L, ldx) >= (1ull << 32)) return QG_ERR_UNSUPPORTED;
+  if ((L.mx_pack || L.f8) && (uint64_t)m * x_pitch(L, ldx) >= (1ull << 32)) return QG_ERR_UNSUPPORTED;
   if (flush && (flush_bytes % 16 != 0 || !aligned16(flush))) return QG_ERR_ALIGNMENT;
   std::vector<Variant> cand;
   tune_candidates(*w, m, &cand);

@@ -79,8 +79,8 @@ inline bool mx_tok(const qg_layer_desc &d) { return d.wtype == QG_W_MXFP4 && d.a
 // W8A8 FP8 with block scales (e4m3 x e4m3, fp32 scales)
 inline bool w8a8(const qg_layer_desc &d) { return d.wtype == QG_W_FP8 && d.atype == QG_A_FP8_BLOCK; }
 // Layers of the MX tiled kernel (MXFP4 weights with MXFP8, MXFP4 or per-token
-// FP8 activations)
-inline bool mx_tiled_fmt(const qg_layer_desc &d) { return mx_a8(d) || mx_a4(d) || mx_tok(d); }
+// FP8 activations; W8A8)
+inline bool mx_tiled_fmt(const qg_layer_desc &d) { return mx_a8(d) || mx_a4(d) || mx_tok(d) || w8a8(d); }
 
 // Kernel format of a layer (the FMT of the skinny and decode kernels, see
 // FmtTraits in qg_wave.h).  e0m3 weights are stored as offset-binary INT4 and
@@ -114,10 +114,11 @@ inline int ext_wave_cap(const qg_layer_desc &d) {
 }
 // Formats served by the LDS-tiled kernels (large M, MoE tiles): the 4- and
 // 3-bit integer formats (e0m3 included), MXFP4 with bf16, MXFP8, MXFP4 or
-// per-token FP8 activations.  The others run the decode and skinny kernels.
+// per-token FP8 activations, and W8A8.  The others run the decode and skinny
+// kernels.
 inline bool has_tiled(const qg_layer_desc &d) {
   const int f = kernel_fmt(d);
-  return f <= 6 || f == 14;
+  return f <= 6 || f >= 14;
 }
 
 constexpr int kTileN = 16;    // N per tile
@@ -262,9 +263,10 @@ constexpr int kMoeSmallTileRows = 64;
 // a4: the activations are e2m1 (a.ldx then counts bytes, K / 2 per row
 // minimum).  rs: e4m3 activations with one fp32 scale per row (a.x_scales):
 // unit block scales in the MFMA, each output row times its row's scale; no
-// scale copies, no workspace; 8-wave forms.
+// scale copies, no workspace; 8-wave forms.  f8: W8A8 (e4m3 x e4m3, fp32
+// block scales; bn must be 128; no workspace).
 hipError_t launch_mx_tiled(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
-                           void *ws, hipStream_t s, bool a4 = false, bool rs = false);
+                           void *ws, hipStream_t s, bool a4 = false, bool rs = false, bool f8 = false);
 uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks);
 int mx_tiled_waves();  // QG_MX_WAVES (4 or 8), else the default
 // Integer formats at large M: group row sums of X into ws, then the tiled

@@ -38,6 +38,17 @@
 // workgroup barrier.  Inside a K step the next row
 // block's LDS reads are scheduled ahead of the current block's 8 MFMAs.
 //
+// W8A8 block FP8 (F8; the announcement's "W8A8 / W4A8 / W4A4" section): e4m3
+// weights in 2-KB blocks of the scaled MFMA's 8-bit operand layout with one
+// fp32 scale per 128 x 128 block, e4m3 activations with one fp32 scale per
+// row and 128 K.  Per K step each 16 x 16 block is one scaled MFMA with unit
+// scales and C = 0 (the weights as its A operand, so lane (q, r) receives
+// columns 4q .. 4q + 3 of activation row r), then one fp32 fma per element
+// with fl32(sa[row] * sw[n-tile]); the epilogue stores the transposed blocks.
+// The activation scales are copied per step, 4 bytes per row (a 64-lane
+// gather per 64 rows); the weight scales go to the SW ring as 16 bytes (four
+// steps) per n-tile.
+//
 // Per-token FP8 activations (RS; the announcement's "End to end" section
 // serves W4A8 with them): e4m3 A operands under a unit block scale (code
 // 127), no SA copies, and each output row multiplied by its row's fp32 scale
@@ -77,17 +88,21 @@ __device__ __forceinline__ f32x4 mfma_e2m1_e2m1(i32x4 a, i32x4 b, f32x4 c, int s
 
 // BM x BN tile, WM x WN waves, each wave (BM / WM) x (BN / WN).  SAR: the
 // activation scales go to a two-slot ring of 4-step runs (16 bytes per row)
-// instead of 4 bytes per row in every stage.  A4: e2m1 activations.
-template <int BM, int BN, int WM, int WN, bool SAR, bool A4 = false>
+// instead of 4 bytes per row in every stage.  A4: e2m1 activations.  F8:
+// W8A8 (2-KB weight blocks, fp32 scales).
+template <int BM, int BN, int WM, int WN, bool SAR, bool A4 = false, bool F8 = false>
 struct MxCfg {
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int NBLK = BN / 16;                      // packed n-tiles per tile
   static constexpr int AROW = A4 ? 64 : 128;                // A bytes per row and K step
   static constexpr int A = BM * AROW;
-  static constexpr int B = NBLK * 1024;
+  static constexpr int BBLK = F8 ? 2048 : 1024;             // bytes of one packed block
+  static constexpr int B = NBLK * BBLK;
+  static constexpr int B_COPIES = B / 1024;                 // 1-KB copies of B per stage
   static constexpr int SA = SAR ? 0 : BM * 4;
-  static constexpr int SW_PIECES = (NBLK + 3) / 4;          // 1-KB copies: 4 n-tiles' 256-B units each
+  // 1-KB copies: 4 n-tiles' 256-B units each (F8: one copy, 16 bytes per n-tile)
+  static constexpr int SW_PIECES = F8 ? 1 : (NBLK + 3) / 4;
   static constexpr int SW = SW_PIECES * 1024;               // one slot (units past NBLK unused)
   static constexpr int STAGE = A + B + SA;
   static constexpr int OFF_SW = 3 * STAGE;                  // the two SW slots
@@ -99,7 +114,7 @@ struct MxCfg {
   // 8 waves) the last waves repeat the final copy, the same bytes to the
   // same place
   static constexpr int A_LOADS = (A_COPIES + WAVES - 1) / WAVES;
-  static constexpr int B_LOADS = (NBLK + WAVES - 1) / WAVES;  // 1-KB blocks of B per wave
+  static constexpr int B_LOADS = (B_COPIES + WAVES - 1) / WAVES;  // 1-KB copies of B per wave
   static constexpr int SA_WAVES = BM / 64;                  // waves that copy a 256-B SA piece
   static constexpr int AB_LOADS = A_LOADS + B_LOADS;
   static constexpr int MB = BM / WM / 16;                   // 16-row blocks per wave
@@ -107,13 +122,15 @@ struct MxCfg {
   static_assert(BN % (16 * WN) == 0, "column blocks per wave");
   static_assert(A_COPIES >= 1 && BM * AROW % 1024 == 0, "A copies");
   static_assert(WAVES >= SA_WAVES && WAVES >= SW_PIECES, "SA / SW pieces");
+  static_assert(!F8 || (!SAR && !A4 && NBLK <= 64), "W8A8: per-step activation scales, e4m3 rows");
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4, bool RS>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4, bool RS, bool F8>
 __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   static_assert(!RS || (!SAR && !A4), "per-token scales: e4m3 rows, no activation scale ring");
-  using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
+  static_assert(!(RS && F8), "one activation scale form");
+  using C = MxCfg<BM, BN, WM, WN, SAR, A4, F8>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,7 +144,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   if (!tiled_work<BM>(a, MOE, (a.n_tiles + C::NBLK - 1) / C::NBLK, &tr, &tn, &wexp)) return;
   const int nt0 = tn * C::NBLK;      // first 16-column n-tile
   const int kbs = a.k_blocks;
-  const int kq = a.k >> 5;           // activation scale bytes per row
+  const int kq = F8 ? kbs * 4 : a.k >> 5;  // activation scale bytes per row
   const uint8_t *x = (const uint8_t *)a.x;
   const uint8_t *wsc = wexp + a.scales_offset;
 
@@ -148,12 +165,14 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     }
   }
   const uint8_t *b_base = wexp + 16 * lane;
-  // copy i of this wave: tile block (and LDS slot) min(B_LOADS wave + i, NBLK - 1)
-  auto blk_of = [&](int i) { return min(wave * C::B_LOADS + i, C::NBLK - 1); };
-  uint32_t b_blk[C::B_LOADS];  // first packed block of each of the wave's n-tiles
+  // copy i of this wave: 1-KB piece (and LDS slot) min(B_LOADS wave + i,
+  // B_COPIES - 1) of the tile's blocks (F8: two pieces per 2-KB block)
+  constexpr int PB = F8 ? 1 : 0;  // log2 of the pieces per block
+  auto blk_of = [&](int i) { return min(wave * C::B_LOADS + i, C::B_COPIES - 1); };
+  uint32_t b_blk[C::B_LOADS];  // first packed block of the n-tile of each of the wave's pieces
 #pragma unroll
   for (int i = 0; i < C::B_LOADS; ++i)
-    b_blk[i] = (uint32_t)min(nt0 + blk_of(i), a.n_tiles - 1) * kbs;
+    b_blk[i] = (uint32_t)min(nt0 + (blk_of(i) >> PB), a.n_tiles - 1) * kbs;
   // SA: BM rows of 4 bytes.  Dense 256-row tiles: one 1-KB copy by wave 0
   // from the scales regrouped by K step (rows padded to 256, so the copy
   // stays in the buffer; rows past M are never stored).  Otherwise BM / 64
@@ -161,20 +180,25 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   // With SAR (K % 512 == 0 and 16-byte aligned scales) the first BM / 64
   // waves copy, every fourth step, the 16 bytes of 4 steps of one row per
   // lane straight from the row-major scales into the SA ring.
-  constexpr bool SA_X4 = !SAR && !MOE && BM == 256;
+  constexpr bool SA_X4 = !F8 && !SAR && !MOE && BM == 256;
   const bool sa_wave = !RS && (SA_X4 ? wave == 0 : wave < C::SA_WAVES);
   const int64_t m_pad = ((int64_t)a.m + 255) & ~(int64_t)255;  // regrouped row stride
   const int64_t sa_row = SA_X4 ? (int64_t)tr.base + 4 * lane : tr.x(a, (sa_wave ? wave : 0) * 64 + lane);
   // per K step: + 4 bytes (rows of kq bytes) or + 4 m_pad bytes (dense, regrouped by step)
-  const bool sa_rows = MOE || SAR;
+  const bool sa_rows = MOE || SAR || F8;
   const uint8_t *sa_src = RS ? nullptr : sa_rows ? a.x_scales + sa_row * kq : (const uint8_t *)(a.x_scales_t + sa_row);
   const int64_t sa_step = sa_rows ? 4 : 4 * m_pad;
   // SW: copy p (by wave p < SW_PIECES) moves the 256-B units of n-tiles
   // 4p .. 4p + 3 of the tile for K steps 4j .. 4j + 3 (unit of n-tile nt at
   // nt * kb_pad / 4 * 256 + 256 j); lanes 16u .. 16u + 15 copy unit u
+  // F8: lane l copies the 16 bytes (four steps' fp32 scales) of n-tile
+  // nt0 + l (clamped; lanes past the tile's n-tiles fill unused slot bytes)
   const bool sw_wave = wave < C::SW_PIECES;
-  const uint32_t sw_off = (uint32_t)((uint64_t)min(nt0 + 4 * wave + (lane >> 4), a.n_tiles - 1) *
-                                         (a.kb_pad >> 2) * 256 + 16 * (lane & 15));
+  const uint32_t sw_off =
+      F8 ? (uint32_t)((uint64_t)min(nt0 + lane, a.n_tiles - 1) * a.kb_pad * 4)
+         : (uint32_t)((uint64_t)min(nt0 + 4 * wave + (lane >> 4), a.n_tiles - 1) * (a.kb_pad >> 2) * 256 +
+                      16 * (lane & 15));
+  constexpr int SW_STEP = F8 ? 4 : 64;  // scale bytes per n-tile and K step
 
   auto issue = [&](int kb, int buf) {
     uint8_t *st = smem + buf * C::STAGE;
@@ -184,7 +208,8 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
       lds_dma16(xk + a_off[i], st + a_copy(i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_LOADS; ++i)
-      lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << 10), st + C::A + blk_of(i) * 1024);
+      lds_dma16(b_base + ((uint64_t)(b_blk[i] + kb) << (10 + PB)) + (F8 ? (blk_of(i) & 1) * 1024 : 0),
+                st + C::A + blk_of(i) * 1024);
     if constexpr (SAR) {
       if ((kb & 3) == 0 && sa_wave)
         lds_dma16(sa_src + sa_step * kb, smem + C::OFF_SAR + ((kb >> 2) & 1) * C::SAR_SLOT + wave * 1024);
@@ -195,7 +220,7 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
         lds_dma4(sa_src + sa_step * kb, st + C::A + C::B + wave * 256);
     }
     if ((kb & 3) == 0 && sw_wave)
-      lds_dma16(wsc + 64 * kb + sw_off, smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW + wave * 1024);
+      lds_dma16(wsc + SW_STEP * kb + sw_off, smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW + wave * 1024);
   };
 
   f32x4 acc[C::MB][C::NB];
@@ -230,6 +255,40 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();  // stage kb is in LDS; stage kb - 1 is free
     if (kb + 2 < kbs) issue(kb + 2, (kb + 2) % kStages);
     const uint8_t *st = smem + (kb % kStages) * C::STAGE;
+    if constexpr (F8) {
+      // weights (A operand, 32 bytes per lane) and their step scales
+      i32x8 wf[C::NB];
+      float swf[C::NB];
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j) {
+        const int blk = wn * C::NB + j;
+        const u32x4 lo = *(const u32x4 *)(st + C::A + blk * 2048 + 32 * lane);
+        const u32x4 hi = *(const u32x4 *)(st + C::A + blk * 2048 + 32 * lane + 16);
+        wf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        swf[j] = *(const float *)(smem + C::OFF_SW + ((kb >> 2) & 1) * C::SW + blk * 16 + 4 * (kb & 3));
+      }
+      const int mbv = WM == 1 ? min(C::MB, (tr.rows + 15) >> 4) : C::MB;  // (small tiles: live row blocks)
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        if (i >= mbv) continue;  // workgroup-uniform
+        const int row = wm * (BM / WM) + i * 16 + r16;
+        const uint8_t *ap = st + row * C::AROW;
+        const u32x4 lo = *(const u32x4 *)(ap + 16 * (q ^ (row & 7)));
+        const u32x4 hi = *(const u32x4 *)(ap + 16 * ((4 + q) ^ (row & 7)));
+        const i32x8 af = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        const float sa = *(const float *)(st + C::A + C::B + 4 * row);
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+          // cbsz = blgp = 0: both operands e4m3; scale codes 127 = 2^0
+          const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], af, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                            0, 0, 0, 127, 0, 127);
+          const float f = sa * swf[j];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] = __builtin_fmaf(p[e], f, acc[i][j][e]);
+        }
+      }
+      return;
+    }
     i32x4 bf[C::NB];
 #pragma unroll
     for (int j = 0; j < C::NB; ++j) {
@@ -318,6 +377,21 @@ __global__ __launch_bounds__(64 * WM * WN) void mx_tiled_kernel(GemmArgs a) {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  if constexpr (F8) {
+    // transposed blocks: lane (q, r) holds row r, columns 4q .. 4q + 3
+    store_slabs<C::MB, C::NB>(
+        a, tr,
+        [&](int i, uint8_t *l, int pitch, bool f32) {
+#pragma unroll
+          for (int j = 0; j < C::NB; ++j) {
+            const f32x4 v = acc[i][j];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) slab_put(l, pitch, f32, r16, 16 * j + 4 * q + e, v[e]);
+          }
+        },
+        wm * (BM / WM), (nt0 + wn * C::NB) * 16, smem + wave * store_tile_lds_bytes<C::MB, C::NB>());
+    return;
+  }
   store_tile<C::MB, C::NB>(a, tr,
                            [&](int i, int j) {
                              f32x4 v = acc[i][j];
@@ -361,16 +435,17 @@ uint64_t mx_tiled_ws_bytes(int64_t m, int64_t k_blocks) {
   return (uint64_t)((m + 255) & ~(int64_t)255) * (uint64_t)k_blocks * 4;
 }
 
-template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4 = false, bool RS = false>
+template <int BM, int BN, int WM, int WN, bool MOE, bool SAR, bool A4 = false, bool RS = false,
+          bool F8 = false>
 static hipError_t launch_mx_tiled_bm(const GemmArgs &a, int64_t tiles_cap, hipStream_t s) {
-  using C = MxCfg<BM, BN, WM, WN, SAR, A4>;
+  using C = MxCfg<BM, BN, WM, WN, SAR, A4, F8>;
   static_assert(C::LDS >= C::WAVES * store_tile_lds_bytes<C::MB, C::NB>(), "epilogue LDS");
   const int64_t m_tiles = MOE ? tiles_cap : (a.m + BM - 1) / BM;
   const int64_t n_tiles_wg = (a.n_tiles + C::NBLK - 1) / C::NBLK;
   const int64_t total = m_tiles * n_tiles_wg;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const size_t lds = (size_t)C::LDS;
-  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR, A4, RS>;
+  auto kern = mx_tiled_kernel<BM, BN, WM, WN, MOE, SAR, A4, RS, F8>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(per_xcd * kXcds)), dim3(C::THREADS), lds, s, a);
@@ -436,6 +511,17 @@ static hipError_t launch_mx_shape_rs(const GemmArgs &a, int bm, int bn, bool moe
   return launch_mx_tiled_bm<128, 256, 4, 2, false, false, false, true>(a, 0, s);
 }
 
+// W8A8: 128-column tiles (the 2-KB weight blocks fill LDS twice as fast);
+// dense 256 or 128 rows, MoE 128-row tiles and 64 x 128 small tiles.
+static hipError_t launch_mx_shape_f8(const GemmArgs &a, int bm, bool moe, int64_t tiles_cap, hipStream_t s) {
+  if (moe) {
+    if (bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, false, false, false, true>(a, tiles_cap, s);
+    return launch_mx_tiled_bm<kMoeTileRows, 128, 4, 2, true, false, false, false, true>(a, tiles_cap, s);
+  }
+  if (bm == 256) return launch_mx_tiled_bm<256, 128, 4, 2, false, false, false, false, true>(a, 0, s);
+  return launch_mx_tiled_bm<128, 128, 4, 2, false, false, false, false, true>(a, 0, s);
+}
+
 // Dense: bm-row tiles (128 or 256) of bn columns (192, 224 or 256 with 8
 // waves; 256 with 4).  MoE: the tile list a.tiles (capacity tiles_cap) of
 // kMoeTileRows x 256 tiles, or (bm = 64, 8 waves) 64 x 128 small tiles, one
@@ -446,8 +532,9 @@ static hipError_t launch_mx_shape_rs(const GemmArgs &a, int bm, int bn, bool moe
 // (a.ldx in bytes).  rs: per-token FP8 activations (8 waves whatever `waves`
 // says).
 hipError_t launch_mx_tiled(const GemmArgs &a_in, int bm, int bn, bool moe, int64_t tiles_cap, int waves,
-                           void *ws, hipStream_t s, bool a4, bool rs) {
+                           void *ws, hipStream_t s, bool a4, bool rs, bool f8) {
   if (a_in.k % 128 != 0) return hipErrorInvalidValue;
+  if (f8) return (a4 || rs || bn != 128) ? hipErrorInvalidValue : launch_mx_shape_f8(a_in, bm, moe, tiles_cap, s);
   if (rs) return a4 ? hipErrorInvalidValue : launch_mx_shape_rs(a_in, bm, bn, moe, tiles_cap, s);
   GemmArgs a = a_in;
   const bool sar = a.k % 512 == 0 && ((uintptr_t)a.x_scales & 15) == 0;

@@ -275,11 +275,14 @@ def _check_w8a8_f32(y, layer, acts, rows, disp, e=0, ref=None):
     bound = MM.w8a8_error_bound(acts.codes[rows], acts.scales[rows], wc, wcol)
     dev = np.abs(np.asarray(y, np.float64) - exact)
     assert np.all(dev <= bound), (float((dev / np.maximum(bound, 1e-300)).max()), disp)
-    if "skinny" in disp:
+    if "skinny" in disp or "tiled" in disp:
         import re
         v = dict(re.findall(r"(\w+)=(\d+)", disp))
-        pred = MM.gemm_w8a8(acts.codes[rows], acts.scales[rows], wc, wcol, int(v["KR"]), int(v["W"]),
-                            int(v.get("splits", 1)))
+        if "tiled" in disp:  # one chain over every K step in order
+            kr, waves, splits = layer.k // 128, 1, 1
+        else:
+            kr, waves, splits = int(v["KR"]), int(v["W"]), int(v.get("splits", 1))
+        pred = MM.gemm_w8a8(acts.codes[rows], acts.scales[rows], wc, wcol, kr, waves, splits)
         got = np.asarray(y, np.float32)
         diff = pred != got
         ulps = np.abs(got[diff].astype(np.float64) - pred[diff]) / np.spacing(np.abs(pred[diff]))
@@ -288,13 +291,17 @@ def _check_w8a8_f32(y, layer, acts, rows, disp, e=0, ref=None):
         assert int(diff.sum()) <= max(1, pred.size // 1000) and np.all(ulps <= 1.0), (int(diff.sum()), disp)
 
 
-@pytest.mark.parametrize("m", [1, 16, 64, 300])
+@pytest.mark.parametrize("m", [1, 16, 64, 128, 300])
 @pytest.mark.parametrize("nk", [(512, 1024), (200, 640)])
 def test_w8a8_dense(m, nk):
+    """Below 128 rows the skinny kernel; from 128 rows the tiled kernel's
+    W8A8 form (128 x 128 tiles, 256 x 128 from 256 rows; 300 rows leave a
+    ragged tile, N = 200 a ragged column tile, K = 640 five steps)."""
     n, k = nk
     layer = W8A8(n, k, seed=100)
     acts = BlockActs(m, k, seed=101 + m)
     disp = qg.describe_dispatch(layer.w, m)
+    assert ("f8_tiled" in disp) == (m >= 128), disp
     yref = oracle.gemm(acts.xdq, layer.wdq())
     ys = {}
     for otype in (qg.O_BF16, qg.O_F32):
@@ -305,14 +312,15 @@ def test_w8a8_dense(m, nk):
     _check_w8a8_f32(ys[qg.O_F32].cpu().numpy(), layer, acts, np.arange(m), disp, ref=yref)
 
 
-def test_w8a8_identity_rows_are_exact():
+@pytest.mark.parametrize("m", [8, 136])
+def test_w8a8_identity_rows_are_exact(m):
     """Unit activations (e4m3 1.0, scale 1) at block edges: each fp32 row is a
     column of the dequantized weight, e4m3(w) * sw[n // 128][k // 128], rounded
     once to fp32 (the step's exact partial times its scale; every other step
-    adds an exact zero)."""
-    n, k, m = 160, 512, 8
+    adds an exact zero).  8 rows: the skinny kernel; 136: the tiled kernel."""
+    n, k = 160, 512
     layer = W8A8(n, k, seed=102)
-    cols = [0, 127, 128, 255, 256, 383, 384, 511]
+    cols = [[0, 127, 128, 255, 256, 383, 384, 511][i % 8] for i in range(m)]
     codes = np.zeros((m, k), np.uint8)
     for i, c in enumerate(cols):
         codes[i, c] = 0x38
@@ -325,8 +333,11 @@ def test_w8a8_identity_rows_are_exact():
         assert np.array_equal(y[i], wdq[:, c].astype(np.float32).astype(np.float64)), (i, c)
 
 
-def test_w8a8_moe():
-    t, e, topk, n, k = 40, 8, 2, 256, 512
+@pytest.mark.parametrize("t", [40, 300])
+def test_w8a8_moe(t):
+    """40 tokens x top-2 (80 pairs: the skinny kernel) and 300 x top-2 (600
+    pairs: 128-row tiles for experts with >= 64 rows, 64-row tiles below)."""
+    e, topk, n, k = 8, 2, 256, 512
     ids = synth.route(synth.rng(11, 1), t, e, topk)
     layer = W8A8(n, k, seed=12, experts=e)
     acts = BlockActs(t, k, seed=13)
@@ -337,6 +348,7 @@ def test_w8a8_moe():
     print(f"  bf16 err {eb:.3e} fp32 err {ef:.3e}", flush=True)
     assert eb <= TOL_BF16
     assert np.array_equal(yb, oracle.round_bf16(yf))
+    print(f"  MoE dispatch: {qg.describe_moe_dispatch(layer.w, t, topk)}", flush=True)
     flat = ids.reshape(-1)
     for ex in np.unique(flat):
         pairs = np.nonzero(flat == ex)[0]
