@@ -57,12 +57,14 @@ struct Overrides {
   int moe_group_m = 0;      // QG_MOE_GROUP_M: 1..64
   int moe_small_bm = 0;     // QG_MOE_SMALL_BM: 32
   int moe_small = -1;       // QG_MOE_SMALL: 0 or 1
+  int moe_mx_bn = 0;        // QG_MOE_MX_BN: 128 or 256 (columns of the MX MoE tiles)
   int group_m = 0;          // QG_GROUP_M: 1..64
 };
 
 const char *const kOverrideNames[] = {"QG_TUNE", "QG_DECODE", "QG_DECODE_WIDE", "QG_TILED", "QG_TILED_BM", "QG_MX_BN",
                                       "QG_MX_WAVES", "QG_A16_WAVES", "QG_A16_BN", "QG_MOE_TILED_MIN",
-                                      "QG_MOE_GROUP_M", "QG_MOE_SMALL_BM", "QG_MOE_SMALL", "QG_GROUP_M"};
+                                      "QG_MOE_GROUP_M", "QG_MOE_SMALL_BM", "QG_MOE_SMALL", "QG_MOE_MX_BN",
+                                      "QG_GROUP_M"};
 
 // Applies one named override to o (value NULL or "" clears it).  Returns
 // false for an unknown name.
@@ -113,6 +115,8 @@ bool apply_override(Overrides *o, const char *name, const char *val) {
     o->moe_tiled_min = set ? std::max(0, iv) : -1;
   } else if (!strcmp(name, "QG_MOE_GROUP_M")) {
     o->moe_group_m = (iv >= 1 && iv <= 64) ? iv : 0;
+  } else if (!strcmp(name, "QG_MOE_MX_BN")) {
+    o->moe_mx_bn = (iv == 128 || iv == 256) ? iv : 0;
   } else if (!strcmp(name, "QG_MOE_SMALL_BM")) {
     o->moe_small_bm = iv == 32 ? 32 : 0;
   } else if (!strcmp(name, "QG_MOE_SMALL")) {
@@ -611,6 +615,18 @@ int a16_tiled_bn() {
 }
 
 // Raster group of the tiled MoE launches (QG_MOE_GROUP_M overrides).
+// Columns of the MX tiled kernel's 128-row MoE tiles: 128.  A 128 x 128 tile
+// needs half the LDS of a 128 x 256 one and under 100 VGPRs per lane, so two
+// workgroups share a CU and one tile's ring fill and output store overlap the
+// other's MFMAs (E = 128 top-8 W4A8 at T = 4096: gate_up 231 against 252 us,
+// down 268 against 272 us; T = 512 down 69.6 against 76.7 us).  W8A8 has only
+// the 128-column form.  QG_MOE_MX_BN = 256 selects the wide tiles.
+static int moe_mx_bn(const qg_weight &w) {
+  if (w8a8(w.desc)) return 128;
+  if (ov().moe_mx_bn) return ov().moe_mx_bn;
+  return 128;
+}
+
 static int moe_group_m() {
   return ov().moe_group_m ? ov().moe_group_m : 1;
 }
@@ -1061,7 +1077,7 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
     a.group_m = moe_group_m();
     void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
     if (L.mx_pack || L.f8)
-      he = launch_mx_tiled(a, kMoeTileRows, L.f8 ? 128 : 256, true, cap, mx_tiled_waves(), nullptr, stream, L.a4,
+      he = launch_mx_tiled(a, kMoeTileRows, moe_mx_bn(wk), true, cap, mx_tiled_waves(), nullptr, stream, L.a4,
                            mx_tok(d), L.f8);
     else
       he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
@@ -1092,6 +1108,11 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
 
 static void describe_variant(const Variant &v, const Layout &L, int k_blocks, char *buf, uint64_t buf_bytes);
 
+// Columns of the 128-row MoE tiles a layer runs (for the description).
+static int moe_tile_bn(const qg_weight &w, const Layout &L) {
+  return (L.mx_pack || L.f8) ? moe_mx_bn(w) : a16_tiled_bn();
+}
+
 extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_tokens, int32_t topk, char *buf,
                                               uint64_t buf_bytes) {
   Layout L;
@@ -1108,11 +1129,12 @@ extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_to
   if (min_rows <= 0)
     snprintf(buf, buf_bytes, "%s for every expert", skinny);
   else if (moe_small_tiles(wk, pairs, min_rows))
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
-             kMoeTileRows, min_rows, fam, (L.mx_pack || L.f8) ? kMoeSmallTileRows : moe_small_bm());
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
+             kMoeTileRows, moe_tile_bn(wk, L), min_rows, fam,
+             (L.mx_pack || L.f8) ? kMoeSmallTileRows : moe_small_bm());
   else
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d for experts with >= %d rows; %s below", fam, kMoeTileRows, min_rows,
-             skinny);
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d for experts with >= %d rows; %s below", fam, kMoeTileRows,
+             moe_tile_bn(wk, L), min_rows, skinny);
   return QG_OK;
 }
 

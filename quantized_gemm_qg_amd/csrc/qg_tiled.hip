@@ -457,6 +457,7 @@ static hipError_t launch_mx_shape(const GemmArgs &a, int bm, int bn, bool moe, i
                                   hipStream_t s) {
   if (waves == 8) {
     if (moe && bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, SAR>(a, tiles_cap, s);
+    if (moe && bn == 128) return launch_mx_tiled_bm<kMoeTileRows, 128, 4, 2, true, SAR>(a, tiles_cap, s);
     if (moe) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true, SAR>(a, tiles_cap, s);
     if (bm == 256) {
       if (bn == 192) return launch_mx_tiled_bm<256, 192, 4, 2, false, SAR>(a, 0, s);
@@ -478,6 +479,7 @@ static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, bool moe
                                      hipStream_t s) {
   if (moe) {
     if (waves == 8 && bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, SAR, true>(a, tiles_cap, s);
+    if (waves == 8 && bn == 128) return launch_mx_tiled_bm<kMoeTileRows, 128, 4, 2, true, SAR, true>(a, tiles_cap, s);
     if (waves == 8) return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true, SAR, true>(a, tiles_cap, s);
     return launch_mx_tiled_bm<kMoeTileRows, 256, 2, 2, true, SAR, true>(a, tiles_cap, s);
   }
@@ -499,6 +501,7 @@ static hipError_t launch_mx_shape_a4(const GemmArgs &a, int bm, int bn, bool moe
 static hipError_t launch_mx_shape_rs(const GemmArgs &a, int bm, int bn, bool moe, int64_t tiles_cap, hipStream_t s) {
   if (moe) {
     if (bm == 64) return launch_mx_tiled_bm<64, 128, 1, 8, true, false, false, true>(a, tiles_cap, s);
+    if (bn == 128) return launch_mx_tiled_bm<kMoeTileRows, 128, 4, 2, true, false, false, true>(a, tiles_cap, s);
     return launch_mx_tiled_bm<kMoeTileRows, 256, 4, 2, true, false, false, true>(a, tiles_cap, s);
   }
   if (bm == 256) {

@@ -77,6 +77,7 @@ SPLITS = {
     "skinny": {"QG_MOE_TILED_MIN": "0"},   # every expert on the skinny kernel
     "tiled": {"QG_MOE_TILED_MIN": "1"},    # every expert with a row on 128-row tiles
     "tiled_bn128": {"QG_MOE_TILED_MIN": "1", "QG_A16_BN": "128"},  # the same, 128-column tiles
+    "tiled_mx_bn256": {"QG_MOE_TILED_MIN": "1", "QG_MOE_MX_BN": "256"},  # MX: 256-column tiles
     "mixed": {"QG_MOE_TILED_MIN": "12", "QG_MOE_SMALL": "1"},  # >= 12 rows: 128-row tiles; fewer: small tiles
     "mixed_skinny": {"QG_MOE_TILED_MIN": "12", "QG_MOE_SMALL": "0"},  # fewer: skinny kernel
     "small": {"QG_MOE_TILED_MIN": "1000", "QG_MOE_SMALL": "1"},  # every expert on 64-row small tiles
@@ -91,6 +92,8 @@ def test_moe_small_all_row_modes(override, wtype, split):
     (128-row tiles, 64-row small tiles, the skinny kernel)."""
     if wtype == qg.W_MXFP4 and split in ("tiled_bn128", "small32"):
         pytest.skip("same dispatch as another split for MXFP4")
+    if wtype != qg.W_MXFP4 and split == "tiled_mx_bn256":
+        pytest.skip("same dispatch as the tiled split for the integer formats")
     for var, val in SPLITS[split].items():
         override(var, val)
     t, e, topk, n, k = 37, 16, 4, 80, 640
