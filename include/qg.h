@@ -296,7 +296,33 @@ qg_status qg_gemm_autotune(const qg_weight *w, const void *x, const void *x_scal
                            int64_t ldx, void *y, int32_t otype, int64_t ldy, void *ws, uint64_t ws_bytes,
                            const void *flush, uint64_t flush_bytes, int32_t reps, hipStream_t stream,
                            char *chosen, uint64_t chosen_bytes, float *chosen_us);
-/* Forget every autotuned entry (back to the heuristics). */
+/* MoE autotune (announcement, section "Future plans": benchmark candidate
+ * configurations on the target device, complementing the heuristics).
+ * qg_moe_autotune runs this grouped GEMM (the arguments of qg_moe_gemm, with
+ * num_tokens >= 1 and the pairs already sorted by qg_moe_sort) once per
+ * candidate dispatch plan -- every expert on the skinny kernel, or experts
+ * with >= 16, 32, 64 or 128 rows on the tiled kernels' 128-row tiles and the
+ * rest on the 64-row small tiles or the skinny kernel, MX tiles 128 or 256
+ * columns wide -- times each with HIP events over `reps` calls (1..64) after
+ * one warm-up call, and records the fastest plan in a process-wide table keyed
+ * by (wtype, atype, group, N, K, experts) and the bucket of num_tokens * topk
+ * (1-8, 9-64, 65-512, 513-4096, 4097-32768, more).  From then on qg_moe_gemm,
+ * qg_moe_workspace_size and qg_describe_moe_dispatch use that plan for the
+ * bucket (unless an experiment override of the MoE dispatch is set); query
+ * qg_moe_workspace_size again after tuning.  y is overwritten (the last
+ * candidate's result).
+ *   ws     device, 256-B aligned, qg_moe_autotune_workspace_size bytes;
+ *          contents on entry do not matter.  Not a qg_moe_gemm workspace.
+ *   flush, flush_bytes, reps, chosen, chosen_bytes, chosen_us  as in
+ *          qg_gemm_autotune (chosen: the plan's description).
+ * Synchronizes `stream`.  Thread-safe (the table is guarded by a mutex). */
+qg_status qg_moe_autotune_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk, uint64_t *bytes);
+qg_status qg_moe_autotune(const qg_weight *w, const void *x, const void *x_scales, int32_t x_rows,
+                          const int32_t *sorted_pair_ids, const int32_t *expert_offsets, int64_t num_tokens,
+                          int32_t topk, void *y, int32_t otype, int32_t y_rows, void *ws, uint64_t ws_bytes,
+                          const void *flush, uint64_t flush_bytes, int32_t reps, hipStream_t stream, char *chosen,
+                          uint64_t chosen_bytes, float *chosen_us);
+/* Forget every autotuned entry, dense and MoE (back to the heuristics). */
 void qg_autotune_reset(void);
 
 /* Experiment overrides of the tuning table, for tests and parameter sweeps
@@ -307,7 +333,7 @@ void qg_autotune_reset(void);
  * kernel, "T,KR[,splits]" picks an instance), QG_TILED ("0" disables the
  * large-M kernels), QG_TILED_BM, QG_MX_BN, QG_MX_WAVES, QG_A16_WAVES,
  * QG_A16_BN, QG_MOE_TILED_MIN, QG_MOE_GROUP_M, QG_MOE_SMALL_BM, QG_MOE_SMALL,
- * QG_GROUP_M; value NULL or "" clears the override.  An unknown name returns
+ * QG_MOE_MX_BN, QG_DECODE_WIDE, QG_GROUP_M; value NULL or "" clears the override.  An unknown name returns
  * QG_ERR_INVALID_ARGUMENT.  A value outside an override's range is ignored
  * (the heuristic applies).  Thread-safe; a dispatch sees the overrides before
  * or after a concurrent change, never a mix.  qg_clear_overrides clears all

@@ -32,7 +32,7 @@ EXPORTS = (
     "qg_moe_combine", "qg_gemm_workspace_size_ex", "qg_gemm_ex",
     "qg_gemm_autotune_workspace_size", "qg_gemm_autotune", "qg_autotune_reset", "qg_quantize_mxfp4",
     "qg_set_override", "qg_clear_overrides", "qg_describe_dispatch_ex", "qg_gemm_noalloc", "qg_quantize_fp8",
-    "qg_describe_moe_dispatch",
+    "qg_describe_moe_dispatch", "qg_moe_autotune_workspace_size", "qg_moe_autotune",
 )
 NOALLOC_SCRATCH_BYTES = 8 << 20
 GEMM_BATCH_INVARIANT = 1
@@ -103,6 +103,9 @@ def _load():
         "qg_gemm_autotune_workspace_size": (I32, [W, I64, ctypes.POINTER(U64)]),
         "qg_gemm_autotune": (I32, [W, P, P, I64, I64, P, I32, I64, P, U64, P, U64, I32, P, ctypes.c_char_p, U64,
                                    ctypes.POINTER(ctypes.c_float)]),
+        "qg_moe_autotune_workspace_size": (I32, [W, I64, I32, ctypes.POINTER(U64)]),
+        "qg_moe_autotune": (I32, [W, P, P, I32, P, P, I64, I32, P, I32, I32, P, U64, P, U64, I32, P,
+                                  ctypes.c_char_p, U64, ctypes.POINTER(ctypes.c_float)]),
         "qg_autotune_reset": (None, []),
         "qg_set_override": (I32, [ctypes.c_char_p, ctypes.c_char_p]),
         "qg_clear_overrides": (None, []),
@@ -321,6 +324,27 @@ def gemm_autotune(w: Weight, x, x_scales, m: int, ldx: int, y, otype: int, ldy: 
     _check(_lib.qg_gemm_autotune(ctypes.byref(w), _ptr(x), _ptr(x_scales), m, ldx, _ptr(y), otype, ldy, _ptr(ws),
                                  ws_bytes, _ptr(flush), flush_bytes, reps, _stream(stream), buf, 256,
                                  ctypes.byref(us)), "qg_gemm_autotune")
+    return buf.value.decode(), us.value
+
+
+def moe_autotune_workspace_size(w: Weight, num_tokens: int, topk: int) -> int:
+    out = ctypes.c_uint64()
+    _check(_lib.qg_moe_autotune_workspace_size(ctypes.byref(w), num_tokens, topk, ctypes.byref(out)),
+           "qg_moe_autotune_workspace_size")
+    return out.value
+
+
+def moe_autotune(w: Weight, x, x_scales, x_rows: int, sorted_ids, offsets, num_tokens: int, topk: int, y,
+                 otype: int, y_rows: int, ws, ws_bytes: int, flush=None, flush_bytes: int = 0, reps: int = 10,
+                 stream=None) -> tuple[str, float]:
+    """Time the candidate dispatch plans of this grouped GEMM and keep the
+    fastest for its (layer, pair-count bucket); returns (description, mean us
+    per call)."""
+    buf = ctypes.create_string_buffer(256)
+    us = ctypes.c_float()
+    _check(_lib.qg_moe_autotune(ctypes.byref(w), _ptr(x), _ptr(x_scales), x_rows, _ptr(sorted_ids), _ptr(offsets),
+                                num_tokens, topk, _ptr(y), otype, y_rows, _ptr(ws), ws_bytes, _ptr(flush),
+                                flush_bytes, reps, _stream(stream), buf, 256, ctypes.byref(us)), "qg_moe_autotune")
     return buf.value.decode(), us.value
 
 

@@ -574,14 +574,18 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
 // overrides (0 disables the tiled kernels).
 static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows);
 
-static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
+// Whether the tiled kernels can serve this MoE call at all.
+static bool moe_tiled_ok(const qg_weight &w, int64_t x_rows_count) {
   const qg_layer_desc &d = w.desc;
-  if (d.k % 128 != 0 || d.num_experts > kMaxExperts || !has_tiled(d)) return 0;
+  if (d.k % 128 != 0 || d.num_experts > kMaxExperts || !has_tiled(d)) return false;
   const bool mx = mx_a8(d) || mx_tok(d) || w8a8(d);  // one byte per activation element
   // 32-bit offsets inside the kernels
-  if ((uint64_t)x_rows_count * d.k * (mx ? 1 : 2) >= (1ull << 31) ||
-      (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31))
-    return 0;
+  return (uint64_t)x_rows_count * d.k * (mx ? 1 : 2) < (1ull << 31) &&
+         (uint64_t)w.n_tiles * w.k_blocks * 1024 < (1ull << 31);
+}
+
+static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
+  if (!moe_tiled_ok(w, x_rows_count)) return 0;
   int min_rows = 64;
   if (ov().moe_tiled_min >= 0) min_rows = ov().moe_tiled_min;
   if (min_rows <= 0) return 0;
@@ -664,12 +668,78 @@ static bool moe_small_tiles(const qg_weight &w, int64_t pairs, int min_rows) {
 
 static uint64_t moe_list_bytes(int64_t cap) { return align_up((uint64_t)(2 + 2 * cap) * 4, 256); }
 
+// Autotune limits: timed launches per candidate, and the sink of the cache
+// flush reads at the end of an autotune workspace.
+constexpr int kTuneMaxReps = 64;
+constexpr uint64_t kTuneSinkBytes = 16384;
+
+// The MoE dispatch of one call: experts with >= min_rows rows run the tiled
+// kernels' 128-row tiles (min_rows 0: none do), the others the small-tile
+// form (small) or the skinny kernel; mx_bn: columns of the MX tiled kernel's
+// 128-row tiles.
+struct MoePlan {
+  int min_rows;
+  bool small;
+  int mx_bn;
+};
+
+// MoE autotune table (announcement, "Future plans": autotune on the target
+// device; here for the grouped GEMM's dispatch): the fastest plan per layer
+// shape and pair-count bucket, consulted unless an experiment override of the
+// MoE dispatch is set.
+namespace {
+struct MoeTuneEntry {
+  int32_t wtype, atype, group, experts, bucket;
+  int64_t n, k;
+  MoePlan plan;
+};
+std::mutex g_moe_tune_mu;
+std::vector<MoeTuneEntry> g_moe_tune;
+}  // namespace
+
+// pair-count buckets: 1-8, 9-64, 65-512, 513-4096, 4097-32768, more
+static int pairs_bucket(int64_t pairs) {
+  static const int64_t edges[] = {8, 64, 512, 4096, 32768};
+  int b = 0;
+  while (b < 5 && pairs > edges[b]) ++b;
+  return b;
+}
+
+static bool moe_tune_key(const MoeTuneEntry &e, const qg_weight &w, int b) {
+  const qg_layer_desc &d = w.desc;
+  return e.wtype == d.wtype && e.atype == d.atype && e.group == d.group_size && e.experts == d.num_experts &&
+         e.bucket == b && e.n == d.n && e.k == d.k;
+}
+
+static bool moe_overridden() {
+  return ov().moe_tiled_min >= 0 || ov().moe_small >= 0 || ov().moe_mx_bn != 0;
+}
+
+static MoePlan moe_plan(const qg_weight &w, int64_t pairs, int64_t x_rows_count) {
+  if (!moe_overridden()) {
+    std::lock_guard<std::mutex> lock(g_moe_tune_mu);
+    const int b = pairs_bucket(pairs);
+    for (const MoeTuneEntry &e : g_moe_tune)
+      if (moe_tune_key(e, w, b)) {
+        MoePlan p = e.plan;
+        if (p.min_rows > 0 && !moe_tiled_ok(w, x_rows_count)) p = MoePlan{0, false, p.mx_bn};
+        return p;
+      }
+  }
+  MoePlan p;
+  p.min_rows = moe_tiled_min_rows(w, pairs, x_rows_count);
+  p.small = moe_small_tiles(w, pairs, p.min_rows);
+  p.mx_bn = moe_mx_bn(w);
+  return p;
+}
+
 // MoE workspace: [tile list][small-tile list][group row sums of X (integer
 // formats)]
-static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_count, int min_rows) {
+static uint64_t moe_ws_bytes(const qg_weight &w, int64_t pairs, int64_t x_rows_count, const MoePlan &plan) {
+  const int min_rows = plan.min_rows;
   if (min_rows <= 0) return 0;
   uint64_t b = moe_list_bytes(moe_tiles_cap(w, pairs, min_rows));
-  if (moe_small_tiles(w, pairs, min_rows)) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
+  if (plan.small) b += moe_list_bytes(moe_small_tiles_cap(w, pairs));
   if (!mx_a8(w.desc) && !mx_tok(w.desc) && !w8a8(w.desc)) b += a16_tiled_ws_bytes(w.desc, x_rows_count);
   return b;
 }
@@ -994,7 +1064,7 @@ extern "C" qg_status qg_moe_workspace_size(const qg_weight *w, int64_t num_token
   // the sort's need, or the grouped GEMM's with X indexed by pair (the larger
   // of the two x row counts); W4A4 needs what W4A8 does
   const qg_weight wk = mx_kernel_weight(*w, L);
-  const uint64_t gemm = moe_ws_bytes(wk, pairs, pairs, moe_tiled_min_rows(wk, pairs, pairs));
+  const uint64_t gemm = moe_ws_bytes(wk, pairs, pairs, moe_plan(wk, pairs, pairs));
   *bytes = std::max<uint64_t>(align_up((uint64_t)(w->desc.num_experts + 1) * 4, 256), gemm);
   return QG_OK;
 }
@@ -1014,40 +1084,19 @@ extern "C" qg_status qg_moe_sort(const int32_t *topk_ids, int64_t num_tokens, in
                                     expert_offsets, (int32_t *)ws, stream));
 }
 
-extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales,
-                                 int32_t x_rows, const int32_t *sorted_pair_ids,
-                                 const int32_t *expert_offsets, int64_t num_tokens, int32_t topk,
-                                 void *y, int32_t otype, int32_t y_rows, void *ws,
-                                 uint64_t ws_bytes, hipStream_t stream) {
-  Layout L;
-  qg_status st = check_weight(w, &L);
-  if (st != QG_OK) return st;
+// The launches of one validated MoE call under `plan` (ws holds at least
+// moe_ws_bytes of it).
+static hipError_t moe_run(const qg_weight *w, const Layout &L, const MoePlan &plan, const void *x,
+                          const void *x_scales, int32_t x_rows, const int32_t *sorted_pair_ids,
+                          const int32_t *expert_offsets, int64_t num_tokens, int32_t topk, void *y, int32_t otype,
+                          int32_t y_rows, void *ws, hipStream_t stream) {
   // W4A4: W4A8's dispatch, launched on e2m1 rows
   const qg_weight wk = mx_kernel_weight(*w, L);
   const qg_layer_desc &d = wk.desc;
-  if (num_tokens < 0 || topk <= 0 || (otype != QG_O_BF16 && otype != QG_O_F32))
-    return QG_ERR_INVALID_ARGUMENT;
-  if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
-  if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
-  if (d.num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
   const int64_t pairs = num_tokens * topk;
-  if (pairs > (1ll << 30)) return QG_ERR_UNSUPPORTED;
-  if (pairs == 0) return QG_OK;
-  if (!x || !y || !sorted_pair_ids || !expert_offsets) return QG_ERR_INVALID_ARGUMENT;
-  if (L.xs_kind && !x_scales) return QG_ERR_INVALID_ARGUMENT;
-  if (L.xs_kind >= 2 && ((uintptr_t)x_scales & 3u) != 0) return QG_ERR_ALIGNMENT;
-  const int yel = otype == QG_O_F32 ? 4 : 2;
-  if (!aligned16(x) || !aligned16(y) || x_pitch(L, d.k) % 16 != 0 || (d.n * yel) % 4 != 0)
-    return QG_ERR_ALIGNMENT;
   const Variant v = select_moe(wk, pairs);
   const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
-  const int min_rows = moe_tiled_min_rows(wk, pairs, x_rows_count);
-  const uint64_t need = moe_ws_bytes(wk, pairs, x_rows_count, min_rows);
-  if (need > 0) {
-    if (!ws) return QG_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
-    if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
-  }
+  const int min_rows = plan.min_rows;
   GemmArgs a;
   base_args(wk, &a);
   a.x = x;
@@ -1063,38 +1112,39 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   a.x_rows = x_rows;
   a.y_rows = y_rows;
   hipError_t he = hipSuccess;
+  const bool mxt = L.mx_pack || L.f8;  // the MX tiled kernel's layouts
   if (min_rows > 0) {
     // experts with >= min_rows rows: tile list, then the tiled kernel
     const int64_t cap = moe_tiles_cap(wk, pairs, min_rows);
-    const bool small = moe_small_tiles(wk, pairs, min_rows);
+    const bool small = plan.small;
     const int64_t cap_s = small ? moe_small_tiles_cap(wk, pairs) : 0;
     int32_t *tiles = (int32_t *)ws;
     int32_t *tiles_s = (int32_t *)((uint8_t *)ws + moe_list_bytes(cap));
     he = launch_moe_tiles(expert_offsets, d.num_experts, min_rows, 0, kMoeTileRows, (int32_t)pairs,
                           (int32_t)cap, tiles, stream);
-    if (he != hipSuccess) return hip_status(he);
+    if (he != hipSuccess) return he;
     a.tiles = tiles;
     a.group_m = moe_group_m();
     void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
-    if (L.mx_pack || L.f8)
-      he = launch_mx_tiled(a, kMoeTileRows, moe_mx_bn(wk), true, cap, mx_tiled_waves(), nullptr, stream, L.a4,
+    if (mxt)
+      he = launch_mx_tiled(a, kMoeTileRows, plan.mx_bn, true, cap, mx_tiled_waves(), nullptr, stream, L.a4,
                            mx_tok(d), L.f8);
     else
       he = launch_a16_tiled(a, d, kMoeTileRows, a16_tiled_bn(), true, x_rows_count, cap, a16_tiled_waves(),
                             xs, true, stream);
-    if (he != hipSuccess) return hip_status(he);
+    if (he != hipSuccess) return he;
     if (small) {
       // the MX small tiles have 64 rows (QG_MOE_SMALL_BM applies to the
       // integer formats; the list capacity covers either)
-      const int sbm = (L.mx_pack || L.f8) ? kMoeSmallTileRows : moe_small_bm();
+      const int sbm = mxt ? kMoeSmallTileRows : moe_small_bm();
       he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
                             (int32_t)cap_s, tiles_s, stream);
-      if (he != hipSuccess) return hip_status(he);
+      if (he != hipSuccess) return he;
       a.tiles = tiles_s;
       a.group_m = 1;
-      he = (L.mx_pack || L.f8) ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4, mx_tok(d), L.f8)
-                   : launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
-      return hip_status(he);  // every expert with rows is covered
+      return mxt ? launch_mx_tiled(a, sbm, 128, true, cap_s, 8, nullptr, stream, L.a4, mx_tok(d), L.f8)
+                 : launch_a16_tiled(a, d, sbm, 128, true, x_rows_count, cap_s, 8, xs, false, stream);
+      // (every expert with rows is covered)
     }
     a.moe_min_rows = min_rows;
   }
@@ -1102,15 +1152,200 @@ extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *
   const int64_t max_tiles = (pairs + 15) / 16 + d.num_experts;
   // (the skinny kernel's format comes from the layer's own description:
   // FMT 6 widens e2m1 fragments in registers)
-  he = L.is_mx ? launch_moe_mx(a, w->desc, v, max_tiles, stream) : launch_moe_a16(a, d, v, max_tiles, stream);
-  return hip_status(he);
+  return L.is_mx ? launch_moe_mx(a, w->desc, v, max_tiles, stream) : launch_moe_a16(a, d, v, max_tiles, stream);
+}
+
+// Argument checks shared by qg_moe_gemm and qg_moe_autotune (pairs > 0 only;
+// the workspace is checked by the caller).
+static qg_status moe_check(const qg_weight *w, const Layout &L, const void *x, const void *x_scales, int32_t x_rows,
+                           const int32_t *sorted_pair_ids, const int32_t *expert_offsets, int32_t otype,
+                           int32_t y_rows, const void *y) {
+  const qg_layer_desc &d = w->desc;
+  if (!x || !y || !sorted_pair_ids || !expert_offsets) return QG_ERR_INVALID_ARGUMENT;
+  if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  if (L.xs_kind && !x_scales) return QG_ERR_INVALID_ARGUMENT;
+  if (L.xs_kind >= 2 && ((uintptr_t)x_scales & 3u) != 0) return QG_ERR_ALIGNMENT;
+  const int yel = otype == QG_O_F32 ? 4 : 2;
+  if (!aligned16(x) || !aligned16(y) || x_pitch(L, d.k) % 16 != 0 || (d.n * yel) % 4 != 0)
+    return QG_ERR_ALIGNMENT;
+  return QG_OK;
+}
+
+extern "C" qg_status qg_moe_gemm(const qg_weight *w, const void *x, const void *x_scales,
+                                 int32_t x_rows, const int32_t *sorted_pair_ids,
+                                 const int32_t *expert_offsets, int64_t num_tokens, int32_t topk,
+                                 void *y, int32_t otype, int32_t y_rows, void *ws,
+                                 uint64_t ws_bytes, hipStream_t stream) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  const qg_weight wk = mx_kernel_weight(*w, L);
+  if (num_tokens < 0 || topk <= 0 || (otype != QG_O_BF16 && otype != QG_O_F32))
+    return QG_ERR_INVALID_ARGUMENT;
+  if (x_rows < QG_ROWS_BY_TOKEN || x_rows > QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  if (y_rows != QG_ROWS_BY_PAIR && y_rows != QG_ROWS_SORTED) return QG_ERR_INVALID_ARGUMENT;
+  if (w->desc.num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
+  const int64_t pairs = num_tokens * topk;
+  if (pairs > (1ll << 30)) return QG_ERR_UNSUPPORTED;
+  if (pairs == 0) return QG_OK;
+  st = moe_check(w, L, x, x_scales, x_rows, sorted_pair_ids, expert_offsets, otype, y_rows, y);
+  if (st != QG_OK) return st;
+  const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
+  const MoePlan plan = moe_plan(wk, pairs, x_rows_count);
+  const uint64_t need = moe_ws_bytes(wk, pairs, x_rows_count, plan);
+  if (need > 0) {
+    if (!ws) return QG_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < need) return QG_ERR_BUFFER_TOO_SMALL;
+    if (((uintptr_t)ws & 255u) != 0) return QG_ERR_ALIGNMENT;
+  }
+  return hip_status(moe_run(w, L, plan, x, x_scales, x_rows, sorted_pair_ids, expert_offsets, num_tokens, topk, y,
+                            otype, y_rows, ws, stream));
+}
+
+// MoE autotune candidates: every expert on the skinny kernel, or the 128-row
+// tiles from 16, 32, 64 or 128 rows with the rest on the small tiles or the
+// skinny kernel, for the MX tiled kernel in 128- and 256-column tiles.
+static void moe_tune_candidates(const qg_weight &wk, int64_t pairs, int64_t x_rows_count, std::vector<MoePlan> *out) {
+  const MoePlan heur = moe_plan(wk, pairs, x_rows_count);
+  out->push_back(heur);
+  auto add = [&](const MoePlan &p) {
+    for (const MoePlan &q : *out)
+      if (q.min_rows == p.min_rows && q.small == p.small && q.mx_bn == p.mx_bn) return;
+    out->push_back(p);
+  };
+  add(MoePlan{0, false, heur.mx_bn});
+  if (!moe_tiled_ok(wk, x_rows_count)) return;
+  const bool mxt = mx_tiled_fmt(wk.desc);
+  for (int r : {16, 32, 64, 128})
+    for (int small = 0; small < 2; ++small)
+      for (int bn : {128, 256}) {
+        if (bn == 256 && (!mxt || w8a8(wk.desc))) continue;
+        add(MoePlan{r, small != 0, bn});
+      }
+}
+
+static void describe_moe_plan(const qg_weight &wk, const Layout &L, const MoePlan &plan, int64_t pairs, char *buf,
+                              uint64_t buf_bytes);
+
+extern "C" qg_status qg_moe_autotune_workspace_size(const qg_weight *w, int64_t num_tokens, int32_t topk,
+                                                    uint64_t *bytes) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  if (!bytes || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
+  const qg_weight wk = mx_kernel_weight(*w, L);
+  const int64_t pairs = num_tokens * topk;
+  std::vector<MoePlan> cand;
+  moe_tune_candidates(wk, std::max<int64_t>(pairs, 1), pairs, &cand);
+  uint64_t b = 0;
+  for (const MoePlan &p : cand) b = std::max(b, moe_ws_bytes(wk, pairs, pairs, p));
+  *bytes = align_up(b, 256) + kTuneSinkBytes;
+  return QG_OK;
+}
+
+extern "C" qg_status qg_moe_autotune(const qg_weight *w, const void *x, const void *x_scales, int32_t x_rows,
+                                     const int32_t *sorted_pair_ids, const int32_t *expert_offsets,
+                                     int64_t num_tokens, int32_t topk, void *y, int32_t otype, int32_t y_rows,
+                                     void *ws, uint64_t ws_bytes, const void *flush, uint64_t flush_bytes,
+                                     int32_t reps, hipStream_t stream, char *chosen, uint64_t chosen_bytes,
+                                     float *chosen_us) {
+  Layout L;
+  qg_status st = check_weight(w, &L);
+  if (st != QG_OK) return st;
+  const qg_weight wk = mx_kernel_weight(*w, L);
+  if (num_tokens < 1 || topk <= 0 || reps < 1 || reps > kTuneMaxReps) return QG_ERR_INVALID_ARGUMENT;
+  if (otype != QG_O_BF16 && otype != QG_O_F32) return QG_ERR_INVALID_ARGUMENT;
+  if (w->desc.num_experts > kMaxExperts) return QG_ERR_UNSUPPORTED;
+  const int64_t pairs = num_tokens * topk;
+  if (pairs > (1ll << 30)) return QG_ERR_UNSUPPORTED;
+  st = moe_check(w, L, x, x_scales, x_rows, sorted_pair_ids, expert_offsets, otype, y_rows, y);
+  if (st != QG_OK) return st;
+  if (!ws || ((uintptr_t)ws & 255u) != 0) return !ws ? QG_ERR_INVALID_ARGUMENT : QG_ERR_ALIGNMENT;
+  if (flush && (flush_bytes % 16 != 0 || !aligned16(flush))) return QG_ERR_ALIGNMENT;
+  const int64_t x_rows_count = x_rows == QG_ROWS_BY_TOKEN ? num_tokens : pairs;
+  std::vector<MoePlan> cand;
+  moe_tune_candidates(wk, pairs, x_rows_count, &cand);
+  uint64_t db = 0;
+  for (const MoePlan &p : cand) db = std::max(db, moe_ws_bytes(wk, pairs, x_rows_count, p));
+  db = align_up(db, 256);
+  if (ws_bytes < db + kTuneSinkBytes) return QG_ERR_BUFFER_TOO_SMALL;
+  uint8_t *sink = (uint8_t *)ws + db;
+
+  hipEvent_t ev[2 * kTuneMaxReps];
+  int made = 0;
+  hipError_t he = hipSuccess;
+  for (; made < 2 * reps; ++made)
+    if ((he = hipEventCreate(&ev[made])) != hipSuccess) break;
+  int best = -1;
+  float best_us = 0.f;
+  for (size_t i = 0; he == hipSuccess && i < cand.size(); ++i) {
+    const MoePlan &p = cand[i];
+    auto run = [&]() {
+      return moe_run(w, L, p, x, x_scales, x_rows, sorted_pair_ids, expert_offsets, num_tokens, topk, y, otype,
+                     y_rows, ws, stream);
+    };
+    if (run() != hipSuccess) continue;  // a form this shape does not compile to: skip it
+    for (int r = 0; r < reps && he == hipSuccess; ++r) {
+      if (flush && flush_bytes) he = launch_stream_read(flush, flush_bytes, sink, stream);
+      if (he == hipSuccess) he = hipEventRecord(ev[2 * r], stream);
+      if (he == hipSuccess) he = run();
+      if (he == hipSuccess) he = hipEventRecord(ev[2 * r + 1], stream);
+    }
+    if (he == hipSuccess) he = hipEventSynchronize(ev[2 * reps - 1]);
+    float total = 0.f;
+    for (int r = 0; r < reps && he == hipSuccess; ++r) {
+      float ms = 0.f;
+      he = hipEventElapsedTime(&ms, ev[2 * r], ev[2 * r + 1]);
+      total += ms;
+    }
+    if (he != hipSuccess) break;
+    const float us = total * 1000.f / (float)reps;
+    if (best < 0 || us < best_us) {
+      best = (int)i;
+      best_us = us;
+    }
+  }
+  for (int e = 0; e < made; ++e) hipEventDestroy(ev[e]);
+  if (he != hipSuccess) return hip_status(he);
+  if (best < 0) return QG_ERR_UNSUPPORTED;
+  {
+    std::lock_guard<std::mutex> lock(g_moe_tune_mu);
+    const int b = pairs_bucket(pairs);
+    bool found = false;
+    for (MoeTuneEntry &e : g_moe_tune)
+      if (moe_tune_key(e, wk, b)) {
+        e.plan = cand[best];
+        found = true;
+      }
+    if (!found)
+      g_moe_tune.push_back(MoeTuneEntry{wk.desc.wtype, wk.desc.atype, wk.desc.group_size, wk.desc.num_experts, b,
+                                        wk.desc.n, wk.desc.k, cand[best]});
+  }
+  if (chosen && chosen_bytes) describe_moe_plan(wk, L, cand[best], pairs, chosen, chosen_bytes);
+  if (chosen_us) *chosen_us = best_us;
+  return QG_OK;
 }
 
 static void describe_variant(const Variant &v, const Layout &L, int k_blocks, char *buf, uint64_t buf_bytes);
 
-// Columns of the 128-row MoE tiles a layer runs (for the description).
-static int moe_tile_bn(const qg_weight &w, const Layout &L) {
-  return (L.mx_pack || L.f8) ? moe_mx_bn(w) : a16_tiled_bn();
+static void describe_moe_plan(const qg_weight &wk, const Layout &L, const MoePlan &plan, int64_t pairs, char *buf,
+                              uint64_t buf_bytes) {
+  const Variant v = select_moe(wk, std::max<int64_t>(pairs, 1));
+  char skinny[96];
+  describe_variant(v, L, wk.k_blocks, skinny, sizeof skinny);
+  const int min_rows = plan.min_rows;
+  const bool mxt = L.mx_pack || L.f8;
+  const char *fam = L.f8 ? "f8" : L.mx_pack ? "mx" : "a16";
+  const int bn = mxt ? plan.mx_bn : a16_tiled_bn();
+  if (min_rows <= 0)
+    snprintf(buf, buf_bytes, "%s for every expert", skinny);
+  else if (plan.small)
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
+             kMoeTileRows, bn, min_rows, fam, mxt ? kMoeSmallTileRows : moe_small_bm());
+  else
+    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d for experts with >= %d rows; %s below", fam, kMoeTileRows, bn,
+             min_rows, skinny);
 }
 
 extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_tokens, int32_t topk, char *buf,
@@ -1121,20 +1356,8 @@ extern "C" qg_status qg_describe_moe_dispatch(const qg_weight *w, int64_t num_to
   if (!buf || buf_bytes == 0 || num_tokens < 0 || topk <= 0) return QG_ERR_INVALID_ARGUMENT;
   const qg_weight wk = mx_kernel_weight(*w, L);
   const int64_t pairs = num_tokens * topk;
-  const Variant v = select_moe(wk, std::max<int64_t>(pairs, 1));
-  char skinny[96];
-  describe_variant(v, L, w->k_blocks, skinny, sizeof skinny);
-  const int min_rows = pairs > 0 ? moe_tiled_min_rows(wk, pairs, pairs) : 0;
-  const char *fam = L.f8 ? "f8" : L.mx_pack ? "mx" : "a16";
-  if (min_rows <= 0)
-    snprintf(buf, buf_bytes, "%s for every expert", skinny);
-  else if (moe_small_tiles(wk, pairs, min_rows))
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d for experts with >= %d rows; %s_tiled small BM=%d below", fam,
-             kMoeTileRows, moe_tile_bn(wk, L), min_rows, fam,
-             (L.mx_pack || L.f8) ? kMoeSmallTileRows : moe_small_bm());
-  else
-    snprintf(buf, buf_bytes, "%s_tiled BM=%d BN=%d for experts with >= %d rows; %s below", fam, kMoeTileRows,
-             moe_tile_bn(wk, L), min_rows, skinny);
+  const MoePlan plan = pairs > 0 ? moe_plan(wk, pairs, pairs) : MoePlan{0, false, moe_mx_bn(wk)};
+  describe_moe_plan(wk, L, plan, pairs, buf, buf_bytes);
   return QG_OK;
 }
 
@@ -1291,8 +1514,6 @@ static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> 
   }
 }
 
-constexpr int kTuneMaxReps = 64;
-constexpr uint64_t kTuneSinkBytes = 16384;
 
 // Autotune workspace: a dense workspace for every candidate (the counter
 // prefix, cleared by the call, then the largest candidate's partials or
@@ -1408,8 +1629,12 @@ extern "C" void qg_clear_overrides(void) {
 }
 
 extern "C" void qg_autotune_reset(void) {
-  std::lock_guard<std::mutex> lock(g_tune_mu);
-  g_tune.clear();
+  {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    g_tune.clear();
+  }
+  std::lock_guard<std::mutex> lock(g_moe_tune_mu);
+  g_moe_tune.clear();
 }
 
 extern "C" qg_status qg_describe_dispatch_ex(const qg_weight *w, int64_t m, uint32_t flags, char *buf,

@@ -102,3 +102,69 @@ def test_autotune_entries_are_per_activation_type():
     acts = Acts(False, m, k, seed=50)
     y = run_gemm(a16, acts, m, qg.O_F32)
     assert err(y, oracle.gemm(acts.xdq, a16.wdq())) <= TOL_F32
+
+
+# ---------------------------------------------------------------------------
+# MoE autotune (qg_moe_autotune)
+# ---------------------------------------------------------------------------
+
+def _moe_inputs(wtype, t, e, topk, n, k, seed):
+    import synth
+    from test_gpu_moe import sort_on_gpu
+    g = 32 if wtype == qg.W_MXFP4 else 128
+    ids = synth.route(synth.rng(seed, wtype), t, e, topk)
+    layer = Layer(wtype, n, k, g, seed=seed + 1, experts=e)
+    sorted_ids, offsets = sort_on_gpu(ids, e, layer)
+    acts = Acts(wtype == qg.W_MXFP4, t, k, seed=seed + 2)
+    return ids, layer, sorted_ids, offsets, acts
+
+
+@pytest.mark.parametrize("wtype", [qg.W_UINT4, qg.W_MXFP4])
+def test_moe_autotune_records_and_dispatches(wtype):
+    """The tuned plan is the one qg_describe_moe_dispatch then names for the
+    pair-count bucket, qg_moe_gemm runs it against the oracle (MX: bit for
+    bit against the MFMA model of the plan's kernels), another bucket keeps
+    the heuristic, and qg_autotune_reset restores it."""
+    from test_gpu_moe import check_f32, run_moe
+    t, e, topk, n, k = 300, 8, 2, 256, 1024
+    ids, layer, sorted_ids, offsets, acts = _moe_inputs(wtype, t, e, topk, n, k, seed=70)
+    heur = qg.describe_moe_dispatch(layer.w, t, topk)
+    other = qg.describe_moe_dispatch(layer.w, 3, topk)
+    y = torch.empty((t * topk, n), dtype=torch.bfloat16, device="cuda")
+    wsb = qg.moe_autotune_workspace_size(layer.w, t, topk)
+    ws = torch.full((wsb,), 0x7F, dtype=torch.uint8, device="cuda")  # contents must not matter
+    flush = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    chosen, us = qg.moe_autotune(layer.w, acts.x, acts.xs, qg.ROWS_BY_TOKEN, sorted_ids, offsets, t, topk, y,
+                                 qg.O_BF16, qg.ROWS_BY_PAIR, ws, wsb, flush, flush.numel(), 3)
+    torch.cuda.synchronize()
+    print(f"  heuristic: {heur}\n  chosen: {chosen} ({us:.1f} us)", flush=True)
+    assert us > 0
+    assert qg.describe_moe_dispatch(layer.w, t, topk) == chosen
+    assert qg.describe_moe_dispatch(layer.w, 3, topk) == other  # another bucket
+    ref = oracle.moe_gemm(layer.wdq, acts.xdq, ids, rows_by_token=True)
+    ys = {o: run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, o)
+          for o in (qg.O_BF16, qg.O_F32)}
+    assert oracle.normwise_error(ys[qg.O_BF16], ref) <= TOL_BF16
+    check_f32(layer, acts, ids, ys[qg.O_F32], ref, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR)
+    qg.autotune_reset()
+    assert qg.describe_moe_dispatch(layer.w, t, topk) == heur
+
+
+def test_moe_autotune_every_candidate_is_correct():
+    """Each plan the tuner may pick, forced through the overrides, matches the
+    oracle (the candidates are the same kernel forms)."""
+    from test_gpu_moe import check_f32, run_moe
+    t, e, topk, n, k = 200, 8, 2, 128, 512
+    ids, layer, sorted_ids, offsets, acts = _moe_inputs(qg.W_MXFP4, t, e, topk, n, k, seed=80)
+    ref = oracle.moe_gemm(layer.wdq, acts.xdq, ids, rows_by_token=True)
+    for r in ("0", "16", "128"):
+        for small in ("0", "1"):
+            for bn in ("128", "256"):
+                qg.clear_overrides()
+                qg.set_override("QG_MOE_TILED_MIN", r)
+                qg.set_override("QG_MOE_SMALL", small)
+                qg.set_override("QG_MOE_MX_BN", bn)
+                print(f"  {qg.describe_moe_dispatch(layer.w, t, topk)}", flush=True)
+                y = run_moe(layer, acts, sorted_ids, offsets, t, topk, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR, qg.O_F32)
+                check_f32(layer, acts, ids, y, ref, qg.ROWS_BY_TOKEN, qg.ROWS_BY_PAIR)
+    qg.clear_overrides()
