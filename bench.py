@@ -224,7 +224,10 @@ def fp8_acts_device(torch, rows, k, block, gen):
     return q.view(torch.uint8).contiguous(), (s[:, 0] if block is None else s).contiguous()
 
 
-def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters, atype=None):
+def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, tokens, iters, atype=None, tune=False):
+    """gate_up + down of one MoE layer (T tokens, top-k routing).  tune: run
+    qg_moe_autotune on both GEMMs first (cold caches), time the tuned plans,
+    and reset the table afterwards."""
     fp4 = wtype == qg.W_MXFP4 and atype == qg.A_BF16  # MXFP4 weights x bf16 activations
     tok = atype == qg.A_FP8_TOKEN                       # MXFP4 weights x per-token FP8
     f8 = wtype == qg.W_FP8                              # W8A8 block FP8
@@ -265,6 +268,18 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
         xs = hs = None
     y1 = torch.empty((p, n1), dtype=torch.bfloat16, device="cuda")
     y2 = torch.empty((p, n2), dtype=torch.bfloat16, device="cuda")
+    chosen = None
+    if tune:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        chosen = []
+        for L, xx, xxs, xr, yy in ((up, x, xs, qg.ROWS_BY_TOKEN, y1), (down, h, hs, qg.ROWS_BY_PAIR, y2)):
+            wsb_t = qg.moe_autotune_workspace_size(L.ws[0], tokens, topk)
+            wst = torch.empty(wsb_t, dtype=torch.uint8, device="cuda")
+            c, _ = qg.moe_autotune(L.ws[0], xx, xxs, xr, sorted_ids, offsets, tokens, topk, yy, qg.O_BF16,
+                                   qg.ROWS_BY_PAIR, wst, wsb_t, flush, flush.numel(), 3)
+            chosen.append(c)
+            del wst
+        del flush
     gws = max(qg.moe_workspace_size(up.ws[0], tokens, topk), qg.moe_workspace_size(down.ws[0], tokens, topk))
     gw = torch.empty(max(gws, 1), dtype=torch.uint8, device="cuda")
     t_up = timed(torch, lambda i: qg.moe_gemm(up.ws[i % copies], x, xs, qg.ROWS_BY_TOKEN, sorted_ids,
@@ -284,6 +299,9 @@ def bench_moe(qg, synth, torch, name, wtype, experts, topk, n1, k1, n2, k2, toke
            "weight_GBs": round(gbs, 1), "mfma_frac": round(tflops / peak, 4),
            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
            "dispatch": moe_dispatch(qg, up.ws[0], ids, experts)}
+    if tune:
+        out["tuned_plans"] = chosen
+        qg.autotune_reset()
     del up, down
     torch.cuda.empty_cache()
     print(f"[bench] {name} T={tokens}: {out}", file=sys.stderr, flush=True)
@@ -314,6 +332,17 @@ def bench_moe_large(qg, synth, torch):
         "w4a8_E128_top8_T4096": bench_moe(qg, synth, torch, "moe_w4a8", qg.W_MXFP4, 128, 8, 1280, 4096, 4096,
                                           640, 4096, iters=5),
     }
+
+
+def bench_moe_tuned(qg, synth, torch):
+    """The W4A16 and W4A8 MoE layers after qg_moe_autotune of both GEMMs."""
+    out = {"w4a16_E256_top8_T4096_autotuned": bench_moe(
+        qg, synth, torch, "moe_w4a16 tuned", qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, 4096, iters=5, tune=True)}
+    for tokens in (64, 4096):
+        out[f"w4a8_E128_top8_T{tokens}_autotuned"] = bench_moe(
+            qg, synth, torch, "moe_w4a8 tuned", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
+            iters=5 if tokens > 512 else 30, tune=True)
+    return out
 
 
 def bench_moe_formats(qg, synth, torch):
@@ -366,28 +395,30 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """Bytes per launch recorded for the current kernel sources, else None."""
+def measured_traffic(n: int, k: int):
+    """Bytes per launch of the M = 1 decode GEMM (n, k) recorded for the
+    current kernel sources (`traffic_bytes_per_launch_{n}x{k}:`), else None."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
     vals = {}
+    key = f"traffic_bytes_per_launch_{n}x{k}:"
     for line in text.splitlines():
-        for key in ("source_hash:", "traffic_bytes_per_launch:"):
-            if line.strip().startswith(key):
-                vals[key] = line.split(":", 1)[1].strip().strip("`")
-    if vals.get("source_hash:") != kernel_source_hash() or "traffic_bytes_per_launch:" not in vals:
+        for kk in ("source_hash:", key):
+            if line.strip().startswith(kk):
+                vals[kk] = line.split(":", 1)[1].strip().strip("`")
+    if vals.get("source_hash:") != kernel_source_hash() or key not in vals:
         return None
-    return int(vals["traffic_bytes_per_launch:"])
+    return int(vals[key])
 
 
 def pmc_workload(qg, synth, torch):
     """A short run for rocprofv3 counter passes: qg_stream_copy of 256 MiB
-    (three launches, the calibration), then the dominant decode kernel (dense
-    W4A16 UINT4 + zp, M=1, N=4096, K=14336) 20 times on rotating weight
-    copies, then the 16-row decode GEMMs (UINT4 + zp and INT3, both decode
-    shapes) 20 times each."""
+    (three launches, the calibration), then the two M = 1 decode GEMMs of the
+    headline step (dense W4A16 UINT4 + zp, (N, K) = (4096, 14336) then
+    (14336, 4096)) 20 times each on rotating weight copies, then the 16-row
+    decode GEMMs (UINT4 + zp and INT3, both decode shapes) 20 times each."""
     n_copy = 256 << 20
     src = torch.empty(n_copy, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty(n_copy, dtype=torch.uint8, device="cuda")
@@ -396,15 +427,17 @@ def pmc_workload(qg, synth, torch):
         qg.stream_copy(dst, src, n_copy, stream)
     torch.cuda.synchronize()
     del src, dst
-    L = DenseWeights(qg, synth, torch, qg.W_UINT4, 4096, 14336, 128, seed=1)
-    x, _, _ = make_x(qg, synth, torch, False, 1, 14336, seed=11)
-    f = dense_launcher(qg, torch, L, x, None, 1)
-    for i in range(20):
-        f(i)
-    torch.cuda.synchronize()
-    print(f"pmc workload: copy {n_copy} B x3, decode N=4096 K=14336 M=1 x20 "
-          f"({L.bytes} algorithmic bytes per launch), source hash {kernel_source_hash()}", flush=True)
-    del L
+    print(f"pmc workload: copy {n_copy} B x3, source hash {kernel_source_hash()}", flush=True)
+    for n, k in ((4096, 14336), (14336, 4096)):
+        L = DenseWeights(qg, synth, torch, qg.W_UINT4, n, k, 128, seed=1)
+        x, _, _ = make_x(qg, synth, torch, False, 1, k, seed=11)
+        f = dense_launcher(qg, torch, L, x, None, 1)
+        for i in range(20):
+            f(i)
+        torch.cuda.synchronize()
+        print(f"pmc workload: decode N={n} K={k} M=1 x20 ({L.bytes} algorithmic bytes per launch): "
+              f"{qg.describe_dispatch(L.ws[0], 1)}", flush=True)
+        del L
     for wtype, name in ((qg.W_UINT4, "uint4_zp"), (qg.W_INT3, "int3")):
         for i, (n, k) in enumerate([(14336, 4096), (4096, 14336)]):
             L = DenseWeights(qg, synth, torch, wtype, n, k, 128, seed=30 + i)
@@ -726,6 +759,8 @@ def main():
                     help="only the MoE configurations at T=4096 (for profiling the grouped kernels)")
     ap.add_argument("--ceiling", action="store_true",
                     help="only the plain stream-read ceiling at one decode GEMM's weight bytes")
+    ap.add_argument("--moe-tuned", action="store_true",
+                    help="only the MoE configurations after qg_moe_autotune")
     ap.add_argument("--moe-formats", action="store_true",
                     help="only the W8A8 and per-token W4A8 MoE configurations")
     ap.add_argument("--formats", action="store_true",
@@ -763,6 +798,9 @@ def main():
         return
     if args.moe_formats:
         print(json.dumps(bench_moe_formats(qg, synth, torch)), flush=True)
+        return
+    if args.moe_tuned:
+        print(json.dumps(bench_moe_tuned(qg, synth, torch)), flush=True)
         return
     if args.ceiling:
         print(json.dumps(bench_stream_ceiling(qg, torch)), flush=True)
@@ -817,7 +855,7 @@ def main():
         "per_kernel_us": [round(t * 1e3, 3) for t in per_kernel_ms],
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic() if dom == 1 else None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(layers[dom].n, layers[dom].k),
             "kernel": f"{qg.describe_dispatch(layers[dom].ws[0], 1)}: dense W4A16 N={layers[dom].n} "
                       f"K={layers[dom].k} M=1",
             "bytes_per_launch": layers[dom].bytes,
@@ -931,6 +969,7 @@ def main():
                 qg, synth, torch, "moe_w4a4", qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens,
                 iters=5 if tokens > 512 else 30, atype=qg.A_MXFP4)
         moe.update(bench_moe_formats(qg, synth, torch))
+        moe.update(bench_moe_tuned(qg, synth, torch))
         extra["moe"] = moe
         out["extra"] = extra
 

@@ -322,8 +322,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
   const int gpb = 128 / w.desc.group_size;
   if ((int64_t)W * KR * S * gpb > w.groups_padded) return false;  // scale reads stay in the row
   if (S > 1 && (w.n_tiles + T - 1) / T > kMaxSplitCounters) return false;  // one counter per column block
-  const uint64_t lds = align_up((uint64_t)m * ((uint64_t)W * KR * 256 + 16), 256) + (uint64_t)W * T * m * 64;
-  if (lds > 160 * 1024 - 256) return false;  // (+ the kernel's static LDS)
+  if (decode_lds_bytes(m, W, T, KR) > 160 * 1024 - 256) return false;  // (+ the kernel's static LDS)
   *v = Variant{3, T, KR, W, S, 0, 0};
   return true;
 }

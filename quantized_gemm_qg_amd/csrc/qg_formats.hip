@@ -82,8 +82,7 @@ hipError_t launch_skinny_ext(const GemmArgs &a, int fmt, int group, const Varian
 template <int FMT, int GROUP>
 static hipError_t launch_decode_x(const GemmArgs &a, const Variant &v, hipStream_t s) {
   const int n_blocks = (a.n_tiles + v.T - 1) / v.T;
-  const size_t lds = (((size_t)a.m * ((size_t)v.W * v.KR * 256 + 16) + 255) & ~(size_t)255) +
-                     (size_t)v.W * v.T * a.m * 16 * sizeof(float);
+  const size_t lds = (size_t)decode_lds_bytes(a.m, v.W, v.T, v.KR);
   if (lds > 160 * 1024 - 256) return hipErrorInvalidValue;  // (+ the kernel's static LDS)
   if (v.T != 1 || (v.KR != 4 && v.KR != 8)) return hipErrorInvalidValue;
   auto pick = [&](auto kr_tag) {

@@ -151,6 +151,17 @@ struct Layout {
 
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
 
+// LDS of the decode kernel: the rows (m x W KR 128 bf16, each row padded by 16
+// bytes) and the waves' partial tiles (W x T x m x 16 floats).  With more than
+// one row the partials reuse the rows' space once every wave is done with
+// them (one workgroup barrier), so up to 8 rows of 4096 fit two workgroups
+// per CU and 16 rows fit one.
+inline uint64_t decode_lds_bytes(int64_t m, int W, int T, int KR) {
+  const uint64_t x = align_up((uint64_t)m * ((uint64_t)W * KR * 256 + 16), 256);
+  const uint64_t red = (uint64_t)W * T * m * 64;
+  return m == 1 ? x + red : (x > red ? x : red);
+}
+
 // Validates a descriptor; fills the layout on success.
 qg_status make_layout(const qg_layer_desc *d, Layout *out);
 

@@ -222,8 +222,7 @@ static hipError_t launch_dense(const GemmArgs &a, const qg_layer_desc &d, const 
 template <int FMT, int GROUP>
 static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream_t s) {
   const int n_blocks = (a.n_tiles + v.T - 1) / v.T;
-  const size_t lds = (((size_t)a.m * ((size_t)v.W * v.KR * 256 + 16) + 255) & ~(size_t)255) +
-                     (size_t)v.W * v.T * a.m * 16 * sizeof(float);
+  const size_t lds = (size_t)decode_lds_bytes(a.m, v.W, v.T, v.KR);
   if (lds > 160 * 1024 - 256) return hipErrorInvalidValue;  // (+ the kernel's static LDS)
 #define QG_DECODE_LAUNCH(TV, KRV)                                                            \
   {                                                                                          \

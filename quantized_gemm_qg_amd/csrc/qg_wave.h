@@ -992,7 +992,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
   const int rows = ER == 1 ? 1 : a.m;         // 1..16 (ER = 1: a single row)
   const int kspan = nwaves * KR * 128;        // K covered by the waves of one split
   const int xpitch = kspan * 2 + 16;          // bytes per row in LDS (padded: bank spread)
-  float *red = (float *)(dsm + ((rows * xpitch + 255) & ~255));  // [waves][T][rows][16]
+  // [waves][T][rows][16]: behind the rows for one row, else over them (written
+  // after the barrier that ends every wave's reads of the rows)
+  float *red = (float *)(ER == 1 ? dsm + ((rows * xpitch + 255) & ~255) : dsm);
   __shared__ int last_flag;
   const int nt0 = blockIdx.x * T;
   const int split = blockIdx.y;
@@ -1054,6 +1056,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void decode_kernel(GemmArgs a) {
         a, a.wbase, xrow, nt0, (split * nwaves + wave) * KR, acc, x_ready, ks0);
 
   // 3. reduce the waves (valid rows only) and store
+  if constexpr (ER != 1) __syncthreads();  // (the partials overwrite the rows)
 #pragma unroll
   for (int t = 0; t < T; ++t)
 #pragma unroll
