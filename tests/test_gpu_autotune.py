@@ -153,13 +153,25 @@ def test_moe_autotune_records_and_dispatches(wtype):
 def test_moe_autotune_every_candidate_is_correct():
     """Each plan the tuner may pick, forced through the overrides, matches the
     oracle (the candidates are the same kernel forms)."""
-    from test_gpu_moe import check_f32, run_moe
     t, e, topk, n, k = 200, 8, 2, 128, 512
     ids, layer, sorted_ids, offsets, acts = _moe_inputs(qg.W_MXFP4, t, e, topk, n, k, seed=80)
+    _every_plan(layer, acts, ids, sorted_ids, offsets, t, topk, ("128", "256"))
+
+
+def test_moe_autotune_every_candidate_is_correct_integer():
+    """The same for an integer format (the small tiles compute the group row
+    sums of X themselves when no 128-row tile runs)."""
+    t, e, topk, n, k = 200, 8, 2, 128, 512
+    ids, layer, sorted_ids, offsets, acts = _moe_inputs(qg.W_UINT4, t, e, topk, n, k, seed=81)
+    _every_plan(layer, acts, ids, sorted_ids, offsets, t, topk, ("128",))
+
+
+def _every_plan(layer, acts, ids, sorted_ids, offsets, t, topk, bns):
+    from test_gpu_moe import check_f32, run_moe
     ref = oracle.moe_gemm(layer.wdq, acts.xdq, ids, rows_by_token=True)
-    for r in ("0", "16", "128"):
+    for r in ("0", "16", "128", "1073741824"):  # (the last: every expert on the small tiles)
         for small in ("0", "1"):
-            for bn in ("128", "256"):
+            for bn in bns:
                 qg.clear_overrides()
                 qg.set_override("QG_MOE_TILED_MIN", r)
                 qg.set_override("QG_MOE_SMALL", small)
