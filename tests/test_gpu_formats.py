@@ -198,12 +198,12 @@ def test_w4a8_per_token_dense(m, nk):
     assert int(diff.sum()) <= max(1, got.size // 1000) and np.all(ulps <= 1.0)
 
 
-@pytest.mark.parametrize("t", [33, 300])
-def test_w4a8_per_token_moe(t):
+@pytest.mark.parametrize("t,k", [(33, 512), (300, 512), (300, 640)])
+def test_w4a8_per_token_moe(t, k):
     """33 tokens x top-4 (132 pairs, every expert on the skinny kernel) and
     300 x top-4 (1200 pairs over 8 experts: the 128-row tiles of the MX tiled
-    kernel)."""
-    e, topk, n, k = 8, 4, 128, 512
+    kernel), at K = 512 and 640."""
+    e, topk, n = 8, 4, 128
     ids = synth.route(synth.rng(6, 1), t, e, topk)
     layer = Layer(qg.W_MXFP4, n, k, 32, seed=7, experts=e, atype=qg.A_FP8_TOKEN)
     acts = TokActs(t, k, seed=8)
@@ -292,11 +292,12 @@ def _check_w8a8_f32(y, layer, acts, rows, disp, e=0, ref=None):
 
 
 @pytest.mark.parametrize("m", [1, 16, 64, 128, 300])
-@pytest.mark.parametrize("nk", [(512, 1024), (200, 640)])
+@pytest.mark.parametrize("nk", [(512, 1024), (200, 640), (136, 384), (72, 128)])
 def test_w8a8_dense(m, nk):
     """Below 128 rows the skinny kernel; from 128 rows the tiled kernel's
     W8A8 form (128 x 128 tiles, 256 x 128 from 256 rows; 300 rows leave a
-    ragged tile, N = 200 a ragged column tile, K = 640 five steps)."""
+    ragged tile, N = 200 a ragged column tile, K = 640 five steps, K = 384
+    three, K = 128 one; N = 136 and 72 end inside a 16-column tile)."""
     n, k = nk
     layer = W8A8(n, k, seed=100)
     acts = BlockActs(m, k, seed=101 + m)
@@ -333,11 +334,13 @@ def test_w8a8_identity_rows_are_exact(m):
         assert np.array_equal(y[i], wdq[:, c].astype(np.float32).astype(np.float64)), (i, c)
 
 
-@pytest.mark.parametrize("t", [40, 300])
-def test_w8a8_moe(t):
+@pytest.mark.parametrize("t,k", [(40, 512), (300, 512), (300, 640)])
+def test_w8a8_moe(t, k):
     """40 tokens x top-2 (80 pairs: the skinny kernel) and 300 x top-2 (600
-    pairs: 128-row tiles for experts with >= 64 rows, 64-row tiles below)."""
-    e, topk, n, k = 8, 2, 256, 512
+    pairs: 128-row tiles for experts with >= 64 rows, 64-row tiles below);
+    K = 640 is five K steps (the weight-scale ring's second group holds one
+    step)."""
+    e, topk, n = 8, 2, 256
     ids = synth.route(synth.rng(11, 1), t, e, topk)
     layer = W8A8(n, k, seed=12, experts=e)
     acts = BlockActs(t, k, seed=13)
