@@ -130,11 +130,13 @@ typedef enum { QG_ROWS_BY_TOKEN = 0, QG_ROWS_BY_PAIR = 1, QG_ROWS_SORTED = 2 } q
  *   MXFP4, E8M0 scales, FP8_TOKEN activations, group 32 (W4A8 with per-token
  *   FP8 activations, section "End to end": the scaled MFMA with unit
  *   activation block scales, each output row times its row's fp32 scale;
- *   skinny kernel);
+ *   skinny kernel below 128 rows (dense) or for experts with few rows (MoE),
+ *   the LDS-tiled scaled-MFMA kernel otherwise);
  *   FP8 (e4m3), F32 scales, FP8_BLOCK activations, group 128 (W8A8 with
  *   block-wise scaling, section "W8A8 / W4A8 / W4A4": one fp32 scale per
  *   128 x 128 block of W, scales [N/128 rounded up][K/128]; K % 128 == 0;
- *   skinny kernel);
+ *   skinny kernel below 128 rows (dense) or for experts with few rows (MoE),
+ *   the LDS-tiled e4m3 x e4m3 scaled-MFMA kernel otherwise);
  *   MXFP4, E8M0 scales, MXFP8 activations, group 32 (W4A8 on the scaled MFMA);
  *   MXFP4, E8M0 scales, BF16 activations, group 32 (each code dequantized in
  *   the kernel to the exact bf16 e2m1 * 2^(e-127); the announcement's
