@@ -19,6 +19,8 @@
 namespace qg {
 
 static thread_local int32_t g_last_hip_error = 0;
+
+constexpr int kNumCUs = 256;  // MI355X compute units (8 XCDs x 32)
 void set_last_hip_error(int32_t e) { g_last_hip_error = e; }
 
 static qg_status hip_status(hipError_t e) {
@@ -254,7 +256,7 @@ static void sanitize(const qg_layer_desc &d, Variant *v) {
 static int mx_tile_cols(int64_t n, int64_t m, int bm) {
   if (mx_tiled_waves() != 8) return 256;  // the 4-wave form is built for 256 only
   if (ov().mx_bn) return ov().mx_bn;
-  constexpr int kCus = 256;
+  constexpr int kCus = kNumCUs;
   const int64_t m_tiles = (m + bm - 1) / bm;
   int best = 256;
   double best_eff = 0.0;
@@ -310,7 +312,7 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
   const bool compiled = ext_a16(w.desc) ? (T == 1 && (KR == 4 || KR == 8))
                         : (g == 32 && T == 1 && (KR == 4 || KR == 8)) ||
                               (!fp4_a16(w.desc) &&
-                               ((g == 128 && ((T == 4 && KR == 2) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
+                               ((g == 128 && ((T == 4 && KR == 2) || (T == 4 && KR == 4) || (T == 2 && KR == 4) || (T == 1 && KR == 4) ||
                                               (T == 1 && KR == 8) || (T == 2 && KR == 8))) ||
                                 (g == 64 && ((T == 4 && KR == 2) || (T == 2 && KR == 4)))));
   if (!compiled || S < 1 || S > 8) return false;
@@ -325,6 +327,19 @@ static bool decode_fits(const qg_weight &w, int64_t m, int T, int KR, int S, Var
   if (decode_lds_bytes(m, W, T, KR) > 160 * 1024 - 256) return false;  // (+ the kernel's static LDS)
   *v = Variant{3, T, KR, W, S, 0, 0};
   return true;
+}
+
+// Rounds of resident workgroups a decode launch takes: a CU holds as many
+// workgroups as its LDS (160 KB) and its waves allow; the waves per CU follow
+// the instances' registers (T * KR = 16: ~124 VGPRs, 4 waves per SIMD; the
+// others up to 90, 5 to 8 waves per SIMD, taken as 7).
+static int64_t decode_rounds(const qg_weight &w, int64_t m, const Variant &v) {
+  const uint64_t lds = decode_lds_bytes(m, v.W, v.T, v.KR) + 256;
+  int64_t per_cu = (int64_t)((160 * 1024) / lds);
+  per_cu = std::min<int64_t>(per_cu, (v.T * v.KR >= 16 ? 16 : 28) / v.W);
+  if (per_cu < 1) per_cu = 1;
+  const int64_t wgs = (int64_t)((w.n_tiles + v.T - 1) / v.T) * v.splits;
+  return (wgs + kNumCUs * per_cu - 1) / (kNumCUs * per_cu);
 }
 
 // Wide decode form (2 .. 16 rows, K % 512 == 0): W waves along N, one K slice
@@ -373,6 +388,19 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
     const int f = kernel_fmt(d);
     const bool bits8 = f == 7 || f == 8 || f == 13;
     if (m >= (bits8 ? 9 : 8) && decode_wide_fits(w, m, bits8 ? 4 : 8, 8, v)) return true;
+  }
+  // Rows that fill more than half of a CU's LDS leave one two-tile workgroup
+  // per CU, and more such workgroups than CUs run in two rounds; four tiles
+  // per workgroup take fewer rounds, each row copy serving twice the columns
+  // (14336 x 4096 at M = 16: 11.1 against 12.9 us; at M = 8, where two
+  // two-tile workgroups share a CU and one round covers N, 10.3 against 9.8)
+  if (!ext_a16(d) && m > 1) {
+    Variant v2, v4;
+    if (decode_fits(w, m, 2, 4, 1, &v2) && decode_fits(w, m, 4, 4, 1, &v4) &&
+        decode_rounds(w, m, v4) < decode_rounds(w, m, v2)) {
+      *v = v4;
+      return true;
+    }
   }
   static const int pairs_one[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
   static const int pairs_rows[][2] = {{2, 4}, {1, 8}, {2, 8}, {4, 2}};

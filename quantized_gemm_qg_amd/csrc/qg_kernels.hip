@@ -240,6 +240,7 @@ static hipError_t launch_decode_g(const GemmArgs &a, const Variant &v, hipStream
     if (v.T == 2 && v.KR == 4) QG_DECODE_LAUNCH(2, 4)
   }
   if constexpr (GROUP == 128) {
+    if (v.T == 4 && v.KR == 4) QG_DECODE_LAUNCH(4, 4)
     if (v.T == 1 && v.KR == 4) QG_DECODE_LAUNCH(1, 4)
     if (v.T == 1 && v.KR == 8) QG_DECODE_LAUNCH(1, 8)
     if (v.T == 2 && v.KR == 8) QG_DECODE_LAUNCH(2, 8)

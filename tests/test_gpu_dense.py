@@ -156,7 +156,7 @@ def test_decode_full_size(wtype, nk):
     n, k = nk
     print(f"decode wtype={wtype} N={n} K={k}", flush=True)
     layer = Layer(wtype, n, k, 128, seed=11)
-    for m in (1, 4, 8, 16):
+    for m in (1, 4, 8, 10, 16):
         _check(layer, Acts(False, m, k, seed=20 + m), m)
 
 
@@ -295,7 +295,7 @@ def test_w4a16_large_m_full_size_sampled_rows(nk):
 # ---------------------------------------------------------------------------
 
 # "T,KR" or "T,KR,splits" (split K across workgroups)
-DECODE_VARIANTS = {128: ["4,2", "2,4", "1,4", "1,8", "2,8", "1,4,2", "1,4,3", "1,8,2", "2,4,2"],
+DECODE_VARIANTS = {128: ["4,2", "2,4", "4,4", "1,4", "1,8", "2,8", "1,4,2", "1,4,3", "1,8,2", "2,4,2", "4,4,2"],
                    64: ["4,2", "2,4", "2,4,2"],
                    32: ["1,4", "1,8", "1,4,2", "1,8,2"]}
 
