@@ -253,17 +253,19 @@ constexpr int store_tile_lds_bytes() {
 
 // The store path of store_tile for any accumulator layout: write_slab(i, lds,
 // pitch, f32) writes the wave's 16-row slab i ([16][16 NJ] of fp32 or bf16 at
-// `pitch` bytes per row); the rows are then stored from LDS.
-template <int MI, int NJ, typename W>
-__device__ __forceinline__ void store_slabs(const GemmArgs &a, const TileRows &tr, W &&write_slab,
-                                            int row0, int col0, uint8_t *lds) {
+// `pitch` bytes per row); the rows are then stored from LDS.  The element
+// type is a template constant here (store_slabs below picks the instance
+// once), so the per-element writes of the slabs carry no branch on it.
+template <int MI, int NJ, bool F32, typename W>
+__device__ __forceinline__ void store_slabs_el(const GemmArgs &a, const TileRows &tr, W &write_slab, int row0,
+                                               int col0, uint8_t *lds) {
   constexpr int WN = 16 * NJ;  // columns of the wave tile
   const int lane = threadIdx.x & 63;
-  const bool f32 = a.otype == QG_O_F32;
-  const int el = f32 ? 4 : 2;
-  const int pitch = WN * el + 16;           // padded row pitch (bytes)
-  const int cpr = WN * el / 16;             // 16-byte chunks per row
-  const int rows_per_pass = 64 / cpr;
+  constexpr bool f32 = F32;
+  constexpr int el = f32 ? 4 : 2;
+  constexpr int pitch = WN * el + 16;       // padded row pitch (bytes)
+  constexpr int cpr = WN * el / 16;         // 16-byte chunks per row
+  constexpr int rows_per_pass = 64 / cpr;
   const bool vec16 = ((a.ldy * el) & 15) == 0;  // y itself is 16-byte aligned
   int *yrow = (int *)(lds + 16 * (WN * 4 + 16));  // [16 MI] output rows of the wave
 #pragma unroll
@@ -294,14 +296,27 @@ __device__ __forceinline__ void store_slabs(const GemmArgs &a, const TileRows &t
             uint32_t *d4 = (uint32_t *)dst;
             d4[0] = v.x; d4[1] = v.y; d4[2] = v.z; d4[3] = v.w;
           }
-        } else {  // right edge of the matrix: element by element
-          const uint8_t *src = (const uint8_t *)&v;
-          for (int b = 0; b < (a.n - col) * el; ++b) dst[b] = src[b];
+        } else {  // right edge of the matrix: the chunk's first (N - col) elements, byte by byte
+          const int nb = (a.n - col) * el;
+#pragma unroll
+          for (int b = 0; b < 16; ++b) {
+            const uint32_t dw = b < 4 ? v.x : b < 8 ? v.y : b < 12 ? v.z : v.w;
+            if (b < nb) dst[b] = (uint8_t)(dw >> (8 * (b & 3)));
+          }
         }
       }
     }
     asm volatile("" ::: "memory");  // next slab's writes stay below these reads
   }
+}
+
+template <int MI, int NJ, typename W>
+__device__ __forceinline__ void store_slabs(const GemmArgs &a, const TileRows &tr, W &&write_slab,
+                                            int row0, int col0, uint8_t *lds) {
+  if (a.otype == QG_O_F32)
+    store_slabs_el<MI, NJ, true>(a, tr, write_slab, row0, col0, lds);
+  else
+    store_slabs_el<MI, NJ, false>(a, tr, write_slab, row0, col0, lds);
 }
 
 // one fp32 / bf16 element of a slab in LDS
