@@ -143,6 +143,44 @@ def test_zero_rows_is_noop():
     assert (y == 7.0).all()
 
 
+def gemm_padded_rows(layer, acts, m, otype, ldy, fill=7.0):
+    """One qg_gemm into rows of ldy >= N elements pre-filled with `fill`;
+    returns the [m, ldy] output."""
+    dt = torch.float32 if otype == qg.O_F32 else torch.bfloat16
+    y = torch.full((m, ldy), fill, dtype=dt, device="cuda")
+    ws_bytes = qg.gemm_workspace_size(layer.w, m)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    qg.gemm(layer.w, acts.x, acts.xs, m, layer.k, y, otype, ldy, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_MXFP4])
+def test_tiled_right_edge_inside_padded_rows(wtype):
+    """N = 102 ends inside the last 16-byte chunk of a row (bf16: 6 of its 8
+    elements, fp32: 2 of 4), which the tiled kernels' epilogue writes byte by
+    byte; rows of ldy = 104 keep every row start 16-byte aligned.  The valid
+    columns match the oracle, the two padding columns keep their values."""
+    m, n, k, ldy = 256, 102, 512, 104
+    layer = Layer(wtype, n, k, 32 if wtype == qg.W_MXFP4 else 128, seed=81)
+    acts = Acts(wtype == qg.W_MXFP4, m, k, seed=82)
+    disp = qg.describe_dispatch(layer.w, m)
+    assert "tiled" in disp, disp
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        y = gemm_padded_rows(layer, acts, m, otype, ldy)
+        assert (y[:, n:] == 7.0).all(), otype
+        ys[otype] = y[:, :n].contiguous()
+        print(f"  {disp} otype={otype} err={err(ys[otype], yref):.3e}", flush=True)
+    assert err(ys[qg.O_BF16], yref) <= TOL_BF16
+    if layer.mx:
+        check_mx_f32(layer, acts, m, ys[qg.O_F32])
+    else:
+        assert err(ys[qg.O_F32], yref) <= TOL_F32
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+
+
 # ---------------------------------------------------------------------------
 # full-size decode shapes (dense W4A16, memory bound): every element compared
 # ---------------------------------------------------------------------------

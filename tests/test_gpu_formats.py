@@ -313,6 +313,27 @@ def test_w8a8_dense(m, nk):
     _check_w8a8_f32(ys[qg.O_F32].cpu().numpy(), layer, acts, np.arange(m), disp, ref=yref)
 
 
+def test_w8a8_tiled_right_edge_inside_padded_rows():
+    """The W8A8 tiled form (transposed epilogue) with N = 102 inside rows of
+    ldy = 104: the last chunk of each row is written byte by byte, the padding
+    columns keep their values, the valid ones meet the W8A8 bounds."""
+    from test_gpu_dense import gemm_padded_rows
+    m, n, k, ldy = 256, 102, 512, 104
+    layer = W8A8(n, k, seed=103)
+    acts = BlockActs(m, k, seed=104)
+    disp = qg.describe_dispatch(layer.w, m)
+    assert "f8_tiled" in disp, disp
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {}
+    for otype in (qg.O_BF16, qg.O_F32):
+        y = gemm_padded_rows(layer, acts, m, otype, ldy)
+        assert (y[:, n:] == 7.0).all(), otype
+        ys[otype] = y[:, :n].contiguous()
+    assert err(ys[qg.O_BF16], yref) <= TOL_BF16
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    _check_w8a8_f32(ys[qg.O_F32].cpu().numpy(), layer, acts, np.arange(m), disp, ref=yref)
+
+
 @pytest.mark.parametrize("m", [8, 136])
 def test_w8a8_identity_rows_are_exact(m):
     """Unit activations (e4m3 1.0, scale 1) at block edges: each fp32 row is a
