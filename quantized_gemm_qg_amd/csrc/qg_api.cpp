@@ -1152,10 +1152,17 @@ static hipError_t moe_run(const qg_weight *w, const Layout &L, const MoePlan &pl
     int32_t *tiles = (int32_t *)ws;
     int32_t *tiles_s = (int32_t *)((uint8_t *)ws + moe_list_bytes(cap));
     void *xs = (uint8_t *)tiles_s + (small ? moe_list_bytes(cap_s) : 0);  // integer formats only
-    if (!small || min_rows < kMoeAllSmall) {
+    // the small tiles' rows (QG_MOE_SMALL_BM applies to the integer formats)
+    const int sbm = mxt ? kMoeSmallTileRows : moe_small_bm();
+    const bool both = small && min_rows < kMoeAllSmall;
+    if (both)  // the two tile lists in one launch
+      he = launch_moe_tiles2(expert_offsets, d.num_experts, (int32_t)pairs, min_rows, (int32_t)cap, tiles, sbm,
+                             (int32_t)cap_s, tiles_s, stream);
+    else if (!small)
       he = launch_moe_tiles(expert_offsets, d.num_experts, min_rows, 0, kMoeTileRows, (int32_t)pairs,
                             (int32_t)cap, tiles, stream);
-      if (he != hipSuccess) return he;
+    if (he != hipSuccess) return he;
+    if (!small || min_rows < kMoeAllSmall) {
       a.tiles = tiles;
       a.group_m = moe_group_m();
       if (mxt)
@@ -1167,12 +1174,12 @@ static hipError_t moe_run(const qg_weight *w, const Layout &L, const MoePlan &pl
       if (he != hipSuccess) return he;
     }
     if (small) {
-      // the MX small tiles have 64 rows (QG_MOE_SMALL_BM applies to the
-      // integer formats; the list capacity covers either)
-      const int sbm = mxt ? kMoeSmallTileRows : moe_small_bm();
-      he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
-                            (int32_t)cap_s, tiles_s, stream);
-      if (he != hipSuccess) return he;
+      // (the list capacity covers either small-tile height)
+      if (!both) {
+        he = launch_moe_tiles(expert_offsets, d.num_experts, 1, min_rows, sbm, (int32_t)pairs,
+                              (int32_t)cap_s, tiles_s, stream);
+        if (he != hipSuccess) return he;
+      }
       a.tiles = tiles_s;
       a.group_m = 1;
       // (the integer formats' row sums come from the 128-row launch unless it

@@ -297,6 +297,12 @@ uint64_t a16_tiled_ws_bytes(const qg_layer_desc &d, int64_t m);
 hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows,
                             int32_t max_rows, int32_t bm, int32_t pairs, int32_t capacity,
                             int32_t *tiles, hipStream_t s);
+// Both lists of a split in one launch: experts with >= min_rows rows in
+// kMoeTileRows-row tiles (tiles, capacity) and the others with rows in
+// small_bm-row tiles (tiles_small, capacity_small).
+hipError_t launch_moe_tiles2(const int32_t *offsets, int32_t experts, int32_t pairs, int32_t min_rows,
+                             int32_t capacity, int32_t *tiles, int32_t small_bm, int32_t capacity_small,
+                             int32_t *tiles_small, hipStream_t s);
 hipError_t launch_stream_read(const void *src, uint64_t bytes, void *sink, hipStream_t s);
 hipError_t launch_stream_copy(void *dst, const void *src, uint64_t bytes, hipStream_t s);
 // Activation-side kernels (qg_act.hip): bf16 -> MXFP8, SiLU-gated product,

@@ -116,14 +116,24 @@ __global__ __launch_bounds__(1024) void moe_sort_kernel(const int32_t *ids, int6
   }
 }
 
-// Tile list of the tiled MoE kernels: experts with at least min_rows rows, cut
-// into bm-row tiles.  tiles[0] = count, tiles[1] = 0, then (expert, first
-// sorted row) per tile in expert order; at most `capacity` tiles are written
-// (counts are clamped to [0, pairs], so malformed offsets cannot overrun it).
-__global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t *offsets, int32_t experts,
-                                                         int32_t min_rows, int32_t max_rows, int32_t bm,
-                                                         int32_t pairs, int32_t capacity, int32_t *tiles) {
+// Tile list of the tiled MoE kernels: experts with min_rows <= rows <
+// max_rows (max_rows <= 0: no bound), cut into bm-row tiles.  tiles[0] =
+// count, tiles[1] = 0, then (expert, first sorted row) per tile in expert
+// order; at most `capacity` tiles are written (counts are clamped to [0,
+// pairs], so malformed offsets cannot overrun it).  Workgroup b builds list
+// b (a launch builds one list, or both lists of a split between 128-row and
+// small tiles).
+struct TileListArgs {
+  int32_t min_rows, max_rows, bm, capacity;
+  int32_t *tiles;
+};
+
+__global__ __launch_bounds__(1024) void moe_tiles_kernel(const int32_t *offsets, int32_t experts, int32_t pairs,
+                                                         TileListArgs l0, TileListArgs l1) {
   __shared__ int wave_tot[16];
+  const TileListArgs &l = blockIdx.x == 0 ? l0 : l1;
+  const int min_rows = l.min_rows, max_rows = l.max_rows, bm = l.bm, capacity = l.capacity;
+  int32_t *tiles = l.tiles;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int per = (experts + nth - 1) / nth;
   const int e0 = tid * per;
@@ -356,8 +366,17 @@ hipError_t launch_moe_mx(const GemmArgs &a, const qg_layer_desc &d, const Varian
 hipError_t launch_moe_tiles(const int32_t *offsets, int32_t experts, int32_t min_rows,
                             int32_t max_rows, int32_t bm, int32_t pairs, int32_t capacity,
                             int32_t *tiles, hipStream_t s) {
-  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, experts, min_rows,
-                     max_rows, bm, pairs, capacity, tiles);
+  const TileListArgs l{min_rows, max_rows, bm, capacity, tiles};
+  hipLaunchKernelGGL(moe_tiles_kernel, dim3(1), dim3(1024), 0, s, offsets, experts, pairs, l, l);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_tiles2(const int32_t *offsets, int32_t experts, int32_t pairs, int32_t min_rows,
+                             int32_t capacity, int32_t *tiles, int32_t small_bm, int32_t capacity_small,
+                             int32_t *tiles_small, hipStream_t s) {
+  const TileListArgs big{min_rows, 0, kMoeTileRows, capacity, tiles};
+  const TileListArgs small{1, min_rows, small_bm, capacity_small, tiles_small};
+  hipLaunchKernelGGL(moe_tiles_kernel, dim3(2), dim3(1024), 0, s, offsets, experts, pairs, big, small);
   return hipGetLastError();
 }
 
