@@ -361,6 +361,25 @@ def test_dispatch_table_covers_k():
     assert qg.gemm_workspace_size(_bound(qg.layer_desc(qg.W_UINT4, 14336, 4096, 128)), 1) == 0
 
 
+def test_decode_four_tiles_when_rows_fill_lds():
+    """Rows that fill more than half of a CU's LDS leave one two-tile decode
+    workgroup per CU: where that needs more rounds of resident workgroups than
+    four tiles per workgroup, the four-tile instance runs (14336 x 4096 from
+    10 rows; 28672 x 4096, whose two-tile form exceeds one round already at 4
+    rows); one row keeps one tile per workgroup."""
+    def t_of(n, k, m):
+        s = qg.describe_dispatch(_bound(qg.layer_desc(qg.W_UINT4, n, k, 128)), m)
+        assert s.startswith("a16_decode T="), s
+        return int(re.search(r"T=(\d+)", s).group(1)), int(re.search(r"KR=(\d+)", s).group(1))
+    assert t_of(14336, 4096, 1) == (1, 8)
+    for m in (2, 4, 8, 9):
+        assert t_of(14336, 4096, m) == (2, 4), m
+    for m in (10, 12, 16):
+        assert t_of(14336, 4096, m) == (4, 4), m
+    for m in (4, 8, 16):
+        assert t_of(28672, 4096, m) == (4, 4), m
+
+
 def test_binding_maps_a_single_hip_runtime():
     """libqg must share the caller's (torch's) HIP runtime: one libamdhip64 mapped."""
     import subprocess
