@@ -402,6 +402,14 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
       return true;
     }
   }
+  // INT3 (3-bit, no zero points) at one row: two n-tiles of 8 blocks per wave
+  // while that leaves 200 to 512 workgroups (14336 x 4096: 6.75 against 7.00
+  // us; 8192 x 8192: 6.83 against 7.10; 28672 x 4096, 896 workgroups: 10.7
+  // against 10.0 us for one n-tile; UINT3 and the 4-bit formats: no gain)
+  if (m == 1 && d.wtype == QG_W_INT3) {
+    const int64_t wgs = (w.n_tiles + 1) / 2;
+    if (wgs >= 200 && wgs <= 512 && decode_fits(w, m, 2, 8, 1, v)) return true;
+  }
   static const int pairs_one[][2] = {{1, 8}, {2, 4}, {2, 8}, {4, 2}};
   static const int pairs_rows[][2] = {{2, 4}, {1, 8}, {2, 8}, {4, 2}};
   static const int pairs_ext[][2] = {{1, 8}, {1, 4}, {1, 4}, {1, 4}};

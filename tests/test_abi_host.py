@@ -380,6 +380,20 @@ def test_decode_four_tiles_when_rows_fill_lds():
         assert t_of(28672, 4096, m) == (4, 4), m
 
 
+def test_decode_int3_one_row_two_tiles():
+    """INT3 at one row: two n-tiles of 8 blocks per wave while that leaves 200
+    to 512 workgroups, one n-tile otherwise; other formats one n-tile."""
+    def t_kr(wt, n, k):
+        s = qg.describe_dispatch(_bound(qg.layer_desc(wt, n, k, 128)), 1)
+        return tuple(int(v) for v in re.findall(r"(?:T|KR)=(\d+)", s))
+    assert t_kr(qg.W_INT3, 14336, 4096) == (2, 8)
+    assert t_kr(qg.W_INT3, 8192, 8192) == (2, 8)
+    assert t_kr(qg.W_INT3, 28672, 4096) == (1, 8)
+    assert t_kr(qg.W_INT3, 4096, 14336) == (1, 8)
+    for wt in (qg.W_UINT3, qg.W_INT4, qg.W_UINT4):
+        assert t_kr(wt, 14336, 4096) == (1, 8), wt
+
+
 def test_binding_maps_a_single_hip_runtime():
     """libqg must share the caller's (torch's) HIP runtime: one libamdhip64 mapped."""
     import subprocess
