@@ -197,7 +197,9 @@ static int clamp_kr(const qg_layer_desc &d, int T, int kr) {
 // per wave and enough workgroups to cover all 256 CUs, and avoids a K split
 // (which costs a partials round trip and a counter-clearing launch) unless N
 // alone gives too few workgroups.
-static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles) {
+// m: the dense call's rows (0 for MoE and batch-invariant dispatch, whose
+// choice must not depend on them).
+static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int64_t m_tiles, int64_t m = 0) {
   const bool mx = mx_a8(d) || mx_a4(d) || mx_tok(d);
   // T x KR per wave: 4 x 2 (integer formats), 2 x 4 (MX), 2 x 2 (1-, 2-,
   // 8-bit integers, e4m3 weights, W8A8); fewer for short K.
@@ -206,6 +208,27 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
   // when N alone would leave more than half of the CUs idle.
   const bool narrow = ext_a16(d) || w8a8(d);
   int T = mx || narrow ? 2 : 4, KR = mx ? 4 : 2;
+  if (w8a8(d) && m >= 1 && m <= 8) {
+    // W8A8 up to 8 rows: one n-tile of 4 blocks per wave (one row: 14336 x
+    // 4096 15.1 against 17.9 us, 28672 x 4096 24.5 against 33.6, 4096 x
+    // 14336 18.0 against 19.5; at 16 rows no gain)
+    T = 1;
+    KR = 4;
+  } else if ((mx_a8(d) || mx_tok(d)) && m >= 4 && k_blocks <= 32 && n_tiles >= 800) {
+    // MX activations from 4 rows, K <= 4096 over many columns: four n-tiles
+    // of 2 blocks per wave, 16 waves (14336 x 4096 at 16 rows: 10.3 against
+    // 12.1 us per-token, 10.8 against 13.3 MXFP8; at 4 rows 3-8 % less)
+    T = 4;
+    KR = 2;
+  }
+  // dense launches over K >= 4096 of several 16-row tiles (W8A8 from 9
+  // rows): each wave walks its K range in two passes (see below)
+  const bool mx8 = mx_a8(d) || mx_tok(d), int_a16 = !mx && !narrow && !fp4_a16(d);
+  const bool two_pass = k_blocks >= 32 && (w8a8(d) ? m > 8 : (mx8 || int_a16) && m > 16);
+  if (two_pass && mx8) {
+    T = 4;
+    KR = 2;
+  }
   while (KR > 1 && KR > k_blocks) KR /= 2;
   const bool long_k = (k_blocks + KR - 1) / KR > 16;  // K gets split anyway
   while (!long_k && T > 1 && (int64_t)((n_tiles + T - 1) / T) * m_tiles < 128) T /= 2;
@@ -222,6 +245,24 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
     ++splits;
   v.W = (waves_k + splits - 1) / splits;
   v.splits = (waves_k + v.W - 1) / v.W;
+  if (two_pass) {
+    // Each wave accumulates its two passes in registers, leaving fewer
+    // partials to reduce and fewer, fuller workgroups; the waves per
+    // workgroup shrink as the rows grow (the rest of K splits across
+    // workgroups).  Autotune sweeps over 4096 x 14336, 8192 x 8192 and
+    // 14336 x 4096: MXFP8 8192 x 8192 at 32 rows 16.7 against 25.1 us for
+    // one pass over 4 waves x 4 splits, 4096 x 14336 at 128 rows 45.6
+    // against 70.6 on the tiled kernel; W4A16 8192 x 8192 at 64 rows 40.4
+    // against 51.2, 4096 x 14336 at 128 rows 66.3 against 94.0; W8A8 14336 x
+    // 4096 at 16 rows 18.6 against 20.9
+    const int w_cap = mx8 ? (m <= 32 ? 16 : m <= 64 ? 8 : 4)
+                      : w8a8(d) ? (m <= 16 ? 8 : m <= 32 ? 16 : 4)
+                                : (m <= 64 ? 8 : 4);
+    const int per = (waves_k + 1) / 2;
+    const int sp = (per + w_cap - 1) / w_cap;
+    v.W = (per + sp - 1) / sp;
+    v.splits = (per + v.W - 1) / v.W;
+  }
   // a cross-workgroup split needs one arrival counter per output tile in the
   // workspace's counter prefix; past that the workgroup loops over K instead
   if (v.splits > 1 && n_blocks * m_tiles > kMaxSplitCounters) {
@@ -283,13 +324,44 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
               (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31)))
     return false;
   // (W4A4 has only the MX tiled kernel, which serves every M)
-  if (m < (mx_a4(w.desc) ? 1 : mx ? 128 : 256)) return false;
+  if (m < (mx_a4(w.desc) ? 1 : mx ? 128 : 256)) {
+    // MX and W8A8 below 128 rows: the skinny kernel streams the weights
+    // once per 16 rows, the tiled kernel once, so where N gives enough
+    // 128-row tiles the tiled kernel wins from a few dozen rows (W8A8 14336
+    // x 4096 at 32 rows: 29.5 against 39.5 us, 28672 x 4096 at 16 rows: 30.4
+    // against 39.6; W4A8 14336 x 4096 at 64 rows: 23.6 against 35.3, 28672
+    // x 4096 at 32 rows: 23.9 against 35.9; 8192 x 8192 and 4096 x 14336,
+    // with fewer tiles, stay on the skinny kernel's K splits)
+    // Integer formats from 128 rows where N gives 96 or more 128-column
+    // tiles (W4A16 14336 x 4096 at 128 rows: 49.4 against 78.3 us; 8192 x
+    // 8192 and 4096 x 14336 stay on the skinny kernel's two-pass splits)
+    if (!mx) {
+      if (m < 128 || (w.desc.n + 127) / 128 < 96) return false;
+    } else {
+      if (m <= 8) return false;
+      const int64_t tbn = w8a8(w.desc) ? 128 : mx_tile_cols(w.desc.n, m, 128);
+      const int64_t wgs = (w.desc.n + tbn - 1) / tbn;
+      const bool go = w8a8(w.desc) ? (m > 32 && wgs >= 64) || (m > 16 && wgs >= 100) || wgs >= 200
+                                   : (m > 32 && wgs >= 64) || (m > 16 && wgs >= 128);
+      if (!go) return false;
+    }
+  } else if (mx && !mx_a4(w.desc) && !w8a8(w.desc) && m < 256 && w.k_blocks >= 32 &&
+             (w.desc.n + mx_tile_cols(w.desc.n, m, 128) - 1) / mx_tile_cols(w.desc.n, m, 128) < 32) {
+    // MX from 128 rows over fewer than 32 column tiles and K >= 4096: the
+    // tiled kernel leaves most CUs idle, the skinny kernel's two-pass K
+    // splits fill them
+    // (4096 x 14336 at 128 rows: 45.6 against 70.6 us per-token, 52.2
+    // against 73.4 MXFP8; 8192 x 8192, 43 tiles, stays tiled)
+    return false;
+  }
   // 256-row tiles halve the weight re-reads and win at every measured shape
   // once M fills them; 128-row tiles for M in [128, 256)
   int bm = m >= 256 ? 256 : 128;
   if (ov().tiled_bm) bm = ov().tiled_bm;
   int bn = 128;
-  if (!mx && a16_tiled_bn() == 256) {
+  // (integer formats below 256 rows: 128 x 128 tiles, twice the tiles of
+  // 128 x 256 over the few row tiles)
+  if (!mx && a16_tiled_bn() == 256 && m >= 256) {
     bm = 128;
     bn = 256;
   }
@@ -568,7 +640,7 @@ static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
       if (split_counters(w, v, m) > kMaxSplitCounters) v.splits = 1;
       return v;
     }
-    return skinny_for(w.desc, w.n_tiles, w.k_blocks, (m + 15) / 16);
+    return skinny_for(w.desc, w.n_tiles, w.k_blocks, (m + 15) / 16, m);
   }
   if (tiled_for(w, m, &v)) return v;
   if (!ov().tune && decode_for(w, m, &v)) return v;
@@ -579,7 +651,7 @@ static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
     return v;
   }
   const int64_t m_tiles = (m + 15) / 16;
-  return skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles);
+  return skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles, m);
 }
 
 Variant select_moe(const qg_weight &w, int64_t pairs) {
@@ -1555,6 +1627,9 @@ static void tune_candidates(const qg_weight &w, int64_t m, std::vector<Variant> 
           const int W = (waves_k + S - 1) / S;
           if (W < 1 || W > 16) continue;
           add(Variant{0, T, KR, W, (waves_k + W - 1) / W, 0, 0});
+          // each wave walking its K range in two passes
+          const int per = (waves_k + 1) / 2, W2 = (per + S - 1) / S;
+          if (waves_k >= 8 && W2 >= 1 && W2 <= 16) add(Variant{0, T, KR, W2, (per + W2 - 1) / W2, 0, 0});
         }
       }
   }

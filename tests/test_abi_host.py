@@ -349,8 +349,12 @@ def test_dispatch_table_covers_k():
                     assert (S - 1) * W * KR < -(-k // 128) and (W * KR) % 4 == 0, s
                     assert qg.gemm_workspace_size(w, m) >= 65536 + S * -(-n // (16 * T)) * T * 256 * 4
                 continue
-            T, KR, W, S = (int(v) for v in re.findall(r"=(\d+)", s))
-            assert W * KR * S >= -(-k // 128), s
+            # skinny: the waves of all splits cover K in P passes, none empty
+            vals = [int(v) for v in re.findall(r"=(\d+)", s)]
+            T, KR, W, S = vals[:4]
+            P = vals[4] if len(vals) > 4 else 1
+            span, kb = W * KR * S, -(-k // 128)
+            assert span * P >= kb and span * (P - 1) < kb, s
             assert 1 <= W <= 16
     # a split-K layout (long K over too few column tiles to fill the CUs)
     # asks for a workspace
@@ -676,3 +680,49 @@ def test_noalloc_validates_before_any_device_call():
     with pytest.raises(qg.QGError) as e:
         qg.gemm_noalloc(w, FAKE_DEV, None, 32768, 14336, FAKE_DEV, qg.O_BF16, 1024, stream=0)
     assert e.value.status == qg.QG_ERR_BUFFER_TOO_SMALL
+
+
+def test_skinny_two_passes_from_two_row_tiles():
+    """Dense launches over K >= 4096 with two or more 16-row tiles (W8A8 from
+    9 rows): every wave walks its K range in two passes, the waves per
+    workgroup capped by the rows; one pass at one tile, and for the grouped
+    (MoE) and batch-invariant launches."""
+    def parse(wt, n, k, g, m, atype=None):
+        s = qg.describe_dispatch(_bound(qg.layer_desc(wt, n, k, g, atype=atype)), m)
+        vals = [int(v) for v in re.findall(r"=(\d+)", s)]
+        return s, vals
+    for wt, g, atype, lo, caps in [
+            (qg.W_INT4, 128, None, 17, {24: 8, 64: 8, 128: 4}),
+            (qg.W_MXFP4, 32, None, 17, {24: 16, 64: 8, 200: 4}),
+            (qg.W_MXFP4, 32, qg.A_FP8_TOKEN, 17, {32: 16, 48: 8, 128: 4}),
+            (qg.W_FP8, 128, qg.A_FP8_BLOCK, 9, {9: 8, 16: 8, 32: 16})]:
+        for m, cap in caps.items():
+            s, v = parse(wt, 4096, 14336, g, m, atype)
+            assert "skinny" in s and s.endswith("passes=2"), (wt, m, s)
+            T, KR, W, S, P = v
+            per = -(-(-(-112 // KR)) // 2)  # half of the waves along K (K blocks of 128)
+            assert W <= cap and W * S >= per and W * (S - 1) < per, (wt, m, s)
+        s, _ = parse(wt, 4096, 14336, g, lo - 1, atype)
+        assert "passes" not in s, (wt, s)
+    # K below 4096: one pass
+    assert "passes" not in parse(qg.W_INT4, 4096, 2048, 128, 64)[0]
+    # 1-, 2-, 8-bit integers keep one pass
+    assert "passes" not in parse(qg.W_UINT8, 4096, 14336, 128, 64)[0]
+
+
+def test_tiled_needs_enough_column_tiles_below_256_rows():
+    """Integer formats take the tiled kernel from 128 rows (128 x 128 tiles)
+    where N gives 96 or more 128-column tiles; MX (not W8A8) below 256 rows
+    over K >= 4096 needs 32 or more column tiles."""
+    def d(wt, n, k, g, m, atype=None):
+        return qg.describe_dispatch(_bound(qg.layer_desc(wt, n, k, g, atype=atype)), m)
+    assert d(qg.W_INT4, 14336, 4096, 128, 128) == "a16_tiled BM=128 BN=128"
+    assert "skinny" in d(qg.W_INT4, 8192, 8192, 128, 128)
+    assert "skinny" in d(qg.W_INT4, 14336, 4096, 128, 127)
+    assert "tiled" in d(qg.W_INT4, 8192, 8192, 128, 256)
+    assert "skinny" in d(qg.W_MXFP4, 4096, 14336, 32, 128)
+    assert "skinny" in d(qg.W_MXFP4, 4096, 14336, 32, 255)
+    assert "tiled" in d(qg.W_MXFP4, 4096, 14336, 32, 256)
+    assert "tiled" in d(qg.W_MXFP4, 8192, 8192, 32, 128)
+    assert "tiled" in d(qg.W_MXFP4, 136, 896, 32, 130)
+    assert "tiled" in d(qg.W_FP8, 4096, 14336, 128, 128, qg.A_FP8_BLOCK)

@@ -12,7 +12,7 @@ import mx_mfma_model as MM
 import oracle
 import quantized_gemm_qg_amd as qg
 import synth
-from gpu_harness import (TOL_BF16, TOL_F32, Acts, Layer, assert_bf16_is_rne, err, moe_mx_forms, mx_codes,
+from gpu_harness import (TOL_BF16, TOL_F32, Acts, Layer, assert_bf16_is_rne, check_mx_f32, err, moe_mx_forms, mx_codes,
                          require_gpu, run_gemm, to_dev)
 from oracle import quantize as Q
 
@@ -332,6 +332,49 @@ def test_w8a8_tiled_right_edge_inside_padded_rows():
     assert err(ys[qg.O_BF16], yref) <= TOL_BF16
     assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
     _check_w8a8_f32(ys[qg.O_F32].cpu().numpy(), layer, acts, np.arange(m), disp, ref=yref)
+
+
+@pytest.mark.parametrize("m", [40, 100])
+def test_tiled_below_128_rows(m):
+    """Wide layers run the MX and W8A8 tiled forms from a few dozen rows (one
+    partial 128-row tile): W8A8 at N = 8192, MXFP8 and per-token W4A8 at
+    N = 12288, each against the oracle and its instruction model."""
+    k = 256
+    # W8A8
+    layer = W8A8(8192, k, seed=107)
+    acts = BlockActs(m, k, seed=108)
+    disp = qg.describe_dispatch(layer.w, m)
+    assert "f8_tiled" in disp, disp
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {o: run_gemm(layer, acts, m, o) for o in (qg.O_BF16, qg.O_F32)}
+    assert err(ys[qg.O_BF16], yref) <= TOL_BF16
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    _check_w8a8_f32(ys[qg.O_F32].cpu().numpy(), layer, acts, np.arange(m), disp, ref=yref)
+    # per-token FP8 W4A8
+    n = 12288
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=109, atype=qg.A_FP8_TOKEN)
+    acts = TokActs(m, k, seed=110)
+    disp = qg.describe_dispatch(layer.w, m)
+    assert "mx_tiled" in disp, disp
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {o: run_gemm(layer, acts, m, o) for o in (qg.O_BF16, qg.O_F32)}
+    assert err(ys[qg.O_BF16], yref) <= TOL_BF16
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    want = _tok_model(layer, acts, np.arange(m), np.arange(n), disp)
+    got = ys[qg.O_F32].cpu().numpy()
+    diff = got != want
+    ulps = np.abs(got[diff].astype(np.float64) - want[diff]) / np.spacing(np.abs(want[diff]))
+    assert int(diff.sum()) <= max(1, got.size // 1000) and np.all(ulps <= 1.0)
+    # MXFP4 x MXFP8
+    layer = Layer(qg.W_MXFP4, n, k, 32, seed=111)
+    acts = Acts(True, m, k, seed=112)
+    disp = qg.describe_dispatch(layer.w, m)
+    assert "mx_tiled" in disp, disp
+    yref = oracle.gemm(acts.xdq, layer.wdq())
+    ys = {o: run_gemm(layer, acts, m, o) for o in (qg.O_BF16, qg.O_F32)}
+    assert err(ys[qg.O_BF16], yref) <= TOL_BF16
+    assert_bf16_is_rne(ys[qg.O_BF16], ys[qg.O_F32])
+    check_mx_f32(layer, acts, m, ys[qg.O_F32])
 
 
 @pytest.mark.parametrize("m", [8, 136])
