@@ -333,10 +333,13 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
     // x 4096 at 32 rows: 23.9 against 35.9; 8192 x 8192 and 4096 x 14336,
     // with fewer tiles, stay on the skinny kernel's K splits)
     // Integer formats from 128 rows where N gives 96 or more 128-column
-    // tiles (W4A16 14336 x 4096 at 128 rows: 49.4 against 78.3 us; 8192 x
-    // 8192 and 4096 x 14336 stay on the skinny kernel's two-pass splits)
+    // tiles, from 192 rows where it gives 64 (W4A16 14336 x 4096 at 128
+    // rows: 49.4 against 78.3 us; 8192 x 8192 at 200 rows 95.1 against
+    // 117.8, at 128 rows the skinny kernel's two-pass splits win; 4096 x
+    // 14336 stays on them)
     if (!mx) {
-      if (m < 128 || (w.desc.n + 127) / 128 < 96) return false;
+      const int64_t tiles = (w.desc.n + 127) / 128;
+      if (m < 128 || tiles < 64 || (tiles < 96 && m < 192)) return false;
     } else {
       if (m <= 8) return false;
       const int64_t tbn = w8a8(w.desc) ? 128 : mx_tile_cols(w.desc.n, m, 128);
@@ -436,6 +439,15 @@ static bool decode_wide_fits(const qg_weight &w, int64_t m, int W, int KR, Varia
   return true;
 }
 
+// The wide form's K slice: 16 blocks, or 8 where K has at most 64 blocks, so
+// that 4 slices do not leave one workgroup of 8 waves per CU (8192 x 8192,
+// INT4 at M = 16: 11.4 against 12.7 us; 4096 x 14336, 7 slices of 16: 10.7
+// against 14 slices of 8, slower).
+static bool decode_wide_pick(const qg_weight &w, int64_t m, Variant *v) {
+  if (w.k_blocks <= 64 && decode_wide_fits(w, m, 8, 8, v)) return true;
+  return decode_wide_fits(w, m, 8, 16, v) || decode_wide_fits(w, m, 8, 8, v);
+}
+
 static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
   const qg_layer_desc &d = w.desc;
   if (!decode_capable(d) || m < 1 || m > 16 || d.k % 512 != 0) return false;
@@ -502,10 +514,10 @@ static bool decode_for(const qg_weight &w, int64_t m, Variant *v) {
     // K slice once per 8 column tiles (4096 x 14336, UINT4: 10.6 us at M = 8
     // against 14.1 us for two K halves in this form, 11.3 us at M = 16
     // against 20.6 us on the skinny kernel), else K halves
-    if (m > 1 && (decode_wide_fits(w, m, 8, 16, v) || decode_wide_fits(w, m, 8, 8, v))) return true;
+    if (m > 1 && decode_wide_pick(w, m, v)) return true;
     if (m > 1 && decode_fits(w, m, p[0], p[1], 2, v)) return true;
   }
-  return m > 1 && (decode_wide_fits(w, m, 8, 16, v) || decode_wide_fits(w, m, 8, 8, v));
+  return m > 1 && decode_wide_pick(w, m, v);
 }
 
 // Batch-invariant dispatch: the variant depends on (N, K) only, so each

@@ -718,6 +718,8 @@ def test_tiled_needs_enough_column_tiles_below_256_rows():
         return qg.describe_dispatch(_bound(qg.layer_desc(wt, n, k, g, atype=atype)), m)
     assert d(qg.W_INT4, 14336, 4096, 128, 128) == "a16_tiled BM=128 BN=128"
     assert "skinny" in d(qg.W_INT4, 8192, 8192, 128, 128)
+    assert d(qg.W_INT4, 8192, 8192, 128, 192) == "a16_tiled BM=128 BN=128"
+    assert "skinny" in d(qg.W_INT4, 4096, 14336, 128, 255)
     assert "skinny" in d(qg.W_INT4, 14336, 4096, 128, 127)
     assert "tiled" in d(qg.W_INT4, 8192, 8192, 128, 256)
     assert "skinny" in d(qg.W_MXFP4, 4096, 14336, 32, 128)
@@ -726,3 +728,15 @@ def test_tiled_needs_enough_column_tiles_below_256_rows():
     assert "tiled" in d(qg.W_MXFP4, 8192, 8192, 32, 128)
     assert "tiled" in d(qg.W_MXFP4, 136, 896, 32, 130)
     assert "tiled" in d(qg.W_FP8, 4096, 14336, 128, 128, qg.A_FP8_BLOCK)
+
+
+def test_decode_wide_slices_by_k():
+    """Rows too long for LDS over all of K take the wide decode in K slices
+    of 16 blocks, or of 8 where K has at most 64 blocks (4 slices of 16 would
+    leave one workgroup per CU)."""
+    def d(n, k, m):
+        return qg.describe_dispatch(_bound(qg.layer_desc(qg.W_INT4, n, k, 128)), m)
+    assert d(4096, 14336, 16) == "a16_decode_wide KR=16 W=8 splits=7"
+    assert d(8192, 8192, 16) == "a16_decode_wide KR=8 W=8 splits=8"
+    assert d(4096, 8192, 12) == "a16_decode_wide KR=8 W=8 splits=8"
+    assert d(14336, 4096, 16).startswith("a16_decode T=")
