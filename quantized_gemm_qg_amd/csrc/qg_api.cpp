@@ -54,7 +54,7 @@ struct Overrides {
   int mx_bn = 0;            // QG_MX_BN: 192, 224 or 256
   int mx_waves = 0;         // QG_MX_WAVES: 4 or 8
   int a16_waves = 0;        // QG_A16_WAVES: 4 or 8
-  int a16_bn = 0;           // QG_A16_BN: 128
+  int a16_bn = 0;           // QG_A16_BN: 128 or 256 (fixes the integer-format tile width)
   int moe_tiled_min = -1;   // QG_MOE_TILED_MIN: >= 0 (0 disables the tiled MoE kernels)
   int moe_group_m = 0;      // QG_MOE_GROUP_M: 1..64
   int moe_small_bm = 0;     // QG_MOE_SMALL_BM: 32
@@ -112,7 +112,7 @@ bool apply_override(Overrides *o, const char *name, const char *val) {
   } else if (!strcmp(name, "QG_A16_WAVES")) {
     o->a16_waves = (iv == 4 || iv == 8) ? iv : 0;
   } else if (!strcmp(name, "QG_A16_BN")) {
-    o->a16_bn = iv == 128 ? 128 : 0;
+    o->a16_bn = (iv == 128 || iv == 256) ? iv : 0;
   } else if (!strcmp(name, "QG_MOE_TILED_MIN")) {
     o->moe_tiled_min = set ? std::max(0, iv) : -1;
   } else if (!strcmp(name, "QG_MOE_GROUP_M")) {
@@ -315,6 +315,51 @@ static int mx_tile_cols(int64_t n, int64_t m, int bm) {
   return best;
 }
 
+// Tile shape of a dense tiled launch (mx: the MX / W8A8 kernel, else the
+// integer-format kernel) for M >= 128, or any M for W4A4.
+static Variant tiled_shape(const qg_weight &w, int64_t m, bool mx) {
+  const bool w8 = w8a8(w.desc);
+  if (ov().tiled_bm || ov().mx_bn || ov().a16_bn || ov().mx_waves || ov().a16_waves) {
+    // explicit tile or wave overrides: 256-row tiles from 256 rows (integer
+    // formats: 128 x 256, or QG_TILED_BM rows x 128 with QG_A16_BN=128)
+    int bm = m >= 256 ? 256 : 128;
+    if (ov().tiled_bm) bm = ov().tiled_bm;
+    int bn = 128;
+    if (!mx && a16_tiled_bn() == 256 && m >= 256) {
+      bm = 128;
+      bn = 256;
+    }
+    return Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, w8 ? 128 : mx ? mx_tile_cols(w.desc.n, m, bm) : bn};
+  }
+  // The larger tile (256 rows for MX and W8A8, 128 x 256 for the integer
+  // formats, from 256 rows) halves the re-reads of one operand and wins
+  // once the tiles fill the CUs (M = 4096); over fewer tiles than CUs the
+  // 128-row (128 x 128) tile doubles the workgroups.  Cost: rounds of 256
+  // CUs (one workgroup each) times the tile's area, the smaller tile's
+  // taken dearer for its lower reuse: 15 % (MX, W8A8), 40 % (integer
+  // formats, whose 128 x 256 tile also unpacks each code for fewer waves;
+  // 3072 x 4096 at M = 4096: 128.2 us in two rounds of 128 x 256 against
+  // 140.2 in three of 128 x 128).  Autotune sweeps at 256 to 4096 rows:
+  // W4A8 per-token 4096 x 14336 at 256 rows 70.9 against 118.2 us, 14336 x
+  // 4096 24.1 against 39.1; W8A8 8192 x 8192 56.6 against 90.5, 3072 x 4096
+  // at M = 4096 BM = 128; W4A16 8192 x 8192 95.2 against 126.4, 14336 x
+  // 4096 at 384 rows and above keeping 128 x 256.
+  auto cost = [&](int tbm, int tbn, bool small) {
+    const int64_t tiles = ((m + tbm - 1) / tbm) * ((w.desc.n + tbn - 1) / tbn);
+    return (double)((tiles + kNumCUs - 1) / kNumCUs) * tbm * tbn * (small ? (mx ? 1.15 : 1.4) : 1.0);
+  };
+  // (W8A8: 128-column tiles, the only width its 2-KB weight blocks fit)
+  int bm = 128, bn = w8 ? 128 : mx ? mx_tile_cols(w.desc.n, m, 128) : 128;
+  if (m >= 256) {
+    const int bm2 = mx ? 256 : 128, bn2 = w8 ? 128 : mx ? mx_tile_cols(w.desc.n, m, 256) : 256;
+    if (cost(bm2, bn2, false) <= cost(bm, bn, true)) {
+      bm = bm2;
+      bn = bn2;
+    }
+  }
+  return Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, bn};
+}
+
 static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
   if (w.desc.k % 128 != 0 || !has_tiled(w.desc)) return false;
   if (ov().tiled_off) return false;
@@ -324,7 +369,7 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
               (uint64_t)w.n_tiles * w.k_blocks * 1024 >= (1ull << 31)))
     return false;
   // (W4A4 has only the MX tiled kernel, which serves every M)
-  if (m < (mx_a4(w.desc) ? 1 : mx ? 128 : 256)) {
+  if (m < (mx_a4(w.desc) ? 1 : mx ? 128 : 384)) {
     // MX and W8A8 below 128 rows: the skinny kernel streams the weights
     // once per 16 rows, the tiled kernel once, so where N gives enough
     // 128-row tiles the tiled kernel wins from a few dozen rows (W8A8 14336
@@ -332,14 +377,17 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
     // against 39.6; W4A8 14336 x 4096 at 64 rows: 23.6 against 35.3, 28672
     // x 4096 at 32 rows: 23.9 against 35.9; 8192 x 8192 and 4096 x 14336,
     // with fewer tiles, stay on the skinny kernel's K splits)
-    // Integer formats from 128 rows where N gives 96 or more 128-column
-    // tiles, from 192 rows where it gives 64 (W4A16 14336 x 4096 at 128
-    // rows: 49.4 against 78.3 us; 8192 x 8192 at 200 rows 95.1 against
-    // 117.8, at 128 rows the skinny kernel's two-pass splits win; 4096 x
-    // 14336 stays on them)
+    // Integer formats below 384 rows: from 128 rows where N gives 96 or
+    // more 128-column tiles, from 192 rows where it gives 64 (W4A16 14336 x
+    // 4096 at 128 rows: 49.4 against 78.3 us; 8192 x 8192 at 200 rows 95.1
+    // against 117.8, at 128 rows the skinny kernel's two-pass splits win;
+    // 4096 x 14336 at 256 rows 121.5 against 161.5 and 3072 x 4096 28.4
+    // against 49.0 on them; from 256 rows over K < 4096, where the skinny
+    // kernel takes one pass, and from 384 rows the tiled kernel)
     if (!mx) {
       const int64_t tiles = (w.desc.n + 127) / 128;
-      if (m < 128 || tiles < 64 || (tiles < 96 && m < 192)) return false;
+      if (m < 256 || w.k_blocks >= 32)  // (from 256 rows over K < 4096: tiled)
+        if (m < 128 || tiles < 64 || (tiles < 96 && m < 192)) return false;
     } else {
       if (m <= 8) return false;
       const int64_t tbn = w8a8(w.desc) ? 128 : mx_tile_cols(w.desc.n, m, 128);
@@ -357,19 +405,7 @@ static bool tiled_for(const qg_weight &w, int64_t m, Variant *v) {
     // against 73.4 MXFP8; 8192 x 8192, 43 tiles, stays tiled)
     return false;
   }
-  // 256-row tiles halve the weight re-reads and win at every measured shape
-  // once M fills them; 128-row tiles for M in [128, 256)
-  int bm = m >= 256 ? 256 : 128;
-  if (ov().tiled_bm) bm = ov().tiled_bm;
-  int bn = 128;
-  // (integer formats below 256 rows: 128 x 128 tiles, twice the tiles of
-  // 128 x 256 over the few row tiles)
-  if (!mx && a16_tiled_bn() == 256 && m >= 256) {
-    bm = 128;
-    bn = 256;
-  }
-  // (W8A8: 128-column tiles, the only width its 2-KB weight blocks fit)
-  *v = Variant{mx ? 1 : 2, 1, 1, 1, 1, bm, w8a8(w.desc) ? 128 : mx ? mx_tile_cols(w.desc.n, m, bm) : bn};
+  *v = tiled_shape(w, m, mx);
   return true;
 }
 
@@ -643,10 +679,7 @@ static Variant select_dense_heuristic(const qg_weight &w, int64_t m) {
   if (mx_a4(w.desc)) {
     // from 128 rows the tiled kernel with e2m1 operands; below, the MX skinny
     // kernel, which widens each e2m1 fragment exactly to e4m3 in registers
-    if (m >= 128 && !ov().tiled_off) {
-      const int bm = ov().tiled_bm ? ov().tiled_bm : m >= 256 ? 256 : 128;
-      return Variant{1, 1, 1, 1, 1, bm, mx_tile_cols(w.desc.n, m, bm)};
-    }
+    if (m >= 128 && !ov().tiled_off) return tiled_shape(w, m, true);
     if (env_variant(&v)) {
       sanitize(w.desc, &v);
       if (split_counters(w, v, m) > kMaxSplitCounters) v.splits = 1;

@@ -740,3 +740,41 @@ def test_decode_wide_slices_by_k():
     assert d(8192, 8192, 16) == "a16_decode_wide KR=8 W=8 splits=8"
     assert d(4096, 8192, 12) == "a16_decode_wide KR=8 W=8 splits=8"
     assert d(14336, 4096, 16).startswith("a16_decode T=")
+
+
+def test_tiled_shape_by_rounds_and_area():
+    """The larger tile (256 rows; integer formats 128 x 256) from 256 rows
+    only where its rounds of 256 CUs times its area do not exceed the
+    128-row tile's (taken 15 % dearer for MX and W8A8, 40 % for the integer
+    formats); explicit tile overrides keep 256-row tiles from 256 rows."""
+    def d(wt, n, k, g, m, atype=None):
+        return qg.describe_dispatch(_bound(qg.layer_desc(wt, n, k, g, atype=atype)), m)
+    tok, f8 = qg.A_FP8_TOKEN, qg.A_FP8_BLOCK
+    # few tiles: 128-row tiles double the workgroups
+    assert d(qg.W_MXFP4, 4096, 14336, 32, 512, tok) == "mx_tiled BM=128 BN=192"
+    assert d(qg.W_FP8, 8192, 8192, 128, 512, f8) == "f8_tiled BM=128 BN=128"
+    assert d(qg.W_INT4, 8192, 8192, 128, 512) == "a16_tiled BM=128 BN=128"
+    assert d(qg.W_MXFP4, 4096, 14336, 32, 512, qg.A_MXFP4) == "mx_tiled BM=128 BN=192"
+    # many tiles (M = 4096): the larger tile
+    assert d(qg.W_MXFP4, 14336, 4096, 32, 4096, tok) == "mx_tiled BM=256 BN=224"
+    assert d(qg.W_MXFP4, 3072, 4096, 32, 4096) == "mx_tiled BM=256 BN=192"
+    assert d(qg.W_FP8, 14336, 4096, 128, 4096, f8) == "f8_tiled BM=256 BN=128"
+    assert d(qg.W_INT4, 3072, 4096, 128, 4096) == "a16_tiled BM=128 BN=256"
+    assert d(qg.W_INT4, 14336, 4096, 128, 4096) == "a16_tiled BM=128 BN=256"
+    # (W8A8 3072 x 4096: three rounds of 128-row tiles beat two of 256)
+    assert d(qg.W_FP8, 3072, 4096, 128, 4096, f8) == "f8_tiled BM=128 BN=128"
+    # integer formats from 256 to 383 rows over K >= 4096 and few columns:
+    # the skinny kernel's two passes; over K < 4096 the tiled kernel
+    assert "skinny" in d(qg.W_INT4, 3072, 4096, 128, 256)
+    assert "skinny" in d(qg.W_INT4, 4096, 14336, 128, 383)
+    assert "tiled" in d(qg.W_INT4, 4096, 14336, 128, 384)
+    assert "tiled" in d(qg.W_INT4, 200, 640, 128, 300)
+    try:
+        qg.set_override("QG_MX_BN", "256")
+        assert d(qg.W_MXFP4, 128, 1024, 32, 256) == "mx_tiled BM=256 BN=256"
+        qg.set_override("QG_MX_BN", None)
+        qg.set_override("QG_A16_BN", "256")
+        assert d(qg.W_UINT4, 128, 1024, 128, 256) == "a16_tiled BM=128 BN=256"
+    finally:
+        qg.set_override("QG_MX_BN", None)
+        qg.set_override("QG_A16_BN", None)
