@@ -208,24 +208,43 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
   // when N alone would leave more than half of the CUs idle.
   const bool narrow = ext_a16(d) || w8a8(d);
   int T = mx || narrow ? 2 : 4, KR = mx ? 4 : 2;
+  const bool mx8 = mx_a8(d) || mx_tok(d), int_a16 = !mx && !narrow && !fp4_a16(d);
+  int pass_cap = 0;  // the few-row two-pass rules' waves per workgroup
   if (w8a8(d) && m >= 1 && m <= 8) {
     // W8A8 up to 8 rows: one n-tile of 4 blocks per wave (one row: 14336 x
     // 4096 15.1 against 17.9 us, 28672 x 4096 24.5 against 33.6, 4096 x
-    // 14336 18.0 against 19.5; at 16 rows no gain)
+    // 14336 18.0 against 19.5; at 16 rows no gain); K of 4096 to 8191: 2
+    // blocks in two passes of 8 waves (14336 x 4096 at one row 14.6
+    // against 15.0, 28672 x 4096 at 8 rows 28.9 against 30.1)
     T = 1;
     KR = 4;
-  } else if ((mx_a8(d) || mx_tok(d)) && m >= 4 && k_blocks <= 32 && n_tiles >= 800) {
+    if (k_blocks >= 32 && k_blocks < 64) {
+      KR = 2;
+      pass_cap = 8;
+    }
+  } else if (mx8 && k_blocks <= 32 && n_tiles >= 800 && (m >= 4 || (m >= 1 && n_tiles > 1024 && k_blocks >= 32))) {
     // MX activations from 4 rows, K <= 4096 over many columns: four n-tiles
     // of 2 blocks per wave, 16 waves (14336 x 4096 at 16 rows: 10.3 against
-    // 12.1 us per-token, 10.8 against 13.3 MXFP8; at 4 rows 3-8 % less)
+    // 12.1 us per-token, 10.8 against 13.3 MXFP8; at 4 rows 3-8 % less);
+    // beyond 16384 columns, from one row, two passes of 8 waves (28672 x
+    // 4096 per-token at 4 rows 15.3 against 17.8, at one row 15.0 against
+    // 16.4; MXFP8 at 16 rows 18.3 against 20.5)
     T = 4;
     KR = 2;
+    if (n_tiles > 1024 && k_blocks >= 32) pass_cap = 8;
+  } else if (mx8 && m == 1 && (k_blocks == 32 || k_blocks > 64)) {
+    // MX activations at one row over K = 4096 or K > 8192: 2 n-tiles of 2
+    // blocks in two passes of up to 8 waves (14336 x 4096 per-token 8.9
+    // against 9.5 us, 4096 x 14336 10.7 against 11.4; at K = 8192 one pass
+    // of 16 waves needs no K split and stays faster, 10.2 against 10.6)
+    T = 2;
+    KR = 2;
+    pass_cap = 8;
   }
   // dense launches over K >= 4096 of several 16-row tiles (W8A8 from 9
   // rows): each wave walks its K range in two passes (see below)
-  const bool mx8 = mx_a8(d) || mx_tok(d), int_a16 = !mx && !narrow && !fp4_a16(d);
-  const bool two_pass = k_blocks >= 32 && (w8a8(d) ? m > 8 : (mx8 || int_a16) && m > 16);
-  if (two_pass && mx8) {
+  bool two_pass = pass_cap > 0 || (k_blocks >= 32 && (w8a8(d) ? m > 8 : (mx8 || int_a16) && m > 16));
+  if (two_pass && mx8 && !pass_cap) {
     T = 4;
     KR = 2;
   }
@@ -243,6 +262,15 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
          ((waves_k + splits - 1) / splits > 16 ||
           (n_blocks * m_tiles * splits < 128 && waves_k / (splits + 1) >= 4)))
     ++splits;
+  // W8A8 up to 8 rows over K of 16 waves or more: two K passes where N
+  // gives 128 column blocks (4096 x 14336 at one row: 15.7 against 18.9 us
+  // for one pass of 14 waves x 2 splits; 8192 x 8192 15.5 against 17.9 for
+  // one pass of 16 waves), else beyond 16 waves 4 waves per split, at most
+  // 8 splits (1024 x 28672: 10.5 us)
+  if (w8a8(d) && m >= 1 && m <= 8 && waves_k >= 16) {
+    if (n_blocks >= 128) two_pass = true;
+    else if (waves_k > 16) splits = std::max(splits, std::min(8, (waves_k + 3) / 4));
+  }
   v.W = (waves_k + splits - 1) / splits;
   v.splits = (waves_k + v.W - 1) / v.W;
   if (two_pass) {
@@ -255,7 +283,8 @@ static Variant skinny_for(const qg_layer_desc &d, int n_tiles, int k_blocks, int
     // against 70.6 on the tiled kernel; W4A16 8192 x 8192 at 64 rows 40.4
     // against 51.2, 4096 x 14336 at 128 rows 66.3 against 94.0; W8A8 14336 x
     // 4096 at 16 rows 18.6 against 20.9
-    const int w_cap = mx8 ? (m <= 32 ? 16 : m <= 64 ? 8 : 4)
+    const int w_cap = pass_cap ? pass_cap
+                      : mx8 ? (m <= 32 ? 16 : m <= 64 ? 8 : 4)
                       : w8a8(d) ? (m <= 16 ? 8 : m <= 32 ? 16 : 4)
                                 : (m <= 64 ? 8 : 4);
     const int per = (waves_k + 1) / 2;

@@ -702,8 +702,19 @@ def test_skinny_two_passes_from_two_row_tiles():
             T, KR, W, S, P = v
             per = -(-(-(-112 // KR)) // 2)  # half of the waves along K (K blocks of 128)
             assert W <= cap and W * S >= per and W * (S - 1) < per, (wt, m, s)
-        s, _ = parse(wt, 4096, 14336, g, lo - 1, atype)
-        assert "passes" not in s, (wt, s)
+        if wt in (qg.W_INT4,):  # (W8A8 and MX take two passes at few rows too)
+            s, _ = parse(wt, 4096, 14336, g, lo - 1, atype)
+            assert "passes" not in s, (wt, s)
+    # few-row rules: one row of MX activations, (2, 2) in two passes of <= 8
+    # waves; beyond 16384 columns four tiles from one row; elsewhere one pass
+    assert parse(qg.W_MXFP4, 14336, 4096, 32, 1, qg.A_FP8_TOKEN)[0] == \
+        "mx_skinny T=2 KR=2 W=8 splits=1 passes=2"
+    assert parse(qg.W_MXFP4, 4096, 14336, 32, 1)[0] == "mx_skinny T=2 KR=2 W=7 splits=4 passes=2"
+    assert parse(qg.W_MXFP4, 28672, 4096, 32, 4)[0] == "mx_skinny T=4 KR=2 W=8 splits=1 passes=2"
+    assert parse(qg.W_MXFP4, 14336, 4096, 32, 4)[0] == "mx_skinny T=4 KR=2 W=16 splits=1"
+    assert "passes" not in parse(qg.W_MXFP4, 4096, 14336, 32, 16)[0]
+    assert "passes" not in parse(qg.W_MXFP4, 4096, 2048, 32, 1)[0]
+    assert parse(qg.W_MXFP4, 8192, 8192, 32, 1)[0] == "mx_skinny T=2 KR=4 W=16 splits=1"
     # K below 4096: one pass
     assert "passes" not in parse(qg.W_INT4, 4096, 2048, 128, 64)[0]
     # 1-, 2-, 8-bit integers keep one pass
@@ -778,3 +789,18 @@ def test_tiled_shape_by_rounds_and_area():
     finally:
         qg.set_override("QG_MX_BN", None)
         qg.set_override("QG_A16_BN", None)
+
+
+def test_w8a8_few_rows_long_k_splits():
+    """W8A8 up to 8 rows over K of 16 or more waves of 4 blocks: two K
+    passes where N gives 128 column blocks, else beyond 16 waves 4 waves per
+    split, at most 8 splits; K below 16 waves keeps one workgroup."""
+    def d(n, k, m):
+        return qg.describe_dispatch(_bound(qg.layer_desc(qg.W_FP8, n, k, 128, atype=qg.A_FP8_BLOCK)), m)
+    for m in (1, 4, 8):
+        assert d(4096, 14336, m) == "f8_skinny T=1 KR=4 W=7 splits=2 passes=2"
+        assert d(1024, 28672, m) == "f8_skinny T=1 KR=4 W=7 splits=8"
+        assert d(8192, 8192, m) == "f8_skinny T=1 KR=4 W=8 splits=1 passes=2"
+        # (K of 4096 to 8191: 2 blocks in two passes of 8 waves)
+        assert d(14336, 4096, m) == "f8_skinny T=1 KR=2 W=8 splits=1 passes=2"
+        assert d(4096, 2048, m) == "f8_skinny T=1 KR=4 W=4 splits=1"
