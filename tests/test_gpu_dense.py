@@ -107,7 +107,7 @@ def test_split_k_path_matches(override):
         ref = oracle.gemm(acts.xdq, layer.wdq())
         for tune in ("1,2,4,4", "1,1,2,16", "2,2,4,4", "4,2,8,2", "1,4,1,8"):
             override("QG_TUNE", tune)
-            assert int(qg.describe_dispatch(layer.w, m).split("splits=")[1]) > 1
+            assert int(qg.describe_dispatch(layer.w, m).split("splits=")[1].split()[0]) > 1
             need = qg.gemm_workspace_size(layer.w, m)
             assert 0 < need <= ws.numel()
             for _ in range(2):
@@ -499,7 +499,7 @@ def test_workspace_shared_by_mx_tiled_scratch_and_split_skinny():
     b = Layer(qg.W_MXFP4, 1040, k, 32, seed=86)
     assert "mx_tiled" in qg.describe_dispatch(a.w, 256)
     for L in (a, b):
-        assert int(qg.describe_dispatch(L.w, 1).split("splits=")[1]) > 1, qg.describe_dispatch(L.w, 1)
+        assert int(qg.describe_dispatch(L.w, 1).split("splits=")[1].split()[0]) > 1, qg.describe_dispatch(L.w, 1)
     need = max(qg.gemm_workspace_size(L.w, m) for L in (a, b) for m in (1, 256))
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for rnd in range(2):

@@ -33,8 +33,10 @@ def _both(layer, acts, m, otype):
     return y_ws, y_na, wsb
 
 
-# (1024 x 14336: 64 column tiles, so the M = 1 decode call splits K in two)
-@pytest.mark.parametrize("wtype,n,k,g,ms", [(qg.W_UINT4, 1024, 14336, 128, (300, 1)),
+# (1024 x 14336: 400 rows take the tiled kernel (group row sums in the
+# scratch), 200 rows the skinny kernel's K splits (partials, 6 MB), one row
+# the decode kernel's K split in two (64 column tiles))
+@pytest.mark.parametrize("wtype,n,k,g,ms", [(qg.W_UINT4, 1024, 14336, 128, (400, 200, 1)),
                                            (qg.W_MXFP4, 512, 8320, 32, (256, 1))])
 def test_noalloc_matches_gemm_on_consecutive_calls(wtype, n, k, g, ms):
     layer = Layer(wtype, n, k, g, seed=95)
