@@ -715,6 +715,10 @@ def test_skinny_two_passes_from_two_row_tiles():
     assert "passes" not in parse(qg.W_MXFP4, 4096, 14336, 32, 16)[0]
     assert "passes" not in parse(qg.W_MXFP4, 4096, 2048, 32, 1)[0]
     assert parse(qg.W_MXFP4, 8192, 8192, 32, 1)[0] == "mx_skinny T=2 KR=4 W=16 splits=1"
+    # UINT4 (zero points) up to 32 rows: two n-tiles per wave, then four
+    assert parse(qg.W_UINT4, 14336, 4096, 128, 24)[0] == "a16_skinny T=2 KR=2 W=8 splits=1 passes=2"
+    assert parse(qg.W_UINT4, 14336, 4096, 128, 33)[0].startswith("a16_skinny T=4")
+    assert parse(qg.W_INT4, 14336, 4096, 128, 24)[0].startswith("a16_skinny T=4")
     # K below 4096: one pass
     assert "passes" not in parse(qg.W_INT4, 4096, 2048, 128, 64)[0]
     # 1-, 2-, 8-bit integers keep one pass
