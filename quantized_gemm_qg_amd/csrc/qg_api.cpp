@@ -792,11 +792,13 @@ static int moe_tiled_min_rows(const qg_weight &w, int64_t pairs, int64_t x_rows_
   const qg_layer_desc &d = w.desc;
   if (ov().moe_tiled_min >= 0) {
     min_rows = ov().moe_tiled_min;
-  } else if (pairs < 256 && !mx_a8(d) && !mx_a4(d) && !mx_tok(d) && !ext_a16(d) && !fp4_a16(d) && !w8a8(d)) {
-    // 4- and 3-bit integers below 256 pairs: every expert on the skinny
-    // kernel's 4-wave launch, a hot expert's 64+ rows included (E = 256
-    // top-8, 4096 x 7168 gate_up at T = 16: 122 against 140 us with that
-    // expert on 128-row tiles; T = 31 167 against 176)
+  } else if (pairs < 256 && !mx_a4(d) && !ext_a16(d) && !fp4_a16(d) && !w8a8(d)) {
+    // 4- and 3-bit integers, MXFP8 and per-token activations below 256
+    // pairs: every expert on the skinny kernel's 4-wave launch, a hot
+    // expert's 64+ rows included (E = 256 top-8 W4A16, 4096 x 7168 gate_up
+    // at T = 16: 122 against 140 us with that expert on 128-row tiles; E =
+    // 128 top-8 W4A8 gate_up + down at T = 31 69.9 against 78.2, per-token
+    // at T = 16 49.4 against 58.0)
     return 0;
   }
   if (min_rows <= 0) return 0;

@@ -816,15 +816,16 @@ def test_w8a8_few_rows_long_k_splits():
 
 
 def test_moe_integer_formats_below_256_pairs_all_skinny():
-    """4- and 3-bit integer MoE layers below 256 pairs put every expert on
-    the skinny kernel's 4-wave launch (a hot expert's 64+ rows included);
-    from 256 pairs the tiled and small-tile split; MX keeps its split."""
+    """4- and 3-bit integer and MXFP8-activation MoE layers below 256 pairs
+    put every expert on the skinny kernel's 4-wave launch (a hot expert's
+    64+ rows included); from 256 pairs the tiled and small-tile split."""
     w = _bound(qg.layer_desc(qg.W_INT4, 4096, 7168, 128, num_experts=256))
     for t in (1, 16, 31):
         assert qg.describe_moe_dispatch(w, t, 8).endswith("for every expert"), t
     assert "a16_tiled BM=128" in qg.describe_moe_dispatch(w, 32, 8)
-    mx = _bound(qg.layer_desc(qg.W_MXFP4, 4096, 7168, 32, num_experts=256))
-    assert "mx_tiled BM=128" in qg.describe_moe_dispatch(mx, 16, 8)
+    mx = _bound(qg.layer_desc(qg.W_MXFP4, 1280, 4096, 32, num_experts=128))
+    assert qg.describe_moe_dispatch(mx, 16, 8).endswith("for every expert")
+    assert "mx_tiled BM=128" in qg.describe_moe_dispatch(mx, 32, 8)
     try:  # an explicit threshold still applies
         qg.set_override("QG_MOE_TILED_MIN", "64")
         assert "a16_tiled BM=128" in qg.describe_moe_dispatch(w, 16, 8)
