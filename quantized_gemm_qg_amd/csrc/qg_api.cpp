@@ -755,8 +755,12 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
     // MXFP8 and per-token activations: two n-tiles of 2 blocks, 4 waves,
     // looping over K (E = 128 top-8 W4A8, 1280 x 4096 gate_up at T = 1:
     // 11.1 against 11.9 us; 4096 x 640 down at T = 64: 24.7 against 25.5)
-    const int kr = clamp_kr(d, 2, 2);
-    return Variant{0, 2, kr, std::max(1, std::min(4, (w.k_blocks + kr - 1) / kr)), 1, 0, 0};
+    // From 64 pairs over K <= 1024 (8 blocks): four n-tiles on 2 waves
+    // (4096 x 640 down at T = 8: 15.3 against 18.6 us, T = 31 26.1 against
+    // 33.3, per-token at T = 16 21.9 against 24.6)
+    const bool short_k = pairs >= 64 && w.k_blocks <= 8;
+    const int t = short_k ? 4 : 2, kr = clamp_kr(d, t, 2);
+    return Variant{0, t, kr, std::max(1, std::min(short_k ? 2 : 4, (w.k_blocks + kr - 1) / kr)), 1, 0, 0};
   }
   const int64_t m_tiles = std::max<int64_t>(1, (pairs + 15) / 16);
   Variant s = skinny_for(w.desc, w.n_tiles, w.k_blocks, m_tiles);
