@@ -204,9 +204,17 @@ def test_moe_w4a16_256_experts_t64():
     _moe_full(qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, 64, seed=40)
 
 
-@pytest.mark.parametrize("tokens", [1, 64, 512])
+@pytest.mark.parametrize("tokens", [1, 16, 64, 512])
 def test_moe_w4a8_128_experts_padding_shape(tokens):
+    """(T = 16: 128 pairs, every expert on the grouped skinny kernel, gate_up
+    looping over K, the K = 640 down projection on four n-tiles of 2 waves.)"""
     _moe_full(qg.W_MXFP4, 128, 8, 1280, 4096, 4096, 640, tokens, seed=50)
+
+
+def test_moe_w4a16_256_experts_t16():
+    """128 pairs: every expert on the grouped skinny kernel (four n-tiles of
+    2 blocks on 4 waves, looping over K = 7168 and K = 2048)."""
+    _moe_full(qg.W_INT4, 256, 8, 4096, 7168, 7168, 2048, 16, seed=41)
 
 
 @pytest.mark.parametrize("wtype", [qg.W_INT4, qg.W_UINT4, qg.W_MXFP4])
