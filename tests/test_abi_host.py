@@ -837,3 +837,13 @@ def test_moe_integer_formats_below_256_pairs_all_skinny():
         assert "a16_tiled BM=128" in qg.describe_moe_dispatch(w, 16, 8)
     finally:
         qg.set_override("QG_MOE_TILED_MIN", None)
+
+
+def test_moe_w8a8_long_k_four_waves():
+    """W8A8 grouped skinny launches over K > 1024 loop over K on 4 waves:
+    (1, 4) below 64 pairs, (2, 2) from 64; K <= 1024 keeps the dense rule."""
+    up = _bound(qg.layer_desc(qg.W_FP8, 1280, 4096, 128, atype=qg.A_FP8_BLOCK, num_experts=128))
+    assert qg.describe_dispatch(up, 8) == "f8_skinny T=1 KR=4 W=4 splits=1 passes=2"
+    assert qg.describe_dispatch(up, 128) == "f8_skinny T=2 KR=2 W=4 splits=1 passes=4"
+    down = _bound(qg.layer_desc(qg.W_FP8, 4096, 640, 128, atype=qg.A_FP8_BLOCK, num_experts=128))
+    assert qg.describe_dispatch(down, 128) == "f8_skinny T=2 KR=2 W=3 splits=1"
