@@ -742,12 +742,13 @@ Variant select_moe(const qg_weight &w, int64_t pairs) {
   // the grouped kernel keeps K inside one workgroup (no cross-workgroup
   // split); past W waves of KR blocks the workgroup loops over K
   const qg_layer_desc &d = w.desc;
-  if (!mx_a8(d) && !mx_a4(d) && !mx_tok(d) && !ext_a16(d) && !fp4_a16(d) && !w8a8(d)) {
-    // 4- and 3-bit integers: four n-tiles of 2 blocks, 4 waves, looping over
-    // K; the persistent grid then holds 4x the workgroups of 16-wave ones
-    // (E = 256 top-8, 4096 x 7168 gate_up at T = 1: 31.8 against 58.9 us for
-    // (1, 4) over 14 waves, at T = 16 144 against 329; 7168 x 2048 down at
-    // T = 16 80.0 against 90.2 for (4, 2) over 8 waves)
+  if (!mx_a8(d) && !mx_a4(d) && !mx_tok(d) && !ext_a16(d) && !w8a8(d)) {
+    // 4- and 3-bit integers, MXFP4 x bf16: four n-tiles of 2 blocks, 4
+    // waves, looping over K; the persistent grid then holds 4x the
+    // workgroups of 16-wave ones (E = 256 top-8, 4096 x 7168 gate_up at T =
+    // 1: 31.8 against 58.9 us for (1, 4) over 14 waves, at T = 16 144
+    // against 329, MXFP4 x bf16 138 against 321; 7168 x 2048 down at T = 16
+    // 80.0 against 90.2 for (4, 2) over 8 waves)
     const int kr = clamp_kr(d, 4, 2);
     return Variant{0, 4, kr, std::max(1, std::min(4, (w.k_blocks + kr - 1) / kr)), 1, 0, 0};
   }

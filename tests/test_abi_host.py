@@ -847,3 +847,11 @@ def test_moe_w8a8_long_k_four_waves():
     assert qg.describe_dispatch(up, 128) == "f8_skinny T=2 KR=2 W=4 splits=1 passes=4"
     down = _bound(qg.layer_desc(qg.W_FP8, 4096, 640, 128, atype=qg.A_FP8_BLOCK, num_experts=128))
     assert qg.describe_dispatch(down, 128) == "f8_skinny T=2 KR=2 W=3 splits=1"
+
+
+def test_moe_fp4_bf16_four_tiles_four_waves():
+    """MXFP4 x bf16 grouped skinny launches take the integer formats' form:
+    four n-tiles of 2 blocks on 4 waves, looping over K."""
+    w = _bound(qg.layer_desc(qg.W_MXFP4, 4096, 7168, 32, atype=qg.A_BF16, num_experts=256))
+    for pairs in (8, 128):
+        assert qg.describe_dispatch(w, pairs) == "a16_skinny T=4 KR=2 W=4 splits=1 passes=7"
